@@ -1,0 +1,324 @@
+"""CPU oracle of the P-EAGLE parallel draft step and the greedy verify step. TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import this module. The GPU
+path never calls it; it shares no code with the HIP kernels or their host library.
+
+Everything is computed in float64 with plain NumPy, in the order the method describes. Sources (page
+titles; sections):
+  [AWS-P]  "Parallelize speculative decoding with P-EAGLE on Amazon SageMaker AI" (Chinese translation of
+           the AWS post): solution overview -> "sequential dependency in autoregressive EAGLE",
+           "how P-EAGLE breaks the chain", "step-by-step drafting process".
+  [AWS-S]  Korean summary of the same post, detail items 3 (core idea) and 8 (internals).
+  [LESSON] "EAGLE-3 speculative decoding in production" (Korean lesson): concept section (speedup
+           formula and worked example), break-even section, production recipe (alpha measurement).
+  [JP]     Japanese commentary on the same AWS post, section "implementation and performance" (fused
+           kernels that rebuild the batch metadata).
+
+Readings where the pages leave a step open (each is listed with its reason in the design notes):
+  * row 0 = fc(concat(h_low, h_mid, h_high)) + E[last_token] (a sum, not a concatenation);
+    rows 1..K-1 = h_shared + emb_mask, without fc;
+  * decoder layer = pre-RMSNorm GQA attention + pre-RMSNorm SwiGLU MLP, residual stream, no biases;
+  * RoPE: rotate-half pairs (i, i + hd/2), inv_freq_i = base^(-2i/hd), position of row j = L_b + j;
+    cached context keys are already rotated;
+  * row j attends to the L_b context positions and to new rows 0..j (causal inside the K block);
+    q head h reads kv head floor(h / G);
+  * LM head is untied; draft token = argmax with ties to the lowest index;
+  * verify is greedy exact match; the bonus token comes from the same target pass.
+
+Parity status: each function below is pinned by tests under tests/ (closed forms, invariants, special
+cases, brute force on tiny inputs). The full-step logit values have no printed worked example on the
+pages; beyond the invariants they are pinned by the separately written sequential single-row step.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# --------------------------------------------------------------------------------------------------
+# [LESSON] concept section: tokens per target pass = 1 + K*alpha; speedup = (1 + K*alpha) / (1 + eps)
+# [LESSON] break-even section: S = 1  <=>  alpha = eps / K
+
+
+def tokens_per_target_pass(K: int, alpha: float) -> float:
+    return 1.0 + K * alpha
+
+
+def speedup(K: int, alpha: float, eps: float) -> float:
+    return tokens_per_target_pass(K, alpha) / (1.0 + eps)
+
+
+def breakeven_alpha(eps: float, K: int) -> float:
+    return eps / K
+
+
+def alpha_hat(accept_len: np.ndarray, K: int) -> float:
+    """[LESSON] production recipe: alpha = accepted draft tokens per request / draft length.
+    accept_len counts the bonus token, so accepted drafts = accept_len - 1."""
+    a = np.asarray(accept_len, dtype=np.int64)
+    return float((a - 1).sum()) / (a.size * K)
+
+
+def expected_accept_len_iid(p: float, K: int) -> float:
+    """E[accept_len] when each of the K positions matches independently with probability p and
+    acceptance stops at the first mismatch: sum_{i=0..K} p^i (textbook geometric prefix)."""
+    return float(sum(p ** i for i in range(K + 1)))
+
+
+# --------------------------------------------------------------------------------------------------
+# building blocks
+
+
+def rms_norm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * g
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    return x / (1.0 + np.exp(-x))
+
+
+def rope_angles(pos: np.ndarray, head_dim: int, base: float) -> np.ndarray:
+    """angles [P, hd/2] = pos * base^(-2i/hd)."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    inv_freq = base ** (-2.0 * i / head_dim)
+    return np.asarray(pos, dtype=np.float64)[:, None] * inv_freq[None, :]
+
+
+def rope(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
+    """Rotate-half RoPE. x [P, H, hd] at positions pos [P]."""
+    hd = x.shape[-1]
+    h = hd // 2
+    ang = rope_angles(pos, hd, base)
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    x1, x2 = x[..., :h], x[..., h:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def argmax_first(z: np.ndarray) -> np.ndarray:
+    """argmax over the last axis; among equal maxima the lowest index (numpy's documented rule)."""
+    return np.argmax(z, axis=-1).astype(np.int32)
+
+
+def linear(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """y = x . W^T with W stored [out, in]."""
+    return x @ w.T
+
+
+# --------------------------------------------------------------------------------------------------
+# [AWS-P] step-by-step drafting process, step 2: build the K input positions
+
+
+def build_rows(W: dict, last_token: np.ndarray, target_hidden: np.ndarray, K: int) -> np.ndarray:
+    """X [B, K, d].
+
+    Position 1 of the pages (row 0 here) has real context: the token just produced by the target plus
+    the hidden states captured from three target layers (low, middle, high; concatenated to 3d).
+    Positions 2..K (rows 1..K-1) carry no real input: the learned shared hidden state h_shared stands in
+    for the drafter's previous hidden state and the learned mask-token embedding emb_mask for the
+    unknown previous token ([AWS-P] "how P-EAGLE breaks the chain").
+    """
+    B = last_token.shape[0]
+    d = W["emb_mask"].shape[0]
+    X = np.empty((B, K, d), dtype=np.float64)
+    X[:, 0, :] = linear(target_hidden, W["fc"]) + W["embed"][last_token]
+    X[:, 1:, :] = (W["h_shared"] + W["emb_mask"])[None, None, :]
+    return X
+
+
+# --------------------------------------------------------------------------------------------------
+# attention of one request
+
+
+def attention_request(q: np.ndarray, k_ctx: np.ndarray, v_ctx: np.ndarray, k_new: np.ndarray,
+                      v_new: np.ndarray) -> np.ndarray:
+    """One request's GQA attention.
+
+    q [K, Hq, hd] (rotated); k_ctx, v_ctx [Hkv, L, hd] (context, keys already rotated);
+    k_new, v_new [K, Hkv, hd] (this step's rows, keys rotated). Row j sees all L context positions and
+    new rows 0..j. Returns o [K, Hq, hd].
+    """
+    K, Hq, hd = q.shape
+    Hkv, L, _ = k_ctx.shape
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(hd)
+    o = np.empty_like(q)
+    for h in range(Hq):
+        g = h // G
+        keys = np.concatenate([k_ctx[g], k_new[:, g, :]], axis=0)  # [L + K, hd]
+        vals = np.concatenate([v_ctx[g], v_new[:, g, :]], axis=0)
+        for j in range(K):
+            n = L + j + 1
+            s = keys[:n] @ q[j, h] * scale
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            o[j, h] = p @ vals[:n]
+    return o
+
+
+# --------------------------------------------------------------------------------------------------
+# the drafter forward over prebuilt rows
+
+
+def draft_rows(shape, W: dict, X: np.ndarray, seq_len: np.ndarray, kv_context) -> dict:
+    """Run rows X [B, K, d] through the drafter's layers and LM head.
+
+    kv_context(layer, b) -> (k_ctx [Hkv, L_b, hd], v_ctx [Hkv, L_b, hd]) float64.
+    Returns logits [B, K, V], draft [B, K], hidden [B, K, d] (before the final norm) and the rotated
+    keys / values of the new rows per layer (k_new[l], v_new[l] [B, K, Hkv, hd]).
+    """
+    B, K, d = X.shape
+    Hq, Hkv, hd = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+    eps = shape.rms_eps
+    x = X.reshape(B * K, d).astype(np.float64, copy=True)
+    pos = (np.asarray(seq_len, dtype=np.int64)[:, None] + np.arange(K)[None, :]).reshape(-1)
+    k_new_all, v_new_all = [], []
+    for l in range(shape.n_layers):
+        u = rms_norm(x, W[f"l{l}.attn_norm"], eps)
+        qkv = linear(u, W[f"l{l}.wqkv"])
+        q = qkv[:, : Hq * hd].reshape(B * K, Hq, hd)
+        k = qkv[:, Hq * hd: (Hq + Hkv) * hd].reshape(B * K, Hkv, hd)
+        v = qkv[:, (Hq + Hkv) * hd:].reshape(B * K, Hkv, hd)
+        q = rope(q, pos, shape.rope_base)
+        k = rope(k, pos, shape.rope_base)
+        o = np.empty_like(q)
+        for b in range(B):
+            rows = slice(b * K, (b + 1) * K)
+            k_ctx, v_ctx = kv_context(l, b)
+            o[rows] = attention_request(q[rows], k_ctx, v_ctx, k[rows], v[rows])
+        x = x + linear(o.reshape(B * K, Hq * hd), W[f"l{l}.wo"])
+        u = rms_norm(x, W[f"l{l}.mlp_norm"], eps)
+        a = silu(linear(u, W[f"l{l}.wgate"])) * linear(u, W[f"l{l}.wup"])
+        x = x + linear(a, W[f"l{l}.wdown"])
+        k_new_all.append(k.reshape(B, K, Hkv, hd))
+        v_new_all.append(v.reshape(B, K, Hkv, hd))
+    z = linear(rms_norm(x, W["final_norm"], eps), W["lm_head"])
+    logits = z.reshape(B, K, -1)
+    return {"logits": logits, "draft": argmax_first(logits), "hidden": x.reshape(B, K, d),
+            "k_new": k_new_all, "v_new": v_new_all}
+
+
+def draft_step(shape, W: dict, state: dict, kv_context, K: int) -> dict:
+    """[AWS-P] step 2: build K rows per request, one forward pass, K draft tokens at once."""
+    X = build_rows(W, state["last_token"], state["target_hidden"], K)
+    out = draft_rows(shape, W, X, state["seq_len"], kv_context)
+    out["rows"] = X
+    return out
+
+
+# --------------------------------------------------------------------------------------------------
+# written separately, loop by loop: one sequential EAGLE-style draft for one request
+
+
+def eagle_step_sequential(shape, W: dict, token: int, hid3: np.ndarray, L: int, kv_ctx_layers) -> tuple:
+    """One autoregressive EAGLE draft pass for a single request ([AWS-P] "sequential dependency in
+    autoregressive EAGLE"): the input is the embedding of the token just produced plus the projected
+    target hidden states; one row goes through the layers at position L; the LM head gives one token.
+
+    Written with explicit per-head and per-key loops, independently of draft_rows. Returns
+    (token, logits [V]).
+    """
+    d = shape.d_model
+    Hq, Hkv, hd = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+    G = Hq // Hkv
+    half = hd // 2
+    eps = shape.rms_eps
+    fc = W["fc"]
+    x = np.array([float(np.dot(fc[r], hid3)) for r in range(d)]) + W["embed"][token]
+
+    def norm(v, g):
+        return v * (1.0 / math.sqrt(float(np.dot(v, v)) / d + eps)) * g
+
+    def rot(vec):
+        out = vec.copy()
+        for i in range(half):
+            theta = L * shape.rope_base ** (-(2.0 * i) / hd)
+            c, s = math.cos(theta), math.sin(theta)
+            out[i] = vec[i] * c - vec[i + half] * s
+            out[i + half] = vec[i + half] * c + vec[i] * s
+        return out
+
+    for l in range(shape.n_layers):
+        k_ctx, v_ctx = kv_ctx_layers[l]
+        u = norm(x, W[f"l{l}.attn_norm"])
+        wqkv = W[f"l{l}.wqkv"]
+        attn = np.zeros(Hq * hd)
+        k_self = [rot(wqkv[(Hq + g) * hd:(Hq + g + 1) * hd] @ u) for g in range(Hkv)]
+        v_self = [wqkv[(Hq + Hkv + g) * hd:(Hq + Hkv + g + 1) * hd] @ u for g in range(Hkv)]
+        for h in range(Hq):
+            qh = rot(wqkv[h * hd:(h + 1) * hd] @ u)
+            g = h // G
+            scores = [float(np.dot(qh, k_ctx[g, t])) / math.sqrt(hd) for t in range(L)]
+            scores.append(float(np.dot(qh, k_self[g])) / math.sqrt(hd))
+            m = max(scores)
+            wts = [math.exp(sc - m) for sc in scores]
+            tot = sum(wts)
+            acc = np.zeros(hd)
+            for t in range(L):
+                acc += wts[t] * v_ctx[g, t]
+            acc += wts[L] * v_self[g]
+            attn[h * hd:(h + 1) * hd] = acc / tot
+        x = x + W[f"l{l}.wo"] @ attn
+        u = norm(x, W[f"l{l}.mlp_norm"])
+        gate = W[f"l{l}.wgate"] @ u
+        up = W[f"l{l}.wup"] @ u
+        act = np.array([gv / (1.0 + math.exp(-gv)) * uv for gv, uv in zip(gate, up)])
+        x = x + W[f"l{l}.wdown"] @ act
+    z = W["lm_head"] @ norm(x, W["final_norm"])
+    best = 0
+    for v in range(1, z.shape[0]):
+        if z[v] > z[best]:
+            best = v
+    return best, z
+
+
+# --------------------------------------------------------------------------------------------------
+# [AWS-P] step-by-step drafting process, final sentence: the target verifies all K candidates in one
+# pass with the standard acceptance rule. Greedy reading: accept while the draft equals the target's
+# argmax; the target's argmax at the first mismatch (or after K matches) is the bonus token.
+
+
+def verify(target_logits: np.ndarray, draft: np.ndarray) -> dict:
+    """target_logits [B, K+1, V] (position i predicts the token after draft i-1; i = 0 follows the
+    last target token), draft [B, K]. Returns t [B, K+1], n [B] (accepted drafts), accept_len [B] = n+1,
+    bonus [B]."""
+    t = argmax_first(target_logits)
+    B, K = draft.shape
+    n = np.empty(B, dtype=np.int32)
+    for b in range(B):
+        i = 0
+        while i < K and draft[b, i] == t[b, i]:
+            i += 1
+        n[b] = i
+    accept_len = n + 1
+    bonus = t[np.arange(B), n]
+    return {"t": t, "n": n, "accept_len": accept_len.astype(np.int32), "bonus": bonus.astype(np.int32)}
+
+
+def compact(v: dict, req_slot: np.ndarray, seq_len: np.ndarray, finished=None) -> dict:
+    """Batch-metadata rebuild after verify ([JP] implementation and performance: the metadata the
+    serving loop needs for the next step).
+
+    cu_accept [B+1]: exclusive prefix sum of accept_len; out_tokens: request b's accepted tokens (the
+    target argmax prefix t[b, 0..n_b]) at cu_accept[b]...; seq_len' = seq_len + accept_len;
+    last_token' = bonus; surviving (not finished) requests keep their order.
+    """
+    acc = v["accept_len"]
+    B = acc.shape[0]
+    cu = np.zeros(B + 1, dtype=np.int32)
+    for b in range(B):
+        cu[b + 1] = cu[b] + acc[b]
+    out = np.empty(cu[B], dtype=np.int32)
+    for b in range(B):
+        for i in range(acc[b]):
+            out[cu[b] + i] = v["t"][b, i]
+    seq_next_all = (np.asarray(seq_len) + acc).astype(np.int32)
+    fin = np.zeros(B, dtype=bool) if finished is None else np.asarray(finished).astype(bool)
+    keep = [b for b in range(B) if not fin[b]]
+    keep_index = np.array(keep, dtype=np.int32)
+    return {"cu_accept": cu, "out_tokens": out, "keep_index": keep_index, "n_keep": len(keep),
+            "req_slot_next": np.asarray(req_slot, dtype=np.int32)[keep_index],
+            "seq_len_next": seq_next_all[keep_index],
+            "last_token_next": v["bonus"][keep_index].astype(np.int32)}

@@ -1,0 +1,351 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix (no GPU).
+
+Each test names the passage or the mathematical fact it relies on. Expected values here never come
+from the oracle itself: they are printed on the pages (tests/golden), closed forms, hand-computed
+values, textbook special cases, or a brute-force recount written differently.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import pe_oracle as O
+from synth import DrafterShape, Workload, make_weights, make_state, random_draft, plant_target_logits
+from synth.inputs import to_f64, kv_block
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+# a tiny drafter: 2 layers, GQA with G = 2, small vocab
+MINI = DrafterShape("mini-f32", 2, 32, 4, 2, 8, 48, 64, "f32")
+
+
+def _weights64(shape, seed):
+    raw = make_weights(shape, seed)
+    return {k: to_f64(v, shape.dtype) for k, v in raw.items()}
+
+
+def _ctx(shape, L, seed, nlayers=None):
+    rng = np.random.default_rng(seed)
+    n = shape.n_layers if nlayers is None else nlayers
+    return [(rng.standard_normal((shape.n_kv_heads, L, shape.head_dim)),
+             rng.standard_normal((shape.n_kv_heads, L, shape.head_dim))) for _ in range(n)]
+
+
+# ---------------------------------------------------------------- speedup formula (lesson, concept)
+
+def test_speedup_worked_example_from_page():
+    g = json.load(open(os.path.join(GOLDEN, "lesson_speedup.json")))["speedup_worked_example"]
+    K, a, e = g["K"], g["alpha"], g["verify_overhead"]
+    assert O.tokens_per_target_pass(K, a) == pytest.approx(g["tokens_per_target_pass"], abs=1e-12)
+    s = O.speedup(K, a, e)
+    assert s == pytest.approx(g["numerator"] / g["denominator"], abs=1e-12)
+    assert round(s, 1) == g["speedup_as_printed"]
+
+
+def test_breakeven_worked_example_from_page():
+    g = json.load(open(os.path.join(GOLDEN, "lesson_speedup.json")))["breakeven_worked_example"]
+    a = O.breakeven_alpha(g["verify_overhead"], g["K"])
+    assert a == pytest.approx(g["alpha_breakeven_as_printed"], abs=1e-12)
+    # at the break-even alpha the speedup is exactly 1 (closed form)
+    assert O.speedup(g["K"], a, g["verify_overhead"]) == pytest.approx(1.0, abs=1e-12)
+
+
+def test_alpha_hat_identity():
+    # production recipe: alpha = accepted drafts per request / draft length, so that
+    # mean accepted tokens per target pass = 1 + K * alpha exactly.
+    rng = np.random.default_rng(5)
+    for K in (1, 3, 7, 11):
+        acc = rng.integers(1, K + 2, size=97)
+        assert acc.mean() == pytest.approx(O.tokens_per_target_pass(K, O.alpha_hat(acc, K)), abs=1e-12)
+
+
+def test_expected_accept_len_closed_form():
+    # geometric prefix: sum_{i=0..K} p^i = (1 - p^(K+1)) / (1 - p)
+    for p, K in ((0.7, 4), (0.6, 7), (0.85, 11)):
+        assert O.expected_accept_len_iid(p, K) == pytest.approx((1 - p ** (K + 1)) / (1 - p), rel=1e-12)
+    assert O.expected_accept_len_iid(1.0, 5) == 6.0
+
+
+# ---------------------------------------------------------------- verify / accept (greedy)
+
+def _planted(K, V, pattern, rng):
+    """Target logits whose argmax at position i equals draft[i] iff pattern[i] == '1'."""
+    draft = rng.integers(0, V, size=K)
+    T = rng.standard_normal((K + 1, V)) * 0.1
+    tgt = []
+    for i in range(K):
+        tok = int(draft[i]) if pattern[i] == "1" else (int(draft[i]) + 1 + int(rng.integers(0, V - 1))) % V
+        T[i, tok] = 5.0
+        tgt.append(tok)
+    bonus_tok = int(rng.integers(0, V))
+    T[K, bonus_tok] = 5.0
+    tgt.append(bonus_tok)
+    return T, draft, tgt
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
+def test_verify_brute_force_all_patterns(K):
+    V = 16
+    rng = np.random.default_rng(100 + K)
+    for bits in itertools.product("01", repeat=K):
+        pattern = "".join(bits)
+        T, draft, tgt = _planted(K, V, pattern, rng)
+        v = O.verify(T[None], draft[None])
+        first_zero = pattern.find("0")
+        n_expect = K if first_zero < 0 else first_zero
+        assert v["n"][0] == n_expect
+        assert v["accept_len"][0] == n_expect + 1
+        assert v["bonus"][0] == tgt[n_expect]
+        # output identical to the target's greedy tokens
+        assert list(v["t"][0, : n_expect + 1]) == tgt[: n_expect + 1]
+
+
+def test_verify_invariant_all_match_and_first_mismatch():
+    rng = np.random.default_rng(7)
+    for K in (1, 4, 10):
+        T, draft, _ = _planted(K, 50, "1" * K, rng)
+        assert O.verify(T[None], draft[None])["accept_len"][0] == K + 1
+        T, draft, _ = _planted(K, 50, "0" + "1" * (K - 1), rng)
+        assert O.verify(T[None], draft[None])["accept_len"][0] == 1
+
+
+def test_argmax_ties_lowest_index():
+    z = np.array([[0.0, 3.0, 1.0, 3.0, 3.0], [2.0, 2.0, 2.0, 2.0, 2.0]])
+    assert list(O.argmax_first(z)) == [1, 0]
+
+
+def test_compact_against_recount():
+    rng = np.random.default_rng(11)
+    for B, K in ((1, 3), (5, 4), (33, 7)):
+        T = rng.standard_normal((B, K + 1, 20))
+        draft = rng.integers(0, 20, size=(B, K))
+        # make roughly half the positions match
+        t0 = T.argmax(-1)
+        m = rng.random((B, K)) < 0.6
+        draft[m] = t0[:, :K][m]
+        v = O.verify(T, draft)
+        fin = (rng.random(B) < 0.3).astype(np.uint8)
+        slot = rng.permutation(B + 3)[:B]
+        seq = rng.integers(10, 100, size=B)
+        c = O.compact(v, slot, seq, fin)
+        assert list(c["cu_accept"]) == [0] + list(np.cumsum(v["accept_len"]))
+        toks = [int(x) for b in range(B) for x in t0[b, : v["accept_len"][b]]]
+        assert list(c["out_tokens"]) == toks
+        keep = [b for b, f in enumerate(fin) if f == 0]
+        assert list(c["keep_index"]) == keep and c["n_keep"] == len(keep)
+        assert list(c["req_slot_next"]) == [slot[b] for b in keep]
+        assert list(c["seq_len_next"]) == [seq[b] + v["accept_len"][b] for b in keep]
+        assert list(c["last_token_next"]) == [t0[b, v["n"][b]] for b in keep]
+
+
+def test_planted_generator_acceptance_statistics():
+    # per-position i.i.d. planting with probability p gives E[accept_len] = sum_i p^i (C-11 reading);
+    # checked within 5 sigma over many requests
+    w = Workload("stat", MINI, 4000, 5, (8, 8), 0.7, 77)
+    st = make_state(w)
+    draft = random_draft(w)
+    T = plant_target_logits(w, draft, st["alpha"])
+    acc = O.verify(T, draft)["accept_len"].astype(np.float64)
+    mu = O.expected_accept_len_iid(0.7, 5)
+    assert abs(acc.mean() - mu) < 5 * acc.std() / math.sqrt(acc.size)
+
+
+# ---------------------------------------------------------------- building blocks
+
+def test_linear_orientation_hand_example():
+    W = np.array([[1.0, 2.0], [3.0, 4.0]])
+    assert list(O.linear(np.array([[1.0, 1.0]]), W)[0]) == [3.0, 7.0]
+
+
+def test_rms_norm_hand_example_and_closed_form():
+    out = O.rms_norm(np.array([3.0, 4.0]), np.ones(2), 0.0)
+    assert out == pytest.approx([3 / math.sqrt(12.5), 4 / math.sqrt(12.5)], rel=1e-15)
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((5, 64)) * 3
+    g = 1 + 0.02 * rng.standard_normal(64)
+    eps = 1e-6
+    y = O.rms_norm(x, g, eps) / g
+    ms = np.mean(x * x, -1)
+    assert np.mean(y * y, -1) == pytest.approx(ms / (ms + eps), rel=1e-12)
+
+
+def test_silu_closed_forms():
+    assert O.silu(np.array(0.0)) == 0.0
+    assert float(O.silu(np.array(1.0))) == pytest.approx(1 / (1 + math.exp(-1)), rel=1e-15)
+    x = np.linspace(-6, 6, 25)
+    assert O.silu(x) - O.silu(-x) == pytest.approx(x, abs=1e-12)
+
+
+def test_rope_hand_values_pin_pairing_and_frequencies():
+    # hd = 4, base 10000: inv_freq = [1, 10000^(-1/2)] = [1, 0.01]; rotate-half pairs (0,2) and (1,3)
+    e0 = np.array([[[1.0, 0.0, 0.0, 0.0]]])
+    y = O.rope(e0, np.array([1]), 10000.0)[0, 0]
+    assert y == pytest.approx([math.cos(1.0), 0.0, math.sin(1.0), 0.0], abs=1e-15)
+    e1 = np.array([[[0.0, 1.0, 0.0, 0.0]]])
+    y = O.rope(e1, np.array([100]), 10000.0)[0, 0]
+    assert y == pytest.approx([0.0, math.cos(1.0), 0.0, math.sin(1.0)], abs=1e-13)
+    e2 = np.array([[[0.0, 0.0, 1.0, 0.0]]])
+    y = O.rope(e2, np.array([1]), 10000.0)[0, 0]
+    assert y == pytest.approx([-math.sin(1.0), 0.0, math.cos(1.0), 0.0], abs=1e-15)
+
+
+def test_rope_identity_norm_and_relative_position():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((3, 2, 16))
+    assert np.array_equal(O.rope(x, np.zeros(3, dtype=int), 10000.0), x)
+    y = O.rope(x, np.array([5, 77, 4000]), 10000.0)
+    assert np.linalg.norm(y, axis=-1) == pytest.approx(np.linalg.norm(x, axis=-1), rel=1e-12)
+    q, k = rng.standard_normal((1, 1, 16)), rng.standard_normal((1, 1, 16))
+    d1 = np.sum(O.rope(q, np.array([9]), 1e4) * O.rope(k, np.array([3]), 1e4))
+    d2 = np.sum(O.rope(q, np.array([1009]), 1e4) * O.rope(k, np.array([1003]), 1e4))
+    assert d1 == pytest.approx(d2, rel=1e-9)
+
+
+# ---------------------------------------------------------------- attention
+
+def _attn_brute(q, k_ctx, v_ctx, k_new, v_new):
+    """per-key loop, with an explicit mask test"""
+    K, Hq, hd = q.shape
+    Hkv, L, _ = k_ctx.shape
+    G = Hq // Hkv
+    o = np.zeros_like(q)
+    for j in range(K):
+        for h in range(Hq):
+            g = h // G
+            num = np.zeros(hd)
+            den = 0.0
+            allk = [(k_ctx[g, t], v_ctx[g, t], t) for t in range(L)] + \
+                   [(k_new[i, g], v_new[i, g], L + i) for i in range(K)]
+            m = max(float(np.dot(q[j, h], kk)) / math.sqrt(hd) for kk, _, pos in allk if pos <= L + j)
+            for kk, vv, pos in allk:
+                if pos > L + j:
+                    continue
+                wgt = math.exp(float(np.dot(q[j, h], kk)) / math.sqrt(hd) - m)
+                num += wgt * vv
+                den += wgt
+            o[j, h] = num / den
+    return o
+
+
+def test_attention_matches_brute_force():
+    rng = np.random.default_rng(3)
+    for (K, Hq, Hkv, hd, L) in ((1, 2, 1, 4, 0), (3, 4, 2, 8, 5), (4, 8, 2, 8, 9)):
+        q = rng.standard_normal((K, Hq, hd))
+        kc, vc = rng.standard_normal((Hkv, L, hd)), rng.standard_normal((Hkv, L, hd))
+        kn, vn = rng.standard_normal((K, Hkv, hd)), rng.standard_normal((K, Hkv, hd))
+        assert O.attention_request(q, kc, vc, kn, vn) == pytest.approx(_attn_brute(q, kc, vc, kn, vn),
+                                                                       rel=1e-12, abs=1e-12)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(4)
+    # one key (L = 0, K = 1): softmax of a single score is 1, output is that value row exactly
+    q = rng.standard_normal((1, 4, 8))
+    kn, vn = rng.standard_normal((1, 2, 8)), rng.standard_normal((1, 2, 8))
+    o = O.attention_request(q, np.zeros((2, 0, 8)), np.zeros((2, 0, 8)), kn, vn)
+    assert np.array_equal(o[0, :2], np.repeat(vn[0, :1], 2, 0)) and np.array_equal(o[0, 2:], np.repeat(vn[0, 1:], 2, 0))
+    # identical keys: uniform weights, output = mean of the visible values
+    L, K = 6, 3
+    key = rng.standard_normal(8)
+    kc = np.tile(key, (1, L, 1))
+    kn = np.tile(key, (K, 1, 1))
+    vc, vn = rng.standard_normal((1, L, 8)), rng.standard_normal((K, 1, 8))
+    o = O.attention_request(rng.standard_normal((K, 2, 8)), kc, vc, kn, vn)
+    allv = np.concatenate([vc[0], vn[:, 0]], 0)
+    for j in range(K):
+        assert o[j, 0] == pytest.approx(allv[: L + j + 1].mean(0), rel=1e-12)
+
+
+# ---------------------------------------------------------------- row building and whole-step invariants
+
+def test_build_rows_structure():
+    # "Paris" example: K = 4, position 1 is real, positions 2..4 are the learned placeholders
+    W = _weights64(MINI, 9)
+    st = make_state(Workload("r", MINI, 3, 4, (5, 5), 0.7, 9))
+    hid = to_f64(st["target_hidden"], "f32")
+    X = O.build_rows(W, st["last_token"], hid, 4)
+    for j in (1, 2, 3):
+        assert np.array_equal(X[:, j], np.broadcast_to(W["h_shared"] + W["emb_mask"], X[:, j].shape))
+    assert X[:, 0] == pytest.approx(hid @ W["fc"].T + W["embed"][st["last_token"]], rel=1e-14)
+    W0 = dict(W, fc=np.zeros_like(W["fc"]))
+    X0 = O.build_rows(W0, st["last_token"], hid, 4)
+    assert np.array_equal(X0[:, 0], W["embed"][st["last_token"]])
+
+
+def _step(shape, W, tokens, hid, seq, ctx, K):
+    st = {"last_token": np.asarray(tokens), "target_hidden": hid, "seq_len": np.asarray(seq)}
+    return O.draft_step(shape, W, st, lambda l, b: ctx[b][l], K)
+
+
+def test_k1_parallel_equals_sequential_eagle_step():
+    # invariant 2: with K = 1 there are no placeholders; the step is one autoregressive EAGLE pass
+    W = _weights64(MINI, 21)
+    rng = np.random.default_rng(21)
+    for L in (0, 1, 7):
+        tok = int(rng.integers(0, MINI.vocab))
+        hid = rng.standard_normal((1, 3 * MINI.d_model))
+        ctx = _ctx(MINI, L, 100 + L)
+        out = _step(MINI, W, [tok], hid, [L], [ctx], 1)
+        t_seq, z_seq = O.eagle_step_sequential(MINI, W, tok, hid[0], L, ctx)
+        assert out["logits"][0, 0] == pytest.approx(z_seq, rel=1e-10, abs=1e-12)
+        assert out["draft"][0, 0] == t_seq
+
+
+def test_row0_of_k_block_equals_k1_step():
+    W = _weights64(MINI, 22)
+    rng = np.random.default_rng(22)
+    hid = rng.standard_normal((2, 3 * MINI.d_model))
+    ctx = [_ctx(MINI, 4, 1), _ctx(MINI, 9, 2)]
+    a = _step(MINI, W, [3, 40], hid, [4, 9], ctx, 1)
+    b = _step(MINI, W, [3, 40], hid, [4, 9], ctx, 5)
+    assert b["logits"][:, 0] == pytest.approx(a["logits"][:, 0], rel=1e-12, abs=1e-13)
+
+
+def test_causality_later_rows_do_not_change_earlier_rows():
+    # invariant 3: under the causal mask, perturbing rows j' > j leaves rows <= j unchanged
+    W = _weights64(MINI, 23)
+    rng = np.random.default_rng(23)
+    K = 5
+    st = {"last_token": np.array([7, 11]), "target_hidden": rng.standard_normal((2, 3 * MINI.d_model)),
+          "seq_len": np.array([6, 3])}
+    ctx = [_ctx(MINI, 6, 3), _ctx(MINI, 3, 4)]
+    X = O.build_rows(W, st["last_token"], st["target_hidden"], K)
+    base = O.draft_rows(MINI, W, X, st["seq_len"], lambda l, b: ctx[b][l])
+    for j in range(K - 1):
+        Xp = X.copy()
+        Xp[:, j + 1:] += rng.standard_normal(Xp[:, j + 1:].shape)
+        pert = O.draft_rows(MINI, W, Xp, st["seq_len"], lambda l, b: ctx[b][l])
+        assert np.allclose(pert["logits"][:, : j + 1], base["logits"][:, : j + 1], rtol=1e-13, atol=1e-13)
+        assert not np.allclose(pert["logits"][:, j + 1:], base["logits"][:, j + 1:])
+        for l in range(MINI.n_layers):
+            assert np.allclose(pert["k_new"][l][:, : j + 1], base["k_new"][l][:, : j + 1], rtol=1e-13, atol=1e-13)
+
+
+def test_requests_are_independent():
+    # a request's draft depends only on its own state and cache
+    W = _weights64(MINI, 24)
+    rng = np.random.default_rng(24)
+    hid = rng.standard_normal((3, 3 * MINI.d_model))
+    ctx = [_ctx(MINI, 4, 5), _ctx(MINI, 8, 6), _ctx(MINI, 2, 7)]
+    full = _step(MINI, W, [1, 2, 3], hid, [4, 8, 2], ctx, 3)
+    one = _step(MINI, W, [2], hid[1:2], [8], ctx[1:2], 3)
+    assert one["logits"][0] == pytest.approx(full["logits"][1], rel=1e-12, abs=1e-13)
+
+
+# ---------------------------------------------------------------- the shared input generator
+
+def test_bf16_rounding_nearest_even():
+    from synth import bf16_bits
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 1.0 + 2 ** -8 + 2 ** -20], dtype=np.float32)
+    assert list(bf16_bits(x)) == [0x3F80, 0x3F80, 0x3F82, 0xC020, 0x3F81]
+
+
+def test_kv_blocks_reproducible_per_request():
+    w = Workload("kv", MINI, 3, 2, (4, 9), 0.7, 31)
+    a = kv_block(w, 1, 0, 2, 5)
+    b = kv_block(w, 1, 0, 2, 5)
+    assert np.array_equal(a, b) and not np.array_equal(a, kv_block(w, 1, 1, 2, 5))
