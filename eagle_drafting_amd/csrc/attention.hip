@@ -1,0 +1,339 @@
+// Drafter attention: request b's K new rows against its cache slot, causal inside the K block.
+//
+// Row j of request b sits at position L_b + j and sees cache positions 0 .. L_b + j (the L_b context
+// positions plus new rows 0..j, whose rotated keys and values were just appended). Grouped-query
+// attention: q head h reads kv head h / G. Scores are scaled by 1/sqrt(hd); softmax in fp32.
+//
+// bf16 path (gfx950 MFMA): one workgroup per (request, kv head, key split). The G*K query rows of the
+// kv head form the MFMA column operand, so every staged key/value tile is used by all of them: scores are
+// computed transposed, S^T = K_tile . Q^T (keys x rows), which leaves each lane owning one query row —
+// the same row ownership as O^T = V^T . P^T — so the online-softmax rescaling needs no lane exchange
+// beyond two xor-shuffles for the per-row max and sum. K and V tiles are staged through LDS with 16-byte
+// coalesced loads. Each (split, sub-stream) writes an unnormalised partial (O, m, l); a second kernel
+// merges them in a fixed order (log-sum-exp), so results are independent of scheduling.
+#include "common.h"
+#include "kernels.h"
+
+namespace pe {
+
+static inline int attn_sub_streams(int R) {
+  const int RT = (R + 15) / 16;
+  return RT == 1 ? 4 : RT == 2 ? 2 : 1;
+}
+
+AttnPlan plan_attention(int B, int K, int Hq, int Hkv, int max_ctx) {
+  AttnPlan p;
+  const int R = (Hq / Hkv) * K;
+  p.sub = attn_sub_streams(R);
+  // aim for ~1024 workgroups at full context; chunks are whole 128-key staging rounds
+  long long want = (long long)B * Hkv * (long long)(max_ctx + K) / 1024;
+  int chunk = (int)((want + 127) / 128) * 128;
+  if (chunk < 128) chunk = 128;
+  if (chunk > 4096) chunk = 4096;
+  p.chunk = chunk;
+  p.nsplit = (max_ctx + K + chunk - 1) / chunk;
+  return p;
+}
+
+size_t attn_partial_floats(int M, int Hq, int hd, const AttnPlan& p) {
+  return (size_t)M * Hq * p.nsplit * p.sub * (hd + 2);
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc,
+                                                        const bf16_t* __restrict__ Vc,
+                                                        const int* __restrict__ seq_len,
+                                                        const int* __restrict__ req_slot, int K, int Hq, int Hkv,
+                                                        int max_ctx, int n_slots, int chunk, int nsplit, int sub,
+                                                        float* __restrict__ part, float scale) {
+  constexpr int KT = 32;                      // keys per MFMA key tile
+  constexpr int NKT = HD == 128 ? 2 : 4;      // key tiles staged per round
+  constexpr int KEYS = KT * NKT;              // keys staged per round
+  constexpr int STR = HD + 8;                 // LDS row stride (elements), 16 B of padding
+  constexpr int HS = HD / 32;                 // k-steps of the score contraction
+  constexpr int CT = HD / 16;                 // 16-column tiles of the output
+  __shared__ __attribute__((aligned(16))) bf16_t sK[KEYS * STR];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[KEYS * STR];
+
+  const int b = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
+  const int split = blockIdx.y;
+  const int G = Hq / Hkv, R = G * K, RT = (R + 15) / 16;
+  const int L = seq_len[b], slot = req_slot[b];
+  if (slot < 0 || slot >= n_slots || L < 0 || L + K > max_ctx) return;
+  const int Lk = L + K;
+  const int k_begin = split * chunk;
+  if (k_begin >= Lk) return;
+  const int k_end = min(Lk, k_begin + chunk);
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lr = lane & 15, lq = lane >> 4;
+  int rt0, nrt, ks_id;
+  if (sub > 1) {  // RT * sub == 4: waves share row tiles and take alternate key tiles
+    rt0 = wave % RT;
+    nrt = 1;
+    ks_id = wave / RT;
+  } else {  // rows spread over waves (row tiles w and w + 4)
+    rt0 = wave;
+    nrt = (wave < RT ? 1 : 0) + (wave + 4 < RT ? 1 : 0);
+    ks_id = 0;
+  }
+
+  const bf16x8_t zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+  bf16x8_t qf[2][HS];
+  f32x4_t o[2][CT];
+  float m_run[2], l_run[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    m_run[t] = -1e30f;
+    l_run[t] = 0.f;
+#pragma unroll
+    for (int hs = 0; hs < HS; ++hs) qf[t][hs] = zero8;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) o[t][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (t < nrt) {
+      const int row = (rt0 + 4 * t) * 16 + lr;
+      if (row < R) {
+        const int hl = row / K, j = row % K;
+        const bf16_t* q = Q + ((size_t)(b * K + j) * Hq + (g * G + hl)) * HD;
+#pragma unroll
+        for (int hs = 0; hs < HS; ++hs) qf[t][hs] = *(const bf16x8_t*)(q + 32 * hs + 8 * lq);
+      }
+    }
+  }
+
+  const size_t head_off = ((size_t)slot * Hkv + g) * max_ctx * HD;
+  const bf16_t* kb = Kc + head_off;
+  const bf16_t* vb = Vc + head_off;
+
+  for (int base = k_begin; base < k_end; base += KEYS) {
+    constexpr int PIECES = KEYS * HD / 8;
+    for (int p = threadIdx.x; p < PIECES; p += 256) {
+      const int key = p / (HD / 8), c8 = p % (HD / 8);
+      const int kp = base + key;
+      bf16x8_t kv = zero8, vv = zero8;
+      if (kp < k_end) {
+        kv = *(const bf16x8_t*)(kb + (size_t)kp * HD + 8 * c8);
+        vv = *(const bf16x8_t*)(vb + (size_t)kp * HD + 8 * c8);
+      }
+      *(bf16x8_t*)(sK + key * STR + 8 * c8) = kv;
+      *(bf16x8_t*)(sV + key * STR + 8 * c8) = vv;
+    }
+    __syncthreads();
+    if (nrt > 0) {
+      for (int kt = 0; kt < NKT; ++kt) {
+        const int tb = base + kt * KT;
+        if (tb >= k_end) break;
+        if (sub > 1 && (((tb - k_begin) / KT) % sub) != ks_id) continue;
+        bf16x8_t pf[2];
+        float alpha[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          pf[t] = zero8;
+          alpha[t] = 1.f;
+          if (t >= nrt) continue;
+          f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int hs = 0; hs < HS; ++hs) {
+            const bf16x8_t ka0 = *(const bf16x8_t*)(sK + (kt * KT + lr) * STR + 32 * hs + 8 * lq);
+            const bf16x8_t ka1 = *(const bf16x8_t*)(sK + (kt * KT + 16 + lr) * STR + 32 * hs + 8 * lq);
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0, qf[t][hs], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1, qf[t][hs], s1, 0, 0, 0);
+          }
+          const int row = (rt0 + 4 * t) * 16 + lr;
+          const int lim = row < R ? min(k_end, L + (row % K) + 1) : 0;  // visible keys: < lim
+          float sv[8];
+          float tmax = -INFINITY;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int k0 = tb + 4 * lq + r, k1 = tb + 16 + 4 * lq + r;
+            sv[r] = k0 < lim ? s0[r] * scale : -INFINITY;
+            sv[4 + r] = k1 < lim ? s1[r] * scale : -INFINITY;
+            tmax = fmaxf(tmax, fmaxf(sv[r], sv[4 + r]));
+          }
+          tmax = fmaxf(tmax, __shfl_xor(tmax, 16, PE_WAVE));
+          tmax = fmaxf(tmax, __shfl_xor(tmax, 32, PE_WAVE));
+          const float mnew = fmaxf(m_run[t], tmax);
+          alpha[t] = __expf(m_run[t] - mnew);
+          float psum = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float pe = __expf(sv[e] - mnew);
+            psum += pe;
+            pf[t][e] = (short)f32_to_bf16(pe);
+          }
+          psum += __shfl_xor(psum, 16, PE_WAVE);
+          psum += __shfl_xor(psum, 32, PE_WAVE);
+          l_run[t] = l_run[t] * alpha[t] + psum;
+          m_run[t] = mnew;
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          bf16x8_t va;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            va[e] = (short)sV[(kt * KT + 4 * lq + e) * STR + ct * 16 + lr];
+            va[4 + e] = (short)sV[(kt * KT + 16 + 4 * lq + e) * STR + ct * 16 + lr];
+          }
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            if (t >= nrt) continue;
+            f32x4_t acc = o[t][ct];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] *= alpha[t];
+            o[t][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[t], acc, 0, 0, 0);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  const int nsub = nsplit * sub;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (t >= nrt) continue;
+    const int row = (rt0 + 4 * t) * 16 + lr;
+    if (row >= R) continue;
+    const int hl = row / K, j = row % K;
+    const size_t rid = ((size_t)b * Hq + (g * G + hl)) * K + j;
+    float* dst = part + (rid * nsub + (size_t)split * sub + ks_id) * (HD + 2);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[ct * 16 + 4 * lq + r] = o[t][ct][r];
+    if (lq == 0) {
+      dst[HD] = m_run[t];
+      dst[HD + 1] = l_run[t];
+    }
+  }
+}
+
+// O[b*K + j][h] = sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s over the splits that hold keys
+template <int HD>
+__global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restrict__ part, bf16_t* __restrict__ O,
+                                                          const int* __restrict__ seq_len,
+                                                          const int* __restrict__ req_slot, int K, int Hq,
+                                                          int max_ctx, int n_slots, int chunk, int nsplit,
+                                                          int sub) {
+  const int rid = blockIdx.x;
+  const int j = rid % K, h = (rid / K) % Hq, b = rid / (K * Hq);
+  bf16_t* out = O + ((size_t)(b * K + j) * Hq + h) * HD;
+  const int L = seq_len[b], slot = req_slot[b];
+  if (slot < 0 || slot >= n_slots || L < 0 || L + K > max_ctx) {
+    for (int c = threadIdx.x; c < HD; c += 64) out[c] = 0;
+    return;
+  }
+  const int ns = ((L + K + chunk - 1) / chunk) * sub;
+  const float* src = part + (size_t)rid * nsplit * sub * (HD + 2);
+  float M = -1e30f;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, src[(size_t)s * (HD + 2) + HD]);
+  float den = 0.f;
+  for (int s = 0; s < ns; ++s) den += __expf(src[(size_t)s * (HD + 2) + HD] - M) * src[(size_t)s * (HD + 2) + HD + 1];
+  const float inv = 1.f / den;
+  for (int c = threadIdx.x; c < HD; c += 64) {
+    float num = 0.f;
+    for (int s = 0; s < ns; ++s) num += __expf(src[(size_t)s * (HD + 2) + HD] - M) * src[(size_t)s * (HD + 2) + c];
+    out[c] = f32_to_bf16(num * inv);
+  }
+}
+
+hipError_t launch_attention_bf16(const AttnPlan& p, const void* Q, const void* Kc, const void* Vc,
+                                 const int* seq_len, const int* req_slot, int B, int K, int Hq, int Hkv, int hd,
+                                 int max_ctx, int n_slots, float* part, hipStream_t st) {
+  dim3 grid(B * Hkv, p.nsplit), block(256);
+  const float scale = 1.0f / sqrtf((float)hd);
+  if (hd == 128)
+    hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, block, 0, st, (const bf16_t*)Q, (const bf16_t*)Kc,
+                       (const bf16_t*)Vc, seq_len, req_slot, K, Hq, Hkv, max_ctx, n_slots, p.chunk, p.nsplit, p.sub,
+                       part, scale);
+  else
+    hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, block, 0, st, (const bf16_t*)Q, (const bf16_t*)Kc,
+                       (const bf16_t*)Vc, seq_len, req_slot, K, Hq, Hkv, max_ctx, n_slots, p.chunk, p.nsplit, p.sub,
+                       part, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_combine_bf16(const AttnPlan& p, const float* part, void* O, const int* seq_len,
+                                         const int* req_slot, int B, int K, int Hq, int Hkv, int hd, int max_ctx,
+                                         int n_slots, hipStream_t st) {
+  (void)Hkv;
+  dim3 grid(B * Hq * K), block(64);
+  if (hd == 128)
+    hipLaunchKernelGGL(attn_combine_kernel<128>, grid, block, 0, st, part, (bf16_t*)O, seq_len, req_slot, K, Hq,
+                       max_ctx, n_slots, p.chunk, p.nsplit, p.sub);
+  else
+    hipLaunchKernelGGL(attn_combine_kernel<64>, grid, block, 0, st, part, (bf16_t*)O, seq_len, req_slot, K, Hq,
+                       max_ctx, n_slots, p.chunk, p.nsplit, p.sub);
+  return hipGetLastError();
+}
+
+// fp32 path (small fp32 drafter): one workgroup per (request, q head, row); scores of all visible keys in
+// LDS, exact two-pass softmax, then the value sum.
+__global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__ Q, const float* __restrict__ Kc,
+                                                       const float* __restrict__ Vc, const int* __restrict__ seq_len,
+                                                       const int* __restrict__ req_slot, int K, int Hq, int Hkv,
+                                                       int hd, int max_ctx, int n_slots, float* __restrict__ O,
+                                                       float scale) {
+  extern __shared__ float smem[];
+  float* sc = smem;              // [max_ctx]
+  float* sq = smem + max_ctx;    // [hd]
+  float* red = sq + hd;          // [256]
+  const int rid = blockIdx.x;
+  const int j = rid % K, h = (rid / K) % Hq, b = rid / (K * Hq);
+  const int g = h / (Hq / Hkv);
+  const int m = b * K + j;
+  float* out = O + ((size_t)m * Hq + h) * hd;
+  const int L = seq_len[b], slot = req_slot[b];
+  if (slot < 0 || slot >= n_slots || L < 0 || L + K > max_ctx) {
+    for (int c = threadIdx.x; c < hd; c += 256) out[c] = 0.f;
+    return;
+  }
+  const int n = L + j + 1;
+  for (int c = threadIdx.x; c < hd; c += 256) sq[c] = Q[((size_t)m * Hq + h) * hd + c];
+  __syncthreads();
+  const float* kb = Kc + ((size_t)slot * Hkv + g) * max_ctx * hd;
+  const float* vb = Vc + ((size_t)slot * Hkv + g) * max_ctx * hd;
+  float lmax = -INFINITY;
+  for (int t = threadIdx.x; t < n; t += 256) {
+    float s = 0.f;
+    for (int c = 0; c < hd; ++c) s = fmaf(sq[c], kb[(size_t)t * hd + c], s);
+    s *= scale;
+    sc[t] = s;
+    lmax = fmaxf(lmax, s);
+  }
+  lmax = wave_max(lmax);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = lmax;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float lsum = 0.f;
+  for (int t = threadIdx.x; t < n; t += 256) {
+    const float p = __expf(sc[t] - M);
+    sc[t] = p;
+    lsum += p;
+  }
+  const float den = block_sum<256>(lsum, red);  // also orders the score writes before the value pass
+  const int groups = 256 / hd;
+  const int c = threadIdx.x % hd, grp = threadIdx.x / hd;
+  float acc = 0.f;
+  if (grp < groups)
+    for (int t = grp; t < n; t += groups) acc = fmaf(sc[t], vb[(size_t)t * hd + c], acc);
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x < hd) {
+    float tot = 0.f;
+    for (int q = 0; q < groups; ++q) tot += red[q * hd + threadIdx.x];
+    out[threadIdx.x] = tot / den;
+  }
+}
+
+hipError_t launch_attention_f32(const float* Q, const float* Kc, const float* Vc, const int* seq_len,
+                                const int* req_slot, int B, int K, int Hq, int Hkv, int hd, int max_ctx, int n_slots,
+                                float* O, hipStream_t st) {
+  const size_t shmem = (size_t)(max_ctx + hd + 256) * sizeof(float);
+  hipLaunchKernelGGL(attn_f32_kernel, dim3(B * Hq * K), dim3(256), shmem, st, Q, Kc, Vc, seq_len, req_slot, K, Hq,
+                     Hkv, hd, max_ctx, n_slots, O, 1.0f / sqrtf((float)hd));
+  return hipGetLastError();
+}
+
+}  // namespace pe

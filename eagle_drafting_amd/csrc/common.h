@@ -1,0 +1,76 @@
+// Device helpers shared by the gfx950 kernels of the P-EAGLE draft / verify path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+#define PE_WAVE 64
+
+// device flag bits (mirrors pe_device_flags)
+#define PE_FLAG_TOKEN 1
+#define PE_FLAG_SLOT 2
+#define PE_FLAG_POS 4
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// round to nearest even; NaN stays NaN
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
+
+__device__ __forceinline__ void raise_flag(int* flags, int bit) {
+  __hip_atomic_fetch_or(flags, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// (value, index) pair ordering of the argmax: larger value wins, equal values go to the lower index
+__device__ __forceinline__ bool am_better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+__device__ __forceinline__ void am_wave_reduce(float& v, int& i, int width) {
+  for (int off = width / 2; off > 0; off >>= 1) {
+    float ov = __shfl_xor(v, off, PE_WAVE);
+    int oi = __shfl_xor(i, off, PE_WAVE);
+    if (am_better(ov, oi, v, i)) { v = ov; i = oi; }
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, PE_WAVE);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, PE_WAVE));
+  return v;
+}
+
+// sum over a block of NT threads (NT multiple of 64, <= 1024); every thread gets the total.
+// Fixed reduction order, so results are bit-reproducible.
+template <int NT>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / PE_WAVE, l = threadIdx.x % PE_WAVE;
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int k = 0; k < NT / PE_WAVE; ++k) t += red[k];
+  __syncthreads();
+  return t;
+}

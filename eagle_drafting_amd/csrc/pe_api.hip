@@ -1,0 +1,487 @@
+// C ABI of the P-EAGLE draft / verify path (declared in include/pe.h): argument checks, workspace,
+// weight repacking, and the launch sequence of one parallel draft step and one greedy verify.
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "pe.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace pe;
+
+struct pe_ctx {
+  pe_config cfg{};
+  pe_weights w{};
+  pe_kv kv{};
+  hipStream_t stream = nullptr;
+  int device = 0;
+  bool bf16 = true;
+
+  // bf16 path: projections repacked into MFMA fragments (library-owned)
+  char* packed = nullptr;
+  const void* p_fc = nullptr;
+  const void* p_qkv[PE_MAX_LAYERS] = {};
+  const void* p_o[PE_MAX_LAYERS] = {};
+  const void* p_gu[PE_MAX_LAYERS] = {};  // gate and up, 16-column tiles interleaved
+  const void* p_down[PE_MAX_LAYERS] = {};
+  const void* p_lm = nullptr;
+
+  // workspace
+  char* ws = nullptr;
+  float* X = nullptr;      // residual stream [Mmax, d] fp32
+  void* U = nullptr;       // normalised activations [Mmax, d]
+  void* Qb = nullptr;      // rotated queries [Mmax, Hq hd]
+  void* Ob = nullptr;      // attention output [Mmax, Hq hd]
+  void* Ab = nullptr;      // SwiGLU output [Mmax, F]
+  float* P = nullptr;      // split-K partials
+  float* attn = nullptr;   // attention split partials
+  float* am_val = nullptr; // argmax partials
+  int* am_idx = nullptr;
+  int* t_ws = nullptr;     // target argmax [max_batch, max_k + 1]
+  float* logits_ws = nullptr;  // fp32 path: logits when the caller passes none
+  float2* rope = nullptr;  // [max_ctx, hd/2] (cos, sin)
+  int* flags = nullptr;
+
+  std::string err;
+
+  bool prof = false;
+  std::vector<hipEvent_t> ev_a[PE_PROF_COUNT], ev_b[PE_PROF_COUNT];
+  size_t ev_used[PE_PROF_COUNT] = {};
+};
+
+static std::string g_init_err;
+
+static pe_status fail(pe_ctx* c, pe_status s, const std::string& msg) {
+  if (c) c->err = msg; else g_init_err = msg;
+  return s;
+}
+
+#define HIP_TRY(ctx, call)                                                                   \
+  do {                                                                                       \
+    hipError_t e_ = (call);                                                                  \
+    if (e_ != hipSuccess)                                                                    \
+      return fail(ctx, PE_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_));       \
+  } while (0)
+
+static pe_status check_cfg(const pe_config* c, std::string& why) {
+  if (!c) { why = "cfg is NULL"; return PE_ERR_INVALID; }
+  if (c->n_layers < 1 || c->n_layers > PE_MAX_LAYERS) { why = "n_layers out of [1, 8]"; return PE_ERR_INVALID; }
+  if (c->d_model <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 || c->ffn_dim <= 0 ||
+      c->vocab <= 0) { why = "non-positive dimension"; return PE_ERR_INVALID; }
+  if (c->n_q_heads % c->n_kv_heads) { why = "n_q_heads must be a multiple of n_kv_heads"; return PE_ERR_INVALID; }
+  if (c->head_dim % 2) { why = "head_dim must be even"; return PE_ERR_INVALID; }
+  if (c->dtype != PE_F32 && c->dtype != PE_BF16) { why = "dtype must be PE_F32 or PE_BF16"; return PE_ERR_INVALID; }
+  if (!(c->rms_eps >= 0.f) || !(c->rope_base > 1.f)) { why = "rms_eps < 0 or rope_base <= 1"; return PE_ERR_INVALID; }
+  if (c->max_batch < 1 || c->max_batch > PE_MAX_BATCH) { why = "max_batch out of [1, 1024]"; return PE_ERR_INVALID; }
+  if (c->max_k < 1 || c->max_k > PE_MAX_K) { why = "max_k out of [1, 16]"; return PE_ERR_INVALID; }
+  if (c->max_ctx < c->max_k || c->n_slots < 1) { why = "max_ctx < max_k or n_slots < 1"; return PE_ERR_INVALID; }
+  if (c->head_dim != 64 && c->head_dim != 128) { why = "head_dim must be 64 or 128"; return PE_ERR_UNSUPPORTED; }
+  if (c->d_model % 32 || c->ffn_dim % 32) { why = "d_model and ffn_dim must be multiples of 32"; return PE_ERR_UNSUPPORTED; }
+  if (c->vocab % 8) { why = "vocab must be a multiple of 8"; return PE_ERR_UNSUPPORTED; }
+  if (c->dtype == PE_BF16 && (c->n_q_heads / c->n_kv_heads) * c->max_k > 128) {
+    why = "(n_q_heads / n_kv_heads) * max_k must be <= 128"; return PE_ERR_UNSUPPORTED;
+  }
+  if (c->dtype == PE_F32 && c->max_ctx > 12288) { why = "fp32 drafter supports max_ctx <= 12288"; return PE_ERR_UNSUPPORTED; }
+  if ((long long)c->n_slots * c->n_kv_heads * c->max_ctx * c->head_dim > (1LL << 40)) {
+    why = "KV cache too large"; return PE_ERR_UNSUPPORTED;
+  }
+  return PE_OK;
+}
+
+extern "C" pe_status pe_config_validate(const pe_config* cfg) {
+  std::string why;
+  pe_status s = check_cfg(cfg, why);
+  if (s != PE_OK) g_init_err = why;
+  return s;
+}
+
+extern "C" const char* pe_status_string(pe_status s) {
+  switch (s) {
+    case PE_OK: return "ok";
+    case PE_ERR_INVALID: return "invalid argument";
+    case PE_ERR_UNSUPPORTED: return "unsupported";
+    case PE_ERR_OOM: return "out of device memory";
+    case PE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+extern "C" const char* pe_last_error(const pe_ctx* ctx) { return ctx ? ctx->err.c_str() : g_init_err.c_str(); }
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static size_t packed_bytes(int N, int Kd) { return (size_t)n_tiles(N) * k_steps(Kd) * 1024; }
+
+static void free_ctx(pe_ctx* c) {
+  if (!c) return;
+  for (int k = 0; k < PE_PROF_COUNT; ++k) {
+    for (auto e : c->ev_a[k]) (void)hipEventDestroy(e);
+    for (auto e : c->ev_b[k]) (void)hipEventDestroy(e);
+  }
+  if (c->packed) (void)hipFree(c->packed);
+  if (c->ws) (void)hipFree(c->ws);
+  delete c;
+}
+
+extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe_kv* kv, void* stream,
+                             pe_ctx** out) {
+  std::string why;
+  if (!out) return fail(nullptr, PE_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  pe_status s = check_cfg(cfg, why);
+  if (s != PE_OK) return fail(nullptr, s, why);
+  if (!w || !kv) return fail(nullptr, PE_ERR_INVALID, "weights or kv is NULL");
+  const pe_config& c = *cfg;
+  if (!w->fc || !w->embed || !w->emb_mask || !w->h_shared || !w->final_norm || !w->lm_head)
+    return fail(nullptr, PE_ERR_INVALID, "a global weight pointer is NULL");
+  for (int l = 0; l < c.n_layers; ++l)
+    if (!w->attn_norm[l] || !w->wqkv[l] || !w->wo[l] || !w->mlp_norm[l] || !w->wgate[l] || !w->wup[l] ||
+        !w->wdown[l] || !kv->k[l] || !kv->v[l])
+      return fail(nullptr, PE_ERR_INVALID, "a per-layer weight or cache pointer is NULL");
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(nullptr, PE_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess)
+    return fail(nullptr, PE_ERR_HIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(nullptr, PE_ERR_UNSUPPORTED, std::string("device is ") + prop.gcnArchName + ", not gfx950");
+
+  pe_ctx* ctx = new pe_ctx();
+  ctx->cfg = c;
+  ctx->w = *w;
+  ctx->kv = *kv;
+  ctx->stream = (hipStream_t)stream;
+  ctx->device = dev;
+  ctx->bf16 = c.dtype == PE_BF16;
+  const int d = c.d_model, F = c.ffn_dim, V = c.vocab, hd = c.head_dim;
+  const int qd = c.n_q_heads * hd, qkvd = (c.n_q_heads + 2 * c.n_kv_heads) * hd;
+  const int Mmax = c.max_batch * c.max_k;
+  const size_t es = ctx->bf16 ? 2 : 4;
+
+  // ---- packed weights (bf16 path)
+  if (ctx->bf16) {
+    size_t off = 0;
+    std::vector<size_t> offs;
+    auto take = [&](size_t b) { size_t o = off; off = align256(off + b); return o; };
+    const size_t o_fc = take(packed_bytes(d, 3 * d));
+    size_t o_qkv[PE_MAX_LAYERS], o_o[PE_MAX_LAYERS], o_gu[PE_MAX_LAYERS], o_dn[PE_MAX_LAYERS];
+    for (int l = 0; l < c.n_layers; ++l) {
+      o_qkv[l] = take(packed_bytes(qkvd, d));
+      o_o[l] = take(packed_bytes(d, qd));
+      o_gu[l] = take(2 * packed_bytes(F, d));
+      o_dn[l] = take(packed_bytes(d, F));
+    }
+    const size_t o_lm = take(packed_bytes(V, d));
+    if (hipMalloc((void**)&ctx->packed, off) != hipSuccess) {
+      free_ctx(ctx);
+      return fail(nullptr, PE_ERR_OOM, "hipMalloc of packed weights failed");
+    }
+    char* base = ctx->packed;
+    hipStream_t st = ctx->stream;
+    auto chk = [&](hipError_t r) { return r == hipSuccess; };
+    bool ok = chk(launch_pack_bf16(w->fc, d, 3 * d, base + o_fc, 1, 0, st));
+    ctx->p_fc = base + o_fc;
+    for (int l = 0; l < c.n_layers && ok; ++l) {
+      ok = ok && chk(launch_pack_bf16(w->wqkv[l], qkvd, d, base + o_qkv[l], 1, 0, st));
+      ok = ok && chk(launch_pack_bf16(w->wo[l], d, qd, base + o_o[l], 1, 0, st));
+      ok = ok && chk(launch_pack_bf16(w->wgate[l], F, d, base + o_gu[l], 2, 0, st));
+      ok = ok && chk(launch_pack_bf16(w->wup[l], F, d, base + o_gu[l], 2, 1, st));
+      ok = ok && chk(launch_pack_bf16(w->wdown[l], d, F, base + o_dn[l], 1, 0, st));
+      ctx->p_qkv[l] = base + o_qkv[l];
+      ctx->p_o[l] = base + o_o[l];
+      ctx->p_gu[l] = base + o_gu[l];
+      ctx->p_down[l] = base + o_dn[l];
+    }
+    ok = ok && chk(launch_pack_bf16(w->lm_head, V, d, base + o_lm, 1, 0, st));
+    ctx->p_lm = base + o_lm;
+    if (!ok) {
+      free_ctx(ctx);
+      return fail(nullptr, PE_ERR_HIP, "weight packing launch failed");
+    }
+  }
+
+  // ---- workspace sizes (maxima over every B <= max_batch, K <= max_k)
+  size_t p_floats = 0, attn_floats = 0, am_floats = 0;
+  for (int M = 1; M <= Mmax; ++M) {
+    if (ctx->bf16) {
+      const int Ns[4] = {qkvd, d, 2 * F, d}, Ks[4] = {d, qd, d, F};
+      for (int i = 0; i < 4; ++i) {
+        GemmPlan p = plan_gemm(M, Ns[i], Ks[i], false);
+        p_floats = std::max(p_floats, (size_t)p.S * M * Ns[i]);
+      }
+      GemmPlan pl = plan_gemm(M, V, d, true);
+      am_floats = std::max(am_floats, (size_t)M * pl.ngroups);
+    } else {
+      p_floats = std::max(p_floats, (size_t)M * std::max(std::max(qkvd, 2 * F), d));
+      am_floats = std::max(am_floats, (size_t)M * plan_argmax_chunks(M, V));
+    }
+  }
+  for (int B = 1; B <= c.max_batch; ++B) {
+    if (ctx->bf16) {
+      GemmPlan p = plan_gemm(B, d, 3 * d, false);
+      p_floats = std::max(p_floats, (size_t)p.S * B * d);
+      for (int K = 1; K <= c.max_k; ++K) {
+        AttnPlan ap = plan_attention(B, K, c.n_q_heads, c.n_kv_heads, c.max_ctx);
+        attn_floats = std::max(attn_floats, attn_partial_floats(B * K, c.n_q_heads, hd, ap));
+      }
+    } else {
+      p_floats = std::max(p_floats, (size_t)B * d);
+    }
+    for (int K = 1; K <= c.max_k; ++K) {
+      const int rows = B * (K + 1);
+      am_floats = std::max(am_floats, (size_t)rows * plan_argmax_chunks(rows, V));
+    }
+  }
+  size_t off = 0;
+  auto take = [&](size_t b) { size_t o = off; off = align256(off + b); return o; };
+  const size_t oX = take((size_t)Mmax * d * 4), oU = take((size_t)Mmax * d * es), oQ = take((size_t)Mmax * qd * es),
+               oO = take((size_t)Mmax * qd * es), oA = take((size_t)Mmax * F * es), oP = take(p_floats * 4),
+               oAt = take(std::max(attn_floats, (size_t)1) * 4), oAv = take(am_floats * 4), oAi = take(am_floats * 4),
+               oT = take((size_t)c.max_batch * (c.max_k + 1) * 4),
+               oL = take(ctx->bf16 ? 0 : (size_t)Mmax * V * 4), oR = take((size_t)c.max_ctx * (hd / 2) * 8),
+               oF = take(256);
+  if (hipMalloc((void**)&ctx->ws, off) != hipSuccess) {
+    free_ctx(ctx);
+    return fail(nullptr, PE_ERR_OOM, "hipMalloc of workspace failed");
+  }
+  char* b = ctx->ws;
+  ctx->X = (float*)(b + oX);
+  ctx->U = b + oU;
+  ctx->Qb = b + oQ;
+  ctx->Ob = b + oO;
+  ctx->Ab = b + oA;
+  ctx->P = (float*)(b + oP);
+  ctx->attn = (float*)(b + oAt);
+  ctx->am_val = (float*)(b + oAv);
+  ctx->am_idx = (int*)(b + oAi);
+  ctx->t_ws = (int*)(b + oT);
+  ctx->logits_ws = ctx->bf16 ? nullptr : (float*)(b + oL);
+  ctx->rope = (float2*)(b + oR);
+  ctx->flags = (int*)(b + oF);
+
+  hipError_t r = launch_rope_table(ctx->rope, c.max_ctx, hd, (double)c.rope_base, ctx->stream);
+  if (r == hipSuccess) r = hipMemsetAsync(ctx->flags, 0, 256, ctx->stream);
+  if (r == hipSuccess) r = hipStreamSynchronize(ctx->stream);
+  if (r != hipSuccess) {
+    std::string msg = std::string("pe_init: ") + hipGetErrorString(r);
+    free_ctx(ctx);
+    return fail(nullptr, PE_ERR_HIP, msg);
+  }
+  *out = ctx;
+  return PE_OK;
+}
+
+extern "C" pe_status pe_destroy(pe_ctx* ctx) {
+  if (!ctx) return PE_OK;
+  hipError_t e = hipStreamSynchronize(ctx->stream);
+  free_ctx(ctx);
+  if (e != hipSuccess) return fail(nullptr, PE_ERR_HIP, std::string("pe_destroy: ") + hipGetErrorString(e));
+  return PE_OK;
+}
+
+// ---- per-launch event timing of selected kernels
+static hipError_t prof_mark(pe_ctx* c, int which, bool begin) {
+  if (!c->prof) return hipSuccess;
+  auto& pool = begin ? c->ev_a[which] : c->ev_b[which];
+  size_t i = c->ev_used[which];
+  if (i >= 65536) return hipSuccess;  // stop recording beyond the cap
+  while (pool.size() <= i) {
+    hipEvent_t e;
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) return r;
+    pool.push_back(e);
+  }
+  hipError_t r = hipEventRecord(pool[i], c->stream);
+  if (!begin) c->ev_used[which] = i + 1;
+  return r;
+}
+
+extern "C" pe_status pe_profile_enable(pe_ctx* ctx, int32_t on) {
+  if (!ctx) return fail(nullptr, PE_ERR_INVALID, "ctx is NULL");
+  HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
+  ctx->prof = on != 0;
+  for (int k = 0; k < PE_PROF_COUNT; ++k) ctx->ev_used[k] = 0;
+  return PE_OK;
+}
+
+extern "C" pe_status pe_profile_read(pe_ctx* ctx, int32_t which, double* total_ms, int64_t* launches) {
+  if (!ctx || !total_ms || !launches) return fail(ctx, PE_ERR_INVALID, "NULL argument");
+  if (which < 0 || which >= PE_PROF_COUNT) return fail(ctx, PE_ERR_INVALID, "unknown kernel id");
+  HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
+  double tot = 0.0;
+  for (size_t i = 0; i < ctx->ev_used[which]; ++i) {
+    float ms = 0.f;
+    HIP_TRY(ctx, hipEventElapsedTime(&ms, ctx->ev_a[which][i], ctx->ev_b[which][i]));
+    tot += ms;
+  }
+  *total_ms = tot;
+  *launches = (int64_t)ctx->ev_used[which];
+  return PE_OK;
+}
+
+extern "C" pe_status pe_device_flags(pe_ctx* ctx, int32_t clear, int32_t* flags) {
+  if (!ctx || !flags) return fail(ctx, PE_ERR_INVALID, "NULL argument");
+  HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
+  HIP_TRY(ctx, hipMemcpy(flags, ctx->flags, sizeof(int32_t), hipMemcpyDeviceToHost));
+  if (clear) {
+    HIP_TRY(ctx, hipMemsetAsync(ctx->flags, 0, sizeof(int32_t), ctx->stream));
+    HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
+  }
+  return PE_OK;
+}
+
+#define LAUNCH(call) HIP_TRY(ctx, (call))
+
+static pe_status run_draft(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_slot, const int32_t* seq_len,
+                           const int32_t* last_token, const void* target_hidden, const float* rows,
+                           int32_t* draft_tokens, float* logits) {
+  if (!ctx) return fail(nullptr, PE_ERR_INVALID, "ctx is NULL");
+  const pe_config& c = ctx->cfg;
+  if (B < 1 || B > c.max_batch) return fail(ctx, PE_ERR_INVALID, "B out of [1, max_batch]");
+  if (K < 1 || K > c.max_k) return fail(ctx, PE_ERR_INVALID, "K out of [1, max_k]");
+  if (!req_slot || !seq_len || !draft_tokens) return fail(ctx, PE_ERR_INVALID, "NULL request array");
+  if (!rows && (!last_token || !target_hidden)) return fail(ctx, PE_ERR_INVALID, "NULL last_token / target_hidden");
+  if (target_hidden && ((uintptr_t)target_hidden & 15)) return fail(ctx, PE_ERR_INVALID, "target_hidden not 16-byte aligned");
+
+  hipStream_t st = ctx->stream;
+  const int dt = ctx->bf16 ? 1 : 0;
+  const int d = c.d_model, F = c.ffn_dim, V = c.vocab, hd = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+  const int qd = Hq * hd, qkvd = (Hq + 2 * Hkv) * hd;
+  const int M = B * K;
+  const float eps = c.rms_eps;
+  const pe_weights& w = ctx->w;
+
+  // a1: input rows (+ RMSNorm of layer 0)
+  int S = 1;
+  if (!rows) {
+    if (ctx->bf16) {
+      GemmPlan p = plan_gemm(B, d, 3 * d, false);
+      LAUNCH(launch_gemm_bf16_partial(p, target_hidden, 3 * d, B, 3 * d, ctx->p_fc, d, ctx->P, st));
+      S = p.S;
+    } else {
+      LAUNCH(launch_gemm_f32((const float*)target_hidden, 3 * d, B, 3 * d, (const float*)w.fc, d, ctx->P, d, st));
+    }
+  }
+  LAUNCH(launch_rowbuild_norm(dt, ctx->X, ctx->U, ctx->P, S, rows, B, K, d, last_token, w.embed, w.emb_mask,
+                              w.h_shared, w.attn_norm[0], eps, V, ctx->flags, st));
+  for (int l = 0; l < c.n_layers; ++l) {
+    // a3-a4: QKV projection, RoPE, KV append
+    if (ctx->bf16) {
+      GemmPlan p = plan_gemm(M, qkvd, d, false);
+      LAUNCH(launch_gemm_bf16_partial(p, ctx->U, d, M, d, ctx->p_qkv[l], qkvd, ctx->P, st));
+      S = p.S;
+    } else {
+      LAUNCH(launch_gemm_f32((const float*)ctx->U, d, M, d, (const float*)w.wqkv[l], qkvd, ctx->P, qkvd, st));
+      S = 1;
+    }
+    LAUNCH(launch_rope_kv(dt, ctx->Qb, ctx->kv.k[l], ctx->kv.v[l], ctx->P, S, B, K, Hq, Hkv, hd, seq_len, req_slot,
+                          c.max_ctx, c.n_slots, ctx->rope, ctx->flags, st));
+    // a5: attention
+    LAUNCH(prof_mark(ctx, PE_PROF_ATTENTION, true));
+    if (ctx->bf16) {
+      AttnPlan ap = plan_attention(B, K, Hq, Hkv, c.max_ctx);
+      LAUNCH(launch_attention_bf16(ap, ctx->Qb, ctx->kv.k[l], ctx->kv.v[l], seq_len, req_slot, B, K, Hq, Hkv, hd,
+                                   c.max_ctx, c.n_slots, ctx->attn, st));
+      LAUNCH(prof_mark(ctx, PE_PROF_ATTENTION, false));
+      LAUNCH(launch_attention_combine_bf16(ap, ctx->attn, ctx->Ob, seq_len, req_slot, B, K, Hq, Hkv, hd, c.max_ctx,
+                                           c.n_slots, st));
+    } else {
+      LAUNCH(launch_attention_f32((const float*)ctx->Qb, (const float*)ctx->kv.k[l], (const float*)ctx->kv.v[l],
+                                  seq_len, req_slot, B, K, Hq, Hkv, hd, c.max_ctx, c.n_slots, (float*)ctx->Ob, st));
+      LAUNCH(prof_mark(ctx, PE_PROF_ATTENTION, false));
+    }
+    // a6: output projection + residual, RMSNorm
+    if (ctx->bf16) {
+      GemmPlan p = plan_gemm(M, d, qd, false);
+      LAUNCH(launch_gemm_bf16_partial(p, ctx->Ob, qd, M, qd, ctx->p_o[l], d, ctx->P, st));
+      S = p.S;
+    } else {
+      LAUNCH(launch_gemm_f32((const float*)ctx->Ob, qd, M, qd, (const float*)w.wo[l], d, ctx->P, d, st));
+      S = 1;
+    }
+    LAUNCH(launch_residual_norm(dt, ctx->X, ctx->U, ctx->P, S, M, d, w.mlp_norm[l], eps, st));
+    // a7: gate/up + SwiGLU
+    LAUNCH(prof_mark(ctx, PE_PROF_GATE_UP, true));
+    if (ctx->bf16) {
+      GemmPlan p = plan_gemm(M, 2 * F, d, false);
+      LAUNCH(launch_gemm_bf16_partial(p, ctx->U, d, M, d, ctx->p_gu[l], 2 * F, ctx->P, st));
+      S = p.S;
+    } else {
+      LAUNCH(launch_gemm_f32((const float*)ctx->U, d, M, d, (const float*)w.wgate[l], F, ctx->P, 2 * F, st));
+      LAUNCH(launch_gemm_f32((const float*)ctx->U, d, M, d, (const float*)w.wup[l], F, ctx->P + F, 2 * F, st));
+      S = 1;
+    }
+    LAUNCH(prof_mark(ctx, PE_PROF_GATE_UP, false));
+    LAUNCH(launch_swiglu(dt, ctx->Ab, ctx->P, S, M, F, ctx->bf16, st));
+    // a8: down projection + residual, RMSNorm for the next layer (or the final norm)
+    if (ctx->bf16) {
+      GemmPlan p = plan_gemm(M, d, F, false);
+      LAUNCH(launch_gemm_bf16_partial(p, ctx->Ab, F, M, F, ctx->p_down[l], d, ctx->P, st));
+      S = p.S;
+    } else {
+      LAUNCH(launch_gemm_f32((const float*)ctx->Ab, F, M, F, (const float*)w.wdown[l], d, ctx->P, d, st));
+      S = 1;
+    }
+    const void* g_next = l + 1 < c.n_layers ? w.attn_norm[l + 1] : w.final_norm;
+    LAUNCH(launch_residual_norm(dt, ctx->X, ctx->U, ctx->P, S, M, d, g_next, eps, st));
+  }
+  // a9-a10: LM head + argmax
+  LAUNCH(prof_mark(ctx, PE_PROF_LM_HEAD, true));
+  if (ctx->bf16) {
+    GemmPlan p = plan_gemm(M, V, d, true);
+    LAUNCH(launch_gemm_bf16_argmax(p, ctx->U, d, M, d, ctx->p_lm, V, ctx->am_val, ctx->am_idx, logits, st));
+    LAUNCH(prof_mark(ctx, PE_PROF_LM_HEAD, false));
+    LAUNCH(launch_argmax_final(ctx->am_val, ctx->am_idx, M, p.ngroups, draft_tokens, st));
+  } else {
+    float* z = logits ? logits : ctx->logits_ws;
+    LAUNCH(launch_gemm_f32((const float*)ctx->U, d, M, d, (const float*)w.lm_head, V, z, V, st));
+    LAUNCH(prof_mark(ctx, PE_PROF_LM_HEAD, false));
+    const int nch = plan_argmax_chunks(M, V);
+    LAUNCH(launch_argmax_rows(0, z, M, V, nch, ctx->am_val, ctx->am_idx, st));
+    LAUNCH(launch_argmax_final(ctx->am_val, ctx->am_idx, M, nch, draft_tokens, st));
+  }
+  return PE_OK;
+}
+
+extern "C" pe_status pe_draft_step(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_slot, const int32_t* seq_len,
+                                   const int32_t* last_token, const void* target_hidden, int32_t* draft_tokens,
+                                   float* logits) {
+  if (ctx && (!last_token || !target_hidden)) return fail(ctx, PE_ERR_INVALID, "NULL last_token / target_hidden");
+  return run_draft(ctx, B, K, req_slot, seq_len, last_token, target_hidden, nullptr, draft_tokens, logits);
+}
+
+extern "C" pe_status pe_draft_rows(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_slot, const int32_t* seq_len,
+                                   const float* rows, int32_t* draft_tokens, float* logits) {
+  if (ctx && !rows) return fail(ctx, PE_ERR_INVALID, "rows is NULL");
+  return run_draft(ctx, B, K, req_slot, seq_len, nullptr, nullptr, rows, draft_tokens, logits);
+}
+
+extern "C" pe_status pe_verify(pe_ctx* ctx, int32_t B, int32_t K, const void* target_logits,
+                               const int32_t* draft_tokens, const uint8_t* finished, const int32_t* req_slot,
+                               const int32_t* seq_len, int32_t* accept_len, int32_t* cu_accept, int32_t* out_tokens,
+                               int32_t* keep_index, int32_t* n_keep, int32_t* req_slot_next, int32_t* seq_len_next,
+                               int32_t* last_token_next) {
+  if (!ctx) return fail(nullptr, PE_ERR_INVALID, "ctx is NULL");
+  const pe_config& c = ctx->cfg;
+  if (B < 1 || B > c.max_batch) return fail(ctx, PE_ERR_INVALID, "B out of [1, max_batch]");
+  if (K < 1 || K > c.max_k) return fail(ctx, PE_ERR_INVALID, "K out of [1, max_k]");
+  if (!target_logits || !draft_tokens || !req_slot || !seq_len || !accept_len || !cu_accept || !out_tokens ||
+      !keep_index || !n_keep || !req_slot_next || !seq_len_next || !last_token_next)
+    return fail(ctx, PE_ERR_INVALID, "NULL argument");
+  if ((uintptr_t)target_logits & 15) return fail(ctx, PE_ERR_INVALID, "target_logits not 16-byte aligned");
+  hipStream_t st = ctx->stream;
+  const int rows = B * (K + 1);
+  const int nch = plan_argmax_chunks(rows, c.vocab);
+  LAUNCH(prof_mark(ctx, PE_PROF_VERIFY_SCAN, true));
+  LAUNCH(launch_argmax_rows(ctx->bf16 ? 1 : 0, target_logits, rows, c.vocab, nch, ctx->am_val, ctx->am_idx, st));
+  LAUNCH(prof_mark(ctx, PE_PROF_VERIFY_SCAN, false));
+  LAUNCH(launch_accept_compact(ctx->am_val, ctx->am_idx, nch, B, K, draft_tokens, finished, req_slot, seq_len,
+                               ctx->t_ws, accept_len, cu_accept, out_tokens, keep_index, n_keep, req_slot_next,
+                               seq_len_next, last_token_next, st));
+  return PE_OK;
+}

@@ -1,0 +1,173 @@
+/*
+ * pe.h — C ABI of the P-EAGLE parallel-drafting hot path on one AMD Instinct MI355X (gfx950).
+ *
+ * The method (source: "Parallelize speculative decoding with P-EAGLE on Amazon SageMaker AI", solution
+ * overview: "how P-EAGLE breaks the chain" and "step-by-step drafting process"): for every request the
+ * drafter builds K input rows in one go — row 0 from the token the target just produced and the hidden
+ * states captured at three target layers, rows 1..K-1 from two learned placeholders (the shared hidden
+ * state h_shared and the mask-token embedding emb_mask) — runs all K rows through its transformer layers
+ * and LM head in a single forward pass, and emits K draft tokens at once. The target then checks the K
+ * candidates in one verification pass with the standard acceptance rule (greedy form here).
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" point to GPU memory of the device that was current at pe_init; "host"
+ *     pointers to CPU memory. The caller owns every buffer it passes; the library never frees them.
+ *   - Matrices are row-major. A weight matrix W of a projection y = x . W^T is stored [out, in].
+ *   - Element type: pe_config.dtype (PE_F32 or PE_BF16) for weights, KV cache, target hiddens and target
+ *     logits. Token ids, lengths and slots are int32. Logits written by the library are float32.
+ *   - Calls enqueue work on the stream given to pe_init and return without waiting for the GPU.
+ *     pe_draft_step, pe_draft_rows and pe_verify allocate nothing.
+ *   - A ctx is used by one host thread at a time. Calls on one ctx run in stream order.
+ *   - Errors: every call returns a pe_status. Host-checkable problems (null pointers, sizes out of
+ *     range, unsupported shapes) return PE_ERR_INVALID / PE_ERR_UNSUPPORTED before anything is enqueued.
+ *     HIP failures return PE_ERR_HIP; pe_last_error gives the message. Device-value preconditions
+ *     (token ids < vocab, slots < n_slots, seq_len + K <= max_ctx) are the caller's contract; kernels
+ *     skip any access that would break them and raise a flag readable through pe_device_flags.
+ */
+#ifndef PE_H
+#define PE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PE_MAX_LAYERS 8
+#define PE_MAX_BATCH 1024
+#define PE_MAX_K 16
+
+typedef enum {
+  PE_OK = 0,
+  PE_ERR_INVALID = 1,     /* bad argument (null pointer, size out of range) */
+  PE_ERR_UNSUPPORTED = 2, /* valid but not supported here (shape, dtype, device) */
+  PE_ERR_OOM = 3,         /* workspace allocation failed in pe_init */
+  PE_ERR_HIP = 4          /* a HIP runtime call failed; see pe_last_error */
+} pe_status;
+
+typedef enum { PE_F32 = 0, PE_BF16 = 1 } pe_dtype;
+
+/* Drafter shape and capacity. */
+typedef struct pe_config {
+  int32_t n_layers;   /* transformer layers of the drafter, 1..PE_MAX_LAYERS (4 in practice) */
+  int32_t d_model;    /* width d; multiple of 32 */
+  int32_t n_q_heads;  /* Hq */
+  int32_t n_kv_heads; /* Hkv; Hq % Hkv == 0 (grouped-query attention, q head h reads kv head h / (Hq/Hkv)) */
+  int32_t head_dim;   /* hd; 64 or 128 */
+  int32_t ffn_dim;    /* F of the SwiGLU MLP; multiple of 32 */
+  int32_t vocab;      /* V */
+  float rms_eps;      /* RMSNorm epsilon */
+  float rope_base;    /* RoPE base (rotate-half pairs (i, i+hd/2), inv_freq_i = base^(-2i/hd)) */
+  int32_t dtype;      /* pe_dtype */
+  int32_t max_batch;  /* largest B passed to any call, 1..PE_MAX_BATCH */
+  int32_t max_k;      /* largest K passed to any call, 1..PE_MAX_K */
+  int32_t max_ctx;    /* positions per KV slot */
+  int32_t n_slots;    /* KV slots */
+} pe_config;
+
+/* Drafter weights (device, element type = dtype). Must stay valid and unchanged until pe_destroy:
+ * pe_init copies the projection matrices into its own tiled layout, but reads embed, emb_mask,
+ * h_shared and the norm gains in place on every step. */
+typedef struct pe_weights {
+  const void* fc;          /* [d, 3d]: projection of the three captured target hidden states */
+  const void* embed;       /* [V, d]: token embedding */
+  const void* emb_mask;    /* [d]: learned mask-token embedding (rows 1..K-1) */
+  const void* h_shared;    /* [d]: learned shared hidden state (rows 1..K-1) */
+  const void* final_norm;  /* [d]: RMSNorm gain before the LM head */
+  const void* lm_head;     /* [V, d] */
+  const void* attn_norm[PE_MAX_LAYERS]; /* [d] */
+  const void* wqkv[PE_MAX_LAYERS];      /* [(Hq + 2 Hkv) hd, d]: q heads, then k heads, then v heads */
+  const void* wo[PE_MAX_LAYERS];        /* [d, Hq hd] */
+  const void* mlp_norm[PE_MAX_LAYERS];  /* [d] */
+  const void* wgate[PE_MAX_LAYERS];     /* [F, d] */
+  const void* wup[PE_MAX_LAYERS];       /* [F, d] */
+  const void* wdown[PE_MAX_LAYERS];     /* [d, F] */
+} pe_weights;
+
+/* Drafter KV cache (device, element type = dtype), one K and one V tensor per layer, each
+ * [n_slots][Hkv][max_ctx][hd]. Keys are stored already rotated by RoPE. Owned by the caller. */
+typedef struct pe_kv {
+  void* k[PE_MAX_LAYERS];
+  void* v[PE_MAX_LAYERS];
+} pe_kv;
+
+typedef struct pe_ctx pe_ctx;
+
+/* Host-only check of a configuration; touches no GPU. */
+pe_status pe_config_validate(const pe_config* cfg);
+
+/* Create a context on the current HIP device (which must be gfx950): validates cfg, allocates the
+ * workspace for max_batch x max_k rows, copies the projection matrices into the library's tiled layout
+ * and builds the RoPE table. stream: a hipStream_t (NULL = default stream). Synchronizes before return. */
+pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe_kv* kv, void* stream, pe_ctx** out);
+
+/* The parallel draft step (solution overview, step 2). For request b (0 <= b < B):
+ *   row 0     = fc . concat(target_hidden[b]) + embed[last_token[b]]
+ *   rows 1..K-1 = h_shared + emb_mask
+ * at positions seq_len[b] + j. All B*K rows go through the drafter layers (RMSNorm, GQA attention over
+ * the request's cache slot with a causal mask inside the K block, SwiGLU MLP) and the LM head;
+ * draft_tokens[b*K + j] = argmax over the vocabulary (lowest index among equal maxima).
+ * The K and V rows of this step are written to cache slot req_slot[b] at positions seq_len[b]..+K-1;
+ * seq_len itself is not changed.
+ *   req_slot, seq_len, last_token: device int32 [B]
+ *   target_hidden: device [B, 3d] (dtype); the three captured hidden states as consecutive d-blocks
+ *   draft_tokens:  device int32 [B, K] (written)
+ *   logits:        device float32 [B, K, V] or NULL; written when not NULL. */
+pe_status pe_draft_step(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_slot, const int32_t* seq_len,
+                        const int32_t* last_token, const void* target_hidden, int32_t* draft_tokens,
+                        float* logits);
+
+/* Same drafter pass over caller-built input rows (device float32 [B, K, d]) instead of the row
+ * builder: lets a caller feed arbitrary rows, e.g. to check that row j never depends on rows after j. */
+pe_status pe_draft_rows(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_slot, const int32_t* seq_len,
+                        const float* rows, int32_t* draft_tokens, float* logits);
+
+/* Greedy verification and batch-metadata rebuild (solution overview, step 2, last sentence; batch
+ * metadata as in the pages' fused metadata kernels). With t[b][i] = argmax_v target_logits[b][i][v]
+ * (lowest index on ties) for i = 0..K:
+ *   n_b = first i < K with draft_tokens[b][i] != t[b][i], or K;   accept_len[b] = n_b + 1
+ *   cu_accept[0] = 0, cu_accept[b+1] = cu_accept[b] + accept_len[b]
+ *   out_tokens[cu_accept[b] + i] = t[b][i] for i <= n_b   (accepted drafts, then the bonus token)
+ *   requests with finished[b] == 0 survive, in order: keep_index[0..n_keep-1] lists them and
+ *   req_slot_next[i] = req_slot[keep_index[i]], seq_len_next[i] = seq_len[keep_index[i]] +
+ *   accept_len[keep_index[i]], last_token_next[i] = t[keep_index[i]][n_{keep_index[i]}] (the bonus).
+ *   target_logits: device [B, K+1, V] (dtype)      draft_tokens: device int32 [B, K]
+ *   finished: device uint8 [B] or NULL (none finished)
+ *   req_slot, seq_len: device int32 [B]
+ *   outputs (device int32): accept_len [B], cu_accept [B+1], out_tokens [B*(K+1)] (first cu_accept[B]
+ *   valid), keep_index [B], n_keep [1], req_slot_next / seq_len_next / last_token_next [B] (first
+ *   n_keep valid). Output buffers must not alias inputs. */
+pe_status pe_verify(pe_ctx* ctx, int32_t B, int32_t K, const void* target_logits, const int32_t* draft_tokens,
+                    const uint8_t* finished, const int32_t* req_slot, const int32_t* seq_len,
+                    int32_t* accept_len, int32_t* cu_accept, int32_t* out_tokens, int32_t* keep_index,
+                    int32_t* n_keep, int32_t* req_slot_next, int32_t* seq_len_next, int32_t* last_token_next);
+
+/* Waits for the ctx's stream, then frees everything pe_init allocated. NULL is allowed. */
+pe_status pe_destroy(pe_ctx* ctx);
+
+/* Device flags raised by kernels that skipped an access breaking a device-value precondition
+ * (bit 0: token id out of range, bit 1: slot out of range, bit 2: position beyond max_ctx).
+ * Synchronizes the stream; clear != 0 resets the flags. */
+pe_status pe_device_flags(pe_ctx* ctx, int32_t clear, int32_t* flags);
+
+/* Per-launch timing of selected kernels with HIP events recorded on the ctx's stream.
+ * pe_profile_enable(ctx, 1) starts recording (resets the totals); pe_profile_read synchronizes and
+ * returns the summed duration in milliseconds and the number of launches of one kernel. */
+typedef enum {
+  PE_PROF_LM_HEAD = 0,     /* LM-head GEMM with fused argmax partials */
+  PE_PROF_ATTENTION = 1,   /* attention main kernel (every layer) */
+  PE_PROF_GATE_UP = 2,     /* MLP gate/up GEMM (every layer) */
+  PE_PROF_VERIFY_SCAN = 3, /* verify's vocabulary argmax scan */
+  PE_PROF_COUNT = 4
+} pe_prof_kernel;
+pe_status pe_profile_enable(pe_ctx* ctx, int32_t on);
+pe_status pe_profile_read(pe_ctx* ctx, int32_t which, double* total_ms, int64_t* launches);
+
+const char* pe_status_string(pe_status s);
+/* Message of the last failed call on ctx (or of the last failed pe_init when ctx is NULL). */
+const char* pe_last_error(const pe_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PE_H */

@@ -1,7 +1,7 @@
 """Seeded generators for drafter weights, request state, KV caches and target logits.
 
-Every tensor has its own child generator (numpy PCG64 seeded with [workload seed, tensor code, ...]),
-so any tensor or any request's KV block can be regenerated alone, in any order.
+Every tensor has its own child generators (numpy PCG64 seeded with [seed, tensor code, ..., chunk]), so
+any tensor or any request's KV block can be regenerated alone, in any order and with any thread count.
 
 bf16 tensors are produced by round-to-nearest-even of float32 draws and returned as raw uint16 bits;
 `bf16_bits_to_f32` gives the exact float32 values those bits encode.
@@ -9,11 +9,13 @@ bf16 tensors are produced by round-to-nearest-even of float32 draws and returned
 
 from __future__ import annotations
 
+import os
+
 import numpy as np
 
 from .workloads import DrafterShape, Workload
 
-_CHUNK = 1 << 24
+_CHUNK = 1 << 22
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -21,10 +23,18 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float32)
     flat = x.reshape(-1)
     out = np.empty(flat.shape, dtype=np.uint16)
-    for s in range(0, flat.size, _CHUNK):
+
+    def conv(s):
         u = flat[s:s + _CHUNK].view(np.uint32)
         r = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)
         out[s:s + _CHUNK] = r.astype(np.uint16)
+
+    starts = range(0, flat.size, _CHUNK)
+    if flat.size > _CHUNK:
+        list(_pool().map(conv, starts))
+    else:
+        for s in starts:
+            conv(s)
     return out.reshape(x.shape)
 
 
@@ -40,16 +50,38 @@ def _rng(*key) -> np.random.Generator:
     return np.random.default_rng([int(k) for k in key])
 
 
-def _normal(rng: np.random.Generator, shape, scale=1.0, loc=0.0) -> np.ndarray:
+_POOL = None
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        from concurrent.futures import ThreadPoolExecutor
+        _POOL = ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1))
+    return _POOL
+
+
+def _normal(key: tuple, shape, scale=1.0, loc=0.0) -> np.ndarray:
+    """N(loc, scale^2) float32 draws; chunk c of 2^22 values comes from child generator [*key, c], so
+    the values do not depend on how many threads fill them."""
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.float32)
-    for s in range(0, n, _CHUNK):
-        e = min(n, s + _CHUNK)
-        out[s:e] = rng.standard_normal(e - s, dtype=np.float32)
-    if scale != 1.0:
-        out *= np.float32(scale)
-    if loc != 0.0:
-        out += np.float32(loc)
+
+    def fill(c):
+        s0, s1 = c * _CHUNK, min(n, (c + 1) * _CHUNK)
+        part = out[s0:s1]
+        _rng(*key, c).standard_normal(s1 - s0, dtype=np.float32, out=part)
+        if scale != 1.0:
+            part *= np.float32(scale)
+        if loc != 0.0:
+            part += np.float32(loc)
+
+    nchunks = (n + _CHUNK - 1) // _CHUNK
+    if nchunks <= 1:
+        for c in range(nchunks):
+            fill(c)
+    else:
+        list(_pool().map(fill, range(nchunks)))
     return out.reshape(shape)
 
 
@@ -84,7 +116,7 @@ def weight_shapes(s: DrafterShape) -> dict:
     return shapes
 
 
-def make_weight(s: DrafterShape, seed: int, name: str) -> np.ndarray:
+def make_weight(s: DrafterShape, name: str, seed: int = None) -> np.ndarray:
     """One drafter tensor. Matrices are [out, in] (y = x . W^T), drawn N(0, 0.02); norm gains are
     1 + N(0, 0.02). Returned as float32 (f32 shapes) or bf16 bits (bf16 shapes)."""
     shape = weight_shapes(s)[name]
@@ -93,16 +125,16 @@ def make_weight(s: DrafterShape, seed: int, name: str) -> np.ndarray:
         layer = int(layer[1:])
     else:
         layer, base = 0, name
-    rng = _rng(seed, _CODES[base], layer)
+    key = (s.weight_seed if seed is None else seed, _CODES[base], layer)
     if base.endswith("norm"):
-        x = _normal(rng, shape, 0.02, 1.0)
+        x = _normal(key, shape, 0.02, 1.0)
     else:
-        x = _normal(rng, shape, 0.02)
+        x = _normal(key, shape, 0.02)
     return _encode(x, s.dtype)
 
 
-def make_weights(s: DrafterShape, seed: int) -> dict:
-    return {name: make_weight(s, seed, name) for name in weight_shapes(s)}
+def make_weights(s: DrafterShape, seed: int = None) -> dict:
+    return {name: make_weight(s, name, seed) for name in weight_shapes(s)}
 
 
 def make_state(w: Workload, step: int = 0) -> dict:
@@ -121,7 +153,7 @@ def make_state(w: Workload, step: int = 0) -> dict:
     seq_len = rng.integers(lo, hi + 1, size=w.B).astype(np.int32)
     req_slot = rng.permutation(w.n_slots)[: w.B].astype(np.int32)
     last_token = rng.integers(0, s.vocab, size=w.B).astype(np.int32)
-    hid = _normal(rng, (w.B, 3 * s.d_model))
+    hid = _normal((w.seed, 101, step), (w.B, 3 * s.d_model))
     if isinstance(w.alpha, tuple):
         alpha = rng.uniform(w.alpha[0], w.alpha[1], size=w.B)
     else:
@@ -134,8 +166,7 @@ def kv_block(w: Workload, layer: int, kind: int, request_key: int, L: int) -> np
     """Context keys (kind 0) or values (kind 1) of one request: [Hkv, L, hd] N(0, 1), encoded.
     Cached keys count as already rotated by RoPE."""
     s = w.shape
-    rng = _rng(w.seed, 200 + kind, layer, request_key)
-    return _encode(_normal(rng, (s.n_kv_heads, L, s.head_dim)), s.dtype)
+    return _encode(_normal((w.seed, 200 + kind, layer, request_key), (s.n_kv_heads, L, s.head_dim)), s.dtype)
 
 
 def make_kv_cache(w: Workload, layer: int, kind: int, state: dict, request_keys=None) -> np.ndarray:
@@ -144,11 +175,21 @@ def make_kv_cache(w: Workload, layer: int, kind: int, state: dict, request_keys=
     s = w.shape
     dt = np.float32 if s.dtype == "f32" else np.uint16
     cache = np.zeros((w.n_slots, s.n_kv_heads, w.max_ctx, s.head_dim), dtype=dt)
-    keys = range(w.B) if request_keys is None else request_keys
-    for b, key in zip(range(w.B), keys):
+    keys = list(range(w.B) if request_keys is None else request_keys)
+
+    def fill(b):
         L = int(state["seq_len"][b])
-        cache[state["req_slot"][b], :, :L, :] = kv_block(w, layer, kind, key, L)
+        cache[state["req_slot"][b], :, :L, :] = kv_block(w, layer, kind, keys[b], L)
+
+    global _KV_POOL
+    if _KV_POOL is None:
+        from concurrent.futures import ThreadPoolExecutor
+        _KV_POOL = ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1))
+    list(_KV_POOL.map(fill, range(w.B)))
     return cache
+
+
+_KV_POOL = None
 
 
 def random_draft(w: Workload, step: int = 0) -> np.ndarray:
@@ -168,7 +209,7 @@ def plant_target_logits(w: Workload, draft: np.ndarray, alpha: np.ndarray, step:
     V = s.vocab
     rng = _rng(w.seed, 400, step)
     B, K = draft.shape
-    T = _normal(rng, (B, K + 1, V))
+    T = _normal((w.seed, 401, step), (B, K + 1, V))
     if s.dtype == "bf16":
         T = round_bf16(T)
     hit = rng.random((B, K)) < alpha[:, None]
@@ -202,5 +243,5 @@ def new_request(w: Workload, step: int, index: int) -> dict:
     rng = _rng(w.seed, 600, step, index)
     L = int(rng.integers(w.new_ctx[0], w.new_ctx[1] + 1))
     tok = int(rng.integers(0, s.vocab))
-    hid = _encode(_normal(rng, (3 * s.d_model,)), s.dtype)
+    hid = _encode(_normal((w.seed, 601, step, index), (3 * s.d_model,)), s.dtype)
     return {"seq_len": L, "last_token": tok, "target_hidden": hid, "request_key": 10_000 * (step + 1) + index}

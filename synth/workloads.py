@@ -24,6 +24,7 @@ class DrafterShape:
     ffn_dim: int
     vocab: int
     dtype: str  # "f32" or "bf16": weights, KV cache, target hiddens and target logits
+    weight_seed: int = 0  # seed of this synthetic drafter's weights (shared by every workload on it)
     rms_eps: float = 1e-6
     rope_base: float = 10000.0
 
@@ -48,9 +49,9 @@ class DrafterShape:
         return 4 if self.dtype == "f32" else 2
 
 
-TINY_FP32 = DrafterShape("tiny-fp32", 1, 256, 4, 4, 64, 512, 4096, "f32")
-QWEN3_CODER = DrafterShape("qwen3-coder-30b-a3b-shaped", 4, 2048, 32, 4, 128, 6144, 151936, "bf16")
-GPT_OSS_20B = DrafterShape("gpt-oss-20b-shaped", 4, 2880, 64, 8, 64, 8640, 201088, "bf16")
+TINY_FP32 = DrafterShape("tiny-fp32", 1, 256, 4, 4, 64, 512, 4096, "f32", 1000)
+QWEN3_CODER = DrafterShape("qwen3-coder-30b-a3b-shaped", 4, 2048, 32, 4, 128, 6144, 151936, "bf16", 2000)
+GPT_OSS_20B = DrafterShape("gpt-oss-20b-shaped", 4, 2880, 64, 8, 64, 8640, 201088, "bf16", 5000)
 
 
 @dataclass(frozen=True)

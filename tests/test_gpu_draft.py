@@ -1,0 +1,134 @@
+"""GPU parity of the parallel draft step (pe_draft_step / pe_draft_rows) against the oracle, plus the
+method's invariants on the GPU.
+
+Per request: logits within the row-relative tolerance (1e-4 fp32, 2e-2 bf16), draft tokens identical up
+to the top-2-gap exemption, and this step's K/V rows appended to the cache within the same tolerance.
+Workloads whose full oracle run would take minutes are checked on sampled requests (requests are
+independent, so a sampled request's oracle result is exact for it).
+"""
+
+import numpy as np
+import pytest
+
+from synth import WORKLOADS, Workload, TINY_FP32, QWEN3_CODER, make_state
+from tests.gpu_util import (TOL, GpuDrafter, check_logits, check_rows, check_tokens, log, oracle_draft,
+                            shape_weights64)
+
+pytestmark = pytest.mark.gpu
+
+
+def _parity(g, requests, K=None, rows=None, rows_host=None, check_kv=True):
+    w = g.w
+    K = K or w.K
+    tol = TOL[w.shape.dtype]
+    draft, z = g.draft(K=K, rows=rows)
+    W64 = shape_weights64(w.shape)
+    req = list(requests)
+    ref = oracle_draft(w, W64, g.state, K, req, rows=rows_host)
+    err = check_logits(z.cpu().numpy()[req], ref["logits"], tol, w.name)
+    strict, exempt = check_tokens(draft.cpu().numpy()[req], ref["logits"], tol, w.name)
+    kv_err = 0.0
+    if check_kv:
+        for l in range(w.shape.n_layers):
+            for i, b in enumerate(req):
+                k, v = g.kv_rows(l, b, K)
+                kv_err = max(kv_err, check_rows(k, ref["k_new"][l][i], tol, f"{w.name} K rows l{l} b{b}"),
+                             check_rows(v, ref["v_new"][l][i], tol, f"{w.name} V rows l{l} b{b}"))
+    log(f"  {w.name}: requests {req[:6]}{'...' if len(req) > 6 else ''} logit err {err:.2e}, kv err {kv_err:.2e}, "
+        f"tokens strict {strict}/{len(req) * K}, exempt {exempt}")
+    return draft, z, ref
+
+
+def _sample(w, state, n=3):
+    rng = np.random.default_rng(w.seed + 7)
+    pick = {0, w.B - 1, int(np.argmax(state["seq_len"]))}
+    pick |= set(int(x) for x in rng.choice(w.B, size=min(n, w.B), replace=False))
+    return sorted(pick)
+
+
+FULL = ["tiny-fp32-B1-K4-L64", "qwen3coder-bf16-B1-K3-L2048"] + \
+       [n for n, w in WORKLOADS.items() if "sweep" in w.tags]
+SAMPLED = [n for n, w in WORKLOADS.items() if "churn" in w.tags or "large" in w.tags]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_draft_parity_full(name):
+    w = WORKLOADS[name]
+    log(f"draft parity {name}")
+    g = GpuDrafter(w)
+    try:
+        _parity(g, range(w.B))
+    finally:
+        g.close()
+
+
+@pytest.mark.parametrize("name", SAMPLED)
+def test_draft_parity_sampled(name):
+    w = WORKLOADS[name]
+    log(f"draft parity (sampled requests) {name}")
+    g = GpuDrafter(w)
+    try:
+        _parity(g, _sample(w, g.state))
+    finally:
+        g.close()
+
+
+@pytest.mark.parametrize("shape", [TINY_FP32, QWEN3_CODER], ids=lambda s: s.name)
+def test_empty_and_short_contexts(shape):
+    # L_b = 0 (the request has no drafter context yet: row j sees only new rows 0..j) and tiny L_b
+    w = Workload(f"{shape.name}-short-ctx", shape, 4, 3, (0, 3), 0.7, 7100)
+    state = make_state(w)
+    state["seq_len"][:] = [0, 1, 0, 3]
+    g = GpuDrafter(w, state=state)
+    try:
+        _parity(g, range(w.B))
+    finally:
+        g.close()
+
+
+def _random_rows(w, seed):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((w.B, w.K, w.shape.d_model)).astype(np.float32)
+
+
+@pytest.mark.parametrize("shape", [TINY_FP32, QWEN3_CODER], ids=lambda s: s.name)
+def test_draft_rows_parity_and_causality(shape):
+    """Invariant 3: under the causal mask, row j's output does not change when rows after j change.
+    The rows are arbitrary (harness-drawn), fed through pe_draft_rows; bit-identical on the GPU."""
+    import torch
+    w = Workload(f"{shape.name}-rows", shape, 2, 5, (40, 90), 0.7, 7200)
+    g = GpuDrafter(w)
+    try:
+        X = _random_rows(w, 1)
+        Xd = torch.from_numpy(X).cuda()
+        draft0, z0 = _parity(g, range(w.B), rows=Xd, rows_host=X.astype(np.float64), check_kv=False)
+        z0 = z0.cpu().numpy()
+        for j in range(w.K - 1):
+            Xp = X.copy()
+            Xp[:, j + 1:] += np.random.default_rng(10 + j).standard_normal(Xp[:, j + 1:].shape).astype(np.float32)
+            _, zp = g.draft(rows=torch.from_numpy(Xp).cuda())
+            zp = zp.cpu().numpy()
+            assert np.array_equal(zp[:, : j + 1], z0[:, : j + 1]), f"row <= {j} changed"
+            assert not np.array_equal(zp[:, j + 1:], z0[:, j + 1:])
+        log("  causality holds bit-exactly")
+    finally:
+        g.close()
+
+
+@pytest.mark.parametrize("shape", [TINY_FP32, QWEN3_CODER], ids=lambda s: s.name)
+def test_k1_equals_row0_and_determinism(shape):
+    """Invariant 2 on the GPU: K = 1 (plain EAGLE step, no placeholders) matches row 0 of the K-row
+    step within tolerance; repeated runs are bit-identical."""
+    w = Workload(f"{shape.name}-k1", shape, 3, 6, (100, 300), 0.7, 7300)
+    g = GpuDrafter(w)
+    tol = TOL[shape.dtype]
+    try:
+        d6, z6 = g.draft(K=6)
+        d6b, z6b = g.draft(K=6)
+        assert np.array_equal(z6.cpu().numpy(), z6b.cpu().numpy()) and np.array_equal(d6.cpu().numpy(),
+                                                                                    d6b.cpu().numpy())
+        _, _, ref = _parity(g, range(w.B), K=1)
+        check_logits(z6.cpu().numpy()[:, 0], ref["logits"][:, 0], tol, "row 0 of K=6 vs oracle K=1")
+        check_tokens(d6.cpu().numpy()[:, 0], ref["logits"][:, 0], tol, "row 0 token")
+    finally:
+        g.close()

@@ -24,7 +24,7 @@ MINI = DrafterShape("mini-f32", 2, 32, 4, 2, 8, 48, 64, "f32")
 
 
 def _weights64(shape, seed):
-    raw = make_weights(shape, seed)
+    raw = make_weights(shape, seed=seed)
     return {k: to_f64(v, shape.dtype) for k, v in raw.items()}
 
 
