@@ -1,0 +1,264 @@
+"""Benchmark of the P-EAGLE parallel draft step + greedy verify on one MI355X.
+
+One step = pe_draft_step (row build, 4 drafter layers, LM head, argmax: K draft tokens for each of B
+requests in one pass) + pe_verify (target argmax over K+1 positions, accepted prefix, bonus token,
+batch-metadata rebuild), over inputs already resident in HBM. Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload NAME] [--no-cpu-baseline]
+
+The default workload is the Qwen3-Coder-30B-A3B-shaped bf16 drafter at B = 1, K = 3, context 2048.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HEADLINE = "qwen3coder-bf16-B1-K3-L2048"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+METRIC = "draft tokens/s and draft+verify steps/s at B×K; % of HBM/MFMA roofline"
+
+
+def algorithmic_bytes(w, state):
+    """Bytes the step must move at minimum: every weight once, the gathered embedding rows, the target
+    hiddens, each request's KV context (plus this step's rows) read once, this step's KV rows written once,
+    and the target logits read once by verify. Activations, partials and logits dumps are not counted."""
+    s = w.shape
+    e = s.elem_bytes
+    d, V, F = s.d_model, s.vocab, s.ffn_dim
+    per_layer = s.qkv_dim * d + d * s.q_dim + 3 * d * F + 2 * d
+    weights = (3 * d * d + s.n_layers * per_layer + d * V + d + 2 * d) * e
+    L = state["seq_len"].astype(np.int64)
+    kv_row = 2 * s.n_kv_heads * s.head_dim * e
+    kv_read = s.n_layers * int((L + w.K).sum()) * kv_row
+    kv_write = s.n_layers * w.B * w.K * kv_row
+    inputs = w.B * d * e + w.B * 3 * d * e
+    draft = weights + kv_read + kv_write + inputs
+    verify = w.B * (w.K + 1) * V * e
+    lm_head = d * V * e
+    return {"draft": draft, "verify": verify, "step": draft + verify, "lm_head": lm_head,
+            "weights": weights, "kv_read": kv_read}
+
+
+def lm_head_flops(w):
+    return 2.0 * w.B * w.K * w.shape.d_model * w.shape.vocab
+
+
+def traffic_from_profile(workload_name):
+    """HBM bytes per LM-head launch measured by rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, scaled by
+    the plain-copy calibration), if the committed measurement was taken with the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "lm_head_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(os.path.join(ROOT, "eagle_drafting_amd", "csrc", "gemm.hip"), "rb").read()
+    if rec.get("workload") != workload_name or rec.get("gemm_src_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, state, target_logits_host, target_seconds):
+    """The oracle, as it stands, on this host: repeated draft + verify + compact steps of the same
+    workload until about target_seconds of work."""
+    from oracle import pe_oracle as O
+    from synth.inputs import kv_block, make_weights, to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the visible CPUs
+        threads = os.cpu_count() or 1
+    s = w.shape
+    W = {k: to_f64(v, s.dtype) for k, v in make_weights(s).items()}
+    ctx_cache = {}
+
+    def ctx(l, b):
+        if (l, b) not in ctx_cache:
+            L = int(state["seq_len"][b])
+            ctx_cache[(l, b)] = (to_f64(kv_block(w, l, 0, b, L), s.dtype), to_f64(kv_block(w, l, 1, b, L), s.dtype))
+        return ctx_cache[(l, b)]
+
+    for l in range(s.n_layers):
+        for b in range(w.B):
+            ctx(l, b)
+    st = {"last_token": state["last_token"], "target_hidden": to_f64(state["target_hidden"], s.dtype),
+          "seq_len": state["seq_len"]}
+    T = to_f64(target_logits_host, s.dtype)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        out = O.draft_step(s, W, st, ctx, w.K)
+        v = O.verify(T, out["draft"])
+        O.compact(v, state["req_slot"], state["seq_len"])
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= target_seconds or n >= 200:
+            break
+    return {"value": w.B * w.K * n / el, "unit": "draft tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} full draft+verify steps of {w.name} (float64 NumPy oracle), {el:.1f} s",
+            "steps_per_s": n / el}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference kernel for HBM counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py: this path runs on one GPU (each request's draft and verify are independent; "
+              f"scale-out is data-parallel over requests and is not built). --gpus {args.gpus} is not supported.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import eagle_drafting_amd as pe
+    from synth import WORKLOADS, churn_finished, make_state, plant_target_logits
+    from synth.device import config_args, to_device, upload_kv, upload_state, upload_weights
+
+    w = WORKLOADS[args.workload]
+    s = w.shape
+    torch.cuda.set_device(0)
+    dev, _ = upload_weights(s)
+    state = make_state(w)
+    kc, vc = upload_kv(w, state)
+    d = upload_state(state, s.dtype)
+    stream = torch.cuda.current_stream()
+    ctx = pe.pe_init(pe.make_config(**config_args(w)), pe.make_weights(dev, s.n_layers), pe.make_kv(kc, vc),
+                     stream.cuda_stream)
+    B, K, V = w.B, w.K, s.vocab
+    i32 = dict(dtype=torch.int32, device="cuda")
+    draft = torch.empty((B, K), **i32)
+    outs = [torch.empty(n, **i32) for n in (B, B + 1, B * (K + 1), B, 1, B, B, B)]
+
+    # target logits planted on this drafter's own draft tokens (the draft is deterministic, so every
+    # timed step sees the same acceptance pattern)
+    pe.pe_draft_step(ctx, B, K, d["req_slot"], d["seq_len"], d["last_token"], d["target_hidden"], draft, None)
+    torch.cuda.synchronize()
+    draft_host = draft.cpu().numpy()
+    T_host = plant_target_logits(w, draft_host, state["alpha"])
+    T = to_device(T_host, s.dtype)
+    fin = to_device(churn_finished(w, 0), "u8") if w.churn else None
+
+    def draft_call():
+        pe.pe_draft_step(ctx, B, K, d["req_slot"], d["seq_len"], d["last_token"], d["target_hidden"], draft, None)
+
+    def verify_call():
+        pe.pe_verify(ctx, B, K, T, draft, fin, d["req_slot"], d["seq_len"], *outs)
+
+    for _ in range(args.warmup):
+        draft_call()
+        verify_call()
+    pe.pe_profile_enable(ctx, 1 << pe.PE_PROF_LM_HEAD)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        draft_call()
+        verify_call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = ev0.elapsed_time(ev1)
+    lm_ms, lm_n = pe.pe_profile_read(ctx, pe.PE_PROF_LM_HEAD)
+    ms_step = ms / args.steps
+    accept = outs[0].cpu().numpy()
+
+    # breakdown (outside the timed region): draft alone, verify alone, per-kernel events
+    pe.pe_profile_enable(ctx, (1 << 4) - 1)
+    reps = max(10, args.steps // 2)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record(stream)
+    for _ in range(reps):
+        draft_call()
+    e[1].record(stream)
+    for _ in range(reps):
+        verify_call()
+    e[2].record(stream)
+    torch.cuda.synchronize()
+    t_draft = e[0].elapsed_time(e[1]) / reps
+    t_verify = e[1].elapsed_time(e[2]) / reps
+    kern = {}
+    for name, kid in (("lm_head", pe.PE_PROF_LM_HEAD), ("attention", pe.PE_PROF_ATTENTION),
+                      ("gate_up", pe.PE_PROF_GATE_UP), ("verify_scan", pe.PE_PROF_VERIFY_SCAN)):
+        tot, n = pe.pe_profile_read(ctx, kid)
+        kern[name] = {"avg_us": 1e3 * tot / max(n, 1), "launches": n}
+    pe.pe_profile_enable(ctx, 0)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    flags = pe.pe_device_flags(ctx)
+    pe.pe_destroy(ctx)
+
+    ab = algorithmic_bytes(w, state)
+    lm_us = 1e3 * lm_ms / max(lm_n, 1)
+    achieved = ab["lm_head"] / (lm_us * 1e-6) / 1e9
+    traffic = traffic_from_profile(w.name)
+    result = {
+        "metric": METRIC,
+        "value": B * K / (ms_step * 1e-3),
+        "unit": "draft tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": s.dtype,
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) hiddens/KV, planted target logits)",
+        "config": {"workload": w.name, "drafter_shape": s.name, "B": B, "K": K,
+                   "context": list(w.ctx), "layers": s.n_layers, "d": s.d_model, "vocab": V},
+        "steps_per_s": 1e3 / ms_step,
+        "request_steps_per_s": B * 1e3 / ms_step,
+        "wall_ms_per_step": 1e3 * wall / args.steps,
+        "t_draft_us": 1e3 * t_draft,
+        "t_verify_us": 1e3 * t_verify,
+        "step_hbm_frac": ab["step"] / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
+        "draft_hbm_frac": ab["draft"] / (t_draft * 1e-3) / (PEAK_HBM_GBS * 1e9),
+        "algorithmic_MB": {k: v / 1e6 for k, v in ab.items()},
+        "mean_accept_len": float(accept.mean()),
+        "alpha_hat": float((accept - 1).sum() / (accept.size * K)),
+        "kernels": kern,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "LM-head GEMM with fused argmax partials",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": traffic,
+            "bytes_per_launch": ab["lm_head"],
+            "avg_launch_us": lm_us,
+            "launches": lm_n,
+            "mfma_frac": lm_head_flops(w) / (lm_us * 1e-6) / (PEAK_BF16_TFLOPS * 1e12),
+        },
+        "device_flags": flags,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, state, T_host, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -152,8 +152,9 @@ def pe_device_flags(ctx, clear: bool = False) -> int:
     return out.value
 
 
-def pe_profile_enable(ctx, on: bool = True):
-    _check(load_library().pe_profile_enable(ctx, 1 if on else 0), ctx)
+def pe_profile_enable(ctx, mask: int = (1 << 4) - 1):
+    """Record per-launch events for the kernels whose bit (1 << PE_PROF_*) is set; 0 stops."""
+    _check(load_library().pe_profile_enable(ctx, int(mask)), ctx)
 
 
 def pe_profile_read(ctx, which: int):

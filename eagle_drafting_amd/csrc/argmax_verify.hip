@@ -70,25 +70,48 @@ hipError_t launch_argmax_rows(int dtype, const void* X, int rows, int V, int nch
   return hipGetLastError();
 }
 
-// one wave per row: reduce the row's partials in order
-__global__ __launch_bounds__(256) void argmax_final_kernel(const float* __restrict__ pv, const int* __restrict__ pi,
-                                                           int rows, int nchunks, int* __restrict__ out) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
+// best (value, index) over the nchunks partials of one row, by the calling wave (all lanes get it)
+__device__ __forceinline__ int am_row_reduce(const float* __restrict__ pv, const int* __restrict__ pi, int nchunks,
+                                             int lane) {
   float b = -INFINITY;
   int i = 0x7fffffff;
   for (int c = lane; c < nchunks; c += 64) {
+    const float v = pv[c];
+    const int k = pi[c];
+    if (am_better(v, k, b, i)) { b = v; i = k; }
+  }
+  am_wave_reduce(b, i, 64);
+  return i;
+}
+
+// one workgroup per row: each wave reduces a quarter of the partials, then the four are combined
+__global__ __launch_bounds__(256) void argmax_final_kernel(const float* __restrict__ pv, const int* __restrict__ pi,
+                                                           int rows, int nchunks, int* __restrict__ out) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int row = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int q = (nchunks + 3) / 4;
+  const int c0 = wave * q, c1 = min(nchunks, c0 + q);
+  float b = -INFINITY;
+  int i = 0x7fffffff;
+  for (int c = c0 + lane; c < c1; c += 64) {
     const float v = pv[(size_t)row * nchunks + c];
     const int k = pi[(size_t)row * nchunks + c];
     if (am_better(v, k, b, i)) { b = v; i = k; }
   }
   am_wave_reduce(b, i, 64);
-  if (lane == 0) out[row] = i;
+  if (lane == 0) { sv[wave] = b; si[wave] = i; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (am_better(sv[w], si[w], b, i)) { b = sv[w]; i = si[w]; }
+    out[row] = i;
+  }
 }
 
 hipError_t launch_argmax_final(const float* pv, const int* pi, int rows, int nchunks, int* out, hipStream_t st) {
-  hipLaunchKernelGGL(argmax_final_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, pv, pi, rows, nchunks, out);
+  hipLaunchKernelGGL(argmax_final_kernel, dim3(rows), dim3(256), 0, st, pv, pi, rows, nchunks, out);
   return hipGetLastError();
 }
 
@@ -119,16 +142,13 @@ __global__ __launch_bounds__(1024) void accept_compact_kernel(
   __shared__ int buf[1024];
   const int tid = threadIdx.x;
   const int rows = B * (K + 1);
-  // target argmax t[b][i] from the scan partials
-  for (int r = tid; r < rows; r += 1024) {
-    float b = -INFINITY;
-    int i = 0x7fffffff;
-    for (int c = 0; c < nchunks; ++c) {
-      const float v = pv[(size_t)r * nchunks + c];
-      const int k = pi[(size_t)r * nchunks + c];
-      if (am_better(v, k, b, i)) { b = v; i = k; }
+  // target argmax t[b][i] from the scan partials: one wave per row
+  {
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int r = wave; r < rows; r += 16) {
+      const int i = am_row_reduce(pv + (size_t)r * nchunks, pi + (size_t)r * nchunks, nchunks, lane);
+      if (lane == 0) t_ws[r] = i;
     }
-    t_ws[r] = i;
   }
   __syncthreads();
   int n = 0, al = 0, bonus = 0, keep = 0;

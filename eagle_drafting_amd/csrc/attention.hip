@@ -16,6 +16,8 @@
 
 namespace pe {
 
+#define ATTN_MAX_PARTIALS 1024  // (split, sub-stream) partials per query row
+
 static inline int attn_sub_streams(int R) {
   const int RT = (R + 15) / 16;
   return RT == 1 ? 4 : RT == 2 ? 2 : 1;
@@ -30,6 +32,7 @@ AttnPlan plan_attention(int B, int K, int Hq, int Hkv, int max_ctx) {
   int chunk = (int)((want + 127) / 128) * 128;
   if (chunk < 128) chunk = 128;
   if (chunk > 4096) chunk = 4096;
+  while ((long long)((max_ctx + K + chunk - 1) / chunk) * p.sub > ATTN_MAX_PARTIALS) chunk *= 2;
   p.chunk = chunk;
   p.nsplit = (max_ctx + K + chunk - 1) / chunk;
   return p;
@@ -223,16 +226,32 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restric
     for (int c = threadIdx.x; c < HD; c += 64) out[c] = 0;
     return;
   }
+  __shared__ float sw[ATTN_MAX_PARTIALS];
   const int ns = ((L + K + chunk - 1) / chunk) * sub;
   const float* src = part + (size_t)rid * nsplit * sub * (HD + 2);
+  // all (m_s, l_s) in parallel: one load per lane, then wave reductions
   float M = -1e30f;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, src[(size_t)s * (HD + 2) + HD]);
+  for (int s = threadIdx.x; s < ns; s += 64) {
+    const float m = src[(size_t)s * (HD + 2) + HD];
+    sw[s] = m;
+    M = fmaxf(M, m);
+  }
+  M = wave_max(M);
   float den = 0.f;
-  for (int s = 0; s < ns; ++s) den += __expf(src[(size_t)s * (HD + 2) + HD] - M) * src[(size_t)s * (HD + 2) + HD + 1];
+  for (int s = threadIdx.x; s < ns; s += 64) {
+    const float w = __expf(sw[s] - M);
+    sw[s] = w;
+    den += w * src[(size_t)s * (HD + 2) + HD + 1];
+  }
+  den = wave_sum(den);
+  __syncthreads();
   const float inv = 1.f / den;
-  for (int c = threadIdx.x; c < HD; c += 64) {
+#pragma unroll
+  for (int c0 = 0; c0 < HD; c0 += 64) {
+    const int c = c0 + threadIdx.x;
     float num = 0.f;
-    for (int s = 0; s < ns; ++s) num += __expf(src[(size_t)s * (HD + 2) + HD] - M) * src[(size_t)s * (HD + 2) + c];
+#pragma unroll 8
+    for (int s = 0; s < ns; ++s) num += sw[s] * src[(size_t)s * (HD + 2) + c];
     out[c] = f32_to_bf16(num * inv);
   }
 }

@@ -1,11 +1,18 @@
-// Projections of the drafter (fc, QKV, O, gate/up, down, LM head): y = A . W^T.
+// Projections of the drafter (fc, QKV, O, gate/up, down, LM head): y = A . W^T, with the neighbouring
+// row-wise steps fused into the projection so that a draft step is a short chain of kernels.
 //
-// bf16 path: the weight matrix is repacked once (pe_init) into 1 KiB MFMA fragments, so a wave's
-// B-operand load for one 16 x 32 tile is a single contiguous 1 KiB read (64 lanes x 16 B). The
-// activations (M = B*K rows, small) are staged through LDS in A-fragment order and shared by the four
-// waves of a workgroup; each wave owns one 16-column tile and accumulates MT 16x16 fp32 tiles with
-// v_mfma_f32_16x16x32_bf16. Split-K partials are written in fp32 and summed, in a fixed order, by the
-// consumer kernel, so results do not depend on scheduling.
+// Weights are repacked once (pe_init) into 1 KiB MFMA fragments: a wave's B-operand load for one
+// 16-column x 32-k tile is one contiguous 1 KiB read (64 lanes x 16 B). The repack may also permute the
+// output columns inside a 16-column tile so that values one epilogue combines sit in the same tile:
+// the two halves of every RoPE pair (QKV) and each gate/up pair (SwiGLU).
+//
+// A workgroup owns NT 16-column tiles and one block of MT*16 rows over the WHOLE reduction dimension;
+// its NW waves split the k range (NW/NT parts), each accumulating MT 16x16 fp32 tiles with
+// v_mfma_f32_16x16x32_bf16, and the parts are summed through LDS in a fixed order. No workgroup depends
+// on another, so results are deterministic and no device-wide synchronisation is needed.
+// The A operand is read straight from global memory (it is tiny: M = B*K rows): either a bf16 matrix or
+// RMSNorm(X) of the fp32 residual stream, normalised on the fly from per-16-column partial sums of
+// squares that the kernel which last updated X wrote.
 //
 // MFMA lane layout (16x16x32, wave64): A lane l holds A[l%16][k-group l/16] (8 values), B lane l holds
 // B[k-group l/16][l%16], D lane l holds D[4(l/16)+r][l%16], r = 0..3. A and B use the same k grouping,
@@ -15,9 +22,23 @@
 
 namespace pe {
 
-__global__ __launch_bounds__(256) void pack_bf16_kernel(const bf16_t* __restrict__ W, int N, int Kd,
-                                                        bf16x8_t* __restrict__ dst, int Nt, int Ks, int mul,
-                                                        int add) {
+// Source row of packed row r (0..15) of tile t.
+__device__ __forceinline__ int pack_src_row(int mode, int t, int r, int hd, int* which) {
+  *which = 0;
+  if (mode == PACK_PAIRS) {  // tile holds 8 RoPE pairs of one head: first halves, then second halves
+    const int tph = hd / 16, h = t / tph, tt = t % tph;
+    return h * hd + (r < 8 ? 8 * tt + r : hd / 2 + 8 * tt + (r - 8));
+  }
+  if (mode == PACK_GATEUP) {  // tile holds gate rows 8t..8t+7, then up rows 8t..8t+7
+    *which = r < 8 ? 0 : 1;
+    return 8 * t + (r & 7);
+  }
+  return 16 * t + r;
+}
+
+__global__ __launch_bounds__(256) void pack_bf16_kernel(const bf16_t* __restrict__ W0, const bf16_t* __restrict__ W1,
+                                                        int N, int Kd, bf16x8_t* __restrict__ dst, int Nt, int Ks,
+                                                        int mode, int hd) {
   const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
   const size_t total = (size_t)Nt * Ks * 64;
   if (gid >= total) return;
@@ -25,7 +46,9 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(const bf16_t* __restrict
   const size_t frag = gid >> 6;
   const int s = (int)(frag % Ks);
   const int t = (int)(frag / Ks);
-  const int row = 16 * t + (lane & 15);
+  int which;
+  const int row = pack_src_row(mode, t, lane & 15, hd, &which);
+  const bf16_t* W = which ? W1 : W0;
   const int col = 32 * s + 8 * (lane >> 4);
   bf16x8_t v;
 #pragma unroll
@@ -34,160 +57,343 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(const bf16_t* __restrict
     if (row < N && col + e < Kd) x = (short)W[(size_t)row * Kd + col + e];
     v[e] = x;
   }
-  dst[((size_t)(t * mul + add) * Ks + s) * 64 + lane] = v;
+  dst[frag * 64 + lane] = v;
 }
 
-hipError_t launch_pack_bf16(const void* W, int N, int Kd, void* dst, int tile_mul, int tile_add, hipStream_t st) {
-  const int Nt = n_tiles(N), Ks = k_steps(Kd);
+hipError_t launch_pack_bf16(const void* W0, const void* W1, int N, int Kd, int mode, int hd, void* dst,
+                            hipStream_t st) {
+  const int Nt = mode == PACK_GATEUP ? (2 * N + 15) / 16 : n_tiles(N);
+  const int Ks = k_steps(Kd);
   const size_t total = (size_t)Nt * Ks * 64;
-  const unsigned grid = (unsigned)((total + 255) / 256);
-  hipLaunchKernelGGL(pack_bf16_kernel, dim3(grid), dim3(256), 0, st, (const bf16_t*)W, N, Kd, (bf16x8_t*)dst, Nt,
-                     Ks, tile_mul, tile_add);
+  hipLaunchKernelGGL(pack_bf16_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, (const bf16_t*)W0,
+                     (const bf16_t*)W1, N, Kd, (bf16x8_t*)dst, Nt, Ks, mode, hd);
   return hipGetLastError();
 }
 
-GemmPlan plan_gemm(int M, int N, int Kd, bool argmax_epilogue) {
+GemmPlan plan_gemm(int M, int N, int Kd, bool argmax) {
   GemmPlan p;
-  const int Nt = n_tiles(N), Ks = k_steps(Kd);
+  const int Ks = k_steps(Kd);
+  p.Nt = n_tiles(N);
   p.MT = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
   p.mblocks = (M + 16 * p.MT - 1) / (16 * p.MT);
-  p.ngroups = (Nt + 3) / 4;
-  int S = 1;
-  if (!argmax_epilogue) {
-    const int base = p.ngroups * p.mblocks;
-    S = (1024 + base - 1) / base;
-    const int smax = Ks / 4 > 1 ? Ks / 4 : 1;  // at least 4 k-steps (128 k) per split
-    if (S > smax) S = smax;
-    if (S < 1) S = 1;
+  if (argmax) {
+    p.NT = 4;
+    p.NW = 4;
+  } else {
+    p.NT = 1;
+    // enough waves in flight (about 4096 in total) while each wave streams at least 8 k-steps;
+    // register budget caps NW by MT (LDS for the cross-wave sum is NW * MT KiB)
+    const int cap = p.MT == 1 ? 16 : p.MT == 2 ? 8 : 4;
+    const int groups = p.Nt * p.mblocks;
+    int nw = 4;
+    while (nw < cap && groups * nw < 4096 && Ks / (2 * nw) >= 8) nw *= 2;
+    p.NW = nw;
   }
-  p.kps = (Ks + S - 1) / S;
-  p.S = (Ks + p.kps - 1) / p.kps;
+  p.ngroups = (p.Nt + p.NT - 1) / p.NT;
   return p;
 }
 
-constexpr int GEMM_KC = 8;  // k-steps staged per chunk
+template <int MT>
+struct KChunk {
+  static constexpr int value = MT <= 2 ? 8 : (MT == 4 ? 4 : 2);
+};
 
-template <int MT, bool ARGMAX>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16_t* __restrict__ A, int lda, int M, int Kd,
-                                                        const bf16x8_t* __restrict__ Wp, int Nt, int Ks, int N,
-                                                        int kps, float* __restrict__ P,
-                                                        float* __restrict__ am_val, int* __restrict__ am_idx,
-                                                        int ngroups, float* __restrict__ logits) {
-  __shared__ bf16x8_t sA[MT * GEMM_KC * 64];
-  __shared__ float s_rv[ARGMAX ? 4 * MT * 16 : 1];
-  __shared__ int s_ri[ARGMAX ? 4 * MT * 16 : 1];
+// One A-operand fragment piece: rows of A (bf16), or x * g of the residual stream (bf16); the per-row
+// 1/RMS of a normalised operand is applied to the product rows in the epilogue instead, so the main
+// loop never waits for it (RMSNorm is a per-row scale, and y = (s * x * g) . W^T = s * ((x * g) . W^T)).
+template <int AM>
+__device__ __forceinline__ bf16x8_t load_a(const GemmArgs& g, int row, int col) {
+  if (AM == A_BF16) return *(const bf16x8_t*)(g.A + (size_t)row * g.lda + col);
+  const float4 x0 = *(const float4*)(g.X + (size_t)row * g.Kd + col);
+  const float4 x1 = *(const float4*)(g.X + (size_t)row * g.Kd + col + 4);
+  const bf16x8_t gg = *(const bf16x8_t*)(g.gain + col);
+  const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  bf16x8_t v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (short)f32_to_bf16(xs[e] * bf16_to_f32((bf16_t)gg[e]));
+  return v;
+}
 
+template <int MT, int NW, int NT, int AM, int EP>
+__global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
+  constexpr int KP = NW / NT;            // k parts
+  constexpr bool STAGE = KP == 1;        // every wave covers the same k range: share A through LDS
+  constexpr int KC = KChunk<MT>::value;  // k-steps loaded per round
+  __shared__ float s_red[NW * MT * 256];
+  __shared__ bf16x8_t sA[STAGE ? MT * KC * 64 : 1];
+  __shared__ float s_inv[MT * 16];
+
+  const int M = g.M, Kd = g.Kd, N = g.N, Ks = g.Ks;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nt = blockIdx.x * 4 + wave;
-  const bool active = nt < Nt;
+  const int tl = wave % NT, kp = wave / NT;
+  const int nt = blockIdx.x * NT + tl;
+  const bool active = nt < g.Nt;
   const int m0 = blockIdx.y * MT * 16;
-  const int split = blockIdx.z;
-  const int s_begin = split * kps;
+  const int kps = (Ks + KP - 1) / KP;
+  const int s_begin = kp * kps;
   const int s_end = min(Ks, s_begin + kps);
 
   f32x4_t acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const bf16x8_t* wsrc = Wp + (size_t)(active ? nt : 0) * Ks * 64 + lane;
+  const bf16x8_t* wsrc = (const bf16x8_t*)g.Wp_raw + (size_t)(active ? nt : 0) * Ks * 64 + lane;
   const bf16x8_t zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
 
-  for (int c0 = s_begin; c0 < s_end; c0 += GEMM_KC) {
-    const int nk = min(GEMM_KC, s_end - c0);
-    bf16x8_t b[GEMM_KC];
+  for (int c0 = s_begin; c0 < s_end; c0 += KC) {
+    const int nk = min(KC, s_end - c0);
+    bf16x8_t b[KC];
 #pragma unroll
-    for (int kk = 0; kk < GEMM_KC; ++kk) b[kk] = (active && kk < nk) ? wsrc[(size_t)(c0 + kk) * 64] : zero8;
-    for (int p = threadIdx.x; p < MT * GEMM_KC * 64; p += 256) {
-      const int ln = p & 63, kk = (p >> 6) % GEMM_KC, mt = (p >> 6) / GEMM_KC;
-      const int row = m0 + mt * 16 + (ln & 15);
-      const int col = (c0 + kk) * 32 + 8 * (ln >> 4);
-      bf16x8_t v = zero8;
-      if (kk < nk && row < M && col < Kd) v = *(const bf16x8_t*)(A + (size_t)row * lda + col);
-      sA[p] = v;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < GEMM_KC; ++kk) {
-      if (kk < nk) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sA[(mt * GEMM_KC + kk) * 64 + lane], b[kk], acc[mt], 0,
-                                                            0, 0);
+    for (int kk = 0; kk < KC; ++kk) b[kk] = (active && kk < nk) ? wsrc[(size_t)(c0 + kk) * 64] : zero8;
+    if (STAGE) {
+      for (int p = threadIdx.x; p < MT * KC * 64; p += NW * 64) {
+        const int ln = p & 63, kk = (p >> 6) % KC, mt = (p >> 6) / KC;
+        const int row = m0 + mt * 16 + (ln & 15);
+        const int col = (c0 + kk) * 32 + 8 * (ln >> 4);
+        sA[p] = (kk < nk && row < M && col < Kd) ? load_a<AM>(g, row, col) : zero8;
       }
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk) {
+        if (kk < nk) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sA[(mt * KC + kk) * 64 + lane], b[kk], acc[mt], 0, 0, 0);
+        }
+      }
+      __syncthreads();
+    } else {
+      bf16x8_t a[KC][MT];
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int row = m0 + mt * 16 + (lane & 15);
+          const int col = (c0 + kk) * 32 + 8 * (lane >> 4);
+          a[kk][mt] = (kk < nk && row < M && col < Kd) ? load_a<AM>(g, row, col) : zero8;
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk) {
+        if (kk < nk) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk][mt], b[kk], acc[mt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  if (AM == A_NORM) {
+    // 1 / RMS of each row of X from the per-16-column partial sums of squares: one wave per row, all
+    // partials loaded at once (fixed reduction order)
+    const int nrows = min(MT * 16, M - m0);
+    for (int r = wave; r < nrows; r += NW) {
+      const float* src = g.ssq_in + (size_t)(m0 + r) * g.nssq;
+      float t = 0.f;
+      for (int i = lane; i < g.nssq; i += 64) t += src[i];
+      t = wave_sum(t);
+      if (lane == 0) s_inv[r] = rsqrtf(t / (float)Kd + g.eps);
+    }
+  }
+
+  // cross-wave sum of the k parts (fixed order): s_red[((kp * NT + tl) * MT + mt) * 256 + row16 * 16 + col]
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      s_red[((kp * NT + tl) * MT + mt) * 256 + (4 * (lane >> 4) + r) * 16 + (lane & 15)] = acc[mt][r];
+  __syncthreads();
+  if (KP > 1) {
+    for (int idx = threadIdx.x; idx < NT * MT * 256; idx += NW * 64) {
+      float v = s_red[idx];
+#pragma unroll
+      for (int q = 1; q < KP; ++q) v += s_red[q * NT * MT * 256 + idx];
+      s_red[idx] = v;
     }
     __syncthreads();
   }
+  // reduced tile: y(tile t, local row r, column c), scaled by the row's 1/RMS for a normalised operand
+  auto Y = [&](int t, int r, int c) {
+    const float v = s_red[(t * MT + (r >> 4)) * 256 + (r & 15) * 16 + c];
+    return AM == A_NORM ? v * s_inv[r] : v;
+  };
+  const int rows = min(MT * 16, M - m0);
+  constexpr int NTH = NW * 64;
 
-  const int n = nt * 16 + (lane & 15);
-  if (!ARGMAX) {
-    if (active && n < N) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m0 + mt * 16 + 4 * (lane >> 4) + r;
-          if (m < M) P[((size_t)split * M + m) * N + n] = acc[mt][r];
-        }
+  if (EP == EPI_ARGMAX) {
+    // best (value, index) of each row over the workgroup's NT*16 columns; optional logits
+    for (int r = wave; r < rows; r += NW) {
+      const int m = m0 + r;
+      const int t = lane >> 4, c = lane & 15;
+      const int n = (blockIdx.x * NT + t) * 16 + c;
+      const bool ok = t < NT && n < N;
+      float v = ok ? Y(t, r, c) : -INFINITY;
+      int idx = ok ? n : 0x7fffffff;
+      if (g.logits && ok) g.logits[(size_t)m * N + n] = v;
+      am_wave_reduce(v, idx, 64);
+      if (lane == 0) {
+        g.am_val[(size_t)m * g.ngroups + blockIdx.x] = v;
+        g.am_idx[(size_t)m * g.ngroups + blockIdx.x] = idx;
+      }
     }
-  } else {
-    const bool ok = active && n < N;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rl = mt * 16 + 4 * (lane >> 4) + r;
-        const int m = m0 + rl;
-        float v = ok ? acc[mt][r] : -INFINITY;
-        int idx = ok ? n : 0x7fffffff;
-        if (logits && ok && m < M) logits[(size_t)m * N + n] = acc[mt][r];
-        am_wave_reduce(v, idx, 16);
-        if ((lane & 15) == 0) {
-          s_rv[wave * MT * 16 + rl] = v;
-          s_ri[wave * MT * 16 + rl] = idx;
+  } else if (EP == EPI_RESID) {
+    // X[m][n] += y; per-row sum of squares of the new X over this tile
+    for (int idx = threadIdx.x; idx < rows * 16; idx += NTH) {
+      const int r = idx >> 4, c = idx & 15;
+      const int m = m0 + r, n = nt * 16 + c;
+      float v = 0.f;
+      if (n < N) {
+        v = g.Xout[(size_t)m * N + n] + Y(0, r, c);
+        g.Xout[(size_t)m * N + n] = v;
+      }
+      float sq = v * v;
+      for (int off = 8; off > 0; off >>= 1) sq += __shfl_xor(sq, off, PE_WAVE);
+      if (c == 0) g.ssq_out[(size_t)m * g.nssq_out + nt] = sq;
+    }
+  } else if (EP == EPI_ROWS) {
+    // parallel-draft input rows: row 0 = fc . concat(h) + embed[last_token]; rows 1..K-1 = h_shared + emb_mask
+    const int Kr = g.Kdraft;
+    for (int idx = threadIdx.x; idx < rows * 16; idx += NTH) {
+      const int r = idx >> 4, c = idx & 15;
+      const int b = m0 + r, n = nt * 16 + c;
+      const int tok = g.last_token[b];
+      const bool tok_ok = tok >= 0 && tok < g.V;
+      if (!tok_ok && c == 0) raise_flag(g.flags, PE_FLAG_TOKEN);
+      float x0 = 0.f, ph = 0.f;
+      if (n < N) {
+        x0 = Y(0, r, c) + (tok_ok ? bf16_to_f32(g.embed[(size_t)tok * N + n]) : 0.f);
+        ph = bf16_to_f32(g.h_shared[n]) + bf16_to_f32(g.emb_mask[n]);
+        g.Xout[(size_t)(b * Kr) * N + n] = x0;
+        for (int j = 1; j < Kr; ++j) g.Xout[(size_t)(b * Kr + j) * N + n] = ph;
+      }
+      float s0 = x0 * x0, s1 = ph * ph;
+      for (int off = 8; off > 0; off >>= 1) {
+        s0 += __shfl_xor(s0, off, PE_WAVE);
+        s1 += __shfl_xor(s1, off, PE_WAVE);
+      }
+      if (c == 0) {
+        g.ssq_out[(size_t)(b * Kr) * g.nssq_out + nt] = s0;
+        for (int j = 1; j < Kr; ++j) g.ssq_out[(size_t)(b * Kr + j) * g.nssq_out + nt] = s1;
+      }
+    }
+  } else if (EP == EPI_SWIGLU) {
+    // tile nt: columns 0..7 = gate of f = 8 nt + e, columns 8..15 = up of the same f
+    const int F = g.F;
+    for (int idx = threadIdx.x; idx < rows * 8; idx += NTH) {
+      const int r = idx >> 3, e = idx & 7;
+      const int m = m0 + r, f = 8 * nt + e;
+      if (f >= F) continue;
+      const float gs = Y(0, r, e), us = Y(0, r, 8 + e);
+      const float silu = gs / (1.f + __expf(-gs));
+      g.Aout[(size_t)m * F + f] = f32_to_bf16(silu * us);
+    }
+  } else if (EP == EPI_QKV) {
+    // tile nt of head u holds pairs i = 8 tt + e: columns e (first half) and 8 + e (second half).
+    // q, k: rotate-half RoPE at position seq_len[b] + j; k and v are appended to the cache.
+    const int hd = g.hd, half = hd / 2, Hq = g.Hq, Hkv = g.Hkv;
+    const int tph = hd / 16, u = nt / tph, tt = nt % tph;
+    for (int idx = threadIdx.x; idx < rows * 8; idx += NTH) {
+      const int r = idx >> 3, e = idx & 7;
+      const int m = m0 + r, i = 8 * tt + e;
+      const int b = m / g.Kdraft, j = m % g.Kdraft;
+      const int pos = g.seq_len[b] + j;
+      const int slot = g.req_slot[b];
+      const bool pos_ok = pos >= 0 && pos < g.max_ctx;
+      const bool slot_ok = slot >= 0 && slot < g.n_slots;
+      if (e == 0 && tt == 0) {
+        if (!pos_ok) raise_flag(g.flags, PE_FLAG_POS);
+        if (!slot_ok) raise_flag(g.flags, PE_FLAG_SLOT);
+      }
+      const float x1 = Y(0, r, e), x2 = Y(0, r, 8 + e);
+      if (u >= Hq + Hkv) {
+        if (pos_ok && slot_ok) {
+          bf16_t* v = g.Vc + (((size_t)slot * Hkv + (u - Hq - Hkv)) * g.max_ctx + pos) * hd;
+          v[i] = f32_to_bf16(x1);
+          v[i + half] = f32_to_bf16(x2);
         }
+        continue;
       }
-    __syncthreads();
-    for (int rl = threadIdx.x; rl < MT * 16; rl += 256) {
-      float bv = s_rv[rl];
-      int bi = s_ri[rl];
-      for (int w = 1; w < 4; ++w) {
-        const float v = s_rv[w * MT * 16 + rl];
-        const int i = s_ri[w * MT * 16 + rl];
-        if (am_better(v, i, bv, bi)) { bv = v; bi = i; }
-      }
-      const int m = m0 + rl;
-      if (m < M) {
-        am_val[(size_t)m * ngroups + blockIdx.x] = bv;
-        am_idx[(size_t)m * ngroups + blockIdx.x] = bi;
+      const float2 t = g.rope[(size_t)(pos_ok ? pos : 0) * half + i];
+      const float y1 = x1 * t.x - x2 * t.y;
+      const float y2 = x2 * t.x + x1 * t.y;
+      if (u < Hq) {
+        bf16_t* q = g.Q + ((size_t)m * Hq + u) * hd;
+        q[i] = f32_to_bf16(y1);
+        q[i + half] = f32_to_bf16(y2);
+      } else if (pos_ok && slot_ok) {
+        bf16_t* k = g.Kc + (((size_t)slot * Hkv + (u - Hq)) * g.max_ctx + pos) * hd;
+        k[i] = f32_to_bf16(y1);
+        k[i + half] = f32_to_bf16(y2);
       }
     }
   }
 }
 
-template <bool ARGMAX>
-static hipError_t launch_gemm_bf16(const GemmPlan& p, const void* A, int lda, int M, int Kd, const void* Wp, int N,
-                                   float* P, float* am_val, int* am_idx, float* logits, hipStream_t st) {
-  const int Nt = n_tiles(N), Ks = k_steps(Kd);
-  dim3 grid(p.ngroups, p.mblocks, p.S), block(256);
-  const bf16_t* a = (const bf16_t*)A;
-  const bf16x8_t* w = (const bf16x8_t*)Wp;
-  switch (p.MT) {
-    case 1: hipLaunchKernelGGL((gemm_bf16_kernel<1, ARGMAX>), grid, block, 0, st, a, lda, M, Kd, w, Nt, Ks, N, p.kps, P, am_val, am_idx, p.ngroups, logits); break;
-    case 2: hipLaunchKernelGGL((gemm_bf16_kernel<2, ARGMAX>), grid, block, 0, st, a, lda, M, Kd, w, Nt, Ks, N, p.kps, P, am_val, am_idx, p.ngroups, logits); break;
-    case 4: hipLaunchKernelGGL((gemm_bf16_kernel<4, ARGMAX>), grid, block, 0, st, a, lda, M, Kd, w, Nt, Ks, N, p.kps, P, am_val, am_idx, p.ngroups, logits); break;
-    default: hipLaunchKernelGGL((gemm_bf16_kernel<8, ARGMAX>), grid, block, 0, st, a, lda, M, Kd, w, Nt, Ks, N, p.kps, P, am_val, am_idx, p.ngroups, logits); break;
+template <int MT, int NW, int NT, int AM, int EP>
+static void launch_one(const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((gemm_kernel<MT, NW, NT, AM, EP>), dim3(p.ngroups, p.mblocks), dim3(NW * 64), 0, st, a);
+}
+
+template <int AM, int EP>
+static hipError_t launch_split_nw(const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
+#define PE_NW_CASES(MT_)                                            \
+  if (p.MT == MT_) {                                                \
+    if (p.NW == 16) launch_one<MT_, (MT_ == 1 ? 16 : 4), 1, AM, EP>(p, a, st); \
+    else if (p.NW == 8) launch_one<MT_, (MT_ <= 2 ? 8 : 4), 1, AM, EP>(p, a, st); \
+    else launch_one<MT_, 4, 1, AM, EP>(p, a, st);                   \
+    return hipGetLastError();                                       \
   }
+  PE_NW_CASES(1)
+  PE_NW_CASES(2)
+  PE_NW_CASES(4)
+  PE_NW_CASES(8)
+#undef PE_NW_CASES
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm(const GemmPlan& p, GemmArgs a, int a_mode, int epi, hipStream_t st) {
+  a.Nt = p.Nt;
+  a.Ks = k_steps(a.Kd);
+  a.ngroups = p.ngroups;
+  if (epi == EPI_ARGMAX) {
+    if (a_mode != A_NORM || p.NT != 4 || p.NW != 4) return hipErrorInvalidValue;
+    switch (p.MT) {
+      case 1: launch_one<1, 4, 4, A_NORM, EPI_ARGMAX>(p, a, st); break;
+      case 2: launch_one<2, 4, 4, A_NORM, EPI_ARGMAX>(p, a, st); break;
+      case 4: launch_one<4, 4, 4, A_NORM, EPI_ARGMAX>(p, a, st); break;
+      default: launch_one<8, 4, 4, A_NORM, EPI_ARGMAX>(p, a, st); break;
+    }
+    return hipGetLastError();
+  }
+  if (p.NT != 1) return hipErrorInvalidValue;
+  if (a_mode == A_BF16 && epi == EPI_RESID) return launch_split_nw<A_BF16, EPI_RESID>(p, a, st);
+  if (a_mode == A_BF16 && epi == EPI_ROWS) return launch_split_nw<A_BF16, EPI_ROWS>(p, a, st);
+  if (a_mode == A_NORM && epi == EPI_QKV) return launch_split_nw<A_NORM, EPI_QKV>(p, a, st);
+  if (a_mode == A_NORM && epi == EPI_SWIGLU) return launch_split_nw<A_NORM, EPI_SWIGLU>(p, a, st);
+  return hipErrorInvalidValue;
+}
+
+// X = caller rows; per-16-column sums of squares (the input of the first normalised projection)
+__global__ __launch_bounds__(256) void rows_ssq_kernel(const float* __restrict__ rows, float* __restrict__ X,
+                                                       float* __restrict__ ssq, int d, int nssq) {
+  const int m = blockIdx.x;
+  for (int c0 = 0; c0 < nssq * 16; c0 += 256) {
+    const int c = c0 + threadIdx.x;
+    float v = 0.f;
+    if (c < d) {
+      v = rows[(size_t)m * d + c];
+      X[(size_t)m * d + c] = v;
+    }
+    float sq = v * v;
+    for (int off = 8; off > 0; off >>= 1) sq += __shfl_xor(sq, off, PE_WAVE);
+    if ((c & 15) == 0 && c / 16 < nssq) ssq[(size_t)m * nssq + c / 16] = sq;
+  }
+}
+
+hipError_t launch_rows_ssq(const float* rows, float* X, float* ssq, int M, int d, hipStream_t st) {
+  hipLaunchKernelGGL(rows_ssq_kernel, dim3(M), dim3(256), 0, st, rows, X, ssq, d, (d + 15) / 16);
   return hipGetLastError();
-}
-
-hipError_t launch_gemm_bf16_partial(const GemmPlan& p, const void* A, int lda, int M, int Kd, const void* Wp, int N,
-                                    float* P, hipStream_t st) {
-  return launch_gemm_bf16<false>(p, A, lda, M, Kd, Wp, N, P, nullptr, nullptr, nullptr, st);
-}
-
-hipError_t launch_gemm_bf16_argmax(const GemmPlan& p, const void* A, int lda, int M, int Kd, const void* Wp, int N,
-                                   float* am_val, int* am_idx, float* logits, hipStream_t st) {
-  return launch_gemm_bf16<true>(p, A, lda, M, Kd, Wp, N, nullptr, am_val, am_idx, logits, st);
 }
 
 // fp32 weights (the small fp32 drafter): one wave per output column, lanes stride over k.

@@ -7,29 +7,55 @@
 namespace pe {
 
 // ---- weight packing: W [N, Kd] bf16 -> 1 KiB MFMA fragments ----------------------------------
-// Fragment (t, s) holds rows 16t..16t+15, columns 32s..32s+31; lane l's 16 bytes are
-// W[16t + (l & 15)][32s + 8(l >> 4) .. +7]. Fragments are stored tile-major: ((t*mul+add) * Ks + s).
-hipError_t launch_pack_bf16(const void* W, int N, int Kd, void* dst, int tile_mul, int tile_add, hipStream_t st);
+// Fragment (t, s) holds 16 output rows and columns 32s..32s+31 of the reduction dimension; lane l's 16
+// bytes are W[src(t, l & 15)][32s + 8(l >> 4) .. +7]. Fragments are stored tile-major: (t * Ks + s).
+// PACK_PLAIN: src(t, r) = 16t + r.
+// PACK_PAIRS: the 16 rows of a tile are 8 RoPE pairs of one head of width hd: rows 8tt+e and
+//             hd/2 + 8tt + e of head t / (hd/16), tt = t % (hd/16) (q, k and v heads alike).
+// PACK_GATEUP: rows 8t..8t+7 of W0 (gate) then rows 8t..8t+7 of W1 (up); 2N/16 tiles.
+enum { PACK_PLAIN = 0, PACK_PAIRS = 1, PACK_GATEUP = 2 };
+hipError_t launch_pack_bf16(const void* W0, const void* W1, int N, int Kd, int mode, int hd, void* dst,
+                            hipStream_t st);
 inline int n_tiles(int N) { return (N + 15) / 16; }
 inline int k_steps(int Kd) { return (Kd + 31) / 32; }
 
-// ---- GEMM y = A . W^T -------------------------------------------------------------------------
+// ---- GEMM y = A . W^T with fused prologue / epilogue ---------------------------------------------
 struct GemmPlan {
+  int Nt;       // 16-column tiles
   int MT;       // 16-row MFMA tiles per workgroup (1, 2, 4 or 8)
   int mblocks;  // workgroups along M
-  int ngroups;  // workgroups along N (64 columns each)
-  int S;        // K splits (fp32 partials [S][M][N])
-  int kps;      // k-steps (of 32) per split
+  int NT;       // 16-column tiles per workgroup
+  int NW;       // waves per workgroup (they split the reduction dimension NW/NT ways)
+  int ngroups;  // workgroups along N
 };
-GemmPlan plan_gemm(int M, int N, int Kd, bool argmax_epilogue);
+GemmPlan plan_gemm(int M, int N, int Kd, bool argmax);
 
-// partial mode: P[s][m][n] = sum over split s's k range
-hipError_t launch_gemm_bf16_partial(const GemmPlan& p, const void* A, int lda, int M, int Kd, const void* Wp,
-                                    int N, float* P, hipStream_t st);
-// argmax mode (S == 1): per (row, 64-column group) best (value, index); optional fp32 logits [M][N]
-hipError_t launch_gemm_bf16_argmax(const GemmPlan& p, const void* A, int lda, int M, int Kd, const void* Wp,
-                                   int N, float* am_val, int* am_idx, float* logits, hipStream_t st);
-// fp32 weights, unpacked [N, Kd]: out[m * ldo + n] (one split)
+enum { A_BF16 = 0, A_NORM = 1 };  // A operand: bf16 matrix, or RMSNorm(X) of the fp32 residual stream
+enum { EPI_RESID = 0, EPI_ROWS = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_ARGMAX = 4 };
+
+struct GemmArgs {
+  int M, Kd, N;
+  int Nt, Ks, ngroups;  // filled by launch_gemm from the plan
+  // A operand
+  const uint16_t* A; int lda;                                        // A_BF16
+  const float* X; const float* ssq_in; int nssq; const uint16_t* gain; float eps;  // A_NORM
+  const void* Wp_raw;  // packed weights
+  // EPI_RESID / EPI_ROWS: residual stream (+=, or rows written) and per-16-column sums of squares
+  float* Xout; float* ssq_out; int nssq_out;
+  // EPI_SWIGLU: A [M][F]
+  uint16_t* Aout; int F;
+  // EPI_QKV
+  uint16_t* Q; uint16_t* Kc; uint16_t* Vc;
+  const int* seq_len; const int* req_slot; const float2* rope;
+  int Kdraft, Hq, Hkv, hd, max_ctx, n_slots; int* flags;
+  // EPI_ROWS
+  const int* last_token; const uint16_t* embed; const uint16_t* emb_mask; const uint16_t* h_shared; int V;
+  // EPI_ARGMAX: per (row, workgroup) best (value, index); optional fp32 logits [M][N]
+  float* am_val; int* am_idx; float* logits;
+};
+hipError_t launch_gemm(const GemmPlan& p, GemmArgs a, int a_mode, int epi, hipStream_t st);
+hipError_t launch_rows_ssq(const float* rows, float* X, float* ssq, int M, int d, hipStream_t st);
+// fp32 weights, unpacked [N, Kd]: out[m * ldo + n]
 hipError_t launch_gemm_f32(const float* A, int lda, int M, int Kd, const float* W, int N, float* out, int ldo,
                            hipStream_t st);
 

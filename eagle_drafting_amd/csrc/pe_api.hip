@@ -42,11 +42,12 @@ struct pe_ctx {
   int* t_ws = nullptr;     // target argmax [max_batch, max_k + 1]
   float* logits_ws = nullptr;  // fp32 path: logits when the caller passes none
   float2* rope = nullptr;  // [max_ctx, hd/2] (cos, sin)
+  float* ssq = nullptr;    // per-16-column sums of squares of X rows [Mmax, d/16]
   int* flags = nullptr;
 
   std::string err;
 
-  bool prof = false;
+  int prof = 0;  // bitmask of recorded kernels
   std::vector<hipEvent_t> ev_a[PE_PROF_COUNT], ev_b[PE_PROF_COUNT];
   size_t ev_used[PE_PROF_COUNT] = {};
 };
@@ -184,20 +185,19 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
     char* base = ctx->packed;
     hipStream_t st = ctx->stream;
     auto chk = [&](hipError_t r) { return r == hipSuccess; };
-    bool ok = chk(launch_pack_bf16(w->fc, d, 3 * d, base + o_fc, 1, 0, st));
+    bool ok = chk(launch_pack_bf16(w->fc, nullptr, d, 3 * d, PACK_PLAIN, 0, base + o_fc, st));
     ctx->p_fc = base + o_fc;
     for (int l = 0; l < c.n_layers && ok; ++l) {
-      ok = ok && chk(launch_pack_bf16(w->wqkv[l], qkvd, d, base + o_qkv[l], 1, 0, st));
-      ok = ok && chk(launch_pack_bf16(w->wo[l], d, qd, base + o_o[l], 1, 0, st));
-      ok = ok && chk(launch_pack_bf16(w->wgate[l], F, d, base + o_gu[l], 2, 0, st));
-      ok = ok && chk(launch_pack_bf16(w->wup[l], F, d, base + o_gu[l], 2, 1, st));
-      ok = ok && chk(launch_pack_bf16(w->wdown[l], d, F, base + o_dn[l], 1, 0, st));
+      ok = ok && chk(launch_pack_bf16(w->wqkv[l], nullptr, qkvd, d, PACK_PAIRS, hd, base + o_qkv[l], st));
+      ok = ok && chk(launch_pack_bf16(w->wo[l], nullptr, d, qd, PACK_PLAIN, 0, base + o_o[l], st));
+      ok = ok && chk(launch_pack_bf16(w->wgate[l], w->wup[l], F, d, PACK_GATEUP, 0, base + o_gu[l], st));
+      ok = ok && chk(launch_pack_bf16(w->wdown[l], nullptr, d, F, PACK_PLAIN, 0, base + o_dn[l], st));
       ctx->p_qkv[l] = base + o_qkv[l];
       ctx->p_o[l] = base + o_o[l];
       ctx->p_gu[l] = base + o_gu[l];
       ctx->p_down[l] = base + o_dn[l];
     }
-    ok = ok && chk(launch_pack_bf16(w->lm_head, V, d, base + o_lm, 1, 0, st));
+    ok = ok && chk(launch_pack_bf16(w->lm_head, nullptr, V, d, PACK_PLAIN, 0, base + o_lm, st));
     ctx->p_lm = base + o_lm;
     if (!ok) {
       free_ctx(ctx);
@@ -209,11 +209,6 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
   size_t p_floats = 0, attn_floats = 0, am_floats = 0;
   for (int M = 1; M <= Mmax; ++M) {
     if (ctx->bf16) {
-      const int Ns[4] = {qkvd, d, 2 * F, d}, Ks[4] = {d, qd, d, F};
-      for (int i = 0; i < 4; ++i) {
-        GemmPlan p = plan_gemm(M, Ns[i], Ks[i], false);
-        p_floats = std::max(p_floats, (size_t)p.S * M * Ns[i]);
-      }
       GemmPlan pl = plan_gemm(M, V, d, true);
       am_floats = std::max(am_floats, (size_t)M * pl.ngroups);
     } else {
@@ -223,8 +218,6 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
   }
   for (int B = 1; B <= c.max_batch; ++B) {
     if (ctx->bf16) {
-      GemmPlan p = plan_gemm(B, d, 3 * d, false);
-      p_floats = std::max(p_floats, (size_t)p.S * B * d);
       for (int K = 1; K <= c.max_k; ++K) {
         AttnPlan ap = plan_attention(B, K, c.n_q_heads, c.n_kv_heads, c.max_ctx);
         attn_floats = std::max(attn_floats, attn_partial_floats(B * K, c.n_q_heads, hd, ap));
@@ -237,6 +230,7 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
       am_floats = std::max(am_floats, (size_t)rows * plan_argmax_chunks(rows, V));
     }
   }
+  const int nssq = (d + 15) / 16;
   size_t off = 0;
   auto take = [&](size_t b) { size_t o = off; off = align256(off + b); return o; };
   const size_t oX = take((size_t)Mmax * d * 4), oU = take((size_t)Mmax * d * es), oQ = take((size_t)Mmax * qd * es),
@@ -244,7 +238,7 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
                oAt = take(std::max(attn_floats, (size_t)1) * 4), oAv = take(am_floats * 4), oAi = take(am_floats * 4),
                oT = take((size_t)c.max_batch * (c.max_k + 1) * 4),
                oL = take(ctx->bf16 ? 0 : (size_t)Mmax * V * 4), oR = take((size_t)c.max_ctx * (hd / 2) * 8),
-               oF = take(256);
+               oS = take((size_t)Mmax * nssq * 4), oF = take(256);
   if (hipMalloc((void**)&ctx->ws, off) != hipSuccess) {
     free_ctx(ctx);
     return fail(nullptr, PE_ERR_OOM, "hipMalloc of workspace failed");
@@ -262,6 +256,7 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
   ctx->t_ws = (int*)(b + oT);
   ctx->logits_ws = ctx->bf16 ? nullptr : (float*)(b + oL);
   ctx->rope = (float2*)(b + oR);
+  ctx->ssq = (float*)(b + oS);
   ctx->flags = (int*)(b + oF);
 
   hipError_t r = launch_rope_table(ctx->rope, c.max_ctx, hd, (double)c.rope_base, ctx->stream);
@@ -286,7 +281,7 @@ extern "C" pe_status pe_destroy(pe_ctx* ctx) {
 
 // ---- per-launch event timing of selected kernels
 static hipError_t prof_mark(pe_ctx* c, int which, bool begin) {
-  if (!c->prof) return hipSuccess;
+  if (!(c->prof & (1 << which))) return hipSuccess;
   auto& pool = begin ? c->ev_a[which] : c->ev_b[which];
   size_t i = c->ev_used[which];
   if (i >= 65536) return hipSuccess;  // stop recording beyond the cap
@@ -301,10 +296,10 @@ static hipError_t prof_mark(pe_ctx* c, int which, bool begin) {
   return r;
 }
 
-extern "C" pe_status pe_profile_enable(pe_ctx* ctx, int32_t on) {
+extern "C" pe_status pe_profile_enable(pe_ctx* ctx, int32_t mask) {
   if (!ctx) return fail(nullptr, PE_ERR_INVALID, "ctx is NULL");
   HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
-  ctx->prof = on != 0;
+  ctx->prof = mask & ((1 << PE_PROF_COUNT) - 1);
   for (int k = 0; k < PE_PROF_COUNT; ++k) ctx->ev_used[k] = 0;
   return PE_OK;
 }
@@ -337,6 +332,144 @@ extern "C" pe_status pe_device_flags(pe_ctx* ctx, int32_t clear, int32_t* flags)
 
 #define LAUNCH(call) HIP_TRY(ctx, (call))
 
+// fp32 drafter: one kernel per step of the layer (small shapes only)
+static pe_status draft_f32(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_slot, const int32_t* seq_len,
+                           const int32_t* last_token, const void* target_hidden, const float* rows,
+                           int32_t* draft_tokens, float* logits) {
+  const pe_config& c = ctx->cfg;
+  hipStream_t st = ctx->stream;
+  const int d = c.d_model, F = c.ffn_dim, V = c.vocab, hd = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+  const int qd = Hq * hd, qkvd = (Hq + 2 * Hkv) * hd;
+  const int M = B * K;
+  const float eps = c.rms_eps;
+  const pe_weights& w = ctx->w;
+  float* P = ctx->P;
+  if (!rows) LAUNCH(launch_gemm_f32((const float*)target_hidden, 3 * d, B, 3 * d, (const float*)w.fc, d, P, d, st));
+  LAUNCH(launch_rowbuild_norm(0, ctx->X, ctx->U, P, 1, rows, B, K, d, last_token, w.embed, w.emb_mask, w.h_shared,
+                              w.attn_norm[0], eps, V, ctx->flags, st));
+  for (int l = 0; l < c.n_layers; ++l) {
+    LAUNCH(launch_gemm_f32((const float*)ctx->U, d, M, d, (const float*)w.wqkv[l], qkvd, P, qkvd, st));
+    LAUNCH(launch_rope_kv(0, ctx->Qb, ctx->kv.k[l], ctx->kv.v[l], P, 1, B, K, Hq, Hkv, hd, seq_len, req_slot,
+                          c.max_ctx, c.n_slots, ctx->rope, ctx->flags, st));
+    LAUNCH(prof_mark(ctx, PE_PROF_ATTENTION, true));
+    LAUNCH(launch_attention_f32((const float*)ctx->Qb, (const float*)ctx->kv.k[l], (const float*)ctx->kv.v[l], seq_len,
+                                req_slot, B, K, Hq, Hkv, hd, c.max_ctx, c.n_slots, (float*)ctx->Ob, st));
+    LAUNCH(prof_mark(ctx, PE_PROF_ATTENTION, false));
+    LAUNCH(launch_gemm_f32((const float*)ctx->Ob, qd, M, qd, (const float*)w.wo[l], d, P, d, st));
+    LAUNCH(launch_residual_norm(0, ctx->X, ctx->U, P, 1, M, d, w.mlp_norm[l], eps, st));
+    LAUNCH(prof_mark(ctx, PE_PROF_GATE_UP, true));
+    LAUNCH(launch_gemm_f32((const float*)ctx->U, d, M, d, (const float*)w.wgate[l], F, P, 2 * F, st));
+    LAUNCH(launch_gemm_f32((const float*)ctx->U, d, M, d, (const float*)w.wup[l], F, P + F, 2 * F, st));
+    LAUNCH(prof_mark(ctx, PE_PROF_GATE_UP, false));
+    LAUNCH(launch_swiglu(0, ctx->Ab, P, 1, M, F, false, st));
+    LAUNCH(launch_gemm_f32((const float*)ctx->Ab, F, M, F, (const float*)w.wdown[l], d, P, d, st));
+    const void* g_next = l + 1 < c.n_layers ? w.attn_norm[l + 1] : w.final_norm;
+    LAUNCH(launch_residual_norm(0, ctx->X, ctx->U, P, 1, M, d, g_next, eps, st));
+  }
+  float* z = logits ? logits : ctx->logits_ws;
+  LAUNCH(prof_mark(ctx, PE_PROF_LM_HEAD, true));
+  LAUNCH(launch_gemm_f32((const float*)ctx->U, d, M, d, (const float*)w.lm_head, V, z, V, st));
+  LAUNCH(prof_mark(ctx, PE_PROF_LM_HEAD, false));
+  const int nch = plan_argmax_chunks(M, V);
+  LAUNCH(launch_argmax_rows(0, z, M, V, nch, ctx->am_val, ctx->am_idx, st));
+  LAUNCH(launch_argmax_final(ctx->am_val, ctx->am_idx, M, nch, draft_tokens, st));
+  return PE_OK;
+}
+
+// bf16 drafter: per layer six kernels (QKV+RoPE+KV append, attention, combine, O+residual, gate/up+SwiGLU,
+// down+residual); RMSNorm is applied while the next projection reads its input.
+static pe_status draft_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_slot, const int32_t* seq_len,
+                            const int32_t* last_token, const void* target_hidden, const float* rows,
+                            int32_t* draft_tokens, float* logits) {
+  const pe_config& c = ctx->cfg;
+  hipStream_t st = ctx->stream;
+  const int d = c.d_model, F = c.ffn_dim, V = c.vocab, hd = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+  const int qd = Hq * hd, qkvd = (Hq + 2 * Hkv) * hd;
+  const int M = B * K;
+  const int nssq = (d + 15) / 16;
+  const pe_weights& w = ctx->w;
+
+  GemmArgs base{};
+  base.X = ctx->X;
+  base.Xout = ctx->X;
+  base.ssq_in = ctx->ssq;
+  base.ssq_out = ctx->ssq;
+  base.nssq = nssq;
+  base.nssq_out = nssq;
+  base.eps = c.rms_eps;
+  base.flags = ctx->flags;
+
+  // a1 (+ the sums of squares for layer 0's RMSNorm): the K input rows of every request
+  if (!rows) {
+    GemmArgs a = base;
+    a.M = B; a.Kd = 3 * d; a.N = d;
+    a.A = (const uint16_t*)target_hidden; a.lda = 3 * d;
+    a.Wp_raw = ctx->p_fc;
+    a.Kdraft = K; a.last_token = last_token; a.V = V;
+    a.embed = (const uint16_t*)w.embed; a.emb_mask = (const uint16_t*)w.emb_mask; a.h_shared = (const uint16_t*)w.h_shared;
+    LAUNCH(launch_gemm(plan_gemm(B, d, 3 * d, false), a, A_BF16, EPI_ROWS, st));
+  } else {
+    LAUNCH(launch_rows_ssq(rows, ctx->X, ctx->ssq, M, d, st));
+  }
+  for (int l = 0; l < c.n_layers; ++l) {
+    {  // a2-a4: RMSNorm, QKV, RoPE, KV append
+      GemmArgs a = base;
+      a.M = M; a.Kd = d; a.N = qkvd;
+      a.gain = (const uint16_t*)w.attn_norm[l];
+      a.Wp_raw = ctx->p_qkv[l];
+      a.Q = (uint16_t*)ctx->Qb; a.Kc = (uint16_t*)ctx->kv.k[l]; a.Vc = (uint16_t*)ctx->kv.v[l];
+      a.seq_len = seq_len; a.req_slot = req_slot; a.rope = ctx->rope;
+      a.Kdraft = K; a.Hq = Hq; a.Hkv = Hkv; a.hd = hd; a.max_ctx = c.max_ctx; a.n_slots = c.n_slots;
+      LAUNCH(launch_gemm(plan_gemm(M, qkvd, d, false), a, A_NORM, EPI_QKV, st));
+    }
+    // a5: attention
+    AttnPlan ap = plan_attention(B, K, Hq, Hkv, c.max_ctx);
+    LAUNCH(prof_mark(ctx, PE_PROF_ATTENTION, true));
+    LAUNCH(launch_attention_bf16(ap, ctx->Qb, ctx->kv.k[l], ctx->kv.v[l], seq_len, req_slot, B, K, Hq, Hkv, hd,
+                                 c.max_ctx, c.n_slots, ctx->attn, st));
+    LAUNCH(prof_mark(ctx, PE_PROF_ATTENTION, false));
+    LAUNCH(launch_attention_combine_bf16(ap, ctx->attn, ctx->Ob, seq_len, req_slot, B, K, Hq, Hkv, hd, c.max_ctx,
+                                         c.n_slots, st));
+    {  // a6: output projection + residual
+      GemmArgs a = base;
+      a.M = M; a.Kd = qd; a.N = d;
+      a.A = (const uint16_t*)ctx->Ob; a.lda = qd;
+      a.Wp_raw = ctx->p_o[l];
+      LAUNCH(launch_gemm(plan_gemm(M, d, qd, false), a, A_BF16, EPI_RESID, st));
+    }
+    {  // a7: RMSNorm, gate/up, SwiGLU
+      GemmArgs a = base;
+      a.M = M; a.Kd = d; a.N = 2 * F;
+      a.gain = (const uint16_t*)w.mlp_norm[l];
+      a.Wp_raw = ctx->p_gu[l];
+      a.Aout = (uint16_t*)ctx->Ab;
+      a.F = F;
+      LAUNCH(prof_mark(ctx, PE_PROF_GATE_UP, true));
+      LAUNCH(launch_gemm(plan_gemm(M, 2 * F, d, false), a, A_NORM, EPI_SWIGLU, st));
+      LAUNCH(prof_mark(ctx, PE_PROF_GATE_UP, false));
+    }
+    {  // a8: down projection + residual
+      GemmArgs a = base;
+      a.M = M; a.Kd = F; a.N = d;
+      a.A = (const uint16_t*)ctx->Ab; a.lda = F;
+      a.Wp_raw = ctx->p_down[l];
+      LAUNCH(launch_gemm(plan_gemm(M, d, F, false), a, A_BF16, EPI_RESID, st));
+    }
+  }
+  // a9-a10: final RMSNorm, LM head, argmax
+  GemmArgs a = base;
+  a.M = M; a.Kd = d; a.N = V;
+  a.gain = (const uint16_t*)w.final_norm;
+  a.Wp_raw = ctx->p_lm;
+  a.am_val = ctx->am_val; a.am_idx = ctx->am_idx; a.logits = logits;
+  GemmPlan p = plan_gemm(M, V, d, true);
+  LAUNCH(prof_mark(ctx, PE_PROF_LM_HEAD, true));
+  LAUNCH(launch_gemm(p, a, A_NORM, EPI_ARGMAX, st));
+  LAUNCH(prof_mark(ctx, PE_PROF_LM_HEAD, false));
+  LAUNCH(launch_argmax_final(ctx->am_val, ctx->am_idx, M, p.ngroups, draft_tokens, st));
+  return PE_OK;
+}
+
 static pe_status run_draft(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_slot, const int32_t* seq_len,
                            const int32_t* last_token, const void* target_hidden, const float* rows,
                            int32_t* draft_tokens, float* logits) {
@@ -347,105 +480,8 @@ static pe_status run_draft(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req
   if (!req_slot || !seq_len || !draft_tokens) return fail(ctx, PE_ERR_INVALID, "NULL request array");
   if (!rows && (!last_token || !target_hidden)) return fail(ctx, PE_ERR_INVALID, "NULL last_token / target_hidden");
   if (target_hidden && ((uintptr_t)target_hidden & 15)) return fail(ctx, PE_ERR_INVALID, "target_hidden not 16-byte aligned");
-
-  hipStream_t st = ctx->stream;
-  const int dt = ctx->bf16 ? 1 : 0;
-  const int d = c.d_model, F = c.ffn_dim, V = c.vocab, hd = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
-  const int qd = Hq * hd, qkvd = (Hq + 2 * Hkv) * hd;
-  const int M = B * K;
-  const float eps = c.rms_eps;
-  const pe_weights& w = ctx->w;
-
-  // a1: input rows (+ RMSNorm of layer 0)
-  int S = 1;
-  if (!rows) {
-    if (ctx->bf16) {
-      GemmPlan p = plan_gemm(B, d, 3 * d, false);
-      LAUNCH(launch_gemm_bf16_partial(p, target_hidden, 3 * d, B, 3 * d, ctx->p_fc, d, ctx->P, st));
-      S = p.S;
-    } else {
-      LAUNCH(launch_gemm_f32((const float*)target_hidden, 3 * d, B, 3 * d, (const float*)w.fc, d, ctx->P, d, st));
-    }
-  }
-  LAUNCH(launch_rowbuild_norm(dt, ctx->X, ctx->U, ctx->P, S, rows, B, K, d, last_token, w.embed, w.emb_mask,
-                              w.h_shared, w.attn_norm[0], eps, V, ctx->flags, st));
-  for (int l = 0; l < c.n_layers; ++l) {
-    // a3-a4: QKV projection, RoPE, KV append
-    if (ctx->bf16) {
-      GemmPlan p = plan_gemm(M, qkvd, d, false);
-      LAUNCH(launch_gemm_bf16_partial(p, ctx->U, d, M, d, ctx->p_qkv[l], qkvd, ctx->P, st));
-      S = p.S;
-    } else {
-      LAUNCH(launch_gemm_f32((const float*)ctx->U, d, M, d, (const float*)w.wqkv[l], qkvd, ctx->P, qkvd, st));
-      S = 1;
-    }
-    LAUNCH(launch_rope_kv(dt, ctx->Qb, ctx->kv.k[l], ctx->kv.v[l], ctx->P, S, B, K, Hq, Hkv, hd, seq_len, req_slot,
-                          c.max_ctx, c.n_slots, ctx->rope, ctx->flags, st));
-    // a5: attention
-    LAUNCH(prof_mark(ctx, PE_PROF_ATTENTION, true));
-    if (ctx->bf16) {
-      AttnPlan ap = plan_attention(B, K, Hq, Hkv, c.max_ctx);
-      LAUNCH(launch_attention_bf16(ap, ctx->Qb, ctx->kv.k[l], ctx->kv.v[l], seq_len, req_slot, B, K, Hq, Hkv, hd,
-                                   c.max_ctx, c.n_slots, ctx->attn, st));
-      LAUNCH(prof_mark(ctx, PE_PROF_ATTENTION, false));
-      LAUNCH(launch_attention_combine_bf16(ap, ctx->attn, ctx->Ob, seq_len, req_slot, B, K, Hq, Hkv, hd, c.max_ctx,
-                                           c.n_slots, st));
-    } else {
-      LAUNCH(launch_attention_f32((const float*)ctx->Qb, (const float*)ctx->kv.k[l], (const float*)ctx->kv.v[l],
-                                  seq_len, req_slot, B, K, Hq, Hkv, hd, c.max_ctx, c.n_slots, (float*)ctx->Ob, st));
-      LAUNCH(prof_mark(ctx, PE_PROF_ATTENTION, false));
-    }
-    // a6: output projection + residual, RMSNorm
-    if (ctx->bf16) {
-      GemmPlan p = plan_gemm(M, d, qd, false);
-      LAUNCH(launch_gemm_bf16_partial(p, ctx->Ob, qd, M, qd, ctx->p_o[l], d, ctx->P, st));
-      S = p.S;
-    } else {
-      LAUNCH(launch_gemm_f32((const float*)ctx->Ob, qd, M, qd, (const float*)w.wo[l], d, ctx->P, d, st));
-      S = 1;
-    }
-    LAUNCH(launch_residual_norm(dt, ctx->X, ctx->U, ctx->P, S, M, d, w.mlp_norm[l], eps, st));
-    // a7: gate/up + SwiGLU
-    LAUNCH(prof_mark(ctx, PE_PROF_GATE_UP, true));
-    if (ctx->bf16) {
-      GemmPlan p = plan_gemm(M, 2 * F, d, false);
-      LAUNCH(launch_gemm_bf16_partial(p, ctx->U, d, M, d, ctx->p_gu[l], 2 * F, ctx->P, st));
-      S = p.S;
-    } else {
-      LAUNCH(launch_gemm_f32((const float*)ctx->U, d, M, d, (const float*)w.wgate[l], F, ctx->P, 2 * F, st));
-      LAUNCH(launch_gemm_f32((const float*)ctx->U, d, M, d, (const float*)w.wup[l], F, ctx->P + F, 2 * F, st));
-      S = 1;
-    }
-    LAUNCH(prof_mark(ctx, PE_PROF_GATE_UP, false));
-    LAUNCH(launch_swiglu(dt, ctx->Ab, ctx->P, S, M, F, ctx->bf16, st));
-    // a8: down projection + residual, RMSNorm for the next layer (or the final norm)
-    if (ctx->bf16) {
-      GemmPlan p = plan_gemm(M, d, F, false);
-      LAUNCH(launch_gemm_bf16_partial(p, ctx->Ab, F, M, F, ctx->p_down[l], d, ctx->P, st));
-      S = p.S;
-    } else {
-      LAUNCH(launch_gemm_f32((const float*)ctx->Ab, F, M, F, (const float*)w.wdown[l], d, ctx->P, d, st));
-      S = 1;
-    }
-    const void* g_next = l + 1 < c.n_layers ? w.attn_norm[l + 1] : w.final_norm;
-    LAUNCH(launch_residual_norm(dt, ctx->X, ctx->U, ctx->P, S, M, d, g_next, eps, st));
-  }
-  // a9-a10: LM head + argmax
-  LAUNCH(prof_mark(ctx, PE_PROF_LM_HEAD, true));
-  if (ctx->bf16) {
-    GemmPlan p = plan_gemm(M, V, d, true);
-    LAUNCH(launch_gemm_bf16_argmax(p, ctx->U, d, M, d, ctx->p_lm, V, ctx->am_val, ctx->am_idx, logits, st));
-    LAUNCH(prof_mark(ctx, PE_PROF_LM_HEAD, false));
-    LAUNCH(launch_argmax_final(ctx->am_val, ctx->am_idx, M, p.ngroups, draft_tokens, st));
-  } else {
-    float* z = logits ? logits : ctx->logits_ws;
-    LAUNCH(launch_gemm_f32((const float*)ctx->U, d, M, d, (const float*)w.lm_head, V, z, V, st));
-    LAUNCH(prof_mark(ctx, PE_PROF_LM_HEAD, false));
-    const int nch = plan_argmax_chunks(M, V);
-    LAUNCH(launch_argmax_rows(0, z, M, V, nch, ctx->am_val, ctx->am_idx, st));
-    LAUNCH(launch_argmax_final(ctx->am_val, ctx->am_idx, M, nch, draft_tokens, st));
-  }
-  return PE_OK;
+  if (ctx->bf16) return draft_bf16(ctx, B, K, req_slot, seq_len, last_token, target_hidden, rows, draft_tokens, logits);
+  return draft_f32(ctx, B, K, req_slot, seq_len, last_token, target_hidden, rows, draft_tokens, logits);
 }
 
 extern "C" pe_status pe_draft_step(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_slot, const int32_t* seq_len,

@@ -150,9 +150,10 @@ pe_status pe_destroy(pe_ctx* ctx);
  * Synchronizes the stream; clear != 0 resets the flags. */
 pe_status pe_device_flags(pe_ctx* ctx, int32_t clear, int32_t* flags);
 
-/* Per-launch timing of selected kernels with HIP events recorded on the ctx's stream.
- * pe_profile_enable(ctx, 1) starts recording (resets the totals); pe_profile_read synchronizes and
- * returns the summed duration in milliseconds and the number of launches of one kernel. */
+/* Per-launch timing of selected kernels with HIP events recorded on the ctx's stream around each launch.
+ * pe_profile_enable(ctx, mask) synchronizes, resets the totals and records the kernels whose bit
+ * (1 << pe_prof_kernel) is set in mask (0 stops recording); pe_profile_read synchronizes and returns the
+ * summed duration in milliseconds and the number of recorded launches of one kernel. */
 typedef enum {
   PE_PROF_LM_HEAD = 0,     /* LM-head GEMM with fused argmax partials */
   PE_PROF_ATTENTION = 1,   /* attention main kernel (every layer) */
@@ -160,7 +161,7 @@ typedef enum {
   PE_PROF_VERIFY_SCAN = 3, /* verify's vocabulary argmax scan */
   PE_PROF_COUNT = 4
 } pe_prof_kernel;
-pe_status pe_profile_enable(pe_ctx* ctx, int32_t on);
+pe_status pe_profile_enable(pe_ctx* ctx, int32_t mask);
 pe_status pe_profile_read(pe_ctx* ctx, int32_t which, double* total_ms, int64_t* launches);
 
 const char* pe_status_string(pe_status s);

@@ -101,7 +101,7 @@ def test_draft_rows_parity_and_causality(shape):
     try:
         X = _random_rows(w, 1)
         Xd = torch.from_numpy(X).cuda()
-        draft0, z0 = _parity(g, range(w.B), rows=Xd, rows_host=X.astype(np.float64), check_kv=False)
+        draft0, z0, _ = _parity(g, range(w.B), rows=Xd, rows_host=X.astype(np.float64), check_kv=False)
         z0 = z0.cpu().numpy()
         for j in range(w.K - 1):
             Xp = X.copy()
