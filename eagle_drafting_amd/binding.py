@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import sys
 from ctypes import POINTER, c_char_p, c_double, c_float, c_int32, c_int64, c_void_p
 
 PE_MAX_LAYERS = 8
@@ -66,6 +67,14 @@ def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m eagle_drafting_amd.build` "
                           "(hipcc, gfx950); the draft/verify path has no other implementation")
+    # libpe.so needs the HIP runtime by soname; when PyTorch (which ships its own copy of that runtime) is
+    # present, load it first so that the process holds one runtime and torch's device buffers and
+    # streams are valid for the library.
+    if "torch" not in sys.modules:
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
     lib = ctypes.CDLL(path)
     vp, i32 = c_void_p, c_int32
     sig = {

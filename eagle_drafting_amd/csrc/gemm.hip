@@ -140,6 +140,30 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
   const bf16x8_t* wsrc = (const bf16x8_t*)g.Wp_raw + (size_t)(active ? nt : 0) * Ks * 64 + lane;
   const bf16x8_t zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
 
+  // Side inputs of the epilogue, loaded before the weight stream so that their latency overlaps it:
+  // the wave's first row of 1/RMS partials, this thread's first residual element, its first row's
+  // sequence position and slot, its first ROWS-epilogue token.
+  const int nrows = min(MT * 16, M - m0);
+  constexpr int NTH = NW * 64;
+  float pre_ssq[4] = {0.f, 0.f, 0.f, 0.f};
+  if (AM == A_NORM && wave < nrows) {
+    const float* src = g.ssq_in + (size_t)(m0 + wave) * g.nssq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lane + 64 * i < g.nssq) pre_ssq[i] = src[lane + 64 * i];
+  }
+  float pre_x = 0.f;
+  if (EP == EPI_RESID && (int)threadIdx.x < nrows * 16 && nt * 16 + (threadIdx.x & 15) < N)
+    pre_x = g.Xout[(size_t)(m0 + (threadIdx.x >> 4)) * N + nt * 16 + (threadIdx.x & 15)];
+  int pre_seq = 0, pre_slot = 0;
+  if (EP == EPI_QKV && (int)threadIdx.x < nrows * 8) {
+    const int b = (m0 + (threadIdx.x >> 3)) / g.Kdraft;
+    pre_seq = g.seq_len[b];
+    pre_slot = g.req_slot[b];
+  }
+  int pre_tok = 0;
+  if (EP == EPI_ROWS && (int)threadIdx.x < nrows * 16) pre_tok = g.last_token[m0 + (threadIdx.x >> 4)];
+
   for (int c0 = s_begin; c0 < s_end; c0 += KC) {
     const int nk = min(KC, s_end - c0);
     bf16x8_t b[KC];
@@ -186,12 +210,16 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
 
   if (AM == A_NORM) {
     // 1 / RMS of each row of X from the per-16-column partial sums of squares: one wave per row, all
-    // partials loaded at once (fixed reduction order)
-    const int nrows = min(MT * 16, M - m0);
+    // partials loaded at once (the first row's were prefetched), fixed reduction order
     for (int r = wave; r < nrows; r += NW) {
       const float* src = g.ssq_in + (size_t)(m0 + r) * g.nssq;
       float t = 0.f;
-      for (int i = lane; i < g.nssq; i += 64) t += src[i];
+      if (r == wave) {
+        t = (pre_ssq[0] + pre_ssq[1]) + (pre_ssq[2] + pre_ssq[3]);
+        for (int i = lane + 256; i < g.nssq; i += 64) t += src[i];
+      } else {
+        for (int i = lane; i < g.nssq; i += 64) t += src[i];
+      }
       t = wave_sum(t);
       if (lane == 0) s_inv[r] = rsqrtf(t / (float)Kd + g.eps);
     }
@@ -218,8 +246,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
     const float v = s_red[(t * MT + (r >> 4)) * 256 + (r & 15) * 16 + c];
     return AM == A_NORM ? v * s_inv[r] : v;
   };
-  const int rows = min(MT * 16, M - m0);
-  constexpr int NTH = NW * 64;
+  const int rows = nrows;
 
   if (EP == EPI_ARGMAX) {
     // best (value, index) of each row over the workgroup's NT*16 columns; optional logits
@@ -244,7 +271,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
       const int m = m0 + r, n = nt * 16 + c;
       float v = 0.f;
       if (n < N) {
-        v = g.Xout[(size_t)m * N + n] + Y(0, r, c);
+        v = (idx == (int)threadIdx.x ? pre_x : g.Xout[(size_t)m * N + n]) + Y(0, r, c);
         g.Xout[(size_t)m * N + n] = v;
       }
       float sq = v * v;
@@ -257,7 +284,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
     for (int idx = threadIdx.x; idx < rows * 16; idx += NTH) {
       const int r = idx >> 4, c = idx & 15;
       const int b = m0 + r, n = nt * 16 + c;
-      const int tok = g.last_token[b];
+      const int tok = idx == (int)threadIdx.x ? pre_tok : g.last_token[b];
       const bool tok_ok = tok >= 0 && tok < g.V;
       if (!tok_ok && c == 0) raise_flag(g.flags, PE_FLAG_TOKEN);
       float x0 = 0.f, ph = 0.f;
@@ -297,8 +324,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
       const int r = idx >> 3, e = idx & 7;
       const int m = m0 + r, i = 8 * tt + e;
       const int b = m / g.Kdraft, j = m % g.Kdraft;
-      const int pos = g.seq_len[b] + j;
-      const int slot = g.req_slot[b];
+      const bool first = idx == (int)threadIdx.x;
+      const int pos = (first ? pre_seq : g.seq_len[b]) + j;
+      const int slot = first ? pre_slot : g.req_slot[b];
       const bool pos_ok = pos >= 0 && pos < g.max_ctx;
       const bool slot_ok = slot >= 0 && slot < g.n_slots;
       if (e == 0 && tt == 0) {
