@@ -10,9 +10,10 @@
 // its NW waves split the k range (NW/NT parts), each accumulating MT 16x16 fp32 tiles with
 // v_mfma_f32_16x16x32_bf16, and the parts are summed through LDS in a fixed order. No workgroup depends
 // on another, so results are deterministic and no device-wide synchronisation is needed.
-// The A operand is read straight from global memory (it is tiny: M = B*K rows): either a bf16 matrix or
-// RMSNorm(X) of the fp32 residual stream, normalised on the fly from per-16-column partial sums of
-// squares that the kernel which last updated X wrote.
+// The A operand is a bf16 matrix that every wave reads straight from global memory into MFMA fragments
+// (it is tiny: M = B*K rows, and stays in cache). A normalised operand is bf16(x * g), written by the kernel that last
+// updated the residual stream x together with per-16-column sums of squares; RMSNorm is a per-row scale,
+// so the epilogue multiplies each product row by 1/RMS(x): y = (x * g / rms) . W^T = ((x * g) . W^T) / rms.
 //
 // MFMA lane layout (16x16x32, wave64): A lane l holds A[l%16][k-group l/16] (8 values), B lane l holds
 // B[k-group l/16][l%16], D lane l holds D[4(l/16)+r][l%16], r = 0..3. A and B use the same k grouping,
@@ -83,10 +84,12 @@ GemmPlan plan_gemm(int M, int N, int Kd, bool argmax) {
     p.NT = 1;
     // enough waves in flight (about 4096 in total) while each wave streams at least 8 k-steps;
     // register budget caps NW by MT (LDS for the cross-wave sum is NW * MT KiB)
+    // about one residency round of waves in total (~4096), each wave streaming at least 8 k-steps;
+    // the register budget caps NW by MT (LDS for the cross-wave sum is NW * MT KiB)
     const int cap = p.MT == 1 ? 16 : p.MT == 2 ? 8 : 4;
     const int groups = p.Nt * p.mblocks;
     int nw = 4;
-    while (nw < cap && groups * nw < 4096 && Ks / (2 * nw) >= 8) nw *= 2;
+    while (nw < cap && groups * nw * 2 <= 4096 && Ks / (2 * nw) >= 8) nw *= 2;
     p.NW = nw;
   }
   p.ngroups = (p.Nt + p.NT - 1) / p.NT;
@@ -98,130 +101,112 @@ struct KChunk {
   static constexpr int value = MT <= 2 ? 8 : (MT == 4 ? 4 : 2);
 };
 
-// One A-operand fragment piece: rows of A (bf16), or x * g of the residual stream (bf16); the per-row
-// 1/RMS of a normalised operand is applied to the product rows in the epilogue instead, so the main
-// loop never waits for it (RMSNorm is a per-row scale, and y = (s * x * g) . W^T = s * ((x * g) . W^T)).
-template <int AM>
-__device__ __forceinline__ bf16x8_t load_a(const GemmArgs& g, int row, int col) {
-  if (AM == A_BF16) return *(const bf16x8_t*)(g.A + (size_t)row * g.lda + col);
-  const float4 x0 = *(const float4*)(g.X + (size_t)row * g.Kd + col);
-  const float4 x1 = *(const float4*)(g.X + (size_t)row * g.Kd + col + 4);
-  const bf16x8_t gg = *(const bf16x8_t*)(g.gain + col);
-  const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-  bf16x8_t v;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = (short)f32_to_bf16(xs[e] * bf16_to_f32((bf16_t)gg[e]));
-  return v;
-}
-
 template <int MT, int NW, int NT, int AM, int EP>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
   constexpr int KP = NW / NT;            // k parts
-  constexpr bool STAGE = KP == 1;        // every wave covers the same k range: share A through LDS
   constexpr int KC = KChunk<MT>::value;  // k-steps loaded per round
+  constexpr int NTH = NW * 64;
   __shared__ float s_red[NW * MT * 256];
-  __shared__ bf16x8_t sA[STAGE ? MT * KC * 64 : 1];
   __shared__ float s_inv[MT * 16];
 
-  const int M = g.M, Kd = g.Kd, N = g.N, Ks = g.Ks;
+  const int M = g.M, N = g.N, Ks = g.Ks;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int tl = wave % NT, kp = wave / NT;
   const int nt = blockIdx.x * NT + tl;
-  const bool active = nt < g.Nt;
+  const int ntc = min(nt, g.Nt - 1);  // clamped tile: a wave past the last tile streams a valid one, unused
   const int m0 = blockIdx.y * MT * 16;
   const int kps = (Ks + KP - 1) / KP;
   const int s_begin = kp * kps;
   const int s_end = min(Ks, s_begin + kps);
+  const int nrows = min(MT * 16, M - m0);
 
   f32x4_t acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const bf16x8_t* wsrc = (const bf16x8_t*)g.Wp_raw + (size_t)(active ? nt : 0) * Ks * 64 + lane;
-  const bf16x8_t zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+  const bf16x8_t* wsrc = (const bf16x8_t*)g.Wp_raw + (size_t)ntc * Ks * 64 + lane;
 
-  // Side inputs of the epilogue, loaded before the weight stream so that their latency overlaps it:
-  // the wave's first row of 1/RMS partials, this thread's first residual element, its first row's
-  // sequence position and slot, its first ROWS-epilogue token.
-  const int nrows = min(MT * 16, M - m0);
-  constexpr int NTH = NW * 64;
-  float pre_ssq[4] = {0.f, 0.f, 0.f, 0.f};
-  if (AM == A_NORM && wave < nrows) {
-    const float* src = g.ssq_in + (size_t)(m0 + wave) * g.nssq;
+  // Main loop, KC k-steps per round. Every load is unconditional (addresses clamped into range; rows >= M
+  // and k-steps past the split are computed but never used), so the weight loads of a round are all in
+  // flight before the first MFMA waits. The first round is peeled so that its loads are issued before
+  // anything else in the kernel.
+  // A through a raw buffer descriptor: lanes of padding rows (row >= M) use an out-of-range offset, which
+  // returns zeros without any memory request, so only real rows cost bandwidth.
+  const __amdgpu_buffer_rsrc_t a_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, M * g.lda * 2, 0x00020000);
+  bf16x8_t a[KC][MT], b[KC];
+  auto load_round = [&](int c0) {
+    const int nk = max(1, min(KC, s_end - c0));
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i < g.nssq) pre_ssq[i] = src[lane + 64 * i];
-  }
-  float pre_x = 0.f;
-  if (EP == EPI_RESID && (int)threadIdx.x < nrows * 16 && nt * 16 + (threadIdx.x & 15) < N)
-    pre_x = g.Xout[(size_t)(m0 + (threadIdx.x >> 4)) * N + nt * 16 + (threadIdx.x & 15)];
-  int pre_seq = 0, pre_slot = 0;
-  if (EP == EPI_QKV && (int)threadIdx.x < nrows * 8) {
-    const int b = (m0 + (threadIdx.x >> 3)) / g.Kdraft;
-    pre_seq = g.seq_len[b];
-    pre_slot = g.req_slot[b];
-  }
-  int pre_tok = 0;
-  if (EP == EPI_ROWS && (int)threadIdx.x < nrows * 16) pre_tok = g.last_token[m0 + (threadIdx.x >> 4)];
-
-  for (int c0 = s_begin; c0 < s_end; c0 += KC) {
-    const int nk = min(KC, s_end - c0);
-    bf16x8_t b[KC];
+    for (int kk = 0; kk < KC; ++kk) {
+      const int ks = min(c0 + min(kk, nk - 1), Ks - 1);
 #pragma unroll
-    for (int kk = 0; kk < KC; ++kk) b[kk] = (active && kk < nk) ? wsrc[(size_t)(c0 + kk) * 64] : zero8;
-    if (STAGE) {
-      for (int p = threadIdx.x; p < MT * KC * 64; p += NW * 64) {
-        const int ln = p & 63, kk = (p >> 6) % KC, mt = (p >> 6) / KC;
-        const int row = m0 + mt * 16 + (ln & 15);
-        const int col = (c0 + kk) * 32 + 8 * (ln >> 4);
-        sA[p] = (kk < nk && row < M && col < Kd) ? load_a<AM>(g, row, col) : zero8;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int kk = 0; kk < KC; ++kk) {
-        if (kk < nk) {
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sA[(mt * KC + kk) * 64 + lane], b[kk], acc[mt], 0, 0, 0);
-        }
-      }
-      __syncthreads();
-    } else {
-      bf16x8_t a[KC][MT];
-#pragma unroll
-      for (int kk = 0; kk < KC; ++kk) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const int row = m0 + mt * 16 + (lane & 15);
-          const int col = (c0 + kk) * 32 + 8 * (lane >> 4);
-          a[kk][mt] = (kk < nk && row < M && col < Kd) ? load_a<AM>(g, row, col) : zero8;
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < KC; ++kk) {
-        if (kk < nk) {
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk][mt], b[kk], acc[mt], 0, 0, 0);
-        }
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = m0 + mt * 16 + (lane & 15);
+        const int off = row < M ? (row * g.lda + ks * 32 + 8 * (lane >> 4)) * 2 : 0x7ffffff0;
+        a[kk][mt] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0));
       }
     }
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) b[kk] = wsrc[(size_t)min(c0 + min(kk, nk - 1), Ks - 1) * 64];
+  };
+  auto mma_round = [&](int c0) {
+    const int nk = min(KC, s_end - c0);
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) {
+      if (kk < nk) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk][mt], b[kk], acc[mt], 0, 0, 0);
+      }
+    }
+  };
+  load_round(s_begin);
+
+  // Side inputs of the epilogue, issued right after the first weight round so that their latency overlaps it.
+  // Loads are unconditional, with indices clamped into range (values that are not needed are ignored),
+  // so that no branch forces the weight loads to wait for them.
+  float pre_ssq[4] = {0.f, 0.f, 0.f, 0.f};
+  if (AM == A_NORM) {
+    const float* src = g.ssq_in + (size_t)(m0 + min(wave, nrows - 1)) * g.nssq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pre_ssq[i] = src[min(lane + 64 * i, g.nssq - 1)];  // masked when used
+  }
+  const int pr16 = min((int)threadIdx.x >> 4, nrows - 1);  // first epilogue row of a 16-wide epilogue
+  const int pr8 = min((int)threadIdx.x >> 3, nrows - 1);   // ... of an 8-wide epilogue
+  float pre_x = 0.f;
+  if (EP == EPI_RESID) pre_x = g.Xout[(size_t)(m0 + pr16) * N + min(ntc * 16 + (int)(threadIdx.x & 15), N - 1)];
+  int pre_seq = 0, pre_slot = 0;  // raw values; arithmetic on them waits until the epilogue
+  if (EP == EPI_QKV) {
+    pre_seq = g.seq_len[(m0 + pr8) / g.Kdraft];
+    pre_slot = g.req_slot[(m0 + pr8) / g.Kdraft];
+  }
+  int pre_tok = 0;
+  if (EP == EPI_ROWS) pre_tok = g.last_token[m0 + pr16];
+
+  mma_round(s_begin);
+  for (int c0 = s_begin + KC; c0 < s_end; c0 += KC) {
+    load_round(c0);
+    mma_round(c0);
   }
 
   if (AM == A_NORM) {
-    // 1 / RMS of each row of X from the per-16-column partial sums of squares: one wave per row, all
+    // 1 / RMS of each row of x from the per-16-column partial sums of squares: one wave per row, all
     // partials loaded at once (the first row's were prefetched), fixed reduction order
     for (int r = wave; r < nrows; r += NW) {
       const float* src = g.ssq_in + (size_t)(m0 + r) * g.nssq;
       float t = 0.f;
       if (r == wave) {
-        t = (pre_ssq[0] + pre_ssq[1]) + (pre_ssq[2] + pre_ssq[3]);
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = lane + 64 * i < g.nssq ? pre_ssq[i] : 0.f;
+        t = (v[0] + v[1]) + (v[2] + v[3]);
         for (int i = lane + 256; i < g.nssq; i += 64) t += src[i];
       } else {
         for (int i = lane; i < g.nssq; i += 64) t += src[i];
       }
       t = wave_sum(t);
-      if (lane == 0) s_inv[r] = rsqrtf(t / (float)Kd + g.eps);
+      if (lane == 0) s_inv[r] = rsqrtf(t / (float)g.Kd + g.eps);
     }
   }
 
@@ -233,7 +218,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
       s_red[((kp * NT + tl) * MT + mt) * 256 + (4 * (lane >> 4) + r) * 16 + (lane & 15)] = acc[mt][r];
   __syncthreads();
   if (KP > 1) {
-    for (int idx = threadIdx.x; idx < NT * MT * 256; idx += NW * 64) {
+    for (int idx = threadIdx.x; idx < NT * MT * 256; idx += NTH) {
       float v = s_red[idx];
 #pragma unroll
       for (int q = 1; q < KP; ++q) v += s_red[q * NT * MT * 256 + idx];
@@ -265,7 +250,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
       }
     }
   } else if (EP == EPI_RESID) {
-    // X[m][n] += y; per-row sum of squares of the new X over this tile
+    // X[m][n] += y; XG = bf16(X * gain_next); per-row sum of squares of the new X over this tile
     for (int idx = threadIdx.x; idx < rows * 16; idx += NTH) {
       const int r = idx >> 4, c = idx & 15;
       const int m = m0 + r, n = nt * 16 + c;
@@ -273,6 +258,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
       if (n < N) {
         v = (idx == (int)threadIdx.x ? pre_x : g.Xout[(size_t)m * N + n]) + Y(0, r, c);
         g.Xout[(size_t)m * N + n] = v;
+        g.XGout[(size_t)m * N + n] = f32_to_bf16(v * bf16_to_f32(g.gain_next[n]));
       }
       float sq = v * v;
       for (int off = 8; off > 0; off >>= 1) sq += __shfl_xor(sq, off, PE_WAVE);
@@ -284,15 +270,23 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
     for (int idx = threadIdx.x; idx < rows * 16; idx += NTH) {
       const int r = idx >> 4, c = idx & 15;
       const int b = m0 + r, n = nt * 16 + c;
-      const int tok = idx == (int)threadIdx.x ? pre_tok : g.last_token[b];
+      const bool first = idx == (int)threadIdx.x;
+      const int tok = first ? pre_tok : g.last_token[b];
       const bool tok_ok = tok >= 0 && tok < g.V;
       if (!tok_ok && c == 0) raise_flag(g.flags, PE_FLAG_TOKEN);
       float x0 = 0.f, ph = 0.f;
       if (n < N) {
-        x0 = Y(0, r, c) + (tok_ok ? bf16_to_f32(g.embed[(size_t)tok * N + n]) : 0.f);
+        const float e = tok_ok ? bf16_to_f32(g.embed[(size_t)tok * N + n]) : 0.f;
+        x0 = Y(0, r, c) + e;
         ph = bf16_to_f32(g.h_shared[n]) + bf16_to_f32(g.emb_mask[n]);
+        const float gn = bf16_to_f32(g.gain_next[n]);
         g.Xout[(size_t)(b * Kr) * N + n] = x0;
-        for (int j = 1; j < Kr; ++j) g.Xout[(size_t)(b * Kr + j) * N + n] = ph;
+        g.XGout[(size_t)(b * Kr) * N + n] = f32_to_bf16(x0 * gn);
+        const bf16_t phg = f32_to_bf16(ph * gn);
+        for (int j = 1; j < Kr; ++j) {
+          g.Xout[(size_t)(b * Kr + j) * N + n] = ph;
+          g.XGout[(size_t)(b * Kr + j) * N + n] = phg;
+        }
       }
       float s0 = x0 * x0, s1 = ph * ph;
       for (int off = 8; off > 0; off >>= 1) {
@@ -402,9 +396,11 @@ hipError_t launch_gemm(const GemmPlan& p, GemmArgs a, int a_mode, int epi, hipSt
   return hipErrorInvalidValue;
 }
 
-// X = caller rows; per-16-column sums of squares (the input of the first normalised projection)
+// X = caller rows; per-16-column sums of squares and XG = bf16(x * gain) (the operand of the first
+// normalised projection)
 __global__ __launch_bounds__(256) void rows_ssq_kernel(const float* __restrict__ rows, float* __restrict__ X,
-                                                       float* __restrict__ ssq, int d, int nssq) {
+                                                       float* __restrict__ ssq, bf16_t* __restrict__ XG,
+                                                       const bf16_t* __restrict__ gain, int d, int nssq) {
   const int m = blockIdx.x;
   for (int c0 = 0; c0 < nssq * 16; c0 += 256) {
     const int c = c0 + threadIdx.x;
@@ -412,6 +408,7 @@ __global__ __launch_bounds__(256) void rows_ssq_kernel(const float* __restrict__
     if (c < d) {
       v = rows[(size_t)m * d + c];
       X[(size_t)m * d + c] = v;
+      XG[(size_t)m * d + c] = f32_to_bf16(v * bf16_to_f32(gain[c]));
     }
     float sq = v * v;
     for (int off = 8; off > 0; off >>= 1) sq += __shfl_xor(sq, off, PE_WAVE);
@@ -419,8 +416,10 @@ __global__ __launch_bounds__(256) void rows_ssq_kernel(const float* __restrict__
   }
 }
 
-hipError_t launch_rows_ssq(const float* rows, float* X, float* ssq, int M, int d, hipStream_t st) {
-  hipLaunchKernelGGL(rows_ssq_kernel, dim3(M), dim3(256), 0, st, rows, X, ssq, d, (d + 15) / 16);
+hipError_t launch_rows_ssq(const float* rows, float* X, float* ssq, uint16_t* XG, const uint16_t* gain, int M, int d,
+                           hipStream_t st) {
+  hipLaunchKernelGGL(rows_ssq_kernel, dim3(M), dim3(256), 0, st, rows, X, ssq, (bf16_t*)XG, (const bf16_t*)gain, d,
+                     (d + 15) / 16);
   return hipGetLastError();
 }
 

@@ -30,18 +30,22 @@ struct GemmPlan {
 };
 GemmPlan plan_gemm(int M, int N, int Kd, bool argmax);
 
-enum { A_BF16 = 0, A_NORM = 1 };  // A operand: bf16 matrix, or RMSNorm(X) of the fp32 residual stream
+// A operand: always a bf16 matrix. A_NORM marks a normalised operand: A = bf16(x * g) of the residual stream
+// (written by the producer of x), and the epilogue scales each product row by 1/RMS(x) from the
+// producer's per-16-column sums of squares (RMSNorm is a per-row scale).
+enum { A_BF16 = 0, A_NORM = 1 };
 enum { EPI_RESID = 0, EPI_ROWS = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_ARGMAX = 4 };
 
 struct GemmArgs {
   int M, Kd, N;
   int Nt, Ks, ngroups;  // filled by launch_gemm from the plan
   // A operand
-  const uint16_t* A; int lda;                                        // A_BF16
-  const float* X; const float* ssq_in; int nssq; const uint16_t* gain; float eps;  // A_NORM
+  const uint16_t* A; int lda;
+  const float* ssq_in; int nssq; float eps;  // A_NORM
   const void* Wp_raw;  // packed weights
-  // EPI_RESID / EPI_ROWS: residual stream (+=, or rows written) and per-16-column sums of squares
-  float* Xout; float* ssq_out; int nssq_out;
+  // EPI_RESID / EPI_ROWS: residual stream (+=, or rows written), per-16-column sums of squares, and the
+  // next normalised operand XG = bf16(x * gain_next)
+  float* Xout; float* ssq_out; int nssq_out; uint16_t* XGout; const uint16_t* gain_next;
   // EPI_SWIGLU: A [M][F]
   uint16_t* Aout; int F;
   // EPI_QKV
@@ -54,7 +58,8 @@ struct GemmArgs {
   float* am_val; int* am_idx; float* logits;
 };
 hipError_t launch_gemm(const GemmPlan& p, GemmArgs a, int a_mode, int epi, hipStream_t st);
-hipError_t launch_rows_ssq(const float* rows, float* X, float* ssq, int M, int d, hipStream_t st);
+hipError_t launch_rows_ssq(const float* rows, float* X, float* ssq, uint16_t* XG, const uint16_t* gain, int M, int d,
+                           hipStream_t st);
 // fp32 weights, unpacked [N, Kd]: out[m * ldo + n]
 hipError_t launch_gemm_f32(const float* A, int lda, int M, int Kd, const float* W, int N, float* out, int ldo,
                            hipStream_t st);

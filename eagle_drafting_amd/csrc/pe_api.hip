@@ -389,9 +389,11 @@ static pe_status draft_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* re
   const int nssq = (d + 15) / 16;
   const pe_weights& w = ctx->w;
 
+  // XG = bf16(x * g) of the next normalised projection lives in the U buffer
+  uint16_t* XG = (uint16_t*)ctx->U;
   GemmArgs base{};
-  base.X = ctx->X;
   base.Xout = ctx->X;
+  base.XGout = XG;
   base.ssq_in = ctx->ssq;
   base.ssq_out = ctx->ssq;
   base.nssq = nssq;
@@ -407,15 +409,16 @@ static pe_status draft_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* re
     a.Wp_raw = ctx->p_fc;
     a.Kdraft = K; a.last_token = last_token; a.V = V;
     a.embed = (const uint16_t*)w.embed; a.emb_mask = (const uint16_t*)w.emb_mask; a.h_shared = (const uint16_t*)w.h_shared;
+    a.gain_next = (const uint16_t*)w.attn_norm[0];
     LAUNCH(launch_gemm(plan_gemm(B, d, 3 * d, false), a, A_BF16, EPI_ROWS, st));
   } else {
-    LAUNCH(launch_rows_ssq(rows, ctx->X, ctx->ssq, M, d, st));
+    LAUNCH(launch_rows_ssq(rows, ctx->X, ctx->ssq, XG, (const uint16_t*)w.attn_norm[0], M, d, st));
   }
   for (int l = 0; l < c.n_layers; ++l) {
     {  // a2-a4: RMSNorm, QKV, RoPE, KV append
       GemmArgs a = base;
       a.M = M; a.Kd = d; a.N = qkvd;
-      a.gain = (const uint16_t*)w.attn_norm[l];
+      a.A = XG; a.lda = d;
       a.Wp_raw = ctx->p_qkv[l];
       a.Q = (uint16_t*)ctx->Qb; a.Kc = (uint16_t*)ctx->kv.k[l]; a.Vc = (uint16_t*)ctx->kv.v[l];
       a.seq_len = seq_len; a.req_slot = req_slot; a.rope = ctx->rope;
@@ -434,13 +437,14 @@ static pe_status draft_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* re
       GemmArgs a = base;
       a.M = M; a.Kd = qd; a.N = d;
       a.A = (const uint16_t*)ctx->Ob; a.lda = qd;
+      a.gain_next = (const uint16_t*)w.mlp_norm[l];
       a.Wp_raw = ctx->p_o[l];
       LAUNCH(launch_gemm(plan_gemm(M, d, qd, false), a, A_BF16, EPI_RESID, st));
     }
     {  // a7: RMSNorm, gate/up, SwiGLU
       GemmArgs a = base;
       a.M = M; a.Kd = d; a.N = 2 * F;
-      a.gain = (const uint16_t*)w.mlp_norm[l];
+      a.A = XG; a.lda = d;
       a.Wp_raw = ctx->p_gu[l];
       a.Aout = (uint16_t*)ctx->Ab;
       a.F = F;
@@ -452,6 +456,7 @@ static pe_status draft_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* re
       GemmArgs a = base;
       a.M = M; a.Kd = F; a.N = d;
       a.A = (const uint16_t*)ctx->Ab; a.lda = F;
+      a.gain_next = (const uint16_t*)(l + 1 < c.n_layers ? w.attn_norm[l + 1] : w.final_norm);
       a.Wp_raw = ctx->p_down[l];
       LAUNCH(launch_gemm(plan_gemm(M, d, F, false), a, A_BF16, EPI_RESID, st));
     }
@@ -459,7 +464,7 @@ static pe_status draft_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* re
   // a9-a10: final RMSNorm, LM head, argmax
   GemmArgs a = base;
   a.M = M; a.Kd = d; a.N = V;
-  a.gain = (const uint16_t*)w.final_norm;
+  a.A = XG; a.lda = d;
   a.Wp_raw = ctx->p_lm;
   a.am_val = ctx->am_val; a.am_idx = ctx->am_idx; a.logits = logits;
   GemmPlan p = plan_gemm(M, V, d, true);
