@@ -8,9 +8,12 @@
 // kv head form the MFMA column operand, so every staged key/value tile is used by all of them: scores are
 // computed transposed, S^T = K_tile . Q^T (keys x rows), which leaves each lane owning one query row —
 // the same row ownership as O^T = V^T . P^T — so the online-softmax rescaling needs no lane exchange
-// beyond two xor-shuffles for the per-row max and sum. K and V tiles are staged through LDS with 16-byte
-// coalesced loads. Each (split, sub-stream) writes an unnormalised partial (O, m, l); a second kernel
-// merges them in a fixed order (log-sum-exp), so results are independent of scheduling.
+// beyond two xor-shuffles for the per-row max and sum. Key/value rounds are loaded into registers one
+// round ahead of the round being multiplied (coalesced 16-byte loads), then staged in LDS: keys in the
+// order the score tiles use (so that each lane's eight probabilities are eight consecutive keys), values
+// transposed (dimension-major), so the V^T operand is one 16-byte LDS read per lane. Each (split,
+// sub-stream) writes an unnormalised partial (O, m, l); a second kernel merges them in a fixed order
+// (log-sum-exp), so results are independent of scheduling.
 #include "common.h"
 #include "kernels.h"
 
@@ -23,14 +26,17 @@ static inline int attn_sub_streams(int R) {
   return RT == 1 ? 4 : RT == 2 ? 2 : 1;
 }
 
-AttnPlan plan_attention(int B, int K, int Hq, int Hkv, int max_ctx) {
+static inline int attn_round_keys(int hd) { return hd == 128 ? 64 : 128; }
+
+AttnPlan plan_attention(int B, int K, int Hq, int Hkv, int hd, int max_ctx) {
   AttnPlan p;
   const int R = (Hq / Hkv) * K;
+  const int KEYS = attn_round_keys(hd);
   p.sub = attn_sub_streams(R);
-  // aim for ~1024 workgroups at full context; chunks are whole 128-key staging rounds
+  // aim for ~1024 workgroups at full context; chunks are whole staging rounds
   long long want = (long long)B * Hkv * (long long)(max_ctx + K) / 1024;
-  int chunk = (int)((want + 127) / 128) * 128;
-  if (chunk < 128) chunk = 128;
+  int chunk = (int)((want + KEYS - 1) / KEYS) * KEYS;
+  if (chunk < KEYS) chunk = KEYS;
   if (chunk > 4096) chunk = 4096;
   while ((long long)((max_ctx + K + chunk - 1) / chunk) * p.sub > ATTN_MAX_PARTIALS) chunk *= 2;
   p.chunk = chunk;
@@ -42,7 +48,8 @@ size_t attn_partial_floats(int M, int Hq, int hd, const AttnPlan& p) {
   return (size_t)M * Hq * p.nsplit * p.sub * (hd + 2);
 }
 
-template <int HD>
+// NR: row tiles per wave (1, or 2 when more than 64 query rows share a kv head)
+template <int HD, int NR>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc,
                                                         const bf16_t* __restrict__ Vc,
                                                         const int* __restrict__ seq_len,
@@ -50,13 +57,17 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
                                                         int max_ctx, int n_slots, int chunk, int nsplit, int sub,
                                                         float* __restrict__ part, float scale) {
   constexpr int KT = 32;                      // keys per MFMA key tile
-  constexpr int NKT = HD == 128 ? 2 : 4;      // key tiles staged per round
-  constexpr int KEYS = KT * NKT;              // keys staged per round
-  constexpr int STR = HD + 8;                 // LDS row stride (elements), 16 B of padding
+  constexpr int KEYS = HD == 128 ? 64 : 128;  // keys staged per round (16 KiB of K and of V)
+  constexpr int NKT = KEYS / KT;              // key tiles per round
+  constexpr int STR = HD + 8;                 // sK row stride (elements), 16 B of padding
+  constexpr int VSTR = KEYS + 8;              // sVt row stride (elements)
   constexpr int HS = HD / 32;                 // k-steps of the score contraction
   constexpr int CT = HD / 16;                 // 16-column tiles of the output
+  constexpr int C8 = HD / 8;                  // 16-byte pieces per key row
+  // sK row of key k within a round: key 32 a' + 8 a + 4 h + r sits at row 32 a' + 16 h + 4 a + r, so score
+  // tile h's MFMA row 4 a + r is key 8 a + 4 h + r
   __shared__ __attribute__((aligned(16))) bf16_t sK[KEYS * STR];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[KEYS * STR];
+  __shared__ __attribute__((aligned(16))) bf16_t sVt[HD * VSTR];  // [dim][key]
 
   const int b = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
   const int split = blockIdx.y;
@@ -68,7 +79,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
   if (k_begin >= Lk) return;
   const int k_end = min(Lk, k_begin + chunk);
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lq = lane >> 4;
   int rt0, nrt, ks_id;
   if (sub > 1) {  // RT * sub == 4: waves share row tiles and take alternate key tiles
@@ -77,16 +88,48 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
     ks_id = wave / RT;
   } else {  // rows spread over waves (row tiles w and w + 4)
     rt0 = wave;
-    nrt = (wave < RT ? 1 : 0) + (wave + 4 < RT ? 1 : 0);
+    nrt = (wave < RT ? 1 : 0) + (NR > 1 && wave + 4 < RT ? 1 : 0);
     ks_id = 0;
   }
 
-  const bf16x8_t zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-  bf16x8_t qf[2][HS];
-  f32x4_t o[2][CT];
-  float m_run[2], l_run[2];
+  const size_t head_off = ((size_t)slot * Hkv + g) * max_ctx * HD;
+  const bf16_t* kb = Kc + head_off;
+  const bf16_t* vb = Vc + head_off;
+
+  // staging: this thread moves keys 4 kq .. 4 kq + 3, dimensions 8 c8 .. 8 c8 + 7 of each round. Keys past
+  // k_end are clamped to the last valid key (finite values; their scores are masked out).
+  const int kq = tid / C8, c8 = tid % C8;
+  bf16x8_t rk[4], rv[4];
+  auto gload = [&](int base) {
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+    for (int q = 0; q < 4; ++q) {
+      const int kp = min(base + 4 * kq + q, k_end - 1);
+      rk[q] = *(const bf16x8_t*)(kb + (size_t)kp * HD + 8 * c8);
+      rv[q] = *(const bf16x8_t*)(vb + (size_t)kp * HD + 8 * c8);
+    }
+  };
+  auto sstore = [&]() {
+    const int kk = kq & 7;  // 4 kq = 32 a' + 8 a + 4 h  with a' = kq / 8, a = kk / 2, h = kk % 2
+    const int row0 = (kq >> 3) * 32 + (kk & 1) * 16 + 4 * (kk >> 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *(bf16x8_t*)(sK + (row0 + q) * STR + 8 * c8) = rk[q];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint2 w;
+      w.x = (uint32_t)(uint16_t)rv[0][e] | ((uint32_t)(uint16_t)rv[1][e] << 16);
+      w.y = (uint32_t)(uint16_t)rv[2][e] | ((uint32_t)(uint16_t)rv[3][e] << 16);
+      *(uint2*)(sVt + (8 * c8 + e) * VSTR + 4 * kq) = w;
+    }
+  };
+
+  gload(k_begin);
+
+  const bf16x8_t zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+  bf16x8_t qf[NR][HS];
+  f32x4_t o[NR][CT];
+  float m_run[NR], l_run[NR];
+#pragma unroll
+  for (int t = 0; t < NR; ++t) {
     m_run[t] = -1e30f;
     l_run[t] = 0.f;
 #pragma unroll
@@ -104,33 +147,20 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
     }
   }
 
-  const size_t head_off = ((size_t)slot * Hkv + g) * max_ctx * HD;
-  const bf16_t* kb = Kc + head_off;
-  const bf16_t* vb = Vc + head_off;
-
   for (int base = k_begin; base < k_end; base += KEYS) {
-    constexpr int PIECES = KEYS * HD / 8;
-    for (int p = threadIdx.x; p < PIECES; p += 256) {
-      const int key = p / (HD / 8), c8 = p % (HD / 8);
-      const int kp = base + key;
-      bf16x8_t kv = zero8, vv = zero8;
-      if (kp < k_end) {
-        kv = *(const bf16x8_t*)(kb + (size_t)kp * HD + 8 * c8);
-        vv = *(const bf16x8_t*)(vb + (size_t)kp * HD + 8 * c8);
-      }
-      *(bf16x8_t*)(sK + key * STR + 8 * c8) = kv;
-      *(bf16x8_t*)(sV + key * STR + 8 * c8) = vv;
-    }
+    if (base != k_begin) __syncthreads();  // every wave is done with the previous round's tiles
+    sstore();
     __syncthreads();
+    if (base + KEYS < k_end) gload(base + KEYS);
     if (nrt > 0) {
       for (int kt = 0; kt < NKT; ++kt) {
         const int tb = base + kt * KT;
         if (tb >= k_end) break;
         if (sub > 1 && (((tb - k_begin) / KT) % sub) != ks_id) continue;
-        bf16x8_t pf[2];
-        float alpha[2];
+        bf16x8_t pf[NR];
+        float alpha[NR];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < NR; ++t) {
           pf[t] = zero8;
           alpha[t] = 1.f;
           if (t >= nrt) continue;
@@ -148,7 +178,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
           float tmax = -INFINITY;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int k0 = tb + 4 * lq + r, k1 = tb + 16 + 4 * lq + r;
+            const int k0 = tb + 8 * lq + r, k1 = k0 + 4;  // keys of score rows 4 lq + r of tiles 0 and 1
             sv[r] = k0 < lim ? s0[r] * scale : -INFINITY;
             sv[4 + r] = k1 < lim ? s1[r] * scale : -INFINITY;
             tmax = fmaxf(tmax, fmaxf(sv[r], sv[4 + r]));
@@ -159,7 +189,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
           alpha[t] = __expf(m_run[t] - mnew);
           float psum = 0.f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
+          for (int e = 0; e < 8; ++e) {  // pf element e: key tb + 8 lq + e
             const float pe = __expf(sv[e] - mnew);
             psum += pe;
             pf[t][e] = (short)f32_to_bf16(pe);
@@ -171,14 +201,9 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
         }
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-          bf16x8_t va;
+          const bf16x8_t va = *(const bf16x8_t*)(sVt + (ct * 16 + lr) * VSTR + kt * KT + 8 * lq);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            va[e] = (short)sV[(kt * KT + 4 * lq + e) * STR + ct * 16 + lr];
-            va[4 + e] = (short)sV[(kt * KT + 16 + 4 * lq + e) * STR + ct * 16 + lr];
-          }
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
+          for (int t = 0; t < NR; ++t) {
             if (t >= nrt) continue;
             f32x4_t acc = o[t][ct];
 #pragma unroll
@@ -188,12 +213,11 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
         }
       }
     }
-    __syncthreads();
   }
 
   const int nsub = nsplit * sub;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < NR; ++t) {
     if (t >= nrt) continue;
     const int row = (rt0 + 4 * t) * 16 + lr;
     if (row >= R) continue;
@@ -211,7 +235,6 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
   }
 }
 
-// O[b*K + j][h] = sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s over the splits that hold keys
 template <int HD>
 __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restrict__ part, bf16_t* __restrict__ O,
                                                           const int* __restrict__ seq_len,
@@ -227,21 +250,23 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restric
     return;
   }
   __shared__ float sw[ATTN_MAX_PARTIALS];
+  __shared__ float sl[ATTN_MAX_PARTIALS];
   const int ns = ((L + K + chunk - 1) / chunk) * sub;
   const float* src = part + (size_t)rid * nsplit * sub * (HD + 2);
-  // all (m_s, l_s) in parallel: one load per lane, then wave reductions
+  // all (m_s, l_s) in parallel: one load of each per lane, then wave reductions
   float M = -1e30f;
   for (int s = threadIdx.x; s < ns; s += 64) {
     const float m = src[(size_t)s * (HD + 2) + HD];
+    sl[s] = src[(size_t)s * (HD + 2) + HD + 1];
     sw[s] = m;
     M = fmaxf(M, m);
   }
   M = wave_max(M);
   float den = 0.f;
-  for (int s = threadIdx.x; s < ns; s += 64) {
+  for (int s = threadIdx.x; s < ns; s += 64) {  // the entries this thread wrote
     const float w = __expf(sw[s] - M);
     sw[s] = w;
-    den += w * src[(size_t)s * (HD + 2) + HD + 1];
+    den += w * sl[s];
   }
   den = wave_sum(den);
   __syncthreads();
@@ -261,14 +286,19 @@ hipError_t launch_attention_bf16(const AttnPlan& p, const void* Q, const void* K
                                  int max_ctx, int n_slots, float* part, hipStream_t st) {
   dim3 grid(B * Hkv, p.nsplit), block(256);
   const float scale = 1.0f / sqrtf((float)hd);
-  if (hd == 128)
-    hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, block, 0, st, (const bf16_t*)Q, (const bf16_t*)Kc,
-                       (const bf16_t*)Vc, seq_len, req_slot, K, Hq, Hkv, max_ctx, n_slots, p.chunk, p.nsplit, p.sub,
-                       part, scale);
-  else
-    hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, block, 0, st, (const bf16_t*)Q, (const bf16_t*)Kc,
-                       (const bf16_t*)Vc, seq_len, req_slot, K, Hq, Hkv, max_ctx, n_slots, p.chunk, p.nsplit, p.sub,
-                       part, scale);
+  const bool two = (Hq / Hkv) * K > 64;
+#define PE_ATTN_LAUNCH(HDV, NRV)                                                                              \
+  hipLaunchKernelGGL((attn_bf16_kernel<HDV, NRV>), grid, block, 0, st, (const bf16_t*)Q, (const bf16_t*)Kc,     \
+                     (const bf16_t*)Vc, seq_len, req_slot, K, Hq, Hkv, max_ctx, n_slots, p.chunk, p.nsplit, p.sub, \
+                     part, scale)
+  if (hd == 128) {
+    if (two) PE_ATTN_LAUNCH(128, 2);
+    else PE_ATTN_LAUNCH(128, 1);
+  } else {
+    if (two) PE_ATTN_LAUNCH(64, 2);
+    else PE_ATTN_LAUNCH(64, 1);
+  }
+#undef PE_ATTN_LAUNCH
   return hipGetLastError();
 }
 

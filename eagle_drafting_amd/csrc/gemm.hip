@@ -75,6 +75,22 @@ GemmPlan plan_gemm(int M, int N, int Kd, bool argmax) {
   GemmPlan p;
   const int Ks = k_steps(Kd);
   p.Nt = n_tiles(N);
+  p.tiled = 0;
+  if (M > 32) {
+    // 128 x 128 tiles read each weight once per 128 rows and each activation once per 128 columns; used
+    // when they alone give at least one workgroup per compute unit (the LM head always does) or when the
+    // skinny kernel's re-reads of the activations (once per 16 columns) dominate
+    const int tg = (p.Nt + 7) / 8, tm = (M + 127) / 128;
+    if (argmax || tg * tm >= 256 || M >= 256) {
+      p.tiled = 1;
+      p.MT = 8;
+      p.NT = 8;
+      p.NW = 4;
+      p.mblocks = tm;
+      p.ngroups = tg;
+      return p;
+    }
+  }
   p.MT = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
   p.mblocks = (M + 16 * p.MT - 1) / (16 * p.MT);
   if (argmax) {
@@ -82,8 +98,6 @@ GemmPlan plan_gemm(int M, int N, int Kd, bool argmax) {
     p.NW = 4;
   } else {
     p.NT = 1;
-    // enough waves in flight (about 4096 in total) while each wave streams at least 8 k-steps;
-    // register budget caps NW by MT (LDS for the cross-wave sum is NW * MT KiB)
     // about one residency round of waves in total (~4096), each wave streaming at least 8 k-steps;
     // the register budget caps NW by MT (LDS for the cross-wave sum is NW * MT KiB)
     const int cap = p.MT == 1 ? 16 : p.MT == 2 ? 8 : 4;
@@ -378,6 +392,8 @@ hipError_t launch_gemm(const GemmPlan& p, GemmArgs a, int a_mode, int epi, hipSt
   a.Nt = p.Nt;
   a.Ks = k_steps(a.Kd);
   a.ngroups = p.ngroups;
+  a.mblocks = p.mblocks;
+  if (p.tiled) return launch_gemm_tiled(p, a, a_mode, epi, st);
   if (epi == EPI_ARGMAX) {
     if (a_mode != A_NORM || p.NT != 4 || p.NW != 4) return hipErrorInvalidValue;
     switch (p.MT) {

@@ -1,0 +1,317 @@
+// Projections for larger draft batches (M = B*K rows > 32): LDS-tiled bf16 MFMA GEMM with the same fused
+// epilogues as the small-batch kernel.
+//
+// Workgroup tile 128 rows x 128 columns, 4 waves in a 2 x 2 arrangement (each wave 64 x 64: 4 x 4 MFMA
+// tiles of v_mfma_f32_16x16x32_bf16). Each stage covers 64 of the reduction dimension; A (activations) and
+// B (packed weight fragments) of the next stage are loaded into registers while the current stage is
+// multiplied out of LDS, then stored into the other LDS buffer (double buffering, one barrier per stage).
+// LDS holds both operands in MFMA fragment order (1 KiB per 16 x 32 fragment), so every ds_read is a
+// contiguous, conflict-free 16 B per lane.
+//
+// Epilogue: the 128 x 128 fp32 product tile is written into the same 64 KiB of LDS (columns XOR-swizzled
+// by 16 per group of 4 rows, so the accumulator layout's stores hit distinct banks), then read back as
+// 16-byte row chunks: half a wave covers one 128-column row, so global reads and writes of the residual
+// stream, the caches and the logits are coalesced, and per-row reductions (sums of squares, argmax) are
+// 32-lane shuffles. Gate/up and RoPE pairs, which the weight repack put 8 columns apart, are read as two
+// chunks of the same row.
+#include "common.h"
+#include "kernels.h"
+
+namespace pe {
+
+template <int AM, int EP>
+__global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
+  constexpr int BM = 128, BN = 128;
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * 2 * 8 * 64 * 16];  // 64 KiB
+  __shared__ float s_inv[BM];
+  bf16x8_t(*As)[2][8][64] = (bf16x8_t(*)[2][8][64])smem;                      // [buffer][k-step][m-tile][lane]
+  bf16x8_t(*Bs)[2][8][64] = (bf16x8_t(*)[2][8][64])(smem + 2 * 2 * 8 * 64 * 16);  // [buffer][k-step][n-tile][lane]
+  float* Cs = (float*)smem;                                                  // [BM][BN], after the main loop
+
+  const int M = g.M, N = g.N, Ks = g.Ks, Nt = g.Nt;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  // Workgroup w runs on XCD w % 8 (round-robin dispatch). Each XCD takes every 8th column group and runs
+  // all row blocks of one column group back to back, so a weight tile is fetched from HBM once and its
+  // other row blocks hit that XCD's L2.
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int ng = (slot / g.mblocks) * 8 + xcd;
+  if (ng >= g.ngroups) return;
+  const int m0 = (slot % g.mblocks) * BM;
+  const int nt0 = ng * 8;
+  const int nstage = (Ks + 1) / 2;
+
+  const __amdgpu_buffer_rsrc_t a_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, M * g.lda * 2, 0x00020000);
+  const bf16x8_t* W = (const bf16x8_t*)g.Wp_raw;
+
+  // this thread's four 16-byte pieces of each operand per stage: p = tid + 256 q over [k-step][tile][lane]
+  bf16x8_t ra[4], rb[4];
+  auto gload = [&](int st) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int p = tid + 256 * q;
+      const int ks = p >> 9, t = (p >> 6) & 7, ln = p & 63;
+      const int kstep = min(2 * st + ks, Ks - 1);
+      const int row = m0 + 16 * t + (ln & 15);
+      const int off = row < M ? (row * g.lda + kstep * 32 + 8 * (ln >> 4)) * 2 : 0x7ffffff0;
+      ra[q] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0));
+      const int ntile = min(nt0 + t, Nt - 1);
+      rb[q] = W[((size_t)ntile * Ks + kstep) * 64 + ln];
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int p = tid + 256 * q;
+      const int ks = p >> 9, t = (p >> 6) & 7, ln = p & 63;
+      As[buf][ks][t][ln] = ra[q];
+      Bs[buf][ks][t][ln] = rb[q];
+    }
+  };
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int st = 0; st < nstage; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nstage) gload(st + 1);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (2 * st + ks < Ks) {
+        bf16x8_t af[4], bf[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[i] = As[buf][ks][wm * 4 + i][lane];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bf[j] = Bs[buf][ks][wn * 4 + j][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    if (st + 1 < nstage) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // product tile -> LDS. Lane l holds rows 4(l/16)+r of column l%16 of each 16 x 16 tile; the column of
+  // row R is stored at (col ^ 16 ((R >> 2) & 3)).
+  {
+    const int c = lane & 15, rq = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * (wm * 4 + i) + 4 * rq + r;
+          const int col = (16 * (wn * 4 + j) + c) ^ (rq << 4);
+          Cs[row * BN + col] = acc[i][j][r];
+        }
+  }
+  if (AM == A_NORM) {
+    // 1 / RMS per row from the producer's partial sums of squares (two threads per row)
+    const int r = tid >> 1, h = tid & 1;
+    float t = 0.f;
+    if (m0 + r < M) {
+      const float* src = g.ssq_in + (size_t)(m0 + r) * g.nssq;
+      for (int i = h; i < g.nssq; i += 2) t += src[i];
+    }
+    t += __shfl_xor(t, 1, PE_WAVE);
+    if (h == 0) s_inv[r] = rsqrtf(t / (float)g.Kd + g.eps);
+  }
+  __syncthreads();
+
+  // 4 consecutive columns [c0, c0 + 4) of local row rl, scaled by 1/RMS for a normalised operand
+  auto cload = [&](int rl, int c0) {
+    float4 v = *(const float4*)&Cs[rl * BN + (c0 ^ (((rl >> 2) & 3) << 4))];
+    if (AM == A_NORM) {
+      const float s = s_inv[rl];
+      v.x *= s; v.y *= s; v.z *= s; v.w *= s;
+    }
+    return v;
+  };
+  const int n0 = nt0 * 16;
+
+  if (EP == EPI_ARGMAX || EP == EPI_RESID || EP == EPI_ROWS) {
+    // half a wave per row: lane h (0..31) holds columns 4h..4h+3; 8 rows per pass
+    const int h = lane & 31;
+    const int c0 = 4 * h, n = n0 + c0;
+    for (int rl = 2 * wave + (lane >> 5); rl < BM; rl += 8) {
+      const int m = m0 + rl;
+      const float4 v = cload(rl, c0);
+      const float vv[4] = {v.x, v.y, v.z, v.w};
+      if (EP == EPI_ARGMAX) {
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < N && am_better(vv[e], n + e, bv, bi)) { bv = vv[e]; bi = n + e; }
+        if (g.logits && m < M) {
+          float* z = g.logits + (size_t)m * N;
+          if (n + 3 < N && (N & 3) == 0) *(float4*)(z + n) = v;
+          else
+            for (int e = 0; e < 4; ++e)
+              if (n + e < N) z[n + e] = vv[e];
+        }
+        am_wave_reduce(bv, bi, 32);
+        if (h == 0 && m < M) {
+          g.am_val[(size_t)m * g.ngroups + ng] = bv;
+          g.am_idx[(size_t)m * g.ngroups + ng] = bi;
+        }
+      } else {
+        float sq0 = 0.f, sq1 = 0.f;
+        if (m < M) {
+          float x[4], x1[4];
+          float gn[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) gn[e] = n + e < N ? bf16_to_f32(g.gain_next[n + e]) : 0.f;
+          if (EP == EPI_RESID) {
+            // X += y; XG = bf16(X * gain_next)
+            float* xr = g.Xout + (size_t)m * N;
+            const bool full = n + 3 < N && (N & 3) == 0;
+            if (full) {
+              const float4 o = *(const float4*)(xr + n);
+              x[0] = o.x + vv[0]; x[1] = o.y + vv[1]; x[2] = o.z + vv[2]; x[3] = o.w + vv[3];
+              *(float4*)(xr + n) = make_float4(x[0], x[1], x[2], x[3]);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                x[e] = n + e < N ? xr[n + e] + vv[e] : 0.f;
+                if (n + e < N) xr[n + e] = x[e];
+              }
+            }
+            bf16_t* xg = g.XGout + (size_t)m * N;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (n + e < N) xg[n + e] = f32_to_bf16(x[e] * gn[e]);
+              sq0 += x[e] * x[e];
+            }
+          } else {
+            // m is a request b: row 0 = fc . concat(h) + embed[last_token]; rows 1..K-1 = h_shared + emb_mask
+            const int Kr = g.Kdraft;
+            const int tok = g.last_token[m];
+            const bool tok_ok = tok >= 0 && tok < g.V;
+            if (!tok_ok && h == 0 && ng == 0) raise_flag(g.flags, PE_FLAG_TOKEN);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const bool ok = n + e < N;
+              x[e] = ok ? vv[e] + (tok_ok ? bf16_to_f32(g.embed[(size_t)tok * N + n + e]) : 0.f) : 0.f;
+              x1[e] = ok ? bf16_to_f32(g.h_shared[n + e]) + bf16_to_f32(g.emb_mask[n + e]) : 0.f;
+              sq0 += x[e] * x[e];
+              sq1 += x1[e] * x1[e];
+            }
+            for (int jj = 0; jj < Kr; ++jj) {
+              const float* src = jj == 0 ? x : x1;
+              float* xr = g.Xout + (size_t)(m * Kr + jj) * N;
+              bf16_t* xg = g.XGout + (size_t)(m * Kr + jj) * N;
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (n + e < N) {
+                  xr[n + e] = src[e];
+                  xg[n + e] = f32_to_bf16(src[e] * gn[e]);
+                }
+            }
+          }
+        }
+        // one partial sum of squares per row and 128-column workgroup tile
+        for (int off = 16; off > 0; off >>= 1) {
+          sq0 += __shfl_xor(sq0, off, PE_WAVE);
+          if (EP == EPI_ROWS) sq1 += __shfl_xor(sq1, off, PE_WAVE);
+        }
+        if (h == 0 && m < M) {
+          if (EP == EPI_RESID) {
+            g.ssq_out[(size_t)m * g.nssq_out + ng] = sq0;
+          } else {
+            const int Kr = g.Kdraft;
+            g.ssq_out[(size_t)(m * Kr) * g.nssq_out + ng] = sq0;
+            for (int jj = 1; jj < Kr; ++jj) g.ssq_out[(size_t)(m * Kr + jj) * g.nssq_out + ng] = sq1;
+          }
+        }
+      }
+    }
+    return;
+  }
+
+  // paired epilogues: within 16-column tile t, columns e and 8 + e (e < 8) form pair 8 (nt0 + t) + e.
+  // Sixteen threads per row, each taking 4 consecutive pairs (chunk ch: tile ch / 2, e0 = 4 (ch % 2)).
+  const int ch = tid & 15;
+  const int t = ch >> 1, e0 = 4 * (ch & 1);
+  const int nt = nt0 + t;
+  for (int rl = tid >> 4; rl < BM; rl += 16) {
+    const int m = m0 + rl;
+    if (m >= M || nt >= Nt) continue;
+    const float4 a4 = cload(rl, 16 * t + e0), b4 = cload(rl, 16 * t + 8 + e0);
+    const float x1[4] = {a4.x, a4.y, a4.z, a4.w}, x2[4] = {b4.x, b4.y, b4.z, b4.w};
+    if (EP == EPI_SWIGLU) {
+      // gate of f = 8 nt + e, up of the same f
+      const int f0 = 8 * nt + e0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (f0 + e < g.F) g.Aout[(size_t)m * g.F + f0 + e] = f32_to_bf16(x1[e] / (1.f + __expf(-x1[e])) * x2[e]);
+    } else if (EP == EPI_QKV) {
+      // the two halves of RoPE pair ip = 8 tt + e of head u
+      const int hd = g.hd, half = hd / 2, tph = hd / 16;
+      const int u = nt / tph, tt = nt % tph, ip0 = 8 * tt + e0;
+      const int b = m / g.Kdraft, jr = m % g.Kdraft;
+      const int pos = g.seq_len[b] + jr;
+      const int slot = g.req_slot[b];
+      const bool pos_ok = pos >= 0 && pos < g.max_ctx;
+      const bool slot_ok = slot >= 0 && slot < g.n_slots;
+      if (ch == 0 && ng == 0) {
+        if (!pos_ok) raise_flag(g.flags, PE_FLAG_POS);
+        if (!slot_ok) raise_flag(g.flags, PE_FLAG_SLOT);
+      }
+      bf16_t* dst;
+      bool rot = true;
+      if (u < g.Hq) {
+        dst = g.Q + ((size_t)m * g.Hq + u) * hd;
+      } else {
+        if (!(pos_ok && slot_ok)) continue;
+        const bool isv = u >= g.Hq + g.Hkv;
+        bf16_t* cache = isv ? g.Vc : g.Kc;
+        dst = cache + (((size_t)slot * g.Hkv + (u - g.Hq - (isv ? g.Hkv : 0))) * g.max_ctx + pos) * hd;
+        rot = !isv;
+      }
+      float y1[4], y2[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (rot) {
+          const float2 cs = g.rope[(size_t)(pos_ok ? pos : 0) * half + ip0 + e];
+          y1[e] = x1[e] * cs.x - x2[e] * cs.y;
+          y2[e] = x2[e] * cs.x + x1[e] * cs.y;
+        } else {
+          y1[e] = x1[e];
+          y2[e] = x2[e];
+        }
+      }
+      // 4 consecutive bf16 of each half (8-byte stores)
+      uint2 w1, w2;
+      w1.x = (uint32_t)f32_to_bf16(y1[0]) | ((uint32_t)f32_to_bf16(y1[1]) << 16);
+      w1.y = (uint32_t)f32_to_bf16(y1[2]) | ((uint32_t)f32_to_bf16(y1[3]) << 16);
+      w2.x = (uint32_t)f32_to_bf16(y2[0]) | ((uint32_t)f32_to_bf16(y2[1]) << 16);
+      w2.y = (uint32_t)f32_to_bf16(y2[2]) | ((uint32_t)f32_to_bf16(y2[3]) << 16);
+      *(uint2*)(dst + ip0) = w1;
+      *(uint2*)(dst + ip0 + half) = w2;
+    }
+  }
+}
+
+hipError_t launch_gemm_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st) {
+  dim3 grid(8 * ((p.ngroups + 7) / 8) * p.mblocks), block(256);
+  if (a_mode == A_BF16 && epi == EPI_RESID) hipLaunchKernelGGL((gemm_tiled_kernel<A_BF16, EPI_RESID>), grid, block, 0, st, a);
+  else if (a_mode == A_BF16 && epi == EPI_ROWS) hipLaunchKernelGGL((gemm_tiled_kernel<A_BF16, EPI_ROWS>), grid, block, 0, st, a);
+  else if (a_mode == A_NORM && epi == EPI_QKV) hipLaunchKernelGGL((gemm_tiled_kernel<A_NORM, EPI_QKV>), grid, block, 0, st, a);
+  else if (a_mode == A_NORM && epi == EPI_SWIGLU) hipLaunchKernelGGL((gemm_tiled_kernel<A_NORM, EPI_SWIGLU>), grid, block, 0, st, a);
+  else if (a_mode == A_NORM && epi == EPI_ARGMAX) hipLaunchKernelGGL((gemm_tiled_kernel<A_NORM, EPI_ARGMAX>), grid, block, 0, st, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace pe

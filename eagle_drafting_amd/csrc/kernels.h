@@ -27,8 +27,13 @@ struct GemmPlan {
   int NT;       // 16-column tiles per workgroup
   int NW;       // waves per workgroup (they split the reduction dimension NW/NT ways)
   int ngroups;  // workgroups along N
+  int tiled;    // 1: LDS-tiled 128 x 128 kernel (larger M); 0: skinny split-K kernel
 };
 GemmPlan plan_gemm(int M, int N, int Kd, bool argmax);
+// Partial sums of squares per row that a residual-stream producer with plan p writes (one per 16 columns
+// for the skinny kernel, one per 128-column workgroup tile for the tiled one); the consumer sums exactly
+// that many.
+inline int gemm_ssq_parts(const GemmPlan& p) { return p.tiled ? p.ngroups : p.Nt; }
 
 // A operand: always a bf16 matrix. A_NORM marks a normalised operand: A = bf16(x * g) of the residual stream
 // (written by the producer of x), and the epilogue scales each product row by 1/RMS(x) from the
@@ -38,7 +43,7 @@ enum { EPI_RESID = 0, EPI_ROWS = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_ARGMAX = 4 
 
 struct GemmArgs {
   int M, Kd, N;
-  int Nt, Ks, ngroups;  // filled by launch_gemm from the plan
+  int Nt, Ks, ngroups, mblocks;  // filled by launch_gemm from the plan
   // A operand
   const uint16_t* A; int lda;
   const float* ssq_in; int nssq; float eps;  // A_NORM
@@ -58,6 +63,7 @@ struct GemmArgs {
   float* am_val; int* am_idx; float* logits;
 };
 hipError_t launch_gemm(const GemmPlan& p, GemmArgs a, int a_mode, int epi, hipStream_t st);
+hipError_t launch_gemm_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st);
 hipError_t launch_rows_ssq(const float* rows, float* X, float* ssq, uint16_t* XG, const uint16_t* gain, int M, int d,
                            hipStream_t st);
 // fp32 weights, unpacked [N, Kd]: out[m * ldo + n]
@@ -84,7 +90,7 @@ struct AttnPlan {
   int nsplit;  // splits (grid y)
   int sub;     // key sub-streams per split inside a workgroup
 };
-AttnPlan plan_attention(int B, int K, int Hq, int Hkv, int max_ctx);
+AttnPlan plan_attention(int B, int K, int Hq, int Hkv, int hd, int max_ctx);
 size_t attn_partial_floats(int M, int Hq, int hd, const AttnPlan& p);
 hipError_t launch_attention_bf16(const AttnPlan& p, const void* Q, const void* Kc, const void* Vc,
                                  const int* seq_len, const int* req_slot, int B, int K, int Hq, int Hkv, int hd,

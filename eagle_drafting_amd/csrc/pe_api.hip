@@ -141,6 +141,9 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
     if (!w->attn_norm[l] || !w->wqkv[l] || !w->wo[l] || !w->mlp_norm[l] || !w->wgate[l] || !w->wup[l] ||
         !w->wdown[l] || !kv->k[l] || !kv->v[l])
       return fail(nullptr, PE_ERR_INVALID, "a per-layer weight or cache pointer is NULL");
+  for (int l = 0; l < c.n_layers; ++l)
+    if (((uintptr_t)kv->k[l] | (uintptr_t)kv->v[l]) & 15)
+      return fail(nullptr, PE_ERR_INVALID, "KV cache pointers must be 16-byte aligned");
 
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -219,7 +222,7 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
   for (int B = 1; B <= c.max_batch; ++B) {
     if (ctx->bf16) {
       for (int K = 1; K <= c.max_k; ++K) {
-        AttnPlan ap = plan_attention(B, K, c.n_q_heads, c.n_kv_heads, c.max_ctx);
+        AttnPlan ap = plan_attention(B, K, c.n_q_heads, c.n_kv_heads, hd, c.max_ctx);
         attn_floats = std::max(attn_floats, attn_partial_floats(B * K, c.n_q_heads, hd, ap));
       }
     } else {
@@ -386,8 +389,9 @@ static pe_status draft_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* re
   const int d = c.d_model, F = c.ffn_dim, V = c.vocab, hd = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
   const int qd = Hq * hd, qkvd = (Hq + 2 * Hkv) * hd;
   const int M = B * K;
-  const int nssq = (d + 15) / 16;
   const pe_weights& w = ctx->w;
+  // partial sums of squares per row written by the latest residual-stream producer
+  int nssq = (d + 15) / 16;
 
   // XG = bf16(x * g) of the next normalised projection lives in the U buffer
   uint16_t* XG = (uint16_t*)ctx->U;
@@ -396,8 +400,6 @@ static pe_status draft_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* re
   base.XGout = XG;
   base.ssq_in = ctx->ssq;
   base.ssq_out = ctx->ssq;
-  base.nssq = nssq;
-  base.nssq_out = nssq;
   base.eps = c.rms_eps;
   base.flags = ctx->flags;
 
@@ -410,7 +412,9 @@ static pe_status draft_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* re
     a.Kdraft = K; a.last_token = last_token; a.V = V;
     a.embed = (const uint16_t*)w.embed; a.emb_mask = (const uint16_t*)w.emb_mask; a.h_shared = (const uint16_t*)w.h_shared;
     a.gain_next = (const uint16_t*)w.attn_norm[0];
-    LAUNCH(launch_gemm(plan_gemm(B, d, 3 * d, false), a, A_BF16, EPI_ROWS, st));
+    const GemmPlan p = plan_gemm(B, d, 3 * d, false);
+    a.nssq_out = nssq = gemm_ssq_parts(p);
+    LAUNCH(launch_gemm(p, a, A_BF16, EPI_ROWS, st));
   } else {
     LAUNCH(launch_rows_ssq(rows, ctx->X, ctx->ssq, XG, (const uint16_t*)w.attn_norm[0], M, d, st));
   }
@@ -423,10 +427,11 @@ static pe_status draft_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* re
       a.Q = (uint16_t*)ctx->Qb; a.Kc = (uint16_t*)ctx->kv.k[l]; a.Vc = (uint16_t*)ctx->kv.v[l];
       a.seq_len = seq_len; a.req_slot = req_slot; a.rope = ctx->rope;
       a.Kdraft = K; a.Hq = Hq; a.Hkv = Hkv; a.hd = hd; a.max_ctx = c.max_ctx; a.n_slots = c.n_slots;
+      a.nssq = nssq;
       LAUNCH(launch_gemm(plan_gemm(M, qkvd, d, false), a, A_NORM, EPI_QKV, st));
     }
     // a5: attention
-    AttnPlan ap = plan_attention(B, K, Hq, Hkv, c.max_ctx);
+    AttnPlan ap = plan_attention(B, K, Hq, Hkv, hd, c.max_ctx);
     LAUNCH(prof_mark(ctx, PE_PROF_ATTENTION, true));
     LAUNCH(launch_attention_bf16(ap, ctx->Qb, ctx->kv.k[l], ctx->kv.v[l], seq_len, req_slot, B, K, Hq, Hkv, hd,
                                  c.max_ctx, c.n_slots, ctx->attn, st));
@@ -439,7 +444,9 @@ static pe_status draft_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* re
       a.A = (const uint16_t*)ctx->Ob; a.lda = qd;
       a.gain_next = (const uint16_t*)w.mlp_norm[l];
       a.Wp_raw = ctx->p_o[l];
-      LAUNCH(launch_gemm(plan_gemm(M, d, qd, false), a, A_BF16, EPI_RESID, st));
+      const GemmPlan p = plan_gemm(M, d, qd, false);
+      a.nssq_out = nssq = gemm_ssq_parts(p);
+      LAUNCH(launch_gemm(p, a, A_BF16, EPI_RESID, st));
     }
     {  // a7: RMSNorm, gate/up, SwiGLU
       GemmArgs a = base;
@@ -448,6 +455,7 @@ static pe_status draft_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* re
       a.Wp_raw = ctx->p_gu[l];
       a.Aout = (uint16_t*)ctx->Ab;
       a.F = F;
+      a.nssq = nssq;
       LAUNCH(prof_mark(ctx, PE_PROF_GATE_UP, true));
       LAUNCH(launch_gemm(plan_gemm(M, 2 * F, d, false), a, A_NORM, EPI_SWIGLU, st));
       LAUNCH(prof_mark(ctx, PE_PROF_GATE_UP, false));
@@ -458,7 +466,9 @@ static pe_status draft_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* re
       a.A = (const uint16_t*)ctx->Ab; a.lda = F;
       a.gain_next = (const uint16_t*)(l + 1 < c.n_layers ? w.attn_norm[l + 1] : w.final_norm);
       a.Wp_raw = ctx->p_down[l];
-      LAUNCH(launch_gemm(plan_gemm(M, d, F, false), a, A_BF16, EPI_RESID, st));
+      const GemmPlan p = plan_gemm(M, d, F, false);
+      a.nssq_out = nssq = gemm_ssq_parts(p);
+      LAUNCH(launch_gemm(p, a, A_BF16, EPI_RESID, st));
     }
   }
   // a9-a10: final RMSNorm, LM head, argmax
@@ -467,6 +477,7 @@ static pe_status draft_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* re
   a.A = XG; a.lda = d;
   a.Wp_raw = ctx->p_lm;
   a.am_val = ctx->am_val; a.am_idx = ctx->am_idx; a.logits = logits;
+  a.nssq = nssq;
   GemmPlan p = plan_gemm(M, V, d, true);
   LAUNCH(prof_mark(ctx, PE_PROF_LM_HEAD, true));
   LAUNCH(launch_gemm(p, a, A_NORM, EPI_ARGMAX, st));
@@ -485,6 +496,8 @@ static pe_status run_draft(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req
   if (!req_slot || !seq_len || !draft_tokens) return fail(ctx, PE_ERR_INVALID, "NULL request array");
   if (!rows && (!last_token || !target_hidden)) return fail(ctx, PE_ERR_INVALID, "NULL last_token / target_hidden");
   if (target_hidden && ((uintptr_t)target_hidden & 15)) return fail(ctx, PE_ERR_INVALID, "target_hidden not 16-byte aligned");
+  if (logits && ((uintptr_t)logits & 15)) return fail(ctx, PE_ERR_INVALID, "logits not 16-byte aligned");
+  if (rows && ((uintptr_t)rows & 15)) return fail(ctx, PE_ERR_INVALID, "rows not 16-byte aligned");
   if (ctx->bf16) return draft_bf16(ctx, B, K, req_slot, seq_len, last_token, target_hidden, rows, draft_tokens, logits);
   return draft_f32(ctx, B, K, req_slot, seq_len, last_token, target_hidden, rows, draft_tokens, logits);
 }

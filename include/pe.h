@@ -13,6 +13,8 @@
  *   - Pointers marked "device" point to GPU memory of the device that was current at pe_init; "host"
  *     pointers to CPU memory. The caller owns every buffer it passes; the library never frees them.
  *   - Matrices are row-major. A weight matrix W of a projection y = x . W^T is stored [out, in].
+ *   - Device arrays of activations, caches and logits (target_hidden, rows, logits, target_logits and
+ *     the KV cache) must be 16-byte aligned; calls reject other addresses with PE_ERR_INVALID.
  *   - Element type: pe_config.dtype (PE_F32 or PE_BF16) for weights, KV cache, target hiddens and target
  *     logits. Token ids, lengths and slots are int32. Logits written by the library are float32.
  *   - Calls enqueue work on the stream given to pe_init and return without waiting for the GPU.
