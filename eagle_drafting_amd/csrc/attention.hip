@@ -48,9 +48,10 @@ size_t attn_partial_floats(int M, int Hq, int hd, const AttnPlan& p) {
   return (size_t)M * Hq * p.nsplit * p.sub * (hd + 2);
 }
 
-// NR: row tiles per wave (1, or 2 when more than 64 query rows share a kv head)
-template <int HD, int NR>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc,
+// NW: waves per workgroup, 4 or (when more than 64 query rows share a kv head) 8; each wave owns one
+// 16-row tile of the kv head's query rows
+template <int HD, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc,
                                                         const bf16_t* __restrict__ Vc,
                                                         const int* __restrict__ seq_len,
                                                         const int* __restrict__ req_slot, int K, int Hq, int Hkv,
@@ -64,6 +65,8 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
   constexpr int HS = HD / 32;                 // k-steps of the score contraction
   constexpr int CT = HD / 16;                 // 16-column tiles of the output
   constexpr int C8 = HD / 8;                  // 16-byte pieces per key row
+  constexpr int PK = KEYS * C8 / (NW * 64);   // keys staged per thread per round (4 or 2)
+  constexpr int NR = 1;
   // sK row of key k within a round: key 32 a' + 8 a + 4 h + r sits at row 32 a' + 16 h + 4 a + r, so score
   // tile h's MFMA row 4 a + r is key 8 a + 4 h + r
   __shared__ __attribute__((aligned(16))) bf16_t sK[KEYS * STR];
@@ -82,13 +85,13 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lq = lane >> 4;
   int rt0, nrt, ks_id;
-  if (sub > 1) {  // RT * sub == 4: waves share row tiles and take alternate key tiles
+  if (sub > 1) {  // RT * sub == NW: waves share row tiles and take alternate key tiles
     rt0 = wave % RT;
     nrt = 1;
     ks_id = wave / RT;
-  } else {  // rows spread over waves (row tiles w and w + 4)
+  } else {  // wave w owns row tile w
     rt0 = wave;
-    nrt = (wave < RT ? 1 : 0) + (NR > 1 && wave + 4 < RT ? 1 : 0);
+    nrt = wave < RT ? 1 : 0;
     ks_id = 0;
   }
 
@@ -96,29 +99,37 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
   const bf16_t* kb = Kc + head_off;
   const bf16_t* vb = Vc + head_off;
 
-  // staging: this thread moves keys 4 kq .. 4 kq + 3, dimensions 8 c8 .. 8 c8 + 7 of each round. Keys past
-  // k_end are clamped to the last valid key (finite values; their scores are masked out).
+  // staging: this thread moves keys PK kq .. PK kq + PK - 1, dimensions 8 c8 .. 8 c8 + 7 of each round.
+  // Keys past k_end are clamped to the last valid key (finite values; their scores are masked out).
   const int kq = tid / C8, c8 = tid % C8;
-  bf16x8_t rk[4], rv[4];
+  bf16x8_t rk[PK], rv[PK];
   auto gload = [&](int base) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int kp = min(base + 4 * kq + q, k_end - 1);
+    for (int q = 0; q < PK; ++q) {
+      const int kp = min(base + PK * kq + q, k_end - 1);
       rk[q] = *(const bf16x8_t*)(kb + (size_t)kp * HD + 8 * c8);
       rv[q] = *(const bf16x8_t*)(vb + (size_t)kp * HD + 8 * c8);
     }
   };
   auto sstore = [&]() {
-    const int kk = kq & 7;  // 4 kq = 32 a' + 8 a + 4 h  with a' = kq / 8, a = kk / 2, h = kk % 2
-    const int row0 = (kq >> 3) * 32 + (kk & 1) * 16 + 4 * (kk >> 1);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) *(bf16x8_t*)(sK + (row0 + q) * STR + 8 * c8) = rk[q];
+    for (int q = 0; q < PK; ++q) {
+      const int k = PK * kq + q;  // k = 32 a' + 8 a + 4 h + r  ->  row 32 a' + 16 h + 4 a + r
+      const int row = (k >> 5) * 32 + ((k >> 2) & 1) * 16 + 4 * ((k >> 3) & 3) + (k & 3);
+      *(bf16x8_t*)(sK + row * STR + 8 * c8) = rk[q];
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      uint2 w;
-      w.x = (uint32_t)(uint16_t)rv[0][e] | ((uint32_t)(uint16_t)rv[1][e] << 16);
-      w.y = (uint32_t)(uint16_t)rv[2][e] | ((uint32_t)(uint16_t)rv[3][e] << 16);
-      *(uint2*)(sVt + (8 * c8 + e) * VSTR + 4 * kq) = w;
+      bf16_t* dst = sVt + (8 * c8 + e) * VSTR + PK * kq;
+      const uint32_t w0 = (uint32_t)(uint16_t)rv[0][e] | ((uint32_t)(uint16_t)rv[1][e] << 16);
+      if (PK == 4) {
+        uint2 w;
+        w.x = w0;
+        w.y = (uint32_t)(uint16_t)rv[PK - 2][e] | ((uint32_t)(uint16_t)rv[PK - 1][e] << 16);
+        *(uint2*)dst = w;
+      } else {
+        *(uint32_t*)dst = w0;
+      }
     }
   };
 
@@ -284,19 +295,19 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restric
 hipError_t launch_attention_bf16(const AttnPlan& p, const void* Q, const void* Kc, const void* Vc,
                                  const int* seq_len, const int* req_slot, int B, int K, int Hq, int Hkv, int hd,
                                  int max_ctx, int n_slots, float* part, hipStream_t st) {
-  dim3 grid(B * Hkv, p.nsplit), block(256);
+  dim3 grid(B * Hkv, p.nsplit);
   const float scale = 1.0f / sqrtf((float)hd);
-  const bool two = (Hq / Hkv) * K > 64;
-#define PE_ATTN_LAUNCH(HDV, NRV)                                                                              \
-  hipLaunchKernelGGL((attn_bf16_kernel<HDV, NRV>), grid, block, 0, st, (const bf16_t*)Q, (const bf16_t*)Kc,     \
-                     (const bf16_t*)Vc, seq_len, req_slot, K, Hq, Hkv, max_ctx, n_slots, p.chunk, p.nsplit, p.sub, \
+  const bool eight = (Hq / Hkv) * K > 64;
+#define PE_ATTN_LAUNCH(HDV, NWV)                                                                                   \
+  hipLaunchKernelGGL((attn_bf16_kernel<HDV, NWV>), grid, dim3(NWV * 64), 0, st, (const bf16_t*)Q, (const bf16_t*)Kc, \
+                     (const bf16_t*)Vc, seq_len, req_slot, K, Hq, Hkv, max_ctx, n_slots, p.chunk, p.nsplit, p.sub,  \
                      part, scale)
   if (hd == 128) {
-    if (two) PE_ATTN_LAUNCH(128, 2);
-    else PE_ATTN_LAUNCH(128, 1);
+    if (eight) PE_ATTN_LAUNCH(128, 8);
+    else PE_ATTN_LAUNCH(128, 4);
   } else {
-    if (two) PE_ATTN_LAUNCH(64, 2);
-    else PE_ATTN_LAUNCH(64, 1);
+    if (eight) PE_ATTN_LAUNCH(64, 8);
+    else PE_ATTN_LAUNCH(64, 4);
   }
 #undef PE_ATTN_LAUNCH
   return hipGetLastError();

@@ -7,6 +7,7 @@
 typedef uint16_t bf16_t;  // raw bfloat16 bits
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
 #define PE_WAVE 64
 

@@ -1,19 +1,18 @@
 // Projections for larger draft batches (M = B*K rows > 32): LDS-tiled bf16 MFMA GEMM with the same fused
 // epilogues as the small-batch kernel.
 //
-// Workgroup tile 128 rows x 128 columns, 4 waves in a 2 x 2 arrangement (each wave 64 x 64: 4 x 4 MFMA
-// tiles of v_mfma_f32_16x16x32_bf16). Each stage covers 64 of the reduction dimension; A (activations) and
-// B (packed weight fragments) of the next stage are loaded into registers while the current stage is
-// multiplied out of LDS, then stored into the other LDS buffer (double buffering, one barrier per stage).
-// LDS holds both operands in MFMA fragment order (1 KiB per 16 x 32 fragment), so every ds_read is a
-// contiguous, conflict-free 16 B per lane.
+// Workgroup tile 128 rows x 128 columns, 4 waves in a 2 x 2 arrangement (each wave 64 x 64: 2 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16, the bf16 MFMA with the highest sustained rate on gfx950). Each stage covers 64
+// of the reduction dimension. LDS holds both operands as 16 x 32 fragments (1 KiB each, the layout of the
+// packed weights), two buffers; global loads run two stages ahead in two register sets, so a load has two
+// stages of MFMA work to arrive in. Every ds_read is 16 B per lane and each 16-lane group reads 256
+// contiguous bytes.
 //
-// Epilogue: the 128 x 128 fp32 product tile is written into the same 64 KiB of LDS (columns XOR-swizzled
-// by 16 per group of 4 rows, so the accumulator layout's stores hit distinct banks), then read back as
-// 16-byte row chunks: half a wave covers one 128-column row, so global reads and writes of the residual
-// stream, the caches and the logits are coalesced, and per-row reductions (sums of squares, argmax) are
-// 32-lane shuffles. Gate/up and RoPE pairs, which the weight repack put 8 columns apart, are read as two
-// chunks of the same row.
+// Epilogue: the 128 x 128 fp32 product tile is written into the same 64 KiB of LDS (column XOR-swizzle so
+// the two lane halves of the accumulator layout hit distinct banks), then read back as 16-byte row chunks:
+// half a wave covers one 128-column row, so global reads and writes of the residual stream, the caches and
+// the logits are coalesced, and per-row reductions (sums of squares, argmax) are 32-lane shuffles. Gate/up
+// and RoPE pairs, which the weight repack put 8 columns apart, are read as two chunks of the same row.
 #include "common.h"
 #include "kernels.h"
 
@@ -45,9 +44,12 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
       __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, M * g.lda * 2, 0x00020000);
   const bf16x8_t* W = (const bf16x8_t*)g.Wp_raw;
 
-  // this thread's four 16-byte pieces of each operand per stage: p = tid + 256 q over [k-step][tile][lane]
-  bf16x8_t ra[4], rb[4];
-  auto gload = [&](int st) {
+  // this thread's four 16-byte pieces of each operand per stage: p = tid + 256 q over [k-step][tile][lane].
+  // Two register sets: the loads of stage s + 2 are in flight while stage s is multiplied and stage s + 1
+  // is stored into LDS.
+  typedef bf16x8_t Regs[8];  // [0..3] activations, [4..7] weights
+  Regs r0, r1;
+  auto gload = [&](Regs& r, int st) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int p = tid + 256 * q;
@@ -55,64 +57,84 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
       const int kstep = min(2 * st + ks, Ks - 1);
       const int row = m0 + 16 * t + (ln & 15);
       const int off = row < M ? (row * g.lda + kstep * 32 + 8 * (ln >> 4)) * 2 : 0x7ffffff0;
-      ra[q] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0));
+      r[q] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0));
       const int ntile = min(nt0 + t, Nt - 1);
-      rb[q] = W[((size_t)ntile * Ks + kstep) * 64 + ln];
+      r[4 + q] = W[((size_t)ntile * Ks + kstep) * 64 + ln];
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](const Regs& r, int buf) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int p = tid + 256 * q;
       const int ks = p >> 9, t = (p >> 6) & 7, ln = p & 63;
-      As[buf][ks][t][ln] = ra[q];
-      Bs[buf][ks][t][ln] = rb[q];
+      As[buf][ks][t][ln] = r[q];
+      Bs[buf][ks][t][ln] = r[4 + q];
     }
   };
 
-  f32x4_t acc[4][4];
+  // 32 x 32 x 16 products out of the 16 x 32 fragments: lane l of the operand of rows (or columns)
+  // 32 b .. 32 b + 31 and k-half u takes fragment 2 b + (l % 32) / 16, fragment lane l % 16 + 16 (2 u + l / 32)
+  const int fr_t = (lane & 31) >> 4, fr_l = (lane & 15) + 16 * (lane >> 5);
+  f32x16_t acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int st = 0; st < nstage; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nstage) gload(st + 1);
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  auto compute = [&](int buf, int st) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       if (2 * st + ks < Ks) {
-        bf16x8_t af[4], bf[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = As[buf][ks][wm * 4 + i][lane];
+        for (int u = 0; u < 2; ++u) {
+          bf16x8_t af[2], bf[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bf[j] = Bs[buf][ks][wn * 4 + j][lane];
+          for (int i = 0; i < 2; ++i) af[i] = As[buf][ks][wm * 4 + 2 * i + fr_t][fr_l + 32 * u];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+          for (int j = 0; j < 2; ++j) bf[j] = Bs[buf][ks][wn * 4 + 2 * j + fr_t][fr_l + 32 * u];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
       }
     }
-    if (st + 1 < nstage) sstore(buf ^ 1);
+  };
+
+  gload(r0, 0);
+  if (nstage > 1) gload(r1, 1);
+  sstore(r0, 0);
+  __syncthreads();
+  for (int st = 0; st < nstage; st += 2) {
+    // stage st is in buffer 0, stage st + 1 in r1
+    if (st + 2 < nstage) gload(r0, st + 2);
+    compute(0, st);
+    if (st + 1 < nstage) sstore(r1, 1);
+    __syncthreads();
+    if (st + 1 >= nstage) break;
+    // stage st + 1 is in buffer 1, stage st + 2 in r0
+    if (st + 3 < nstage) gload(r1, st + 3);
+    compute(1, st + 1);
+    if (st + 2 < nstage) sstore(r0, 0);
     __syncthreads();
   }
 
-  // product tile -> LDS. Lane l holds rows 4(l/16)+r of column l%16 of each 16 x 16 tile; the column of
-  // row R is stored at (col ^ 16 ((R >> 2) & 3)).
+  // product tile -> LDS. Lane l holds, for e = 0..15, row 8 (e / 4) + 4 (l / 32) + e % 4 of column l % 32 of
+  // each 32 x 32 block; the column of local row R is stored at col ^ swz(R), swz(R) = 32 ((R >> 2) & 1), so
+  // the two lane halves (rows 4 apart) write different banks.
   {
-    const int c = lane & 15, rq = lane >> 4;
+    const int c = lane & 31, hq = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * (wm * 4 + i) + 4 * rq + r;
-          const int col = (16 * (wn * 4 + j) + c) ^ (rq << 4);
-          Cs[row * BN + col] = acc[i][j][r];
+        for (int e = 0; e < 16; ++e) {
+          const int row = 64 * wm + 32 * i + 8 * (e >> 2) + 4 * hq + (e & 3);
+          const int col = (64 * wn + 32 * j + c) ^ (hq << 5);
+          Cs[row * BN + col] = acc[i][j][e];
         }
   }
   if (AM == A_NORM) {
@@ -130,7 +152,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
 
   // 4 consecutive columns [c0, c0 + 4) of local row rl, scaled by 1/RMS for a normalised operand
   auto cload = [&](int rl, int c0) {
-    float4 v = *(const float4*)&Cs[rl * BN + (c0 ^ (((rl >> 2) & 3) << 4))];
+    float4 v = *(const float4*)&Cs[rl * BN + (c0 ^ (((rl >> 2) & 1) << 5))];
     if (AM == A_NORM) {
       const float s = s_inv[rl];
       v.x *= s; v.y *= s; v.z *= s; v.w *= s;
