@@ -77,11 +77,12 @@ GemmPlan plan_gemm(int M, int N, int Kd, bool argmax) {
   p.Nt = n_tiles(N);
   p.tiled = 0;
   if (M > 32) {
-    // 128 x 128 tiles read each weight once per 128 rows and each activation once per 128 columns; used
-    // when they alone give at least one workgroup per compute unit (the LM head always does) or when the
-    // skinny kernel's re-reads of the activations (once per 16 columns) dominate
+    // 128 x 128 tiles read each weight once per 128 rows and each activation once per 128 columns. The
+    // skinny kernel re-reads the activations once per 16 columns, which dominates once M > 32 unless the
+    // tiled grid would be too small to keep the weight stream going (narrow outputs, N / 128 * M / 128 <
+    // 64 workgroups); the LM head always has enough columns.
     const int tg = (p.Nt + 7) / 8, tm = (M + 127) / 128;
-    if (argmax || tg * tm >= 256 || M >= 256) {
+    if (argmax || tg * tm >= 64 || M >= 256) {
       p.tiled = 1;
       p.MT = 8;
       p.NT = 8;

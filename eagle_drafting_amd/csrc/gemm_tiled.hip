@@ -49,15 +49,22 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
   // is stored into LDS.
   typedef bf16x8_t Regs[8];  // [0..3] activations, [4..7] weights
   Regs r0, r1;
+  // Activations: piece p covers row p / 8 and 16-byte segment p % 8 of the stage's 64 columns, so 8
+  // consecutive lanes read one 128-byte row segment. Their LDS slot is the fragment lane
+  // (row % 16) + 16 (segment % 4) of k-step segment / 4, XOR-swizzled by 4 (segment % 4) so that the
+  // lanes of one row land in different banks. Weights: packed fragments, 1 KiB per wave instruction.
+  auto asw = [](int lp) { return lp ^ ((lp >> 4) << 2); };
   auto gload = [&](Regs& r, int st) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int p = tid + 256 * q;
+      const int arow = p >> 3, seg = p & 7;
+      const int akstep = min(2 * st + (seg >> 2), Ks - 1);
+      const int row = m0 + arow;
+      const int off = row < M ? (row * g.lda + akstep * 32 + 8 * (seg & 3)) * 2 : 0x7ffffff0;
+      r[q] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0));
       const int ks = p >> 9, t = (p >> 6) & 7, ln = p & 63;
       const int kstep = min(2 * st + ks, Ks - 1);
-      const int row = m0 + 16 * t + (ln & 15);
-      const int off = row < M ? (row * g.lda + kstep * 32 + 8 * (ln >> 4)) * 2 : 0x7ffffff0;
-      r[q] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0));
       const int ntile = min(nt0 + t, Nt - 1);
       r[4 + q] = W[((size_t)ntile * Ks + kstep) * 64 + ln];
     }
@@ -66,8 +73,9 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int p = tid + 256 * q;
+      const int arow = p >> 3, seg = p & 7;
+      As[buf][seg >> 2][arow >> 4][asw((arow & 15) + 16 * (seg & 3))] = r[q];
       const int ks = p >> 9, t = (p >> 6) & 7, ln = p & 63;
-      As[buf][ks][t][ln] = r[q];
       Bs[buf][ks][t][ln] = r[4 + q];
     }
   };
@@ -90,7 +98,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
         for (int u = 0; u < 2; ++u) {
           bf16x8_t af[2], bf[2];
 #pragma unroll
-          for (int i = 0; i < 2; ++i) af[i] = As[buf][ks][wm * 4 + 2 * i + fr_t][fr_l + 32 * u];
+          for (int i = 0; i < 2; ++i) af[i] = As[buf][ks][wm * 4 + 2 * i + fr_t][asw(fr_l + 32 * u)];
 #pragma unroll
           for (int j = 0; j < 2; ++j) bf[j] = Bs[buf][ks][wn * 4 + 2 * j + fr_t][fr_l + 32 * u];
 #pragma unroll
@@ -104,18 +112,18 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
   };
 
   gload(r0, 0);
-  if (nstage > 1) gload(r1, 1);
+  gload(r1, min(1, nstage - 1));
   sstore(r0, 0);
   __syncthreads();
   for (int st = 0; st < nstage; st += 2) {
     // stage st is in buffer 0, stage st + 1 in r1
-    if (st + 2 < nstage) gload(r0, st + 2);
+    gload(r0, min(st + 2, nstage - 1));
     compute(0, st);
     if (st + 1 < nstage) sstore(r1, 1);
     __syncthreads();
     if (st + 1 >= nstage) break;
     // stage st + 1 is in buffer 1, stage st + 2 in r0
-    if (st + 3 < nstage) gload(r1, st + 3);
+    gload(r1, min(st + 3, nstage - 1));
     compute(1, st + 1);
     if (st + 2 < nstage) sstore(r0, 0);
     __syncthreads();
