@@ -19,7 +19,7 @@
 
 namespace pe {
 
-#define ATTN_MAX_PARTIALS 1024  // (split, sub-stream) partials per query row
+#define ATTN_MAX_PARTIALS 1024  // split partials per query row
 
 static inline int attn_sub_streams(int R) {
   const int RT = (R + 15) / 16;
@@ -38,14 +38,14 @@ AttnPlan plan_attention(int B, int K, int Hq, int Hkv, int hd, int max_ctx) {
   int chunk = (int)((want + KEYS - 1) / KEYS) * KEYS;
   if (chunk < KEYS) chunk = KEYS;
   if (chunk > 4096) chunk = 4096;
-  while ((long long)((max_ctx + K + chunk - 1) / chunk) * p.sub > ATTN_MAX_PARTIALS) chunk *= 2;
+  while ((max_ctx + K + chunk - 1) / chunk > ATTN_MAX_PARTIALS) chunk *= 2;
   p.chunk = chunk;
   p.nsplit = (max_ctx + K + chunk - 1) / chunk;
   return p;
 }
 
 size_t attn_partial_floats(int M, int Hq, int hd, const AttnPlan& p) {
-  return (size_t)M * Hq * p.nsplit * p.sub * (hd + 2);
+  return (size_t)M * Hq * p.nsplit * (hd + 2);
 }
 
 // NW: waves per workgroup, 4 or (when more than 64 query rows share a kv head) 8; each wave owns one
@@ -69,8 +69,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(const bf16_t* __rest
   constexpr int NR = 1;
   // sK row of key k within a round: key 32 a' + 8 a + 4 h + r sits at row 32 a' + 16 h + 4 a + r, so score
   // tile h's MFMA row 4 a + r is key 8 a + 4 h + r
-  __shared__ __attribute__((aligned(16))) bf16_t sK[KEYS * STR];
-  __shared__ __attribute__((aligned(16))) bf16_t sVt[HD * VSTR];  // [dim][key]
+  __shared__ __attribute__((aligned(16))) char smem[(KEYS * STR + HD * VSTR) * sizeof(bf16_t)];
+  bf16_t* sK = (bf16_t*)smem;                 // [key][dim]
+  bf16_t* sVt = sK + KEYS * STR;              // [dim][key]
 
   const int b = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
   const int split = blockIdx.y;
@@ -226,7 +227,39 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(const bf16_t* __rest
     }
   }
 
-  const int nsub = nsplit * sub;
+  if (sub > 1) {
+    // merge the key sub-streams of each row tile inside the workgroup (fixed order), so that a split
+    // leaves one partial per row: sub-stream s > 0 parks (O, m, l) in LDS, sub-stream 0 folds them in
+    static_assert((HD + 2) * 16 * 3 * sizeof(float) <= sizeof(smem), "merge scratch exceeds LDS");
+    float* red = (float*)smem;
+    __syncthreads();  // every wave is done with the staged tiles
+    if (ks_id > 0) {
+      float* slot = red + (size_t)((ks_id - 1) * RT + rt0) * 16 * (HD + 2) + lr * (HD + 2);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) slot[ct * 16 + 4 * lq + r] = o[0][ct][r];
+      if (lq == 0) {
+        slot[HD] = m_run[0];
+        slot[HD + 1] = l_run[0];
+      }
+    }
+    __syncthreads();
+    if (ks_id > 0) return;
+    for (int q = 1; q < sub; ++q) {
+      const float* slot = red + (size_t)((q - 1) * RT + rt0) * 16 * (HD + 2) + lr * (HD + 2);
+      const float mq = slot[HD], lqs = slot[HD + 1];
+      const float mn = fmaxf(m_run[0], mq);
+      const float a0 = __expf(m_run[0] - mn), aq = __expf(mq - mn);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[0][ct][r] = o[0][ct][r] * a0 + slot[ct * 16 + 4 * lq + r] * aq;
+      l_run[0] = l_run[0] * a0 + lqs * aq;
+      m_run[0] = mn;
+    }
+  }
+
 #pragma unroll
   for (int t = 0; t < NR; ++t) {
     if (t >= nrt) continue;
@@ -234,7 +267,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(const bf16_t* __rest
     if (row >= R) continue;
     const int hl = row / K, j = row % K;
     const size_t rid = ((size_t)b * Hq + (g * G + hl)) * K + j;
-    float* dst = part + (rid * nsub + (size_t)split * sub + ks_id) * (HD + 2);
+    float* dst = part + (rid * nsplit + split) * (HD + 2);
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -246,50 +279,67 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(const bf16_t* __rest
   }
 }
 
+// O[b*K + j][h] = sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s over the splits that hold keys. One
+// workgroup per query row: 4 groups of 64 threads take every 4th split (HD / 64 columns per thread),
+// then the groups are added in a fixed order.
 template <int HD>
-__global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restrict__ part, bf16_t* __restrict__ O,
-                                                          const int* __restrict__ seq_len,
-                                                          const int* __restrict__ req_slot, int K, int Hq,
-                                                          int max_ctx, int n_slots, int chunk, int nsplit,
-                                                          int sub) {
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part, bf16_t* __restrict__ O,
+                                                           const int* __restrict__ seq_len,
+                                                           const int* __restrict__ req_slot, int K, int Hq,
+                                                           int max_ctx, int n_slots, int chunk, int nsplit) {
+  constexpr int CPT = HD / 64;  // columns per thread
   const int rid = blockIdx.x;
   const int j = rid % K, h = (rid / K) % Hq, b = rid / (K * Hq);
   bf16_t* out = O + ((size_t)(b * K + j) * Hq + h) * HD;
   const int L = seq_len[b], slot = req_slot[b];
   if (slot < 0 || slot >= n_slots || L < 0 || L + K > max_ctx) {
-    for (int c = threadIdx.x; c < HD; c += 64) out[c] = 0;
+    for (int c = threadIdx.x; c < HD; c += 256) out[c] = 0;
     return;
   }
   __shared__ float sw[ATTN_MAX_PARTIALS];
-  __shared__ float sl[ATTN_MAX_PARTIALS];
-  const int ns = ((L + K + chunk - 1) / chunk) * sub;
-  const float* src = part + (size_t)rid * nsplit * sub * (HD + 2);
-  // all (m_s, l_s) in parallel: one load of each per lane, then wave reductions
+  __shared__ float sred[4][HD];
+  __shared__ float swave[8];
+  const int ns = (L + K + chunk - 1) / chunk;
+  const float* src = part + (size_t)rid * nsplit * (HD + 2);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // pass 1: M = max_s m_s
   float M = -1e30f;
-  for (int s = threadIdx.x; s < ns; s += 64) {
+  for (int s = tid; s < ns; s += 256) {
     const float m = src[(size_t)s * (HD + 2) + HD];
-    sl[s] = src[(size_t)s * (HD + 2) + HD + 1];
     sw[s] = m;
     M = fmaxf(M, m);
   }
   M = wave_max(M);
+  if (lane == 0) swave[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(swave[0], swave[1]), fmaxf(swave[2], swave[3]));
+  // pass 2: weights w_s = e^(m_s - M) (each thread rewrites the entries it wrote) and the denominator
   float den = 0.f;
-  for (int s = threadIdx.x; s < ns; s += 64) {  // the entries this thread wrote
+  for (int s = tid; s < ns; s += 256) {
     const float w = __expf(sw[s] - M);
     sw[s] = w;
-    den += w * sl[s];
+    den += w * src[(size_t)s * (HD + 2) + HD + 1];
   }
   den = wave_sum(den);
+  if (lane == 0) swave[4 + wave] = den;
   __syncthreads();
-  const float inv = 1.f / den;
+  // pass 3: numerators; group `wave` takes splits wave, wave + 4, ...
+  float num[CPT];
 #pragma unroll
-  for (int c0 = 0; c0 < HD; c0 += 64) {
-    const int c = c0 + threadIdx.x;
-    float num = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < ns; ++s) num += sw[s] * src[(size_t)s * (HD + 2) + c];
-    out[c] = f32_to_bf16(num * inv);
+  for (int e = 0; e < CPT; ++e) num[e] = 0.f;
+#pragma unroll 4
+  for (int s = wave; s < ns; s += 4) {
+    const float w = sw[s];
+    const float* ps = src + (size_t)s * (HD + 2) + CPT * lane;
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) num[e] += w * ps[e];
   }
+#pragma unroll
+  for (int e = 0; e < CPT; ++e) sred[wave][CPT * lane + e] = num[e];
+  __syncthreads();
+  const float inv = 1.f / ((swave[4] + swave[5]) + (swave[6] + swave[7]));
+  for (int c = tid; c < HD; c += 256)
+    out[c] = f32_to_bf16(((sred[0][c] + sred[1][c]) + (sred[2][c] + sred[3][c])) * inv);
 }
 
 hipError_t launch_attention_bf16(const AttnPlan& p, const void* Q, const void* Kc, const void* Vc,
@@ -317,13 +367,13 @@ hipError_t launch_attention_combine_bf16(const AttnPlan& p, const float* part, v
                                          const int* req_slot, int B, int K, int Hq, int Hkv, int hd, int max_ctx,
                                          int n_slots, hipStream_t st) {
   (void)Hkv;
-  dim3 grid(B * Hq * K), block(64);
+  dim3 grid(B * Hq * K), block(256);
   if (hd == 128)
     hipLaunchKernelGGL(attn_combine_kernel<128>, grid, block, 0, st, part, (bf16_t*)O, seq_len, req_slot, K, Hq,
-                       max_ctx, n_slots, p.chunk, p.nsplit, p.sub);
+                       max_ctx, n_slots, p.chunk, p.nsplit);
   else
     hipLaunchKernelGGL(attn_combine_kernel<64>, grid, block, 0, st, part, (bf16_t*)O, seq_len, req_slot, K, Hq,
-                       max_ctx, n_slots, p.chunk, p.nsplit, p.sub);
+                       max_ctx, n_slots, p.chunk, p.nsplit);
   return hipGetLastError();
 }
 
