@@ -3,10 +3,12 @@
 //
 // Workgroup tile 128 rows x 128 columns, 4 waves in a 2 x 2 arrangement (each wave 64 x 64: 2 x 2 blocks of
 // v_mfma_f32_32x32x16_bf16, the bf16 MFMA with the highest sustained rate on gfx950). Each stage covers 64
-// of the reduction dimension. LDS holds both operands as 16 x 32 fragments (1 KiB each, the layout of the
-// packed weights), two buffers; global loads run two stages ahead in two register sets, so a load has two
-// stages of MFMA work to arrive in. Every ds_read is 16 B per lane and each 16-lane group reads 256
-// contiguous bytes.
+// of the reduction dimension. Activations are staged through two LDS buffers as 16 x 32 fragments (the
+// layout of the packed weights); weights go from the packed fragments straight into registers (each
+// fragment is used by the two waves of a column half). Activation loads run two stages ahead, weight
+// loads one; the stage loop is branch-free (even stage count, zero activations past the end), so the
+// compiler's wait counts stay exact, and the next fragment pair is read from LDS while the current
+// products run.
 //
 // Epilogue: the 128 x 128 fp32 product tile is written into the same 64 KiB of LDS (column XOR-swizzle so
 // the two lane halves of the accumulator layout hit distinct banks), then read back as 16-byte row chunks:
@@ -21,10 +23,9 @@ namespace pe {
 template <int AM, int EP>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
   constexpr int BM = 128, BN = 128;
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * 2 * 8 * 64 * 16];  // 64 KiB
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * 2 * 8 * 64 * 16];  // 64 KiB: product tile; A buffers in the first half
   __shared__ float s_inv[BM];
   bf16x8_t(*As)[2][8][64] = (bf16x8_t(*)[2][8][64])smem;                      // [buffer][k-step][m-tile][lane]
-  bf16x8_t(*Bs)[2][8][64] = (bf16x8_t(*)[2][8][64])(smem + 2 * 2 * 8 * 64 * 16);  // [buffer][k-step][n-tile][lane]
   float* Cs = (float*)smem;                                                  // [BM][BN], after the main loop
 
   const int M = g.M, N = g.N, Ks = g.Ks, Nt = g.Nt;
@@ -38,51 +39,59 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
   if (ng >= g.ngroups) return;
   const int m0 = (slot % g.mblocks) * BM;
   const int nt0 = ng * 8;
-  const int nstage = (Ks + 1) / 2;
+  // stages of 64 reduction columns, rounded up to an even count; activation loads past the last k-step
+  // return zeros (out-of-range buffer offset), so padded stages add nothing and the loop has no branches
+  const int nstage = ((Ks + 1) / 2 + 1) & ~1;
 
   const __amdgpu_buffer_rsrc_t a_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, M * g.lda * 2, 0x00020000);
   const bf16x8_t* W = (const bf16x8_t*)g.Wp_raw;
 
-  // this thread's four 16-byte pieces of each operand per stage: p = tid + 256 q over [k-step][tile][lane].
-  // Two register sets: the loads of stage s + 2 are in flight while stage s is multiplied and stage s + 1
-  // is stored into LDS.
-  typedef bf16x8_t Regs[8];  // [0..3] activations, [4..7] weights
-  Regs r0, r1;
-  // Activations: piece p covers row p / 8 and 16-byte segment p % 8 of the stage's 64 columns, so 8
-  // consecutive lanes read one 128-byte row segment. Their LDS slot is the fragment lane
-  // (row % 16) + 16 (segment % 4) of k-step segment / 4, XOR-swizzled by 4 (segment % 4) so that the
-  // lanes of one row land in different banks. Weights: packed fragments, 1 KiB per wave instruction.
+  // Activations go through LDS (shared by the two waves of a row half); weights go straight from the
+  // packed fragments into the registers of the waves that use them (each fragment is needed by the two
+  // waves of a column half). Activations: piece p = tid + 256 q covers row p / 8 and 16-byte segment p % 8
+  // of the stage's 64 columns (8 lanes read one 128-byte row segment); their LDS slot is fragment lane
+  // (row % 16) + 16 (segment % 4) of k-step segment / 4, XOR-swizzled by 4 (segment % 4).
   auto asw = [](int lp) { return lp ^ ((lp >> 4) << 2); };
-  auto gload = [&](Regs& r, int st) {
+  typedef bf16x8_t RegA[4];
+  typedef bf16x8_t RegB[8];  // [(ks * 2 + u) * 2 + j]
+  RegA ra0, ra1;
+  RegB rb0, rb1;
+  // 32 x 32 x 16 products out of the 16 x 32 fragments: lane l of the operand of rows (or columns)
+  // 32 b .. 32 b + 31 and k-half u takes fragment 2 b + (l % 32) / 16, fragment lane l % 16 + 16 (2 u + l / 32)
+  const int fr_t = (lane & 31) >> 4, fr_l = (lane & 15) + 16 * (lane >> 5);
+  auto gload_a = [&](RegA& r, int st) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int p = tid + 256 * q;
       const int arow = p >> 3, seg = p & 7;
-      const int akstep = min(2 * st + (seg >> 2), Ks - 1);
+      const int akstep = 2 * st + (seg >> 2);
       const int row = m0 + arow;
-      const int off = row < M ? (row * g.lda + akstep * 32 + 8 * (seg & 3)) * 2 : 0x7ffffff0;
+      const int off = row < M && akstep < Ks ? (row * g.lda + akstep * 32 + 8 * (seg & 3)) * 2 : 0x7ffffff0;
       r[q] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0));
-      const int ks = p >> 9, t = (p >> 6) & 7, ln = p & 63;
-      const int kstep = min(2 * st + ks, Ks - 1);
-      const int ntile = min(nt0 + t, Nt - 1);
-      r[4 + q] = W[((size_t)ntile * Ks + kstep) * 64 + ln];
     }
   };
-  auto sstore = [&](const Regs& r, int buf) {
+  auto gload_b = [&](RegB& r, int st) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int kstep = min(2 * st + ks, Ks - 1);
+          const int ntile = min(nt0 + wn * 4 + 2 * j + fr_t, Nt - 1);
+          r[(ks * 2 + u) * 2 + j] = W[((size_t)ntile * Ks + kstep) * 64 + fr_l + 32 * u];
+        }
+  };
+  auto sstore = [&](const RegA& r, int buf) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int p = tid + 256 * q;
       const int arow = p >> 3, seg = p & 7;
       As[buf][seg >> 2][arow >> 4][asw((arow & 15) + 16 * (seg & 3))] = r[q];
-      const int ks = p >> 9, t = (p >> 6) & 7, ln = p & 63;
-      Bs[buf][ks][t][ln] = r[4 + q];
     }
   };
 
-  // 32 x 32 x 16 products out of the 16 x 32 fragments: lane l of the operand of rows (or columns)
-  // 32 b .. 32 b + 31 and k-half u takes fragment 2 b + (l % 32) / 16, fragment lane l % 16 + 16 (2 u + l / 32)
-  const int fr_t = (lane & 31) >> 4, fr_l = (lane & 15) + 16 * (lane >> 5);
   f32x16_t acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -90,42 +99,55 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-  auto compute = [&](int buf, int st) {
+  // four groups (k-step, k-half) of four products; the two A fragments of the next group are read from
+  // LDS while the current group's products run
+  auto compute = [&](int buf, const RegB& rb) {
+    bf16x8_t af[2], an[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      if (2 * st + ks < Ks) {
+    for (int i = 0; i < 2; ++i) af[i] = As[buf][0][wm * 4 + 2 * i + fr_t][asw(fr_l)];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          bf16x8_t af[2], bf[2];
+    for (int gi = 0; gi < 4; ++gi) {
+      const int ks = gi >> 1, u = gi & 1;
+      if (gi < 3) {
+        const int ks1 = (gi + 1) >> 1, u1 = (gi + 1) & 1;
 #pragma unroll
-          for (int i = 0; i < 2; ++i) af[i] = As[buf][ks][wm * 4 + 2 * i + fr_t][asw(fr_l + 32 * u)];
+        for (int i = 0; i < 2; ++i) an[i] = As[buf][ks1][wm * 4 + 2 * i + fr_t][asw(fr_l + 32 * u1)];
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int j = 0; j < 2; ++j) bf[j] = Bs[buf][ks][wn * 4 + 2 * j + fr_t][fr_l + 32 * u];
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], rb[(ks * 2 + u) * 2 + j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (gi < 3) {
+        af[0] = an[0];
+        af[1] = an[1];
       }
     }
   };
 
-  gload(r0, 0);
-  gload(r1, min(1, nstage - 1));
-  sstore(r0, 0);
+  // activations run two stages ahead (register set, then LDS buffer), weights one stage ahead
+  gload_a(ra0, 0);
+  gload_b(rb0, 0);
+  gload_a(ra1, 1);
+  sstore(ra0, 0);
   __syncthreads();
   for (int st = 0; st < nstage; st += 2) {
-    // stage st is in buffer 0, stage st + 1 in r1
-    gload(r0, min(st + 2, nstage - 1));
-    compute(0, st);
-    if (st + 1 < nstage) sstore(r1, 1);
+    // loads past the end (stages nstage, nstage + 1) read zeros / valid clamped weights and are unused
+    gload_a(ra0, st + 2);
+    gload_b(rb1, st + 1);
+    __builtin_amdgcn_sched_barrier(0);  // issue the loads before the products, store after them
+    compute(0, rb0);
+    __builtin_amdgcn_sched_barrier(0);
+    sstore(ra1, 1);
     __syncthreads();
-    if (st + 1 >= nstage) break;
-    // stage st + 1 is in buffer 1, stage st + 2 in r0
-    gload(r1, min(st + 3, nstage - 1));
-    compute(1, st + 1);
-    if (st + 2 < nstage) sstore(r0, 0);
+    gload_a(ra1, st + 3);
+    gload_b(rb0, st + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1, rb1);
+    __builtin_amdgcn_sched_barrier(0);
+    sstore(ra0, 0);
     __syncthreads();
   }
 
