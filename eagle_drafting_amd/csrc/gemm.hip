@@ -148,7 +148,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
   // A through a raw buffer descriptor: lanes of padding rows (row >= M) use an out-of-range offset, which
   // returns zeros without any memory request, so only real rows cost bandwidth.
   const __amdgpu_buffer_rsrc_t a_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, M * g.lda * 2, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, (gemm_a_row(g, M - 1) + 1) * g.lda * 2, 0x00020000);
   bf16x8_t a[KC][MT], b[KC];
   auto load_round = [&](int c0) {
     const int nk = max(1, min(KC, s_end - c0));
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int row = m0 + mt * 16 + (lane & 15);
-        const int off = row < M ? (row * g.lda + ks * 32 + 8 * (lane >> 4)) * 2 : 0x7ffffff0;
+        const int off = row < M ? (gemm_a_row(g, row) * g.lda + ks * 32 + 8 * (lane >> 4)) * 2 : 0x7ffffff0;
         a[kk][mt] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0));
       }
     }
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
   // so that no branch forces the weight loads to wait for them.
   float pre_ssq[4] = {0.f, 0.f, 0.f, 0.f};
   if (AM == A_NORM) {
-    const float* src = g.ssq_in + (size_t)(m0 + min(wave, nrows - 1)) * g.nssq;
+    const float* src = g.ssq_in + (size_t)gemm_a_row(g, m0 + min(wave, nrows - 1)) * g.nssq;
 #pragma unroll
     for (int i = 0; i < 4; ++i) pre_ssq[i] = src[min(lane + 64 * i, g.nssq - 1)];  // masked when used
   }
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
     // 1 / RMS of each row of x from the per-16-column partial sums of squares: one wave per row, all
     // partials loaded at once (the first row's were prefetched), fixed reduction order
     for (int r = wave; r < nrows; r += NW) {
-      const float* src = g.ssq_in + (size_t)(m0 + r) * g.nssq;
+      const float* src = g.ssq_in + (size_t)gemm_a_row(g, m0 + r) * g.nssq;
       float t = 0.f;
       if (r == wave) {
         float v[4];
@@ -443,13 +443,14 @@ hipError_t launch_rows_ssq(const float* rows, float* X, float* ssq, uint16_t* XG
 // fp32 weights (the small fp32 drafter): one wave per output column, lanes stride over k.
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A, int lda, int M, int Kd,
                                                        const float* __restrict__ W, int N, float* __restrict__ out,
-                                                       int ldo) {
+                                                       int ldo, int rows_in, int rows_out) {
   const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (n >= N) return;
   const float* w = W + (size_t)n * Kd;
   for (int m = 0; m < M; ++m) {
-    const float* a = A + (size_t)m * lda;
+    const int ar = rows_out > 0 ? (m / rows_out) * rows_in + m % rows_out : m;
+    const float* a = A + (size_t)ar * lda;
     float s = 0.f;
     for (int k = lane; k < Kd; k += 64) s = fmaf(a[k], w[k], s);
     s = wave_sum(s);
@@ -458,8 +459,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 }
 
 hipError_t launch_gemm_f32(const float* A, int lda, int M, int Kd, const float* W, int N, float* out, int ldo,
-                           hipStream_t st) {
-  hipLaunchKernelGGL(gemm_f32_kernel, dim3((N + 3) / 4), dim3(256), 0, st, A, lda, M, Kd, W, N, out, ldo);
+                           hipStream_t st, int rows_in, int rows_out) {
+  hipLaunchKernelGGL(gemm_f32_kernel, dim3((N + 3) / 4), dim3(256), 0, st, A, lda, M, Kd, W, N, out, ldo, rows_in,
+                     rows_out);
   return hipGetLastError();
 }
 

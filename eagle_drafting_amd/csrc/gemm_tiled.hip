@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
   const int nstage = ((Ks + 1) / 2 + 1) & ~1;
 
   const __amdgpu_buffer_rsrc_t a_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, M * g.lda * 2, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, (gemm_a_row(g, M - 1) + 1) * g.lda * 2, 0x00020000);
   const bf16x8_t* W = (const bf16x8_t*)g.Wp_raw;
 
   // Activations go through LDS (shared by the two waves of a row half); weights go straight from the
@@ -67,7 +67,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
       const int arow = p >> 3, seg = p & 7;
       const int akstep = 2 * st + (seg >> 2);
       const int row = m0 + arow;
-      const int off = row < M && akstep < Ks ? (row * g.lda + akstep * 32 + 8 * (seg & 3)) * 2 : 0x7ffffff0;
+      const int off =
+          row < M && akstep < Ks ? (gemm_a_row(g, row) * g.lda + akstep * 32 + 8 * (seg & 3)) * 2 : 0x7ffffff0;
       r[q] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0));
     }
   };
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
     const int r = tid >> 1, h = tid & 1;
     float t = 0.f;
     if (m0 + r < M) {
-      const float* src = g.ssq_in + (size_t)(m0 + r) * g.nssq;
+      const float* src = g.ssq_in + (size_t)gemm_a_row(g, m0 + r) * g.nssq;
       for (int i = h; i < g.nssq; i += 2) t += src[i];
     }
     t += __shfl_xor(t, 1, PE_WAVE);

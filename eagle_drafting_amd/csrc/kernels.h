@@ -61,14 +61,21 @@ struct GemmArgs {
   const int* last_token; const uint16_t* embed; const uint16_t* emb_mask; const uint16_t* h_shared; int V;
   // EPI_ARGMAX: per (row, workgroup) best (value, index); optional fp32 logits [M][N]
   float* am_val; int* am_idx; float* logits;
+  // row m of the product reads operand row (m / rows_out) * rows_in + m % rows_out (and that row's sums
+  // of squares): the LM head runs on rows_out of every rows_in rows per request. 0 = identity.
+  int rows_in, rows_out;
 };
+// operand row of product row m
+__host__ __device__ inline int gemm_a_row(const GemmArgs& g, int m) {
+  return g.rows_out > 0 ? (m / g.rows_out) * g.rows_in + m % g.rows_out : m;
+}
 hipError_t launch_gemm(const GemmPlan& p, GemmArgs a, int a_mode, int epi, hipStream_t st);
 hipError_t launch_gemm_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st);
 hipError_t launch_rows_ssq(const float* rows, float* X, float* ssq, uint16_t* XG, const uint16_t* gain, int M, int d,
                            hipStream_t st);
 // fp32 weights, unpacked [N, Kd]: out[m * ldo + n]
 hipError_t launch_gemm_f32(const float* A, int lda, int M, int Kd, const float* W, int N, float* out, int ldo,
-                           hipStream_t st);
+                           hipStream_t st, int rows_in = 0, int rows_out = 0);
 
 // ---- row-wise kernels (dtype: 0 = f32, 1 = bf16 for activations / weights) -------------------
 hipError_t launch_rowbuild_norm(int dtype, float* X, void* U, const float* P, int S, const float* rows_in, int B,

@@ -77,12 +77,12 @@ static pe_status check_cfg(const pe_config* c, std::string& why) {
   if (!(c->rms_eps >= 0.f) || !(c->rope_base > 1.f)) { why = "rms_eps < 0 or rope_base <= 1"; return PE_ERR_INVALID; }
   if (c->max_batch < 1 || c->max_batch > PE_MAX_BATCH) { why = "max_batch out of [1, 1024]"; return PE_ERR_INVALID; }
   if (c->max_k < 1 || c->max_k > PE_MAX_K) { why = "max_k out of [1, 16]"; return PE_ERR_INVALID; }
-  if (c->max_ctx < c->max_k || c->n_slots < 1) { why = "max_ctx < max_k or n_slots < 1"; return PE_ERR_INVALID; }
+  if (c->max_ctx < c->max_k + 1 || c->n_slots < 1) { why = "max_ctx < max_k + 1 or n_slots < 1"; return PE_ERR_INVALID; }
   if (c->head_dim != 64 && c->head_dim != 128) { why = "head_dim must be 64 or 128"; return PE_ERR_UNSUPPORTED; }
   if (c->d_model % 32 || c->ffn_dim % 32) { why = "d_model and ffn_dim must be multiples of 32"; return PE_ERR_UNSUPPORTED; }
   if (c->vocab % 8) { why = "vocab must be a multiple of 8"; return PE_ERR_UNSUPPORTED; }
-  if (c->dtype == PE_BF16 && (c->n_q_heads / c->n_kv_heads) * c->max_k > 128) {
-    why = "(n_q_heads / n_kv_heads) * max_k must be <= 128"; return PE_ERR_UNSUPPORTED;
+  if (c->dtype == PE_BF16 && (c->n_q_heads / c->n_kv_heads) * (c->max_k + 1) > 128) {
+    why = "(n_q_heads / n_kv_heads) * (max_k + 1) must be <= 128"; return PE_ERR_UNSUPPORTED;
   }
   if (c->dtype == PE_F32 && c->max_ctx > 12288) { why = "fp32 drafter supports max_ctx <= 12288"; return PE_ERR_UNSUPPORTED; }
   if ((long long)c->n_slots * c->n_kv_heads * c->max_ctx * c->head_dim > (1LL << 40)) {
@@ -164,7 +164,8 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
   ctx->bf16 = c.dtype == PE_BF16;
   const int d = c.d_model, F = c.ffn_dim, V = c.vocab, hd = c.head_dim;
   const int qd = c.n_q_heads * hd, qkvd = (c.n_q_heads + 2 * c.n_kv_heads) * hd;
-  const int Mmax = c.max_batch * c.max_k;
+  // a draft step runs K + 1 rows per request (the K draft rows and one trailing placeholder row)
+  const int Mmax = c.max_batch * (c.max_k + 1);
   const size_t es = ctx->bf16 ? 2 : 4;
 
   // ---- packed weights (bf16 path)
@@ -221,7 +222,7 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
   }
   for (int B = 1; B <= c.max_batch; ++B) {
     if (ctx->bf16) {
-      for (int K = 1; K <= c.max_k; ++K) {
+      for (int K = 1; K <= c.max_k + 1; ++K) {
         AttnPlan ap = plan_attention(B, K, c.n_q_heads, c.n_kv_heads, hd, c.max_ctx);
         attn_floats = std::max(attn_floats, attn_partial_floats(B * K, c.n_q_heads, hd, ap));
       }
@@ -336,7 +337,8 @@ extern "C" pe_status pe_device_flags(pe_ctx* ctx, int32_t clear, int32_t* flags)
 #define LAUNCH(call) HIP_TRY(ctx, (call))
 
 // fp32 drafter: one kernel per step of the layer (small shapes only)
-static pe_status draft_f32(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_slot, const int32_t* seq_len,
+static pe_status draft_f32(pe_ctx* ctx, int32_t B, int32_t K, int32_t Kout, const int32_t* req_slot,
+                           const int32_t* seq_len,
                            const int32_t* last_token, const void* target_hidden, const float* rows,
                            int32_t* draft_tokens, float* logits) {
   const pe_config& c = ctx->cfg;
@@ -369,19 +371,22 @@ static pe_status draft_f32(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req
     const void* g_next = l + 1 < c.n_layers ? w.attn_norm[l + 1] : w.final_norm;
     LAUNCH(launch_residual_norm(0, ctx->X, ctx->U, P, 1, M, d, g_next, eps, st));
   }
+  // LM head and argmax on the Kout emitted rows of every request
+  const int Mo = B * Kout;
   float* z = logits ? logits : ctx->logits_ws;
   LAUNCH(prof_mark(ctx, PE_PROF_LM_HEAD, true));
-  LAUNCH(launch_gemm_f32((const float*)ctx->U, d, M, d, (const float*)w.lm_head, V, z, V, st));
+  LAUNCH(launch_gemm_f32((const float*)ctx->U, d, Mo, d, (const float*)w.lm_head, V, z, V, st, K, Kout));
   LAUNCH(prof_mark(ctx, PE_PROF_LM_HEAD, false));
-  const int nch = plan_argmax_chunks(M, V);
-  LAUNCH(launch_argmax_rows(0, z, M, V, nch, ctx->am_val, ctx->am_idx, st));
-  LAUNCH(launch_argmax_final(ctx->am_val, ctx->am_idx, M, nch, draft_tokens, st));
+  const int nch = plan_argmax_chunks(Mo, V);
+  LAUNCH(launch_argmax_rows(0, z, Mo, V, nch, ctx->am_val, ctx->am_idx, st));
+  LAUNCH(launch_argmax_final(ctx->am_val, ctx->am_idx, Mo, nch, draft_tokens, st));
   return PE_OK;
 }
 
 // bf16 drafter: per layer six kernels (QKV+RoPE+KV append, attention, combine, O+residual, gate/up+SwiGLU,
 // down+residual); RMSNorm is applied while the next projection reads its input.
-static pe_status draft_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_slot, const int32_t* seq_len,
+static pe_status draft_bf16(pe_ctx* ctx, int32_t B, int32_t K, int32_t Kout, const int32_t* req_slot,
+                            const int32_t* seq_len,
                             const int32_t* last_token, const void* target_hidden, const float* rows,
                             int32_t* draft_tokens, float* logits) {
   const pe_config& c = ctx->cfg;
@@ -471,18 +476,20 @@ static pe_status draft_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* re
       LAUNCH(launch_gemm(p, a, A_BF16, EPI_RESID, st));
     }
   }
-  // a9-a10: final RMSNorm, LM head, argmax
+  // a9-a10: final RMSNorm, LM head, argmax on the Kout emitted rows of every request
+  const int Mo = B * Kout;
   GemmArgs a = base;
-  a.M = M; a.Kd = d; a.N = V;
+  a.M = Mo; a.Kd = d; a.N = V;
   a.A = XG; a.lda = d;
+  a.rows_in = K; a.rows_out = Kout;
   a.Wp_raw = ctx->p_lm;
   a.am_val = ctx->am_val; a.am_idx = ctx->am_idx; a.logits = logits;
   a.nssq = nssq;
-  GemmPlan p = plan_gemm(M, V, d, true);
+  GemmPlan p = plan_gemm(Mo, V, d, true);
   LAUNCH(prof_mark(ctx, PE_PROF_LM_HEAD, true));
   LAUNCH(launch_gemm(p, a, A_NORM, EPI_ARGMAX, st));
   LAUNCH(prof_mark(ctx, PE_PROF_LM_HEAD, false));
-  LAUNCH(launch_argmax_final(ctx->am_val, ctx->am_idx, M, p.ngroups, draft_tokens, st));
+  LAUNCH(launch_argmax_final(ctx->am_val, ctx->am_idx, Mo, p.ngroups, draft_tokens, st));
   return PE_OK;
 }
 
@@ -498,8 +505,13 @@ static pe_status run_draft(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req
   if (target_hidden && ((uintptr_t)target_hidden & 15)) return fail(ctx, PE_ERR_INVALID, "target_hidden not 16-byte aligned");
   if (logits && ((uintptr_t)logits & 15)) return fail(ctx, PE_ERR_INVALID, "logits not 16-byte aligned");
   if (rows && ((uintptr_t)rows & 15)) return fail(ctx, PE_ERR_INVALID, "rows not 16-byte aligned");
-  if (ctx->bf16) return draft_bf16(ctx, B, K, req_slot, seq_len, last_token, target_hidden, rows, draft_tokens, logits);
-  return draft_f32(ctx, B, K, req_slot, seq_len, last_token, target_hidden, rows, draft_tokens, logits);
+  // A draft step from the row builder also runs one placeholder row after the K draft rows (position
+  // L_b + K), so the cache holds K/V for every position a verify can accept (accept_len <= K + 1); its
+  // outputs are not emitted. Caller-built rows are run as given.
+  const int Kr = rows ? K : K + 1;
+  if (ctx->bf16)
+    return draft_bf16(ctx, B, Kr, K, req_slot, seq_len, last_token, target_hidden, rows, draft_tokens, logits);
+  return draft_f32(ctx, B, Kr, K, req_slot, seq_len, last_token, target_hidden, rows, draft_tokens, logits);
 }
 
 extern "C" pe_status pe_draft_step(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_slot, const int32_t* seq_len,

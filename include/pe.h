@@ -23,7 +23,8 @@
  *   - Errors: every call returns a pe_status. Host-checkable problems (null pointers, sizes out of
  *     range, unsupported shapes) return PE_ERR_INVALID / PE_ERR_UNSUPPORTED before anything is enqueued.
  *     HIP failures return PE_ERR_HIP; pe_last_error gives the message. Device-value preconditions
- *     (token ids < vocab, slots < n_slots, seq_len + K <= max_ctx) are the caller's contract; kernels
+ *     (token ids < vocab, slots < n_slots, seq_len + K + 1 <= max_ctx for pe_draft_step, seq_len + K <=
+ *     max_ctx for pe_draft_rows and pe_verify) are the caller's contract; kernels
  *     skip any access that would break them and raise a flag readable through pe_device_flags.
  */
 #ifndef PE_H
@@ -99,7 +100,7 @@ typedef struct pe_ctx pe_ctx;
 pe_status pe_config_validate(const pe_config* cfg);
 
 /* Create a context on the current HIP device (which must be gfx950): validates cfg, allocates the
- * workspace for max_batch x max_k rows, copies the projection matrices into the library's tiled layout
+ * workspace for max_batch x (max_k + 1) rows, copies the projection matrices into the library's tiled layout
  * and builds the RoPE table. stream: a hipStream_t (NULL = default stream). Synchronizes before return. */
 pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe_kv* kv, void* stream, pe_ctx** out);
 
@@ -109,7 +110,10 @@ pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe_kv* kv, vo
  * at positions seq_len[b] + j. All B*K rows go through the drafter layers (RMSNorm, GQA attention over
  * the request's cache slot with a causal mask inside the K block, SwiGLU MLP) and the LM head;
  * draft_tokens[b*K + j] = argmax over the vocabulary (lowest index among equal maxima).
- * The K and V rows of this step are written to cache slot req_slot[b] at positions seq_len[b]..+K-1;
+ * One more placeholder row (h_shared + emb_mask at position seq_len[b] + K) runs after the K draft rows;
+ * it changes none of them (causal mask) and only its K and V are kept: pe_verify can accept K + 1
+ * tokens (seq_len advances by accept_len), and every position it keeps then holds drafter K/V.
+ * The K and V of rows 0..K are written to cache slot req_slot[b] at positions seq_len[b]..+K;
  * seq_len itself is not changed.
  *   req_slot, seq_len, last_token: device int32 [B]
  *   target_hidden: device [B, 3d] (dtype); the three captured hidden states as consecutive d-blocks
@@ -120,7 +124,8 @@ pe_status pe_draft_step(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_sl
                         float* logits);
 
 /* Same drafter pass over caller-built input rows (device float32 [B, K, d]) instead of the row
- * builder: lets a caller feed arbitrary rows, e.g. to check that row j never depends on rows after j. */
+ * builder: lets a caller feed arbitrary rows, e.g. to check that row j never depends on rows after j.
+ * Exactly the K given rows run (no trailing placeholder row): K/V at positions seq_len[b]..+K-1. */
 pe_status pe_draft_rows(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_slot, const int32_t* seq_len,
                         const float* rows, int32_t* draft_tokens, float* logits);
 

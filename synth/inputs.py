@@ -245,3 +245,10 @@ def new_request(w: Workload, step: int, index: int) -> dict:
     tok = int(rng.integers(0, s.vocab))
     hid = _encode(_normal((w.seed, 601, step, index), (3 * s.d_model,)), s.dtype)
     return {"seq_len": L, "last_token": tok, "target_hidden": hid, "request_key": 10_000 * (step + 1) + index}
+
+
+def step_hiddens(w: Workload, step: int) -> np.ndarray:
+    """Fresh target hidden states [B, 3d] for every request slot of a later step (N(0, 1), encoded):
+    each step's hiddens come from a new target pass."""
+    s = w.shape
+    return _encode(_normal((w.seed, 700, step), (w.B, 3 * s.d_model)), s.dtype)

@@ -1,0 +1,122 @@
+"""GPU parity over several state-advancing draft + verify steps with churn.
+
+Each step: pe_draft_step on the current batch (checked against the oracle's draft step on the oracle's own
+copy of every request's context), target logits planted on the GPU's draft, pe_verify with random
+finished flags (checked bit-exactly against the oracle's verify + compaction), then the next batch is
+built the way a serving loop would: kept requests take req_slot_next / seq_len_next / last_token_next,
+the freed cache slots go to new requests (their contexts written into the device cache), and every
+request gets fresh target hiddens.
+
+Cache reading followed by both sides: a draft step writes the K/V of its K rows and of one trailing
+placeholder row at positions L_b .. L_b + K; after verify, positions up to the new seq_len (L_b +
+accept_len, at most L_b + K + 1) are context, so the oracle appends its own rows 0 .. accept_len - 1 to
+the request's context, and the GPU's later rows simply overwrite the rest. All-accepted steps (accept_len
+= K + 1) are what reads the trailing row.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from oracle import pe_oracle as O
+from synth.inputs import churn_finished, kv_block, new_request, plant_target_logits, step_hiddens, to_f64
+from synth.workloads import QWEN3_CODER, TINY_FP32, Workload
+
+from gpu_util import TOL, GpuDrafter, check_logits, check_tokens, check_verify, log, run_verify, shape_weights64
+
+pytestmark = pytest.mark.gpu
+
+MULTI = [
+    Workload("tiny-fp32-B3-K4-L20to64-steps", TINY_FP32, 3, 4, (20, 64), 0.7, 1100, churn=0.34, new_ctx=(8, 40),
+             steps=5),
+    Workload("qwen3coder-bf16-B4-K3-L256to1024-steps", QWEN3_CODER, 4, 3, (256, 1024), (0.5, 0.9), 2100,
+             churn=0.25, new_ctx=(128, 512), steps=3),
+]
+
+
+def _run(w: Workload):
+    import torch
+    from synth.device import to_device
+
+    s = w.shape
+    tol = TOL[s.dtype]
+    dr = GpuDrafter(w)
+    W64 = shape_weights64(s)
+    B, K, Hkv, hd = w.B, w.K, s.n_kv_heads, s.head_dim
+    st = {k: np.array(v) for k, v in dr.state.items()}
+    keys = list(range(B))                 # request keys (the context generator's identity)
+    L0 = {b: int(st["seq_len"][b]) for b in range(B)}  # generated context length per key
+    ext = {b: [[np.zeros((Hkv, 0, hd)) for _ in range(s.n_layers)] for _ in range(2)] for b in range(B)}
+    try:
+        for step in range(w.steps):
+            log(f"{w.name} step {step}: seq_len {st['seq_len'].tolist()} slots {st['req_slot'].tolist()}")
+            dstate = {"req_slot": to_device(st["req_slot"], "i32"), "seq_len": to_device(st["seq_len"], "i32"),
+                      "last_token": to_device(st["last_token"], "i32"),
+                      "target_hidden": to_device(st["target_hidden"], s.dtype)}
+            draft_dev, z = dr.draft(dstate=dstate)
+            draft = draft_dev.cpu().numpy()
+
+            def ctx(l, i):
+                key = keys[i]
+                pre = [to_f64(kv_block(w, l, kind, key, L0[key]), s.dtype) for kind in (0, 1)]
+                return tuple(np.concatenate([pre[kind], ext[key][kind][l]], axis=1) for kind in (0, 1))
+
+            ref = O.draft_step(s, W64, {"last_token": st["last_token"], "seq_len": st["seq_len"],
+                                        "target_hidden": to_f64(st["target_hidden"], s.dtype)}, ctx, K, tail=True)
+            err = check_logits(z.cpu().numpy(), ref["logits"], tol, f"step {step} logits")
+            strict, exempt = check_tokens(draft, ref["logits"], tol, f"step {step} tokens")
+            log(f"  draft parity: max row-rel err {err:.2e}, {strict}/{B * K} tokens equal, {exempt} near-ties")
+
+            T = plant_target_logits(w, draft, st["alpha"], step)
+            fin = churn_finished(w, step)
+            got = run_verify(dr.pe, dr.ctx, B, K, to_device(T, s.dtype), draft_dev, to_device(fin, "u8"),
+                             dstate["req_slot"], dstate["seq_len"])
+            v, c = check_verify(got, to_f64(T, s.dtype), draft, fin, st["req_slot"], st["seq_len"])
+            log(f"  verify: accept_len {v['accept_len'].tolist()}, finished {fin.tolist()}, kept {c['n_keep']}")
+
+            # the oracle's context grows by its own rows 0 .. accept_len - 1 of this step
+            for b in range(B):
+                a = int(v["accept_len"][b])
+                for l in range(s.n_layers):
+                    for kind, new in ((0, ref["k_new"][l]), (1, ref["v_new"][l])):
+                        rows = new[b, :a].transpose(1, 0, 2)  # [Hkv, a, hd]
+                        ext[keys[b]][kind][l] = np.concatenate([ext[keys[b]][kind][l], rows], axis=1)
+
+            # next batch: kept requests in their compacted order, then new requests in the freed slots
+            n_keep = c["n_keep"]
+            kept = [int(i) for i in c["keep_index"][:n_keep]]
+            nxt = {"req_slot": list(c["req_slot_next"][:n_keep]), "seq_len": list(c["seq_len_next"][:n_keep]),
+                   "last_token": list(c["last_token_next"][:n_keep]), "alpha": [st["alpha"][i] for i in kept]}
+            nkeys = [keys[i] for i in kept]
+            free = [sl for sl in range(w.n_slots) if sl not in set(int(x) for x in nxt["req_slot"])]
+            for i in range(B - n_keep):
+                nr = new_request(w, step, i)
+                slot = free[i]
+                key = nr["request_key"]
+                L0[key] = nr["seq_len"]
+                ext[key] = [[np.zeros((Hkv, 0, hd)) for _ in range(s.n_layers)] for _ in range(2)]
+                for l in range(s.n_layers):
+                    for kind, cache in ((0, dr.kc[l]), (1, dr.vc[l])):
+                        blk = to_device(kv_block(w, l, kind, key, nr["seq_len"]), s.dtype)
+                        cache[slot, :, : nr["seq_len"], :] = blk
+                nxt["req_slot"].append(slot)
+                nxt["seq_len"].append(nr["seq_len"])
+                nxt["last_token"].append(nr["last_token"])
+                nxt["alpha"].append(float(np.mean(w.alpha)) if isinstance(w.alpha, tuple) else float(w.alpha))
+                nkeys.append(key)
+            torch.cuda.synchronize()
+            keys = nkeys
+            st = {"req_slot": np.array(nxt["req_slot"], dtype=np.int32),
+                  "seq_len": np.array(nxt["seq_len"], dtype=np.int32),
+                  "last_token": np.array(nxt["last_token"], dtype=np.int32),
+                  "alpha": np.array(nxt["alpha"], dtype=np.float64),
+                  "target_hidden": step_hiddens(w, step + 1)}
+            assert int(st["seq_len"].max()) + K <= w.max_ctx
+    finally:
+        dr.close()
+
+
+@pytest.mark.parametrize("w", MULTI, ids=lambda w: w.name)
+def test_multistep_churn_parity(w):
+    _run(w)

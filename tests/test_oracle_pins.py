@@ -325,6 +325,37 @@ def test_causality_later_rows_do_not_change_earlier_rows():
             assert np.allclose(pert["k_new"][l][:, : j + 1], base["k_new"][l][:, : j + 1], rtol=1e-13, atol=1e-13)
 
 
+def test_tail_row_leaves_the_draft_unchanged_and_fills_position_L_plus_K():
+    # the trailing placeholder row (run so that an all-accepted verify finds K/V at L + K) comes after the
+    # K draft rows: their logits are those of the plain K-row step, and its layer-0 key is the closed form
+    # rope(W_k . RMSNorm(h_shared + emb_mask), L + K)
+    W = _weights64(MINI, 25)
+    rng = np.random.default_rng(25)
+    K = 3
+    hid = rng.standard_normal((2, 3 * MINI.d_model))
+    seq = [5, 2]
+    ctx = [_ctx(MINI, 5, 8), _ctx(MINI, 2, 9)]
+    st = {"last_token": np.array([4, 9]), "target_hidden": hid, "seq_len": np.array(seq)}
+    plain = O.draft_step(MINI, W, st, lambda l, b: ctx[b][l], K)
+    tail = O.draft_step(MINI, W, st, lambda l, b: ctx[b][l], K, tail=True)
+    assert tail["logits"].shape == plain["logits"].shape
+    assert np.allclose(tail["logits"], plain["logits"], rtol=1e-13, atol=1e-13)
+    assert np.array_equal(tail["draft"], plain["draft"])
+    for l in range(MINI.n_layers):
+        assert tail["k_new"][l].shape[1] == K + 1
+        assert np.allclose(tail["k_new"][l][:, :K], plain["k_new"][l], rtol=1e-13, atol=1e-13)
+    Hq, Hkv, hd = MINI.n_q_heads, MINI.n_kv_heads, MINI.head_dim
+    x = W["h_shared"] + W["emb_mask"]
+    u = x / np.sqrt(np.mean(x * x) + MINI.rms_eps) * W["l0.attn_norm"]
+    k = (W["l0.wqkv"][Hq * hd:(Hq + Hkv) * hd] @ u).reshape(Hkv, hd)
+    for b in range(2):
+        pos = seq[b] + K
+        inv = MINI.rope_base ** (-np.arange(hd // 2) * 2.0 / hd)
+        c, s_ = np.cos(pos * inv), np.sin(pos * inv)
+        want = np.concatenate([k[:, :hd // 2] * c - k[:, hd // 2:] * s_, k[:, hd // 2:] * c + k[:, :hd // 2] * s_], -1)
+        assert np.allclose(tail["k_new"][0][b, K], want, rtol=1e-12, atol=1e-12)
+
+
 def test_requests_are_independent():
     # a request's draft depends only on its own state and cache
     W = _weights64(MINI, 24)
