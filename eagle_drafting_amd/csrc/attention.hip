@@ -51,7 +51,7 @@ size_t attn_partial_floats(int M, int Hq, int hd, const AttnPlan& p) {
 // NW: waves per workgroup, 4 or (when more than 64 query rows share a kv head) 8; each wave owns one
 // 16-row tile of the kv head's query rows
 template <int HD, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc,
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) void attn_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc,
                                                         const bf16_t* __restrict__ Vc,
                                                         const int* __restrict__ seq_len,
                                                         const int* __restrict__ req_slot, int K, int Hq, int Hkv,
@@ -67,6 +67,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(const bf16_t* __rest
   constexpr int C8 = HD / 8;                  // 16-byte pieces per key row
   constexpr int PK = KEYS * C8 / (NW * 64);   // keys staged per thread per round (4 or 2)
   constexpr int NR = 1;
+  // sVt row d holds key k at column k ^ 8 vsw(d): rotating whole 8-key blocks keeps every read of 8
+  // consecutive keys contiguous while the staging writes (4 or 2 keys of 8 dimensions per thread) hit
+  // distinct banks
+  auto vsw = [](int dim) { return HD == 128 ? (dim >> 4) & 7 : (dim >> 3) & 14; };
   // sK row of key k within a round: key 32 a' + 8 a + 4 h + r sits at row 32 a' + 16 h + 4 a + r, so score
   // tile h's MFMA row 4 a + r is key 8 a + 4 h + r
   __shared__ __attribute__((aligned(16))) char smem[(KEYS * STR + HD * VSTR) * sizeof(bf16_t)];
@@ -121,7 +125,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(const bf16_t* __rest
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      bf16_t* dst = sVt + (8 * c8 + e) * VSTR + PK * kq;
+      bf16_t* dst = sVt + (8 * c8 + e) * VSTR + ((PK * kq) ^ (8 * vsw(8 * c8 + e)));
       const uint32_t w0 = (uint32_t)(uint16_t)rv[0][e] | ((uint32_t)(uint16_t)rv[1][e] << 16);
       if (PK == 4) {
         uint2 w;
@@ -191,35 +195,44 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(const bf16_t* __rest
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int k0 = tb + 8 * lq + r, k1 = k0 + 4;  // keys of score rows 4 lq + r of tiles 0 and 1
-            sv[r] = k0 < lim ? s0[r] * scale : -INFINITY;
+            sv[r] = k0 < lim ? s0[r] * scale : -INFINITY;  // scores in log2 units (scale includes log2 e)
             sv[4 + r] = k1 < lim ? s1[r] * scale : -INFINITY;
             tmax = fmaxf(tmax, fmaxf(sv[r], sv[4 + r]));
           }
           tmax = fmaxf(tmax, __shfl_xor(tmax, 16, PE_WAVE));
           tmax = fmaxf(tmax, __shfl_xor(tmax, 32, PE_WAVE));
           const float mnew = fmaxf(m_run[t], tmax);
-          alpha[t] = __expf(m_run[t] - mnew);
-          float psum = 0.f;
+          alpha[t] = __builtin_amdgcn_exp2f(m_run[t] - mnew);
+          float psum = 0.f, pe[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {  // pf element e: key tb + 8 lq + e
-            const float pe = __expf(sv[e] - mnew);
-            psum += pe;
-            pf[t][e] = (short)f32_to_bf16(pe);
+            pe[e] = __builtin_amdgcn_exp2f(sv[e] - mnew);
+            psum += pe[e];
           }
+          typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+          const u32x4_t pk = {f32x2_to_bf16x2(pe[0], pe[1]), f32x2_to_bf16x2(pe[2], pe[3]),
+                              f32x2_to_bf16x2(pe[4], pe[5]), f32x2_to_bf16x2(pe[6], pe[7])};
+          pf[t] = __builtin_bit_cast(bf16x8_t, pk);
           psum += __shfl_xor(psum, 16, PE_WAVE);
           psum += __shfl_xor(psum, 32, PE_WAVE);
           l_run[t] = l_run[t] * alpha[t] + psum;
           m_run[t] = mnew;
         }
+        // the running max rarely moves after the first tiles: skip the rescale when no lane's did
+        bool rescale[NR];
+#pragma unroll
+        for (int t = 0; t < NR; ++t) rescale[t] = __any(alpha[t] != 1.f);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-          const bf16x8_t va = *(const bf16x8_t*)(sVt + (ct * 16 + lr) * VSTR + kt * KT + 8 * lq);
+          const bf16x8_t va =
+              *(const bf16x8_t*)(sVt + (ct * 16 + lr) * VSTR + ((kt * KT + 8 * lq) ^ (8 * vsw(ct * 16 + lr))));
 #pragma unroll
           for (int t = 0; t < NR; ++t) {
             if (t >= nrt) continue;
             f32x4_t acc = o[t][ct];
+            if (rescale[t])
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] *= alpha[t];
+              for (int r = 0; r < 4; ++r) acc[r] *= alpha[t];
             o[t][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[t], acc, 0, 0, 0);
           }
         }
@@ -250,7 +263,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(const bf16_t* __rest
       const float* slot = red + (size_t)((q - 1) * RT + rt0) * 16 * (HD + 2) + lr * (HD + 2);
       const float mq = slot[HD], lqs = slot[HD + 1];
       const float mn = fmaxf(m_run[0], mq);
-      const float a0 = __expf(m_run[0] - mn), aq = __expf(mq - mn);
+      const float a0 = __builtin_amdgcn_exp2f(m_run[0] - mn), aq = __builtin_amdgcn_exp2f(mq - mn);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -279,7 +292,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(const bf16_t* __rest
   }
 }
 
-// O[b*K + j][h] = sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s over the splits that hold keys. One
+// O[b*K + j][h] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the splits that hold keys (m in log2
+// units, as the partial kernel keeps its scores). One
 // workgroup per query row: 4 groups of 64 threads take every 4th split (HD / 64 columns per thread),
 // then the groups are added in a fixed order.
 template <int HD>
@@ -316,7 +330,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   // pass 2: weights w_s = e^(m_s - M) (each thread rewrites the entries it wrote) and the denominator
   float den = 0.f;
   for (int s = tid; s < ns; s += 256) {
-    const float w = __expf(sw[s] - M);
+    const float w = __builtin_amdgcn_exp2f(sw[s] - M);  // m_s are in log2 units
     sw[s] = w;
     den += w * src[(size_t)s * (HD + 2) + HD + 1];
   }
@@ -346,7 +360,8 @@ hipError_t launch_attention_bf16(const AttnPlan& p, const void* Q, const void* K
                                  const int* seq_len, const int* req_slot, int B, int K, int Hq, int Hkv, int hd,
                                  int max_ctx, int n_slots, float* part, hipStream_t st) {
   dim3 grid(B * Hkv, p.nsplit);
-  const float scale = 1.0f / sqrtf((float)hd);
+  // 1/sqrt(hd) and log2(e): scores, maxima and partial m are kept in log2 units (exp2 on the hardware)
+  const float scale = 1.0f / sqrtf((float)hd) * 1.4426950408889634f;
   const bool eight = (Hq / Hkv) * K > 64;
 #define PE_ATTN_LAUNCH(HDV, NWV)                                                                                   \
   hipLaunchKernelGGL((attn_bf16_kernel<HDV, NWV>), grid, dim3(NWV * 64), 0, st, (const bf16_t*)Q, (const bf16_t*)Kc, \

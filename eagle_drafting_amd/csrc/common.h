@@ -18,12 +18,13 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// round to nearest even; NaN stays NaN
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+// round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+typedef __bf16 hw_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float hw_f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+// two values in one instruction: a in the low half, b in the high half
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((hw_f32x2_t){a, b}, hw_bf16x2_t));
 }
 
 template <typename T> __device__ __forceinline__ float to_f32(T v);
