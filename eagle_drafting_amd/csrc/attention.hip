@@ -199,8 +199,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) vo
             sv[4 + r] = k1 < lim ? s1[r] * scale : -INFINITY;
             tmax = fmaxf(tmax, fmaxf(sv[r], sv[4 + r]));
           }
-          tmax = fmaxf(tmax, __shfl_xor(tmax, 16, PE_WAVE));
-          tmax = fmaxf(tmax, __shfl_xor(tmax, 32, PE_WAVE));
+          tmax = rows_max(tmax);  // over the 4 lanes (l, l ^ 16, l ^ 32, l ^ 48) of query row lr
           const float mnew = fmaxf(m_run[t], tmax);
           alpha[t] = __builtin_amdgcn_exp2f(m_run[t] - mnew);
           float psum = 0.f, pe[8];
@@ -213,8 +212,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) vo
           const u32x4_t pk = {f32x2_to_bf16x2(pe[0], pe[1]), f32x2_to_bf16x2(pe[2], pe[3]),
                               f32x2_to_bf16x2(pe[4], pe[5]), f32x2_to_bf16x2(pe[6], pe[7])};
           pf[t] = __builtin_bit_cast(bf16x8_t, pk);
-          psum += __shfl_xor(psum, 16, PE_WAVE);
-          psum += __shfl_xor(psum, 32, PE_WAVE);
+          psum = rows_sum(psum);
           l_run[t] = l_run[t] * alpha[t] + psum;
           m_run[t] = mnew;
         }
