@@ -76,21 +76,30 @@ GemmPlan plan_gemm(int M, int N, int Kd, bool argmax) {
   const int Ks = k_steps(Kd);
   p.Nt = n_tiles(N);
   p.tiled = 0;
+  p.ksplit = 1;
+  p.kper = Ks;
   if (M > 32) {
-    // 128 x 128 tiles read each weight once per 128 rows and each activation once per 128 columns. The
-    // skinny kernel re-reads the activations once per 16 columns, which dominates once M > 32 unless the
-    // tiled grid would be too small to keep the weight stream going (narrow outputs, N / 128 * M / 128 <
-    // 64 workgroups); the LM head always has enough columns.
+    // 128 x 128 tiles read each weight once per 128 rows and each activation once per 128 columns (the
+    // skinny kernel re-reads the activations once per 16 columns). Narrow or short products get too few
+    // tiles to keep the weight stream going; they split the reduction over workgroups (about 512 in all,
+    // at least 8 k-steps each) as long as the fp32 partials stay within the weight bytes
+    // (2 ksplit M N 4 <= N Kd 2); a second kernel adds the partials and runs the epilogue.
     const int tg = (p.Nt + 7) / 8, tm = (M + 127) / 128;
-    if (argmax || tg * tm >= 64 || M >= 256) {
-      p.tiled = 1;
-      p.MT = 8;
-      p.NT = 8;
-      p.NW = 4;
-      p.mblocks = tm;
-      p.ngroups = tg;
-      return p;
+    p.tiled = 1;
+    p.MT = 8;
+    p.NT = 8;
+    p.NW = 4;
+    p.mblocks = tm;
+    p.ngroups = tg;
+    if (!argmax) {
+      int ks = 1;
+      while (tg * tm * ks < 512 && Ks >= 16 * ks && 8LL * ks * M <= Kd) ks *= 2;
+      if (ks > 1) {
+        p.kper = (((Ks + ks - 1) / ks) + 3) & ~3;
+        p.ksplit = (Ks + p.kper - 1) / p.kper;
+      }
     }
+    return p;
   }
   p.MT = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
   p.mblocks = (M + 16 * p.MT - 1) / (16 * p.MT);
@@ -394,6 +403,8 @@ hipError_t launch_gemm(const GemmPlan& p, GemmArgs a, int a_mode, int epi, hipSt
   a.Ks = k_steps(a.Kd);
   a.ngroups = p.ngroups;
   a.mblocks = p.mblocks;
+  a.ksplit = p.ksplit;
+  a.kper = p.kper;
   if (p.tiled) return launch_gemm_tiled(p, a, a_mode, epi, st);
   if (epi == EPI_ARGMAX) {
     if (a_mode != A_NORM || p.NT != 4 || p.NW != 4) return hipErrorInvalidValue;

@@ -20,7 +20,16 @@
 
 namespace pe {
 
-template <int AM, int EP>
+// Product tile epilogue (defined below): Cs holds the 128 x 128 fp32 tile, column-swizzled; with SCALE,
+// s_inv[r] is row r's 1/RMS.
+template <int EP, bool SCALE>
+__device__ void tile_epilogue(const GemmArgs& g, const float* Cs, const float* s_inv, int m0, int nt0, int ng,
+                              int rbeg = 0, int rend = 128);
+
+// SPLIT: the workgroup covers k-steps [blockIdx.y * g.kper, + g.kper) and writes its fp32 partial tile
+// (row-scaled for a normalised operand) to g.part[blockIdx.y]; gemm_split_reduce_kernel adds the partials
+// in a fixed order and runs the epilogue.
+template <int AM, int EP, bool SPLIT>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
   constexpr int BM = 128, BN = 128;
   __shared__ __attribute__((aligned(16))) char smem[2 * 2 * 2 * 8 * 64 * 16];  // 64 KiB: product tile; A buffers in the first half
@@ -41,7 +50,9 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
   const int nt0 = ng * 8;
   // stages of 64 reduction columns, rounded up to an even count; activation loads past the last k-step
   // return zeros (out-of-range buffer offset), so padded stages add nothing and the loop has no branches
-  const int nstage = ((Ks + 1) / 2 + 1) & ~1;
+  const int kb = SPLIT ? blockIdx.y * g.kper : 0;                // first k-step of this workgroup
+  const int ke = SPLIT ? min(Ks, kb + g.kper) : Ks;               // end of its k-steps
+  const int nstage = SPLIT ? g.kper / 2 : ((Ks + 1) / 2 + 1) & ~1;  // even (kper is a multiple of 4)
 
   const __amdgpu_buffer_rsrc_t a_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, (gemm_a_row(g, M - 1) + 1) * g.lda * 2, 0x00020000);
@@ -65,10 +76,10 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
     for (int q = 0; q < 4; ++q) {
       const int p = tid + 256 * q;
       const int arow = p >> 3, seg = p & 7;
-      const int akstep = 2 * st + (seg >> 2);
+      const int akstep = kb + 2 * st + (seg >> 2);
       const int row = m0 + arow;
       const int off =
-          row < M && akstep < Ks ? (gemm_a_row(g, row) * g.lda + akstep * 32 + 8 * (seg & 3)) * 2 : 0x7ffffff0;
+          row < M && akstep < ke ? (gemm_a_row(g, row) * g.lda + akstep * 32 + 8 * (seg & 3)) * 2 : 0x7ffffff0;
       r[q] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0));
     }
   };
@@ -79,7 +90,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int kstep = min(2 * st + ks, Ks - 1);
+          const int kstep = min(kb + 2 * st + ks, Ks - 1);
           const int ntile = min(nt0 + wn * 4 + 2 * j + fr_t, Nt - 1);
           r[(ks * 2 + u) * 2 + j] = W[((size_t)ntile * Ks + kstep) * 64 + fr_l + 32 * u];
         }
@@ -181,10 +192,62 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
   }
   __syncthreads();
 
+  if (SPLIT) tile_epilogue<EPI_PARTIAL, AM == A_NORM>(g, Cs, s_inv, m0, nt0, ng);
+  else tile_epilogue<EP, AM == A_NORM>(g, Cs, s_inv, m0, nt0, ng);
+}
+
+// the fixed-order sum of the K-split partials of rows [16 y, 16 y + 16) of one 128 x 128 tile
+// (y = blockIdx.y), then the epilogue of those rows
+template <int EP>
+__global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs g) {
+  constexpr int BN = 128, RS = 16;
+  __shared__ __attribute__((aligned(16))) float Cl[RS * BN];
+  const int M = g.M, N = g.N;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int ng = (slot / g.mblocks) * 8 + xcd;
+  if (ng >= g.ngroups) return;
+  const int m0 = (slot % g.mblocks) * 128;
+  const int rbeg = RS * blockIdx.y;
+  if (m0 + rbeg >= M) return;
+  float* Cs = Cl - rbeg * BN;  // tile-row indexing: rows rbeg .. rbeg + 15 live in Cl
+  const int nt0 = ng * 8;
+  const int n0 = nt0 * 16;
+  const bool vec = (N & 3) == 0;
+  for (int q = threadIdx.x; q < RS * BN / 4; q += 256) {
+    const int rl = rbeg + (q >> 5), c0 = 4 * (q & 31);
+    const int m = m0 + rl, n = n0 + c0;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (m < M) {
+      for (int k = 0; k < g.ksplit; ++k) {
+        const float* src = g.part + ((size_t)k * M + m) * N + n;
+        if (vec && n + 3 < N) {
+          const float4 v = *(const float4*)src;
+          acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        } else {
+          if (n < N) acc.x += src[0];
+          if (n + 1 < N) acc.y += src[1];
+          if (n + 2 < N) acc.z += src[2];
+          if (n + 3 < N) acc.w += src[3];
+        }
+      }
+    }
+    *(float4*)&Cs[rl * BN + (c0 ^ (((rl >> 2) & 1) << 5))] = acc;
+  }
+  __syncthreads();
+  tile_epilogue<EP, false>(g, Cs, nullptr, m0, nt0, ng, rbeg, rbeg + RS);
+}
+
+template <int EP, bool SCALE>
+__device__ void tile_epilogue(const GemmArgs& g, const float* Cs, const float* s_inv, int m0, int nt0, int ng,
+                              int rbeg, int rend) {
+  constexpr int BM = 128, BN = 128;
+  const int M = g.M, N = g.N, Nt = g.Nt;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+
   // 4 consecutive columns [c0, c0 + 4) of local row rl, scaled by 1/RMS for a normalised operand
   auto cload = [&](int rl, int c0) {
     float4 v = *(const float4*)&Cs[rl * BN + (c0 ^ (((rl >> 2) & 1) << 5))];
-    if (AM == A_NORM) {
+    if (SCALE) {
       const float s = s_inv[rl];
       v.x *= s; v.y *= s; v.z *= s; v.w *= s;
     }
@@ -192,11 +255,32 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
   };
   const int n0 = nt0 * 16;
 
+  if (EP == EPI_PARTIAL) {
+    // raw (row-scaled) partial tile of K-split blockIdx.y
+    const int h = lane & 31;
+    const int c0 = 4 * h, n = n0 + c0;
+    for (int rl = rbeg + 2 * wave + (lane >> 5); rl < rend; rl += 8) {
+      const int m = m0 + rl;
+      if (m >= M) continue;
+      const float4 v = cload(rl, c0);
+      float* dst = g.part + ((size_t)blockIdx.y * M + m) * N + n;
+      if (n + 3 < N && (N & 3) == 0) {
+        *(float4*)dst = v;
+      } else {
+        if (n < N) dst[0] = v.x;
+        if (n + 1 < N) dst[1] = v.y;
+        if (n + 2 < N) dst[2] = v.z;
+        if (n + 3 < N) dst[3] = v.w;
+      }
+    }
+    return;
+  }
+
   if (EP == EPI_ARGMAX || EP == EPI_RESID || EP == EPI_ROWS) {
     // half a wave per row: lane h (0..31) holds columns 4h..4h+3; 8 rows per pass
     const int h = lane & 31;
     const int c0 = 4 * h, n = n0 + c0;
-    for (int rl = 2 * wave + (lane >> 5); rl < BM; rl += 8) {
+    for (int rl = rbeg + 2 * wave + (lane >> 5); rl < rend; rl += 8) {
       const int m = m0 + rl;
       const float4 v = cload(rl, c0);
       const float vv[4] = {v.x, v.y, v.z, v.w};
@@ -297,7 +381,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
   const int ch = tid & 15;
   const int t = ch >> 1, e0 = 4 * (ch & 1);
   const int nt = nt0 + t;
-  for (int rl = tid >> 4; rl < BM; rl += 16) {
+  for (int rl = rbeg + (tid >> 4); rl < rend; rl += 16) {
     const int m = m0 + rl;
     if (m >= M || nt >= Nt) continue;
     const float4 a4 = cload(rl, 16 * t + e0), b4 = cload(rl, 16 * t + 8 + e0);
@@ -357,12 +441,29 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
 }
 
 hipError_t launch_gemm_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st) {
-  dim3 grid(8 * ((p.ngroups + 7) / 8) * p.mblocks), block(256);
-  if (a_mode == A_BF16 && epi == EPI_RESID) hipLaunchKernelGGL((gemm_tiled_kernel<A_BF16, EPI_RESID>), grid, block, 0, st, a);
-  else if (a_mode == A_BF16 && epi == EPI_ROWS) hipLaunchKernelGGL((gemm_tiled_kernel<A_BF16, EPI_ROWS>), grid, block, 0, st, a);
-  else if (a_mode == A_NORM && epi == EPI_QKV) hipLaunchKernelGGL((gemm_tiled_kernel<A_NORM, EPI_QKV>), grid, block, 0, st, a);
-  else if (a_mode == A_NORM && epi == EPI_SWIGLU) hipLaunchKernelGGL((gemm_tiled_kernel<A_NORM, EPI_SWIGLU>), grid, block, 0, st, a);
-  else if (a_mode == A_NORM && epi == EPI_ARGMAX) hipLaunchKernelGGL((gemm_tiled_kernel<A_NORM, EPI_ARGMAX>), grid, block, 0, st, a);
+  const int tiles = 8 * ((p.ngroups + 7) / 8) * p.mblocks;
+  const dim3 block(256);
+  if (p.ksplit > 1) {
+    if (!a.part || epi == EPI_ARGMAX) return hipErrorInvalidValue;
+    const dim3 grid(tiles, p.ksplit);
+    if (a_mode == A_BF16) hipLaunchKernelGGL((gemm_tiled_kernel<A_BF16, EPI_PARTIAL, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((gemm_tiled_kernel<A_NORM, EPI_PARTIAL, true>), grid, block, 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 rgrid(tiles, 8);  // 16-row slices of each tile
+    if (epi == EPI_RESID) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_RESID>), rgrid, block, 0, st, a);
+    else if (epi == EPI_ROWS) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_ROWS>), rgrid, block, 0, st, a);
+    else if (epi == EPI_QKV) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_QKV>), rgrid, block, 0, st, a);
+    else if (epi == EPI_SWIGLU) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_SWIGLU>), rgrid, block, 0, st, a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
+  const dim3 grid(tiles);
+  if (a_mode == A_BF16 && epi == EPI_RESID) hipLaunchKernelGGL((gemm_tiled_kernel<A_BF16, EPI_RESID, false>), grid, block, 0, st, a);
+  else if (a_mode == A_BF16 && epi == EPI_ROWS) hipLaunchKernelGGL((gemm_tiled_kernel<A_BF16, EPI_ROWS, false>), grid, block, 0, st, a);
+  else if (a_mode == A_NORM && epi == EPI_QKV) hipLaunchKernelGGL((gemm_tiled_kernel<A_NORM, EPI_QKV, false>), grid, block, 0, st, a);
+  else if (a_mode == A_NORM && epi == EPI_SWIGLU) hipLaunchKernelGGL((gemm_tiled_kernel<A_NORM, EPI_SWIGLU, false>), grid, block, 0, st, a);
+  else if (a_mode == A_NORM && epi == EPI_ARGMAX) hipLaunchKernelGGL((gemm_tiled_kernel<A_NORM, EPI_ARGMAX, false>), grid, block, 0, st, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -28,6 +28,8 @@ struct GemmPlan {
   int NW;       // waves per workgroup (they split the reduction dimension NW/NT ways)
   int ngroups;  // workgroups along N
   int tiled;    // 1: LDS-tiled 128 x 128 kernel (larger M); 0: skinny split-K kernel
+  int ksplit;   // tiled: workgroups along the reduction dimension (1 = none); > 1 adds a reduce kernel
+  int kper;     // tiled: k-steps (32 columns each) per split, a multiple of 4
 };
 GemmPlan plan_gemm(int M, int N, int Kd, bool argmax);
 // Partial sums of squares per row that a residual-stream producer with plan p writes (one per 16 columns
@@ -39,11 +41,12 @@ inline int gemm_ssq_parts(const GemmPlan& p) { return p.tiled ? p.ngroups : p.Nt
 // (written by the producer of x), and the epilogue scales each product row by 1/RMS(x) from the
 // producer's per-16-column sums of squares (RMSNorm is a per-row scale).
 enum { A_BF16 = 0, A_NORM = 1 };
-enum { EPI_RESID = 0, EPI_ROWS = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_ARGMAX = 4 };
+enum { EPI_RESID = 0, EPI_ROWS = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_ARGMAX = 4,
+       EPI_PARTIAL = 5 /* tiled K-split: raw partial tile, internal */ };
 
 struct GemmArgs {
   int M, Kd, N;
-  int Nt, Ks, ngroups, mblocks;  // filled by launch_gemm from the plan
+  int Nt, Ks, ngroups, mblocks;  // filled by launch_gemm from the plan (with ksplit, kper)
   // A operand
   const uint16_t* A; int lda;
   const float* ssq_in; int nssq; float eps;  // A_NORM
@@ -64,6 +67,8 @@ struct GemmArgs {
   // row m of the product reads operand row (m / rows_out) * rows_in + m % rows_out (and that row's sums
   // of squares): the LM head runs on rows_out of every rows_in rows per request. 0 = identity.
   int rows_in, rows_out;
+  // tiled K-split: fp32 partial tiles [ksplit][M][N] (workspace) and the plan's split shape
+  float* part; int ksplit, kper;
 };
 // operand row of product row m
 __host__ __device__ inline int gemm_a_row(const GemmArgs& g, int m) {

@@ -35,7 +35,8 @@ struct pe_ctx {
   void* Qb = nullptr;      // rotated queries [Mmax, Hq hd]
   void* Ob = nullptr;      // attention output [Mmax, Hq hd]
   void* Ab = nullptr;      // SwiGLU output [Mmax, F]
-  float* P = nullptr;      // split-K partials
+  float* P = nullptr;      // fp32 path: projection outputs
+  float* part = nullptr;   // tiled projections: K-split partial tiles
   float* attn = nullptr;   // attention split partials
   float* am_val = nullptr; // argmax partials
   int* am_idx = nullptr;
@@ -210,11 +211,18 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
   }
 
   // ---- workspace sizes (maxima over every B <= max_batch, K <= max_k)
-  size_t p_floats = 0, attn_floats = 0, am_floats = 0;
+  size_t p_floats = 0, attn_floats = 0, am_floats = 0, part_floats = 0;
   for (int M = 1; M <= Mmax; ++M) {
     if (ctx->bf16) {
       GemmPlan pl = plan_gemm(M, V, d, true);
       am_floats = std::max(am_floats, (size_t)M * pl.ngroups);
+      // K-split partials of the layer projections (and of the row build, whose M is B)
+      const int shapes[5][2] = {{qkvd, d}, {d, qd}, {2 * F, d}, {d, F}, {d, 3 * d}};
+      for (int sh = 0; sh < 5; ++sh) {
+        if (sh == 4 && M > c.max_batch) continue;
+        const GemmPlan ps = plan_gemm(M, shapes[sh][0], shapes[sh][1], false);
+        if (ps.ksplit > 1) part_floats = std::max(part_floats, (size_t)ps.ksplit * M * shapes[sh][0]);
+      }
     } else {
       p_floats = std::max(p_floats, (size_t)M * std::max(std::max(qkvd, 2 * F), d));
       am_floats = std::max(am_floats, (size_t)M * plan_argmax_chunks(M, V));
@@ -242,7 +250,7 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
                oAt = take(std::max(attn_floats, (size_t)1) * 4), oAv = take(am_floats * 4), oAi = take(am_floats * 4),
                oT = take((size_t)c.max_batch * (c.max_k + 1) * 4),
                oL = take(ctx->bf16 ? 0 : (size_t)Mmax * V * 4), oR = take((size_t)c.max_ctx * (hd / 2) * 8),
-               oS = take((size_t)Mmax * nssq * 4), oF = take(256);
+               oS = take((size_t)Mmax * nssq * 4), oF = take(256), oK = take(part_floats * 4);
   if (hipMalloc((void**)&ctx->ws, off) != hipSuccess) {
     free_ctx(ctx);
     return fail(nullptr, PE_ERR_OOM, "hipMalloc of workspace failed");
@@ -262,6 +270,7 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
   ctx->rope = (float2*)(b + oR);
   ctx->ssq = (float*)(b + oS);
   ctx->flags = (int*)(b + oF);
+  ctx->part = part_floats ? (float*)(b + oK) : nullptr;
 
   hipError_t r = launch_rope_table(ctx->rope, c.max_ctx, hd, (double)c.rope_base, ctx->stream);
   if (r == hipSuccess) r = hipMemsetAsync(ctx->flags, 0, 256, ctx->stream);
@@ -407,6 +416,7 @@ static pe_status draft_bf16(pe_ctx* ctx, int32_t B, int32_t K, int32_t Kout, con
   base.ssq_out = ctx->ssq;
   base.eps = c.rms_eps;
   base.flags = ctx->flags;
+  base.part = ctx->part;
 
   // a1 (+ the sums of squares for layer 0's RMSNorm): the K input rows of every request
   if (!rows) {
