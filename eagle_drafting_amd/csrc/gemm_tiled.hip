@@ -217,13 +217,28 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs g) {
     const int rl = rbeg + (q >> 5), c0 = 4 * (q & 31);
     const int m = m0 + rl, n = n0 + c0;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (m < M) {
+    if (m < M && vec && n + 3 < N) {
+      // four partials' loads in flight at a time; added in split order
+      const float* src = g.part + (size_t)m * N + n;
+      const size_t stride = (size_t)M * N;
+      int k = 0;
+      for (; k + 4 <= g.ksplit; k += 4) {
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = *(const float4*)(src + (k + u) * stride);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w;
+        }
+      }
+      for (; k < g.ksplit; ++k) {
+        const float4 v = *(const float4*)(src + k * stride);
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      }
+    } else if (m < M) {
       for (int k = 0; k < g.ksplit; ++k) {
         const float* src = g.part + ((size_t)k * M + m) * N + n;
-        if (vec && n + 3 < N) {
-          const float4 v = *(const float4*)src;
-          acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-        } else {
+        {
           if (n < N) acc.x += src[0];
           if (n + 1 < N) acc.y += src[1];
           if (n + 2 < N) acc.z += src[2];
