@@ -7,8 +7,10 @@
 // layout of the packed weights); weights go from the packed fragments straight into registers (each
 // fragment is used by the two waves of a column half). Activation loads run two stages ahead, weight
 // loads one; the stage loop is branch-free (even stage count, zero activations past the end), so the
-// compiler's wait counts stay exact, and the next fragment pair is read from LDS while the current
-// products run.
+// compiler's wait counts stay exact. The 12 global loads of a stage are issued three at a time between
+// the four MFMA groups (the per-CU vector-memory path takes ~16 cycles per 1 KiB wave load, so issuing
+// them back to back stalls the wave for most of a stage), and the next fragment pair is read from LDS
+// while the current products run.
 //
 // Epilogue: the 128 x 128 fp32 product tile is written into the same 64 KiB of LDS (column XOR-swizzle so
 // the two lane halves of the accumulator layout hit distinct banks), then read back as 16-byte row chunks:
@@ -71,9 +73,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
   // 32 x 32 x 16 products out of the 16 x 32 fragments: lane l of the operand of rows (or columns)
   // 32 b .. 32 b + 31 and k-half u takes fragment 2 b + (l % 32) / 16, fragment lane l % 16 + 16 (2 u + l / 32)
   const int fr_t = (lane & 31) >> 4, fr_l = (lane & 15) + 16 * (lane >> 5);
-  auto gload_a = [&](RegA& r, int st) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
+  auto gload_a1 = [&](RegA& r, int st, int q) {
+    {
       const int p = tid + 256 * q;
       const int arow = p >> 3, seg = p & 7;
       const int akstep = kb + 2 * st + (seg >> 2);
@@ -83,17 +84,19 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
       r[q] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0));
     }
   };
+  auto gload_b1 = [&](RegB& r, int st, int idx) {  // idx = (ks * 2 + u) * 2 + j
+    const int ks = idx >> 2, u = (idx >> 1) & 1, j = idx & 1;
+    const int kstep = min(kb + 2 * st + ks, Ks - 1);
+    const int ntile = min(nt0 + wn * 4 + 2 * j + fr_t, Nt - 1);
+    r[idx] = W[((size_t)ntile * Ks + kstep) * 64 + fr_l + 32 * u];
+  };
+  auto gload_a = [&](RegA& r, int st) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) gload_a1(r, st, q);
+  };
   auto gload_b = [&](RegB& r, int st) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int kstep = min(kb + 2 * st + ks, Ks - 1);
-          const int ntile = min(nt0 + wn * 4 + 2 * j + fr_t, Nt - 1);
-          r[(ks * 2 + u) * 2 + j] = W[((size_t)ntile * Ks + kstep) * 64 + fr_l + 32 * u];
-        }
+    for (int idx = 0; idx < 8; ++idx) gload_b1(r, st, idx);
   };
   auto sstore = [&](const RegA& r, int buf) {
 #pragma unroll
@@ -111,9 +114,10 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-  // four groups (k-step, k-half) of four products; the two A fragments of the next group are read from
-  // LDS while the current group's products run
-  auto compute = [&](int buf, const RegB& rb) {
+  // four groups (k-step, k-half) of four products; each group first reads the next group's A fragments
+  // from LDS and issues three of the 12 global loads of a later stage (one activation piece, two weight
+  // fragments), so the vector-memory path works while the products run instead of before them
+  auto compute_load = [&](int buf, const RegB& rb, RegA& ra_next, int st_a, RegB& rb_next, int st_b) {
     bf16x8_t af[2], an[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) af[i] = As[buf][0][wm * 4 + 2 * i + fr_t][asw(fr_l)];
@@ -125,6 +129,9 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) an[i] = As[buf][ks1][wm * 4 + 2 * i + fr_t][asw(fr_l + 32 * u1)];
       }
+      gload_a1(ra_next, st_a, gi);
+      gload_b1(rb_next, st_b, 2 * gi);
+      gload_b1(rb_next, st_b, 2 * gi + 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -147,18 +154,10 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
   __syncthreads();
   for (int st = 0; st < nstage; st += 2) {
     // loads past the end (stages nstage, nstage + 1) read zeros / valid clamped weights and are unused
-    gload_a(ra0, st + 2);
-    gload_b(rb1, st + 1);
-    __builtin_amdgcn_sched_barrier(0);  // issue the loads before the products, store after them
-    compute(0, rb0);
-    __builtin_amdgcn_sched_barrier(0);
+    compute_load(0, rb0, ra0, st + 2, rb1, st + 1);
     sstore(ra1, 1);
     __syncthreads();
-    gload_a(ra1, st + 3);
-    gload_b(rb0, st + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(1, rb1);
-    __builtin_amdgcn_sched_barrier(0);
+    compute_load(1, rb1, ra1, st + 3, rb0, st + 2);
     sstore(ra0, 0);
     __syncthreads();
   }
