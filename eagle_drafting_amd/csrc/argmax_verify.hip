@@ -84,34 +84,47 @@ __device__ __forceinline__ int am_row_reduce(const float* __restrict__ pv, const
   return i;
 }
 
-// one workgroup per row: each wave reduces a quarter of the partials, then the four are combined
-__global__ __launch_bounds__(256) void argmax_final_kernel(const float* __restrict__ pv, const int* __restrict__ pi,
-                                                           int rows, int nchunks, int* __restrict__ out) {
-  __shared__ float sv[4];
-  __shared__ int si[4];
+// one workgroup of 16 waves per row: every thread reduces a strided share of the partials, then the waves
+// are combined in a fixed order
+__global__ __launch_bounds__(1024) void argmax_final_kernel(const float* __restrict__ pv, const int* __restrict__ pi,
+                                                            int rows, int nchunks, int* __restrict__ out) {
+  __shared__ float sv[16];
+  __shared__ int si[16];
   const int row = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int q = (nchunks + 3) / 4;
-  const int c0 = wave * q, c1 = min(nchunks, c0 + q);
+  const float* v = pv + (size_t)row * nchunks;
+  const int* ix = pi + (size_t)row * nchunks;
   float b = -INFINITY;
   int i = 0x7fffffff;
-  for (int c = c0 + lane; c < c1; c += 64) {
-    const float v = pv[(size_t)row * nchunks + c];
-    const int k = pi[(size_t)row * nchunks + c];
-    if (am_better(v, k, b, i)) { b = v; i = k; }
+  // four chunks per thread per pass, loaded before any is compared (the winner does not depend on the
+  // visiting order: ties go to the smaller index)
+  int c = threadIdx.x;
+  for (; c + 3 * 1024 < nchunks; c += 4 * 1024) {
+    float x[4];
+    int k[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      x[u] = v[c + u * 1024];
+      k[u] = ix[c + u * 1024];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (am_better(x[u], k[u], b, i)) { b = x[u]; i = k[u]; }
   }
+  for (; c < nchunks; c += 1024)
+    if (am_better(v[c], ix[c], b, i)) { b = v[c]; i = ix[c]; }
   am_wave_reduce(b, i, 64);
   if (lane == 0) { sv[wave] = b; si[wave] = i; }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int w = 1; w < 4; ++w)
+    for (int w = 1; w < 16; ++w)
       if (am_better(sv[w], si[w], b, i)) { b = sv[w]; i = si[w]; }
     out[row] = i;
   }
 }
 
 hipError_t launch_argmax_final(const float* pv, const int* pi, int rows, int nchunks, int* out, hipStream_t st) {
-  hipLaunchKernelGGL(argmax_final_kernel, dim3(rows), dim3(256), 0, st, pv, pi, rows, nchunks, out);
+  hipLaunchKernelGGL(argmax_final_kernel, dim3(rows), dim3(1024), 0, st, pv, pi, rows, nchunks, out);
   return hipGetLastError();
 }
 

@@ -104,16 +104,23 @@ GemmPlan plan_gemm(int M, int N, int Kd, bool argmax) {
   p.MT = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
   p.mblocks = (M + 16 * p.MT - 1) / (16 * p.MT);
   if (argmax) {
-    p.NT = 4;
-    p.NW = 4;
+    // vocabulary projection: up to 16 rows, one 16-column tile per workgroup with 8 waves splitting k
+    // (about 9.5 k short workgroups balance across the compute units better than fewer long ones);
+    // more rows keep four tiles per workgroup, one wave each
+    p.NT = p.MT == 1 ? 1 : 4;
+    p.NW = p.MT == 1 ? 8 : 4;
   } else {
     p.NT = 1;
-    // about one residency round of waves in total (~4096), each wave streaming at least 8 k-steps;
+    // about one residency round of waves in total (~4096), each wave streaming at least 8 k-steps and
+    // not a partial second round of 8 (measured: 24 k-steps per wave beat 12, 8 beat 16);
     // the register budget caps NW by MT (LDS for the cross-wave sum is NW * MT KiB)
     const int cap = p.MT == 1 ? 16 : p.MT == 2 ? 8 : 4;
     const int groups = p.Nt * p.mblocks;
     int nw = 4;
-    while (nw < cap && groups * nw * 2 <= 4096 && Ks / (2 * nw) >= 8) nw *= 2;
+    auto per_wave = [&](int w) { return Ks / w; };
+    while (nw < cap && groups * nw * 2 <= 4096 && per_wave(2 * nw) >= 8 &&
+           !(per_wave(2 * nw) > 8 && per_wave(2 * nw) < 16))
+      nw *= 2;
     p.NW = nw;
   }
   p.ngroups = (p.Nt + p.NT - 1) / p.NT;
@@ -407,7 +414,12 @@ hipError_t launch_gemm(const GemmPlan& p, GemmArgs a, int a_mode, int epi, hipSt
   a.kper = p.kper;
   if (p.tiled) return launch_gemm_tiled(p, a, a_mode, epi, st);
   if (epi == EPI_ARGMAX) {
-    if (a_mode != A_NORM || p.NT != 4 || p.NW != 4) return hipErrorInvalidValue;
+    if (a_mode != A_NORM) return hipErrorInvalidValue;
+    if (p.MT == 1 && p.NT == 1 && p.NW == 8) {
+      launch_one<1, 8, 1, A_NORM, EPI_ARGMAX>(p, a, st);
+      return hipGetLastError();
+    }
+    if (p.NT != 4 || p.NW != 4) return hipErrorInvalidValue;
     switch (p.MT) {
       case 1: launch_one<1, 4, 4, A_NORM, EPI_ARGMAX>(p, a, st); break;
       case 2: launch_one<2, 4, 4, A_NORM, EPI_ARGMAX>(p, a, st); break;
