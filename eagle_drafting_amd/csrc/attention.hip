@@ -291,15 +291,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) vo
 }
 
 // O[b*K + j][h] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the splits that hold keys (m in log2
-// units, as the partial kernel keeps its scores). One
-// workgroup per query row: 4 groups of 64 threads take every 4th split (HD / 64 columns per thread),
-// then the groups are added in a fixed order.
+// units, as the partial kernel keeps its scores). One workgroup per query row. Every wave computes the
+// max and the denominator itself (lane l takes splits l, l + 64, ...; the denominator is summed in four
+// residue classes of 64-split blocks, added in a fixed order), and wave w accumulates the numerator of
+// splits w, w + 4, ... (HD / 64 columns per lane); the four numerators are added in a fixed order. All
+// loads of the first rounds are issued before any result is used, so the kernel waits on memory once.
 template <int HD>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part, bf16_t* __restrict__ O,
                                                            const int* __restrict__ seq_len,
                                                            const int* __restrict__ req_slot, int K, int Hq,
                                                            int max_ctx, int n_slots, int chunk, int nsplit) {
-  constexpr int CPT = HD / 64;  // columns per thread
+  constexpr int CPT = HD / 64;  // columns per lane
+  constexpr int PF = 12;        // numerator splits per wave loaded up front
+  constexpr int QB = 4;         // 64-split blocks of (m, l) loaded up front
+  constexpr int RS = HD + 2;    // floats per partial
   const int rid = blockIdx.x;
   const int j = rid % K, h = (rid / K) % Hq, b = rid / (K * Hq);
   bf16_t* out = O + ((size_t)(b * K + j) * Hq + h) * HD;
@@ -308,49 +313,68 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
     for (int c = threadIdx.x; c < HD; c += 256) out[c] = 0;
     return;
   }
-  __shared__ float sw[ATTN_MAX_PARTIALS];
   __shared__ float sred[4][HD];
-  __shared__ float swave[8];
   const int ns = (L + K + chunk - 1) / chunk;
-  const float* src = part + (size_t)rid * nsplit * (HD + 2);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  // pass 1: M = max_s m_s
+  const float* src = part + (size_t)rid * nsplit * RS;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+
+  float pm[PF], po[PF][CPT], mv[QB], lv[QB];
+#pragma unroll
+  for (int t = 0; t < PF; ++t) {
+    const int sp = min(wave + 4 * t, ns - 1);  // clamped; unused past the last split
+    pm[t] = src[(size_t)sp * RS + HD];
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) po[t][e] = src[(size_t)sp * RS + CPT * lane + e];
+  }
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    const int sp = min(64 * q + lane, ns - 1);
+    mv[q] = src[(size_t)sp * RS + HD];
+    lv[q] = src[(size_t)sp * RS + HD + 1];
+  }
+
   float M = -1e30f;
-  for (int s = tid; s < ns; s += 256) {
-    const float m = src[(size_t)s * (HD + 2) + HD];
-    sw[s] = m;
-    M = fmaxf(M, m);
-  }
+#pragma unroll
+  for (int q = 0; q < QB; ++q)
+    if (64 * q + lane < ns) M = fmaxf(M, mv[q]);
+  for (int sp = 64 * QB + lane; sp < ns; sp += 64) M = fmaxf(M, src[(size_t)sp * RS + HD]);
   M = wave_max(M);
-  if (lane == 0) swave[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(swave[0], swave[1]), fmaxf(swave[2], swave[3]));
-  // pass 2: weights w_s = e^(m_s - M) (each thread rewrites the entries it wrote) and the denominator
-  float den = 0.f;
-  for (int s = tid; s < ns; s += 256) {
-    const float w = __builtin_amdgcn_exp2f(sw[s] - M);  // m_s are in log2 units
-    sw[s] = w;
-    den += w * src[(size_t)s * (HD + 2) + HD + 1];
+
+  float dq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < QB; ++q)
+    if (64 * q + lane < ns) dq[q & 3] += __builtin_amdgcn_exp2f(mv[q] - M) * lv[q];
+  for (int q = QB; 64 * q < ns; ++q) {
+    const int sp = 64 * q + lane;
+    if (sp < ns) dq[q & 3] += __builtin_amdgcn_exp2f(src[(size_t)sp * RS + HD] - M) * src[(size_t)sp * RS + HD + 1];
   }
-  den = wave_sum(den);
-  if (lane == 0) swave[4 + wave] = den;
-  __syncthreads();
-  // pass 3: numerators; group `wave` takes splits wave, wave + 4, ...
+  float den[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) den[c] = wave_sum(dq[c]);
+
   float num[CPT];
 #pragma unroll
   for (int e = 0; e < CPT; ++e) num[e] = 0.f;
-#pragma unroll 4
-  for (int s = wave; s < ns; s += 4) {
-    const float w = sw[s];
-    const float* ps = src + (size_t)s * (HD + 2) + CPT * lane;
 #pragma unroll
-    for (int e = 0; e < CPT; ++e) num[e] += w * ps[e];
+  for (int t = 0; t < PF; ++t) {
+    if (wave + 4 * t < ns) {
+      const float w = __builtin_amdgcn_exp2f(pm[t] - M);
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) num[e] += w * po[t][e];
+    }
+  }
+#pragma unroll 4
+  for (int sp = wave + 4 * PF; sp < ns; sp += 4) {
+    const float* ps = src + (size_t)sp * RS;
+    const float w = __builtin_amdgcn_exp2f(ps[HD] - M);
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) num[e] += w * ps[CPT * lane + e];
   }
 #pragma unroll
   for (int e = 0; e < CPT; ++e) sred[wave][CPT * lane + e] = num[e];
   __syncthreads();
-  const float inv = 1.f / ((swave[4] + swave[5]) + (swave[6] + swave[7]));
-  for (int c = tid; c < HD; c += 256)
+  const float inv = 1.f / ((den[0] + den[1]) + (den[2] + den[3]));
+  for (int c = threadIdx.x; c < HD; c += 256)
     out[c] = f32_to_bf16(((sred[0][c] + sred[1][c]) + (sred[2][c] + sred[3][c])) * inv);
 }
 
