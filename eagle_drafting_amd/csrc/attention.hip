@@ -17,6 +17,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace pe {
 
 #define ATTN_MAX_PARTIALS 1024  // split partials per query row
@@ -33,11 +35,15 @@ AttnPlan plan_attention(int B, int K, int Hq, int Hkv, int hd, int max_ctx) {
   const int R = (Hq / Hkv) * K;
   const int KEYS = attn_round_keys(hd);
   p.sub = attn_sub_streams(R);
-  // aim for ~1024 workgroups at full context; chunks are whole staging rounds
-  long long want = (long long)B * Hkv * (long long)(max_ctx + K) / 1024;
-  int chunk = (int)((want + KEYS - 1) / KEYS) * KEYS;
+  // Keys per split: a power of two, at least twice the query rows of a kv head (a split's fp32 partial,
+  // R x (hd + 2) floats, then stays well below the keys it summarises) and at least the share that gives
+  // ~1024 workgroups at full context, at most 1024 keys (measured on the MI355X: B 1 K 3 best at 64 keys,
+  // B 8 K 11 at 256, B 32 K 7 at 256-1024, B 64 K 10 at 1024; whole staging rounds in every case).
+  const long long want = (long long)B * Hkv * (long long)(max_ctx + K) / 1024;
+  const long long need = std::max<long long>(std::max<long long>(2LL * R, want), KEYS);
+  int chunk = KEYS;
+  while (chunk < need && chunk < 1024) chunk *= 2;
   if (chunk < KEYS) chunk = KEYS;
-  if (chunk > 4096) chunk = 4096;
   while ((max_ctx + K + chunk - 1) / chunk > ATTN_MAX_PARTIALS) chunk *= 2;
   p.chunk = chunk;
   p.nsplit = (max_ctx + K + chunk - 1) / chunk;
@@ -318,19 +324,29 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   const float* src = part + (size_t)rid * nsplit * RS;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 
+  // (wave-uniform guards: a row with few splits issues only the loads it needs)
   float pm[PF], po[PF][CPT], mv[QB], lv[QB];
 #pragma unroll
   for (int t = 0; t < PF; ++t) {
-    const int sp = min(wave + 4 * t, ns - 1);  // clamped; unused past the last split
-    pm[t] = src[(size_t)sp * RS + HD];
+    pm[t] = 0.f;
 #pragma unroll
-    for (int e = 0; e < CPT; ++e) po[t][e] = src[(size_t)sp * RS + CPT * lane + e];
+    for (int e = 0; e < CPT; ++e) po[t][e] = 0.f;
+    if (wave + 4 * t < ns) {
+      const int sp = wave + 4 * t;
+      pm[t] = src[(size_t)sp * RS + HD];
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) po[t][e] = src[(size_t)sp * RS + CPT * lane + e];
+    }
   }
 #pragma unroll
   for (int q = 0; q < QB; ++q) {
-    const int sp = min(64 * q + lane, ns - 1);
-    mv[q] = src[(size_t)sp * RS + HD];
-    lv[q] = src[(size_t)sp * RS + HD + 1];
+    mv[q] = 0.f;
+    lv[q] = 0.f;
+    if (64 * q < ns) {
+      const int sp = min(64 * q + lane, ns - 1);  // clamped lanes are masked below
+      mv[q] = src[(size_t)sp * RS + HD];
+      lv[q] = src[(size_t)sp * RS + HD + 1];
+    }
   }
 
   float M = -1e30f;
