@@ -394,6 +394,61 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
     out[c] = f32_to_bf16(((sred[0][c] + sred[1][c]) + (sred[2][c] + sred[3][c])) * inv);
 }
 
+// Same merge for rows with at most 32 splits (larger batches: many (row, head) pairs, few splits each):
+// one wave per pair, four pairs per workgroup. Lane s holds split s's (m, l); every lane loads its HD / 64
+// columns of every split up front; the numerator adds the splits in order.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_combine_wave_kernel(const float* __restrict__ part,
+                                                                bf16_t* __restrict__ O,
+                                                                const int* __restrict__ seq_len,
+                                                                const int* __restrict__ req_slot, int K, int Hq,
+                                                                int max_ctx, int n_slots, int chunk, int nsplit,
+                                                                int npairs) {
+  constexpr int CPT = HD / 64, RS = HD + 2, SMAX = 32;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rid = blockIdx.x * 4 + wave;
+  if (rid >= npairs) return;
+  const int j = rid % K, h = (rid / K) % Hq, b = rid / (K * Hq);
+  bf16_t* out = O + ((size_t)(b * K + j) * Hq + h) * HD;
+  const int L = seq_len[b], slot = req_slot[b];
+  if (slot < 0 || slot >= n_slots || L < 0 || L + K > max_ctx) {
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) out[CPT * lane + e] = 0;
+    return;
+  }
+  const int ns = (L + K + chunk - 1) / chunk;  // 1 .. nsplit <= SMAX
+  const float* src = part + (size_t)rid * nsplit * RS;
+  const int sl = min(lane, ns - 1);
+  const float m_l = src[(size_t)sl * RS + HD], l_l = src[(size_t)sl * RS + HD + 1];
+  float o[SMAX][CPT];
+#pragma unroll
+  for (int t = 0; t < SMAX; ++t) {
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) o[t][e] = 0.f;
+    if (t < ns) {
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) o[t][e] = src[(size_t)t * RS + CPT * lane + e];
+    }
+  }
+  const float M = wave_max(lane < ns ? m_l : -1e30f);
+  const float w_l = lane < ns ? __builtin_amdgcn_exp2f(m_l - M) : 0.f;  // m in log2 units
+  const float den = wave_sum(w_l * l_l);
+  float num[CPT];
+#pragma unroll
+  for (int e = 0; e < CPT; ++e) num[e] = 0.f;
+#pragma unroll
+  for (int t = 0; t < SMAX; ++t) {
+    if (t < ns) {
+      const float wt = __shfl(w_l, t, PE_WAVE);
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) num[e] += wt * o[t][e];
+    }
+  }
+  const float inv = 1.f / den;
+#pragma unroll
+  for (int e = 0; e < CPT; ++e) out[CPT * lane + e] = f32_to_bf16(num[e] * inv);
+}
+
 hipError_t launch_attention_bf16(const AttnPlan& p, const void* Q, const void* Kc, const void* Vc,
                                  const int* seq_len, const int* req_slot, int B, int K, int Hq, int Hkv, int hd,
                                  int max_ctx, int n_slots, float* part, hipStream_t st) {
@@ -420,6 +475,17 @@ hipError_t launch_attention_combine_bf16(const AttnPlan& p, const float* part, v
                                          const int* req_slot, int B, int K, int Hq, int Hkv, int hd, int max_ctx,
                                          int n_slots, hipStream_t st) {
   (void)Hkv;
+  if (p.nsplit <= 32) {
+    const int npairs = B * Hq * K;
+    dim3 grid((npairs + 3) / 4), block(256);
+    if (hd == 128)
+      hipLaunchKernelGGL(attn_combine_wave_kernel<128>, grid, block, 0, st, part, (bf16_t*)O, seq_len, req_slot, K,
+                         Hq, max_ctx, n_slots, p.chunk, p.nsplit, npairs);
+    else
+      hipLaunchKernelGGL(attn_combine_wave_kernel<64>, grid, block, 0, st, part, (bf16_t*)O, seq_len, req_slot, K,
+                         Hq, max_ctx, n_slots, p.chunk, p.nsplit, npairs);
+    return hipGetLastError();
+  }
   dim3 grid(B * Hq * K), block(256);
   if (hd == 128)
     hipLaunchKernelGGL(attn_combine_kernel<128>, grid, block, 0, st, part, (bf16_t*)O, seq_len, req_slot, K, Hq,
