@@ -195,25 +195,41 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) vo
             s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1, qf[t][hs], s1, 0, 0, 0);
           }
           const int row = (rt0 + 4 * t) * 16 + lr;
-          const int lim = row < R ? min(k_end, L + (row % K) + 1) : 0;  // visible keys: < lim
-          float sv[8];
-          float tmax = -INFINITY;
+          float psum = 0.f, pe[8], mnew;
+          if (tb + KT <= L + 1 && tb + KT <= k_end) {
+            // every query row sees every key of the tile (row j sees keys < L + j + 1): no mask; the
+            // scale (which includes log2 e, so scores are in log2 units) is applied inside the exponent
+            const float sr[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+            float rmax = fmaxf(fmaxf(fmaxf(sr[0], sr[4]), fmaxf(sr[1], sr[5])),
+                               fmaxf(fmaxf(sr[2], sr[6]), fmaxf(sr[3], sr[7])));
+            rmax = rows_max(rmax);  // over the 4 lanes (l, l ^ 16, l ^ 32, l ^ 48) of query row lr
+            mnew = fmaxf(m_run[t], rmax * scale);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int k0 = tb + 8 * lq + r, k1 = k0 + 4;  // keys of score rows 4 lq + r of tiles 0 and 1
-            sv[r] = k0 < lim ? s0[r] * scale : -INFINITY;  // scores in log2 units (scale includes log2 e)
-            sv[4 + r] = k1 < lim ? s1[r] * scale : -INFINITY;
-            tmax = fmaxf(tmax, fmaxf(sv[r], sv[4 + r]));
+            for (int e = 0; e < 8; ++e) {  // pf element e: key tb + 8 lq + e
+              const int r = e & 3, hi = e >> 2;
+              pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[4 * hi + r], scale, -mnew));
+              psum += pe[e];
+            }
+          } else {
+            const int lim = row < R ? min(k_end, L + (row % K) + 1) : 0;  // visible keys: < lim
+            float sv[8];
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int k0 = tb + 8 * lq + r, k1 = k0 + 4;  // keys of score rows 4 lq + r of tiles 0 and 1
+              sv[r] = k0 < lim ? s0[r] * scale : -INFINITY;
+              sv[4 + r] = k1 < lim ? s1[r] * scale : -INFINITY;
+              tmax = fmaxf(tmax, fmaxf(sv[r], sv[4 + r]));
+            }
+            tmax = rows_max(tmax);
+            mnew = fmaxf(m_run[t], tmax);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              pe[e] = __builtin_amdgcn_exp2f(sv[e] - mnew);
+              psum += pe[e];
+            }
           }
-          tmax = rows_max(tmax);  // over the 4 lanes (l, l ^ 16, l ^ 32, l ^ 48) of query row lr
-          const float mnew = fmaxf(m_run[t], tmax);
           alpha[t] = __builtin_amdgcn_exp2f(m_run[t] - mnew);
-          float psum = 0.f, pe[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {  // pf element e: key tb + 8 lq + e
-            pe[e] = __builtin_amdgcn_exp2f(sv[e] - mnew);
-            psum += pe[e];
-          }
           typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
           const u32x4_t pk = {f32x2_to_bf16x2(pe[0], pe[1]), f32x2_to_bf16x2(pe[2], pe[3]),
                               f32x2_to_bf16x2(pe[4], pe[5]), f32x2_to_bf16x2(pe[6], pe[7])};
