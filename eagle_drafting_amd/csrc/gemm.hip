@@ -47,10 +47,15 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(const bf16_t* __restrict
   const size_t frag = gid >> 6;
   const int s = (int)(frag % Ks);
   const int t = (int)(frag / Ks);
-  int which;
-  const int row = pack_src_row(mode, t, lane & 15, hd, &which);
+  int which = 0, row, col;
+  if (mode == PACK_KI4) {
+    row = 4 * t + (lane & 3);
+    col = 128 * s + 8 * (4 * (lane >> 4) + ((lane >> 2) & 3));
+  } else {
+    row = pack_src_row(mode, t, lane & 15, hd, &which);
+    col = 32 * s + 8 * (lane >> 4);
+  }
   const bf16_t* W = which ? W1 : W0;
-  const int col = 32 * s + 8 * (lane >> 4);
   bf16x8_t v;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -63,21 +68,35 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(const bf16_t* __restrict
 
 hipError_t launch_pack_bf16(const void* W0, const void* W1, int N, int Kd, int mode, int hd, void* dst,
                             hipStream_t st) {
-  const int Nt = mode == PACK_GATEUP ? (2 * N + 15) / 16 : n_tiles(N);
-  const int Ks = k_steps(Kd);
+  const int Nt = mode == PACK_GATEUP ? (2 * N + 15) / 16 : mode == PACK_KI4 ? n_tiles_ki4(N) : n_tiles(N);
+  const int Ks = mode == PACK_KI4 ? k_steps_ki4(Kd) : k_steps(Kd);
   const size_t total = (size_t)Nt * Ks * 64;
   hipLaunchKernelGGL(pack_bf16_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, (const bf16_t*)W0,
                      (const bf16_t*)W1, N, Kd, (bf16x8_t*)dst, Nt, Ks, mode, hd);
   return hipGetLastError();
 }
 
-GemmPlan plan_gemm(int M, int N, int Kd, bool argmax) {
+GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok) {
   GemmPlan p;
   const int Ks = k_steps(Kd);
   p.Nt = n_tiles(N);
   p.tiled = 0;
   p.ksplit = 1;
   p.kper = Ks;
+  p.ki4 = 0;
+  if (ki4_ok && !argmax && M <= 4 && p.Nt < 256) {
+    // up to 4 rows and a narrow output: 4-column tiles (4x the workgroups of 16-column ones, so every
+    // compute unit streams weights), 4 waves splitting the 128-wide k-steps
+    p.ki4 = 1;
+    p.Nt = n_tiles_ki4(N);
+    p.kper = k_steps_ki4(Kd);
+    p.MT = 1;
+    p.mblocks = 1;
+    p.NT = 1;
+    p.NW = 4;
+    p.ngroups = p.Nt;
+    return p;
+  }
   if (M > 32) {
     // 128 x 128 tiles read each weight once per 128 rows and each activation once per 128 columns (the
     // skinny kernel re-reads the activations once per 16 columns). Narrow or short products get too few
@@ -132,8 +151,11 @@ struct KChunk {
   static constexpr int value = MT <= 2 ? 8 : (MT == 4 ? 4 : 2);
 };
 
-template <int MT, int NW, int NT, int AM, int EP>
+// KI: PACK_KI4 weights (MT == 1, NT == 1, M <= 4): 4-column tiles, activation row m at MFMA rows m + 4h
+template <int MT, int NW, int NT, int AM, int EP, int KI>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
+  static_assert(!KI || (MT == 1 && NT == 1 && (EP == EPI_RESID || EP == EPI_ROWS)), "KI4 layout: residual producers");
+  constexpr int CW = KI ? 4 : 16;  // output columns per tile
   constexpr int KP = NW / NT;            // k parts
   constexpr int KC = KChunk<MT>::value;  // k-steps loaded per round
   constexpr int NTH = NW * 64;
@@ -173,8 +195,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
       const int ks = min(c0 + min(kk, nk - 1), Ks - 1);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const int row = m0 + mt * 16 + (lane & 15);
-        const int off = row < M ? (gemm_a_row(g, row) * g.lda + ks * 32 + 8 * (lane >> 4)) * 2 : 0x7ffffff0;
+        int off;
+        if (KI) {  // MFMA row m + 4h: activation row m, k chunk 4(lane >> 4) + h of the 128-wide step
+          const int row = lane & 3, h = (lane >> 2) & 3;
+          off = row < M ? (gemm_a_row(g, row) * g.lda + ks * 128 + 8 * (4 * (lane >> 4) + h)) * 2 : 0x7ffffff0;
+        } else {
+          const int row = m0 + mt * 16 + (lane & 15);
+          off = row < M ? (gemm_a_row(g, row) * g.lda + ks * 32 + 8 * (lane >> 4)) * 2 : 0x7ffffff0;
+        }
         a[kk][mt] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0));
       }
     }
@@ -197,16 +225,17 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
   // Side inputs of the epilogue, issued right after the first weight round so that their latency overlaps it.
   // Loads are unconditional, with indices clamped into range (values that are not needed are ignored),
   // so that no branch forces the weight loads to wait for them.
-  float pre_ssq[4] = {0.f, 0.f, 0.f, 0.f};
+  // (up to 512 partials: a producer on 4-column tiles writes d / 4 of them)
+  float pre_ssq[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (AM == A_NORM) {
     const float* src = g.ssq_in + (size_t)gemm_a_row(g, m0 + min(wave, nrows - 1)) * g.nssq;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pre_ssq[i] = src[min(lane + 64 * i, g.nssq - 1)];  // masked when used
+    for (int i = 0; i < 8; ++i) pre_ssq[i] = src[min(lane + 64 * i, g.nssq - 1)];  // masked when used
   }
-  const int pr16 = min((int)threadIdx.x >> 4, nrows - 1);  // first epilogue row of a 16-wide epilogue
+  const int pr16 = min((int)threadIdx.x / CW, nrows - 1);  // first epilogue row of a CW-wide epilogue
   const int pr8 = min((int)threadIdx.x >> 3, nrows - 1);   // ... of an 8-wide epilogue
   float pre_x = 0.f;
-  if (EP == EPI_RESID) pre_x = g.Xout[(size_t)(m0 + pr16) * N + min(ntc * 16 + (int)(threadIdx.x & 15), N - 1)];
+  if (EP == EPI_RESID) pre_x = g.Xout[(size_t)(m0 + pr16) * N + min(ntc * CW + (int)(threadIdx.x % CW), N - 1)];
   int pre_seq = 0, pre_slot = 0;  // raw values; arithmetic on them waits until the epilogue
   if (EP == EPI_QKV) {
     pre_seq = g.seq_len[(m0 + pr8) / g.Kdraft];
@@ -228,11 +257,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
       const float* src = g.ssq_in + (size_t)gemm_a_row(g, m0 + r) * g.nssq;
       float t = 0.f;
       if (r == wave) {
-        float v[4];
+        float v[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = lane + 64 * i < g.nssq ? pre_ssq[i] : 0.f;
-        t = (v[0] + v[1]) + (v[2] + v[3]);
-        for (int i = lane + 256; i < g.nssq; i += 64) t += src[i];
+        for (int i = 0; i < 8; ++i) v[i] = lane + 64 * i < g.nssq ? pre_ssq[i] : 0.f;
+        t = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+        for (int i = lane + 512; i < g.nssq; i += 64) t += src[i];
       } else {
         for (int i = lane; i < g.nssq; i += 64) t += src[i];
       }
@@ -259,7 +288,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
   }
   // reduced tile: y(tile t, local row r, column c), scaled by the row's 1/RMS for a normalised operand
   auto Y = [&](int t, int r, int c) {
-    const float v = s_red[(t * MT + (r >> 4)) * 256 + (r & 15) * 16 + c];
+    float v;
+    if (KI)  // diagonal blocks: row r with chunk h sits at MFMA row r + 4h, column c with chunk h at c + 4h
+      v = ((s_red[r * 16 + c] + s_red[(r + 4) * 16 + c + 4]) + s_red[(r + 8) * 16 + c + 8]) +
+          s_red[(r + 12) * 16 + c + 12];
+    else
+      v = s_red[(t * MT + (r >> 4)) * 256 + (r & 15) * 16 + c];
     return AM == A_NORM ? v * s_inv[r] : v;
   };
   const int rows = nrows;
@@ -282,9 +316,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
     }
   } else if (EP == EPI_RESID) {
     // X[m][n] += y; XG = bf16(X * gain_next); per-row sum of squares of the new X over this tile
-    for (int idx = threadIdx.x; idx < rows * 16; idx += NTH) {
-      const int r = idx >> 4, c = idx & 15;
-      const int m = m0 + r, n = nt * 16 + c;
+    for (int idx = threadIdx.x; idx < rows * CW; idx += NTH) {
+      const int r = idx / CW, c = idx % CW;
+      const int m = m0 + r, n = nt * CW + c;
       float v = 0.f;
       if (n < N) {
         v = (idx == (int)threadIdx.x ? pre_x : g.Xout[(size_t)m * N + n]) + Y(0, r, c);
@@ -292,15 +326,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
         g.XGout[(size_t)m * N + n] = f32_to_bf16(v * bf16_to_f32(g.gain_next[n]));
       }
       float sq = v * v;
-      for (int off = 8; off > 0; off >>= 1) sq += __shfl_xor(sq, off, PE_WAVE);
+      for (int off = CW / 2; off > 0; off >>= 1) sq += __shfl_xor(sq, off, PE_WAVE);
       if (c == 0) g.ssq_out[(size_t)m * g.nssq_out + nt] = sq;
     }
   } else if (EP == EPI_ROWS) {
     // parallel-draft input rows: row 0 = fc . concat(h) + embed[last_token]; rows 1..K-1 = h_shared + emb_mask
     const int Kr = g.Kdraft;
-    for (int idx = threadIdx.x; idx < rows * 16; idx += NTH) {
-      const int r = idx >> 4, c = idx & 15;
-      const int b = m0 + r, n = nt * 16 + c;
+    for (int idx = threadIdx.x; idx < rows * CW; idx += NTH) {
+      const int r = idx / CW, c = idx % CW;
+      const int b = m0 + r, n = nt * CW + c;
       const bool first = idx == (int)threadIdx.x;
       const int tok = first ? pre_tok : g.last_token[b];
       const bool tok_ok = tok >= 0 && tok < g.V;
@@ -320,7 +354,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
         }
       }
       float s0 = x0 * x0, s1 = ph * ph;
-      for (int off = 8; off > 0; off >>= 1) {
+      for (int off = CW / 2; off > 0; off >>= 1) {
         s0 += __shfl_xor(s0, off, PE_WAVE);
         s1 += __shfl_xor(s1, off, PE_WAVE);
       }
@@ -383,9 +417,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
   }
 }
 
-template <int MT, int NW, int NT, int AM, int EP>
+template <int MT, int NW, int NT, int AM, int EP, int KI = 0>
 static void launch_one(const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_kernel<MT, NW, NT, AM, EP>), dim3(p.ngroups, p.mblocks), dim3(NW * 64), 0, st, a);
+  hipLaunchKernelGGL((gemm_kernel<MT, NW, NT, AM, EP, KI>), dim3(p.ngroups, p.mblocks), dim3(NW * 64), 0, st, a);
 }
 
 template <int AM, int EP>
@@ -407,12 +441,19 @@ static hipError_t launch_split_nw(const GemmPlan& p, const GemmArgs& a, hipStrea
 
 hipError_t launch_gemm(const GemmPlan& p, GemmArgs a, int a_mode, int epi, hipStream_t st) {
   a.Nt = p.Nt;
-  a.Ks = k_steps(a.Kd);
+  a.Ks = p.ki4 ? k_steps_ki4(a.Kd) : k_steps(a.Kd);
   a.ngroups = p.ngroups;
   a.mblocks = p.mblocks;
   a.ksplit = p.ksplit;
   a.kper = p.kper;
   if (p.tiled) return launch_gemm_tiled(p, a, a_mode, epi, st);
+  if (p.ki4) {
+    if (a_mode != A_BF16 || p.NW != 4 || a.M > 4) return hipErrorInvalidValue;
+    if (epi == EPI_RESID) launch_one<1, 4, 1, A_BF16, EPI_RESID, 1>(p, a, st);
+    else if (epi == EPI_ROWS) launch_one<1, 4, 1, A_BF16, EPI_ROWS, 1>(p, a, st);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   if (epi == EPI_ARGMAX) {
     if (a_mode != A_NORM) return hipErrorInvalidValue;
     if (p.MT == 1 && p.NT == 1 && p.NW == 8) {

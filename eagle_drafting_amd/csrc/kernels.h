@@ -13,11 +13,18 @@ namespace pe {
 // PACK_PAIRS: the 16 rows of a tile are 8 RoPE pairs of one head of width hd: rows 8tt+e and
 //             hd/2 + 8tt + e of head t / (hd/16), tt = t % (hd/16) (q, k and v heads alike).
 // PACK_GATEUP: rows 8t..8t+7 of W0 (gate) then rows 8t..8t+7 of W1 (up); 2N/16 tiles.
-enum { PACK_PLAIN = 0, PACK_PAIRS = 1, PACK_GATEUP = 2 };
+// PACK_KI4 (products of at most 4 rows): fragment (t, s) holds 4 output rows and reduction columns
+// 128s..128s+127; lane l's 16 bytes are W[4t + (l & 3)][128s + 8(4(l >> 4) + ((l >> 2) & 3)) .. +7]: the
+// MFMA's 16 columns are 4 output columns x 4 interleaved 8-wide k chunks. With the activation row m at
+// MFMA row m + 4h reading chunk h the same way, the product of output column c is the sum over h of
+// D[m + 4h][c + 4h]. ceil(N/4) tiles of ceil(Kd/128) fragments: 4x the workgroups of the plain layout.
+enum { PACK_PLAIN = 0, PACK_PAIRS = 1, PACK_GATEUP = 2, PACK_KI4 = 3 };
 hipError_t launch_pack_bf16(const void* W0, const void* W1, int N, int Kd, int mode, int hd, void* dst,
                             hipStream_t st);
 inline int n_tiles(int N) { return (N + 15) / 16; }
 inline int k_steps(int Kd) { return (Kd + 31) / 32; }
+inline int n_tiles_ki4(int N) { return (N + 3) / 4; }
+inline int k_steps_ki4(int Kd) { return (Kd + 127) / 128; }
 
 // ---- GEMM y = A . W^T with fused prologue / epilogue ---------------------------------------------
 struct GemmPlan {
@@ -30,11 +37,14 @@ struct GemmPlan {
   int tiled;    // 1: LDS-tiled 128 x 128 kernel (larger M); 0: skinny split-K kernel
   int ksplit;   // tiled: workgroups along the reduction dimension (1 = none); > 1 adds a reduce kernel
   int kper;     // tiled: k-steps (32 columns each) per split, a multiple of 4
+  int ki4;      // skinny on PACK_KI4 weights: 4-column tiles (Nt counts them), 128-wide k-steps
 };
-GemmPlan plan_gemm(int M, int N, int Kd, bool argmax);
+// ki4_ok: the weights are also packed as PACK_KI4 (the residual-stream producers: fc, O, down), which the
+// plan uses for up to 4 rows when the plain layout would leave most compute units idle
+GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok = false);
 // Partial sums of squares per row that a residual-stream producer with plan p writes (one per 16 columns
-// for the skinny kernel, one per 128-column workgroup tile for the tiled one); the consumer sums exactly
-// that many.
+// for the skinny kernel, one per 4 columns on PACK_KI4 weights, one per 128-column workgroup tile for the
+// tiled one); the consumer sums exactly that many.
 inline int gemm_ssq_parts(const GemmPlan& p) { return p.tiled ? p.ngroups : p.Nt; }
 
 // A operand: always a bf16 matrix. A_NORM marks a normalised operand: A = bf16(x * g) of the residual stream

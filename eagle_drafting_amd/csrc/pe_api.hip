@@ -27,6 +27,10 @@ struct pe_ctx {
   const void* p_gu[PE_MAX_LAYERS] = {};  // gate and up, 16-column tiles interleaved
   const void* p_down[PE_MAX_LAYERS] = {};
   const void* p_lm = nullptr;
+  // the residual-stream producers again in the 4-column layout (PACK_KI4) for draft steps of up to 4 rows
+  const void* p_fc4 = nullptr;
+  const void* p_o4[PE_MAX_LAYERS] = {};
+  const void* p_down4[PE_MAX_LAYERS] = {};
 
   // workspace
   char* ws = nullptr;
@@ -43,7 +47,7 @@ struct pe_ctx {
   int* t_ws = nullptr;     // target argmax [max_batch, max_k + 1]
   float* logits_ws = nullptr;  // fp32 path: logits when the caller passes none
   float2* rope = nullptr;  // [max_ctx, hd/2] (cos, sin)
-  float* ssq = nullptr;    // per-16-column sums of squares of X rows [Mmax, d/16]
+  float* ssq = nullptr;    // partial sums of squares of X rows [Mmax, d/4] (per 16 or per 4 columns)
   int* flags = nullptr;
 
   std::string err;
@@ -115,6 +119,7 @@ extern "C" const char* pe_last_error(const pe_ctx* ctx) { return ctx ? ctx->err.
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 static size_t packed_bytes(int N, int Kd) { return (size_t)n_tiles(N) * k_steps(Kd) * 1024; }
+static size_t packed_ki4_bytes(int N, int Kd) { return (size_t)n_tiles_ki4(N) * k_steps_ki4(Kd) * 1024; }
 
 static void free_ctx(pe_ctx* c) {
   if (!c) return;
@@ -183,6 +188,12 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
       o_dn[l] = take(packed_bytes(d, F));
     }
     const size_t o_lm = take(packed_bytes(V, d));
+    const size_t o_fc4 = take(packed_ki4_bytes(d, 3 * d));
+    size_t o_o4[PE_MAX_LAYERS], o_dn4[PE_MAX_LAYERS];
+    for (int l = 0; l < c.n_layers; ++l) {
+      o_o4[l] = take(packed_ki4_bytes(d, qd));
+      o_dn4[l] = take(packed_ki4_bytes(d, F));
+    }
     if (hipMalloc((void**)&ctx->packed, off) != hipSuccess) {
       free_ctx(ctx);
       return fail(nullptr, PE_ERR_OOM, "hipMalloc of packed weights failed");
@@ -204,6 +215,14 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
     }
     ok = ok && chk(launch_pack_bf16(w->lm_head, nullptr, V, d, PACK_PLAIN, 0, base + o_lm, st));
     ctx->p_lm = base + o_lm;
+    ok = ok && chk(launch_pack_bf16(w->fc, nullptr, d, 3 * d, PACK_KI4, 0, base + o_fc4, st));
+    ctx->p_fc4 = base + o_fc4;
+    for (int l = 0; l < c.n_layers && ok; ++l) {
+      ok = ok && chk(launch_pack_bf16(w->wo[l], nullptr, d, qd, PACK_KI4, 0, base + o_o4[l], st));
+      ok = ok && chk(launch_pack_bf16(w->wdown[l], nullptr, d, F, PACK_KI4, 0, base + o_dn4[l], st));
+      ctx->p_o4[l] = base + o_o4[l];
+      ctx->p_down4[l] = base + o_dn4[l];
+    }
     if (!ok) {
       free_ctx(ctx);
       return fail(nullptr, PE_ERR_HIP, "weight packing launch failed");
@@ -242,7 +261,7 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
       am_floats = std::max(am_floats, (size_t)rows * plan_argmax_chunks(rows, V));
     }
   }
-  const int nssq = (d + 15) / 16;
+  const int nssq = (d + 3) / 4;  // the finest producer granularity (4-column tiles)
   size_t off = 0;
   auto take = [&](size_t b) { size_t o = off; off = align256(off + b); return o; };
   const size_t oX = take((size_t)Mmax * d * 4), oU = take((size_t)Mmax * d * es), oQ = take((size_t)Mmax * qd * es),
@@ -423,11 +442,11 @@ static pe_status draft_bf16(pe_ctx* ctx, int32_t B, int32_t K, int32_t Kout, con
     GemmArgs a = base;
     a.M = B; a.Kd = 3 * d; a.N = d;
     a.A = (const uint16_t*)target_hidden; a.lda = 3 * d;
-    a.Wp_raw = ctx->p_fc;
     a.Kdraft = K; a.last_token = last_token; a.V = V;
     a.embed = (const uint16_t*)w.embed; a.emb_mask = (const uint16_t*)w.emb_mask; a.h_shared = (const uint16_t*)w.h_shared;
     a.gain_next = (const uint16_t*)w.attn_norm[0];
-    const GemmPlan p = plan_gemm(B, d, 3 * d, false);
+    const GemmPlan p = plan_gemm(B, d, 3 * d, false, true);
+    a.Wp_raw = p.ki4 ? ctx->p_fc4 : ctx->p_fc;
     a.nssq_out = nssq = gemm_ssq_parts(p);
     LAUNCH(launch_gemm(p, a, A_BF16, EPI_ROWS, st));
   } else {
@@ -458,8 +477,8 @@ static pe_status draft_bf16(pe_ctx* ctx, int32_t B, int32_t K, int32_t Kout, con
       a.M = M; a.Kd = qd; a.N = d;
       a.A = (const uint16_t*)ctx->Ob; a.lda = qd;
       a.gain_next = (const uint16_t*)w.mlp_norm[l];
-      a.Wp_raw = ctx->p_o[l];
-      const GemmPlan p = plan_gemm(M, d, qd, false);
+      const GemmPlan p = plan_gemm(M, d, qd, false, true);
+      a.Wp_raw = p.ki4 ? ctx->p_o4[l] : ctx->p_o[l];
       a.nssq_out = nssq = gemm_ssq_parts(p);
       LAUNCH(launch_gemm(p, a, A_BF16, EPI_RESID, st));
     }
@@ -480,8 +499,8 @@ static pe_status draft_bf16(pe_ctx* ctx, int32_t B, int32_t K, int32_t Kout, con
       a.M = M; a.Kd = F; a.N = d;
       a.A = (const uint16_t*)ctx->Ab; a.lda = F;
       a.gain_next = (const uint16_t*)(l + 1 < c.n_layers ? w.attn_norm[l + 1] : w.final_norm);
-      a.Wp_raw = ctx->p_down[l];
-      const GemmPlan p = plan_gemm(M, d, F, false);
+      const GemmPlan p = plan_gemm(M, d, F, false, true);
+      a.Wp_raw = p.ki4 ? ctx->p_down4[l] : ctx->p_down[l];
       a.nssq_out = nssq = gemm_ssq_parts(p);
       LAUNCH(launch_gemm(p, a, A_BF16, EPI_RESID, st));
     }
