@@ -86,14 +86,15 @@ GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok) {
   p.ki4 = 0;
   if (ki4_ok && !argmax && M <= 4 && p.Nt < 256) {
     // up to 4 rows and a narrow output: 4-column tiles (4x the workgroups of 16-column ones, so every
-    // compute unit streams weights), 4 waves splitting the 128-wide k-steps
+    // compute unit streams weights); 4 or 8 waves split the 128-wide k-steps so that each loads its share
+    // in one round of at most 8 (measured: O 4 waves x 8 k-steps 5.9 us, down 8 x 6 8.2 us, 4 x 12 8.8 us)
     p.ki4 = 1;
     p.Nt = n_tiles_ki4(N);
     p.kper = k_steps_ki4(Kd);
     p.MT = 1;
     p.mblocks = 1;
     p.NT = 1;
-    p.NW = 4;
+    p.NW = p.kper > 32 ? 8 : 4;
     p.ngroups = p.Nt;
     return p;
   }
@@ -448,9 +449,11 @@ hipError_t launch_gemm(const GemmPlan& p, GemmArgs a, int a_mode, int epi, hipSt
   a.kper = p.kper;
   if (p.tiled) return launch_gemm_tiled(p, a, a_mode, epi, st);
   if (p.ki4) {
-    if (a_mode != A_BF16 || p.NW != 4 || a.M > 4) return hipErrorInvalidValue;
-    if (epi == EPI_RESID) launch_one<1, 4, 1, A_BF16, EPI_RESID, 1>(p, a, st);
-    else if (epi == EPI_ROWS) launch_one<1, 4, 1, A_BF16, EPI_ROWS, 1>(p, a, st);
+    if (a_mode != A_BF16 || (p.NW != 4 && p.NW != 8) || a.M > 4) return hipErrorInvalidValue;
+    if (epi == EPI_RESID && p.NW == 4) launch_one<1, 4, 1, A_BF16, EPI_RESID, 1>(p, a, st);
+    else if (epi == EPI_RESID) launch_one<1, 8, 1, A_BF16, EPI_RESID, 1>(p, a, st);
+    else if (epi == EPI_ROWS && p.NW == 4) launch_one<1, 4, 1, A_BF16, EPI_ROWS, 1>(p, a, st);
+    else if (epi == EPI_ROWS) launch_one<1, 8, 1, A_BF16, EPI_ROWS, 1>(p, a, st);
     else return hipErrorInvalidValue;
     return hipGetLastError();
   }
