@@ -132,3 +132,31 @@ def test_k1_equals_row0_and_determinism(shape):
         check_tokens(d6.cpu().numpy()[:, 0], ref["logits"][:, 0], tol, "row 0 token")
     finally:
         g.close()
+
+
+@pytest.mark.parametrize("B,K", [(1, 1), (1, 2), (2, 1), (3, 1)], ids=lambda v: str(v))
+def test_four_row_products_parity(B, K):
+    """Draft steps of at most 4 rows (B (K + 1) <= 4; (3, 1) has 6) run the residual-stream projections on
+    the 4-column weight packing; ragged contexts, parity against the oracle, K/V rows included."""
+    w = Workload(f"qwen3coder-bf16-B{B}-K{K}-small", QWEN3_CODER, B, K, (60, 400), 0.7, 7400 + 10 * B + K)
+    log(f"four-row products: B {B} K {K} (rows {B * (K + 1)})")
+    g = GpuDrafter(w)
+    try:
+        _parity(g, range(w.B))
+    finally:
+        g.close()
+
+
+@pytest.mark.parametrize("B,K", [(1, 3), (2, 2), (1, 4)], ids=lambda v: str(v))
+def test_four_row_products_rows_path(B, K):
+    """pe_draft_rows with B K <= 4 rows (the 4-column projections without the row build) and 5 rows
+    (the 16-column ones), against the oracle on the same caller rows."""
+    import torch
+    w = Workload(f"qwen3coder-bf16-B{B}-K{K}-rows-small", QWEN3_CODER, B, K, (30, 200), 0.7, 7500 + 10 * B + K)
+    log(f"four-row products, rows path: B {B} K {K}")
+    g = GpuDrafter(w)
+    try:
+        X = _random_rows(w, 3)
+        _parity(g, range(w.B), rows=torch.from_numpy(X).cuda(), rows_host=X.astype(np.float64), check_kv=False)
+    finally:
+        g.close()
