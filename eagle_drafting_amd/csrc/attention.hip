@@ -115,11 +115,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) vo
   const int kq = tid / C8, c8 = tid % C8;
   bf16x8_t rk[PK], rv[PK];
   auto gload = [&](int base) {
+    if (base + KEYS <= k_end) {  // the whole round is inside the split: one address, immediate offsets
+      const size_t o = (size_t)(base + PK * kq) * HD + 8 * c8;
 #pragma unroll
-    for (int q = 0; q < PK; ++q) {
-      const int kp = min(base + PK * kq + q, k_end - 1);
-      rk[q] = *(const bf16x8_t*)(kb + (size_t)kp * HD + 8 * c8);
-      rv[q] = *(const bf16x8_t*)(vb + (size_t)kp * HD + 8 * c8);
+      for (int q = 0; q < PK; ++q) {
+        rk[q] = *(const bf16x8_t*)(kb + o + q * HD);
+        rv[q] = *(const bf16x8_t*)(vb + o + q * HD);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < PK; ++q) {
+        const int kp = min(base + PK * kq + q, k_end - 1);
+        rk[q] = *(const bf16x8_t*)(kb + (size_t)kp * HD + 8 * c8);
+        rv[q] = *(const bf16x8_t*)(vb + (size_t)kp * HD + 8 * c8);
+      }
     }
   };
   auto sstore = [&]() {
@@ -238,10 +247,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) vo
           l_run[t] = l_run[t] * alpha[t] + psum;
           m_run[t] = mnew;
         }
-        // the running max rarely moves after the first tiles: skip the rescale when no lane's did
-        bool rescale[NR];
+        // the running max rarely moves after the first tiles: rescale only when some lane's did (a
+        // wave-uniform branch of its own, so the common case costs no multiplies or selects)
 #pragma unroll
-        for (int t = 0; t < NR; ++t) rescale[t] = __any(alpha[t] != 1.f);
+        for (int t = 0; t < NR; ++t) {
+          if (t < nrt && __any(alpha[t] != 1.f)) {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) o[t][ct][r] *= alpha[t];
+          }
+        }
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           const bf16x8_t va =
@@ -249,11 +265,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) vo
 #pragma unroll
           for (int t = 0; t < NR; ++t) {
             if (t >= nrt) continue;
-            f32x4_t acc = o[t][ct];
-            if (rescale[t])
-#pragma unroll
-              for (int r = 0; r < 4; ++r) acc[r] *= alpha[t];
-            o[t][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[t], acc, 0, 0, 0);
+            o[t][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[t], o[t][ct], 0, 0, 0);
           }
         }
       }
