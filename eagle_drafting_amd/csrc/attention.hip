@@ -196,12 +196,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) vo
           alpha[t] = 1.f;
           if (t >= nrt) continue;
           f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+          // every key fragment of the tile is read before the first product, so the LDS reads overlap
+          // instead of each product waiting for its own
+          bf16x8_t ka[HS][2];
 #pragma unroll
           for (int hs = 0; hs < HS; ++hs) {
-            const bf16x8_t ka0 = *(const bf16x8_t*)(sK + (kt * KT + lr) * STR + 32 * hs + 8 * lq);
-            const bf16x8_t ka1 = *(const bf16x8_t*)(sK + (kt * KT + 16 + lr) * STR + 32 * hs + 8 * lq);
-            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0, qf[t][hs], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1, qf[t][hs], s1, 0, 0, 0);
+            ka[hs][0] = *(const bf16x8_t*)(sK + (kt * KT + lr) * STR + 32 * hs + 8 * lq);
+            ka[hs][1] = *(const bf16x8_t*)(sK + (kt * KT + 16 + lr) * STR + 32 * hs + 8 * lq);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int hs = 0; hs < HS; ++hs) {
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[hs][0], qf[t][hs], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[hs][1], qf[t][hs], s1, 0, 0, 0);
           }
           const int row = (rt0 + 4 * t) * 16 + lr;
           float psum = 0.f, pe[8], mnew;
@@ -258,14 +265,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) vo
               for (int r = 0; r < 4; ++r) o[t][ct][r] *= alpha[t];
           }
         }
+        // value fragments likewise: all reads first, then the products
+        bf16x8_t va[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+          va[ct] = *(const bf16x8_t*)(sVt + (ct * 16 + lr) * VSTR + ((kt * KT + 8 * lq) ^ (8 * vsw(ct * 16 + lr))));
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-          const bf16x8_t va =
-              *(const bf16x8_t*)(sVt + (ct * 16 + lr) * VSTR + ((kt * KT + 8 * lq) ^ (8 * vsw(ct * 16 + lr))));
 #pragma unroll
           for (int t = 0; t < NR; ++t) {
             if (t >= nrt) continue;
-            o[t][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[t], o[t][ct], 0, 0, 0);
+            o[t][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[ct], pf[t], o[t][ct], 0, 0, 0);
           }
         }
       }
