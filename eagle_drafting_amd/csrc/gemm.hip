@@ -141,6 +141,15 @@ GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok) {
     while (nw < cap && groups * nw * 2 <= 4096 && per_wave(2 * nw) >= 8 &&
            !(per_wave(2 * nw) > 8 && per_wave(2 * nw) < 16))
       nw *= 2;
+    if (p.MT == 1) {
+      // one 16-row block: the most waves whose k share is whole 8-step load rounds (measured at 4 rows:
+      // QKV and gate/up 8 waves x 8 k-steps beat 4 x 16 and 16 x 4; down 8 x 24 beat 16 x 12)
+      for (int w = cap; w >= 4; w /= 2)
+        if (((Ks + w - 1) / w) % 8 == 0) {
+          nw = w;
+          break;
+        }
+    }
     p.NW = nw;
   }
   p.ngroups = (p.Nt + p.NT - 1) / p.NT;
