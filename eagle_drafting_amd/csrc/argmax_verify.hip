@@ -155,6 +155,11 @@ __global__ __launch_bounds__(1024) void accept_compact_kernel(
   __shared__ int buf[1024];
   const int tid = threadIdx.x;
   const int rows = B * (K + 1);
+  // this request's draft tokens, loaded before anything waits (K <= max_k <= PE_MAX_K = 16)
+  constexpr int KMAX = 16;
+  int dk[KMAX];
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) dk[i] = (tid < B && i < K) ? draft[(size_t)tid * K + i] : -1;
   // target argmax t[b][i] from the scan partials: one wave per row
   {
     const int wave = tid >> 6, lane = tid & 63;
@@ -167,10 +172,17 @@ __global__ __launch_bounds__(1024) void accept_compact_kernel(
   int n = 0, al = 0, bonus = 0, keep = 0;
   if (tid < B) {
     const int* t = t_ws + (size_t)tid * (K + 1);
-    const int* dr = draft + (size_t)tid * K;
-    while (n < K && dr[n] == t[n]) ++n;
+    int tk[KMAX + 1];
+#pragma unroll
+    for (int i = 0; i <= KMAX; ++i) tk[i] = i <= K ? t[i] : 0;  // all loads in flight together
+    // accepted prefix: the first position whose draft differs from the target argmax
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i)
+      if (n == i && i < K && dk[i] == tk[i]) n = i + 1;
     al = n + 1;
-    bonus = t[n];
+#pragma unroll
+    for (int i = 0; i <= KMAX; ++i)
+      if (i == n) bonus = tk[i];
     accept_len[tid] = al;
     keep = finished ? (finished[tid] == 0 ? 1 : 0) : 1;
   }
