@@ -75,7 +75,19 @@ __device__ __forceinline__ int am_row_reduce(const float* __restrict__ pv, const
                                              int lane) {
   float b = -INFINITY;
   int i = 0x7fffffff;
-  for (int c = lane; c < nchunks; c += 64) {
+  // the first 256 partials are loaded before any is compared (one memory round trip for up to 256)
+  float v4[4];
+  int k4[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int c = lane + 64 * u;
+    v4[u] = c < nchunks ? pv[c] : -INFINITY;
+    k4[u] = c < nchunks ? pi[c] : 0x7fffffff;
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (am_better(v4[u], k4[u], b, i)) { b = v4[u]; i = k4[u]; }
+  for (int c = lane + 256; c < nchunks; c += 64) {
     const float v = pv[c];
     const int k = pi[c];
     if (am_better(v, k, b, i)) { b = v; i = k; }
@@ -128,20 +140,21 @@ hipError_t launch_argmax_final(const float* pv, const int* pi, int rows, int nch
   return hipGetLastError();
 }
 
-// inclusive scan over the 1024 threads of the block (Hillis-Steele in LDS)
+// inclusive scan over the 1024 threads of the block: a shuffle scan inside each wave, then each wave adds
+// the totals of the waves before it (two barriers; buf holds the 16 wave totals)
 __device__ __forceinline__ int block_scan_incl(int v, int* buf) {
-  const int t = threadIdx.x;
-  buf[t] = v;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int add = t >= off ? buf[t - off] : 0;
-    __syncthreads();
-    buf[t] += add;
-    __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off, PE_WAVE);
+    if (lane >= off) v += t;
   }
-  const int r = buf[t];
+  if (lane == 63) buf[wave] = v;
   __syncthreads();
-  return r;
+  int add = 0;
+  for (int w = 0; w < wave; ++w) add += buf[w];
+  __syncthreads();  // buf is reused by the next scan
+  return v + add;
 }
 
 // Greedy acceptance (the target verifies the K drafts in one pass; standard rule, greedy form) and the
@@ -152,7 +165,7 @@ __global__ __launch_bounds__(1024) void accept_compact_kernel(
     const int* __restrict__ seq_len, int* __restrict__ t_ws, int* __restrict__ accept_len,
     int* __restrict__ cu_accept, int* __restrict__ out_tokens, int* __restrict__ keep_index,
     int* __restrict__ n_keep, int* __restrict__ slot_next, int* __restrict__ seq_next, int* __restrict__ last_next) {
-  __shared__ int buf[1024];
+  __shared__ int buf[16];  // per-wave totals of the block scans
   const int tid = threadIdx.x;
   const int rows = B * (K + 1);
   // this request's draft tokens, loaded before anything waits (K <= max_k <= PE_MAX_K = 16)
