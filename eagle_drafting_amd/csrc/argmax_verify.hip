@@ -108,22 +108,22 @@ __global__ __launch_bounds__(1024) void argmax_final_kernel(const float* __restr
   const int* ix = pi + (size_t)row * nchunks;
   float b = -INFINITY;
   int i = 0x7fffffff;
-  // four chunks per thread per pass, loaded before any is compared (the winner does not depend on the
-  // visiting order: ties go to the smaller index)
-  int c = threadIdx.x;
-  for (; c + 3 * 1024 < nchunks; c += 4 * 1024) {
-    float x[4];
-    int k[4];
+  // the first 12 chunks of every thread (12288 partials: the whole row of a 16-column-tile LM head at
+  // V < 196608) are loaded before any is compared; the winner does not depend on the visiting order
+  // (ties go to the smaller index)
+  constexpr int U = 12;
+  float x[U];
+  int k[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      x[u] = v[c + u * 1024];
-      k[u] = ix[c + u * 1024];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (am_better(x[u], k[u], b, i)) { b = x[u]; i = k[u]; }
+  for (int u = 0; u < U; ++u) {
+    const int c = threadIdx.x + u * 1024;
+    x[u] = c < nchunks ? v[c] : -INFINITY;
+    k[u] = c < nchunks ? ix[c] : 0x7fffffff;
   }
-  for (; c < nchunks; c += 1024)
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (am_better(x[u], k[u], b, i)) { b = x[u]; i = k[u]; }
+  for (int c = threadIdx.x + U * 1024; c < nchunks; c += 1024)
     if (am_better(v[c], ix[c], b, i)) { b = v[c]; i = ix[c]; }
   am_wave_reduce(b, i, 64);
   if (lane == 0) { sv[wave] = b; si[wave] = i; }
