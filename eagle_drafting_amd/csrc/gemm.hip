@@ -98,6 +98,31 @@ GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok) {
     p.ngroups = p.Nt;
     return p;
   }
+  // (the stream kernel addresses the packed weights with 32-bit buffer offsets)
+  if (M > 32 && M <= 128 && (long long)p.Nt * Ks * 1024 < 0x7ff00000LL) {
+    // 33..128 rows: the weight-stream kernel (all rows and 128 columns per workgroup, activations staged
+    // once per chunk). Narrow or short products split the reduction over workgroups until there are about
+    // 384 of them, each with at least four chunks, and while the fp32 partials stay within the weight bytes
+    // (2 ksplit M N 4 <= N Kd 2); the split reduce kernel then runs the epilogue.
+    const int tg = (p.Nt + 7) / 8;
+    constexpr int step = 4 * GEMM_STREAM_CH;
+    p.tiled = 2;
+    p.MT = 8;
+    p.NT = 8;
+    p.NW = 4;
+    p.mblocks = 1;
+    p.ngroups = tg;
+    if (!argmax) {
+      int ks = 1;
+      while (tg * ks < 384 && Ks >= 2 * step * ks && 8LL * (2 * ks) * M <= 2LL * Kd) ks *= 2;
+      if (ks > 1) {
+        p.kper = (((Ks + ks - 1) / ks) + step - 1) / step * step;
+        p.ksplit = (Ks + p.kper - 1) / p.kper;
+        if (p.ksplit <= 1) p.kper = Ks;
+      }
+    }
+    return p;
+  }
   if (M > 32) {
     // 128 x 128 tiles read each weight once per 128 rows and each activation once per 128 columns (the
     // skinny kernel re-reads the activations once per 16 columns). Narrow or short products get too few

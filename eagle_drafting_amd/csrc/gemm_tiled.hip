@@ -454,7 +454,230 @@ __device__ void tile_epilogue(const GemmArgs& g, const float* Cs, const float* s
   }
 }
 
+// Projections for 33..128 rows: a weight stream with the activations staged once per reduction chunk.
+//
+// At these row counts every weight byte is used by at most 128 rows, so the product is bound by the weight
+// stream. A workgroup covers all rows (RB blocks of 32) and 128 columns; wave w owns columns 32 w ..
+// 32 w + 31 and every row, so each weight fragment is loaded by exactly one wave, straight into
+// registers, whole chunks (CH k-steps of 32) ahead of its use. The activations of a chunk (32 RB rows x
+// 32 CH columns) are loaded once per workgroup with row-contiguous 16-byte reads and stored into one of
+// two LDS buffers in fragment order, so a chunk costs a single barrier and no wave waits for another's
+// weights. v_mfma_f32_32x32x16_bf16 throughout (lane layout as in the 128 x 128 kernel above).
+// The product tile then goes through LDS (same swizzled layout as above) into the shared epilogues; with
+// SPLIT the workgroup covers k-steps [blockIdx.y * kper, + kper) and writes an fp32 partial tile that
+// gemm_split_reduce_kernel sums in a fixed order.
+template <int AM, int EP, bool SPLIT, int RB, int CH, int NWB>
+__global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs g) {
+  constexpr int BN = 128;
+  constexpr int MTL = 2 * RB;                       // 16-row fragments per chunk k-step
+  constexpr int ABUF = CH * MTL * 64;               // bf16x8 slots per LDS buffer
+  constexpr int NPIECE = (32 * RB * 4 * CH) / 256;  // 16-byte activation pieces per thread
+  static_assert(2 * ABUF * 16 >= 32 * RB * BN * 4, "product tile must fit in the two activation buffers");
+  __shared__ __attribute__((aligned(16))) bf16x8_t smem[2 * ABUF];
+  __shared__ float s_inv[BN];
+  float* Cs = (float*)smem;  // [32 RB][BN] product tile, after the main loop
+
+  const int M = g.M, Ks = g.Ks, Nt = g.Nt;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int ng = blockIdx.x;
+  const int nt0 = ng * 8;
+  const int kb = SPLIT ? blockIdx.y * g.kper : 0;
+  const int ke = SPLIT ? min(Ks, kb + g.kper) : Ks;
+  const int nchunk = (ke - kb + CH - 1) / CH;  // chunks holding this workgroup's k-steps
+
+  // Both operands through raw buffer descriptors: the per-lane part of every offset is fixed for the whole
+  // kernel (one register per activation piece, one for the weights) and the chunk / k-step part is
+  // wave-uniform (a scalar offset). Out-of-range offsets read zeros without a memory request: activation
+  // rows >= M, weight tiles past the last one, and weight k-steps past this workgroup's range (a scalar
+  // offset beyond the buffer), so padded k-steps contribute exact zeros.
+  const __amdgpu_buffer_rsrc_t a_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, (gemm_a_row(g, M - 1) + 1) * g.lda * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)g.Wp_raw, (short)0, (int)((uint32_t)Nt * (uint32_t)Ks * 1024u), 0x00020000);
+  auto asw = [](int lp) { return lp ^ ((lp >> 4) << 2); };
+  const int fr_t = (lane & 31) >> 4, fr_l = (lane & 15) + 16 * (lane >> 5);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int w_lane = fr_t * Ks * 1024 + fr_l * 16;
+  const int w_tile = (nt0 + 2 * wv) * Ks * 1024;
+
+  typedef bf16x8_t RegW[CH][2];
+  typedef bf16x8_t RegA[NPIECE];
+  // piece p = tid + 256 q: row p / (4 CH), 16-byte segment p % (4 CH) of the chunk's 32 CH columns
+  int a_off[NPIECE];
+#pragma unroll
+  for (int q = 0; q < NPIECE; ++q) {
+    const int p = tid + 256 * q;
+    const int row = p / (4 * CH), seg = p % (4 * CH);
+    a_off[q] = row < M ? (gemm_a_row(g, row) * g.lda + kb * 32 + (seg >> 2) * 32 + 8 * (seg & 3)) * 2 : 0x7ffffff0;
+  }
+  // activation k-steps past the workgroup's range meet zero weights, so they need no mask
+  auto gload_a = [&](RegA& r, int c) {
+    const int so = CH * c * 64;
+#pragma unroll
+    for (int q = 0; q < NPIECE; ++q)
+      r[q] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off[q], so, 0));
+  };
+  auto sstore = [&](const RegA& r, int buf) {
+#pragma unroll
+    for (int q = 0; q < NPIECE; ++q) {
+      const int p = tid + 256 * q;
+      const int row = p / (4 * CH), seg = p % (4 * CH);
+      smem[buf * ABUF + ((seg >> 2) * MTL + (row >> 4)) * 64 + asw((row & 15) + 16 * (seg & 3))] = r[q];
+    }
+  };
+  auto gload_w = [&](RegW& r, int c) {
+#pragma unroll
+    for (int ks = 0; ks < CH; ++ks) {
+      const int kstep = kb + CH * c + ks;
+      const int so = kstep < ke ? w_tile + kstep * 1024 : 0x7ffffff0;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        r[ks][u] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_lane + 512 * u, so, 0));
+    }
+  };
+
+  f32x16_t acc[RB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+  auto compute = [&](int buf, const RegW& r) {
+#pragma unroll
+    for (int ks = 0; ks < CH; ++ks)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8_t af[RB];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) af[i] = smem[buf * ABUF + (ks * MTL + 2 * i + fr_t) * 64 + asw(fr_l + 32 * u)];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], r[ks][u], acc[i], 0, 0, 0);
+      }
+  };
+
+  // Vector-memory loads complete in issue order as far as the wait counter is concerned, so waiting for
+  // an activation chunk also waits for every weight load issued before it. Each step therefore stores
+  // the activations of the next chunk (loaded earlier) and issues the activation loads for a later chunk
+  // BEFORE its weight loads, so the weight loads of the chunks after the current one stay in flight
+  // through that wait. Chunk j uses LDS buffer j % 2. Steps past the workgroup's last chunk still issue
+  // their (zero) loads and barriers, so that every wait count is static, but skip the products.
+  if constexpr (NWB == 3) {
+    // weights two chunks ahead (three register sets), activations two chunks ahead (two register sets);
+    // at step j: ra[(j + 1) % 2] holds chunk j + 1, ra[j % 2] chunk j + 2, w[j % 3] chunk j
+    RegW w0, w1, w2;
+    RegA ra0, ra1;
+    gload_a(ra0, 0);
+    gload_a(ra1, 1);
+    gload_w(w0, 0);
+    gload_w(w1, 1);
+    gload_w(w2, 2);
+    sstore(ra0, 0);
+    gload_a(ra0, 2);
+    __syncthreads();
+    auto step = [&](RegA& ra, int sbuf, RegW& w, int j) {
+      sstore(ra, sbuf);
+      gload_a(ra, j + 3);
+      if (j < nchunk) compute(sbuf ^ 1, w);
+      gload_w(w, j + 3);
+      __syncthreads();
+    };
+    for (int c = 0; c < nchunk; c += 6) {
+      step(ra1, 1, w0, c);
+      step(ra0, 0, w1, c + 1);
+      step(ra1, 1, w2, c + 2);
+      step(ra0, 0, w0, c + 3);
+      step(ra1, 1, w1, c + 4);
+      step(ra0, 0, w2, c + 5);
+    }
+  } else {
+    // weights one chunk ahead (two register sets), activations one chunk ahead
+    RegW w0, w1;
+    RegA ra;
+    gload_a(ra, 0);
+    gload_w(w0, 0);
+    sstore(ra, 0);
+    gload_a(ra, 1);
+    gload_w(w1, 1);
+    __syncthreads();
+    auto step = [&](int sbuf, RegW& w, int j) {
+      sstore(ra, sbuf);
+      gload_a(ra, j + 2);
+      if (j < nchunk) compute(sbuf ^ 1, w);
+      gload_w(w, j + 2);
+      __syncthreads();
+    };
+    for (int c = 0; c < nchunk; c += 2) {
+      step(1, w0, c);
+      step(0, w1, c + 1);
+    }
+  }
+
+  // product tile -> LDS (row R's columns XOR-swizzled by 32 ((R >> 2) & 1), as the epilogue reads them)
+  {
+    const int c = lane & 31, hq = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = 32 * i + 8 * (e >> 2) + 4 * hq + (e & 3);
+        Cs[row * BN + ((32 * wave + c) ^ (hq << 5))] = acc[i][e];
+      }
+  }
+  if (AM == A_NORM) {
+    const int r = tid >> 1, h = tid & 1;
+    float t = 0.f;
+    if (r < M) {
+      const float* src = g.ssq_in + (size_t)gemm_a_row(g, r) * g.nssq;
+      for (int i = h; i < g.nssq; i += 2) t += src[i];
+    }
+    t += __shfl_xor(t, 1, PE_WAVE);
+    if (h == 0) s_inv[r] = rsqrtf(t / (float)g.Kd + g.eps);
+  }
+  __syncthreads();
+  if (SPLIT) tile_epilogue<EPI_PARTIAL, AM == A_NORM>(g, Cs, s_inv, 0, nt0, ng, 0, 32 * RB);
+  else tile_epilogue<EP, AM == A_NORM>(g, Cs, s_inv, 0, nt0, ng, 0, 32 * RB);
+}
+
+template <int RB, int CH, int NWB>
+static hipError_t launch_stream_rb(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st) {
+  const dim3 block(256);
+  if (p.ksplit > 1) {
+    if (!a.part || epi == EPI_ARGMAX) return hipErrorInvalidValue;
+    const dim3 grid(p.ngroups, p.ksplit);
+    if (a_mode == A_BF16) hipLaunchKernelGGL((gemm_stream_kernel<A_BF16, EPI_PARTIAL, true, RB, CH, NWB>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((gemm_stream_kernel<A_NORM, EPI_PARTIAL, true, RB, CH, NWB>), grid, block, 0, st, a);
+    return hipGetLastError();
+  }
+  const dim3 grid(p.ngroups);
+  if (a_mode == A_BF16 && epi == EPI_RESID) hipLaunchKernelGGL((gemm_stream_kernel<A_BF16, EPI_RESID, false, RB, CH, NWB>), grid, block, 0, st, a);
+  else if (a_mode == A_BF16 && epi == EPI_ROWS) hipLaunchKernelGGL((gemm_stream_kernel<A_BF16, EPI_ROWS, false, RB, CH, NWB>), grid, block, 0, st, a);
+  else if (a_mode == A_NORM && epi == EPI_QKV) hipLaunchKernelGGL((gemm_stream_kernel<A_NORM, EPI_QKV, false, RB, CH, NWB>), grid, block, 0, st, a);
+  else if (a_mode == A_NORM && epi == EPI_SWIGLU) hipLaunchKernelGGL((gemm_stream_kernel<A_NORM, EPI_SWIGLU, false, RB, CH, NWB>), grid, block, 0, st, a);
+  else if (a_mode == A_NORM && epi == EPI_ARGMAX) hipLaunchKernelGGL((gemm_stream_kernel<A_NORM, EPI_ARGMAX, false, RB, CH, NWB>), grid, block, 0, st, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+static hipError_t launch_gemm_stream(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st) {
+  if (a.M < 1 || a.M > 128) return hipErrorInvalidValue;
+  // weights one chunk ahead (measured: two chunks ahead, with a six-step unroll, was no faster for the
+  // 88-row vocabulary projection and slower for the four-chunk K-split products)
+  hipError_t e;
+  if (a.M <= 64) e = launch_stream_rb<2, GEMM_STREAM_CH, 2>(p, a, a_mode, epi, st);
+  else if (a.M <= 96) e = launch_stream_rb<3, GEMM_STREAM_CH, 2>(p, a, a_mode, epi, st);
+  else e = launch_stream_rb<4, GEMM_STREAM_CH, 2>(p, a, a_mode, epi, st);
+  if (e != hipSuccess || p.ksplit <= 1) return e;
+  const dim3 rgrid(8 * ((p.ngroups + 7) / 8), 8);  // 16-row slices of each 128-column tile
+  const dim3 block(256);
+  if (epi == EPI_RESID) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_RESID>), rgrid, block, 0, st, a);
+  else if (epi == EPI_ROWS) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_ROWS>), rgrid, block, 0, st, a);
+  else if (epi == EPI_QKV) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_QKV>), rgrid, block, 0, st, a);
+  else if (epi == EPI_SWIGLU) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_SWIGLU>), rgrid, block, 0, st, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st) {
+  if (p.tiled == 2) return launch_gemm_stream(p, a, a_mode, epi, st);
   const int tiles = 8 * ((p.ngroups + 7) / 8) * p.mblocks;
   const dim3 block(256);
   if (p.ksplit > 1) {
