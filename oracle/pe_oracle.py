@@ -29,6 +29,11 @@ Readings where the pages leave a step open (each is listed with its reason in th
     placeholder row at position L_b + K (after the K draft rows, so it changes none of them) and keeps
     only its K/V: draft_step(..., tail=True).
 
+  * autoregressive drafting (the baseline parallel drafting replaces) feeds back the drafter's hidden
+    state after its last layer (before the final norm) plus the embedding of the token it just drafted;
+    the pages name the dependency but not which hidden state, so this reading is parity unpinned
+    against the pages (it is pinned against the separately written loop-by-loop pass).
+
 Parity status: each function below is pinned by tests under tests/ (closed forms, invariants, special
 cases, brute force on tiny inputs). The full-step logit values have no printed worked example on the
 pages; beyond the invariants they are pinned by the separately written sequential single-row step.
@@ -218,25 +223,82 @@ def draft_step(shape, W: dict, state: dict, kv_context, K: int, tail: bool = Fal
     return out
 
 
+def draft_autoregressive(shape, W: dict, state: dict, kv_context, K: int, tail: bool = False,
+                         feed: np.ndarray = None) -> dict:
+    """Autoregressive EAGLE-style drafting of K tokens, the chain that parallel drafting removes ([AWS-P]
+    "sequential dependency in autoregressive EAGLE": each draft token needs the previous pass's hidden
+    state and token, so K tokens take K forward passes).
+
+    Pass 0 runs the parallel step's row 0 (fc(concat(h)) + E[last_token]) at position L_b. Pass i >= 1
+    runs one row per request at position L_b + i: the drafter's own hidden state of pass i - 1 (the
+    residual stream after the last layer, before the final norm) plus the embedding of the token pass
+    i - 1 drafted; it attends to the context and to the rows of passes 0..i-1. feed [B, K] optionally
+    replaces the token fed back after pass i (row i of feed), e.g. to follow another implementation's
+    choice at a near-tie. tail=True runs one more pass (layers only) at position L_b + K, so the cache holds
+    K/V for every position an all-accepted verify keeps, as the parallel step's placeholder row does.
+
+    Returns logits [B, K, V], draft [B, K], hidden [B, K, d] and k_new / v_new per layer [B, K(+1), Hkv, hd].
+    """
+    B = state["last_token"].shape[0]
+    seq = np.asarray(state["seq_len"], dtype=np.int64)
+    row0 = build_rows(W, state["last_token"], state["target_hidden"], 1)[:, 0]
+    logits, draft, hidden = [], [], []
+    k_new = [[] for _ in range(shape.n_layers)]
+    v_new = [[] for _ in range(shape.n_layers)]
+
+    def ctx_with_passes(l, b):
+        k_ctx, v_ctx = kv_context(l, b)
+        if not k_new[l]:
+            return k_ctx, v_ctx
+        k_add = np.stack([kn[b] for kn in k_new[l]], axis=1)  # [Hkv, passes, hd]
+        v_add = np.stack([vn[b] for vn in v_new[l]], axis=1)
+        return np.concatenate([k_ctx, k_add], axis=1), np.concatenate([v_ctx, v_add], axis=1)
+
+    row = row0
+    for i in range(K + 1 if tail else K):
+        out = draft_rows(shape, W, row[:, None, :], seq + i, ctx_with_passes)
+        for l in range(shape.n_layers):
+            k_new[l].append(out["k_new"][l][:, 0])
+            v_new[l].append(out["v_new"][l][:, 0])
+        if i == K:
+            break
+        logits.append(out["logits"][:, 0])
+        draft.append(out["draft"][:, 0])
+        hidden.append(out["hidden"][:, 0])
+        tok = draft[-1] if feed is None else np.asarray(feed)[:, i]
+        row = hidden[-1] + W["embed"][tok]
+    return {"logits": np.stack(logits, axis=1), "draft": np.stack(draft, axis=1),
+            "hidden": np.stack(hidden, axis=1),
+            "k_new": [np.stack(k, axis=1) for k in k_new], "v_new": [np.stack(v, axis=1) for v in v_new]}
+
+
 # --------------------------------------------------------------------------------------------------
 # written separately, loop by loop: one sequential EAGLE-style draft for one request
 
 
-def eagle_step_sequential(shape, W: dict, token: int, hid3: np.ndarray, L: int, kv_ctx_layers) -> tuple:
+def eagle_step_sequential(shape, W: dict, token: int, hid3: np.ndarray, L: int, kv_ctx_layers,
+                          row: np.ndarray = None, full: bool = False) -> tuple:
     """One autoregressive EAGLE draft pass for a single request ([AWS-P] "sequential dependency in
     autoregressive EAGLE"): the input is the embedding of the token just produced plus the projected
     target hidden states; one row goes through the layers at position L; the LM head gives one token.
+    kv_ctx_layers[l] = (k [Hkv, >= L, hd], v [Hkv, >= L, hd]): the first L positions are the context.
+    row: a prebuilt input row used instead of fc(hid3) + E[token] (a later autoregressive pass).
 
     Written with explicit per-head and per-key loops, independently of draft_rows. Returns
-    (token, logits [V]).
+    (token, logits [V]); with full=True also the hidden state after the last layer (before the final
+    norm) and this row's rotated keys and values per layer ([Hkv, hd] each).
     """
     d = shape.d_model
     Hq, Hkv, hd = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
     G = Hq // Hkv
     half = hd // 2
     eps = shape.rms_eps
-    fc = W["fc"]
-    x = np.array([float(np.dot(fc[r], hid3)) for r in range(d)]) + W["embed"][token]
+    if row is None:
+        fc = W["fc"]
+        x = np.array([float(np.dot(fc[r], hid3)) for r in range(d)]) + W["embed"][token]
+    else:
+        x = np.array(row, dtype=np.float64)
+    k_rows, v_rows = [], []
 
     def norm(v, g):
         return v * (1.0 / math.sqrt(float(np.dot(v, v)) / d + eps)) * g
@@ -257,6 +319,8 @@ def eagle_step_sequential(shape, W: dict, token: int, hid3: np.ndarray, L: int, 
         attn = np.zeros(Hq * hd)
         k_self = [rot(wqkv[(Hq + g) * hd:(Hq + g + 1) * hd] @ u) for g in range(Hkv)]
         v_self = [wqkv[(Hq + Hkv + g) * hd:(Hq + Hkv + g + 1) * hd] @ u for g in range(Hkv)]
+        k_rows.append(np.array(k_self))
+        v_rows.append(np.array(v_self))
         for h in range(Hq):
             qh = rot(wqkv[h * hd:(h + 1) * hd] @ u)
             g = h // G
@@ -281,6 +345,8 @@ def eagle_step_sequential(shape, W: dict, token: int, hid3: np.ndarray, L: int, 
     for v in range(1, z.shape[0]):
         if z[v] > z[best]:
             best = v
+    if full:
+        return best, z, x, k_rows, v_rows
     return best, z
 
 

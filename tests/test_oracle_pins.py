@@ -380,3 +380,84 @@ def test_kv_blocks_reproducible_per_request():
     a = kv_block(w, 1, 0, 2, 5)
     b = kv_block(w, 1, 0, 2, 5)
     assert np.array_equal(a, b) and not np.array_equal(a, kv_block(w, 1, 1, 2, 5))
+
+
+# ---------------------------------------------------------------- autoregressive drafting (the baseline)
+
+def _ar(shape, W, tokens, hid, seq, ctx, K, tail=False, feed=None):
+    st = {"last_token": np.asarray(tokens), "target_hidden": hid, "seq_len": np.asarray(seq)}
+    return O.draft_autoregressive(shape, W, st, lambda l, b: ctx[b][l], K, tail=tail, feed=feed)
+
+
+def _ar_loops(shape, W, tok, hid, L, ctx, K):
+    """The same chain from the separately written loop-by-loop pass: pass i runs at position L + i over
+    the context plus the K/V of passes 0..i-1, on the row h_{i-1} + E[t_{i-1}]."""
+    ctx = [(k.copy(), v.copy()) for k, v in ctx]
+    toks, zs, row = [], [], None
+    for i in range(K):
+        t, z, x, k_rows, v_rows = O.eagle_step_sequential(shape, W, tok, hid, L + i, ctx, row=row, full=True)
+        toks.append(t)
+        zs.append(z)
+        ctx = [(np.concatenate([k, kr[:, None, :]], axis=1), np.concatenate([v, vr[:, None, :]], axis=1))
+               for (k, v), kr, vr in zip(ctx, k_rows, v_rows)]
+        row = x + W["embed"][t]
+    return toks, np.stack(zs)
+
+
+def test_autoregressive_chain_matches_loop_by_loop_passes():
+    # the vectorised chain (draft_rows per pass, context grown by each pass's K/V) against the explicit
+    # per-head, per-key loops of eagle_step_sequential, pass by pass
+    W = _weights64(MINI, 31)
+    rng = np.random.default_rng(31)
+    for L, K in ((0, 3), (5, 4)):
+        tok = int(rng.integers(0, MINI.vocab))
+        hid = rng.standard_normal((1, 3 * MINI.d_model))
+        ctx = _ctx(MINI, L, 300 + L)
+        out = _ar(MINI, W, [tok], hid, [L], [ctx], K)
+        toks, zs = _ar_loops(MINI, W, tok, hid[0], L, ctx, K)
+        assert out["draft"][0].tolist() == toks
+        assert out["logits"][0] == pytest.approx(zs, rel=1e-9, abs=1e-12)
+
+
+def test_autoregressive_k1_and_pass0_equal_the_parallel_step():
+    # K = 1: one pass, the same as the parallel step with K = 1; for any K, pass 0 sees only the context
+    # and itself, so it equals the parallel step's row 0
+    W = _weights64(MINI, 32)
+    rng = np.random.default_rng(32)
+    toks = rng.integers(0, MINI.vocab, size=2)
+    hid = rng.standard_normal((2, 3 * MINI.d_model))
+    ctx = [_ctx(MINI, 4, 320), _ctx(MINI, 9, 321)]
+    ar1 = _ar(MINI, W, toks, hid, [4, 9], ctx, 1)
+    pe1 = _step(MINI, W, toks, hid, [4, 9], ctx, 1)
+    assert np.array_equal(ar1["logits"], pe1["logits"])
+    ar3 = _ar(MINI, W, toks, hid, [4, 9], ctx, 3)
+    pe3 = _step(MINI, W, toks, hid, [4, 9], ctx, 3)
+    assert np.array_equal(ar3["logits"][:, 0], pe3["logits"][:, 0])
+    assert ar3["logits"].shape == (2, 3, MINI.vocab)
+
+
+def test_autoregressive_tail_and_feed():
+    # the tail pass adds the K/V of position L + K and changes no output; a feed equal to the drafted
+    # tokens changes nothing, a different feed changes every later pass but not pass 0
+    W = _weights64(MINI, 33)
+    rng = np.random.default_rng(33)
+    tok = [int(rng.integers(0, MINI.vocab))]
+    hid = rng.standard_normal((1, 3 * MINI.d_model))
+    ctx = [_ctx(MINI, 6, 330)]
+    a = _ar(MINI, W, tok, hid, [6], ctx, 3)
+    t = _ar(MINI, W, tok, hid, [6], ctx, 3, tail=True)
+    assert np.array_equal(a["logits"], t["logits"])
+    assert a["k_new"][0].shape[1] == 3 and t["k_new"][0].shape[1] == 4
+    assert np.array_equal(t["k_new"][1][:, :3], a["k_new"][1][:, :3])
+    # the tail row is the pass-3 row h_2 + E[d_2] at position L + 3: check its layer-0 key by hand
+    x = a["hidden"][0, 2] + W["embed"][a["draft"][0, 2]]
+    u = O.rms_norm(x[None], W["l0.attn_norm"], MINI.rms_eps)
+    k = O.linear(u, W["l0.wqkv"])[0, MINI.n_q_heads * MINI.head_dim:(MINI.n_q_heads + MINI.n_kv_heads) * MINI.head_dim]
+    k = O.rope(k.reshape(1, MINI.n_kv_heads, MINI.head_dim), np.array([9]), MINI.rope_base)[0]
+    assert t["k_new"][0][0, 3] == pytest.approx(k, rel=1e-12, abs=1e-12)
+    same = _ar(MINI, W, tok, hid, [6], ctx, 3, feed=a["draft"])
+    assert np.array_equal(same["logits"], a["logits"])
+    other = (a["draft"] + 1) % MINI.vocab
+    f = _ar(MINI, W, tok, hid, [6], ctx, 3, feed=other)
+    assert np.array_equal(f["logits"][:, 0], a["logits"][:, 0])
+    assert not np.allclose(f["logits"][:, 1], a["logits"][:, 1])
