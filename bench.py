@@ -79,6 +79,37 @@ def lm_head_roofline(w, ab, lm_us, lm_n, traffic):
     return r
 
 
+def latency_vs_depth(pe, torch, w, cfg_args, dev, kc, vc, d, stream, reps, depths=(1, 3, 7, 11)):
+    """Draft latency against the draft depth K on the same requests and contexts: one parallel pass
+    (pe_draft_step) against K autoregressive passes (pe_draft_ar), the comparison the pages make between
+    parallel and autoregressive drafting. Timed with HIP events on the library stream, outside the
+    step's timed region. bf16 drafters only (the autoregressive entry point needs one)."""
+    s = w.shape
+    if s.dtype != "bf16":
+        return None
+    depths = [k for k in depths if w.ctx[1] + k + 1 <= w.max_ctx]
+    ctx = pe.pe_init(pe.make_config(**cfg_args(w, max_k=max(depths))), pe.make_weights(dev, s.n_layers),
+                     pe.make_kv(kc, vc), stream.cuda_stream)
+    out = {"B": w.B, "K": depths, "parallel_us": [], "autoregressive_us": []}
+    for K in depths:
+        tok = torch.empty((w.B, K), dtype=torch.int32, device="cuda")
+        for fn, key in ((pe.pe_draft_step, "parallel_us"), (pe.pe_draft_ar, "autoregressive_us")):
+            def call():
+                fn(ctx, w.B, K, d["req_slot"], d["seq_len"], d["last_token"], d["target_hidden"], tok, None)
+            for _ in range(3):
+                call()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out[key].append(1e3 * e0.elapsed_time(e1) / reps)
+    pe.pe_destroy(ctx)
+    out["autoregressive_over_parallel"] = [a / p for a, p in zip(out["autoregressive_us"], out["parallel_us"])]
+    return out
+
+
 def traffic_from_profile(workload_name):
     """HBM bytes per LM-head launch measured by rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, scaled by
     the plain-copy calibration), if the committed measurement was taken with the current kernel source."""
@@ -228,6 +259,8 @@ def main():
         kern[name] = {"avg_us": 1e3 * tot / max(n, 1), "launches": n}
     pe.pe_profile_enable(ctx, 0)
 
+    depth = latency_vs_depth(pe, torch, w, config_args, dev, kc, vc, d, stream, reps)
+
     if args.copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
         dst = torch.empty_like(src)
@@ -269,6 +302,7 @@ def main():
         "kernels": kern,
         "roofline": lm_head_roofline(w, ab, lm_us, lm_n, traffic),
         "device_flags": flags,
+        "draft_latency_vs_depth": depth,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, state, T_host, args.cpu_seconds)

@@ -6,6 +6,7 @@ arguments to it. PyTorch is only used by callers for device memory and streams.
 
 from .binding import (  # noqa: F401
     PE_BF16,
+    PE_ERR_UNSUPPORTED,
     PE_F32,
     PE_PROF_ATTENTION,
     PE_PROF_GATE_UP,
@@ -20,6 +21,7 @@ from .binding import (  # noqa: F401
     pe_config_validate,
     pe_destroy,
     pe_device_flags,
+    pe_draft_ar,
     pe_draft_rows,
     pe_draft_step,
     pe_init,

@@ -22,7 +22,7 @@ PE_PROF_LM_HEAD, PE_PROF_ATTENTION, PE_PROF_GATE_UP, PE_PROF_VERIFY_SCAN = 0, 1,
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpe.so")
 
-EXPORTED = ["pe_config_validate", "pe_init", "pe_draft_step", "pe_draft_rows", "pe_verify", "pe_destroy",
+EXPORTED = ["pe_config_validate", "pe_init", "pe_draft_step", "pe_draft_rows", "pe_draft_ar", "pe_verify", "pe_destroy",
             "pe_device_flags", "pe_profile_enable", "pe_profile_read", "pe_status_string", "pe_last_error"]
 
 
@@ -82,6 +82,7 @@ def load_library(path: str = LIB_PATH):
         "pe_init": ([POINTER(pe_config), POINTER(pe_weights), POINTER(pe_kv), vp, POINTER(vp)], i32),
         "pe_draft_step": ([vp, i32, i32, vp, vp, vp, vp, vp, vp], i32),
         "pe_draft_rows": ([vp, i32, i32, vp, vp, vp, vp, vp], i32),
+        "pe_draft_ar": ([vp, i32, i32, vp, vp, vp, vp, vp, vp], i32),
         "pe_verify": ([vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp], i32),
         "pe_destroy": ([vp], i32),
         "pe_device_flags": ([vp, i32, POINTER(i32)], i32),
@@ -136,6 +137,11 @@ def pe_init(cfg: pe_config, weights: pe_weights, kv: pe_kv, stream: int = 0):
 def pe_draft_step(ctx, B, K, req_slot, seq_len, last_token, target_hidden, draft_tokens, logits=None):
     _check(load_library().pe_draft_step(ctx, B, K, _ptr(req_slot), _ptr(seq_len), _ptr(last_token),
                                         _ptr(target_hidden), _ptr(draft_tokens), _ptr(logits)), ctx)
+
+
+def pe_draft_ar(ctx, B, K, req_slot, seq_len, last_token, target_hidden, draft_tokens, logits=None):
+    _check(load_library().pe_draft_ar(ctx, B, K, _ptr(req_slot), _ptr(seq_len), _ptr(last_token),
+                                      _ptr(target_hidden), _ptr(draft_tokens), _ptr(logits)), ctx)
 
 
 def pe_draft_rows(ctx, B, K, req_slot, seq_len, rows, draft_tokens, logits=None):

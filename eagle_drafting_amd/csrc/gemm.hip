@@ -342,7 +342,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
       const bool ok = t < NT && n < N;
       float v = ok ? Y(t, r, c) : -INFINITY;
       int idx = ok ? n : 0x7fffffff;
-      if (g.logits && ok) g.logits[(size_t)m * N + n] = v;
+      if (g.logits && ok) g.logits[(size_t)m * g.ldz + n] = v;
       am_wave_reduce(v, idx, 64);
       if (lane == 0) {
         g.am_val[(size_t)m * g.ngroups + blockIdx.x] = v;
@@ -479,6 +479,7 @@ hipError_t launch_gemm(const GemmPlan& p, GemmArgs a, int a_mode, int epi, hipSt
   a.Ks = p.ki4 ? k_steps_ki4(a.Kd) : k_steps(a.Kd);
   a.ngroups = p.ngroups;
   a.mblocks = p.mblocks;
+  if (a.ldz == 0) a.ldz = a.N;
   a.ksplit = p.ksplit;
   a.kper = p.kper;
   if (p.tiled) return launch_gemm_tiled(p, a, a_mode, epi, st);
@@ -538,6 +539,45 @@ hipError_t launch_rows_ssq(const float* rows, float* X, float* ssq, uint16_t* XG
                            hipStream_t st) {
   hipLaunchKernelGGL(rows_ssq_kernel, dim3(M), dim3(256), 0, st, rows, X, ssq, (bf16_t*)XG, (const bf16_t*)gain, d,
                      (d + 15) / 16);
+  return hipGetLastError();
+}
+
+// autoregressive pass >= 1: the previous pass's residual stream plus the embedding of the token it drafted
+__global__ __launch_bounds__(256) void ar_rows_kernel(float* __restrict__ X, bf16_t* __restrict__ XG,
+                                                      float* __restrict__ ssq, const bf16_t* __restrict__ embed,
+                                                      const bf16_t* __restrict__ gain, const int* __restrict__ prev_tok,
+                                                      int* __restrict__ draft_tokens, int K, int pass,
+                                                      const int* __restrict__ seq_len, int* __restrict__ seq_cur,
+                                                      int d, int V, int* flags) {
+  const int b = blockIdx.x;
+  const int tok = prev_tok[b];
+  const bool ok = tok >= 0 && tok < V;
+  if (threadIdx.x == 0) {
+    draft_tokens[(size_t)b * K + pass - 1] = tok;
+    seq_cur[b] = seq_len[b] + pass;
+    if (!ok) raise_flag(flags, PE_FLAG_TOKEN);
+  }
+  const int nssq = (d + 15) / 16;
+  for (int c0 = 0; c0 < nssq * 16; c0 += 256) {
+    const int c = c0 + threadIdx.x;
+    float v = 0.f;
+    if (c < d) {
+      v = X[(size_t)b * d + c] + (ok ? bf16_to_f32(embed[(size_t)tok * d + c]) : 0.f);
+      X[(size_t)b * d + c] = v;
+      XG[(size_t)b * d + c] = f32_to_bf16(v * bf16_to_f32(gain[c]));
+    }
+    float sq = v * v;
+    for (int off = 8; off > 0; off >>= 1) sq += __shfl_xor(sq, off, PE_WAVE);
+    if ((c & 15) == 0 && c / 16 < nssq) ssq[(size_t)b * nssq + c / 16] = sq;
+  }
+}
+
+hipError_t launch_ar_rows(float* X, uint16_t* XG, float* ssq, const uint16_t* embed, const uint16_t* gain,
+                          const int* prev_tok, int* draft_tokens, int K, int pass, const int* seq_len, int* seq_cur,
+                          int B, int d, int V, int* flags, hipStream_t st) {
+  if (pass < 1 || pass > K) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(ar_rows_kernel, dim3(B), dim3(256), 0, st, X, (bf16_t*)XG, ssq, (const bf16_t*)embed,
+                     (const bf16_t*)gain, prev_tok, draft_tokens, K, pass, seq_len, seq_cur, d, V, flags);
   return hipGetLastError();
 }
 

@@ -305,8 +305,8 @@ __device__ void tile_epilogue(const GemmArgs& g, const float* Cs, const float* s
         for (int e = 0; e < 4; ++e)
           if (n + e < N && am_better(vv[e], n + e, bv, bi)) { bv = vv[e]; bi = n + e; }
         if (g.logits && m < M) {
-          float* z = g.logits + (size_t)m * N;
-          if (n + 3 < N && (N & 3) == 0) *(float4*)(z + n) = v;
+          float* z = g.logits + (size_t)m * g.ldz;
+          if (n + 3 < N && (N & 3) == 0 && (g.ldz & 3) == 0) *(float4*)(z + n) = v;
           else
             for (int e = 0; e < 4; ++e)
               if (n + e < N) z[n + e] = vv[e];

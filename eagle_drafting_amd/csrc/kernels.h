@@ -75,8 +75,9 @@ struct GemmArgs {
   int Kdraft, Hq, Hkv, hd, max_ctx, n_slots; int* flags;
   // EPI_ROWS
   const int* last_token; const uint16_t* embed; const uint16_t* emb_mask; const uint16_t* h_shared; int V;
-  // EPI_ARGMAX: per (row, workgroup) best (value, index); optional fp32 logits [M][N]
-  float* am_val; int* am_idx; float* logits;
+  // EPI_ARGMAX: per (row, workgroup) best (value, index); optional fp32 logits, row m at logits + m * ldz
+  // (ldz = 0 means N)
+  float* am_val; int* am_idx; float* logits; int ldz;
   // row m of the product reads operand row (m / rows_out) * rows_in + m % rows_out (and that row's sums
   // of squares): the LM head runs on rows_out of every rows_in rows per request. 0 = identity.
   int rows_in, rows_out;
@@ -89,6 +90,12 @@ __host__ __device__ inline int gemm_a_row(const GemmArgs& g, int m) {
 }
 hipError_t launch_gemm(const GemmPlan& p, GemmArgs a, int a_mode, int epi, hipStream_t st);
 hipError_t launch_gemm_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st);
+// Autoregressive pass `pass` >= 1: row b = X[b] (the previous pass's residual stream after the last layer)
+// + embed[prev_tok[b]]; records prev_tok[b] as draft pass - 1 of request b (draft_tokens [B, K]), writes the
+// pass's positions seq_cur[b] = seq_len[b] + pass, XG = bf16(x * gain) and per-16-column sums of squares.
+hipError_t launch_ar_rows(float* X, uint16_t* XG, float* ssq, const uint16_t* embed, const uint16_t* gain,
+                          const int* prev_tok, int* draft_tokens, int K, int pass, const int* seq_len, int* seq_cur,
+                          int B, int d, int V, int* flags, hipStream_t st);
 hipError_t launch_rows_ssq(const float* rows, float* X, float* ssq, uint16_t* XG, const uint16_t* gain, int M, int d,
                            hipStream_t st);
 // fp32 weights, unpacked [N, Kd]: out[m * ldo + n]

@@ -49,6 +49,8 @@ struct pe_ctx {
   float2* rope = nullptr;  // [max_ctx, hd/2] (cos, sin)
   float* ssq = nullptr;    // partial sums of squares of X rows [Mmax, d/4] (per 16 or per 4 columns)
   int* flags = nullptr;
+  int* ar_tok = nullptr;   // autoregressive drafting: the token each request drafted in the latest pass [max_batch]
+  int* ar_seq = nullptr;   // ... and the positions of the current pass [max_batch]
 
   std::string err;
 
@@ -269,7 +271,8 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
                oAt = take(std::max(attn_floats, (size_t)1) * 4), oAv = take(am_floats * 4), oAi = take(am_floats * 4),
                oT = take((size_t)c.max_batch * (c.max_k + 1) * 4),
                oL = take(ctx->bf16 ? 0 : (size_t)Mmax * V * 4), oR = take((size_t)c.max_ctx * (hd / 2) * 8),
-               oS = take((size_t)Mmax * nssq * 4), oF = take(256), oK = take(part_floats * 4);
+               oS = take((size_t)Mmax * nssq * 4), oF = take(256), oK = take(part_floats * 4),
+               oArT = take((size_t)c.max_batch * 4), oArS = take((size_t)c.max_batch * 4);
   if (hipMalloc((void**)&ctx->ws, off) != hipSuccess) {
     free_ctx(ctx);
     return fail(nullptr, PE_ERR_OOM, "hipMalloc of workspace failed");
@@ -290,6 +293,8 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
   ctx->ssq = (float*)(b + oS);
   ctx->flags = (int*)(b + oF);
   ctx->part = part_floats ? (float*)(b + oK) : nullptr;
+  ctx->ar_tok = (int*)(b + oArT);
+  ctx->ar_seq = (int*)(b + oArS);
 
   hipError_t r = launch_rope_table(ctx->rope, c.max_ctx, hd, (double)c.rope_base, ctx->stream);
   if (r == hipSuccess) r = hipMemsetAsync(ctx->flags, 0, 256, ctx->stream);
@@ -413,45 +418,50 @@ static pe_status draft_f32(pe_ctx* ctx, int32_t B, int32_t K, int32_t Kout, cons
 
 // bf16 drafter: per layer six kernels (QKV+RoPE+KV append, attention, combine, O+residual, gate/up+SwiGLU,
 // down+residual); RMSNorm is applied while the next projection reads its input.
-static pe_status draft_bf16(pe_ctx* ctx, int32_t B, int32_t K, int32_t Kout, const int32_t* req_slot,
-                            const int32_t* seq_len,
-                            const int32_t* last_token, const void* target_hidden, const float* rows,
-                            int32_t* draft_tokens, float* logits) {
+static GemmArgs gemm_base(pe_ctx* ctx) {
+  GemmArgs base{};
+  base.Xout = ctx->X;
+  base.XGout = (uint16_t*)ctx->U;  // XG = bf16(x * g) of the next normalised projection lives in the U buffer
+  base.ssq_in = ctx->ssq;
+  base.ssq_out = ctx->ssq;
+  base.eps = ctx->cfg.rms_eps;
+  base.flags = ctx->flags;
+  base.part = ctx->part;
+  return base;
+}
+
+// a1 (+ the sums of squares for layer 0's RMSNorm): Kr input rows per request from the row builder
+static pe_status rows_bf16(pe_ctx* ctx, int32_t B, int32_t Kr, const int32_t* last_token, const void* target_hidden,
+                           int& nssq) {
+  const pe_config& c = ctx->cfg;
+  const int d = c.d_model;
+  GemmArgs a = gemm_base(ctx);
+  a.M = B; a.Kd = 3 * d; a.N = d;
+  a.A = (const uint16_t*)target_hidden; a.lda = 3 * d;
+  a.Kdraft = Kr; a.last_token = last_token; a.V = c.vocab;
+  a.embed = (const uint16_t*)ctx->w.embed; a.emb_mask = (const uint16_t*)ctx->w.emb_mask;
+  a.h_shared = (const uint16_t*)ctx->w.h_shared;
+  a.gain_next = (const uint16_t*)ctx->w.attn_norm[0];
+  const GemmPlan p = plan_gemm(B, d, 3 * d, false, true);
+  a.Wp_raw = p.ki4 ? ctx->p_fc4 : ctx->p_fc;
+  a.nssq_out = nssq = gemm_ssq_parts(p);
+  hipStream_t st = ctx->stream;
+  LAUNCH(launch_gemm(p, a, A_BF16, EPI_ROWS, st));
+  return PE_OK;
+}
+
+// a2-a8 for every layer over the B * K rows in X (and their normalised operand); row j of request b sits
+// at position seq_len[b] + j. nssq: the partial sums of squares per row of X on entry, updated on exit.
+static pe_status layers_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_slot, const int32_t* seq_len,
+                             int& nssq) {
   const pe_config& c = ctx->cfg;
   hipStream_t st = ctx->stream;
-  const int d = c.d_model, F = c.ffn_dim, V = c.vocab, hd = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+  const int d = c.d_model, F = c.ffn_dim, hd = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
   const int qd = Hq * hd, qkvd = (Hq + 2 * Hkv) * hd;
   const int M = B * K;
   const pe_weights& w = ctx->w;
-  // partial sums of squares per row written by the latest residual-stream producer
-  int nssq = (d + 15) / 16;
-
-  // XG = bf16(x * g) of the next normalised projection lives in the U buffer
   uint16_t* XG = (uint16_t*)ctx->U;
-  GemmArgs base{};
-  base.Xout = ctx->X;
-  base.XGout = XG;
-  base.ssq_in = ctx->ssq;
-  base.ssq_out = ctx->ssq;
-  base.eps = c.rms_eps;
-  base.flags = ctx->flags;
-  base.part = ctx->part;
-
-  // a1 (+ the sums of squares for layer 0's RMSNorm): the K input rows of every request
-  if (!rows) {
-    GemmArgs a = base;
-    a.M = B; a.Kd = 3 * d; a.N = d;
-    a.A = (const uint16_t*)target_hidden; a.lda = 3 * d;
-    a.Kdraft = K; a.last_token = last_token; a.V = V;
-    a.embed = (const uint16_t*)w.embed; a.emb_mask = (const uint16_t*)w.emb_mask; a.h_shared = (const uint16_t*)w.h_shared;
-    a.gain_next = (const uint16_t*)w.attn_norm[0];
-    const GemmPlan p = plan_gemm(B, d, 3 * d, false, true);
-    a.Wp_raw = p.ki4 ? ctx->p_fc4 : ctx->p_fc;
-    a.nssq_out = nssq = gemm_ssq_parts(p);
-    LAUNCH(launch_gemm(p, a, A_BF16, EPI_ROWS, st));
-  } else {
-    LAUNCH(launch_rows_ssq(rows, ctx->X, ctx->ssq, XG, (const uint16_t*)w.attn_norm[0], M, d, st));
-  }
+  const GemmArgs base = gemm_base(ctx);
   for (int l = 0; l < c.n_layers; ++l) {
     {  // a2-a4: RMSNorm, QKV, RoPE, KV append
       GemmArgs a = base;
@@ -505,20 +515,75 @@ static pe_status draft_bf16(pe_ctx* ctx, int32_t B, int32_t K, int32_t Kout, con
       LAUNCH(launch_gemm(p, a, A_BF16, EPI_RESID, st));
     }
   }
-  // a9-a10: final RMSNorm, LM head, argmax on the Kout emitted rows of every request
+  return PE_OK;
+}
+
+// a9-a10: final RMSNorm, LM head, argmax on the first Kout of the K rows of every request; tokens [B * Kout];
+// logits row (b, j) at logits + (b * Kout + j) * ldz
+static pe_status lm_head_bf16(pe_ctx* ctx, int32_t B, int32_t K, int32_t Kout, int nssq, int32_t* tokens,
+                              float* logits, int ldz) {
+  const pe_config& c = ctx->cfg;
+  hipStream_t st = ctx->stream;
   const int Mo = B * Kout;
-  GemmArgs a = base;
-  a.M = Mo; a.Kd = d; a.N = V;
-  a.A = XG; a.lda = d;
+  GemmArgs a = gemm_base(ctx);
+  a.M = Mo; a.Kd = c.d_model; a.N = c.vocab;
+  a.A = (const uint16_t*)ctx->U; a.lda = c.d_model;
   a.rows_in = K; a.rows_out = Kout;
   a.Wp_raw = ctx->p_lm;
-  a.am_val = ctx->am_val; a.am_idx = ctx->am_idx; a.logits = logits;
+  a.am_val = ctx->am_val; a.am_idx = ctx->am_idx; a.logits = logits; a.ldz = ldz;
   a.nssq = nssq;
-  GemmPlan p = plan_gemm(Mo, V, d, true);
+  GemmPlan p = plan_gemm(Mo, c.vocab, c.d_model, true);
   LAUNCH(prof_mark(ctx, PE_PROF_LM_HEAD, true));
   LAUNCH(launch_gemm(p, a, A_NORM, EPI_ARGMAX, st));
   LAUNCH(prof_mark(ctx, PE_PROF_LM_HEAD, false));
-  LAUNCH(launch_argmax_final(ctx->am_val, ctx->am_idx, Mo, p.ngroups, draft_tokens, st));
+  LAUNCH(launch_argmax_final(ctx->am_val, ctx->am_idx, Mo, p.ngroups, tokens, st));
+  return PE_OK;
+}
+
+#define PE_TRY(expr)                    \
+  do {                                  \
+    const pe_status s_ = (expr);        \
+    if (s_ != PE_OK) return s_;         \
+  } while (0)
+
+static pe_status draft_bf16(pe_ctx* ctx, int32_t B, int32_t K, int32_t Kout, const int32_t* req_slot,
+                            const int32_t* seq_len,
+                            const int32_t* last_token, const void* target_hidden, const float* rows,
+                            int32_t* draft_tokens, float* logits) {
+  int nssq = 0;
+  if (!rows) {
+    PE_TRY(rows_bf16(ctx, B, K, last_token, target_hidden, nssq));
+  } else {
+    hipStream_t st = ctx->stream;
+    const int d = ctx->cfg.d_model;
+    LAUNCH(launch_rows_ssq(rows, ctx->X, ctx->ssq, (uint16_t*)ctx->U, (const uint16_t*)ctx->w.attn_norm[0], B * K, d,
+                           st));
+    nssq = (d + 15) / 16;
+  }
+  PE_TRY(layers_bf16(ctx, B, K, req_slot, seq_len, nssq));
+  return lm_head_bf16(ctx, B, K, Kout, nssq, draft_tokens, logits, ctx->cfg.vocab);
+}
+
+// Autoregressive drafting on the same kernels: pass 0 runs the parallel step's row 0 at position L_b; pass
+// i >= 1 runs the row (residual stream of pass i - 1) + E[token of pass i - 1] at position L_b + i; one more
+// pass (layers only) at L_b + K writes the K/V an all-accepted verify keeps.
+static pe_status draft_ar_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_slot, const int32_t* seq_len,
+                               const int32_t* last_token, const void* target_hidden, int32_t* draft_tokens,
+                               float* logits) {
+  const pe_config& c = ctx->cfg;
+  hipStream_t st = ctx->stream;
+  int nssq = 0;
+  PE_TRY(rows_bf16(ctx, B, 1, last_token, target_hidden, nssq));
+  for (int i = 0;; ++i) {
+    PE_TRY(layers_bf16(ctx, B, 1, req_slot, i == 0 ? seq_len : ctx->ar_seq, nssq));
+    if (i == K) break;
+    PE_TRY(lm_head_bf16(ctx, B, 1, 1, nssq, ctx->ar_tok, logits ? logits + (size_t)i * c.vocab : nullptr,
+                        K * c.vocab));
+    LAUNCH(launch_ar_rows(ctx->X, (uint16_t*)ctx->U, ctx->ssq, (const uint16_t*)ctx->w.embed,
+                          (const uint16_t*)ctx->w.attn_norm[0], ctx->ar_tok, draft_tokens, K, i + 1, seq_len,
+                          ctx->ar_seq, B, c.d_model, c.vocab, ctx->flags, st));
+    nssq = (c.d_model + 15) / 16;
+  }
   return PE_OK;
 }
 
@@ -548,6 +613,21 @@ extern "C" pe_status pe_draft_step(pe_ctx* ctx, int32_t B, int32_t K, const int3
                                    float* logits) {
   if (ctx && (!last_token || !target_hidden)) return fail(ctx, PE_ERR_INVALID, "NULL last_token / target_hidden");
   return run_draft(ctx, B, K, req_slot, seq_len, last_token, target_hidden, nullptr, draft_tokens, logits);
+}
+
+extern "C" pe_status pe_draft_ar(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_slot, const int32_t* seq_len,
+                                 const int32_t* last_token, const void* target_hidden, int32_t* draft_tokens,
+                                 float* logits) {
+  if (!ctx) return fail(nullptr, PE_ERR_INVALID, "ctx is NULL");
+  const pe_config& c = ctx->cfg;
+  if (!ctx->bf16) return fail(ctx, PE_ERR_UNSUPPORTED, "autoregressive drafting needs a bf16 drafter");
+  if (B < 1 || B > c.max_batch) return fail(ctx, PE_ERR_INVALID, "B out of [1, max_batch]");
+  if (K < 1 || K > c.max_k) return fail(ctx, PE_ERR_INVALID, "K out of [1, max_k]");
+  if (!req_slot || !seq_len || !draft_tokens || !last_token || !target_hidden)
+    return fail(ctx, PE_ERR_INVALID, "NULL argument");
+  if ((uintptr_t)target_hidden & 15) return fail(ctx, PE_ERR_INVALID, "target_hidden not 16-byte aligned");
+  if (logits && ((uintptr_t)logits & 15)) return fail(ctx, PE_ERR_INVALID, "logits not 16-byte aligned");
+  return draft_ar_bf16(ctx, B, K, req_slot, seq_len, last_token, target_hidden, draft_tokens, logits);
 }
 
 extern "C" pe_status pe_draft_rows(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_slot, const int32_t* seq_len,

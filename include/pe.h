@@ -18,12 +18,12 @@
  *   - Element type: pe_config.dtype (PE_F32 or PE_BF16) for weights, KV cache, target hiddens and target
  *     logits. Token ids, lengths and slots are int32. Logits written by the library are float32.
  *   - Calls enqueue work on the stream given to pe_init and return without waiting for the GPU.
- *     pe_draft_step, pe_draft_rows and pe_verify allocate nothing.
+ *     pe_draft_step, pe_draft_rows, pe_draft_ar and pe_verify allocate nothing.
  *   - A ctx is used by one host thread at a time. Calls on one ctx run in stream order.
  *   - Errors: every call returns a pe_status. Host-checkable problems (null pointers, sizes out of
  *     range, unsupported shapes) return PE_ERR_INVALID / PE_ERR_UNSUPPORTED before anything is enqueued.
  *     HIP failures return PE_ERR_HIP; pe_last_error gives the message. Device-value preconditions
- *     (token ids < vocab, slots < n_slots, seq_len + K + 1 <= max_ctx for pe_draft_step, seq_len + K <=
+ *     (token ids < vocab, slots < n_slots, seq_len + K + 1 <= max_ctx for pe_draft_step and pe_draft_ar, seq_len + K <=
  *     max_ctx for pe_draft_rows and pe_verify) are the caller's contract; kernels
  *     skip any access that would break them and raise a flag readable through pe_device_flags.
  */
@@ -128,6 +128,20 @@ pe_status pe_draft_step(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_sl
  * Exactly the K given rows run (no trailing placeholder row): K/V at positions seq_len[b]..+K-1. */
 pe_status pe_draft_rows(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_slot, const int32_t* seq_len,
                         const float* rows, int32_t* draft_tokens, float* logits);
+
+/* Autoregressive EAGLE-style drafting on the same kernels: the sequential chain the parallel step
+ * removes (solution overview, "sequential dependency in autoregressive EAGLE": every draft token needs
+ * the previous pass's hidden state and token, so K tokens take K forward passes). bf16 drafters only.
+ * Pass 0 runs one row per request, row 0 of pe_draft_step, at position seq_len[b]. Pass i = 1..K-1 runs
+ * one row per request at position seq_len[b] + i: the drafter's residual stream after its last layer
+ * (before the final norm) in pass i-1 plus embed[draft of pass i-1]; it attends to the context and to the
+ * rows of passes 0..i-1. draft_tokens[b*K + i] = argmax of pass i. One more pass through the layers only
+ * (input: hidden of pass K-1 + embed[draft K-1], position seq_len[b] + K) writes the K/V an all-accepted
+ * verify keeps, so after the call the cache holds the same positions seq_len[b]..+K as after
+ * pe_draft_step. Arguments, layouts and errors as pe_draft_step; a float32 drafter returns
+ * PE_ERR_UNSUPPORTED. Allocates nothing. */
+pe_status pe_draft_ar(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_slot, const int32_t* seq_len,
+                      const int32_t* last_token, const void* target_hidden, int32_t* draft_tokens, float* logits);
 
 /* Greedy verification and batch-metadata rebuild (solution overview, step 2, last sentence; batch
  * metadata as in the pages' fused metadata kernels). With t[b][i] = argmax_v target_logits[b][i][v]
