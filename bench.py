@@ -4,7 +4,7 @@ One step = pe_draft_step (row build, 4 drafter layers, LM head, argmax: K draft 
 requests in one pass) + pe_verify (target argmax over K+1 positions, accepted prefix, bonus token,
 batch-metadata rebuild), over inputs already resident in HBM. Prints one JSON line.
 
-  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload NAME] [--no-cpu-baseline]
+  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload NAME] [--no-cpu-baseline] [--no-depth-sweep]
 
 The default workload is the Qwen3-Coder-30B-A3B-shaped bf16 drafter at B = 1, K = 3, context 2048.
 """
@@ -171,6 +171,8 @@ def main():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-depth-sweep", action="store_true",
+                    help="skip the parallel vs autoregressive latency sweep over K (e.g. under a profiler)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference kernel for HBM counter scaling)")
     args = ap.parse_args()
@@ -259,7 +261,7 @@ def main():
         kern[name] = {"avg_us": 1e3 * tot / max(n, 1), "launches": n}
     pe.pe_profile_enable(ctx, 0)
 
-    depth = latency_vs_depth(pe, torch, w, config_args, dev, kc, vc, d, stream, reps)
+    depth = None if args.no_depth_sweep else latency_vs_depth(pe, torch, w, config_args, dev, kc, vc, d, stream, reps)
 
     if args.copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")

@@ -98,9 +98,10 @@ GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok) {
     p.ngroups = p.Nt;
     return p;
   }
-  // (the stream kernel addresses the packed weights with 32-bit buffer offsets)
-  if (M > 32 && M <= 128 && (long long)p.Nt * Ks * 1024 < 0x7ff00000LL) {
-    // 33..128 rows: the weight-stream kernel (all rows and 128 columns per workgroup, activations staged
+  // (measured: the vocabulary projection is faster in the stream kernel from 9 rows, the layer projections
+  // from 17; the stream kernel addresses the packed weights with 32-bit buffer offsets)
+  if (M > (argmax ? 8 : 16) && M <= 128 && (long long)p.Nt * Ks * 1024 < 0x7ff00000LL) {
+    // up to 128 rows: the weight-stream kernel (all rows and 128 columns per workgroup, activations staged
     // once per chunk). Narrow or short products split the reduction over workgroups until there are about
     // 384 of them, each with at least four chunks, and while the fp32 partials stay within the weight bytes
     // (2 ksplit M N 4 <= N Kd 2); the split reduce kernel then runs the epilogue.

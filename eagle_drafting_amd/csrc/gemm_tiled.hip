@@ -454,7 +454,7 @@ __device__ void tile_epilogue(const GemmArgs& g, const float* Cs, const float* s
   }
 }
 
-// Projections for 33..128 rows: a weight stream with the activations staged once per reduction chunk.
+// Projections for 9..128 rows: a weight stream with the activations staged once per reduction chunk.
 //
 // At these row counts every weight byte is used by at most 128 rows, so the product is bound by the weight
 // stream. A workgroup covers all rows (RB blocks of 32) and 128 columns; wave w owns columns 32 w ..
@@ -662,7 +662,8 @@ static hipError_t launch_gemm_stream(const GemmPlan& p, const GemmArgs& a, int a
   // weights one chunk ahead (measured: two chunks ahead, with a six-step unroll, was no faster for the
   // 88-row vocabulary projection and slower for the four-chunk K-split products)
   hipError_t e;
-  if (a.M <= 64) e = launch_stream_rb<2, GEMM_STREAM_CH, 2>(p, a, a_mode, epi, st);
+  if (a.M <= 32) e = launch_stream_rb<1, GEMM_STREAM_CH, 2>(p, a, a_mode, epi, st);
+  else if (a.M <= 64) e = launch_stream_rb<2, GEMM_STREAM_CH, 2>(p, a, a_mode, epi, st);
   else if (a.M <= 96) e = launch_stream_rb<3, GEMM_STREAM_CH, 2>(p, a, a_mode, epi, st);
   else e = launch_stream_rb<4, GEMM_STREAM_CH, 2>(p, a, a_mode, epi, st);
   if (e != hipSuccess || p.ksplit <= 1) return e;

@@ -27,7 +27,7 @@ inline int n_tiles_ki4(int N) { return (N + 3) / 4; }
 inline int k_steps_ki4(int Kd) { return (Kd + 127) / 128; }
 
 // ---- GEMM y = A . W^T with fused prologue / epilogue ---------------------------------------------
-// k-steps (of 32) per activation chunk of the 33..128-row weight-stream kernel; its K-split plans use
+// k-steps (of 32) per activation chunk of the 9..128-row weight-stream kernel; its K-split plans use
 // multiples of four chunks per split
 constexpr int GEMM_STREAM_CH = 4;
 struct GemmPlan {
@@ -37,7 +37,7 @@ struct GemmPlan {
   int NT;       // 16-column tiles per workgroup
   int NW;       // waves per workgroup (they split the reduction dimension NW/NT ways)
   int ngroups;  // workgroups along N
-  int tiled;    // 2: weight-stream kernel (33..128 rows); 1: LDS-tiled 128 x 128 kernel (larger M); 0: skinny split-K kernel
+  int tiled;    // 2: weight-stream kernel (9..128 rows); 1: LDS-tiled 128 x 128 kernel (larger M); 0: skinny split-K kernel
   int ksplit;   // tiled: workgroups along the reduction dimension (1 = none); > 1 adds a reduce kernel
   int kper;     // tiled: k-steps (32 columns each) per split, a multiple of 4
   int ki4;      // skinny on PACK_KI4 weights: 4-column tiles (Nt counts them), 128-wide k-steps
