@@ -623,14 +623,22 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs g) {
       }
   }
   if (AM == A_NORM) {
-    const int r = tid >> 1, h = tid & 1;
+    // 1 / RMS of each row from the producer's partial sums of squares (up to 512 per row): TPR threads per
+    // row, eight loads in flight per thread, partials combined in a fixed order
+    constexpr int TPR = RB == 1 ? 8 : RB == 2 ? 4 : 2;
+    const int r = tid / TPR, h = tid % TPR;
     float t = 0.f;
     if (r < M) {
       const float* src = g.ssq_in + (size_t)gemm_a_row(g, r) * g.nssq;
-      for (int i = h; i < g.nssq; i += 2) t += src[i];
+      for (int i0 = h; i0 < g.nssq; i0 += 8 * TPR) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = i0 + u * TPR < g.nssq ? src[i0 + u * TPR] : 0.f;
+        t += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+      }
     }
-    t += __shfl_xor(t, 1, PE_WAVE);
-    if (h == 0) s_inv[r] = rsqrtf(t / (float)g.Kd + g.eps);
+    for (int off = TPR / 2; off > 0; off >>= 1) t += __shfl_xor(t, off, PE_WAVE);
+    if (h == 0 && r < 32 * RB) s_inv[r] = rsqrtf(t / (float)g.Kd + g.eps);
   }
   __syncthreads();
   if (SPLIT) tile_epilogue<EPI_PARTIAL, AM == A_NORM>(g, Cs, s_inv, 0, nt0, ng, 0, 32 * RB);
