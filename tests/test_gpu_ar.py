@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 from oracle import pe_oracle as O
-from synth import WORKLOADS
+from synth import QWEN3_CODER, WORKLOADS, Workload
 from synth.inputs import kv_block, to_f64
 from tests.gpu_util import TOL, GpuDrafter, check_logits, check_rows, check_tokens, log, shape_weights64
 
@@ -42,16 +42,23 @@ def _oracle_ar(w, W64, state, K, req, feed):
     return O.draft_autoregressive(w.shape, W64, st, ctx, K, tail=True, feed=feed)
 
 
-@pytest.mark.parametrize("name", ["qwen3coder-bf16-B1-K3-L2048", "qwen3coder-bf16-B4-K3-L1024to4096"])
+_SMALL = {"B9-K2": Workload("qwen3coder-bf16-B9-K2-ar", QWEN3_CODER, 9, 2, (60, 400), 0.7, 7700),
+          "B17-K2": Workload("qwen3coder-bf16-B17-K2-ar", QWEN3_CODER, 17, 2, (60, 400), 0.7, 7701)}
+
+
+@pytest.mark.parametrize("name", ["qwen3coder-bf16-B1-K3-L2048", "qwen3coder-bf16-B4-K3-L1024to4096", "B9-K2",
+                                  "B17-K2"])
 def test_autoregressive_parity(name):
-    w = WORKLOADS[name]
+    """One-row passes of 1 and 4 requests (small-batch kernels), 9 (the LM head on the weight-stream
+    kernel) and 17 (every projection on it); the larger batches on sampled requests."""
+    w = _SMALL.get(name) or WORKLOADS[name]
     log(f"autoregressive draft parity {name}")
     tol = TOL[w.shape.dtype]
     g = GpuDrafter(w)
     try:
         K = w.K
         draft, z = _gpu_ar(g, K)
-        req = list(range(w.B))
+        req = list(range(w.B)) if w.B <= 4 else [0, w.B // 2, w.B - 1]
         ref = _oracle_ar(w, shape_weights64(w.shape), g.state, K, req, feed=draft[req])
         strict = exempt = 0
         for i in range(K):
@@ -64,7 +71,7 @@ def test_autoregressive_parity(name):
                 k, v = g.kv_rows(l, b, K + 1)
                 kv_err = max(kv_err, check_rows(k, ref["k_new"][l][i], tol, f"{name} K rows l{l} b{b}"),
                              check_rows(v, ref["v_new"][l][i], tol, f"{name} V rows l{l} b{b}"))
-        log(f"  {name}: tokens strict {strict}/{len(req) * K}, exempt {exempt}, kv err {kv_err:.2e}")
+        log(f"  {w.name}: tokens strict {strict}/{len(req) * K}, exempt {exempt}, kv err {kv_err:.2e}")
     finally:
         g.close()
 
