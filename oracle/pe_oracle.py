@@ -373,6 +373,62 @@ def verify(target_logits: np.ndarray, draft: np.ndarray) -> dict:
     return {"t": t, "n": n, "accept_len": accept_len.astype(np.int32), "bonus": bonus.astype(np.int32)}
 
 
+# --------------------------------------------------------------------------------------------------
+# The same acceptance rule in its sampling form (temperature > 0; the pages' example request uses 0.3):
+# standard speculative sampling. A draft x drawn from q is accepted with probability min(1, p(x) / q(x));
+# on a rejection the emitted token is drawn from the normalised residual max(0, p - q); after K
+# acceptances the bonus token is drawn from p at position K. Reading: the parallel drafter drafts
+# greedily, so q is a point mass at the draft token; then a draft x is accepted with probability p(x) and
+# a rejection draws from p with x removed. The uniforms are inputs (u for the acceptance tests, v for the
+# draws), so the rule is deterministic given them.
+
+
+def softmax_temperature(z: np.ndarray, temperature: float) -> np.ndarray:
+    """p = softmax(z / temperature) along the last axis, float64."""
+    x = np.asarray(z, dtype=np.float64) / temperature
+    x = x - x.max(axis=-1, keepdims=True)
+    e = np.exp(x)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def draw_inverse_cdf(w: np.ndarray, v: float) -> int:
+    """The smallest x with w[0] + ... + w[x] > v * sum(w), for weights w >= 0 and v in [0, 1)."""
+    c = np.cumsum(np.asarray(w, dtype=np.float64))
+    return int(np.searchsorted(c, v * c[-1], side="right"))
+
+
+def verify_sampled(target_logits: np.ndarray, draft: np.ndarray, temperature: float, u: np.ndarray,
+                   v: np.ndarray) -> dict:
+    """target_logits [B, K+1, V], draft [B, K], uniforms u [B, K] and v [B, K+1] in [0, 1).
+
+    Position i accepts draft[b, i] iff u[b, i] < p_i(draft[b, i]), p_i = softmax(T[b, i] / temperature).
+    At the first rejection n, the emitted token is drawn with v[b, n] from p_n without draft[b, n];
+    after K acceptances the bonus token is drawn with v[b, K] from p_K. Returns the same fields as verify:
+    t [B, K+1] (emitted tokens at positions 0..n, -1 after), n, accept_len = n + 1, bonus."""
+    B, K = draft.shape
+    t = np.full((B, K + 1), -1, dtype=np.int64)
+    n = np.empty(B, dtype=np.int32)
+    for b in range(B):
+        i = 0
+        while True:
+            p = softmax_temperature(target_logits[b, i], temperature)
+            if i == K:
+                t[b, i] = draw_inverse_cdf(p, v[b, i])
+                break
+            x = int(draft[b, i])
+            if u[b, i] < p[x]:
+                t[b, i] = x
+                i += 1
+                continue
+            r = p.copy()
+            r[x] = 0.0
+            t[b, i] = draw_inverse_cdf(r, v[b, i])
+            break
+        n[b] = i
+    bonus = t[np.arange(B), n]
+    return {"t": t, "n": n, "accept_len": (n + 1).astype(np.int32), "bonus": bonus.astype(np.int32)}
+
+
 def compact(v: dict, req_slot: np.ndarray, seq_len: np.ndarray, finished=None) -> dict:
     """Batch-metadata rebuild after verify ([JP] implementation and performance: the metadata the
     serving loop needs for the next step).

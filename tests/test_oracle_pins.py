@@ -461,3 +461,66 @@ def test_autoregressive_tail_and_feed():
     f = _ar(MINI, W, tok, hid, [6], ctx, 3, feed=other)
     assert np.array_equal(f["logits"][:, 0], a["logits"][:, 0])
     assert not np.allclose(f["logits"][:, 1], a["logits"][:, 1])
+
+
+# ---------------------------------------------------------------- sampled verify (temperature > 0)
+
+def test_draw_inverse_cdf_brute_force():
+    w = np.array([0.0, 1.0, 0.0, 2.0, 1.0, 0.0])
+    for v in np.linspace(0.0, 0.999, 37):
+        # brute force: walk the bins of total 4 and stop at the first whose right edge passes v * 4
+        acc, want = 0.0, None
+        for x, wx in enumerate(w):
+            acc += wx
+            if acc > v * 4.0:
+                want = x
+                break
+        assert O.draw_inverse_cdf(w, v) == want
+
+
+def test_sampled_verify_emits_the_target_distribution():
+    # speculative sampling's defining property: whatever the (greedy) draft, the token emitted at the first
+    # position is distributed as p_0 = softmax(T_0 / temperature), and after an acceptance the next one as
+    # p_1; the acceptance rate of draft x is p_0(x). Checked by Monte Carlo against scipy's softmax.
+    from scipy.special import softmax
+    rng = np.random.default_rng(41)
+    V, K, tau = 6, 2, 0.7
+    T = rng.standard_normal((1, K + 1, V)) * 1.5
+    draft = np.array([[int(np.argsort(T[0, 0])[-2]), int(np.argmax(T[0, 1]))]])  # not the argmax at position 0
+    N = 40000
+    p0 = softmax(T[0, 0] / tau)
+    p1 = softmax(T[0, 1] / tau)
+    first, second, acc0 = np.zeros(V), np.zeros(V), 0
+    for _ in range(N):
+        u = rng.random((1, K))
+        v = rng.random((1, K + 1))
+        out = O.verify_sampled(T, draft, tau, u, v)
+        first[out["t"][0, 0]] += 1
+        if out["n"][0] >= 1:
+            acc0 += 1
+            second[out["t"][0, 1]] += 1
+    sig = np.sqrt(p0 * (1 - p0) / N)
+    assert np.all(np.abs(first / N - p0) < 5 * sig + 1e-12)
+    assert abs(acc0 / N - p0[draft[0, 0]]) < 5 * math.sqrt(p0[draft[0, 0]] * (1 - p0[draft[0, 0]]) / N)
+    n1 = second.sum()
+    sig1 = np.sqrt(p1 * (1 - p1) / n1)
+    assert np.all(np.abs(second / n1 - p1) < 5 * sig1 + 1e-12)
+
+
+def test_sampled_verify_near_zero_temperature_is_greedy():
+    # with logit gaps far above the temperature, p is one-hot at the argmax: the sampled rule reduces to
+    # the greedy one (accept while the draft equals the argmax, bonus = argmax at the first mismatch)
+    rng = np.random.default_rng(42)
+    B, K, V = 64, 4, 16
+    T = np.stack([rng.permutation(V) for _ in range(B * (K + 1))]).reshape(B, K + 1, V).astype(np.float64)
+    T = T + rng.standard_normal(T.shape) * 0.01
+    t_greedy = O.argmax_first(T)
+    draft = np.where(rng.random((B, K)) < 0.7, t_greedy[:, :K], (t_greedy[:, :K] + 1) % V)
+    u = rng.uniform(0.01, 0.99, (B, K))
+    v = rng.uniform(0.01, 0.99, (B, K + 1))
+    s = O.verify_sampled(T, draft, 1e-3, u, v)
+    g = O.verify(T, draft)
+    assert np.array_equal(s["accept_len"], g["accept_len"])
+    assert np.array_equal(s["bonus"], g["bonus"])
+    for b in range(B):
+        assert np.array_equal(s["t"][b, :g["accept_len"][b]], g["t"][b, :g["accept_len"][b]])
