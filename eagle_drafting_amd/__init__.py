@@ -6,6 +6,7 @@ arguments to it. PyTorch is only used by callers for device memory and streams.
 
 from .binding import (  # noqa: F401
     PE_BF16,
+    PE_ERR_INVALID,
     PE_ERR_UNSUPPORTED,
     PE_F32,
     PE_PROF_ATTENTION,
@@ -31,5 +32,6 @@ from .binding import (  # noqa: F401
     pe_profile_read,
     pe_status_string,
     pe_verify,
+    pe_verify_sampled,
     pe_weights,
 )

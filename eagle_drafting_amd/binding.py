@@ -22,7 +22,8 @@ PE_PROF_LM_HEAD, PE_PROF_ATTENTION, PE_PROF_GATE_UP, PE_PROF_VERIFY_SCAN = 0, 1,
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpe.so")
 
-EXPORTED = ["pe_config_validate", "pe_init", "pe_draft_step", "pe_draft_rows", "pe_draft_ar", "pe_verify", "pe_destroy",
+EXPORTED = ["pe_config_validate", "pe_init", "pe_draft_step", "pe_draft_rows", "pe_draft_ar", "pe_verify", "pe_verify_sampled",
+            "pe_destroy",
             "pe_device_flags", "pe_profile_enable", "pe_profile_read", "pe_status_string", "pe_last_error"]
 
 
@@ -84,6 +85,8 @@ def load_library(path: str = LIB_PATH):
         "pe_draft_rows": ([vp, i32, i32, vp, vp, vp, vp, vp], i32),
         "pe_draft_ar": ([vp, i32, i32, vp, vp, vp, vp, vp, vp], i32),
         "pe_verify": ([vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp], i32),
+        "pe_verify_sampled": ([vp, i32, i32, vp, vp, c_float, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+                              i32),
         "pe_destroy": ([vp], i32),
         "pe_device_flags": ([vp, i32, POINTER(i32)], i32),
         "pe_profile_enable": ([vp, i32], i32),
@@ -155,6 +158,15 @@ def pe_verify(ctx, B, K, target_logits, draft_tokens, finished, req_slot, seq_le
                                     _ptr(req_slot), _ptr(seq_len), _ptr(accept_len), _ptr(cu_accept),
                                     _ptr(out_tokens), _ptr(keep_index), _ptr(n_keep), _ptr(req_slot_next),
                                     _ptr(seq_len_next), _ptr(last_token_next)), ctx)
+
+
+def pe_verify_sampled(ctx, B, K, target_logits, draft_tokens, temperature, u, v, finished, req_slot, seq_len,
+                      accept_len, cu_accept, out_tokens, keep_index, n_keep, req_slot_next, seq_len_next,
+                      last_token_next):
+    _check(load_library().pe_verify_sampled(
+        ctx, B, K, _ptr(target_logits), _ptr(draft_tokens), float(temperature), _ptr(u), _ptr(v), _ptr(finished),
+        _ptr(req_slot), _ptr(seq_len), _ptr(accept_len), _ptr(cu_accept), _ptr(out_tokens), _ptr(keep_index),
+        _ptr(n_keep), _ptr(req_slot_next), _ptr(seq_len_next), _ptr(last_token_next)), ctx)
 
 
 def pe_destroy(ctx):

@@ -157,6 +157,35 @@ __device__ __forceinline__ int block_scan_incl(int v, int* buf) {
   return v + add;
 }
 
+// Batch-metadata rebuild after the acceptance decision (thread b < B holds request b's accept_len al, the
+// emitted token after its accepted drafts, and keep = not finished): cu_accept = exclusive scan of al,
+// out_tokens[cu_accept[b] + i] = t[b][i] for i < al, stable compaction of the surviving requests.
+__device__ __forceinline__ void compact_tail(int al, int bonus, int keep, int* buf, int B, int K,
+                                             const int* __restrict__ t_ws, const int* __restrict__ req_slot,
+                                             const int* __restrict__ seq_len, int* __restrict__ cu_accept,
+                                             int* __restrict__ out_tokens, int* __restrict__ keep_index,
+                                             int* __restrict__ n_keep, int* __restrict__ slot_next,
+                                             int* __restrict__ seq_next, int* __restrict__ last_next) {
+  const int tid = threadIdx.x;
+  const int incl = block_scan_incl(al, buf);
+  const int excl = incl - al;
+  if (tid < B) {
+    cu_accept[tid] = excl;
+    if (tid == B - 1) cu_accept[B] = incl;
+    const int* t = t_ws + (size_t)tid * (K + 1);
+    for (int i = 0; i < al; ++i) out_tokens[excl + i] = t[i];
+  }
+  const int kincl = block_scan_incl(keep, buf);
+  if (tid < B && keep) {
+    const int pos = kincl - 1;
+    keep_index[pos] = tid;
+    slot_next[pos] = req_slot[tid];
+    seq_next[pos] = seq_len[tid] + al;
+    last_next[pos] = bonus;
+  }
+  if (tid == B - 1) n_keep[0] = kincl;
+}
+
 // Greedy acceptance (the target verifies the K drafts in one pass; standard rule, greedy form) and the
 // batch-metadata rebuild. One workgroup of 1024 threads; thread b handles request b (B <= 1024).
 __global__ __launch_bounds__(1024) void accept_compact_kernel(
@@ -199,23 +228,8 @@ __global__ __launch_bounds__(1024) void accept_compact_kernel(
     accept_len[tid] = al;
     keep = finished ? (finished[tid] == 0 ? 1 : 0) : 1;
   }
-  const int incl = block_scan_incl(al, buf);
-  const int excl = incl - al;
-  if (tid < B) {
-    cu_accept[tid] = excl;
-    if (tid == B - 1) cu_accept[B] = incl;
-    const int* t = t_ws + (size_t)tid * (K + 1);
-    for (int i = 0; i < al; ++i) out_tokens[excl + i] = t[i];
-  }
-  const int kincl = block_scan_incl(keep, buf);
-  if (tid < B && keep) {
-    const int pos = kincl - 1;
-    keep_index[pos] = tid;
-    slot_next[pos] = req_slot[tid];
-    seq_next[pos] = seq_len[tid] + al;
-    last_next[pos] = bonus;
-  }
-  if (tid == B - 1) n_keep[0] = kincl;
+  compact_tail(al, bonus, keep, buf, B, K, t_ws, req_slot, seq_len, cu_accept, out_tokens, keep_index, n_keep,
+               slot_next, seq_next, last_next);
 }
 
 hipError_t launch_accept_compact(const float* pv, const int* pi, int nchunks, int B, int K, const int* draft,
@@ -225,6 +239,237 @@ hipError_t launch_accept_compact(const float* pv, const int* pi, int nchunks, in
   hipLaunchKernelGGL(accept_compact_kernel, dim3(1), dim3(1024), 0, st, pv, pi, nchunks, B, K, draft, finished,
                      req_slot, seq_len, t_ws, accept_len, cu_accept, out_tokens, keep_index, n_keep, slot_next,
                      seq_next, last_next);
+  return hipGetLastError();
+}
+
+// ---- sampled verification (temperature > 0): standard speculative sampling with a greedy drafter ------
+// p_i = softmax(T[b][i] / temperature). Draft x_i is accepted iff u[b][i] < p_i(x_i); at the first rejection
+// n the emitted token is drawn with v[b][n] from p_n without x_n (inverse CDF over the vocabulary); after K
+// acceptances the bonus token is drawn with v[b][K] from p_K.
+
+__device__ __forceinline__ void sm_merge(float& m, float& s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;
+  s = s * __expf(m - M) + s2 * __expf(m2 - M);
+  m = M;
+}
+
+// (max, sum of exp(x - max)) of x = logit / temperature over one chunk of one row; fixed merge order
+template <typename T>
+__global__ __launch_bounds__(256) void softmax_stats_kernel(const T* __restrict__ X, int V, int chunk, int nchunks,
+                                                            float inv_temp, float* __restrict__ pm,
+                                                            float* __restrict__ ps) {
+  constexpr int VEC = 16 / sizeof(T);
+  __shared__ float sm[4], ss[4];
+  const int row = blockIdx.x, c = blockIdx.y;
+  const int begin = c * chunk;
+  const int end = min(V, begin + chunk);
+  const T* x = X + (size_t)row * V;
+  float m = -INFINITY, s = 0.f;
+  auto add = [&](float v) {
+    v *= inv_temp;
+    if (v > m) {
+      s = s * __expf(m - v) + 1.f;
+      m = v;
+    } else {
+      s += __expf(v - m);
+    }
+  };
+  for (int i = begin + threadIdx.x * VEC; i < end; i += 256 * VEC) {
+    if (i + VEC <= end) {
+      union { uint4 u; T e[VEC]; } ld;
+      ld.u = *(const uint4*)(x + i);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) add(to_f32<T>(ld.e[e]));
+    } else {
+      for (int e = i; e < end; ++e) add(to_f32<T>(x[e]));
+    }
+  }
+  for (int off = 1; off < 64; off <<= 1) {
+    const float m2 = __shfl_xor(m, off, PE_WAVE), s2 = __shfl_xor(s, off, PE_WAVE);
+    sm_merge(m, s, m2, s2);
+  }
+  if ((threadIdx.x & 63) == 0) { sm[threadIdx.x >> 6] = m; ss[threadIdx.x >> 6] = s; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float M = sm[0], S = ss[0];
+    for (int w = 1; w < 4; ++w) sm_merge(M, S, sm[w], ss[w]);
+    pm[(size_t)row * nchunks + c] = M;
+    ps[(size_t)row * nchunks + c] = S;
+  }
+}
+
+// One workgroup per request: the positions in order until the first rejection. Chunk statistics go through
+// LDS; the row maximum and total are combined in chunk order by one thread; the draw finds its chunk by a
+// prefix over the chunk totals and its token by a block scan inside the chunk.
+template <typename T>
+__global__ __launch_bounds__(256) void sample_decide_kernel(const T* __restrict__ X, int V, int chunk, int nchunks,
+                                                            float inv_temp, const float* __restrict__ pm,
+                                                            const float* __restrict__ ps, int K,
+                                                            const int* __restrict__ draft, const float* __restrict__ u,
+                                                            const float* __restrict__ v, int* __restrict__ t_ws,
+                                                            int* __restrict__ accept_len) {
+  __shared__ float cm[PE_SAMPLE_MAX_CHUNKS], cs[PE_SAMPLE_MAX_CHUNKS];
+  __shared__ float red[256];
+  __shared__ float sh_M, sh_S, sh_base;
+  __shared__ int sh_k, sh_x;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  int n = K;
+  for (int i = 0; i <= K; ++i) {
+    const int r = b * (K + 1) + i;
+    for (int c = tid; c < nchunks; c += 256) {
+      cm[c] = pm[(size_t)r * nchunks + c];
+      cs[c] = ps[(size_t)r * nchunks + c];
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float M = -INFINITY, S = 0.f;
+      for (int c = 0; c < nchunks; ++c) sm_merge(M, S, cm[c], cs[c]);
+      sh_M = M;
+      sh_S = S;
+    }
+    __syncthreads();
+    const float M = sh_M, S = sh_S;
+    const T* x = X + (size_t)r * V;
+    int excl = -1;
+    float ed = 0.f, theta;
+    if (i < K) {
+      const int d = draft[(size_t)b * K + i];
+      const bool d_ok = d >= 0 && d < V;
+      ed = d_ok ? __expf(to_f32<T>(x[d]) * inv_temp - M) : 0.f;
+      if (tid == 0) sh_k = d_ok && u[(size_t)b * K + i] < ed / S ? 1 : 0;  // one thread decides for all
+      __syncthreads();
+      if (sh_k) {  // accepted
+        if (tid == 0) t_ws[r] = d;
+        __syncthreads();  // cm / cs / sh_k are rewritten for the next position
+        continue;
+      }
+      excl = d_ok ? d : -1;
+      theta = v[(size_t)b * (K + 1) + i] * (S - ed);
+    } else {
+      theta = v[(size_t)b * (K + 1) + i] * S;
+    }
+    __syncthreads();  // sh_k is rewritten below
+    // the chunk holding the draw: first chunk whose running total (without the excluded token) passes theta
+    if (tid == 0) {
+      float acc = 0.f;
+      int k = -1, last = 0;
+      for (int c = 0; c < nchunks; ++c) {
+        float w = cs[c] * __expf(cm[c] - M);
+        if (excl >= c * chunk && excl < (c + 1) * chunk) w = fmaxf(w - ed, 0.f);
+        if (w > 0.f) last = c;
+        if (k < 0 && acc + w > theta) { k = c; sh_base = acc; }
+        acc += w;
+      }
+      if (k < 0) {  // rounding left theta at or past the total: the last chunk with weight
+        k = last;
+        float a2 = 0.f;
+        for (int c = 0; c < last; ++c) {
+          float w = cs[c] * __expf(cm[c] - M);
+          if (excl >= c * chunk && excl < (c + 1) * chunk) w = fmaxf(w - ed, 0.f);
+          a2 += w;
+        }
+        sh_base = a2;
+      }
+      sh_k = k;
+      sh_x = -1;
+    }
+    __syncthreads();
+    const int k = sh_k;
+    const int cb = k * chunk, ce = min(V, cb + chunk);
+    const int per = (ce - cb + 255) / 256;
+    const int lb = cb + tid * per, le = min(ce, lb + per);
+    auto wt = [&](int e) { return e == excl ? 0.f : __expf(to_f32<T>(x[e]) * inv_temp - M); };
+    float local = 0.f;
+    for (int e = lb; e < le; ++e) local += wt(e);
+    // inclusive block scan of the per-thread totals (thread order); thread j owns [lo_j, hi_j) with
+    // lo_j = base + scan[j - 1] and hi_j = base + scan[j] = lo_{j+1}, the last thread also everything past
+    // the chunk's total, so exactly one thread owns theta (theta >= base)
+    red[tid] = local;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const float add = tid >= off ? red[tid - off] : 0.f;
+      __syncthreads();
+      red[tid] += add;
+      __syncthreads();
+    }
+    const float base = sh_base;
+    const float lo = base + (tid == 0 ? 0.f : red[tid - 1]);
+    const float hi = tid == 255 ? INFINITY : base + red[tid];
+    if (lo <= theta && theta < hi) {
+      float a = lo;
+      int pick = -1;
+      for (int e = lb; e < le; ++e) {
+        const float w = wt(e);
+        if (w > 0.f) {
+          pick = e;
+          a += w;
+          if (a > theta) break;
+        }
+      }
+      sh_x = pick;  // rounding may end the range before theta: then its last token with weight
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int xs = sh_x;
+      if (xs < 0) {  // the owner holds no weight: the last token of the chunk with weight
+        xs = cb;
+        for (int e = ce - 1; e >= cb; --e)
+          if (wt(e) > 0.f) { xs = e; break; }
+      }
+      t_ws[r] = xs;
+    }
+    n = i;
+    break;
+  }
+  if (tid == 0) accept_len[b] = n + 1;
+}
+
+// metadata rebuild for the sampled path: one workgroup of 1024 threads, thread b < B handles request b
+__global__ __launch_bounds__(1024) void sampled_compact_kernel(int B, int K, const int* __restrict__ t_ws,
+                                                               const int* __restrict__ accept_len_in,
+                                                               const uint8_t* __restrict__ finished,
+                                                               const int* __restrict__ req_slot,
+                                                               const int* __restrict__ seq_len,
+                                                               int* __restrict__ cu_accept, int* __restrict__ out_tokens,
+                                                               int* __restrict__ keep_index, int* __restrict__ n_keep,
+                                                               int* __restrict__ slot_next, int* __restrict__ seq_next,
+                                                               int* __restrict__ last_next) {
+  __shared__ int buf[16];
+  const int tid = threadIdx.x;
+  int al = 0, bonus = 0, keep = 0;
+  if (tid < B) {
+    al = accept_len_in[tid];
+    bonus = t_ws[(size_t)tid * (K + 1) + al - 1];
+    keep = finished ? (finished[tid] == 0 ? 1 : 0) : 1;
+  }
+  compact_tail(al, bonus, keep, buf, B, K, t_ws, req_slot, seq_len, cu_accept, out_tokens, keep_index, n_keep,
+               slot_next, seq_next, last_next);
+}
+
+hipError_t launch_sampled_verify(int dtype, const void* X, int B, int K, int V, int nchunks, float temperature,
+                                 const int* draft, const float* u, const float* v, const uint8_t* finished,
+                                 const int* req_slot, const int* seq_len, float* pm, float* ps, int* t_ws,
+                                 int* accept_len, int* cu_accept, int* out_tokens, int* keep_index, int* n_keep,
+                                 int* slot_next, int* seq_next, int* last_next, hipStream_t st) {
+  if (nchunks < 1 || nchunks > PE_SAMPLE_MAX_CHUNKS || B < 1 || B > 1024) return hipErrorInvalidValue;
+  int chunk = (V + nchunks - 1) / nchunks;
+  chunk = (chunk + 7) / 8 * 8;  // every chunk start 16-byte aligned (V % 8 == 0)
+  const int rows = B * (K + 1);
+  const float inv_temp = 1.f / temperature;
+  if (dtype == 0) {
+    hipLaunchKernelGGL(softmax_stats_kernel<float>, dim3(rows, nchunks), dim3(256), 0, st, (const float*)X, V, chunk,
+                       nchunks, inv_temp, pm, ps);
+    hipLaunchKernelGGL(sample_decide_kernel<float>, dim3(B), dim3(256), 0, st, (const float*)X, V, chunk, nchunks,
+                       inv_temp, pm, ps, K, draft, u, v, t_ws, accept_len);
+  } else {
+    hipLaunchKernelGGL(softmax_stats_kernel<bf16_t>, dim3(rows, nchunks), dim3(256), 0, st, (const bf16_t*)X, V,
+                       chunk, nchunks, inv_temp, pm, ps);
+    hipLaunchKernelGGL(sample_decide_kernel<bf16_t>, dim3(B), dim3(256), 0, st, (const bf16_t*)X, V, chunk, nchunks,
+                       inv_temp, pm, ps, K, draft, u, v, t_ws, accept_len);
+  }
+  hipLaunchKernelGGL(sampled_compact_kernel, dim3(1), dim3(1024), 0, st, B, K, t_ws, accept_len, finished, req_slot,
+                     seq_len, cu_accept, out_tokens, keep_index, n_keep, slot_next, seq_next, last_next);
   return hipGetLastError();
 }
 

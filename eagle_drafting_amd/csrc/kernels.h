@@ -139,6 +139,14 @@ int plan_argmax_chunks(int rows, int V);
 hipError_t launch_argmax_rows(int dtype, const void* X, int rows, int V, int nchunks, float* pv, int* pi,
                               hipStream_t st);
 hipError_t launch_argmax_final(const float* pv, const int* pi, int rows, int nchunks, int* out, hipStream_t st);
+// sampled verification (temperature > 0): chunk softmax statistics, per-request decisions and draws, then the
+// metadata rebuild; pm / ps hold rows x nchunks floats each (nchunks <= PE_SAMPLE_MAX_CHUNKS)
+constexpr int PE_SAMPLE_MAX_CHUNKS = 1024;
+hipError_t launch_sampled_verify(int dtype, const void* X, int B, int K, int V, int nchunks, float temperature,
+                                 const int* draft, const float* u, const float* v, const uint8_t* finished,
+                                 const int* req_slot, const int* seq_len, float* pm, float* ps, int* t_ws,
+                                 int* accept_len, int* cu_accept, int* out_tokens, int* keep_index, int* n_keep,
+                                 int* slot_next, int* seq_next, int* last_next, hipStream_t st);
 hipError_t launch_accept_compact(const float* pv, const int* pi, int nchunks, int B, int K, const int* draft,
                                  const uint8_t* finished, const int* req_slot, const int* seq_len, int* t_ws,
                                  int* accept_len, int* cu_accept, int* out_tokens, int* keep_index, int* n_keep,

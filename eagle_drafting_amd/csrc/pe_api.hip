@@ -636,6 +636,32 @@ extern "C" pe_status pe_draft_rows(pe_ctx* ctx, int32_t B, int32_t K, const int3
   return run_draft(ctx, B, K, req_slot, seq_len, nullptr, nullptr, rows, draft_tokens, logits);
 }
 
+extern "C" pe_status pe_verify_sampled(pe_ctx* ctx, int32_t B, int32_t K, const void* target_logits,
+                                       const int32_t* draft_tokens, float temperature, const float* u,
+                                       const float* v, const uint8_t* finished, const int32_t* req_slot,
+                                       const int32_t* seq_len, int32_t* accept_len, int32_t* cu_accept,
+                                       int32_t* out_tokens, int32_t* keep_index, int32_t* n_keep,
+                                       int32_t* req_slot_next, int32_t* seq_len_next, int32_t* last_token_next) {
+  if (!ctx) return fail(nullptr, PE_ERR_INVALID, "ctx is NULL");
+  const pe_config& c = ctx->cfg;
+  if (B < 1 || B > c.max_batch) return fail(ctx, PE_ERR_INVALID, "B out of [1, max_batch]");
+  if (K < 1 || K > c.max_k) return fail(ctx, PE_ERR_INVALID, "K out of [1, max_k]");
+  if (!(temperature > 0.f) || temperature > 3.0e38f) return fail(ctx, PE_ERR_INVALID, "temperature must be > 0 and finite");
+  if (!target_logits || !draft_tokens || !u || !v || !req_slot || !seq_len || !accept_len || !cu_accept ||
+      !out_tokens || !keep_index || !n_keep || !req_slot_next || !seq_len_next || !last_token_next)
+    return fail(ctx, PE_ERR_INVALID, "NULL argument");
+  if ((uintptr_t)target_logits & 15) return fail(ctx, PE_ERR_INVALID, "target_logits not 16-byte aligned");
+  if (c.vocab % 8) return fail(ctx, PE_ERR_UNSUPPORTED, "sampled verify needs vocab % 8 == 0");
+  hipStream_t st = ctx->stream;
+  const int rows = B * (K + 1);
+  const int nch = plan_argmax_chunks(rows, c.vocab);
+  LAUNCH(launch_sampled_verify(ctx->bf16 ? 1 : 0, target_logits, B, K, c.vocab, nch, temperature, draft_tokens, u, v,
+                               finished, req_slot, seq_len, ctx->am_val, (float*)ctx->am_idx, ctx->t_ws, accept_len,
+                               cu_accept, out_tokens, keep_index, n_keep, req_slot_next, seq_len_next,
+                               last_token_next, st));
+  return PE_OK;
+}
+
 extern "C" pe_status pe_verify(pe_ctx* ctx, int32_t B, int32_t K, const void* target_logits,
                                const int32_t* draft_tokens, const uint8_t* finished, const int32_t* req_slot,
                                const int32_t* seq_len, int32_t* accept_len, int32_t* cu_accept, int32_t* out_tokens,

@@ -18,7 +18,7 @@
  *   - Element type: pe_config.dtype (PE_F32 or PE_BF16) for weights, KV cache, target hiddens and target
  *     logits. Token ids, lengths and slots are int32. Logits written by the library are float32.
  *   - Calls enqueue work on the stream given to pe_init and return without waiting for the GPU.
- *     pe_draft_step, pe_draft_rows, pe_draft_ar and pe_verify allocate nothing.
+ *     pe_draft_step, pe_draft_rows, pe_draft_ar, pe_verify and pe_verify_sampled allocate nothing.
  *   - A ctx is used by one host thread at a time. Calls on one ctx run in stream order.
  *   - Errors: every call returns a pe_status. Host-checkable problems (null pointers, sizes out of
  *     range, unsupported shapes) return PE_ERR_INVALID / PE_ERR_UNSUPPORTED before anything is enqueued.
@@ -162,6 +162,26 @@ pe_status pe_verify(pe_ctx* ctx, int32_t B, int32_t K, const void* target_logits
                     const uint8_t* finished, const int32_t* req_slot, const int32_t* seq_len,
                     int32_t* accept_len, int32_t* cu_accept, int32_t* out_tokens, int32_t* keep_index,
                     int32_t* n_keep, int32_t* req_slot_next, int32_t* seq_len_next, int32_t* last_token_next);
+
+/* Verification in its sampling form (temperature > 0; same section, the standard acceptance rule as
+ * speculative sampling applies it). Reading: the parallel drafter drafts greedily, so its proposal is a
+ * point mass at each draft token; the rule "accept x with probability min(1, p(x)/q(x)), else draw from
+ * the normalised max(0, p - q)" then becomes, with p_i = softmax(target_logits[b][i] / temperature):
+ *   draft_tokens[b][i] is accepted iff u[b][i] < p_i(draft_tokens[b][i]), for i = 0, 1, ... in order;
+ *   at the first rejection n the emitted token is drawn with v[b][n] from p_n without the draft token;
+ *   after K acceptances the bonus token is drawn with v[b][K] from p_K;
+ *   a draw with uniform w from weights q returns the smallest x with q_0 + ... + q_x > w (q_0 + ... + q_V-1).
+ * Every emitted token is then distributed as the target's p_i. Outputs exactly as pe_verify (the emitted
+ * token after the accepted drafts takes the bonus token's place). u: device float32 [B, K], v: device
+ * float32 [B, K+1], uniforms in [0, 1) drawn by the caller. Decisions and draws are computed in float32,
+ * so a uniform within float32 rounding of a decision boundary may go either way. vocab must be a
+ * multiple of 8. Allocates nothing. */
+pe_status pe_verify_sampled(pe_ctx* ctx, int32_t B, int32_t K, const void* target_logits,
+                            const int32_t* draft_tokens, float temperature, const float* u, const float* v,
+                            const uint8_t* finished, const int32_t* req_slot, const int32_t* seq_len,
+                            int32_t* accept_len, int32_t* cu_accept, int32_t* out_tokens, int32_t* keep_index,
+                            int32_t* n_keep, int32_t* req_slot_next, int32_t* seq_len_next,
+                            int32_t* last_token_next);
 
 /* Waits for the ctx's stream, then frees everything pe_init allocated. NULL is allowed. */
 pe_status pe_destroy(pe_ctx* ctx);
