@@ -261,6 +261,24 @@ def main():
         kern[name] = {"avg_us": 1e3 * tot / max(n, 1), "launches": n}
     pe.pe_profile_enable(ctx, 0)
 
+    # verify in its sampling form at temperature 0.3 (the pages' example request), seeded uniforms
+    rng = np.random.default_rng(w.seed + 23)
+    u_s = torch.from_numpy(rng.random((B, K), dtype=np.float32)).cuda()
+    v_s = torch.from_numpy(rng.random((B, K + 1), dtype=np.float32)).cuda()
+
+    def verify_sampled_call():
+        pe.pe_verify_sampled(ctx, B, K, T, draft, 0.3, u_s, v_s, fin, d["req_slot"], d["seq_len"], *outs)
+
+    for _ in range(3):
+        verify_sampled_call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        verify_sampled_call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_verify_sampled = e0.elapsed_time(e1) / reps
+
     depth = None if args.no_depth_sweep else latency_vs_depth(pe, torch, w, config_args, dev, kc, vc, d, stream, reps)
 
     if args.copy_calibration:
@@ -296,6 +314,7 @@ def main():
         "wall_ms_per_step": 1e3 * wall / args.steps,
         "t_draft_us": 1e3 * t_draft,
         "t_verify_us": 1e3 * t_verify,
+        "t_verify_sampled_us": 1e3 * t_verify_sampled,
         "step_hbm_frac": ab["step"] / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
         "draft_hbm_frac": ab["draft"] / (t_draft * 1e-3) / (PEAK_HBM_GBS * 1e9),
         "algorithmic_MB": {k: v / 1e6 for k, v in ab.items()},

@@ -140,8 +140,13 @@ hipError_t launch_argmax_rows(int dtype, const void* X, int rows, int V, int nch
                               hipStream_t st);
 hipError_t launch_argmax_final(const float* pv, const int* pi, int rows, int nchunks, int* out, hipStream_t st);
 // sampled verification (temperature > 0): chunk softmax statistics, per-request decisions and draws, then the
-// metadata rebuild; pm / ps hold rows x nchunks floats each (nchunks <= PE_SAMPLE_MAX_CHUNKS)
+// metadata rebuild; pm / ps hold rows x nchunks floats each (nchunks = plan_sample_chunks(V))
 constexpr int PE_SAMPLE_MAX_CHUNKS = 1024;
+// chunks per row of the sampled verify: about 2048 tokens each, so that a draw scans one short chunk
+inline int plan_sample_chunks(int V) {
+  const int c = (V + 2047) / 2048;
+  return c < 1 ? 1 : (c > PE_SAMPLE_MAX_CHUNKS ? PE_SAMPLE_MAX_CHUNKS : c);
+}
 hipError_t launch_sampled_verify(int dtype, const void* X, int B, int K, int V, int nchunks, float temperature,
                                  const int* draft, const float* u, const float* v, const uint8_t* finished,
                                  const int* req_slot, const int* seq_len, float* pm, float* ps, int* t_ws,

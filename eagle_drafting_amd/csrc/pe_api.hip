@@ -45,6 +45,7 @@ struct pe_ctx {
   float* am_val = nullptr; // argmax partials
   int* am_idx = nullptr;
   int* t_ws = nullptr;     // target argmax [max_batch, max_k + 1]
+  float* samp = nullptr;   // sampled verify: per-chunk softmax statistics, 2 x [max_batch (max_k + 1), chunks]
   float* logits_ws = nullptr;  // fp32 path: logits when the caller passes none
   float2* rope = nullptr;  // [max_ctx, hd/2] (cos, sin)
   float* ssq = nullptr;    // partial sums of squares of X rows [Mmax, d/4] (per 16 or per 4 columns)
@@ -272,7 +273,8 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
                oT = take((size_t)c.max_batch * (c.max_k + 1) * 4),
                oL = take(ctx->bf16 ? 0 : (size_t)Mmax * V * 4), oR = take((size_t)c.max_ctx * (hd / 2) * 8),
                oS = take((size_t)Mmax * nssq * 4), oF = take(256), oK = take(part_floats * 4),
-               oArT = take((size_t)c.max_batch * 4), oArS = take((size_t)c.max_batch * 4);
+               oArT = take((size_t)c.max_batch * 4), oArS = take((size_t)c.max_batch * 4),
+               oSm = take((size_t)2 * c.max_batch * (c.max_k + 1) * plan_sample_chunks(V) * 4);
   if (hipMalloc((void**)&ctx->ws, off) != hipSuccess) {
     free_ctx(ctx);
     return fail(nullptr, PE_ERR_OOM, "hipMalloc of workspace failed");
@@ -295,6 +297,7 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
   ctx->part = part_floats ? (float*)(b + oK) : nullptr;
   ctx->ar_tok = (int*)(b + oArT);
   ctx->ar_seq = (int*)(b + oArS);
+  ctx->samp = (float*)(b + oSm);
 
   hipError_t r = launch_rope_table(ctx->rope, c.max_ctx, hd, (double)c.rope_base, ctx->stream);
   if (r == hipSuccess) r = hipMemsetAsync(ctx->flags, 0, 256, ctx->stream);
@@ -654,9 +657,11 @@ extern "C" pe_status pe_verify_sampled(pe_ctx* ctx, int32_t B, int32_t K, const 
   if (c.vocab % 8) return fail(ctx, PE_ERR_UNSUPPORTED, "sampled verify needs vocab % 8 == 0");
   hipStream_t st = ctx->stream;
   const int rows = B * (K + 1);
-  const int nch = plan_argmax_chunks(rows, c.vocab);
+  const int nch = plan_sample_chunks(c.vocab);
+  float* pm = ctx->samp;
+  float* ps = ctx->samp + (size_t)rows * nch;
   LAUNCH(launch_sampled_verify(ctx->bf16 ? 1 : 0, target_logits, B, K, c.vocab, nch, temperature, draft_tokens, u, v,
-                               finished, req_slot, seq_len, ctx->am_val, (float*)ctx->am_idx, ctx->t_ws, accept_len,
+                               finished, req_slot, seq_len, pm, ps, ctx->t_ws, accept_len,
                                cu_accept, out_tokens, keep_index, n_keep, req_slot_next, seq_len_next,
                                last_token_next, st));
   return PE_OK;
