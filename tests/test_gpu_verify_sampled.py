@@ -135,3 +135,62 @@ def test_sampled_verify_rejects_bad_temperature():
             assert e.value.status == pe.PE_ERR_INVALID
     finally:
         ctx.close()
+
+
+def test_sampled_verify_gpu_emits_the_target_distribution():
+    # the defining property on the GPU itself: 1024 requests share one target row and one draft (not the
+    # argmax), each with its own uniforms; over 20 calls the first emitted token follows
+    # p_0 = softmax(T_0 / temperature) and the draft is accepted at rate p_0(draft) (5 sigma)
+    from scipy.special import softmax
+    B, K, V, tau = 1024, 1, 16, 0.8
+    rng = np.random.default_rng(77)
+    row = rng.standard_normal((K + 1, V)).astype(np.float32) * 1.5
+    T = np.broadcast_to(row, (B, K + 1, V)).copy()
+    d0 = int(np.argsort(row[0])[-2])
+    draft = np.full((B, K), d0, dtype=np.int32)
+    ctx = VerifyCtx(V, "f32", B, K)
+    counts, acc, N = np.zeros(V), 0, 0
+    try:
+        for it in range(20):
+            u = rng.random((B, K)).astype(np.float32)
+            v = rng.random((B, K + 1)).astype(np.float32)
+            got = _run(ctx.pe, ctx.ctx, to_device(T, "f32"), draft, tau, u, v, None, np.arange(B, dtype=np.int32),
+                       np.zeros(B, dtype=np.int32))
+            first = got["out_tokens"][got["cu_accept"][:B]]
+            np.add.at(counts, first, 1)
+            acc += int((got["accept_len"] == 2).sum())
+            N += B
+    finally:
+        ctx.close()
+    p0 = softmax(row[0].astype(np.float64) / tau)
+    sig = np.sqrt(p0 * (1 - p0) / N)
+    assert np.all(np.abs(counts / N - p0) < 5 * sig + 1e-12), (counts / N, p0)
+    assert abs(acc / N - p0[d0]) < 5 * np.sqrt(p0[d0] * (1 - p0[d0]) / N)
+
+
+@pytest.mark.parametrize("case", ["k1", "all_finished", "largest_batch"])
+def test_sampled_verify_edge_cases(case):
+    rng = np.random.default_rng({"k1": 1, "all_finished": 2, "largest_batch": 3}[case])
+    B, K, V, dtype = {"k1": (5, 1, 4096, "bf16"), "all_finished": (7, 3, 4096, "f32"),
+                      "largest_batch": (1024, 2, 1024, "bf16")}[case]
+    T = rng.standard_normal((B, K + 1, V)).astype(np.float32) * 3.0
+    if dtype == "bf16":
+        from synth.inputs import bf16_bits
+        T_dev_host = bf16_bits(T)
+        T = bf16_bits_to_f32(T_dev_host)
+    else:
+        T_dev_host = T
+    draft = np.where(rng.random((B, K)) < 0.5, T[:, :K].argmax(-1), rng.integers(0, V, (B, K))).astype(np.int32)
+    tau = 0.5
+    u, v = _uniforms(T, draft, tau, 9)
+    fin = np.ones(B, dtype=np.uint8) if case == "all_finished" else (rng.random(B) < 0.3).astype(np.uint8)
+    slot = rng.permutation(B + 3)[:B].astype(np.int32)
+    seq = rng.integers(0, 500, B).astype(np.int32)
+    ctx = VerifyCtx(V, dtype, B, K)
+    try:
+        got = _run(ctx.pe, ctx.ctx, to_device(T_dev_host, dtype), draft, tau, u, v, fin, slot, seq)
+    finally:
+        ctx.close()
+    _check(got, T, draft, tau, u, v, fin, slot, seq)
+    if case == "all_finished":
+        assert int(got["n_keep"][0]) == 0
