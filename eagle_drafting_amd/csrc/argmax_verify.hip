@@ -299,9 +299,10 @@ __global__ __launch_bounds__(256) void softmax_stats_kernel(const T* __restrict_
   }
 }
 
-// One workgroup per request: the positions in order until the first rejection. Chunk statistics go through
-// LDS; the row maximum and total are combined in chunk order by one thread; the draw finds its chunk by a
-// prefix over the chunk totals and its token by a block scan inside the chunk.
+// One workgroup per request. Every position's row maximum and total (its chunk statistics merged by one
+// wave in a fixed order), draft weight and acceptance test are computed up front, one wave per position;
+// one thread then takes the first rejection n. The draw at n finds its chunk by a prefix over the chunk
+// totals and its token by a block scan inside the chunk.
 template <typename T>
 __global__ __launch_bounds__(256) void sample_decide_kernel(const T* __restrict__ X, int V, int chunk, int nchunks,
                                                             float inv_temp, const float* __restrict__ pm,
@@ -309,118 +310,135 @@ __global__ __launch_bounds__(256) void sample_decide_kernel(const T* __restrict_
                                                             const int* __restrict__ draft, const float* __restrict__ u,
                                                             const float* __restrict__ v, int* __restrict__ t_ws,
                                                             int* __restrict__ accept_len) {
+  constexpr int PMAX = 17;  // positions per request (K <= 16)
   __shared__ float cm[PE_SAMPLE_MAX_CHUNKS], cs[PE_SAMPLE_MAX_CHUNKS];
   __shared__ float red[256];
-  __shared__ float sh_M, sh_S, sh_base;
-  __shared__ int sh_k, sh_x;
-  const int b = blockIdx.x, tid = threadIdx.x;
-  int n = K;
-  for (int i = 0; i <= K; ++i) {
+  __shared__ float sM[PMAX], sS[PMAX], sEd[PMAX];
+  __shared__ int sAcc[PMAX];
+  __shared__ float sh_base;
+  __shared__ int sh_k, sh_x, sh_n;
+  const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // per position: (max, total) of the row, the draft's weight and the acceptance test
+  for (int i = wave; i <= K; i += 4) {
     const int r = b * (K + 1) + i;
-    for (int c = tid; c < nchunks; c += 256) {
-      cm[c] = pm[(size_t)r * nchunks + c];
-      cs[c] = ps[(size_t)r * nchunks + c];
+    float m = -INFINITY, sum = 0.f;
+    for (int c = lane; c < nchunks; c += 64) sm_merge(m, sum, pm[(size_t)r * nchunks + c], ps[(size_t)r * nchunks + c]);
+    for (int off = 1; off < 64; off <<= 1) {
+      const float m2 = __shfl_xor(m, off, PE_WAVE), s2 = __shfl_xor(sum, off, PE_WAVE);
+      sm_merge(m, sum, m2, s2);
     }
-    __syncthreads();
-    if (tid == 0) {
-      float M = -INFINITY, S = 0.f;
-      for (int c = 0; c < nchunks; ++c) sm_merge(M, S, cm[c], cs[c]);
-      sh_M = M;
-      sh_S = S;
-    }
-    __syncthreads();
-    const float M = sh_M, S = sh_S;
-    const T* x = X + (size_t)r * V;
-    int excl = -1;
-    float ed = 0.f, theta;
-    if (i < K) {
-      const int d = draft[(size_t)b * K + i];
-      const bool d_ok = d >= 0 && d < V;
-      ed = d_ok ? __expf(to_f32<T>(x[d]) * inv_temp - M) : 0.f;
-      if (tid == 0) sh_k = d_ok && u[(size_t)b * K + i] < ed / S ? 1 : 0;  // one thread decides for all
-      __syncthreads();
-      if (sh_k) {  // accepted
-        if (tid == 0) t_ws[r] = d;
-        __syncthreads();  // cm / cs / sh_k are rewritten for the next position
-        continue;
+    if (lane == 0) {
+      sM[i] = m;
+      sS[i] = sum;
+      float ed = 0.f;
+      int acc = 0;
+      if (i < K) {
+        const int d = draft[(size_t)b * K + i];
+        if (d >= 0 && d < V) {
+          ed = __expf(to_f32<T>(X[(size_t)r * V + d]) * inv_temp - m);
+          acc = u[(size_t)b * K + i] < ed / sum ? 1 : 0;
+        }
       }
-      excl = d_ok ? d : -1;
-      theta = v[(size_t)b * (K + 1) + i] * (S - ed);
-    } else {
-      theta = v[(size_t)b * (K + 1) + i] * S;
+      sEd[i] = ed;
+      sAcc[i] = acc;
     }
-    __syncthreads();  // sh_k is rewritten below
-    // the chunk holding the draw: first chunk whose running total (without the excluded token) passes theta
-    if (tid == 0) {
-      float acc = 0.f;
-      int k = -1, last = 0;
-      for (int c = 0; c < nchunks; ++c) {
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int n = K;
+    for (int i = 0; i < K; ++i)
+      if (!sAcc[i]) { n = i; break; }
+    sh_n = n;
+  }
+  __syncthreads();
+  const int n = sh_n;
+  if (tid < n) t_ws[(size_t)b * (K + 1) + tid] = draft[(size_t)b * K + tid];  // the accepted drafts
+  const int r = b * (K + 1) + n;
+  for (int c = tid; c < nchunks; c += 256) {
+    cm[c] = pm[(size_t)r * nchunks + c];
+    cs[c] = ps[(size_t)r * nchunks + c];
+  }
+  const float M = sM[n], S = sS[n];
+  const T* x = X + (size_t)r * V;
+  int excl = -1;
+  float ed = 0.f, theta;
+  if (n < K) {  // rejection: draw from p_n without the draft
+    const int d = draft[(size_t)b * K + n];
+    excl = d >= 0 && d < V ? d : -1;
+    ed = sEd[n];
+    theta = v[(size_t)b * (K + 1) + n] * (S - ed);
+  } else {  // every draft accepted: the bonus draw from p_K
+    theta = v[(size_t)b * (K + 1) + K] * S;
+  }
+  __syncthreads();
+  // the chunk holding the draw: first chunk whose running total (without the excluded token) passes theta
+  if (tid == 0) {
+    float acc = 0.f;
+    int k = -1, last = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      float w = cs[c] * __expf(cm[c] - M);
+      if (excl >= c * chunk && excl < (c + 1) * chunk) w = fmaxf(w - ed, 0.f);
+      if (w > 0.f) last = c;
+      if (k < 0 && acc + w > theta) { k = c; sh_base = acc; }
+      acc += w;
+    }
+    if (k < 0) {  // rounding left theta at or past the total: the last chunk with weight
+      k = last;
+      float a2 = 0.f;
+      for (int c = 0; c < last; ++c) {
         float w = cs[c] * __expf(cm[c] - M);
         if (excl >= c * chunk && excl < (c + 1) * chunk) w = fmaxf(w - ed, 0.f);
-        if (w > 0.f) last = c;
-        if (k < 0 && acc + w > theta) { k = c; sh_base = acc; }
-        acc += w;
+        a2 += w;
       }
-      if (k < 0) {  // rounding left theta at or past the total: the last chunk with weight
-        k = last;
-        float a2 = 0.f;
-        for (int c = 0; c < last; ++c) {
-          float w = cs[c] * __expf(cm[c] - M);
-          if (excl >= c * chunk && excl < (c + 1) * chunk) w = fmaxf(w - ed, 0.f);
-          a2 += w;
-        }
-        sh_base = a2;
-      }
-      sh_k = k;
-      sh_x = -1;
+      sh_base = a2;
     }
+    sh_k = k;
+    sh_x = -1;
+  }
+  __syncthreads();
+  const int k = sh_k;
+  const int cb = k * chunk, ce = min(V, cb + chunk);
+  const int per = (ce - cb + 255) / 256;
+  const int lb = cb + tid * per, le = min(ce, lb + per);
+  auto wt = [&](int e) { return e == excl ? 0.f : __expf(to_f32<T>(x[e]) * inv_temp - M); };
+  float local = 0.f;
+  for (int e = lb; e < le; ++e) local += wt(e);
+  // inclusive block scan of the per-thread totals (thread order); thread j owns [lo_j, hi_j) with
+  // lo_j = base + scan[j - 1] and hi_j = base + scan[j] = lo_{j+1}, the last thread also everything past
+  // the chunk's total, so exactly one thread owns theta (theta >= base)
+  red[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const float add = tid >= off ? red[tid - off] : 0.f;
     __syncthreads();
-    const int k = sh_k;
-    const int cb = k * chunk, ce = min(V, cb + chunk);
-    const int per = (ce - cb + 255) / 256;
-    const int lb = cb + tid * per, le = min(ce, lb + per);
-    auto wt = [&](int e) { return e == excl ? 0.f : __expf(to_f32<T>(x[e]) * inv_temp - M); };
-    float local = 0.f;
-    for (int e = lb; e < le; ++e) local += wt(e);
-    // inclusive block scan of the per-thread totals (thread order); thread j owns [lo_j, hi_j) with
-    // lo_j = base + scan[j - 1] and hi_j = base + scan[j] = lo_{j+1}, the last thread also everything past
-    // the chunk's total, so exactly one thread owns theta (theta >= base)
-    red[tid] = local;
+    red[tid] += add;
     __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      const float add = tid >= off ? red[tid - off] : 0.f;
-      __syncthreads();
-      red[tid] += add;
-      __syncthreads();
-    }
-    const float base = sh_base;
-    const float lo = base + (tid == 0 ? 0.f : red[tid - 1]);
-    const float hi = tid == 255 ? INFINITY : base + red[tid];
-    if (lo <= theta && theta < hi) {
-      float a = lo;
-      int pick = -1;
-      for (int e = lb; e < le; ++e) {
-        const float w = wt(e);
-        if (w > 0.f) {
-          pick = e;
-          a += w;
-          if (a > theta) break;
-        }
+  }
+  const float base = sh_base;
+  const float lo = base + (tid == 0 ? 0.f : red[tid - 1]);
+  const float hi = tid == 255 ? INFINITY : base + red[tid];
+  if (lo <= theta && theta < hi) {
+    float a = lo;
+    int pick = -1;
+    for (int e = lb; e < le; ++e) {
+      const float w = wt(e);
+      if (w > 0.f) {
+        pick = e;
+        a += w;
+        if (a > theta) break;
       }
-      sh_x = pick;  // rounding may end the range before theta: then its last token with weight
     }
-    __syncthreads();
-    if (tid == 0) {
-      int xs = sh_x;
-      if (xs < 0) {  // the owner holds no weight: the last token of the chunk with weight
-        xs = cb;
-        for (int e = ce - 1; e >= cb; --e)
-          if (wt(e) > 0.f) { xs = e; break; }
-      }
-      t_ws[r] = xs;
+    sh_x = pick;  // rounding may end the range before theta: then its last token with weight
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int xs = sh_x;
+    if (xs < 0) {  // the owner holds no weight: the last token of the chunk with weight
+      xs = cb;
+      for (int e = ce - 1; e >= cb; --e)
+        if (wt(e) > 0.f) { xs = e; break; }
     }
-    n = i;
-    break;
+    t_ws[r] = xs;
   }
   if (tid == 0) accept_len[b] = n + 1;
 }
@@ -452,7 +470,8 @@ hipError_t launch_sampled_verify(int dtype, const void* X, int B, int K, int V, 
                                  const int* req_slot, const int* seq_len, float* pm, float* ps, int* t_ws,
                                  int* accept_len, int* cu_accept, int* out_tokens, int* keep_index, int* n_keep,
                                  int* slot_next, int* seq_next, int* last_next, hipStream_t st) {
-  if (nchunks < 1 || nchunks > PE_SAMPLE_MAX_CHUNKS || B < 1 || B > 1024) return hipErrorInvalidValue;
+  if (nchunks < 1 || nchunks > PE_SAMPLE_MAX_CHUNKS || B < 1 || B > 1024 || K < 1 || K > 16)
+    return hipErrorInvalidValue;
   int chunk = (V + nchunks - 1) / nchunks;
   chunk = (chunk + 7) / 8 * 8;  // every chunk start 16-byte aligned (V % 8 == 0)
   const int rows = B * (K + 1);
