@@ -1,4 +1,5 @@
-"""GPU parity over several state-advancing draft + verify steps with churn.
+"""GPU parity over several state-advancing draft + verify steps with churn, with the greedy verify and with
+the sampled one (temperature > 0, seeded uniforms; its checks are those of test_gpu_verify_sampled).
 
 Each step: pe_draft_step on the current batch (checked against the oracle's draft step on the oracle's own
 copy of every request's context), target logits planted on the GPU's draft, pe_verify with random
@@ -35,7 +36,7 @@ MULTI = [
 ]
 
 
-def _run(w: Workload):
+def _run(w: Workload, tau=None):
     import torch
     from synth.device import to_device
 
@@ -70,9 +71,17 @@ def _run(w: Workload):
 
             T = plant_target_logits(w, draft, st["alpha"], step)
             fin = churn_finished(w, step)
-            got = run_verify(dr.pe, dr.ctx, B, K, to_device(T, s.dtype), draft_dev, to_device(fin, "u8"),
-                             dstate["req_slot"], dstate["seq_len"])
-            v, c = check_verify(got, to_f64(T, s.dtype), draft, fin, st["req_slot"], st["seq_len"])
+            if tau is None:
+                got = run_verify(dr.pe, dr.ctx, B, K, to_device(T, s.dtype), draft_dev, to_device(fin, "u8"),
+                                 dstate["req_slot"], dstate["seq_len"])
+                v, c = check_verify(got, to_f64(T, s.dtype), draft, fin, st["req_slot"], st["seq_len"])
+            else:
+                from test_gpu_verify_sampled import _check, _run as run_sampled, _uniforms
+                Tx = to_f64(T, s.dtype)
+                u_s, v_s = _uniforms(Tx, draft, tau, w.seed + 31 * step)
+                got = run_sampled(dr.pe, dr.ctx, to_device(T, s.dtype), draft, tau, u_s, v_s, fin, st["req_slot"],
+                                  st["seq_len"])
+                v, c = _check(got, Tx, draft, tau, u_s, v_s, fin, st["req_slot"], st["seq_len"])
             log(f"  verify: accept_len {v['accept_len'].tolist()}, finished {fin.tolist()}, kept {c['n_keep']}")
 
             # the oracle's context grows by its own rows 0 .. accept_len - 1 of this step
@@ -120,3 +129,8 @@ def _run(w: Workload):
 @pytest.mark.parametrize("w", MULTI, ids=lambda w: w.name)
 def test_multistep_churn_parity(w):
     _run(w)
+
+
+@pytest.mark.parametrize("w,tau", [(MULTI[0], 0.2), (MULTI[1], 0.1)], ids=lambda v: getattr(v, "name", str(v)))
+def test_multistep_churn_sampled_verify(w, tau):
+    _run(w, tau)

@@ -90,7 +90,7 @@ def _check(got, T, draft, tau, u, v, finished, slot, seq):
     assert np.array_equal(got["req_slot_next"][:nk], c["req_slot_next"])
     assert np.array_equal(got["seq_len_next"][:nk], c["seq_len_next"])
     assert np.array_equal(got["last_token_next"][:nk], c["last_token_next"])
-    return ref
+    return ref, c
 
 
 # at temperature 0.3 and above a planted token (row maximum + 1) holds little of the mass of a 150 k
@@ -116,7 +116,7 @@ def test_sampled_verify_parity(name, tau):
         got = _run(ctx.pe, ctx.ctx, to_device(T, w.shape.dtype), draft, tau, u, v, fin, st["req_slot"], st["seq_len"])
     finally:
         ctx.close()
-    ref = _check(got, T_exact, draft, tau, u, v, fin, st["req_slot"], st["seq_len"])
+    ref, _ = _check(got, T_exact, draft, tau, u, v, fin, st["req_slot"], st["seq_len"])
     log(f"  mean accept_len {ref['accept_len'].mean():.3f}")
 
 
