@@ -162,13 +162,13 @@ def test_four_row_products_rows_path(B, K):
         g.close()
 
 
-@pytest.mark.parametrize("B,K", [(1, 8), (3, 5), (9, 3), (5, 12), (9, 11), (16, 7), (11, 11)],
+@pytest.mark.parametrize("B,K", [(1, 8), (3, 5), (9, 3), (5, 12), (9, 11), (16, 7), (11, 11), (20, 7), (32, 8)],
                          ids=lambda v: str(v))
 def test_stream_kernel_row_counts_parity(B, K):
     """Row counts around every projection-kernel boundary: layer rows B (K + 1) = 9 (small-batch kernel),
-    18 / 36 / 65 / 108 / 128 (weight-stream kernel with 1, 2, 3 and 4 row blocks, 128 the largest) and 132
-    (128 x 128 tiled kernel); LM-head rows B K = 8, 15, 27, 60, 99, 112 and 121. Ragged short contexts,
-    sampled requests, K/V rows included."""
+    18 / 36 / 65 / 108 / 128 (weight-stream kernel with 1, 2, 3 and 4 row blocks, 128 the largest) and
+    132 / 160 / 288 (128 x 128 tiled kernel); LM-head rows B K = 8, 15, 27, 60, 99, 112 (stream kernel) and
+    121, 140, 256 (tiled kernel). Ragged short contexts, sampled requests, K/V rows included."""
     w = Workload(f"qwen3coder-bf16-B{B}-K{K}-rowcounts", QWEN3_CODER, B, K, (60, 400), 0.7, 7600 + 20 * B + K)
     log(f"row counts: B {B} K {K} (layer rows {B * (K + 1)}, LM-head rows {B * K})")
     g = GpuDrafter(w)
