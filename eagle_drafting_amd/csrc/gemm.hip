@@ -103,8 +103,9 @@ GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok) {
   if (M > (argmax ? 8 : 16) && M <= 128 && (long long)p.Nt * Ks * 1024 < 0x7ff00000LL) {
     // up to 128 rows: the weight-stream kernel (all rows and 128 columns per workgroup, activations staged
     // once per chunk). Narrow or short products split the reduction over workgroups until there are about
-    // 384 of them, each with at least four chunks, and while the fp32 partials stay within the weight bytes
-    // (2 ksplit M N 4 <= N Kd 2); the split reduce kernel then runs the epilogue.
+    // 192 of them, each with at least four chunks, and while the fp32 partials stay within the weight bytes
+    // (2 ksplit M N 4 <= N Kd 2); the split reduce kernel then runs the epilogue. (The partials go through
+    // HBM, so fewer splits win: at 96 rows a 192-workgroup target beats 384 by 2-3 % per step.)
     const int tg = (p.Nt + 7) / 8;
     constexpr int step = 4 * GEMM_STREAM_CH;
     p.tiled = 2;
@@ -115,7 +116,7 @@ GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok) {
     p.ngroups = tg;
     if (!argmax) {
       int ks = 1;
-      while (tg * ks < 384 && Ks >= 2 * step * ks && 8LL * (2 * ks) * M <= 2LL * Kd) ks *= 2;
+      while (tg * ks < 192 && Ks >= 2 * step * ks && 8LL * (2 * ks) * M <= 2LL * Kd) ks *= 2;
       if (ks > 1) {
         p.kper = (((Ks + ks - 1) / ks) + step - 1) / step * step;
         p.ksplit = (Ks + p.kper - 1) / p.kper;
