@@ -29,6 +29,10 @@ Readings where the pages leave a step open (each is listed with its reason in th
     placeholder row at position L_b + K (after the K draft rows, so it changes none of them) and keeps
     only its K/V: draft_step(..., tail=True).
 
+  * multi-row catch-up (a step that first re-runs the positions a verify accepted): each real row pairs
+    an emitted token with the target hidden states that produced it, as the pages' position 1 does for
+    the one token; the pages do not describe this step, so its logits are parity unpinned against the
+    pages (pinned against the separately written single-row passes and against the plain step);
   * autoregressive drafting (the baseline parallel drafting replaces) feeds back the drafter's hidden
     state after its last layer (before the final norm) plus the embedding of the token it just drafted;
     the pages name the dependency but not which hidden state, so this reading is parity unpinned
@@ -219,6 +223,52 @@ def draft_step(shape, W: dict, state: dict, kv_context, K: int, tail: bool = Fal
     if tail:
         for key in ("logits", "draft", "hidden"):
             out[key] = out[key][:, :K]
+    out["rows"] = X
+    return out
+
+
+def build_rows_catchup(W: dict, tokens: np.ndarray, target_hidden: np.ndarray, n_real: np.ndarray,
+                       K: int) -> np.ndarray:
+    """X [B, R + K, d] for a step that first catches up on several real positions.
+
+    Request b's rows 0..n_real[b]-1 are real, each built like the pages' position 1: fc of the three
+    captured target hidden states that produced token tokens[b, i], plus that token's embedding. Every
+    later row is the placeholder h_shared + emb_mask ([AWS-P] "how P-EAGLE breaks the chain"). With
+    n_real = 1 and R = 1 this is build_rows with K + 1 rows.
+    tokens [B, R], target_hidden [B, R, 3d]; entries past n_real[b] are ignored.
+    """
+    B, R = tokens.shape
+    d = W["emb_mask"].shape[0]
+    X = np.empty((B, R + K, d), dtype=np.float64)
+    X[:, :, :] = (W["h_shared"] + W["emb_mask"])[None, None, :]
+    for b in range(B):
+        r = int(n_real[b])
+        X[b, :r, :] = linear(target_hidden[b, :r], W["fc"]) + W["embed"][tokens[b, :r]]
+    return X
+
+
+def draft_step_catchup(shape, W: dict, state: dict, kv_context, K: int) -> dict:
+    """One parallel draft step whose input starts with several real positions (multi-row catch-up).
+
+    After a verify that emitted a tokens, the target has computed a hidden state for each of them; the
+    step re-runs those a positions as real rows (the exact drafter K/V for what was accepted) and then the
+    K - 1 placeholder rows of the parallel step. Request b's first row sits at position seq_len[b]; its
+    drafts come from rows n_real[b] - 1 (the last real row: the next token) .. n_real[b] + K - 2.
+    Every request runs R + K rows (R = tokens.shape[1]); the rows after the drafted ones only fill cache
+    positions the causal mask hides from every drafted row.
+
+    state: seq_len [B], tokens [B, R], target_hidden [B, R, 3d], n_real [B] in 1..R.
+    Returns logits [B, K, V], draft [B, K], hidden [B, K, d] of the drafted rows, the built rows, and
+    k_new / v_new per layer [B, R + K, Hkv, hd] of every row.
+    """
+    n_real = np.asarray(state["n_real"], dtype=np.int64)
+    X = build_rows_catchup(W, np.asarray(state["tokens"]), state["target_hidden"], n_real, K)
+    out = draft_rows(shape, W, X, state["seq_len"], kv_context)
+    B = X.shape[0]
+    rows = n_real[:, None] - 1 + np.arange(K)[None, :]
+    bi = np.arange(B)[:, None]
+    for key in ("logits", "draft", "hidden"):
+        out[key] = out[key][bi, rows]
     out["rows"] = X
     return out
 

@@ -463,6 +463,96 @@ def test_autoregressive_tail_and_feed():
     assert not np.allclose(f["logits"][:, 1], a["logits"][:, 1])
 
 
+# ---------------------------------------------------------------- multi-row catch-up step
+
+def _catchup(shape, W, tokens, hid, n_real, seq, ctx, K):
+    st = {"tokens": np.asarray(tokens), "target_hidden": hid, "n_real": np.asarray(n_real),
+          "seq_len": np.asarray(seq)}
+    return O.draft_step_catchup(shape, W, st, lambda l, b: ctx[b][l], K)
+
+
+def _real_row_passes(shape, W, toks, hid, L, ctx):
+    """Real rows one at a time with the separately written single-row pass: row i at position L + i over
+    the context plus the K/V of rows 0..i-1. Returns the last pass's logits, per-row K/V and the context
+    grown by every row but the last."""
+    ctx = [(k.copy(), v.copy()) for k, v in ctx]
+    ks, vs, z, grown = [], [], None, None
+    for i, (t, h) in enumerate(zip(toks, hid)):
+        if i == len(toks) - 1:
+            grown = [(k.copy(), v.copy()) for k, v in ctx]
+        _, z, _, k_rows, v_rows = O.eagle_step_sequential(shape, W, int(t), h, L + i, ctx, full=True)
+        ks.append(k_rows)
+        vs.append(v_rows)
+        ctx = [(np.concatenate([k, kr[:, None, :]], axis=1), np.concatenate([v, vr[:, None, :]], axis=1))
+               for (k, v), kr, vr in zip(ctx, k_rows, v_rows)]
+    return z, ks, vs, grown
+
+
+def test_catchup_real_rows_match_single_row_passes():
+    # each real row is an ordinary EAGLE input (token + the hidden states that produced it) at its own
+    # position; the rows of one request see each other causally, so row i equals a single-row pass over
+    # the context grown by rows 0..i-1; the last real row's logits are draft 0
+    W = _weights64(MINI, 41)
+    rng = np.random.default_rng(41)
+    R, K = 3, 3
+    toks = rng.integers(0, MINI.vocab, size=(2, R))
+    hid = rng.standard_normal((2, R, 3 * MINI.d_model))
+    n_real, seq = [3, 2], [5, 0]
+    ctx = [_ctx(MINI, 5, 410), _ctx(MINI, 0, 411)]
+    out = _catchup(MINI, W, toks, hid, n_real, seq, ctx, K)
+    assert out["logits"].shape == (2, K, MINI.vocab) and out["k_new"][0].shape[1] == R + K
+    for b in range(2):
+        r = n_real[b]
+        z, ks, vs, _ = _real_row_passes(MINI, W, toks[b, :r], hid[b, :r], seq[b], ctx[b])
+        assert out["logits"][b, 0] == pytest.approx(z, rel=1e-9, abs=1e-12)
+        for i in range(r):
+            for l in range(MINI.n_layers):
+                assert out["k_new"][l][b, i] == pytest.approx(ks[i][l], rel=1e-9, abs=1e-12)
+                assert out["v_new"][l][b, i] == pytest.approx(vs[i][l], rel=1e-9, abs=1e-12)
+
+
+def test_catchup_drafts_equal_the_plain_step_on_the_grown_context():
+    # after the real rows 0..r-2 have joined the context (single-row passes), the catch-up step's K drafts
+    # are those of a plain parallel step whose row 0 is the last real row, at position L + r - 1
+    W = _weights64(MINI, 42)
+    rng = np.random.default_rng(42)
+    R, K = 4, 3
+    toks = rng.integers(0, MINI.vocab, size=(2, R))
+    hid = rng.standard_normal((2, R, 3 * MINI.d_model))
+    n_real, seq = [4, 2], [3, 6]
+    ctx = [_ctx(MINI, 3, 420), _ctx(MINI, 6, 421)]
+    out = _catchup(MINI, W, toks, hid, n_real, seq, ctx, K)
+    for b in range(2):
+        r = n_real[b]
+        _, _, _, grown = _real_row_passes(MINI, W, toks[b, :r], hid[b, :r], seq[b], ctx[b])
+        plain = _step(MINI, W, [toks[b, r - 1]], hid[b, r - 1][None], [seq[b] + r - 1], [grown], K)
+        assert out["logits"][b] == pytest.approx(plain["logits"][0], rel=1e-9, abs=1e-12)
+        assert out["draft"][b].tolist() == plain["draft"][0].tolist()
+
+
+def test_catchup_with_one_real_row_is_the_plain_step():
+    # n_real = 1 and R = 1: the K + 1 rows of the plain step with its trailing placeholder row, exactly;
+    # padding entries past n_real (R = 3) change nothing
+    W = _weights64(MINI, 43)
+    rng = np.random.default_rng(43)
+    K = 3
+    toks = rng.integers(0, MINI.vocab, size=(2, 1))
+    hid = rng.standard_normal((2, 1, 3 * MINI.d_model))
+    ctx = [_ctx(MINI, 4, 430), _ctx(MINI, 2, 431)]
+    out = _catchup(MINI, W, toks, hid, [1, 1], [4, 2], ctx, K)
+    st = {"last_token": toks[:, 0], "target_hidden": hid[:, 0], "seq_len": np.asarray([4, 2])}
+    ref = O.draft_step(MINI, W, st, lambda l, b: ctx[b][l], K, tail=True)
+    # (the same arithmetic; the fc product runs per request here, so only the summation order differs)
+    assert out["logits"] == pytest.approx(ref["logits"], rel=1e-12, abs=1e-14)
+    for l in range(MINI.n_layers):
+        assert out["k_new"][l] == pytest.approx(ref["k_new"][l], rel=1e-12, abs=1e-14)
+    toks3 = np.concatenate([toks, rng.integers(0, MINI.vocab, size=(2, 2))], axis=1)
+    hid3 = np.concatenate([hid, rng.standard_normal((2, 2, 3 * MINI.d_model))], axis=1)
+    pad = _catchup(MINI, W, toks3, hid3, [1, 1], [4, 2], ctx, K)
+    assert np.array_equal(pad["logits"], out["logits"])
+    assert np.array_equal(pad["k_new"][0][:, :K + 1], out["k_new"][0])
+
+
 # ---------------------------------------------------------------- sampled verify (temperature > 0)
 
 def test_draw_inverse_cdf_brute_force():
