@@ -110,6 +110,51 @@ def latency_vs_depth(pe, torch, w, cfg_args, dev, kc, vc, d, stream, reps, depth
     return out
 
 
+def catchup_latency(pe, torch, w, cfg_args, dev, kc, vc, d, stream, reps):
+    """Latency of a multi-row catch-up step (pe_draft_catchup) beside the plain step on the same requests:
+    R = K + 1 token / hidden pairs per request (room for a fully accepted previous step), real-row counts
+    drawn uniformly in 1..R, so every request runs R + K rows. bf16 drafters only."""
+    from synth.device import to_device
+    from synth.inputs import catchup_inputs
+    s = w.shape
+    if s.dtype != "bf16":
+        return None
+    K = w.K
+    R = K + 1
+    ctx = pe.pe_init(pe.make_config(**cfg_args(w, max_k=R + K - 1)), pe.make_weights(dev, s.n_layers),
+                     pe.make_kv(kc, vc), stream.cuda_stream)
+    inp = catchup_inputs(w, R)
+    n_real = to_device(inp["n_real"], "i32")
+    tokens = to_device(inp["tokens"], "i32")
+    hid = to_device(inp["target_hidden"], s.dtype)
+    tok = torch.empty((w.B, K), dtype=torch.int32, device="cuda")
+    out = {"B": w.B, "K": K, "R": R, "rows_per_request": R + K, "mean_n_real": float(inp["n_real"].mean())}
+    calls = {"catchup_us": lambda: pe.pe_draft_catchup(ctx, w.B, K, R, d["req_slot"], d["seq_len"], n_real, tokens,
+                                                        hid, tok, None),
+             "plain_step_us": lambda: pe.pe_draft_step(ctx, w.B, K, d["req_slot"], d["seq_len"], d["last_token"],
+                                                       d["target_hidden"], tok, None)}
+    for key, call in calls.items():
+        for _ in range(3):
+            call()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[key] = 1e3 * e0.elapsed_time(e1) / reps
+    pe.pe_destroy(ctx)
+    return out
+
+
+def kernel_source_digest():
+    """sha256 over the sources that define the projection kernels (the LM head among them)."""
+    h = hashlib.sha256()
+    for name in ("gemm.hip", "kernels.h", "common.h"):
+        h.update(open(os.path.join(ROOT, "eagle_drafting_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
+
+
 def traffic_from_profile(workload_name):
     """HBM bytes per LM-head launch measured by rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, scaled by
     the plain-copy calibration), if the committed measurement was taken with the current kernel source."""
@@ -117,8 +162,7 @@ def traffic_from_profile(workload_name):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = open(os.path.join(ROOT, "eagle_drafting_amd", "csrc", "gemm.hip"), "rb").read()
-    if rec.get("workload") != workload_name or rec.get("gemm_src_sha256") != hashlib.sha256(src).hexdigest():
+    if rec.get("workload") != workload_name or rec.get("kernel_src_sha256") != kernel_source_digest():
         return None
     return rec.get("bytes_per_launch")
 
@@ -280,6 +324,7 @@ def main():
     t_verify_sampled = e0.elapsed_time(e1) / reps
 
     depth = None if args.no_depth_sweep else latency_vs_depth(pe, torch, w, config_args, dev, kc, vc, d, stream, reps)
+    catchup = catchup_latency(pe, torch, w, config_args, dev, kc, vc, d, stream, reps)
 
     if args.copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
@@ -324,6 +369,7 @@ def main():
         "roofline": lm_head_roofline(w, ab, lm_us, lm_n, traffic),
         "device_flags": flags,
         "draft_latency_vs_depth": depth,
+        "catchup_step": catchup,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, state, T_host, args.cpu_seconds)

@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     pe_destroy,
     pe_device_flags,
     pe_draft_ar,
+    pe_draft_catchup,
     pe_draft_rows,
     pe_draft_step,
     pe_init,

@@ -22,7 +22,8 @@ PE_PROF_LM_HEAD, PE_PROF_ATTENTION, PE_PROF_GATE_UP, PE_PROF_VERIFY_SCAN = 0, 1,
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpe.so")
 
-EXPORTED = ["pe_config_validate", "pe_init", "pe_draft_step", "pe_draft_rows", "pe_draft_ar", "pe_verify", "pe_verify_sampled",
+EXPORTED = ["pe_config_validate", "pe_init", "pe_draft_step", "pe_draft_rows", "pe_draft_ar", "pe_draft_catchup",
+            "pe_verify", "pe_verify_sampled",
             "pe_destroy",
             "pe_device_flags", "pe_profile_enable", "pe_profile_read", "pe_status_string", "pe_last_error"]
 
@@ -84,6 +85,7 @@ def load_library(path: str = LIB_PATH):
         "pe_draft_step": ([vp, i32, i32, vp, vp, vp, vp, vp, vp], i32),
         "pe_draft_rows": ([vp, i32, i32, vp, vp, vp, vp, vp], i32),
         "pe_draft_ar": ([vp, i32, i32, vp, vp, vp, vp, vp, vp], i32),
+        "pe_draft_catchup": ([vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp], i32),
         "pe_verify": ([vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp], i32),
         "pe_verify_sampled": ([vp, i32, i32, vp, vp, c_float, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
                               i32),
@@ -145,6 +147,11 @@ def pe_draft_step(ctx, B, K, req_slot, seq_len, last_token, target_hidden, draft
 def pe_draft_ar(ctx, B, K, req_slot, seq_len, last_token, target_hidden, draft_tokens, logits=None):
     _check(load_library().pe_draft_ar(ctx, B, K, _ptr(req_slot), _ptr(seq_len), _ptr(last_token),
                                       _ptr(target_hidden), _ptr(draft_tokens), _ptr(logits)), ctx)
+
+
+def pe_draft_catchup(ctx, B, K, R, req_slot, seq_len, n_real, tokens, target_hidden, draft_tokens, logits=None):
+    _check(load_library().pe_draft_catchup(ctx, B, K, R, _ptr(req_slot), _ptr(seq_len), _ptr(n_real), _ptr(tokens),
+                                           _ptr(target_hidden), _ptr(draft_tokens), _ptr(logits)), ctx)
 
 
 def pe_draft_rows(ctx, B, K, req_slot, seq_len, rows, draft_tokens, logits=None):

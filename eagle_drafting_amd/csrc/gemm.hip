@@ -223,8 +223,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
   // A through a raw buffer descriptor: lanes of padding rows (row >= M) use an out-of-range offset, which
   // returns zeros without any memory request, so only real rows cost bandwidth.
   const __amdgpu_buffer_rsrc_t a_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, (gemm_a_row(g, M - 1) + 1) * g.lda * 2, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, gemm_a_rows(g) * g.lda * 2, 0x00020000);
   bf16x8_t a[KC][MT], b[KC];
+  // each lane's operand row start (elements), or -1 for a padding row; resolved once, before the loop
+  int a_row0[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int row = KI ? lane & 3 : m0 + mt * 16 + (lane & 15);
+    a_row0[mt] = row < M ? gemm_a_row(g, row) * g.lda : -1;
+  }
   auto load_round = [&](int c0) {
     const int nk = max(1, min(KC, s_end - c0));
 #pragma unroll
@@ -234,11 +241,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
       for (int mt = 0; mt < MT; ++mt) {
         int off;
         if (KI) {  // MFMA row m + 4h: activation row m, k chunk 4(lane >> 4) + h of the 128-wide step
-          const int row = lane & 3, h = (lane >> 2) & 3;
-          off = row < M ? (gemm_a_row(g, row) * g.lda + ks * 128 + 8 * (4 * (lane >> 4) + h)) * 2 : 0x7ffffff0;
+          const int h = (lane >> 2) & 3;
+          off = a_row0[mt] >= 0 ? (a_row0[mt] + ks * 128 + 8 * (4 * (lane >> 4) + h)) * 2 : 0x7ffffff0;
         } else {
-          const int row = m0 + mt * 16 + (lane & 15);
-          off = row < M ? (gemm_a_row(g, row) * g.lda + ks * 32 + 8 * (lane >> 4)) * 2 : 0x7ffffff0;
+          off = a_row0[mt] >= 0 ? (a_row0[mt] + ks * 32 + 8 * (lane >> 4)) * 2 : 0x7ffffff0;
         }
         a[kk][mt] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0));
       }
@@ -367,28 +373,33 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
       if (c == 0) g.ssq_out[(size_t)m * g.nssq_out + nt] = sq;
     }
   } else if (EP == EPI_ROWS) {
-    // parallel-draft input rows: row 0 = fc . concat(h) + embed[last_token]; rows 1..K-1 = h_shared + emb_mask
-    const int Kr = g.Kdraft;
+    // parallel-draft input rows. Product row m is real row i = m % R of request b = m / R (R = 1 for a
+    // plain step): layer row b Kr + i = fc . concat(h) + embed[token] when i < n_real[b], else the
+    // placeholder h_shared + emb_mask; real row 0 also writes the placeholder rows R .. Kr - 1.
+    const int Kr = g.Kdraft, R = max(g.rows_real, 1);
     for (int idx = threadIdx.x; idx < rows * CW; idx += NTH) {
       const int r = idx / CW, c = idx % CW;
-      const int b = m0 + r, n = nt * CW + c;
+      const int m = m0 + r, n = nt * CW + c;
+      const int b = m / R, i = m % R;
+      const bool real = i < gemm_n_real(g, b);
       const bool first = idx == (int)threadIdx.x;
-      const int tok = first ? pre_tok : g.last_token[b];
+      const int tok = first ? pre_tok : g.last_token[m];
       const bool tok_ok = tok >= 0 && tok < g.V;
-      if (!tok_ok && c == 0) raise_flag(g.flags, PE_FLAG_TOKEN);
+      if (real && !tok_ok && c == 0) raise_flag(g.flags, PE_FLAG_TOKEN);
       float x0 = 0.f, ph = 0.f;
       if (n < N) {
         const float e = tok_ok ? bf16_to_f32(g.embed[(size_t)tok * N + n]) : 0.f;
-        x0 = Y(0, r, c) + e;
         ph = bf16_to_f32(g.h_shared[n]) + bf16_to_f32(g.emb_mask[n]);
+        x0 = real ? Y(0, r, c) + e : ph;
         const float gn = bf16_to_f32(g.gain_next[n]);
-        g.Xout[(size_t)(b * Kr) * N + n] = x0;
-        g.XGout[(size_t)(b * Kr) * N + n] = f32_to_bf16(x0 * gn);
+        g.Xout[(size_t)(b * Kr + i) * N + n] = x0;
+        g.XGout[(size_t)(b * Kr + i) * N + n] = f32_to_bf16(x0 * gn);
         const bf16_t phg = f32_to_bf16(ph * gn);
-        for (int j = 1; j < Kr; ++j) {
-          g.Xout[(size_t)(b * Kr + j) * N + n] = ph;
-          g.XGout[(size_t)(b * Kr + j) * N + n] = phg;
-        }
+        if (i == 0)
+          for (int j = R; j < Kr; ++j) {
+            g.Xout[(size_t)(b * Kr + j) * N + n] = ph;
+            g.XGout[(size_t)(b * Kr + j) * N + n] = phg;
+          }
       }
       float s0 = x0 * x0, s1 = ph * ph;
       for (int off = CW / 2; off > 0; off >>= 1) {
@@ -396,8 +407,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
         s1 += __shfl_xor(s1, off, PE_WAVE);
       }
       if (c == 0) {
-        g.ssq_out[(size_t)(b * Kr) * g.nssq_out + nt] = s0;
-        for (int j = 1; j < Kr; ++j) g.ssq_out[(size_t)(b * Kr + j) * g.nssq_out + nt] = s1;
+        g.ssq_out[(size_t)(b * Kr + i) * g.nssq_out + nt] = s0;
+        if (i == 0)
+          for (int j = R; j < Kr; ++j) g.ssq_out[(size_t)(b * Kr + j) * g.nssq_out + nt] = s1;
       }
     }
   } else if (EP == EPI_SWIGLU) {

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
   const int nstage = SPLIT ? g.kper / 2 : ((Ks + 1) / 2 + 1) & ~1;  // even (kper is a multiple of 4)
 
   const __amdgpu_buffer_rsrc_t a_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, (gemm_a_row(g, M - 1) + 1) * g.lda * 2, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, gemm_a_rows(g) * g.lda * 2, 0x00020000);
   const bf16x8_t* W = (const bf16x8_t*)g.Wp_raw;
 
   // Activations go through LDS (shared by the two waves of a row half); weights go straight from the
@@ -73,14 +73,21 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
   // 32 x 32 x 16 products out of the 16 x 32 fragments: lane l of the operand of rows (or columns)
   // 32 b .. 32 b + 31 and k-half u takes fragment 2 b + (l % 32) / 16, fragment lane l % 16 + 16 (2 u + l / 32)
   const int fr_t = (lane & 31) >> 4, fr_l = (lane & 15) + 16 * (lane >> 5);
+  // operand row start (elements) of each of this thread's four load pieces, or -1 past the last row;
+  // resolved once, before the loop
+  int a_row0[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = m0 + ((tid + 256 * q) >> 3);
+    a_row0[q] = row < M ? gemm_a_row(g, row) * g.lda : -1;
+  }
   auto gload_a1 = [&](RegA& r, int st, int q) {
     {
       const int p = tid + 256 * q;
-      const int arow = p >> 3, seg = p & 7;
+      const int seg = p & 7;
       const int akstep = kb + 2 * st + (seg >> 2);
-      const int row = m0 + arow;
       const int off =
-          row < M && akstep < ke ? (gemm_a_row(g, row) * g.lda + akstep * 32 + 8 * (seg & 3)) * 2 : 0x7ffffff0;
+          a_row0[q] >= 0 && akstep < ke ? (a_row0[q] + akstep * 32 + 8 * (seg & 3)) * 2 : 0x7ffffff0;
       r[q] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0));
     }
   };
@@ -345,30 +352,36 @@ __device__ void tile_epilogue(const GemmArgs& g, const float* Cs, const float* s
               sq0 += x[e] * x[e];
             }
           } else {
-            // m is a request b: row 0 = fc . concat(h) + embed[last_token]; rows 1..K-1 = h_shared + emb_mask
-            const int Kr = g.Kdraft;
+            // m is real row i = m % R of request b = m / R (R = 1 for a plain step): layer row b Kr + i =
+            // fc . concat(h) + embed[token] when i < n_real[b], else h_shared + emb_mask; real row 0 also
+            // writes the placeholder rows R .. Kr - 1
+            const int Kr = g.Kdraft, R = max(g.rows_real, 1);
+            const int b = m / R, i = m % R;
+            const bool real = i < gemm_n_real(g, b);
             const int tok = g.last_token[m];
             const bool tok_ok = tok >= 0 && tok < g.V;
-            if (!tok_ok && h == 0 && ng == 0) raise_flag(g.flags, PE_FLAG_TOKEN);
+            if (real && !tok_ok && h == 0 && ng == 0) raise_flag(g.flags, PE_FLAG_TOKEN);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const bool ok = n + e < N;
-              x[e] = ok ? vv[e] + (tok_ok ? bf16_to_f32(g.embed[(size_t)tok * N + n + e]) : 0.f) : 0.f;
               x1[e] = ok ? bf16_to_f32(g.h_shared[n + e]) + bf16_to_f32(g.emb_mask[n + e]) : 0.f;
+              x[e] = !ok ? 0.f : real ? vv[e] + (tok_ok ? bf16_to_f32(g.embed[(size_t)tok * N + n + e]) : 0.f) : x1[e];
               sq0 += x[e] * x[e];
               sq1 += x1[e] * x1[e];
             }
-            for (int jj = 0; jj < Kr; ++jj) {
-              const float* src = jj == 0 ? x : x1;
-              float* xr = g.Xout + (size_t)(m * Kr + jj) * N;
-              bf16_t* xg = g.XGout + (size_t)(m * Kr + jj) * N;
+            auto put = [&](int lr, const float* src) {  // layer row b Kr + lr
+              float* xr = g.Xout + (size_t)(b * Kr + lr) * N;
+              bf16_t* xg = g.XGout + (size_t)(b * Kr + lr) * N;
 #pragma unroll
               for (int e = 0; e < 4; ++e)
                 if (n + e < N) {
                   xr[n + e] = src[e];
                   xg[n + e] = f32_to_bf16(src[e] * gn[e]);
                 }
-            }
+            };
+            put(i, x);
+            if (i == 0)
+              for (int j = R; j < Kr; ++j) put(j, x1);
           }
         }
         // one partial sum of squares per row and 128-column workgroup tile
@@ -380,9 +393,11 @@ __device__ void tile_epilogue(const GemmArgs& g, const float* Cs, const float* s
           if (EP == EPI_RESID) {
             g.ssq_out[(size_t)m * g.nssq_out + ng] = sq0;
           } else {
-            const int Kr = g.Kdraft;
-            g.ssq_out[(size_t)(m * Kr) * g.nssq_out + ng] = sq0;
-            for (int jj = 1; jj < Kr; ++jj) g.ssq_out[(size_t)(m * Kr + jj) * g.nssq_out + ng] = sq1;
+            const int Kr = g.Kdraft, R = max(g.rows_real, 1);
+            const int b = m / R, i = m % R;
+            g.ssq_out[(size_t)(b * Kr + i) * g.nssq_out + ng] = sq0;
+            if (i == 0)
+              for (int j = R; j < Kr; ++j) g.ssq_out[(size_t)(b * Kr + j) * g.nssq_out + ng] = sq1;
           }
         }
       }
@@ -491,7 +506,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs g) {
   // rows >= M, weight tiles past the last one, and weight k-steps past this workgroup's range (a scalar
   // offset beyond the buffer), so padded k-steps contribute exact zeros.
   const __amdgpu_buffer_rsrc_t a_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, (gemm_a_row(g, M - 1) + 1) * g.lda * 2, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, gemm_a_rows(g) * g.lda * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)g.Wp_raw, (short)0, (int)((uint32_t)Nt * (uint32_t)Ks * 1024u), 0x00020000);
   auto asw = [](int lp) { return lp ^ ((lp >> 4) << 2); };

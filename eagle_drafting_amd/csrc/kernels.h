@@ -81,12 +81,26 @@ struct GemmArgs {
   // row m of the product reads operand row (m / rows_out) * rows_in + m % rows_out (and that row's sums
   // of squares): the LM head runs on rows_out of every rows_in rows per request. 0 = identity.
   int rows_in, rows_out;
+  // catch-up steps: request b has n_real[b] (1 .. rows_real) real input rows; the row build reads rows_real
+  // tokens / hidden triples per request, and the LM head's rows of request b start at operand row
+  // n_real[b] - 1 of its block. NULL = one real row per request.
+  const int* n_real; int rows_real;
   // tiled K-split: fp32 partial tiles [ksplit][M][N] (workspace) and the plan's split shape
   float* part; int ksplit, kper;
 };
+// real input rows of request b (clamped into 1 .. rows_real, so that a bad value stays in bounds)
+__device__ inline int gemm_n_real(const GemmArgs& g, int b) {
+  return g.n_real ? min(max(g.n_real[b], 1), max(g.rows_real, 1)) : 1;
+}
 // operand row of product row m
-__host__ __device__ inline int gemm_a_row(const GemmArgs& g, int m) {
-  return g.rows_out > 0 ? (m / g.rows_out) * g.rows_in + m % g.rows_out : m;
+__device__ inline int gemm_a_row(const GemmArgs& g, int m) {
+  if (g.rows_out <= 0) return m;
+  const int b = m / g.rows_out;
+  return b * g.rows_in + m % g.rows_out + (g.n_real ? gemm_n_real(g, b) - 1 : 0);
+}
+// operand rows the product may read (the size of its buffer range)
+__device__ inline int gemm_a_rows(const GemmArgs& g) {
+  return g.rows_out > 0 ? (g.M + g.rows_out - 1) / g.rows_out * g.rows_in : g.M;
 }
 hipError_t launch_gemm(const GemmPlan& p, GemmArgs a, int a_mode, int epi, hipStream_t st);
 hipError_t launch_gemm_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st);

@@ -238,10 +238,9 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
     if (ctx->bf16) {
       GemmPlan pl = plan_gemm(M, V, d, true);
       am_floats = std::max(am_floats, (size_t)M * pl.ngroups);
-      // K-split partials of the layer projections (and of the row build, whose M is B)
+      // K-split partials of the layer projections and of the row build (B rows, or B R for a catch-up step)
       const int shapes[5][2] = {{qkvd, d}, {d, qd}, {2 * F, d}, {d, F}, {d, 3 * d}};
       for (int sh = 0; sh < 5; ++sh) {
-        if (sh == 4 && M > c.max_batch) continue;
         const GemmPlan ps = plan_gemm(M, shapes[sh][0], shapes[sh][1], false);
         if (ps.ksplit > 1) part_floats = std::max(part_floats, (size_t)ps.ksplit * M * shapes[sh][0]);
       }
@@ -433,19 +432,21 @@ static GemmArgs gemm_base(pe_ctx* ctx) {
   return base;
 }
 
-// a1 (+ the sums of squares for layer 0's RMSNorm): Kr input rows per request from the row builder
+// a1 (+ the sums of squares for layer 0's RMSNorm): Kr input rows per request from the row builder. With
+// n_real, request b's first n_real[b] of its R token / hidden pairs are real rows (catch-up); else R = 1.
 static pe_status rows_bf16(pe_ctx* ctx, int32_t B, int32_t Kr, const int32_t* last_token, const void* target_hidden,
-                           int& nssq) {
+                           int& nssq, int32_t R = 1, const int32_t* n_real = nullptr) {
   const pe_config& c = ctx->cfg;
   const int d = c.d_model;
   GemmArgs a = gemm_base(ctx);
-  a.M = B; a.Kd = 3 * d; a.N = d;
+  a.M = B * R; a.Kd = 3 * d; a.N = d;
   a.A = (const uint16_t*)target_hidden; a.lda = 3 * d;
   a.Kdraft = Kr; a.last_token = last_token; a.V = c.vocab;
+  a.rows_real = R; a.n_real = n_real;
   a.embed = (const uint16_t*)ctx->w.embed; a.emb_mask = (const uint16_t*)ctx->w.emb_mask;
   a.h_shared = (const uint16_t*)ctx->w.h_shared;
   a.gain_next = (const uint16_t*)ctx->w.attn_norm[0];
-  const GemmPlan p = plan_gemm(B, d, 3 * d, false, true);
+  const GemmPlan p = plan_gemm(B * R, d, 3 * d, false, true);
   a.Wp_raw = p.ki4 ? ctx->p_fc4 : ctx->p_fc;
   a.nssq_out = nssq = gemm_ssq_parts(p);
   hipStream_t st = ctx->stream;
@@ -521,10 +522,10 @@ static pe_status layers_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* r
   return PE_OK;
 }
 
-// a9-a10: final RMSNorm, LM head, argmax on the first Kout of the K rows of every request; tokens [B * Kout];
-// logits row (b, j) at logits + (b * Kout + j) * ldz
+// a9-a10: final RMSNorm, LM head, argmax on Kout of the K rows of every request (the first Kout, or with
+// n_real those from row n_real[b] - 1 on); tokens [B * Kout]; logits row (b, j) at logits + (b * Kout + j) * ldz
 static pe_status lm_head_bf16(pe_ctx* ctx, int32_t B, int32_t K, int32_t Kout, int nssq, int32_t* tokens,
-                              float* logits, int ldz) {
+                              float* logits, int ldz, int32_t R = 1, const int32_t* n_real = nullptr) {
   const pe_config& c = ctx->cfg;
   hipStream_t st = ctx->stream;
   const int Mo = B * Kout;
@@ -532,6 +533,7 @@ static pe_status lm_head_bf16(pe_ctx* ctx, int32_t B, int32_t K, int32_t Kout, i
   a.M = Mo; a.Kd = c.d_model; a.N = c.vocab;
   a.A = (const uint16_t*)ctx->U; a.lda = c.d_model;
   a.rows_in = K; a.rows_out = Kout;
+  a.rows_real = R; a.n_real = n_real;
   a.Wp_raw = ctx->p_lm;
   a.am_val = ctx->am_val; a.am_idx = ctx->am_idx; a.logits = logits; a.ldz = ldz;
   a.nssq = nssq;
@@ -590,6 +592,18 @@ static pe_status draft_ar_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t*
   return PE_OK;
 }
 
+// Catch-up step: request b runs its n_real[b] real rows at positions seq_len[b] .. and then placeholder
+// rows, R + K rows in all; the K drafts come from rows n_real[b] - 1 .. n_real[b] + K - 2.
+static pe_status draft_catchup_bf16(pe_ctx* ctx, int32_t B, int32_t K, int32_t R, const int32_t* req_slot,
+                                    const int32_t* seq_len, const int32_t* n_real, const int32_t* tokens,
+                                    const void* target_hidden, int32_t* draft_tokens, float* logits) {
+  int nssq = 0;
+  const int Kr = R + K;
+  PE_TRY(rows_bf16(ctx, B, Kr, tokens, target_hidden, nssq, R, n_real));
+  PE_TRY(layers_bf16(ctx, B, Kr, req_slot, seq_len, nssq));
+  return lm_head_bf16(ctx, B, Kr, K, nssq, draft_tokens, logits, ctx->cfg.vocab, R, n_real);
+}
+
 static pe_status run_draft(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_slot, const int32_t* seq_len,
                            const int32_t* last_token, const void* target_hidden, const float* rows,
                            int32_t* draft_tokens, float* logits) {
@@ -631,6 +645,22 @@ extern "C" pe_status pe_draft_ar(pe_ctx* ctx, int32_t B, int32_t K, const int32_
   if ((uintptr_t)target_hidden & 15) return fail(ctx, PE_ERR_INVALID, "target_hidden not 16-byte aligned");
   if (logits && ((uintptr_t)logits & 15)) return fail(ctx, PE_ERR_INVALID, "logits not 16-byte aligned");
   return draft_ar_bf16(ctx, B, K, req_slot, seq_len, last_token, target_hidden, draft_tokens, logits);
+}
+
+extern "C" pe_status pe_draft_catchup(pe_ctx* ctx, int32_t B, int32_t K, int32_t R, const int32_t* req_slot,
+                                      const int32_t* seq_len, const int32_t* n_real, const int32_t* tokens,
+                                      const void* target_hidden, int32_t* draft_tokens, float* logits) {
+  if (!ctx) return fail(nullptr, PE_ERR_INVALID, "ctx is NULL");
+  const pe_config& c = ctx->cfg;
+  if (!ctx->bf16) return fail(ctx, PE_ERR_UNSUPPORTED, "catch-up steps need a bf16 drafter");
+  if (B < 1 || B > c.max_batch) return fail(ctx, PE_ERR_INVALID, "B out of [1, max_batch]");
+  if (K < 1 || K > c.max_k) return fail(ctx, PE_ERR_INVALID, "K out of [1, max_k]");
+  if (R < 1 || R + K > c.max_k + 1) return fail(ctx, PE_ERR_INVALID, "R out of [1, max_k + 1 - K]");
+  if (!req_slot || !seq_len || !n_real || !tokens || !target_hidden || !draft_tokens)
+    return fail(ctx, PE_ERR_INVALID, "NULL argument");
+  if ((uintptr_t)target_hidden & 15) return fail(ctx, PE_ERR_INVALID, "target_hidden not 16-byte aligned");
+  if (logits && ((uintptr_t)logits & 15)) return fail(ctx, PE_ERR_INVALID, "logits not 16-byte aligned");
+  return draft_catchup_bf16(ctx, B, K, R, req_slot, seq_len, n_real, tokens, target_hidden, draft_tokens, logits);
 }
 
 extern "C" pe_status pe_draft_rows(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_slot, const int32_t* seq_len,

@@ -18,7 +18,8 @@
  *   - Element type: pe_config.dtype (PE_F32 or PE_BF16) for weights, KV cache, target hiddens and target
  *     logits. Token ids, lengths and slots are int32. Logits written by the library are float32.
  *   - Calls enqueue work on the stream given to pe_init and return without waiting for the GPU.
- *     pe_draft_step, pe_draft_rows, pe_draft_ar, pe_verify and pe_verify_sampled allocate nothing.
+ *     pe_draft_step, pe_draft_rows, pe_draft_ar, pe_draft_catchup, pe_verify and pe_verify_sampled
+ *     allocate nothing.
  *   - A ctx is used by one host thread at a time. Calls on one ctx run in stream order.
  *   - Errors: every call returns a pe_status. Host-checkable problems (null pointers, sizes out of
  *     range, unsupported shapes) return PE_ERR_INVALID / PE_ERR_UNSUPPORTED before anything is enqueued.
@@ -142,6 +143,26 @@ pe_status pe_draft_rows(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_sl
  * PE_ERR_UNSUPPORTED. Allocates nothing. */
 pe_status pe_draft_ar(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_slot, const int32_t* seq_len,
                       const int32_t* last_token, const void* target_hidden, int32_t* draft_tokens, float* logits);
+
+/* Multi-row catch-up step: a parallel draft step whose input starts with several real positions, so
+ * that the drafter's K/V for the tokens a verify emitted come from the target's own hidden states.
+ * (Solution overview, step-by-step drafting process: the pages' position 1 pairs the token just produced
+ * with the target hidden states captured while producing it; here every emitted token gets such a row.
+ * The pages do not describe this step; it is a reading.) bf16 drafters only.
+ *   Request b runs R + K rows at positions seq_len[b] .. seq_len[b] + R + K - 1. Rows i < n_real[b] are
+ *   real: fc(target_hidden[b][i]) + embed[tokens[b][i]]; every later row is the placeholder h_shared +
+ *   emb_mask. draft_tokens[b*K + j] = argmax of row n_real[b] - 1 + j (the last real row predicts the
+ *   next token). Rows after the drafted ones only fill cache positions the causal mask hides from them.
+ *   With R = 1 this is pe_draft_step with tokens = last_token.
+ *   R: 1 .. max_k + 1 - K (real rows per request in the arrays; R = K + 1 holds a fully accepted step)
+ *   req_slot, seq_len (position of the first real row), n_real (1 .. R): device int32 [B]
+ *   tokens: device int32 [B, R]   target_hidden: device [B, R, 3 * d_model] (dtype); entries past
+ *   n_real[b] are ignored   draft_tokens: device int32 [B, K]   logits: device float32 [B, K, V] or NULL
+ *   Device contract: seq_len[b] + R + K <= max_ctx; an n_real outside 1..R is clamped into it.
+ *   A float32 drafter returns PE_ERR_UNSUPPORTED. Allocates nothing. */
+pe_status pe_draft_catchup(pe_ctx* ctx, int32_t B, int32_t K, int32_t R, const int32_t* req_slot,
+                           const int32_t* seq_len, const int32_t* n_real, const int32_t* tokens,
+                           const void* target_hidden, int32_t* draft_tokens, float* logits);
 
 /* Greedy verification and batch-metadata rebuild (solution overview, step 2, last sentence; batch
  * metadata as in the pages' fused metadata kernels). With t[b][i] = argmax_v target_logits[b][i][v]

@@ -252,3 +252,20 @@ def step_hiddens(w: Workload, step: int) -> np.ndarray:
     each step's hiddens come from a new target pass."""
     s = w.shape
     return _encode(_normal((w.seed, 700, step), (w.B, 3 * s.d_model)), s.dtype)
+
+
+def catchup_inputs(w: Workload, R: int, step: int = 0) -> dict:
+    """Inputs of a catch-up step: per request R token / hidden pairs and a real-row count.
+
+    tokens [B, R] int32 uniform in [0, V); target_hidden [B, R, 3d] N(0, 1), encoded; n_real [B] uniform
+    in 1..R with request 0 at R and (B > 1) request B - 1 at 1, so both ends are always present.
+    """
+    s = w.shape
+    rng = _rng(w.seed, 800, step)
+    tokens = rng.integers(0, s.vocab, size=(w.B, R)).astype(np.int32)
+    n_real = rng.integers(1, R + 1, size=w.B).astype(np.int32)
+    n_real[0] = R
+    if w.B > 1:
+        n_real[-1] = 1
+    hid = _encode(_normal((w.seed, 801, step), (w.B, R, 3 * s.d_model)), s.dtype)
+    return {"tokens": tokens, "target_hidden": hid, "n_real": n_real}
