@@ -112,15 +112,19 @@ def latency_vs_depth(pe, torch, w, cfg_args, dev, kc, vc, d, stream, reps, depth
 
 def catchup_latency(pe, torch, w, cfg_args, dev, kc, vc, d, stream, reps):
     """Latency of a multi-row catch-up step (pe_draft_catchup) beside the plain step on the same requests:
-    R = K + 1 token / hidden pairs per request (room for a fully accepted previous step), real-row counts
-    drawn uniformly in 1..R, so every request runs R + K rows. bf16 drafters only."""
+    R = K + 1 token / hidden pairs per request (room for a fully accepted previous step; fewer where the
+    config's largest max_k, 16 and 128 query rows per kv head, caps R + K - 1), real-row counts drawn
+    uniformly in 1..R, so every request runs R + K rows. bf16 drafters only."""
     from synth.device import to_device
     from synth.inputs import catchup_inputs
     s = w.shape
     if s.dtype != "bf16":
         return None
     K = w.K
-    R = K + 1
+    max_k = min(16, 128 // (s.n_q_heads // s.n_kv_heads) - 1)
+    R = min(K + 1, max_k + 1 - K)
+    if R < 1:
+        return None
     ctx = pe.pe_init(pe.make_config(**cfg_args(w, max_k=R + K - 1)), pe.make_weights(dev, s.n_layers),
                      pe.make_kv(kc, vc), stream.cuda_stream)
     inp = catchup_inputs(w, R)
