@@ -553,6 +553,96 @@ def test_catchup_with_one_real_row_is_the_plain_step():
     assert np.array_equal(pad["k_new"][0][:, :K + 1], out["k_new"][0])
 
 
+# ---------------------------------------------------------------- concatenated input rows
+
+MINI_CAT = DrafterShape("mini-f32-concat", 2, 32, 4, 2, 8, 48, 64, "f32", row_concat=True)
+
+
+def test_concat_rows_with_zero_embeddings_reduce_to_the_sum_step():
+    # with a zero embedding table and mask, the embedding half normalises to zero, so layer 0 sees only
+    # the hidden half through wqkv[0][:, d:]: the pinned sum-of-rows step with that matrix and zero
+    # embeddings
+    W = _weights64(MINI_CAT, 51)
+    W["embed"] = np.zeros_like(W["embed"])
+    W["emb_mask"] = np.zeros_like(W["emb_mask"])
+    Ws = {k: v for k, v in W.items() if k != "embed_norm"}
+    Ws["l0.wqkv"] = W["l0.wqkv"][:, MINI.d_model:]
+    rng = np.random.default_rng(51)
+    toks = rng.integers(0, MINI.vocab, size=2)
+    hid = rng.standard_normal((2, 3 * MINI.d_model))
+    ctx = [_ctx(MINI, 5, 510), _ctx(MINI, 0, 511)]
+    st = {"last_token": toks, "target_hidden": hid, "seq_len": np.asarray([5, 0])}
+    cat = O.draft_step_concat(MINI_CAT, W, st, lambda l, b: ctx[b][l], 3, tail=True)
+    ref = O.draft_step(MINI, Ws, st, lambda l, b: ctx[b][l], 3, tail=True)
+    assert cat["logits"] == pytest.approx(ref["logits"], rel=1e-12, abs=1e-14)
+    for l in range(MINI.n_layers):
+        assert cat["k_new"][l] == pytest.approx(ref["k_new"][l], rel=1e-12, abs=1e-14)
+
+
+def test_concat_rows_layer0_keys_by_hand():
+    # the order [embedding || hidden], the two gains and the placeholder halves, checked on layer 0's
+    # keys of rows 0 and 1 computed here directly from the definitions
+    W = _weights64(MINI_CAT, 52)
+    rng = np.random.default_rng(52)
+    d, Hq, Hkv, hd = MINI.d_model, MINI.n_q_heads, MINI.n_kv_heads, MINI.head_dim
+    tok = int(rng.integers(0, MINI.vocab))
+    hid = rng.standard_normal((1, 3 * d))
+    L = 4
+    ctx = [_ctx(MINI, L, 520)]
+    out = O.draft_step_concat(MINI_CAT, W, {"last_token": np.asarray([tok]), "target_hidden": hid,
+                                            "seq_len": np.asarray([L])}, lambda l, b: ctx[b][l], 2)
+
+    def norm(v, g):
+        return v / math.sqrt(float(v @ v) / d + MINI.rms_eps) * g
+
+    rows = [(W["embed"][tok], W["fc"] @ hid[0]), (W["emb_mask"], W["h_shared"])]
+    for j, (e, h) in enumerate(rows):
+        u = np.concatenate([norm(e, W["embed_norm"]), norm(h, W["l0.attn_norm"])])
+        k = (W["l0.wqkv"] @ u)[Hq * hd:(Hq + Hkv) * hd].reshape(Hkv, hd)
+        half = hd // 2
+        for g in range(Hkv):
+            rot = np.empty(hd)
+            for i in range(half):
+                th = (L + j) * MINI.rope_base ** (-2.0 * i / hd)
+                rot[i] = k[g, i] * math.cos(th) - k[g, i + half] * math.sin(th)
+                rot[i + half] = k[g, i + half] * math.cos(th) + k[g, i] * math.sin(th)
+            assert out["k_new"][0][0, j, g] == pytest.approx(rot, rel=1e-10, abs=1e-12)
+
+
+def test_concat_embedding_enters_only_through_layer0_attention():
+    # the residual stream is the hidden half: with wqkv[0]'s embedding columns zeroed, neither the
+    # embedding table nor the mask embedding changes any output
+    W = _weights64(MINI_CAT, 54)
+    W["l0.wqkv"] = W["l0.wqkv"].copy()
+    W["l0.wqkv"][:, :MINI.d_model] = 0.0
+    rng = np.random.default_rng(54)
+    hid = rng.standard_normal((2, 3 * MINI.d_model))
+    ctx = [_ctx(MINI, 2, 540), _ctx(MINI, 6, 541)]
+    st = {"last_token": np.asarray([3, 9]), "target_hidden": hid, "seq_len": np.asarray([2, 6])}
+    a = O.draft_step_concat(MINI_CAT, W, st, lambda l, b: ctx[b][l], 3)
+    W2 = dict(W)
+    W2["embed"] = W["embed"] * 3.0 + 0.5
+    W2["emb_mask"] = W["emb_mask"] - 2.0
+    b = O.draft_step_concat(MINI_CAT, W2, st, lambda l, b_: ctx[b_][l], 3)
+    assert np.array_equal(a["logits"], b["logits"])
+
+
+def test_concat_rows_causality():
+    # invariant 3 holds with concatenated rows: changing the token of request 0 changes row 0 onwards,
+    # and rows after j never reach row j (perturb the hidden half of the placeholders via h_shared)
+    W = _weights64(MINI_CAT, 53)
+    rng = np.random.default_rng(53)
+    hid = rng.standard_normal((1, 3 * MINI.d_model))
+    ctx = [_ctx(MINI, 3, 530)]
+    st = {"last_token": np.asarray([7]), "target_hidden": hid, "seq_len": np.asarray([3])}
+    a = O.draft_step_concat(MINI_CAT, W, st, lambda l, b: ctx[b][l], 3)
+    W2 = dict(W)
+    W2["h_shared"] = W["h_shared"] + 1.0
+    b = O.draft_step_concat(MINI_CAT, W2, st, lambda l, b_: ctx[b_][l], 3)
+    assert np.array_equal(a["logits"][:, 0], b["logits"][:, 0])
+    assert not np.allclose(a["logits"][:, 1], b["logits"][:, 1])
+
+
 # ---------------------------------------------------------------- sampled verify (temperature > 0)
 
 def test_draw_inverse_cdf_brute_force():
