@@ -151,6 +151,37 @@ def catchup_latency(pe, torch, w, cfg_args, dev, kc, vc, d, stream, reps):
     return out
 
 
+def concat_rows_latency(pe, torch, w, cfg_args, kc, vc, d, stream, reps):
+    """Latency of the draft step with concatenated input rows ([embedding || hidden] into layer 0's
+    attention; its QKV reads 2d columns) beside the same workload's summed rows: a drafter of the same
+    shape with row_concat set (own seeded weights), the same requests and contexts. bf16 drafters only."""
+    import dataclasses
+    from synth.device import upload_weights
+    s = w.shape
+    if s.dtype != "bf16":
+        return None
+    sc = dataclasses.replace(s, name=s.name + "-concat", row_concat=True, weight_seed=s.weight_seed + 100)
+    wc = dataclasses.replace(w, shape=sc)
+    dev, _ = upload_weights(sc)
+    ctx = pe.pe_init(pe.make_config(**cfg_args(wc)), pe.make_weights(dev, sc.n_layers), pe.make_kv(kc, vc),
+                     stream.cuda_stream)
+    tok = torch.empty((w.B, w.K), dtype=torch.int32, device="cuda")
+
+    def call():
+        pe.pe_draft_step(ctx, w.B, w.K, d["req_slot"], d["seq_len"], d["last_token"], d["target_hidden"], tok, None)
+    for _ in range(3):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    pe.pe_destroy(ctx)
+    del dev
+    return {"B": w.B, "K": w.K, "draft_us": 1e3 * e0.elapsed_time(e1) / reps}
+
+
 def kernel_source_digest():
     """sha256 over the sources that define the projection kernels (the LM head among them)."""
     h = hashlib.sha256()
@@ -329,6 +360,7 @@ def main():
 
     depth = None if args.no_depth_sweep else latency_vs_depth(pe, torch, w, config_args, dev, kc, vc, d, stream, reps)
     catchup = catchup_latency(pe, torch, w, config_args, dev, kc, vc, d, stream, reps)
+    concat = concat_rows_latency(pe, torch, w, config_args, kc, vc, d, stream, reps)
 
     if args.copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
@@ -374,6 +406,7 @@ def main():
         "device_flags": flags,
         "draft_latency_vs_depth": depth,
         "catchup_step": catchup,
+        "concat_rows_step": concat,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, state, T_host, args.cpu_seconds)

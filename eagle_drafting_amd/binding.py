@@ -32,7 +32,7 @@ class pe_config(ctypes.Structure):
     _fields_ = [("n_layers", c_int32), ("d_model", c_int32), ("n_q_heads", c_int32), ("n_kv_heads", c_int32),
                 ("head_dim", c_int32), ("ffn_dim", c_int32), ("vocab", c_int32), ("rms_eps", c_float),
                 ("rope_base", c_float), ("dtype", c_int32), ("max_batch", c_int32), ("max_k", c_int32),
-                ("max_ctx", c_int32), ("n_slots", c_int32)]
+                ("max_ctx", c_int32), ("n_slots", c_int32), ("row_concat", c_int32)]
 
 
 _L = c_void_p * PE_MAX_LAYERS
@@ -41,7 +41,7 @@ _L = c_void_p * PE_MAX_LAYERS
 class pe_weights(ctypes.Structure):
     _fields_ = [("fc", c_void_p), ("embed", c_void_p), ("emb_mask", c_void_p), ("h_shared", c_void_p),
                 ("final_norm", c_void_p), ("lm_head", c_void_p), ("attn_norm", _L), ("wqkv", _L), ("wo", _L),
-                ("mlp_norm", _L), ("wgate", _L), ("wup", _L), ("wdown", _L)]
+                ("mlp_norm", _L), ("wgate", _L), ("wup", _L), ("wdown", _L), ("embed_norm", c_void_p)]
 
 
 class pe_kv(ctypes.Structure):
@@ -201,9 +201,10 @@ def pe_profile_read(ctx, which: int):
 # ---- struct builders (marshalling helpers) ----------------------------------------------------------
 
 def make_config(n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab, dtype, max_batch, max_k,
-                max_ctx, n_slots, rms_eps=1e-6, rope_base=10000.0) -> pe_config:
+                max_ctx, n_slots, rms_eps=1e-6, rope_base=10000.0, row_concat=0) -> pe_config:
     return pe_config(n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab, rms_eps, rope_base,
-                     PE_BF16 if dtype in ("bf16", PE_BF16) else PE_F32, max_batch, max_k, max_ctx, n_slots)
+                     PE_BF16 if dtype in ("bf16", PE_BF16) else PE_F32, max_batch, max_k, max_ctx, n_slots,
+                     int(row_concat))
 
 
 def make_weights(t: dict, n_layers: int) -> pe_weights:
@@ -214,6 +215,8 @@ def make_weights(t: dict, n_layers: int) -> pe_weights:
     for l in range(n_layers):
         for name in ("attn_norm", "wqkv", "wo", "mlp_norm", "wgate", "wup", "wdown"):
             getattr(w, name)[l] = _ptr(t[f"l{l}.{name}"])
+    if "embed_norm" in t:
+        w.embed_norm = _ptr(t["embed_norm"])
     return w
 
 

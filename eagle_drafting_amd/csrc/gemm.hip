@@ -389,16 +389,20 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
       float x0 = 0.f, ph = 0.f;
       if (n < N) {
         const float e = tok_ok ? bf16_to_f32(g.embed[(size_t)tok * N + n]) : 0.f;
-        ph = bf16_to_f32(g.h_shared[n]) + bf16_to_f32(g.emb_mask[n]);
-        x0 = real ? Y(0, r, c) + e : ph;
+        const float em = bf16_to_f32(g.emb_mask[n]);
+        // concatenated rows keep the embedding half apart (Xe); summed rows add it to the hidden half
+        ph = bf16_to_f32(g.h_shared[n]) + (g.Xe ? 0.f : em);
+        x0 = real ? Y(0, r, c) + (g.Xe ? 0.f : e) : ph;
         const float gn = bf16_to_f32(g.gain_next[n]);
         g.Xout[(size_t)(b * Kr + i) * N + n] = x0;
         g.XGout[(size_t)(b * Kr + i) * N + n] = f32_to_bf16(x0 * gn);
+        if (g.Xe) g.Xe[(size_t)(b * Kr + i) * N + n] = real ? e : em;
         const bf16_t phg = f32_to_bf16(ph * gn);
         if (i == 0)
           for (int j = R; j < Kr; ++j) {
             g.Xout[(size_t)(b * Kr + j) * N + n] = ph;
             g.XGout[(size_t)(b * Kr + j) * N + n] = phg;
+            if (g.Xe) g.Xe[(size_t)(b * Kr + j) * N + n] = em;
           }
       }
       float s0 = x0 * x0, s1 = ph * ph;
@@ -525,6 +529,7 @@ hipError_t launch_gemm(const GemmPlan& p, GemmArgs a, int a_mode, int epi, hipSt
   if (a_mode == A_BF16 && epi == EPI_RESID) return launch_split_nw<A_BF16, EPI_RESID>(p, a, st);
   if (a_mode == A_BF16 && epi == EPI_ROWS) return launch_split_nw<A_BF16, EPI_ROWS>(p, a, st);
   if (a_mode == A_NORM && epi == EPI_QKV) return launch_split_nw<A_NORM, EPI_QKV>(p, a, st);
+  if (a_mode == A_BF16 && epi == EPI_QKV) return launch_split_nw<A_BF16, EPI_QKV>(p, a, st);
   if (a_mode == A_NORM && epi == EPI_SWIGLU) return launch_split_nw<A_NORM, EPI_SWIGLU>(p, a, st);
   return hipErrorInvalidValue;
 }

@@ -361,15 +361,19 @@ __device__ void tile_epilogue(const GemmArgs& g, const float* Cs, const float* s
             const int tok = g.last_token[m];
             const bool tok_ok = tok >= 0 && tok < g.V;
             if (real && !tok_ok && h == 0 && ng == 0) raise_flag(g.flags, PE_FLAG_TOKEN);
+            // concatenated rows keep the embedding half apart (Xe); summed rows add it to the hidden half
+            float xe[4], xe1[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const bool ok = n + e < N;
-              x1[e] = ok ? bf16_to_f32(g.h_shared[n + e]) + bf16_to_f32(g.emb_mask[n + e]) : 0.f;
-              x[e] = !ok ? 0.f : real ? vv[e] + (tok_ok ? bf16_to_f32(g.embed[(size_t)tok * N + n + e]) : 0.f) : x1[e];
+              xe1[e] = ok ? bf16_to_f32(g.emb_mask[n + e]) : 0.f;
+              xe[e] = ok && real && tok_ok ? bf16_to_f32(g.embed[(size_t)tok * N + n + e]) : real ? 0.f : xe1[e];
+              x1[e] = ok ? bf16_to_f32(g.h_shared[n + e]) + (g.Xe ? 0.f : xe1[e]) : 0.f;
+              x[e] = !ok ? 0.f : real ? vv[e] + (g.Xe ? 0.f : xe[e]) : x1[e];
               sq0 += x[e] * x[e];
               sq1 += x1[e] * x1[e];
             }
-            auto put = [&](int lr, const float* src) {  // layer row b Kr + lr
+            auto put = [&](int lr, const float* src, const float* srce) {  // layer row b Kr + lr
               float* xr = g.Xout + (size_t)(b * Kr + lr) * N;
               bf16_t* xg = g.XGout + (size_t)(b * Kr + lr) * N;
 #pragma unroll
@@ -377,11 +381,12 @@ __device__ void tile_epilogue(const GemmArgs& g, const float* Cs, const float* s
                 if (n + e < N) {
                   xr[n + e] = src[e];
                   xg[n + e] = f32_to_bf16(src[e] * gn[e]);
+                  if (g.Xe) g.Xe[(size_t)(b * Kr + lr) * N + n + e] = srce[e];
                 }
             };
-            put(i, x);
+            put(i, x, xe);
             if (i == 0)
-              for (int j = R; j < Kr; ++j) put(j, x1);
+              for (int j = R; j < Kr; ++j) put(j, x1, xe1);
           }
         }
         // one partial sum of squares per row and 128-column workgroup tile
@@ -674,6 +679,7 @@ static hipError_t launch_stream_rb(const GemmPlan& p, const GemmArgs& a, int a_m
   if (a_mode == A_BF16 && epi == EPI_RESID) hipLaunchKernelGGL((gemm_stream_kernel<A_BF16, EPI_RESID, false, RB, CH, NWB>), grid, block, 0, st, a);
   else if (a_mode == A_BF16 && epi == EPI_ROWS) hipLaunchKernelGGL((gemm_stream_kernel<A_BF16, EPI_ROWS, false, RB, CH, NWB>), grid, block, 0, st, a);
   else if (a_mode == A_NORM && epi == EPI_QKV) hipLaunchKernelGGL((gemm_stream_kernel<A_NORM, EPI_QKV, false, RB, CH, NWB>), grid, block, 0, st, a);
+  else if (a_mode == A_BF16 && epi == EPI_QKV) hipLaunchKernelGGL((gemm_stream_kernel<A_BF16, EPI_QKV, false, RB, CH, NWB>), grid, block, 0, st, a);
   else if (a_mode == A_NORM && epi == EPI_SWIGLU) hipLaunchKernelGGL((gemm_stream_kernel<A_NORM, EPI_SWIGLU, false, RB, CH, NWB>), grid, block, 0, st, a);
   else if (a_mode == A_NORM && epi == EPI_ARGMAX) hipLaunchKernelGGL((gemm_stream_kernel<A_NORM, EPI_ARGMAX, false, RB, CH, NWB>), grid, block, 0, st, a);
   else return hipErrorInvalidValue;
@@ -723,6 +729,7 @@ hipError_t launch_gemm_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode, i
   if (a_mode == A_BF16 && epi == EPI_RESID) hipLaunchKernelGGL((gemm_tiled_kernel<A_BF16, EPI_RESID, false>), grid, block, 0, st, a);
   else if (a_mode == A_BF16 && epi == EPI_ROWS) hipLaunchKernelGGL((gemm_tiled_kernel<A_BF16, EPI_ROWS, false>), grid, block, 0, st, a);
   else if (a_mode == A_NORM && epi == EPI_QKV) hipLaunchKernelGGL((gemm_tiled_kernel<A_NORM, EPI_QKV, false>), grid, block, 0, st, a);
+  else if (a_mode == A_BF16 && epi == EPI_QKV) hipLaunchKernelGGL((gemm_tiled_kernel<A_BF16, EPI_QKV, false>), grid, block, 0, st, a);
   else if (a_mode == A_NORM && epi == EPI_SWIGLU) hipLaunchKernelGGL((gemm_tiled_kernel<A_NORM, EPI_SWIGLU, false>), grid, block, 0, st, a);
   else if (a_mode == A_NORM && epi == EPI_ARGMAX) hipLaunchKernelGGL((gemm_tiled_kernel<A_NORM, EPI_ARGMAX, false>), grid, block, 0, st, a);
   else return hipErrorInvalidValue;

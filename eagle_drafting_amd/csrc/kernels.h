@@ -73,8 +73,10 @@ struct GemmArgs {
   uint16_t* Q; uint16_t* Kc; uint16_t* Vc;
   const int* seq_len; const int* req_slot; const float2* rope;
   int Kdraft, Hq, Hkv, hd, max_ctx, n_slots; int* flags;
-  // EPI_ROWS
+  // EPI_ROWS; with Xe (concatenated rows) the embedding half is written to Xe [rows, d] instead of being
+  // added to the hidden half in Xout
   const int* last_token; const uint16_t* embed; const uint16_t* emb_mask; const uint16_t* h_shared; int V;
+  float* Xe;
   // EPI_ARGMAX: per (row, workgroup) best (value, index); optional fp32 logits, row m at logits + m * ldz
   // (ldz = 0 means N)
   float* am_val; int* am_idx; float* logits; int ldz;
@@ -110,6 +112,9 @@ hipError_t launch_gemm_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode, i
 hipError_t launch_ar_rows(float* X, uint16_t* XG, float* ssq, const uint16_t* embed, const uint16_t* gain,
                           const int* prev_tok, int* draft_tokens, int K, int pass, const int* seq_len, int* seq_cur,
                           int B, int d, int V, int* flags, hipStream_t st);
+// Concatenated rows: U [M, 2d] = [bf16(RMSNorm(Xe) * g_e) || bf16(RMSNorm(X) * g_h)], one row per workgroup.
+hipError_t launch_concat_norm(const float* X, const float* Xe, const uint16_t* g_h, const uint16_t* g_e, uint16_t* U,
+                              int M, int d, float eps, hipStream_t st);
 hipError_t launch_rows_ssq(const float* rows, float* X, float* ssq, uint16_t* XG, const uint16_t* gain, int M, int d,
                            hipStream_t st);
 // fp32 weights, unpacked [N, Kd]: out[m * ldo + n]

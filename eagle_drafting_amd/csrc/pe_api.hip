@@ -52,6 +52,8 @@ struct pe_ctx {
   int* flags = nullptr;
   int* ar_tok = nullptr;   // autoregressive drafting: the token each request drafted in the latest pass [max_batch]
   int* ar_seq = nullptr;   // ... and the positions of the current pass [max_batch]
+  float* Xe = nullptr;     // concatenated rows: embedding halves [Mmax, d] fp32
+  void* Ucat = nullptr;    // concatenated rows: layer 0's normalised operand [Mmax, 2d] bf16
 
   std::string err;
 
@@ -92,6 +94,8 @@ static pe_status check_cfg(const pe_config* c, std::string& why) {
   if (c->dtype == PE_BF16 && (c->n_q_heads / c->n_kv_heads) * (c->max_k + 1) > 128) {
     why = "(n_q_heads / n_kv_heads) * (max_k + 1) must be <= 128"; return PE_ERR_UNSUPPORTED;
   }
+  if (c->row_concat != 0 && c->row_concat != 1) { why = "row_concat must be 0 or 1"; return PE_ERR_INVALID; }
+  if (c->row_concat && c->dtype != PE_BF16) { why = "concatenated rows need a bf16 drafter"; return PE_ERR_UNSUPPORTED; }
   if (c->dtype == PE_F32 && c->max_ctx > 12288) { why = "fp32 drafter supports max_ctx <= 12288"; return PE_ERR_UNSUPPORTED; }
   if ((long long)c->n_slots * c->n_kv_heads * c->max_ctx * c->head_dim > (1LL << 40)) {
     why = "KV cache too large"; return PE_ERR_UNSUPPORTED;
@@ -146,6 +150,7 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
   const pe_config& c = *cfg;
   if (!w->fc || !w->embed || !w->emb_mask || !w->h_shared || !w->final_norm || !w->lm_head)
     return fail(nullptr, PE_ERR_INVALID, "a global weight pointer is NULL");
+  if (c.row_concat && !w->embed_norm) return fail(nullptr, PE_ERR_INVALID, "row_concat needs embed_norm");
   for (int l = 0; l < c.n_layers; ++l)
     if (!w->attn_norm[l] || !w->wqkv[l] || !w->wo[l] || !w->mlp_norm[l] || !w->wgate[l] || !w->wup[l] ||
         !w->wdown[l] || !kv->k[l] || !kv->v[l])
@@ -185,7 +190,7 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
     const size_t o_fc = take(packed_bytes(d, 3 * d));
     size_t o_qkv[PE_MAX_LAYERS], o_o[PE_MAX_LAYERS], o_gu[PE_MAX_LAYERS], o_dn[PE_MAX_LAYERS];
     for (int l = 0; l < c.n_layers; ++l) {
-      o_qkv[l] = take(packed_bytes(qkvd, d));
+      o_qkv[l] = take(packed_bytes(qkvd, l == 0 && c.row_concat ? 2 * d : d));
       o_o[l] = take(packed_bytes(d, qd));
       o_gu[l] = take(2 * packed_bytes(F, d));
       o_dn[l] = take(packed_bytes(d, F));
@@ -207,7 +212,8 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
     bool ok = chk(launch_pack_bf16(w->fc, nullptr, d, 3 * d, PACK_PLAIN, 0, base + o_fc, st));
     ctx->p_fc = base + o_fc;
     for (int l = 0; l < c.n_layers && ok; ++l) {
-      ok = ok && chk(launch_pack_bf16(w->wqkv[l], nullptr, qkvd, d, PACK_PAIRS, hd, base + o_qkv[l], st));
+      ok = ok && chk(launch_pack_bf16(w->wqkv[l], nullptr, qkvd, l == 0 && c.row_concat ? 2 * d : d, PACK_PAIRS, hd,
+                                      base + o_qkv[l], st));
       ok = ok && chk(launch_pack_bf16(w->wo[l], nullptr, d, qd, PACK_PLAIN, 0, base + o_o[l], st));
       ok = ok && chk(launch_pack_bf16(w->wgate[l], w->wup[l], F, d, PACK_GATEUP, 0, base + o_gu[l], st));
       ok = ok && chk(launch_pack_bf16(w->wdown[l], nullptr, d, F, PACK_PLAIN, 0, base + o_dn[l], st));
@@ -239,8 +245,9 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
       GemmPlan pl = plan_gemm(M, V, d, true);
       am_floats = std::max(am_floats, (size_t)M * pl.ngroups);
       // K-split partials of the layer projections and of the row build (B rows, or B R for a catch-up step)
-      const int shapes[5][2] = {{qkvd, d}, {d, qd}, {2 * F, d}, {d, F}, {d, 3 * d}};
-      for (int sh = 0; sh < 5; ++sh) {
+      // (and layer 0's QKV over concatenated rows, 2d wide)
+      const int shapes[6][2] = {{qkvd, d}, {d, qd}, {2 * F, d}, {d, F}, {d, 3 * d}, {qkvd, 2 * d}};
+      for (int sh = 0; sh < (c.row_concat ? 6 : 5); ++sh) {
         const GemmPlan ps = plan_gemm(M, shapes[sh][0], shapes[sh][1], false);
         if (ps.ksplit > 1) part_floats = std::max(part_floats, (size_t)ps.ksplit * M * shapes[sh][0]);
       }
@@ -273,7 +280,8 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
                oL = take(ctx->bf16 ? 0 : (size_t)Mmax * V * 4), oR = take((size_t)c.max_ctx * (hd / 2) * 8),
                oS = take((size_t)Mmax * nssq * 4), oF = take(256), oK = take(part_floats * 4),
                oArT = take((size_t)c.max_batch * 4), oArS = take((size_t)c.max_batch * 4),
-               oSm = take((size_t)2 * c.max_batch * (c.max_k + 1) * plan_sample_chunks(V) * 4);
+               oSm = take((size_t)2 * c.max_batch * (c.max_k + 1) * plan_sample_chunks(V) * 4),
+               oXe = take(c.row_concat ? (size_t)Mmax * d * 4 : 0), oUc = take(c.row_concat ? (size_t)Mmax * 2 * d * 2 : 0);
   if (hipMalloc((void**)&ctx->ws, off) != hipSuccess) {
     free_ctx(ctx);
     return fail(nullptr, PE_ERR_OOM, "hipMalloc of workspace failed");
@@ -297,6 +305,8 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
   ctx->ar_tok = (int*)(b + oArT);
   ctx->ar_seq = (int*)(b + oArS);
   ctx->samp = (float*)(b + oSm);
+  ctx->Xe = c.row_concat ? (float*)(b + oXe) : nullptr;
+  ctx->Ucat = c.row_concat ? (void*)(b + oUc) : nullptr;
 
   hipError_t r = launch_rope_table(ctx->rope, c.max_ctx, hd, (double)c.rope_base, ctx->stream);
   if (r == hipSuccess) r = hipMemsetAsync(ctx->flags, 0, 256, ctx->stream);
@@ -443,6 +453,7 @@ static pe_status rows_bf16(pe_ctx* ctx, int32_t B, int32_t Kr, const int32_t* la
   a.A = (const uint16_t*)target_hidden; a.lda = 3 * d;
   a.Kdraft = Kr; a.last_token = last_token; a.V = c.vocab;
   a.rows_real = R; a.n_real = n_real;
+  a.Xe = ctx->Xe;
   a.embed = (const uint16_t*)ctx->w.embed; a.emb_mask = (const uint16_t*)ctx->w.emb_mask;
   a.h_shared = (const uint16_t*)ctx->w.h_shared;
   a.gain_next = (const uint16_t*)ctx->w.attn_norm[0];
@@ -467,16 +478,20 @@ static pe_status layers_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* r
   uint16_t* XG = (uint16_t*)ctx->U;
   const GemmArgs base = gemm_base(ctx);
   for (int l = 0; l < c.n_layers; ++l) {
-    {  // a2-a4: RMSNorm, QKV, RoPE, KV append
+    {  // a2-a4: RMSNorm, QKV, RoPE, KV append (concatenated rows: layer 0 reads the normalised 2d-wide rows)
+      const bool cat = l == 0 && ctx->Ucat;
       GemmArgs a = base;
-      a.M = M; a.Kd = d; a.N = qkvd;
-      a.A = XG; a.lda = d;
+      a.M = M; a.Kd = cat ? 2 * d : d; a.N = qkvd;
+      a.A = cat ? (const uint16_t*)ctx->Ucat : XG; a.lda = a.Kd;
       a.Wp_raw = ctx->p_qkv[l];
       a.Q = (uint16_t*)ctx->Qb; a.Kc = (uint16_t*)ctx->kv.k[l]; a.Vc = (uint16_t*)ctx->kv.v[l];
       a.seq_len = seq_len; a.req_slot = req_slot; a.rope = ctx->rope;
       a.Kdraft = K; a.Hq = Hq; a.Hkv = Hkv; a.hd = hd; a.max_ctx = c.max_ctx; a.n_slots = c.n_slots;
       a.nssq = nssq;
-      LAUNCH(launch_gemm(plan_gemm(M, qkvd, d, false), a, A_NORM, EPI_QKV, st));
+      if (cat)
+        LAUNCH(launch_concat_norm(ctx->X, ctx->Xe, (const uint16_t*)w.attn_norm[0], (const uint16_t*)w.embed_norm,
+                                  (uint16_t*)ctx->Ucat, M, d, c.rms_eps, st));
+      LAUNCH(launch_gemm(plan_gemm(M, qkvd, a.Kd, false), a, cat ? A_BF16 : A_NORM, EPI_QKV, st));
     }
     // a5: attention
     AttnPlan ap = plan_attention(B, K, Hq, Hkv, hd, c.max_ctx);
@@ -638,6 +653,7 @@ extern "C" pe_status pe_draft_ar(pe_ctx* ctx, int32_t B, int32_t K, const int32_
   if (!ctx) return fail(nullptr, PE_ERR_INVALID, "ctx is NULL");
   const pe_config& c = ctx->cfg;
   if (!ctx->bf16) return fail(ctx, PE_ERR_UNSUPPORTED, "autoregressive drafting needs a bf16 drafter");
+  if (c.row_concat) return fail(ctx, PE_ERR_UNSUPPORTED, "autoregressive drafting with concatenated rows");
   if (B < 1 || B > c.max_batch) return fail(ctx, PE_ERR_INVALID, "B out of [1, max_batch]");
   if (K < 1 || K > c.max_k) return fail(ctx, PE_ERR_INVALID, "K out of [1, max_k]");
   if (!req_slot || !seq_len || !draft_tokens || !last_token || !target_hidden)
@@ -653,6 +669,7 @@ extern "C" pe_status pe_draft_catchup(pe_ctx* ctx, int32_t B, int32_t K, int32_t
   if (!ctx) return fail(nullptr, PE_ERR_INVALID, "ctx is NULL");
   const pe_config& c = ctx->cfg;
   if (!ctx->bf16) return fail(ctx, PE_ERR_UNSUPPORTED, "catch-up steps need a bf16 drafter");
+  if (c.row_concat) return fail(ctx, PE_ERR_UNSUPPORTED, "catch-up steps with concatenated rows");
   if (B < 1 || B > c.max_batch) return fail(ctx, PE_ERR_INVALID, "B out of [1, max_batch]");
   if (K < 1 || K > c.max_k) return fail(ctx, PE_ERR_INVALID, "K out of [1, max_k]");
   if (R < 1 || R + K > c.max_k + 1) return fail(ctx, PE_ERR_INVALID, "R out of [1, max_k + 1 - K]");
@@ -666,6 +683,7 @@ extern "C" pe_status pe_draft_catchup(pe_ctx* ctx, int32_t B, int32_t K, int32_t
 extern "C" pe_status pe_draft_rows(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req_slot, const int32_t* seq_len,
                                    const float* rows, int32_t* draft_tokens, float* logits) {
   if (ctx && !rows) return fail(ctx, PE_ERR_INVALID, "rows is NULL");
+  if (ctx && ctx->cfg.row_concat) return fail(ctx, PE_ERR_UNSUPPORTED, "caller rows with concatenated rows");
   return run_draft(ctx, B, K, req_slot, seq_len, nullptr, nullptr, rows, draft_tokens, logits);
 }
 

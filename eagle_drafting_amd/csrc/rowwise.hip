@@ -230,4 +230,47 @@ hipError_t launch_rope_table(float2* cs, int max_ctx, int hd, double base, hipSt
   return hipGetLastError();
 }
 
+// Concatenated input rows: U[m] = [bf16(xe * g_e / rms(xe)) || bf16(x * g_h / rms(x))], rms(v) =
+// sqrt(mean(v^2) + eps) over each d-wide half (the embedding half first). One workgroup per row; the two
+// sums of squares are reduced in a fixed order (per thread, then per wave by xor-shuffles, then the four
+// waves in order), so the result does not depend on scheduling.
+__global__ __launch_bounds__(256) void concat_norm_kernel(const float* __restrict__ X, const float* __restrict__ Xe,
+                                                          const bf16_t* __restrict__ g_h,
+                                                          const bf16_t* __restrict__ g_e, bf16_t* __restrict__ U,
+                                                          int d, float eps) {
+  __shared__ float red[2][4];
+  const int m = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const float* x = X + (size_t)m * d;
+  const float* xe = Xe + (size_t)m * d;
+  float sh = 0.f, se = 0.f;
+  for (int c = tid; c < d; c += 256) {
+    sh += x[c] * x[c];
+    se += xe[c] * xe[c];
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    sh += __shfl_xor(sh, off, PE_WAVE);
+    se += __shfl_xor(se, off, PE_WAVE);
+  }
+  if (lane == 0) {
+    red[0][wave] = sh;
+    red[1][wave] = se;
+  }
+  __syncthreads();
+  const float th = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
+  const float te = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+  const float ih = rsqrtf(th / (float)d + eps), ie = rsqrtf(te / (float)d + eps);
+  bf16_t* u = U + (size_t)m * 2 * d;
+  for (int c = tid; c < d; c += 256) {
+    u[c] = f32_to_bf16(xe[c] * ie * bf16_to_f32(g_e[c]));
+    u[d + c] = f32_to_bf16(x[c] * ih * bf16_to_f32(g_h[c]));
+  }
+}
+
+hipError_t launch_concat_norm(const float* X, const float* Xe, const uint16_t* g_h, const uint16_t* g_e, uint16_t* U,
+                              int M, int d, float eps, hipStream_t st) {
+  hipLaunchKernelGGL(concat_norm_kernel, dim3(M), dim3(256), 0, st, X, Xe, (const bf16_t*)g_h, (const bf16_t*)g_e,
+                     (bf16_t*)U, d, eps);
+  return hipGetLastError();
+}
+
 }  // namespace pe

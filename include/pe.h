@@ -67,6 +67,13 @@ typedef struct pe_config {
   int32_t max_k;      /* largest K passed to any call, 1..PE_MAX_K */
   int32_t max_ctx;    /* positions per KV slot */
   int32_t n_slots;    /* KV slots */
+  int32_t row_concat; /* 0: input rows are sums (embedding + hidden), width d. 1: rows are the concatenation
+                         [embedding || hidden] (the pages' wording for positions 1..K): layer 0's attention
+                         reads the 2d-wide row, RMSNorm applied to each half with its own gain (embed_norm
+                         for the embedding, attn_norm[0] for the hidden), and the residual stream is the
+                         hidden half; wqkv[0] is then [(Hq + 2 Hkv) hd, 2d]. bf16 drafters and pe_draft_step
+                         only: caller rows, autoregressive drafting and catch-up steps return
+                         PE_ERR_UNSUPPORTED on such a ctx. */
 } pe_config;
 
 /* Drafter weights (device, element type = dtype). Must stay valid and unchanged until pe_destroy:
@@ -86,6 +93,7 @@ typedef struct pe_weights {
   const void* wgate[PE_MAX_LAYERS];     /* [F, d] */
   const void* wup[PE_MAX_LAYERS];       /* [F, d] */
   const void* wdown[PE_MAX_LAYERS];     /* [d, F] */
+  const void* embed_norm;  /* [d]: RMSNorm gain of the embedding half (row_concat only, else ignored) */
 } pe_weights;
 
 /* Drafter KV cache (device, element type = dtype), one K and one V tensor per layer, each
@@ -108,7 +116,8 @@ pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe_kv* kv, vo
 /* The parallel draft step (solution overview, step 2). For request b (0 <= b < B):
  *   row 0     = fc . concat(target_hidden[b]) + embed[last_token[b]]
  *   rows 1..K-1 = h_shared + emb_mask
- * at positions seq_len[b] + j. All B*K rows go through the drafter layers (RMSNorm, GQA attention over
+ * (with row_concat: row 0 = [embed[last_token[b]] || fc . concat(target_hidden[b])], rows 1..K-1 =
+ * [emb_mask || h_shared]) at positions seq_len[b] + j. All B*K rows go through the drafter layers (RMSNorm, GQA attention over
  * the request's cache slot with a causal mask inside the K block, SwiGLU MLP) and the LM head;
  * draft_tokens[b*K + j] = argmax over the vocabulary (lowest index among equal maxima).
  * One more placeholder row (h_shared + emb_mask at position seq_len[b] + K) runs after the K draft rows;

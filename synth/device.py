@@ -53,4 +53,4 @@ def config_args(w: Workload, max_batch=None, max_k=None, max_ctx=None, n_slots=N
     return dict(n_layers=s.n_layers, d_model=s.d_model, n_q_heads=s.n_q_heads, n_kv_heads=s.n_kv_heads,
                 head_dim=s.head_dim, ffn_dim=s.ffn_dim, vocab=s.vocab, dtype=s.dtype,
                 max_batch=max_batch or w.B, max_k=max_k or w.K, max_ctx=max_ctx or w.max_ctx,
-                n_slots=n_slots or w.n_slots, rms_eps=s.rms_eps, rope_base=s.rope_base)
+                n_slots=n_slots or w.n_slots, rms_eps=s.rms_eps, rope_base=s.rope_base, row_concat=int(s.row_concat))

@@ -97,7 +97,7 @@ def to_f64(arr: np.ndarray, dtype: str) -> np.ndarray:
 
 
 # tensor codes for the per-tensor child generators
-_CODES = {"fc": 1, "embed": 2, "emb_mask": 3, "h_shared": 4, "final_norm": 5, "lm_head": 6,
+_CODES = {"fc": 1, "embed": 2, "emb_mask": 3, "h_shared": 4, "final_norm": 5, "lm_head": 6, "embed_norm": 7,
           "attn_norm": 10, "wqkv": 11, "wo": 12, "mlp_norm": 13, "wgate": 14, "wup": 15, "wdown": 16}
 
 
@@ -113,6 +113,9 @@ def weight_shapes(s: DrafterShape) -> dict:
         shapes[f"l{l}.wgate"] = (F, d)
         shapes[f"l{l}.wup"] = (F, d)
         shapes[f"l{l}.wdown"] = (d, F)
+    if s.row_concat:
+        shapes["l0.wqkv"] = (s.qkv_dim, 2 * d)
+        shapes["embed_norm"] = (d,)
     return shapes
 
 

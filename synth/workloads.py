@@ -27,6 +27,9 @@ class DrafterShape:
     weight_seed: int = 0  # seed of this synthetic drafter's weights (shared by every workload on it)
     rms_eps: float = 1e-6
     rope_base: float = 10000.0
+    # input rows as the concatenation [embedding || hidden] (2d wide into layer 0's attention) instead of
+    # their sum; layer 0's wqkv is then [qkv_dim, 2d] and the embedding half has its own RMSNorm gain
+    row_concat: bool = False
 
     @property
     def group(self) -> int:
@@ -51,6 +54,8 @@ class DrafterShape:
 
 TINY_FP32 = DrafterShape("tiny-fp32", 1, 256, 4, 4, 64, 512, 4096, "f32", 1000)
 QWEN3_CODER = DrafterShape("qwen3-coder-30b-a3b-shaped", 4, 2048, 32, 4, 128, 6144, 151936, "bf16", 2000)
+QWEN3_CODER_CONCAT = DrafterShape("qwen3-coder-30b-a3b-shaped-concat", 4, 2048, 32, 4, 128, 6144, 151936, "bf16",
+                                  2100, row_concat=True)
 GPT_OSS_20B = DrafterShape("gpt-oss-20b-shaped", 4, 2880, 64, 8, 64, 8640, 201088, "bf16", 5000)
 
 

@@ -134,3 +134,75 @@ def test_multistep_churn_parity(w):
 @pytest.mark.parametrize("w,tau", [(MULTI[0], 0.2), (MULTI[1], 0.1)], ids=lambda v: getattr(v, "name", str(v)))
 def test_multistep_churn_sampled_verify(w, tau):
     _run(w, tau)
+
+
+def test_multistep_catchup_parity():
+    """State-advancing steps with catch-up: each step runs the previous verify's emitted tokens as real rows
+    (with fresh target hiddens for each) and then the placeholders (pe_draft_catchup); the real rows' K/V
+    become context, so the oracle grows each request's context by its own real rows only. Drafts against
+    the oracle every step; verify bit-exact; the next step starts at P + n_real with the emitted tokens."""
+    import torch
+    from synth.device import to_device
+    from synth.inputs import catchup_inputs
+
+    w = Workload("qwen3coder-bf16-B4-K3-L256to1024-catchup-steps", QWEN3_CODER, 4, 3, (256, 1024), (0.5, 0.9), 2200,
+                 steps=6)
+    s = w.shape
+    tol = TOL[s.dtype]
+    B, K, R = w.B, w.K, w.K + 1
+    dr = GpuDrafter(w, max_k=R + K - 1)
+    W64 = shape_weights64(s)
+    st = dr.state
+    L0 = [int(x) for x in st["seq_len"]]
+    ext = [[[np.zeros((s.n_kv_heads, 0, s.head_dim)) for _ in range(s.n_layers)] for _ in range(2)] for _ in range(B)]
+    pos = np.array(L0, dtype=np.int32)                      # position of each request's first real row
+    n_real = np.ones(B, dtype=np.int32)
+    tokens = np.zeros((B, R), dtype=np.int32)
+    tokens[:, 0] = st["last_token"]
+    hid = catchup_inputs(w, R, 0)["target_hidden"]
+    hid[:, 0] = st["target_hidden"]
+    try:
+        for step in range(3):
+            log(f"catch-up step {step}: positions {pos.tolist()} n_real {n_real.tolist()}")
+            pos_dev = to_device(pos, "i32")
+            draft_dev = torch.full((B, K), -1, dtype=torch.int32, device="cuda")
+            z = torch.empty((B, K, s.vocab), dtype=torch.float32, device="cuda")
+            dr.pe.pe_draft_catchup(dr.ctx, B, K, R, dr.d["req_slot"], pos_dev, to_device(n_real, "i32"),
+                                   to_device(tokens, "i32"), to_device(hid, s.dtype), draft_dev, z)
+            torch.cuda.synchronize()
+            draft = draft_dev.cpu().numpy()
+
+            def ctx(l, b):
+                pre = [to_f64(kv_block(w, l, kind, b, L0[b]), s.dtype) for kind in (0, 1)]
+                return tuple(np.concatenate([pre[kind], ext[b][kind][l]], axis=1) for kind in (0, 1))
+
+            ref = O.draft_step_catchup(s, W64, {"tokens": tokens, "target_hidden": to_f64(hid, s.dtype),
+                                                "n_real": n_real, "seq_len": pos}, ctx, K)
+            err = check_logits(z.cpu().numpy(), ref["logits"], tol, f"catch-up step {step} logits")
+            strict, exempt = check_tokens(draft, ref["logits"], tol, f"catch-up step {step} tokens")
+            log(f"  draft parity: max row-rel err {err:.2e}, {strict}/{B * K} tokens equal, {exempt} near-ties")
+
+            T = plant_target_logits(w, draft, np.full(B, 0.7), step)
+            fin = np.zeros(B, dtype=np.uint8)
+            got = run_verify(dr.pe, dr.ctx, B, K, to_device(T, s.dtype), draft_dev, None, dr.d["req_slot"], pos_dev)
+            v, c = check_verify(got, to_f64(T, s.dtype), draft, fin, st["req_slot"], pos)
+            log(f"  verify: accept_len {v['accept_len'].tolist()}")
+
+            # the real rows' K/V join the context; the emitted tokens are the next step's real rows
+            for b in range(B):
+                r = int(n_real[b])
+                for l in range(s.n_layers):
+                    for kind, new in ((0, ref["k_new"][l]), (1, ref["v_new"][l])):
+                        ext[b][kind][l] = np.concatenate([ext[b][kind][l], new[b, :r].transpose(1, 0, 2)], axis=1)
+            cu = c["cu_accept"]
+            nxt = catchup_inputs(w, R, step + 1)
+            for b in range(B):
+                a = int(v["accept_len"][b])
+                tokens[b, :a] = c["out_tokens"][cu[b]:cu[b] + a]
+                tokens[b, a:] = 0
+            pos = pos + n_real
+            n_real = v["accept_len"].astype(np.int32)
+            hid = nxt["target_hidden"]
+            assert int(pos.max()) + R + K <= w.max_ctx
+    finally:
+        dr.close()
