@@ -250,6 +250,8 @@ def main():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the catch-up and concatenated-row timings (e.g. under a profiler)")
     ap.add_argument("--no-depth-sweep", action="store_true",
                     help="skip the parallel vs autoregressive latency sweep over K (e.g. under a profiler)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -359,8 +361,10 @@ def main():
     t_verify_sampled = e0.elapsed_time(e1) / reps
 
     depth = None if args.no_depth_sweep else latency_vs_depth(pe, torch, w, config_args, dev, kc, vc, d, stream, reps)
-    catchup = catchup_latency(pe, torch, w, config_args, dev, kc, vc, d, stream, reps)
-    concat = concat_rows_latency(pe, torch, w, config_args, kc, vc, d, stream, reps)
+    catchup = concat = None
+    if not args.no_variants:
+        catchup = catchup_latency(pe, torch, w, config_args, dev, kc, vc, d, stream, reps)
+        concat = concat_rows_latency(pe, torch, w, config_args, kc, vc, d, stream, reps)
 
     if args.copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")

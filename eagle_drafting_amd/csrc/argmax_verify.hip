@@ -202,8 +202,19 @@ __global__ __launch_bounds__(1024) void accept_compact_kernel(
   int dk[KMAX];
 #pragma unroll
   for (int i = 0; i < KMAX; ++i) dk[i] = (tid < B && i < K) ? draft[(size_t)tid * K + i] : -1;
-  // target argmax t[b][i] from the scan partials: one wave per row
-  {
+  // target argmax t[b][i] from the scan partials: one thread per row when rows have few partials (large
+  // batches: many rows, few chunks each), else one wave per row
+  if (nchunks <= 32) {
+    for (int r = tid; r < rows; r += 1024) {
+      const float* v = pv + (size_t)r * nchunks;
+      const int* ix = pi + (size_t)r * nchunks;
+      float b = -INFINITY;
+      int i = 0x7fffffff;
+      for (int c = 0; c < nchunks; ++c)
+        if (am_better(v[c], ix[c], b, i)) { b = v[c]; i = ix[c]; }
+      t_ws[r] = i;
+    }
+  } else {
     const int wave = tid >> 6, lane = tid & 63;
     for (int r = wave; r < rows; r += 16) {
       const int i = am_row_reduce(pv + (size_t)r * nchunks, pi + (size_t)r * nchunks, nchunks, lane);

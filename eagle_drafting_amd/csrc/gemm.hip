@@ -130,7 +130,9 @@ GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok) {
     // skinny kernel re-reads the activations once per 16 columns). Narrow or short products get too few
     // tiles to keep the weight stream going; they split the reduction over workgroups (about 512 in all,
     // at least 8 k-steps each) as long as the fp32 partials stay within the weight bytes
-    // (2 ksplit M N 4 <= N Kd 2); a second kernel adds the partials and runs the epilogue.
+    // (2 ksplit M N 4 <= N Kd 2), and beyond that while the grid does not yet cover the 256 compute units
+    // once (many rows, narrow output: the product is bound by the idle units, not by bytes); a second
+    // kernel adds the partials and runs the epilogue.
     const int tg = (p.Nt + 7) / 8, tm = (M + 127) / 128;
     p.tiled = 1;
     p.MT = 8;
@@ -140,7 +142,7 @@ GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok) {
     p.ngroups = tg;
     if (!argmax) {
       int ks = 1;
-      while (tg * tm * ks < 512 && Ks >= 16 * ks && 8LL * ks * M <= Kd) ks *= 2;
+      while (tg * tm * ks < 512 && Ks >= 16 * ks && (8LL * ks * M <= Kd || tg * tm * ks < 256)) ks *= 2;
       if (ks > 1) {
         p.kper = (((Ks + ks - 1) / ks) + 3) & ~3;
         p.ksplit = (Ks + p.kper - 1) / p.kper;
