@@ -29,7 +29,21 @@ __global__ __launch_bounds__(256) void argmax_rows_kernel(const T* __restrict__ 
   const T* x = X + (size_t)row * V;
   float best = -INFINITY;
   int bi = 0x7fffffff;
-  for (int i = begin + threadIdx.x * VEC; i < end; i += 256 * VEC) {
+  int i = begin + threadIdx.x * VEC;
+  // four 16-byte loads in flight per thread, then their elements in order
+  for (; i + 3 * 256 * VEC + VEC <= end; i += 4 * 256 * VEC) {
+    union { uint4 u; T e[VEC]; } ld[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ld[q].u = *(const uint4*)(x + i + q * 256 * VEC);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)  // increasing index order, so a strict > keeps the first maximum
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float v = to_f32<T>(ld[q].e[e]);
+        if (v > best) { best = v; bi = i + q * 256 * VEC + e; }
+      }
+  }
+  for (; i < end; i += 256 * VEC) {
     if (i + VEC <= end) {
       union { uint4 u; T e[VEC]; } ld;
       ld.u = *(const uint4*)(x + i);
@@ -265,14 +279,20 @@ __device__ __forceinline__ void sm_merge(float& m, float& s, float m2, float s2)
   m = M;
 }
 
-// (max, sum of exp(x - max)) of x = logit / temperature over one chunk of one row; fixed merge order
-template <typename T>
+// (max, sum of exp(x - max)) of x = logit / temperature over one chunk of one row. WPC waves per chunk: 1 (four
+// chunks per workgroup, no block barrier; many rows) or 4 (one chunk per workgroup; few rows, so more waves
+// share the scan). Each lane keeps its running pair over its elements in order; lanes merge by xor-shuffles
+// in a fixed pattern, then (WPC = 4) the four waves in order.
+template <typename T, int WPC>
 __global__ __launch_bounds__(256) void softmax_stats_kernel(const T* __restrict__ X, int V, int chunk, int nchunks,
                                                             float inv_temp, float* __restrict__ pm,
                                                             float* __restrict__ ps) {
   constexpr int VEC = 16 / sizeof(T);
+  constexpr int STEP = 64 * WPC * VEC;  // elements one pass of the chunk's waves covers
   __shared__ float sm[4], ss[4];
-  const int row = blockIdx.x, c = blockIdx.y;
+  const int row = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = blockIdx.y * (4 / WPC) + wave / WPC;
+  if (WPC == 1 && c >= nchunks) return;  // (WPC = 4: the grid holds exactly nchunks workgroups)
   const int begin = c * chunk;
   const int end = min(V, begin + chunk);
   const T* x = X + (size_t)row * V;
@@ -286,7 +306,18 @@ __global__ __launch_bounds__(256) void softmax_stats_kernel(const T* __restrict_
       s += __expf(v - m);
     }
   };
-  for (int i = begin + threadIdx.x * VEC; i < end; i += 256 * VEC) {
+  int i = begin + ((wave % WPC) * 64 + lane) * VEC;
+  // four 16-byte loads in flight per lane, then their elements in order
+  for (; i + 3 * STEP + VEC <= end; i += 4 * STEP) {
+    union { uint4 u; T e[VEC]; } ld[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ld[q].u = *(const uint4*)(x + i + q * STEP);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) add(to_f32<T>(ld[q].e[e]));
+  }
+  for (; i < end; i += STEP) {
     if (i + VEC <= end) {
       union { uint4 u; T e[VEC]; } ld;
       ld.u = *(const uint4*)(x + i);
@@ -300,14 +331,18 @@ __global__ __launch_bounds__(256) void softmax_stats_kernel(const T* __restrict_
     const float m2 = __shfl_xor(m, off, PE_WAVE), s2 = __shfl_xor(s, off, PE_WAVE);
     sm_merge(m, s, m2, s2);
   }
-  if ((threadIdx.x & 63) == 0) { sm[threadIdx.x >> 6] = m; ss[threadIdx.x >> 6] = s; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float M = sm[0], S = ss[0];
-    for (int w = 1; w < 4; ++w) sm_merge(M, S, sm[w], ss[w]);
-    pm[(size_t)row * nchunks + c] = M;
-    ps[(size_t)row * nchunks + c] = S;
+  if (WPC == 4) {
+    if (lane == 0) { sm[wave] = m; ss[wave] = s; }
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    m = sm[0];
+    s = ss[0];
+    for (int w = 1; w < 4; ++w) sm_merge(m, s, sm[w], ss[w]);
+  } else if (lane != 0) {
+    return;
   }
+  pm[(size_t)row * nchunks + c] = m;
+  ps[(size_t)row * nchunks + c] = s;
 }
 
 // One workgroup per request. Every position's row maximum and total (its chunk statistics merged by one
@@ -487,14 +522,21 @@ hipError_t launch_sampled_verify(int dtype, const void* X, int B, int K, int V, 
   chunk = (chunk + 7) / 8 * 8;  // every chunk start 16-byte aligned (V % 8 == 0)
   const int rows = B * (K + 1);
   const float inv_temp = 1.f / temperature;
+  // one wave per chunk once there are enough chunks to fill the compute units with them (measured: B 128 K 7
+  // 119 -> 112 us; four waves per chunk stay faster for a few rows, B 1 K 3 20 against 23 us)
+  const bool many = (long long)rows * nchunks >= 8192;
   if (dtype == 0) {
-    hipLaunchKernelGGL(softmax_stats_kernel<float>, dim3(rows, nchunks), dim3(256), 0, st, (const float*)X, V, chunk,
-                       nchunks, inv_temp, pm, ps);
+    if (many) hipLaunchKernelGGL((softmax_stats_kernel<float, 1>), dim3(rows, (nchunks + 3) / 4), dim3(256), 0, st,
+                                 (const float*)X, V, chunk, nchunks, inv_temp, pm, ps);
+    else hipLaunchKernelGGL((softmax_stats_kernel<float, 4>), dim3(rows, nchunks), dim3(256), 0, st, (const float*)X, V,
+                            chunk, nchunks, inv_temp, pm, ps);
     hipLaunchKernelGGL(sample_decide_kernel<float>, dim3(B), dim3(256), 0, st, (const float*)X, V, chunk, nchunks,
                        inv_temp, pm, ps, K, draft, u, v, t_ws, accept_len);
   } else {
-    hipLaunchKernelGGL(softmax_stats_kernel<bf16_t>, dim3(rows, nchunks), dim3(256), 0, st, (const bf16_t*)X, V,
-                       chunk, nchunks, inv_temp, pm, ps);
+    if (many) hipLaunchKernelGGL((softmax_stats_kernel<bf16_t, 1>), dim3(rows, (nchunks + 3) / 4), dim3(256), 0, st,
+                                 (const bf16_t*)X, V, chunk, nchunks, inv_temp, pm, ps);
+    else hipLaunchKernelGGL((softmax_stats_kernel<bf16_t, 4>), dim3(rows, nchunks), dim3(256), 0, st, (const bf16_t*)X,
+                            V, chunk, nchunks, inv_temp, pm, ps);
     hipLaunchKernelGGL(sample_decide_kernel<bf16_t>, dim3(B), dim3(256), 0, st, (const bf16_t*)X, V, chunk, nchunks,
                        inv_temp, pm, ps, K, draft, u, v, t_ws, accept_len);
   }

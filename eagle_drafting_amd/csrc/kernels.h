@@ -162,6 +162,7 @@ hipError_t launch_argmax_final(const float* pv, const int* pi, int rows, int nch
 // metadata rebuild; pm / ps hold rows x nchunks floats each (nchunks = plan_sample_chunks(V))
 constexpr int PE_SAMPLE_MAX_CHUNKS = 1024;
 // chunks per row of the sampled verify: about 2048 tokens each, so that a draw scans one short chunk
+// (measured: 2-chunk rows at B 128 K 7 made the draws scan 76 k tokens each, 119 -> 198 us)
 inline int plan_sample_chunks(int V) {
   const int c = (V + 2047) / 2048;
   return c < 1 ? 1 : (c > PE_SAMPLE_MAX_CHUNKS ? PE_SAMPLE_MAX_CHUNKS : c);
