@@ -85,6 +85,29 @@ def test_catchup_parity(B, K, R):
         g.close()
 
 
+@pytest.mark.parametrize("name,R", [("qwen3coder-bf16-B1-K3-L2048", 4), ("qwen3coder-bf16-B32-K7-L512to4096-churn", 8)])
+def test_catchup_parity_bench_workloads(name, R):
+    """The bench's catch-up configurations at full size: the headline request (context 2048, R = K + 1)
+    and the 32-request batch (contexts up to 4096, 15 rows per request) on sampled requests."""
+    from synth import WORKLOADS
+    w = WORKLOADS[name]
+    K = w.K
+    log(f"catch-up parity at full size {name} R {R}")
+    tol = TOL[w.shape.dtype]
+    g = GpuDrafter(w, max_k=R + K - 1)
+    try:
+        inp = catchup_inputs(w, R)
+        draft, z = _gpu_catchup(g, K, R, inp)
+        req = [0] if w.B == 1 else [0, 13, w.B - 1]
+        ref = _oracle_catchup(w, shape_weights64(w.shape), g.state, K, inp, req)
+        err = check_logits(z[req], ref["logits"], tol, w.name)
+        strict, exempt = check_tokens(draft[req], ref["logits"], tol, w.name)
+        log(f"  n_real {inp['n_real'][req].tolist()}, logit err {err:.2e}, tokens strict {strict}/{len(req) * K}, "
+            f"exempt {exempt}")
+    finally:
+        g.close()
+
+
 def test_catchup_with_one_real_row_is_the_plain_step():
     # R = 1: the same rows, plans and kernels as pe_draft_step, so the results are bit-identical
     w = Workload("qwen3coder-bf16-B5-K3-catchup-plain", QWEN3_CODER, 5, 3, (60, 400), 0.7, 7900)

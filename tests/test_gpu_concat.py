@@ -57,6 +57,22 @@ def test_concat_rows_parity(B, K):
         g.close()
 
 
+def test_concat_rows_parity_headline_size():
+    """One request at context 2048, K 3: the headline configuration with concatenated rows (the bench's
+    concat_rows_step times this shape)."""
+    w = Workload("qwen3coder-concat-bf16-B1-K3-L2048", QWEN3_CODER_CONCAT, 1, 3, (2048, 2048), 0.7, 8150)
+    tol = TOL[w.shape.dtype]
+    g = GpuDrafter(w)
+    try:
+        draft, z = g.draft()
+        ref = _oracle(w, shape_weights64(w.shape), g.state, 3, [0])
+        err = check_logits(z.cpu().numpy(), ref["logits"], tol, w.name)
+        strict, exempt = check_tokens(draft.cpu().numpy(), ref["logits"], tol, w.name)
+        log(f"  logit err {err:.2e}, tokens strict {strict}/3, exempt {exempt}")
+    finally:
+        g.close()
+
+
 def test_concat_rows_unsupported_entry_points():
     w = Workload("qwen3coder-concat-bf16-B2-K3-args", QWEN3_CODER_CONCAT, 2, 3, (60, 100), 0.7, 8190)
     g = GpuDrafter(w)
