@@ -33,6 +33,10 @@ Readings where the pages leave a step open (each is listed with its reason in th
     [embedding || hidden], 2d wide into layer 0's attention, each half RMS-normalised with its own gain,
     and the hidden half alone is the residual stream (the pages do not say which part carries the
     residual; the hidden half is the one that has the model's width and meaning);
+  * FP8 drafter weights: every projection matrix stored as E4M3 codes with one float32 scale per output
+    row (largest magnitude / 448), the product y = s_n * (q_n . x); activations, norms, embeddings and
+    the KV cache stay bf16 / fp32. The pages give FP8 as the deployment precision of the target, not
+    the drafter's scaling scheme; per-row scales are the plainest reading;
   * multi-row catch-up (a step that first re-runs the positions a verify accepted): each real row pairs
     an emitted token with the target hidden states that produced it, as the pages' position 1 does for
     the one token; the pages do not describe this step, so its logits are parity unpinned against the
@@ -233,6 +237,47 @@ def draft_step(shape, W: dict, state: dict, kv_context, K: int, tail: bool = Fal
         for key in ("logits", "draft", "hidden"):
             out[key] = out[key][:, :K]
     out["rows"] = X
+    return out
+
+
+def fp8_e4m3_round(x: np.ndarray) -> np.ndarray:
+    """Round float values to the nearest value of the FP8 E4M3 format (1 sign, 4 exponent bits with bias 7,
+    3 mantissa bits; largest finite 448; subnormals step 2^-9), ties to the even mantissa. Inputs must lie
+    within +-464 (the caller scales them into +-448); returns the rounded values as float64."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    # spacing of representable values around a: 2^(e - 3) for a in [2^e, 2^(e+1)), e >= -6; 2^-9 below 2^-6
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)
+    step = np.exp2(e - 3.0)
+    q = a / step
+    r = np.floor(q)
+    frac = q - r
+    up = (frac > 0.5) | ((frac == 0.5) & (np.mod(r, 2.0) == 1.0))
+    r = r + up
+    out = np.where(a > 0, r * step, 0.0)
+    return np.copysign(np.minimum(out, 448.0), x)
+
+
+def quantize_fp8_rows(W: np.ndarray) -> np.ndarray:
+    """Per-output-row FP8 weights, dequantized: s_n = max_k |W[n, k]| / 448 (float32), q = E4M3 rounding of
+    float32(W[n, k] / s_n) (float32 division, as the repack computes it), returned as q * s_n in float64.
+    A row of zeros keeps scale 1 (and stays zero)."""
+    W32 = np.asarray(W, dtype=np.float32)
+    amax = np.abs(W32).max(axis=1) if W32.ndim == 2 else np.abs(W32).max()
+    s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    q = fp8_e4m3_round((W32 / s[:, None]).astype(np.float32))
+    return q * s.astype(np.float64)[:, None]
+
+
+def weights_fp8(shape, W: dict) -> dict:
+    """The drafter with every projection matrix (fc, wqkv, wo, wgate, wup, wdown, lm_head) replaced by its
+    per-row FP8 dequantization; embeddings, placeholders and norm gains unchanged."""
+    out = dict(W)
+    for k, v in W.items():
+        base = k.split(".")[-1]
+        if base in ("fc", "wqkv", "wo", "wgate", "wup", "wdown", "lm_head"):
+            out[k] = quantize_fp8_rows(v)
     return out
 
 

@@ -643,6 +643,65 @@ def test_concat_rows_causality():
     assert not np.allclose(a["logits"][:, 1], b["logits"][:, 1])
 
 
+# ---------------------------------------------------------------- FP8 weights
+
+def _e4m3_values():
+    """Every finite E4M3 value from its bit fields: (-1)^s 2^(e-7) (1 + m/8) for e >= 1, (-1)^s m 2^-9 for
+    e = 0; exponent 15 with mantissa 7 is NaN."""
+    vals = []
+    for code in range(256):
+        sgn, e, m = code >> 7, (code >> 3) & 15, code & 7
+        if e == 15 and m == 7:
+            continue
+        v = m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+        vals.append((-v if sgn else v, m & 1))
+    return vals
+
+
+def test_fp8_rounding_brute_force_nearest_even():
+    vals = _e4m3_values()
+    grid = np.array(sorted(set(v for v, _ in vals)))
+    mids = (grid[1:] + grid[:-1]) / 2
+    rng = np.random.default_rng(61)
+    xs = np.concatenate([grid, mids, rng.uniform(-464, 464, 3000), rng.uniform(-0.02, 0.02, 1000)])
+    xs = xs[np.abs(xs) <= 464]
+    got = O.fp8_e4m3_round(xs)
+    for x, g in zip(xs, got):
+        d = [(abs(v - x), odd, v) for v, odd in vals]
+        dmin = min(t[0] for t in d)
+        best = [t for t in d if t[0] == dmin]
+        want = min(best, key=lambda t: t[1])[2] if len(best) > 1 else best[0][2]
+        if x == 0:
+            want = 0.0
+        assert g == want, (x, g, want)
+
+
+def test_fp8_rounding_hand_values():
+    x = np.array([1.0, 1.0625, 1.1875, 448.0, 464.0, 2.0 ** -9, 3 * 2.0 ** -10, -0.5, 0.1, 300.0])
+    want = np.array([1.0, 1.0, 1.25, 448.0, 448.0, 2.0 ** -9, 2.0 ** -8, -0.5, 0.1015625, 288.0])
+    assert np.array_equal(O.fp8_e4m3_round(x), want)
+
+
+def test_fp8_row_quantization_scale_and_round_trip():
+    rng = np.random.default_rng(62)
+    W = rng.standard_normal((6, 40)).astype(np.float32) * 0.02
+    W[3] = 0.0
+    D = O.quantize_fp8_rows(W)
+    # the largest element of each nonzero row maps to +-448 s exactly; a zero row stays zero
+    amax = np.abs(W).max(axis=1)
+    for n in (0, 1, 2, 4, 5):
+        assert np.abs(D[n]).max() == np.float64(np.float32(amax[n] / np.float32(448.0))) * 448.0
+    assert not D[3].any()
+    # quantizing the dequantized weights changes nothing; doubling a row doubles its dequantization
+    assert np.array_equal(O.quantize_fp8_rows(D.astype(np.float32)), D)
+    W2 = W.copy()
+    W2[1] *= 2
+    assert np.array_equal(O.quantize_fp8_rows(W2)[1], 2 * D[1])
+    # relative error of a normal-range value is at most half a mantissa step (2^-4)
+    big = np.abs(W) > amax[:, None] / 448 * 2.0 ** -6
+    assert np.all(np.abs(D - W)[big] <= np.abs(W)[big] * 2.0 ** -4 * (1 + 1e-6))
+
+
 # ---------------------------------------------------------------- sampled verify (temperature > 0)
 
 def test_draw_inverse_cdf_brute_force():
