@@ -182,6 +182,38 @@ def concat_rows_latency(pe, torch, w, cfg_args, kc, vc, d, stream, reps):
     return {"B": w.B, "K": w.K, "draft_us": 1e3 * e0.elapsed_time(e1) / reps}
 
 
+def fp8_weights_latency(pe, torch, w, cfg_args, dev, kc, vc, d, stream, reps):
+    """Draft step with FP8 drafter weights (weight_fp8: E4M3 codes with per-row scales, half the weight
+    bytes) on the same requests, beside the bf16 step; runs where every projection has at most 16 rows
+    (B (K + 1) <= 16, the small-batch kernel). Reports the step and the LM head's average launch."""
+    s = w.shape
+    if s.dtype != "bf16" or w.B * (w.K + 1) > 16:
+        return None
+    ctx = pe.pe_init(pe.make_config(**{**cfg_args(w), "weight_fp8": 1}), pe.make_weights(dev, s.n_layers),
+                     pe.make_kv(kc, vc), stream.cuda_stream)
+    tok = torch.empty((w.B, w.K), dtype=torch.int32, device="cuda")
+
+    def call():
+        pe.pe_draft_step(ctx, w.B, w.K, d["req_slot"], d["seq_len"], d["last_token"], d["target_hidden"], tok, None)
+    for _ in range(3):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    pe.pe_profile_enable(ctx, 1 << pe.PE_PROF_LM_HEAD)
+    for _ in range(reps):
+        call()
+    lm_ms, lm_n = pe.pe_profile_read(ctx, pe.PE_PROF_LM_HEAD)
+    pe.pe_destroy(ctx)
+    lm_us = 1e3 * lm_ms / max(lm_n, 1)
+    lm_bytes = s.vocab * s.d_model + s.vocab * 4  # E4M3 codes + one float32 scale per row
+    return {"B": w.B, "K": w.K, "draft_us": 1e3 * e0.elapsed_time(e1) / reps, "lm_head_us": lm_us,
+            "lm_head_GBps": lm_bytes / (lm_us * 1e-6) / 1e9}
+
+
 def kernel_source_digest():
     """sha256 over the sources that define the projection kernels (the LM head among them)."""
     h = hashlib.sha256()
@@ -361,10 +393,11 @@ def main():
     t_verify_sampled = e0.elapsed_time(e1) / reps
 
     depth = None if args.no_depth_sweep else latency_vs_depth(pe, torch, w, config_args, dev, kc, vc, d, stream, reps)
-    catchup = concat = None
+    catchup = concat = fp8 = None
     if not args.no_variants:
         catchup = catchup_latency(pe, torch, w, config_args, dev, kc, vc, d, stream, reps)
         concat = concat_rows_latency(pe, torch, w, config_args, kc, vc, d, stream, reps)
+        fp8 = fp8_weights_latency(pe, torch, w, config_args, dev, kc, vc, d, stream, reps)
 
     if args.copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
@@ -411,6 +444,7 @@ def main():
         "draft_latency_vs_depth": depth,
         "catchup_step": catchup,
         "concat_rows_step": concat,
+        "fp8_weights_step": fp8,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, state, T_host, args.cpu_seconds)

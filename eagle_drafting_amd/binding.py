@@ -32,7 +32,7 @@ class pe_config(ctypes.Structure):
     _fields_ = [("n_layers", c_int32), ("d_model", c_int32), ("n_q_heads", c_int32), ("n_kv_heads", c_int32),
                 ("head_dim", c_int32), ("ffn_dim", c_int32), ("vocab", c_int32), ("rms_eps", c_float),
                 ("rope_base", c_float), ("dtype", c_int32), ("max_batch", c_int32), ("max_k", c_int32),
-                ("max_ctx", c_int32), ("n_slots", c_int32), ("row_concat", c_int32)]
+                ("max_ctx", c_int32), ("n_slots", c_int32), ("row_concat", c_int32), ("weight_fp8", c_int32)]
 
 
 _L = c_void_p * PE_MAX_LAYERS
@@ -201,10 +201,10 @@ def pe_profile_read(ctx, which: int):
 # ---- struct builders (marshalling helpers) ----------------------------------------------------------
 
 def make_config(n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab, dtype, max_batch, max_k,
-                max_ctx, n_slots, rms_eps=1e-6, rope_base=10000.0, row_concat=0) -> pe_config:
+                max_ctx, n_slots, rms_eps=1e-6, rope_base=10000.0, row_concat=0, weight_fp8=0) -> pe_config:
     return pe_config(n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab, rms_eps, rope_base,
                      PE_BF16 if dtype in ("bf16", PE_BF16) else PE_F32, max_batch, max_k, max_ctx, n_slots,
-                     int(row_concat))
+                     int(row_concat), int(weight_fp8))
 
 
 def make_weights(t: dict, n_layers: int) -> pe_weights:

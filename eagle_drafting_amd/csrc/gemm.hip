@@ -66,6 +66,65 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(const bf16_t* __restrict
   dst[frag * 64 + lane] = v;
 }
 
+// one wave per packed output column: the largest magnitude of its source row, scale = that / 448
+__global__ __launch_bounds__(256) void fp8_scale_kernel(const bf16_t* __restrict__ W0, const bf16_t* __restrict__ W1,
+                                                        int N, int Kd, int Nt, int mode, int hd,
+                                                        float* __restrict__ scales) {
+  const int col = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (col >= Nt * 16) return;
+  int which = 0;
+  const int row = pack_src_row(mode, col / 16, col % 16, hd, &which);
+  const bf16_t* W = which ? W1 : W0;
+  float m = 0.f;
+  if (row < N)
+    for (int k = lane; k < Kd; k += 64) m = fmaxf(m, fabsf(bf16_to_f32(W[(size_t)row * Kd + k])));
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, PE_WAVE));
+  if (lane == 0) scales[col] = m > 0.f ? m / 448.f : 1.f;
+}
+
+// fragment (t, s), lane l: 8 codes of source row src(t, l % 16), columns 32 s + 8 (l / 16) .. + 7
+__global__ __launch_bounds__(256) void pack_fp8_kernel(const bf16_t* __restrict__ W0, const bf16_t* __restrict__ W1,
+                                                       int N, int Kd, uint2* __restrict__ dst, int Nt, int Ks, int mode,
+                                                       int hd, const float* __restrict__ scales) {
+  const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t total = (size_t)Nt * Ks * 64;
+  if (gid >= total) return;
+  const int lane = (int)(gid & 63);
+  const size_t frag = gid >> 6;
+  const int s = (int)(frag % Ks);
+  const int t = (int)(frag / Ks);
+  int which = 0;
+  const int row = pack_src_row(mode, t, lane & 15, hd, &which);
+  const int col = 32 * s + 8 * (lane >> 4);
+  const bf16_t* W = which ? W1 : W0;
+  const float sc = scales[t * 16 + (lane & 15)];
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float v = 0.f;
+    if (row < N && col + e < Kd) v = bf16_to_f32(W[(size_t)row * Kd + col + e]) / sc;
+    x[e] = fminf(fmaxf(v, -448.f), 448.f);  // |w| / s <= 448 already; the clamp only guards rounding
+  }
+  uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0u, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], lo, true);
+  uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0u, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], hi, true);
+  dst[frag * 64 + lane] = make_uint2(lo, hi);
+}
+
+hipError_t launch_pack_fp8(const void* W0, const void* W1, int N, int Kd, int mode, int hd, void* dst, float* scales,
+                           hipStream_t st) {
+  if (mode == PACK_KI4) return hipErrorInvalidValue;
+  const int Nt = mode == PACK_GATEUP ? (2 * N + 15) / 16 : n_tiles(N);
+  const int Ks = k_steps(Kd);
+  hipLaunchKernelGGL(fp8_scale_kernel, dim3((unsigned)((Nt * 16 + 3) / 4)), dim3(256), 0, st, (const bf16_t*)W0,
+                     (const bf16_t*)W1, N, Kd, Nt, mode, hd, scales);
+  const size_t total = (size_t)Nt * Ks * 64;
+  hipLaunchKernelGGL(pack_fp8_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, (const bf16_t*)W0,
+                     (const bf16_t*)W1, N, Kd, (uint2*)dst, Nt, Ks, mode, hd, (const float*)scales);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack_bf16(const void* W0, const void* W1, int N, int Kd, int mode, int hd, void* dst,
                             hipStream_t st) {
   const int Nt = mode == PACK_GATEUP ? (2 * N + 15) / 16 : mode == PACK_KI4 ? n_tiles_ki4(N) : n_tiles(N);
@@ -76,7 +135,7 @@ hipError_t launch_pack_bf16(const void* W0, const void* W1, int N, int Kd, int m
   return hipGetLastError();
 }
 
-GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok) {
+GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok, bool skinny_only) {
   GemmPlan p;
   const int Ks = k_steps(Kd);
   p.Nt = n_tiles(N);
@@ -100,7 +159,7 @@ GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok) {
   }
   // (measured: the vocabulary projection is faster in the stream kernel from 9 rows, the layer projections
   // from 17; the stream kernel addresses the packed weights with 32-bit buffer offsets)
-  if (M > (argmax ? 8 : 16) && M <= 128 && (long long)p.Nt * Ks * 1024 < 0x7ff00000LL) {
+  if (!skinny_only && M > (argmax ? 8 : 16) && M <= 128 && (long long)p.Nt * Ks * 1024 < 0x7ff00000LL) {
     // up to 128 rows: the weight-stream kernel (all rows and 128 columns per workgroup, activations staged
     // once per chunk). Narrow or short products split the reduction over workgroups until there are about
     // 192 of them, each with at least four chunks, and while the fp32 partials stay within the weight bytes
@@ -125,7 +184,7 @@ GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok) {
     }
     return p;
   }
-  if (M > 32) {
+  if (!skinny_only && M > 32) {
     // 128 x 128 tiles read each weight once per 128 rows and each activation once per 128 columns (the
     // skinny kernel re-reads the activations once per 16 columns). Narrow or short products get too few
     // tiles to keep the weight stream going; they split the reduction over workgroups (about 512 in all,
@@ -190,10 +249,23 @@ struct KChunk {
   static constexpr int value = MT <= 2 ? 8 : (MT == 4 ? 4 : 2);
 };
 
+// eight E4M3 codes (one 8-byte fragment lane) as the bf16 MFMA operand; every E4M3 value is exact in bf16
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint2 w) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, true);
+  const f2 c = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, false), d = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, true);
+  const u32x4_t pk = {f32x2_to_bf16x2(a[0], a[1]), f32x2_to_bf16x2(b[0], b[1]), f32x2_to_bf16x2(c[0], c[1]),
+                      f32x2_to_bf16x2(d[0], d[1])};
+  return __builtin_bit_cast(bf16x8_t, pk);
+}
+
 // KI: PACK_KI4 weights (MT == 1, NT == 1, M <= 4): 4-column tiles, activation row m at MFMA rows m + 4h
-template <int MT, int NW, int NT, int AM, int EP, int KI>
+// F8: E4M3 weight fragments (8 bytes per lane) with per-column scales applied in the epilogue
+template <int MT, int NW, int NT, int AM, int EP, int KI, int F8 = 0>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
   static_assert(!KI || (MT == 1 && NT == 1 && (EP == EPI_RESID || EP == EPI_ROWS)), "KI4 layout: residual producers");
+  static_assert(!(KI && F8), "FP8 weights use the 16-column layout");
   constexpr int CW = KI ? 4 : 16;  // output columns per tile
   constexpr int KP = NW / NT;            // k parts
   constexpr int KC = KChunk<MT>::value;  // k-steps loaded per round
@@ -217,6 +289,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const bf16x8_t* wsrc = (const bf16x8_t*)g.Wp_raw + (size_t)ntc * Ks * 64 + lane;
+  const uint2* wsrc8 = (const uint2*)g.Wp_raw + (size_t)ntc * Ks * 64 + lane;
 
   // Main loop, KC k-steps per round. Every load is unconditional (addresses clamped into range; rows >= M
   // and k-steps past the split are computed but never used), so the weight loads of a round are all in
@@ -227,6 +300,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
   const __amdgpu_buffer_rsrc_t a_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, gemm_a_rows(g) * g.lda * 2, 0x00020000);
   bf16x8_t a[KC][MT], b[KC];
+  uint2 b8[KC];  // FP8: the raw codes, converted just before their product so the loads stay in flight
   // each lane's operand row start (elements), or -1 for a padding row; resolved once, before the loop
   int a_row0[MT];
 #pragma unroll
@@ -252,16 +326,21 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
       }
     }
 #pragma unroll
-    for (int kk = 0; kk < KC; ++kk) b[kk] = wsrc[(size_t)min(c0 + min(kk, nk - 1), Ks - 1) * 64];
+    for (int kk = 0; kk < KC; ++kk) {
+      const size_t ks = (size_t)min(c0 + min(kk, nk - 1), Ks - 1) * 64;
+      if (F8) b8[kk] = wsrc8[ks];
+      else b[kk] = wsrc[ks];
+    }
   };
   auto mma_round = [&](int c0) {
     const int nk = min(KC, s_end - c0);
 #pragma unroll
     for (int kk = 0; kk < KC; ++kk) {
       if (kk < nk) {
+        const bf16x8_t bk = F8 ? fp8x8_to_bf16x8(b8[kk]) : b[kk];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk][mt], b[kk], acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk][mt], bk, acc[mt], 0, 0, 0);
       }
     }
   };
@@ -339,6 +418,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
           s_red[(r + 12) * 16 + c + 12];
     else
       v = s_red[(t * MT + (r >> 4)) * 256 + (r & 15) * 16 + c];
+    if (F8) v *= g.wscale[min((int)blockIdx.x * NT + t, g.Nt - 1) * 16 + c];
     return AM == A_NORM ? v * s_inv[r] : v;
   };
   const int rows = nrows;
@@ -472,25 +552,41 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
   }
 }
 
-template <int MT, int NW, int NT, int AM, int EP, int KI = 0>
+template <int MT, int NW, int NT, int AM, int EP, int KI = 0, int F8 = 0>
 static void launch_one(const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_kernel<MT, NW, NT, AM, EP, KI>), dim3(p.ngroups, p.mblocks), dim3(NW * 64), 0, st, a);
+  hipLaunchKernelGGL((gemm_kernel<MT, NW, NT, AM, EP, KI, F8>), dim3(p.ngroups, p.mblocks), dim3(NW * 64), 0, st, a);
 }
 
-template <int AM, int EP>
+template <int AM, int EP, int F8 = 0>
 static hipError_t launch_split_nw(const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
 #define PE_NW_CASES(MT_)                                            \
   if (p.MT == MT_) {                                                \
-    if (p.NW == 16) launch_one<MT_, (MT_ == 1 ? 16 : 4), 1, AM, EP>(p, a, st); \
-    else if (p.NW == 8) launch_one<MT_, (MT_ <= 2 ? 8 : 4), 1, AM, EP>(p, a, st); \
-    else launch_one<MT_, 4, 1, AM, EP>(p, a, st);                   \
+    if (p.NW == 16) launch_one<MT_, (MT_ == 1 ? 16 : 4), 1, AM, EP, 0, F8>(p, a, st); \
+    else if (p.NW == 8) launch_one<MT_, (MT_ <= 2 ? 8 : 4), 1, AM, EP, 0, F8>(p, a, st); \
+    else launch_one<MT_, 4, 1, AM, EP, 0, F8>(p, a, st);            \
     return hipGetLastError();                                       \
   }
   PE_NW_CASES(1)
+  if (F8) return hipErrorInvalidValue;  // FP8 weights: products of up to 16 rows
   PE_NW_CASES(2)
   PE_NW_CASES(4)
   PE_NW_CASES(8)
 #undef PE_NW_CASES
+  return hipErrorInvalidValue;
+}
+
+// FP8 weights: the small-batch kernel only (up to 16 rows, 16-column tiles)
+static hipError_t launch_gemm_fp8(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st) {
+  if (p.tiled || p.ki4 || p.MT != 1 || p.NT != 1) return hipErrorInvalidValue;
+  if (epi == EPI_ARGMAX) {
+    if (a_mode != A_NORM || p.NW != 8) return hipErrorInvalidValue;
+    launch_one<1, 8, 1, A_NORM, EPI_ARGMAX, 0, 1>(p, a, st);
+    return hipGetLastError();
+  }
+  if (a_mode == A_BF16 && epi == EPI_RESID) return launch_split_nw<A_BF16, EPI_RESID, 1>(p, a, st);
+  if (a_mode == A_BF16 && epi == EPI_ROWS) return launch_split_nw<A_BF16, EPI_ROWS, 1>(p, a, st);
+  if (a_mode == A_NORM && epi == EPI_QKV) return launch_split_nw<A_NORM, EPI_QKV, 1>(p, a, st);
+  if (a_mode == A_NORM && epi == EPI_SWIGLU) return launch_split_nw<A_NORM, EPI_SWIGLU, 1>(p, a, st);
   return hipErrorInvalidValue;
 }
 
@@ -502,6 +598,7 @@ hipError_t launch_gemm(const GemmPlan& p, GemmArgs a, int a_mode, int epi, hipSt
   if (a.ldz == 0) a.ldz = a.N;
   a.ksplit = p.ksplit;
   a.kper = p.kper;
+  if (a.wscale) return launch_gemm_fp8(p, a, a_mode, epi, st);
   if (p.tiled) return launch_gemm_tiled(p, a, a_mode, epi, st);
   if (p.ki4) {
     if (a_mode != A_BF16 || (p.NW != 4 && p.NW != 8) || a.M > 4) return hipErrorInvalidValue;

@@ -44,7 +44,8 @@ struct GemmPlan {
 };
 // ki4_ok: the weights are also packed as PACK_KI4 (the residual-stream producers: fc, O, down), which the
 // plan uses for up to 4 rows when the plain layout would leave most compute units idle
-GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok = false);
+// skinny_only: the small-batch kernel whatever M (FP8 weights; M <= 16)
+GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok = false, bool skinny_only = false);
 // Partial sums of squares per row that a residual-stream producer with plan p writes (one per 16 columns
 // for the skinny kernel, one per 4 columns on PACK_KI4 weights, one per 128-column workgroup tile for the
 // tiled one); the consumer sums exactly that many.
@@ -89,6 +90,9 @@ struct GemmArgs {
   const int* n_real; int rows_real;
   // tiled K-split: fp32 partial tiles [ksplit][M][N] (workspace) and the plan's split shape
   float* part; int ksplit, kper;
+  // FP8 weights (small-batch kernel only): Wp_raw holds E4M3 fragments (8 bytes per lane per k-step) and
+  // wscale one float per packed output column (tile t, column c at 16 t + c); y = wscale * (q . x)
+  const float* wscale;
 };
 // real input rows of request b (clamped into 1 .. rows_real, so that a bad value stays in bounds)
 __device__ inline int gemm_n_real(const GemmArgs& g, int b) {
@@ -105,6 +109,11 @@ __device__ inline int gemm_a_rows(const GemmArgs& g) {
   return g.rows_out > 0 ? (g.M + g.rows_out - 1) / g.rows_out * g.rows_in : g.M;
 }
 hipError_t launch_gemm(const GemmPlan& p, GemmArgs a, int a_mode, int epi, hipStream_t st);
+// FP8 repack of one projection (PACK_PLAIN / PACK_PAIRS / PACK_GATEUP layouts): per packed output column the
+// scale s = max |w| / 448 of its source row (1 for a zero row), then E4M3 codes of w / s (round to nearest
+// even) in fragments of 512 bytes (8 codes per lane); dst needs Nt Ks 512 bytes, scales Nt 16 floats
+hipError_t launch_pack_fp8(const void* W0, const void* W1, int N, int Kd, int mode, int hd, void* dst, float* scales,
+                           hipStream_t st);
 hipError_t launch_gemm_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st);
 // Autoregressive pass `pass` >= 1: row b = X[b] (the previous pass's residual stream after the last layer)
 // + embed[prev_tok[b]]; records prev_tok[b] as draft pass - 1 of request b (draft_tokens [B, K]), writes the

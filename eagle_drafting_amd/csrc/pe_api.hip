@@ -31,6 +31,13 @@ struct pe_ctx {
   const void* p_fc4 = nullptr;
   const void* p_o4[PE_MAX_LAYERS] = {};
   const void* p_down4[PE_MAX_LAYERS] = {};
+  // FP8 weights (weight_fp8): E4M3 fragments and per-column scales of every projection
+  bool fp8 = false;
+  char* packed8 = nullptr;
+  const void* q_fc = nullptr; const void* q_qkv[PE_MAX_LAYERS] = {}; const void* q_o[PE_MAX_LAYERS] = {};
+  const void* q_gu[PE_MAX_LAYERS] = {}; const void* q_down[PE_MAX_LAYERS] = {}; const void* q_lm = nullptr;
+  const float* s_fc = nullptr; const float* s_qkv[PE_MAX_LAYERS] = {}; const float* s_o[PE_MAX_LAYERS] = {};
+  const float* s_gu[PE_MAX_LAYERS] = {}; const float* s_down[PE_MAX_LAYERS] = {}; const float* s_lm = nullptr;
 
   // workspace
   char* ws = nullptr;
@@ -96,6 +103,10 @@ static pe_status check_cfg(const pe_config* c, std::string& why) {
   }
   if (c->row_concat != 0 && c->row_concat != 1) { why = "row_concat must be 0 or 1"; return PE_ERR_INVALID; }
   if (c->row_concat && c->dtype != PE_BF16) { why = "concatenated rows need a bf16 drafter"; return PE_ERR_UNSUPPORTED; }
+  if (c->weight_fp8 != 0 && c->weight_fp8 != 1) { why = "weight_fp8 must be 0 or 1"; return PE_ERR_INVALID; }
+  if (c->weight_fp8 && (c->dtype != PE_BF16 || c->row_concat)) {
+    why = "FP8 weights need a bf16 drafter with summed rows"; return PE_ERR_UNSUPPORTED;
+  }
   if (c->dtype == PE_F32 && c->max_ctx > 12288) { why = "fp32 drafter supports max_ctx <= 12288"; return PE_ERR_UNSUPPORTED; }
   if ((long long)c->n_slots * c->n_kv_heads * c->max_ctx * c->head_dim > (1LL << 40)) {
     why = "KV cache too large"; return PE_ERR_UNSUPPORTED;
@@ -125,6 +136,12 @@ extern "C" const char* pe_last_error(const pe_ctx* ctx) { return ctx ? ctx->err.
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// projection plan; FP8 weights always run on the small-batch kernel (16-column tiles)
+static GemmPlan plan_for(const pe_ctx* ctx, int M, int N, int Kd, bool argmax, bool ki4_ok = false) {
+  return ctx->fp8 ? plan_gemm(M, N, Kd, argmax, false, true) : plan_gemm(M, N, Kd, argmax, ki4_ok);
+}
+
+
 static size_t packed_bytes(int N, int Kd) { return (size_t)n_tiles(N) * k_steps(Kd) * 1024; }
 static size_t packed_ki4_bytes(int N, int Kd) { return (size_t)n_tiles_ki4(N) * k_steps_ki4(Kd) * 1024; }
 
@@ -135,6 +152,7 @@ static void free_ctx(pe_ctx* c) {
     for (auto e : c->ev_b[k]) (void)hipEventDestroy(e);
   }
   if (c->packed) (void)hipFree(c->packed);
+  if (c->packed8) (void)hipFree(c->packed8);
   if (c->ws) (void)hipFree(c->ws);
   delete c;
 }
@@ -238,11 +256,61 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
     }
   }
 
+  // ---- FP8 copies of the projections (weight_fp8)
+  if (ctx->bf16 && c.weight_fp8) {
+    ctx->fp8 = true;
+    size_t off = 0;
+    auto take = [&](size_t b) { size_t o = off; off = align256(off + b); return o; };
+    auto q_bytes = [](int Nt, int Kd) { return (size_t)Nt * k_steps(Kd) * 512; };
+    auto s_bytes = [](int Nt) { return (size_t)Nt * 16 * 4; };
+    const size_t o_fc = take(q_bytes(n_tiles(d), 3 * d)), os_fc = take(s_bytes(n_tiles(d)));
+    size_t o_q[PE_MAX_LAYERS][4], os_q[PE_MAX_LAYERS][4];
+    const int nts[4] = {n_tiles(qkvd), n_tiles(d), (2 * F + 15) / 16, n_tiles(d)};
+    const int kds[4] = {d, qd, d, F};
+    for (int l = 0; l < c.n_layers; ++l)
+      for (int j = 0; j < 4; ++j) {
+        o_q[l][j] = take(q_bytes(nts[j], kds[j]));
+        os_q[l][j] = take(s_bytes(nts[j]));
+      }
+    const size_t o_lm = take(q_bytes(n_tiles(V), d)), os_lm = take(s_bytes(n_tiles(V)));
+    if (hipMalloc((void**)&ctx->packed8, off) != hipSuccess) {
+      free_ctx(ctx);
+      return fail(nullptr, PE_ERR_OOM, "hipMalloc of FP8 weights failed");
+    }
+    char* base = ctx->packed8;
+    hipStream_t st = ctx->stream;
+    auto chk = [&](hipError_t r) { return r == hipSuccess; };
+    bool ok = chk(launch_pack_fp8(w->fc, nullptr, d, 3 * d, PACK_PLAIN, 0, base + o_fc, (float*)(base + os_fc), st));
+    ctx->q_fc = base + o_fc;
+    ctx->s_fc = (const float*)(base + os_fc);
+    for (int l = 0; l < c.n_layers && ok; ++l) {
+      ok = ok && chk(launch_pack_fp8(w->wqkv[l], nullptr, qkvd, d, PACK_PAIRS, hd, base + o_q[l][0],
+                                     (float*)(base + os_q[l][0]), st));
+      ok = ok && chk(launch_pack_fp8(w->wo[l], nullptr, d, qd, PACK_PLAIN, 0, base + o_q[l][1],
+                                     (float*)(base + os_q[l][1]), st));
+      ok = ok && chk(launch_pack_fp8(w->wgate[l], w->wup[l], F, d, PACK_GATEUP, 0, base + o_q[l][2],
+                                     (float*)(base + os_q[l][2]), st));
+      ok = ok && chk(launch_pack_fp8(w->wdown[l], nullptr, d, F, PACK_PLAIN, 0, base + o_q[l][3],
+                                     (float*)(base + os_q[l][3]), st));
+      ctx->q_qkv[l] = base + o_q[l][0]; ctx->s_qkv[l] = (const float*)(base + os_q[l][0]);
+      ctx->q_o[l] = base + o_q[l][1]; ctx->s_o[l] = (const float*)(base + os_q[l][1]);
+      ctx->q_gu[l] = base + o_q[l][2]; ctx->s_gu[l] = (const float*)(base + os_q[l][2]);
+      ctx->q_down[l] = base + o_q[l][3]; ctx->s_down[l] = (const float*)(base + os_q[l][3]);
+    }
+    ok = ok && chk(launch_pack_fp8(w->lm_head, nullptr, V, d, PACK_PLAIN, 0, base + o_lm, (float*)(base + os_lm), st));
+    ctx->q_lm = base + o_lm;
+    ctx->s_lm = (const float*)(base + os_lm);
+    if (!ok) {
+      free_ctx(ctx);
+      return fail(nullptr, PE_ERR_HIP, "FP8 weight packing launch failed");
+    }
+  }
+
   // ---- workspace sizes (maxima over every B <= max_batch, K <= max_k)
   size_t p_floats = 0, attn_floats = 0, am_floats = 0, part_floats = 0;
   for (int M = 1; M <= Mmax; ++M) {
     if (ctx->bf16) {
-      GemmPlan pl = plan_gemm(M, V, d, true);
+      GemmPlan pl = plan_for(ctx, M, V, d, true);
       am_floats = std::max(am_floats, (size_t)M * pl.ngroups);
       // K-split partials of the layer projections and of the row build (B rows, or B R for a catch-up step)
       // (and layer 0's QKV over concatenated rows, 2d wide)
@@ -457,8 +525,9 @@ static pe_status rows_bf16(pe_ctx* ctx, int32_t B, int32_t Kr, const int32_t* la
   a.embed = (const uint16_t*)ctx->w.embed; a.emb_mask = (const uint16_t*)ctx->w.emb_mask;
   a.h_shared = (const uint16_t*)ctx->w.h_shared;
   a.gain_next = (const uint16_t*)ctx->w.attn_norm[0];
-  const GemmPlan p = plan_gemm(B * R, d, 3 * d, false, true);
-  a.Wp_raw = p.ki4 ? ctx->p_fc4 : ctx->p_fc;
+  const GemmPlan p = plan_for(ctx, B * R, d, 3 * d, false, true);
+  a.Wp_raw = ctx->fp8 ? ctx->q_fc : p.ki4 ? ctx->p_fc4 : ctx->p_fc;
+  a.wscale = ctx->fp8 ? ctx->s_fc : nullptr;
   a.nssq_out = nssq = gemm_ssq_parts(p);
   hipStream_t st = ctx->stream;
   LAUNCH(launch_gemm(p, a, A_BF16, EPI_ROWS, st));
@@ -483,7 +552,8 @@ static pe_status layers_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* r
       GemmArgs a = base;
       a.M = M; a.Kd = cat ? 2 * d : d; a.N = qkvd;
       a.A = cat ? (const uint16_t*)ctx->Ucat : XG; a.lda = a.Kd;
-      a.Wp_raw = ctx->p_qkv[l];
+      a.Wp_raw = ctx->fp8 ? ctx->q_qkv[l] : ctx->p_qkv[l];
+      a.wscale = ctx->fp8 ? ctx->s_qkv[l] : nullptr;
       a.Q = (uint16_t*)ctx->Qb; a.Kc = (uint16_t*)ctx->kv.k[l]; a.Vc = (uint16_t*)ctx->kv.v[l];
       a.seq_len = seq_len; a.req_slot = req_slot; a.rope = ctx->rope;
       a.Kdraft = K; a.Hq = Hq; a.Hkv = Hkv; a.hd = hd; a.max_ctx = c.max_ctx; a.n_slots = c.n_slots;
@@ -491,7 +561,7 @@ static pe_status layers_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* r
       if (cat)
         LAUNCH(launch_concat_norm(ctx->X, ctx->Xe, (const uint16_t*)w.attn_norm[0], (const uint16_t*)w.embed_norm,
                                   (uint16_t*)ctx->Ucat, M, d, c.rms_eps, st));
-      LAUNCH(launch_gemm(plan_gemm(M, qkvd, a.Kd, false), a, cat ? A_BF16 : A_NORM, EPI_QKV, st));
+      LAUNCH(launch_gemm(plan_for(ctx, M, qkvd, a.Kd, false), a, cat ? A_BF16 : A_NORM, EPI_QKV, st));
     }
     // a5: attention
     AttnPlan ap = plan_attention(B, K, Hq, Hkv, hd, c.max_ctx);
@@ -506,8 +576,9 @@ static pe_status layers_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* r
       a.M = M; a.Kd = qd; a.N = d;
       a.A = (const uint16_t*)ctx->Ob; a.lda = qd;
       a.gain_next = (const uint16_t*)w.mlp_norm[l];
-      const GemmPlan p = plan_gemm(M, d, qd, false, true);
-      a.Wp_raw = p.ki4 ? ctx->p_o4[l] : ctx->p_o[l];
+      const GemmPlan p = plan_for(ctx, M, d, qd, false, true);
+      a.Wp_raw = ctx->fp8 ? ctx->q_o[l] : p.ki4 ? ctx->p_o4[l] : ctx->p_o[l];
+      a.wscale = ctx->fp8 ? ctx->s_o[l] : nullptr;
       a.nssq_out = nssq = gemm_ssq_parts(p);
       LAUNCH(launch_gemm(p, a, A_BF16, EPI_RESID, st));
     }
@@ -515,12 +586,13 @@ static pe_status layers_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* r
       GemmArgs a = base;
       a.M = M; a.Kd = d; a.N = 2 * F;
       a.A = XG; a.lda = d;
-      a.Wp_raw = ctx->p_gu[l];
+      a.Wp_raw = ctx->fp8 ? ctx->q_gu[l] : ctx->p_gu[l];
+      a.wscale = ctx->fp8 ? ctx->s_gu[l] : nullptr;
       a.Aout = (uint16_t*)ctx->Ab;
       a.F = F;
       a.nssq = nssq;
       LAUNCH(prof_mark(ctx, PE_PROF_GATE_UP, true));
-      LAUNCH(launch_gemm(plan_gemm(M, 2 * F, d, false), a, A_NORM, EPI_SWIGLU, st));
+      LAUNCH(launch_gemm(plan_for(ctx, M, 2 * F, d, false), a, A_NORM, EPI_SWIGLU, st));
       LAUNCH(prof_mark(ctx, PE_PROF_GATE_UP, false));
     }
     {  // a8: down projection + residual
@@ -528,8 +600,9 @@ static pe_status layers_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* r
       a.M = M; a.Kd = F; a.N = d;
       a.A = (const uint16_t*)ctx->Ab; a.lda = F;
       a.gain_next = (const uint16_t*)(l + 1 < c.n_layers ? w.attn_norm[l + 1] : w.final_norm);
-      const GemmPlan p = plan_gemm(M, d, F, false, true);
-      a.Wp_raw = p.ki4 ? ctx->p_down4[l] : ctx->p_down[l];
+      const GemmPlan p = plan_for(ctx, M, d, F, false, true);
+      a.Wp_raw = ctx->fp8 ? ctx->q_down[l] : p.ki4 ? ctx->p_down4[l] : ctx->p_down[l];
+      a.wscale = ctx->fp8 ? ctx->s_down[l] : nullptr;
       a.nssq_out = nssq = gemm_ssq_parts(p);
       LAUNCH(launch_gemm(p, a, A_BF16, EPI_RESID, st));
     }
@@ -549,10 +622,11 @@ static pe_status lm_head_bf16(pe_ctx* ctx, int32_t B, int32_t K, int32_t Kout, i
   a.A = (const uint16_t*)ctx->U; a.lda = c.d_model;
   a.rows_in = K; a.rows_out = Kout;
   a.rows_real = R; a.n_real = n_real;
-  a.Wp_raw = ctx->p_lm;
+  a.Wp_raw = ctx->fp8 ? ctx->q_lm : ctx->p_lm;
+  a.wscale = ctx->fp8 ? ctx->s_lm : nullptr;
   a.am_val = ctx->am_val; a.am_idx = ctx->am_idx; a.logits = logits; a.ldz = ldz;
   a.nssq = nssq;
-  GemmPlan p = plan_gemm(Mo, c.vocab, c.d_model, true);
+  GemmPlan p = plan_for(ctx, Mo, c.vocab, c.d_model, true);
   LAUNCH(prof_mark(ctx, PE_PROF_LM_HEAD, true));
   LAUNCH(launch_gemm(p, a, A_NORM, EPI_ARGMAX, st));
   LAUNCH(prof_mark(ctx, PE_PROF_LM_HEAD, false));
@@ -635,6 +709,7 @@ static pe_status run_draft(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req
   // L_b + K), so the cache holds K/V for every position a verify can accept (accept_len <= K + 1); its
   // outputs are not emitted. Caller-built rows are run as given.
   const int Kr = rows ? K : K + 1;
+  if (ctx->fp8 && B * Kr > 16) return fail(ctx, PE_ERR_UNSUPPORTED, "FP8 weights: at most 16 rows per projection");
   if (ctx->bf16)
     return draft_bf16(ctx, B, Kr, K, req_slot, seq_len, last_token, target_hidden, rows, draft_tokens, logits);
   return draft_f32(ctx, B, Kr, K, req_slot, seq_len, last_token, target_hidden, rows, draft_tokens, logits);
@@ -654,6 +729,7 @@ extern "C" pe_status pe_draft_ar(pe_ctx* ctx, int32_t B, int32_t K, const int32_
   const pe_config& c = ctx->cfg;
   if (!ctx->bf16) return fail(ctx, PE_ERR_UNSUPPORTED, "autoregressive drafting needs a bf16 drafter");
   if (c.row_concat) return fail(ctx, PE_ERR_UNSUPPORTED, "autoregressive drafting with concatenated rows");
+  if (ctx->fp8 && B > 16) return fail(ctx, PE_ERR_UNSUPPORTED, "FP8 weights: at most 16 rows per projection");
   if (B < 1 || B > c.max_batch) return fail(ctx, PE_ERR_INVALID, "B out of [1, max_batch]");
   if (K < 1 || K > c.max_k) return fail(ctx, PE_ERR_INVALID, "K out of [1, max_k]");
   if (!req_slot || !seq_len || !draft_tokens || !last_token || !target_hidden)
@@ -670,6 +746,8 @@ extern "C" pe_status pe_draft_catchup(pe_ctx* ctx, int32_t B, int32_t K, int32_t
   const pe_config& c = ctx->cfg;
   if (!ctx->bf16) return fail(ctx, PE_ERR_UNSUPPORTED, "catch-up steps need a bf16 drafter");
   if (c.row_concat) return fail(ctx, PE_ERR_UNSUPPORTED, "catch-up steps with concatenated rows");
+  if (ctx->fp8 && (long long)B * (R + K) > 16)
+    return fail(ctx, PE_ERR_UNSUPPORTED, "FP8 weights: at most 16 rows per projection");
   if (B < 1 || B > c.max_batch) return fail(ctx, PE_ERR_INVALID, "B out of [1, max_batch]");
   if (K < 1 || K > c.max_k) return fail(ctx, PE_ERR_INVALID, "K out of [1, max_k]");
   if (R < 1 || R + K > c.max_k + 1) return fail(ctx, PE_ERR_INVALID, "R out of [1, max_k + 1 - K]");

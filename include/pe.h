@@ -74,6 +74,13 @@ typedef struct pe_config {
                          hidden half; wqkv[0] is then [(Hq + 2 Hkv) hd, 2d]. bf16 drafters and pe_draft_step
                          only: caller rows, autoregressive drafting and catch-up steps return
                          PE_ERR_UNSUPPORTED on such a ctx. */
+  int32_t weight_fp8; /* 0: bf16 projection weights. 1: FP8 drafter weights (the pages' deployment
+                         precision): pe_init stores every projection matrix (fc, wqkv, wo, wgate, wup,
+                         wdown, lm_head) as E4M3 codes of w / s_n (round to nearest even) with one float32
+                         scale per output row, s_n = max_k |w[n][k]| / 448 (1 for a zero row); a product
+                         is s_n * (codes . x) with bf16 activations and fp32 accumulation. bf16 drafters,
+                         summed rows, and calls of at most 16 rows per projection only (B (K + 1) <= 16 for
+                         pe_draft_step; others return PE_ERR_UNSUPPORTED). */
 } pe_config;
 
 /* Drafter weights (device, element type = dtype). Must stay valid and unchanged until pe_destroy:

@@ -49,7 +49,7 @@ def shape_weights64(s):
 class GpuDrafter:
     """One workload's synthetic inputs on the GPU plus an initialised pe ctx."""
 
-    def __init__(self, w, state=None, max_batch=None, max_k=None):
+    def __init__(self, w, state=None, max_batch=None, max_k=None, cfg_extra=None):
         import torch
         import eagle_drafting_amd as pe
         self.torch, self.pe, self.w = torch, pe, w
@@ -59,7 +59,7 @@ class GpuDrafter:
         log("upload kv")
         self.kc, self.vc = upload_kv(w, self.state)
         self.d = upload_state(self.state, s.dtype)
-        self.cfg = pe.make_config(**config_args(w, max_batch, max_k))
+        self.cfg = pe.make_config(**{**config_args(w, max_batch, max_k), **(cfg_extra or {})})
         self.stream = torch.cuda.current_stream().cuda_stream
         self.ctx = pe.pe_init(self.cfg, pe.make_weights(self.dev, s.n_layers), pe.make_kv(self.kc, self.vc),
                               self.stream)

@@ -1,0 +1,71 @@
+"""GPU parity of the draft step with FP8 drafter weights (weight_fp8 = 1) against the oracle's draft step on
+the same weights quantized per output row (oracle.weights_fp8: E4M3 codes of w / s_n, s_n = max |w| / 448,
+both sides deciding the codes in float32).
+
+Per request: logits within the row-relative tolerance, draft tokens identical up to the top-2-gap
+exemption, and the K/V of all K + 1 rows within the same tolerance. FP8 weights run on the small-batch
+kernel only, so the workloads keep B (K + 1) <= 16: the headline request, 4 requests at K = 3 (16 layer
+rows, a 12-row vocabulary projection) and one request at K = 11.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import pe_oracle as O
+from synth import QWEN3_CODER, WORKLOADS, Workload
+from tests.gpu_util import TOL, GpuDrafter, check_logits, check_rows, check_tokens, log, oracle_draft, shape_weights64
+
+pytestmark = pytest.mark.gpu
+
+_W8 = {}
+
+
+def _weights_fp8(shape):
+    if shape.name not in _W8:
+        _W8.clear()
+        _W8[shape.name] = O.weights_fp8(shape, shape_weights64(shape))
+    return _W8[shape.name]
+
+
+@pytest.mark.parametrize("name", ["qwen3coder-bf16-B1-K3-L2048", "qwen3coder-bf16-B4-K3-L1024to4096",
+                                  "qwen3coder-bf16-B1-K11-L1024to4096"])
+def test_fp8_weights_parity(name):
+    w = WORKLOADS[name]
+    log(f"FP8 weights parity {name}")
+    tol = TOL[w.shape.dtype]
+    g = GpuDrafter(w, cfg_extra={"weight_fp8": 1})
+    try:
+        draft, z = g.draft()
+        draft, z = draft.cpu().numpy(), z.cpu().numpy()
+        req = list(range(w.B))
+        W8 = _weights_fp8(w.shape)
+        st = dict(g.state)
+        ref = oracle_draft(w, W8, st, w.K, req)
+        err = check_logits(z[req], ref["logits"], tol, w.name)
+        strict, exempt = check_tokens(draft[req], ref["logits"], tol, w.name)
+        kv_err = 0.0
+        for l in range(w.shape.n_layers):
+            for i, b in enumerate(req):
+                k, v = g.kv_rows(l, b, w.K)
+                kv_err = max(kv_err, check_rows(k, ref["k_new"][l][i], tol, f"{w.name} K rows l{l} b{b}"),
+                             check_rows(v, ref["v_new"][l][i], tol, f"{w.name} V rows l{l} b{b}"))
+        # the quantization is visible: the bf16 oracle differs from the FP8 one by more than rounding
+        d_bf16 = oracle_draft(w, shape_weights64(w.shape), st, w.K, req[:1])["logits"][0]
+        rel_q = np.abs(d_bf16 - ref["logits"][0]).max() / np.abs(ref["logits"][0]).max()
+        log(f"  logit err {err:.2e}, kv err {kv_err:.2e}, tokens strict {strict}/{len(req) * w.K}, exempt {exempt}; "
+            f"bf16 vs fp8 oracle {rel_q:.2e}")
+    finally:
+        g.close()
+
+
+def test_fp8_weights_reject_large_calls():
+    w = Workload("qwen3coder-bf16-B4-K4-fp8-args", QWEN3_CODER, 4, 4, (60, 100), 0.7, 8300)
+    g = GpuDrafter(w, cfg_extra={"weight_fp8": 1})
+    try:
+        with pytest.raises(g.pe.PeError) as e:
+            g.draft()  # B (K + 1) = 20 rows
+        assert e.value.status == g.pe.PE_ERR_UNSUPPORTED
+        draft, z = g.draft(K=3)  # 16 rows: runs
+        assert draft.shape == (4, 3)
+    finally:
+        g.close()
