@@ -82,46 +82,54 @@ __global__ __launch_bounds__(256) void fp8_scale_kernel(const bf16_t* __restrict
   if (lane == 0) scales[col] = m > 0.f ? m / 448.f : 1.f;
 }
 
-// fragment (t, s), lane l: 8 codes of source row src(t, l % 16), columns 32 s + 8 (l / 16) .. + 7
+// fragment pair (t, p), lane l: 16 bytes, the 8 codes of k-step 2p then the 8 of k-step 2p + 1, each of
+// source row src(t, l % 16), columns 32 s + 8 (l / 16) .. + 7 (zero past Kd): one 16-byte load per lane
+// brings two k-steps
 __global__ __launch_bounds__(256) void pack_fp8_kernel(const bf16_t* __restrict__ W0, const bf16_t* __restrict__ W1,
-                                                       int N, int Kd, uint2* __restrict__ dst, int Nt, int Ks, int mode,
-                                                       int hd, const float* __restrict__ scales) {
+                                                       int N, int Kd, uint4* __restrict__ dst, int Nt, int Ks2,
+                                                       int mode, int hd, const float* __restrict__ scales) {
   const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const size_t total = (size_t)Nt * Ks * 64;
+  const size_t total = (size_t)Nt * Ks2 * 64;
   if (gid >= total) return;
   const int lane = (int)(gid & 63);
   const size_t frag = gid >> 6;
-  const int s = (int)(frag % Ks);
-  const int t = (int)(frag / Ks);
+  const int pr = (int)(frag % Ks2);
+  const int t = (int)(frag / Ks2);
   int which = 0;
   const int row = pack_src_row(mode, t, lane & 15, hd, &which);
-  const int col = 32 * s + 8 * (lane >> 4);
   const bf16_t* W = which ? W1 : W0;
   const float sc = scales[t * 16 + (lane & 15)];
-  float x[8];
+  uint32_t w4[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float v = 0.f;
-    if (row < N && col + e < Kd) v = bf16_to_f32(W[(size_t)row * Kd + col + e]) / sc;
-    x[e] = fminf(fmaxf(v, -448.f), 448.f);  // |w| / s <= 448 already; the clamp only guards rounding
+  for (int h = 0; h < 2; ++h) {
+    const int col = 32 * (2 * pr + h) + 8 * (lane >> 4);
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = 0.f;
+      if (row < N && col + e < Kd) v = bf16_to_f32(W[(size_t)row * Kd + col + e]) / sc;
+      x[e] = fminf(fmaxf(v, -448.f), 448.f);  // |w| / s <= 448 already; the clamp only guards rounding
+    }
+    uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0u, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], lo, true);
+    uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0u, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], hi, true);
+    w4[2 * h] = lo;
+    w4[2 * h + 1] = hi;
   }
-  uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0u, false);
-  lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], lo, true);
-  uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0u, false);
-  hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], hi, true);
-  dst[frag * 64 + lane] = make_uint2(lo, hi);
+  dst[frag * 64 + lane] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
 }
 
 hipError_t launch_pack_fp8(const void* W0, const void* W1, int N, int Kd, int mode, int hd, void* dst, float* scales,
                            hipStream_t st) {
   if (mode == PACK_KI4) return hipErrorInvalidValue;
   const int Nt = mode == PACK_GATEUP ? (2 * N + 15) / 16 : n_tiles(N);
-  const int Ks = k_steps(Kd);
+  const int Ks2 = (k_steps(Kd) + 1) / 2;
   hipLaunchKernelGGL(fp8_scale_kernel, dim3((unsigned)((Nt * 16 + 3) / 4)), dim3(256), 0, st, (const bf16_t*)W0,
                      (const bf16_t*)W1, N, Kd, Nt, mode, hd, scales);
-  const size_t total = (size_t)Nt * Ks * 64;
+  const size_t total = (size_t)Nt * Ks2 * 64;
   hipLaunchKernelGGL(pack_fp8_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, (const bf16_t*)W0,
-                     (const bf16_t*)W1, N, Kd, (uint2*)dst, Nt, Ks, mode, hd, (const float*)scales);
+                     (const bf16_t*)W1, N, Kd, (uint4*)dst, Nt, Ks2, mode, hd, (const float*)scales);
   return hipGetLastError();
 }
 
@@ -279,7 +287,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
   const int nt = blockIdx.x * NT + tl;
   const int ntc = min(nt, g.Nt - 1);  // clamped tile: a wave past the last tile streams a valid one, unused
   const int m0 = blockIdx.y * MT * 16;
-  const int kps = (Ks + KP - 1) / KP;
+  // (FP8: k parts start on even k-steps, since one 16-byte load brings a pair of k-steps)
+  const int kps = F8 ? (((Ks + KP - 1) / KP + 1) & ~1) : (Ks + KP - 1) / KP;
   const int s_begin = kp * kps;
   const int s_end = min(Ks, s_begin + kps);
   const int nrows = min(MT * 16, M - m0);
@@ -289,7 +298,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const bf16x8_t* wsrc = (const bf16x8_t*)g.Wp_raw + (size_t)ntc * Ks * 64 + lane;
-  const uint2* wsrc8 = (const uint2*)g.Wp_raw + (size_t)ntc * Ks * 64 + lane;
+  const int Ks2 = (Ks + 1) / 2;
+  const uint4* wsrc8 = (const uint4*)g.Wp_raw + (size_t)ntc * Ks2 * 64 + lane;
 
   // Main loop, KC k-steps per round. Every load is unconditional (addresses clamped into range; rows >= M
   // and k-steps past the split are computed but never used), so the weight loads of a round are all in
@@ -300,7 +310,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
   const __amdgpu_buffer_rsrc_t a_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, gemm_a_rows(g) * g.lda * 2, 0x00020000);
   bf16x8_t a[KC][MT], b[KC];
-  uint2 b8[KC];  // FP8: the raw codes, converted just before their product so the loads stay in flight
+  static_assert(KC % 2 == 0, "FP8 loads bring k-steps in pairs");
+  uint4 b8[KC / 2];  // FP8: raw codes of two k-steps, converted just before their products (loads stay in flight)
   // each lane's operand row start (elements), or -1 for a padding row; resolved once, before the loop
   int a_row0[MT];
 #pragma unroll
@@ -325,11 +336,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
         a[kk][mt] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0));
       }
     }
+    if (F8) {
 #pragma unroll
-    for (int kk = 0; kk < KC; ++kk) {
-      const size_t ks = (size_t)min(c0 + min(kk, nk - 1), Ks - 1) * 64;
-      if (F8) b8[kk] = wsrc8[ks];
-      else b[kk] = wsrc[ks];
+      for (int kk = 0; kk < KC; kk += 2)
+        b8[kk / 2] = wsrc8[(size_t)(min(c0 + min(kk, nk - 1), Ks - 1) >> 1) * 64];
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk) b[kk] = wsrc[(size_t)min(c0 + min(kk, nk - 1), Ks - 1) * 64];
     }
   };
   auto mma_round = [&](int c0) {
@@ -337,7 +350,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int kk = 0; kk < KC; ++kk) {
       if (kk < nk) {
-        const bf16x8_t bk = F8 ? fp8x8_to_bf16x8(b8[kk]) : b[kk];
+        const bf16x8_t bk = F8 ? fp8x8_to_bf16x8(kk & 1 ? make_uint2(b8[kk / 2].z, b8[kk / 2].w)
+                                                       : make_uint2(b8[kk / 2].x, b8[kk / 2].y))
+                               : b[kk];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
           acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk][mt], bk, acc[mt], 0, 0, 0);
@@ -577,12 +592,16 @@ static hipError_t launch_split_nw(const GemmPlan& p, const GemmArgs& a, hipStrea
 
 // FP8 weights: the small-batch kernel only (up to 16 rows, 16-column tiles)
 static hipError_t launch_gemm_fp8(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st) {
-  if (p.tiled || p.ki4 || p.MT != 1 || p.NT != 1) return hipErrorInvalidValue;
+  if (p.tiled || p.ki4 || p.MT != 1) return hipErrorInvalidValue;
   if (epi == EPI_ARGMAX) {
     if (a_mode != A_NORM || p.NW != 8) return hipErrorInvalidValue;
-    launch_one<1, 8, 1, A_NORM, EPI_ARGMAX, 0, 1>(p, a, st);
+    if (p.NT == 4) launch_one<1, 8, 4, A_NORM, EPI_ARGMAX, 0, 1>(p, a, st);
+    else if (p.NT == 2) launch_one<1, 8, 2, A_NORM, EPI_ARGMAX, 0, 1>(p, a, st);
+    else if (p.NT == 1) launch_one<1, 8, 1, A_NORM, EPI_ARGMAX, 0, 1>(p, a, st);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
   }
+  if (p.NT != 1) return hipErrorInvalidValue;
   if (a_mode == A_BF16 && epi == EPI_RESID) return launch_split_nw<A_BF16, EPI_RESID, 1>(p, a, st);
   if (a_mode == A_BF16 && epi == EPI_ROWS) return launch_split_nw<A_BF16, EPI_ROWS, 1>(p, a, st);
   if (a_mode == A_NORM && epi == EPI_QKV) return launch_split_nw<A_NORM, EPI_QKV, 1>(p, a, st);

@@ -90,7 +90,7 @@ struct GemmArgs {
   const int* n_real; int rows_real;
   // tiled K-split: fp32 partial tiles [ksplit][M][N] (workspace) and the plan's split shape
   float* part; int ksplit, kper;
-  // FP8 weights (small-batch kernel only): Wp_raw holds E4M3 fragments (8 bytes per lane per k-step) and
+  // FP8 weights (small-batch kernel only): Wp_raw holds E4M3 fragment pairs (16 bytes per lane: two k-steps) and
   // wscale one float per packed output column (tile t, column c at 16 t + c); y = wscale * (q . x)
   const float* wscale;
 };
@@ -111,7 +111,7 @@ __device__ inline int gemm_a_rows(const GemmArgs& g) {
 hipError_t launch_gemm(const GemmPlan& p, GemmArgs a, int a_mode, int epi, hipStream_t st);
 // FP8 repack of one projection (PACK_PLAIN / PACK_PAIRS / PACK_GATEUP layouts): per packed output column the
 // scale s = max |w| / 448 of its source row (1 for a zero row), then E4M3 codes of w / s (round to nearest
-// even) in fragments of 512 bytes (8 codes per lane); dst needs Nt Ks 512 bytes, scales Nt 16 floats
+// even), two k-steps per 16-byte lane chunk; dst needs Nt ceil(Ks / 2) 1024 bytes, scales Nt 16 floats
 hipError_t launch_pack_fp8(const void* W0, const void* W1, int N, int Kd, int mode, int hd, void* dst, float* scales,
                            hipStream_t st);
 hipError_t launch_gemm_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st);
