@@ -69,3 +69,51 @@ def test_fp8_weights_reject_large_calls():
         assert draft.shape == (4, 3)
     finally:
         g.close()
+
+
+def test_fp8_weights_catchup_and_autoregressive():
+    """The other entry points on an FP8 ctx: a catch-up step (R = 4 real-row slots, 7 rows per request)
+    and autoregressive drafting (one row per pass), against the oracle on the quantized weights."""
+    from synth.device import to_device
+    from synth.inputs import catchup_inputs, kv_block, to_f64
+    w = Workload("qwen3coder-bf16-B2-K3-fp8-entry", QWEN3_CODER, 2, 3, (200, 900), 0.7, 8310)
+    tol = TOL[w.shape.dtype]
+    K, R = 3, 4
+    g = GpuDrafter(w, max_k=R + K - 1, cfg_extra={"weight_fp8": 1})
+    torch = g.torch
+    W8 = _weights_fp8(w.shape)
+    st = g.state
+    req = [0, 1]
+
+    def ctx(l, i):
+        L = int(st["seq_len"][i])
+        return (to_f64(kv_block(w, l, 0, i, L), w.shape.dtype), to_f64(kv_block(w, l, 1, i, L), w.shape.dtype))
+
+    try:
+        inp = catchup_inputs(w, R)
+        draft = torch.full((w.B, K), -1, dtype=torch.int32, device="cuda")
+        z = torch.empty((w.B, K, w.shape.vocab), dtype=torch.float32, device="cuda")
+        g.pe.pe_draft_catchup(g.ctx, w.B, K, R, g.d["req_slot"], g.d["seq_len"], to_device(inp["n_real"], "i32"),
+                              to_device(inp["tokens"], "i32"), to_device(inp["target_hidden"], w.shape.dtype), draft, z)
+        torch.cuda.synchronize()
+        ref = O.draft_step_catchup(w.shape, W8, {"tokens": inp["tokens"], "n_real": inp["n_real"],
+                                                 "target_hidden": to_f64(inp["target_hidden"], w.shape.dtype),
+                                                 "seq_len": st["seq_len"]}, ctx, K)
+        err = check_logits(z.cpu().numpy(), ref["logits"], tol, "fp8 catch-up")
+        check_tokens(draft.cpu().numpy(), ref["logits"], tol, "fp8 catch-up")
+        log(f"  fp8 catch-up: logit err {err:.2e}")
+
+        draft.fill_(-1)
+        g.pe.pe_draft_ar(g.ctx, w.B, K, g.d["req_slot"], g.d["seq_len"], g.d["last_token"], g.d["target_hidden"],
+                         draft, z)
+        torch.cuda.synchronize()
+        d_ar = draft.cpu().numpy()
+        ref = O.draft_autoregressive(w.shape, W8, {"last_token": st["last_token"], "seq_len": st["seq_len"],
+                                                   "target_hidden": to_f64(st["target_hidden"], w.shape.dtype)},
+                                     ctx, K, feed=d_ar)
+        for i in range(K):
+            err = check_logits(z.cpu().numpy()[:, i], ref["logits"][:, i], tol, f"fp8 autoregressive pass {i}")
+            check_tokens(d_ar[:, i], ref["logits"][:, i], tol, f"fp8 autoregressive pass {i}")
+        log(f"  fp8 autoregressive: last pass logit err {err:.2e}")
+    finally:
+        g.close()
