@@ -56,6 +56,15 @@ def test_config_validation_host_only(lib):
         assert b.pe_last_error(None)
     # G * max_k beyond one workgroup's query rows
     assert b.pe_config_validate(_good(n_kv_heads=1, max_k=8)) == b.PE_ERR_UNSUPPORTED
+    # the two variants: flags are 0 / 1, bf16 drafters only, and FP8 weights go with summed rows
+    f32 = dict(dtype="f32", d_model=256, n_q_heads=4, n_kv_heads=4, head_dim=64, ffn_dim=512, vocab=4096, max_ctx=128)
+    assert b.pe_config_validate(_good(row_concat=1)) == b.PE_OK
+    assert b.pe_config_validate(_good(weight_fp8=1)) == b.PE_OK
+    assert b.pe_config_validate(_good(row_concat=2)) == b.PE_ERR_INVALID
+    assert b.pe_config_validate(_good(weight_fp8=-1)) == b.PE_ERR_INVALID
+    assert b.pe_config_validate(_good(row_concat=1, **f32)) == b.PE_ERR_UNSUPPORTED
+    assert b.pe_config_validate(_good(weight_fp8=1, **f32)) == b.PE_ERR_UNSUPPORTED
+    assert b.pe_config_validate(_good(weight_fp8=1, row_concat=1)) == b.PE_ERR_UNSUPPORTED
 
 
 def test_status_strings(lib):
