@@ -27,6 +27,17 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((hw_f32x2_t){a, b}, hw_bf16x2_t));
 }
 
+// eight E4M3 codes (one 8-byte fragment lane) as the bf16 MFMA operand; every E4M3 value is exact in bf16
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint2 w) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, true);
+  const f2 c = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, false), d = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, true);
+  const u32x4_t pk = {f32x2_to_bf16x2(a[0], a[1]), f32x2_to_bf16x2(b[0], b[1]), f32x2_to_bf16x2(c[0], c[1]),
+                      f32x2_to_bf16x2(d[0], d[1])};
+  return __builtin_bit_cast(bf16x8_t, pk);
+}
+
 template <typename T> __device__ __forceinline__ float to_f32(T v);
 template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v); }

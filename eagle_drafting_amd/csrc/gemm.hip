@@ -257,17 +257,6 @@ struct KChunk {
   static constexpr int value = MT <= 2 ? 8 : (MT == 4 ? 4 : 2);
 };
 
-// eight E4M3 codes (one 8-byte fragment lane) as the bf16 MFMA operand; every E4M3 value is exact in bf16
-__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint2 w) {
-  typedef float f2 __attribute__((ext_vector_type(2)));
-  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-  const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, true);
-  const f2 c = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, false), d = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, true);
-  const u32x4_t pk = {f32x2_to_bf16x2(a[0], a[1]), f32x2_to_bf16x2(b[0], b[1]), f32x2_to_bf16x2(c[0], c[1]),
-                      f32x2_to_bf16x2(d[0], d[1])};
-  return __builtin_bit_cast(bf16x8_t, pk);
-}
-
 // KI: PACK_KI4 weights (MT == 1, NT == 1, M <= 4): 4-column tiles, activation row m at MFMA rows m + 4h
 // F8: E4M3 weight fragments (8 bytes per lane) with per-column scales applied in the epilogue
 template <int MT, int NW, int NT, int AM, int EP, int KI, int F8 = 0>
@@ -590,8 +579,9 @@ static hipError_t launch_split_nw(const GemmPlan& p, const GemmArgs& a, hipStrea
   return hipErrorInvalidValue;
 }
 
-// FP8 weights: the small-batch kernel only (up to 16 rows, 16-column tiles)
+// FP8 weights: the small-batch kernel (up to 16 rows, 16-column tiles) or the weight-stream kernel
 static hipError_t launch_gemm_fp8(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st) {
+  if (p.tiled == 2) return launch_gemm_tiled(p, a, a_mode, epi, st);  // the weight-stream kernel (17-128 rows)
   if (p.tiled || p.ki4 || p.MT != 1) return hipErrorInvalidValue;
   if (epi == EPI_ARGMAX) {
     if (a_mode != A_NORM || p.NW != 8) return hipErrorInvalidValue;

@@ -18,6 +18,7 @@
 // the logits are coalesced, and per-row reductions (sums of squares, argmax) are 32-lane shuffles. Gate/up
 // and RoPE pairs, which the weight repack put 8 columns apart, are read as two chunks of the same row.
 #include "common.h"
+#include <type_traits>
 #include "kernels.h"
 
 namespace pe {
@@ -486,8 +487,12 @@ __device__ void tile_epilogue(const GemmArgs& g, const float* Cs, const float* s
 // The product tile then goes through LDS (same swizzled layout as above) into the shared epilogues; with
 // SPLIT the workgroup covers k-steps [blockIdx.y * kper, + kper) and writes an fp32 partial tile that
 // gemm_split_reduce_kernel sums in a fixed order.
-template <int AM, int EP, bool SPLIT, int RB, int CH, int NWB>
+// F8: E4M3 weight fragment pairs (16 bytes per lane hold two k-steps' codes), converted to the bf16 operand
+// in registers; each product column is multiplied by its scale as the tile goes to LDS (so K-split partials
+// are already scaled).
+template <int AM, int EP, bool SPLIT, int RB, int CH, int NWB, int F8 = 0>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs g) {
+  static_assert(!F8 || CH % 2 == 0, "FP8 loads bring k-steps in pairs");
   constexpr int BN = 128;
   constexpr int MTL = 2 * RB;                       // 16-row fragments per chunk k-step
   constexpr int ABUF = CH * MTL * 64;               // bf16x8 slots per LDS buffer
@@ -512,15 +517,18 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs g) {
   // offset beyond the buffer), so padded k-steps contribute exact zeros.
   const __amdgpu_buffer_rsrc_t a_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, gemm_a_rows(g) * g.lda * 2, 0x00020000);
+  const int Kw = F8 ? (Ks + 1) / 2 : Ks;  // 1 KiB weight fragments (FP8: fragment pairs) per tile
   const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)g.Wp_raw, (short)0, (int)((uint32_t)Nt * (uint32_t)Ks * 1024u), 0x00020000);
+      (void*)g.Wp_raw, (short)0, (int)((uint32_t)Nt * (uint32_t)Kw * 1024u), 0x00020000);
   auto asw = [](int lp) { return lp ^ ((lp >> 4) << 2); };
   const int fr_t = (lane & 31) >> 4, fr_l = (lane & 15) + 16 * (lane >> 5);
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int w_lane = fr_t * Ks * 1024 + fr_l * 16;
-  const int w_tile = (nt0 + 2 * wv) * Ks * 1024;
+  const int w_lane = fr_t * Kw * 1024 + fr_l * 16;
+  const int w_tile = (nt0 + 2 * wv) * Kw * 1024;
 
-  typedef bf16x8_t RegW[CH][2];
+  typedef bf16x8_t RegW16[CH][2];
+  typedef uint4 RegW8[CH / 2 > 0 ? CH / 2 : 1][2];
+  using RegW = std::conditional_t<(F8 != 0), RegW8, RegW16>;
   typedef bf16x8_t RegA[NPIECE];
   // piece p = tid + 256 q: row p / (4 CH), 16-byte segment p % (4 CH) of the chunk's 32 CH columns
   int a_off[NPIECE];
@@ -546,13 +554,26 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs g) {
     }
   };
   auto gload_w = [&](RegW& r, int c) {
+    if constexpr (F8 != 0) {
+      // k-steps in pairs (kb, kper and CH are even): pair p holds k-steps 2p and 2p + 1
 #pragma unroll
-    for (int ks = 0; ks < CH; ++ks) {
-      const int kstep = kb + CH * c + ks;
-      const int so = kstep < ke ? w_tile + kstep * 1024 : 0x7ffffff0;
+      for (int kp = 0; kp < CH / 2; ++kp) {
+        const int kstep = kb + CH * c + 2 * kp;
+        const int so = kstep < ke ? w_tile + (kstep >> 1) * 1024 : 0x7ffffff0;
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-        r[ks][u] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_lane + 512 * u, so, 0));
+        for (int u = 0; u < 2; ++u)
+          r[kp][u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_lane + 512 * u, so, 0));
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < CH; ++ks) {
+        const int kstep = kb + CH * c + ks;
+        const int so = kstep < ke ? w_tile + kstep * 1024 : 0x7ffffff0;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          r[ks][u] =
+              __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_lane + 512 * u, so, 0));
+      }
     }
   };
 
@@ -569,8 +590,15 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs g) {
         bf16x8_t af[RB];
 #pragma unroll
         for (int i = 0; i < RB; ++i) af[i] = smem[buf * ABUF + (ks * MTL + 2 * i + fr_t) * 64 + asw(fr_l + 32 * u)];
+        bf16x8_t wk;
+        if constexpr (F8 != 0) {
+          const uint4 q = r[ks / 2][u];
+          wk = fp8x8_to_bf16x8(ks & 1 ? make_uint2(q.z, q.w) : make_uint2(q.x, q.y));
+        } else {
+          wk = r[ks][u];
+        }
 #pragma unroll
-        for (int i = 0; i < RB; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], r[ks][u], acc[i], 0, 0, 0);
+        for (int i = 0; i < RB; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], wk, acc[i], 0, 0, 0);
       }
   };
 
@@ -634,12 +662,13 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs g) {
   // product tile -> LDS (row R's columns XOR-swizzled by 32 ((R >> 2) & 1), as the epilogue reads them)
   {
     const int c = lane & 31, hq = lane >> 5;
+    const float wsc = F8 ? g.wscale[min(nt0 * 16 + 32 * wave + c, Nt * 16 - 1)] : 1.f;
 #pragma unroll
     for (int i = 0; i < RB; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int row = 32 * i + 8 * (e >> 2) + 4 * hq + (e & 3);
-        Cs[row * BN + ((32 * wave + c) ^ (hq << 5))] = acc[i][e];
+        Cs[row * BN + ((32 * wave + c) ^ (hq << 5))] = F8 ? acc[i][e] * wsc : acc[i][e];
       }
   }
   if (AM == A_NORM) {
@@ -665,37 +694,29 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs g) {
   else tile_epilogue<EP, AM == A_NORM>(g, Cs, s_inv, 0, nt0, ng, 0, 32 * RB);
 }
 
-template <int RB, int CH, int NWB>
+template <int RB, int CH, int NWB, int F8 = 0>
 static hipError_t launch_stream_rb(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st) {
   const dim3 block(256);
   if (p.ksplit > 1) {
     if (!a.part || epi == EPI_ARGMAX) return hipErrorInvalidValue;
     const dim3 grid(p.ngroups, p.ksplit);
-    if (a_mode == A_BF16) hipLaunchKernelGGL((gemm_stream_kernel<A_BF16, EPI_PARTIAL, true, RB, CH, NWB>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((gemm_stream_kernel<A_NORM, EPI_PARTIAL, true, RB, CH, NWB>), grid, block, 0, st, a);
+    if (a_mode == A_BF16) hipLaunchKernelGGL((gemm_stream_kernel<A_BF16, EPI_PARTIAL, true, RB, CH, NWB, F8>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((gemm_stream_kernel<A_NORM, EPI_PARTIAL, true, RB, CH, NWB, F8>), grid, block, 0, st, a);
     return hipGetLastError();
   }
   const dim3 grid(p.ngroups);
-  if (a_mode == A_BF16 && epi == EPI_RESID) hipLaunchKernelGGL((gemm_stream_kernel<A_BF16, EPI_RESID, false, RB, CH, NWB>), grid, block, 0, st, a);
-  else if (a_mode == A_BF16 && epi == EPI_ROWS) hipLaunchKernelGGL((gemm_stream_kernel<A_BF16, EPI_ROWS, false, RB, CH, NWB>), grid, block, 0, st, a);
-  else if (a_mode == A_NORM && epi == EPI_QKV) hipLaunchKernelGGL((gemm_stream_kernel<A_NORM, EPI_QKV, false, RB, CH, NWB>), grid, block, 0, st, a);
-  else if (a_mode == A_BF16 && epi == EPI_QKV) hipLaunchKernelGGL((gemm_stream_kernel<A_BF16, EPI_QKV, false, RB, CH, NWB>), grid, block, 0, st, a);
-  else if (a_mode == A_NORM && epi == EPI_SWIGLU) hipLaunchKernelGGL((gemm_stream_kernel<A_NORM, EPI_SWIGLU, false, RB, CH, NWB>), grid, block, 0, st, a);
-  else if (a_mode == A_NORM && epi == EPI_ARGMAX) hipLaunchKernelGGL((gemm_stream_kernel<A_NORM, EPI_ARGMAX, false, RB, CH, NWB>), grid, block, 0, st, a);
+  if (a_mode == A_BF16 && epi == EPI_RESID) hipLaunchKernelGGL((gemm_stream_kernel<A_BF16, EPI_RESID, false, RB, CH, NWB, F8>), grid, block, 0, st, a);
+  else if (a_mode == A_BF16 && epi == EPI_ROWS) hipLaunchKernelGGL((gemm_stream_kernel<A_BF16, EPI_ROWS, false, RB, CH, NWB, F8>), grid, block, 0, st, a);
+  else if (a_mode == A_NORM && epi == EPI_QKV) hipLaunchKernelGGL((gemm_stream_kernel<A_NORM, EPI_QKV, false, RB, CH, NWB, F8>), grid, block, 0, st, a);
+  else if (!F8 && a_mode == A_BF16 && epi == EPI_QKV) hipLaunchKernelGGL((gemm_stream_kernel<A_BF16, EPI_QKV, false, RB, CH, NWB>), grid, block, 0, st, a);
+  else if (a_mode == A_NORM && epi == EPI_SWIGLU) hipLaunchKernelGGL((gemm_stream_kernel<A_NORM, EPI_SWIGLU, false, RB, CH, NWB, F8>), grid, block, 0, st, a);
+  else if (a_mode == A_NORM && epi == EPI_ARGMAX) hipLaunchKernelGGL((gemm_stream_kernel<A_NORM, EPI_ARGMAX, false, RB, CH, NWB, F8>), grid, block, 0, st, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-static hipError_t launch_gemm_stream(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st) {
-  if (a.M < 1 || a.M > 128) return hipErrorInvalidValue;
-  // weights one chunk ahead (measured: two chunks ahead, with a six-step unroll, was no faster for the
-  // 88-row vocabulary projection and slower for the four-chunk K-split products)
-  hipError_t e;
-  if (a.M <= 32) e = launch_stream_rb<1, GEMM_STREAM_CH, 2>(p, a, a_mode, epi, st);
-  else if (a.M <= 64) e = launch_stream_rb<2, GEMM_STREAM_CH, 2>(p, a, a_mode, epi, st);
-  else if (a.M <= 96) e = launch_stream_rb<3, GEMM_STREAM_CH, 2>(p, a, a_mode, epi, st);
-  else e = launch_stream_rb<4, GEMM_STREAM_CH, 2>(p, a, a_mode, epi, st);
-  if (e != hipSuccess || p.ksplit <= 1) return e;
+// the K-split partials of a weight-stream product: sum and epilogue
+static hipError_t launch_split_reduce(const GemmPlan& p, const GemmArgs& a, int epi, hipStream_t st) {
   const dim3 rgrid(8 * ((p.ngroups + 7) / 8), 8);  // 16-row slices of each 128-column tile
   const dim3 block(256);
   if (epi == EPI_RESID) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_RESID>), rgrid, block, 0, st, a);
@@ -704,6 +725,28 @@ static hipError_t launch_gemm_stream(const GemmPlan& p, const GemmArgs& a, int a
   else if (epi == EPI_SWIGLU) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_SWIGLU>), rgrid, block, 0, st, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+static hipError_t launch_gemm_stream(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st) {
+  if (a.M < 1 || a.M > 128) return hipErrorInvalidValue;
+  if (a.wscale) {  // FP8 weights
+    hipError_t e;
+    if (a.M <= 32) e = launch_stream_rb<1, GEMM_STREAM_CH, 2, 1>(p, a, a_mode, epi, st);
+    else if (a.M <= 64) e = launch_stream_rb<2, GEMM_STREAM_CH, 2, 1>(p, a, a_mode, epi, st);
+    else if (a.M <= 96) e = launch_stream_rb<3, GEMM_STREAM_CH, 2, 1>(p, a, a_mode, epi, st);
+    else e = launch_stream_rb<4, GEMM_STREAM_CH, 2, 1>(p, a, a_mode, epi, st);
+    if (e != hipSuccess || p.ksplit <= 1) return e;
+    return launch_split_reduce(p, a, epi, st);
+  }
+  // weights one chunk ahead (measured: two chunks ahead, with a six-step unroll, was no faster for the
+  // 88-row vocabulary projection and slower for the four-chunk K-split products)
+  hipError_t e;
+  if (a.M <= 32) e = launch_stream_rb<1, GEMM_STREAM_CH, 2>(p, a, a_mode, epi, st);
+  else if (a.M <= 64) e = launch_stream_rb<2, GEMM_STREAM_CH, 2>(p, a, a_mode, epi, st);
+  else if (a.M <= 96) e = launch_stream_rb<3, GEMM_STREAM_CH, 2>(p, a, a_mode, epi, st);
+  else e = launch_stream_rb<4, GEMM_STREAM_CH, 2>(p, a, a_mode, epi, st);
+  if (e != hipSuccess || p.ksplit <= 1) return e;
+  return launch_split_reduce(p, a, epi, st);
 }
 
 hipError_t launch_gemm_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st) {
