@@ -579,10 +579,10 @@ static hipError_t launch_split_nw(const GemmPlan& p, const GemmArgs& a, hipStrea
   return hipErrorInvalidValue;
 }
 
-// FP8 weights: the small-batch kernel (up to 16 rows, 16-column tiles) or the weight-stream kernel
+// FP8 weights: the small-batch kernel (up to 16 rows, 16-column tiles), or the weight-stream and tiled kernels
 static hipError_t launch_gemm_fp8(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st) {
-  if (p.tiled == 2) return launch_gemm_tiled(p, a, a_mode, epi, st);  // the weight-stream kernel (17-128 rows)
-  if (p.tiled || p.ki4 || p.MT != 1) return hipErrorInvalidValue;
+  if (p.tiled) return launch_gemm_tiled(p, a, a_mode, epi, st);  // weight-stream (17-128 rows) or 128 x 128 tiles
+  if (p.ki4 || p.MT != 1) return hipErrorInvalidValue;
   if (epi == EPI_ARGMAX) {
     if (a_mode != A_NORM || p.NW != 8) return hipErrorInvalidValue;
     if (p.NT == 4) launch_one<1, 8, 4, A_NORM, EPI_ARGMAX, 0, 1>(p, a, st);

@@ -32,7 +32,9 @@ __device__ void tile_epilogue(const GemmArgs& g, const float* Cs, const float* s
 // SPLIT: the workgroup covers k-steps [blockIdx.y * g.kper, + g.kper) and writes its fp32 partial tile
 // (row-scaled for a normalised operand) to g.part[blockIdx.y]; gemm_split_reduce_kernel adds the partials
 // in a fixed order and runs the epilogue.
-template <int AM, int EP, bool SPLIT>
+// F8: E4M3 weight fragment pairs (one 16-byte lane load holds the stage's two k-steps), converted to the
+// bf16 operand in registers; product columns scaled as the tile goes to LDS.
+template <int AM, int EP, bool SPLIT, int F8 = 0>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
   constexpr int BM = 128, BN = 128;
   __shared__ __attribute__((aligned(16))) char smem[2 * 2 * 2 * 8 * 64 * 16];  // 64 KiB: product tile; A buffers in the first half
@@ -60,6 +62,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
   const __amdgpu_buffer_rsrc_t a_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, gemm_a_rows(g) * g.lda * 2, 0x00020000);
   const bf16x8_t* W = (const bf16x8_t*)g.Wp_raw;
+  const uint4* W8 = (const uint4*)g.Wp_raw;  // F8: fragment pairs, (Ks + 1) / 2 per tile
+  const int Ks2 = (Ks + 1) / 2;
 
   // Activations go through LDS (shared by the two waves of a row half); weights go straight from the
   // packed fragments into the registers of the waves that use them (each fragment is needed by the two
@@ -68,7 +72,9 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
   // (row % 16) + 16 (segment % 4) of k-step segment / 4, XOR-swizzled by 4 (segment % 4).
   auto asw = [](int lp) { return lp ^ ((lp >> 4) << 2); };
   typedef bf16x8_t RegA[4];
-  typedef bf16x8_t RegB[8];  // [(ks * 2 + u) * 2 + j]
+  typedef bf16x8_t RegB16[8];  // [(ks * 2 + u) * 2 + j]
+  typedef uint4 RegB8[4];      // F8: [u * 2 + j], both k-steps of the stage
+  using RegB = std::conditional_t<(F8 != 0), RegB8, RegB16>;
   RegA ra0, ra1;
   RegB rb0, rb1;
   // 32 x 32 x 16 products out of the 16 x 32 fragments: lane l of the operand of rows (or columns)
@@ -94,9 +100,16 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
   };
   auto gload_b1 = [&](RegB& r, int st, int idx) {  // idx = (ks * 2 + u) * 2 + j
     const int ks = idx >> 2, u = (idx >> 1) & 1, j = idx & 1;
-    const int kstep = min(kb + 2 * st + ks, Ks - 1);
     const int ntile = min(nt0 + wn * 4 + 2 * j + fr_t, Nt - 1);
-    r[idx] = W[((size_t)ntile * Ks + kstep) * 64 + fr_l + 32 * u];
+    if constexpr (F8 != 0) {
+      if (ks == 0) {  // one load brings both k-steps of the stage (kb and 2 st are even)
+        const int pr = min(kb + 2 * st, Ks - 1) >> 1;
+        r[u * 2 + j] = W8[((size_t)ntile * Ks2 + pr) * 64 + fr_l + 32 * u];
+      }
+    } else {
+      const int kstep = min(kb + 2 * st + ks, Ks - 1);
+      r[idx] = W[((size_t)ntile * Ks + kstep) * 64 + fr_l + 32 * u];
+    }
   };
   auto gload_a = [&](RegA& r, int st) {
 #pragma unroll
@@ -142,10 +155,17 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
       gload_b1(rb_next, st_b, 2 * gi + 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 2; ++j) {
+        bf16x8_t bw;
+        if constexpr (F8 != 0) {
+          const uint4 q = rb[u * 2 + j];
+          bw = fp8x8_to_bf16x8(ks ? make_uint2(q.z, q.w) : make_uint2(q.x, q.y));
+        } else {
+          bw = rb[(ks * 2 + u) * 2 + j];
+        }
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], rb[(ks * 2 + u) * 2 + j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < 2; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bw, acc[i][j], 0, 0, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
       if (gi < 3) {
         af[0] = an[0];
@@ -183,7 +203,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
         for (int e = 0; e < 16; ++e) {
           const int row = 64 * wm + 32 * i + 8 * (e >> 2) + 4 * hq + (e & 3);
           const int col = (64 * wn + 32 * j + c) ^ (hq << 5);
-          Cs[row * BN + col] = acc[i][j][e];
+          Cs[row * BN + col] =
+              F8 ? acc[i][j][e] * g.wscale[min(nt0 * 16 + 64 * wn + 32 * j + c, Nt * 16 - 1)] : acc[i][j][e];
         }
   }
   if (AM == A_NORM) {
@@ -749,15 +770,15 @@ static hipError_t launch_gemm_stream(const GemmPlan& p, const GemmArgs& a, int a
   return launch_split_reduce(p, a, epi, st);
 }
 
-hipError_t launch_gemm_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st) {
-  if (p.tiled == 2) return launch_gemm_stream(p, a, a_mode, epi, st);
+template <int F8>
+static hipError_t launch_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st) {
   const int tiles = 8 * ((p.ngroups + 7) / 8) * p.mblocks;
   const dim3 block(256);
   if (p.ksplit > 1) {
     if (!a.part || epi == EPI_ARGMAX) return hipErrorInvalidValue;
     const dim3 grid(tiles, p.ksplit);
-    if (a_mode == A_BF16) hipLaunchKernelGGL((gemm_tiled_kernel<A_BF16, EPI_PARTIAL, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((gemm_tiled_kernel<A_NORM, EPI_PARTIAL, true>), grid, block, 0, st, a);
+    if (a_mode == A_BF16) hipLaunchKernelGGL((gemm_tiled_kernel<A_BF16, EPI_PARTIAL, true, F8>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((gemm_tiled_kernel<A_NORM, EPI_PARTIAL, true, F8>), grid, block, 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 rgrid(tiles, 8);  // 16-row slices of each tile
@@ -769,14 +790,19 @@ hipError_t launch_gemm_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode, i
     return hipGetLastError();
   }
   const dim3 grid(tiles);
-  if (a_mode == A_BF16 && epi == EPI_RESID) hipLaunchKernelGGL((gemm_tiled_kernel<A_BF16, EPI_RESID, false>), grid, block, 0, st, a);
-  else if (a_mode == A_BF16 && epi == EPI_ROWS) hipLaunchKernelGGL((gemm_tiled_kernel<A_BF16, EPI_ROWS, false>), grid, block, 0, st, a);
-  else if (a_mode == A_NORM && epi == EPI_QKV) hipLaunchKernelGGL((gemm_tiled_kernel<A_NORM, EPI_QKV, false>), grid, block, 0, st, a);
-  else if (a_mode == A_BF16 && epi == EPI_QKV) hipLaunchKernelGGL((gemm_tiled_kernel<A_BF16, EPI_QKV, false>), grid, block, 0, st, a);
-  else if (a_mode == A_NORM && epi == EPI_SWIGLU) hipLaunchKernelGGL((gemm_tiled_kernel<A_NORM, EPI_SWIGLU, false>), grid, block, 0, st, a);
-  else if (a_mode == A_NORM && epi == EPI_ARGMAX) hipLaunchKernelGGL((gemm_tiled_kernel<A_NORM, EPI_ARGMAX, false>), grid, block, 0, st, a);
+  if (a_mode == A_BF16 && epi == EPI_RESID) hipLaunchKernelGGL((gemm_tiled_kernel<A_BF16, EPI_RESID, false, F8>), grid, block, 0, st, a);
+  else if (a_mode == A_BF16 && epi == EPI_ROWS) hipLaunchKernelGGL((gemm_tiled_kernel<A_BF16, EPI_ROWS, false, F8>), grid, block, 0, st, a);
+  else if (a_mode == A_NORM && epi == EPI_QKV) hipLaunchKernelGGL((gemm_tiled_kernel<A_NORM, EPI_QKV, false, F8>), grid, block, 0, st, a);
+  else if (!F8 && a_mode == A_BF16 && epi == EPI_QKV) hipLaunchKernelGGL((gemm_tiled_kernel<A_BF16, EPI_QKV, false>), grid, block, 0, st, a);
+  else if (a_mode == A_NORM && epi == EPI_SWIGLU) hipLaunchKernelGGL((gemm_tiled_kernel<A_NORM, EPI_SWIGLU, false, F8>), grid, block, 0, st, a);
+  else if (a_mode == A_NORM && epi == EPI_ARGMAX) hipLaunchKernelGGL((gemm_tiled_kernel<A_NORM, EPI_ARGMAX, false, F8>), grid, block, 0, st, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st) {
+  if (p.tiled == 2) return launch_gemm_stream(p, a, a_mode, epi, st);
+  return a.wscale ? launch_tiled<1>(p, a, a_mode, epi, st) : launch_tiled<0>(p, a, a_mode, epi, st);
 }
 
 }  // namespace pe

@@ -142,7 +142,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // two, 69 with four)
 static GemmPlan plan_for(const pe_ctx* ctx, int M, int N, int Kd, bool argmax, bool ki4_ok = false) {
   if (!ctx->fp8) return plan_gemm(M, N, Kd, argmax, ki4_ok);
-  if (M > 16) return plan_gemm(M, N, Kd, argmax, false);  // weight-stream kernel (FP8: at most 128 rows)
+  if (M > 16) return plan_gemm(M, N, Kd, argmax, false);  // weight-stream or tiled kernel
   GemmPlan p = plan_gemm(M, N, Kd, argmax, false, true);
   if (argmax && p.MT == 1) {
     p.NT = 4;
@@ -720,7 +720,6 @@ static pe_status run_draft(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* req
   // L_b + K), so the cache holds K/V for every position a verify can accept (accept_len <= K + 1); its
   // outputs are not emitted. Caller-built rows are run as given.
   const int Kr = rows ? K : K + 1;
-  if (ctx->fp8 && B * Kr > 128) return fail(ctx, PE_ERR_UNSUPPORTED, "FP8 weights: at most 128 rows per projection");
   if (ctx->bf16)
     return draft_bf16(ctx, B, Kr, K, req_slot, seq_len, last_token, target_hidden, rows, draft_tokens, logits);
   return draft_f32(ctx, B, Kr, K, req_slot, seq_len, last_token, target_hidden, rows, draft_tokens, logits);
@@ -740,7 +739,6 @@ extern "C" pe_status pe_draft_ar(pe_ctx* ctx, int32_t B, int32_t K, const int32_
   const pe_config& c = ctx->cfg;
   if (!ctx->bf16) return fail(ctx, PE_ERR_UNSUPPORTED, "autoregressive drafting needs a bf16 drafter");
   if (c.row_concat) return fail(ctx, PE_ERR_UNSUPPORTED, "autoregressive drafting with concatenated rows");
-  if (ctx->fp8 && B > 128) return fail(ctx, PE_ERR_UNSUPPORTED, "FP8 weights: at most 128 rows per projection");
   if (B < 1 || B > c.max_batch) return fail(ctx, PE_ERR_INVALID, "B out of [1, max_batch]");
   if (K < 1 || K > c.max_k) return fail(ctx, PE_ERR_INVALID, "K out of [1, max_k]");
   if (!req_slot || !seq_len || !draft_tokens || !last_token || !target_hidden)
@@ -757,8 +755,6 @@ extern "C" pe_status pe_draft_catchup(pe_ctx* ctx, int32_t B, int32_t K, int32_t
   const pe_config& c = ctx->cfg;
   if (!ctx->bf16) return fail(ctx, PE_ERR_UNSUPPORTED, "catch-up steps need a bf16 drafter");
   if (c.row_concat) return fail(ctx, PE_ERR_UNSUPPORTED, "catch-up steps with concatenated rows");
-  if (ctx->fp8 && (long long)B * (R + K) > 128)
-    return fail(ctx, PE_ERR_UNSUPPORTED, "FP8 weights: at most 128 rows per projection");
   if (B < 1 || B > c.max_batch) return fail(ctx, PE_ERR_INVALID, "B out of [1, max_batch]");
   if (K < 1 || K > c.max_k) return fail(ctx, PE_ERR_INVALID, "K out of [1, max_k]");
   if (R < 1 || R + K > c.max_k + 1) return fail(ctx, PE_ERR_INVALID, "R out of [1, max_k + 1 - K]");

@@ -78,9 +78,8 @@ typedef struct pe_config {
                          precision): pe_init stores every projection matrix (fc, wqkv, wo, wgate, wup,
                          wdown, lm_head) as E4M3 codes of w / s_n (round to nearest even) with one float32
                          scale per output row, s_n = max_k |w[n][k]| / 448 (1 for a zero row); a product
-                         is s_n * (codes . x) with bf16 activations and fp32 accumulation. bf16 drafters,
-                         summed rows, and calls of at most 128 rows per projection only (B (K + 1) <= 128
-                         for pe_draft_step; others return PE_ERR_UNSUPPORTED). */
+                         is s_n * (codes . x) with bf16 activations and fp32 accumulation. bf16 drafters
+                         and summed rows only. */
 } pe_config;
 
 /* Drafter weights (device, element type = dtype). Must stay valid and unchanged until pe_destroy:

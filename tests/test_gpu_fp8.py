@@ -4,8 +4,8 @@ both sides deciding the codes in float32).
 
 Per request: logits within the row-relative tolerance, draft tokens identical up to the top-2-gap
 exemption, and the K/V of the K draft rows within the same tolerance. FP8 weights run on the small-batch
-kernel (up to 16 rows: the headline request, 4 requests at K = 3, one request at K = 11) and on the
-weight-stream kernel (17-128 rows: B 4 K 7, B 8 K 11); more rows are rejected.
+kernel (up to 16 rows: the headline request, 4 requests at K = 3, one request at K = 11), on the
+weight-stream kernel (17-128 rows: B 4 K 7, B 8 K 11) and on the 128 x 128 tiled kernel (B 32 K 7).
 """
 
 import numpy as np
@@ -84,15 +84,28 @@ def test_fp8_weights_parity_stream_kernel(name):
         g.close()
 
 
-def test_fp8_weights_reject_large_calls():
-    w = Workload("qwen3coder-bf16-B16-K8-fp8-args", QWEN3_CODER, 16, 8, (60, 100), 0.7, 8300)
+def test_fp8_weights_parity_tiled_kernel():
+    """More than 128 rows per projection: FP8 codes through the 128 x 128 tiled kernel (32 requests at
+    K = 7: 256 layer rows, a 224-row vocabulary projection; K-split partials scaled before the reduce);
+    sampled requests."""
+    w = WORKLOADS["qwen3coder-bf16-B32-K7-L512to4096-churn"]
+    log(f"FP8 weights parity (tiled kernel) {w.name}")
+    tol = TOL[w.shape.dtype]
     g = GpuDrafter(w, cfg_extra={"weight_fp8": 1})
     try:
-        with pytest.raises(g.pe.PeError) as e:
-            g.draft()  # B (K + 1) = 144 rows
-        assert e.value.status == g.pe.PE_ERR_UNSUPPORTED
-        draft, z = g.draft(K=7)  # 128 rows: runs
-        assert draft.shape == (16, 7)
+        draft, z = g.draft()
+        draft, z = draft.cpu().numpy(), z.cpu().numpy()
+        req = [0, 17, w.B - 1]
+        ref = oracle_draft(w, _weights_fp8(w.shape), dict(g.state), w.K, req)
+        err = check_logits(z[req], ref["logits"], tol, w.name)
+        strict, exempt = check_tokens(draft[req], ref["logits"], tol, w.name)
+        kv_err = 0.0
+        for l in range(w.shape.n_layers):
+            for i, b in enumerate(req):
+                k, v = g.kv_rows(l, b, w.K)
+                kv_err = max(kv_err, check_rows(k, ref["k_new"][l][i], tol, f"{w.name} K rows l{l} b{b}"),
+                             check_rows(v, ref["v_new"][l][i], tol, f"{w.name} V rows l{l} b{b}"))
+        log(f"  logit err {err:.2e}, kv err {kv_err:.2e}, tokens strict {strict}/{len(req) * w.K}, exempt {exempt}")
     finally:
         g.close()
 
