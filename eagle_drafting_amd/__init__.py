@@ -10,8 +10,13 @@ from .binding import (  # noqa: F401
     PE_ERR_UNSUPPORTED,
     PE_F32,
     PE_PROF_ATTENTION,
+    PE_PROF_COUNT,
+    PE_PROF_DOWN,
     PE_PROF_GATE_UP,
     PE_PROF_LM_HEAD,
+    PE_PROF_O_PROJ,
+    PE_PROF_QKV,
+    PE_PROF_ROWS,
     PE_PROF_VERIFY_SCAN,
     PeError,
     load_library,

@@ -19,6 +19,8 @@ PE_MAX_K = 16
 PE_OK, PE_ERR_INVALID, PE_ERR_UNSUPPORTED, PE_ERR_OOM, PE_ERR_HIP = 0, 1, 2, 3, 4
 PE_F32, PE_BF16 = 0, 1
 PE_PROF_LM_HEAD, PE_PROF_ATTENTION, PE_PROF_GATE_UP, PE_PROF_VERIFY_SCAN = 0, 1, 2, 3
+PE_PROF_QKV, PE_PROF_O_PROJ, PE_PROF_DOWN, PE_PROF_ROWS = 4, 5, 6, 7
+PE_PROF_COUNT = 8
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpe.so")
 

@@ -541,7 +541,9 @@ static pe_status rows_bf16(pe_ctx* ctx, int32_t B, int32_t Kr, const int32_t* la
   a.wscale = ctx->fp8 ? ctx->s_fc : nullptr;
   a.nssq_out = nssq = gemm_ssq_parts(p);
   hipStream_t st = ctx->stream;
+  LAUNCH(prof_mark(ctx, PE_PROF_ROWS, true));
   LAUNCH(launch_gemm(p, a, A_BF16, EPI_ROWS, st));
+  LAUNCH(prof_mark(ctx, PE_PROF_ROWS, false));
   return PE_OK;
 }
 
@@ -572,16 +574,18 @@ static pe_status layers_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* r
       if (cat)
         LAUNCH(launch_concat_norm(ctx->X, ctx->Xe, (const uint16_t*)w.attn_norm[0], (const uint16_t*)w.embed_norm,
                                   (uint16_t*)ctx->Ucat, M, d, c.rms_eps, st));
+      LAUNCH(prof_mark(ctx, PE_PROF_QKV, true));
       LAUNCH(launch_gemm(plan_for(ctx, M, qkvd, a.Kd, false), a, cat ? A_BF16 : A_NORM, EPI_QKV, st));
+      LAUNCH(prof_mark(ctx, PE_PROF_QKV, false));
     }
     // a5: attention
     AttnPlan ap = plan_attention(B, K, Hq, Hkv, hd, c.max_ctx);
     LAUNCH(prof_mark(ctx, PE_PROF_ATTENTION, true));
     LAUNCH(launch_attention_bf16(ap, ctx->Qb, ctx->kv.k[l], ctx->kv.v[l], seq_len, req_slot, B, K, Hq, Hkv, hd,
                                  c.max_ctx, c.n_slots, ctx->attn, st));
-    LAUNCH(prof_mark(ctx, PE_PROF_ATTENTION, false));
     LAUNCH(launch_attention_combine_bf16(ap, ctx->attn, ctx->Ob, seq_len, req_slot, B, K, Hq, Hkv, hd, c.max_ctx,
                                          c.n_slots, st));
+    LAUNCH(prof_mark(ctx, PE_PROF_ATTENTION, false));
     {  // a6: output projection + residual
       GemmArgs a = base;
       a.M = M; a.Kd = qd; a.N = d;
@@ -591,7 +595,9 @@ static pe_status layers_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* r
       a.Wp_raw = ctx->fp8 ? ctx->q_o[l] : p.ki4 ? ctx->p_o4[l] : ctx->p_o[l];
       a.wscale = ctx->fp8 ? ctx->s_o[l] : nullptr;
       a.nssq_out = nssq = gemm_ssq_parts(p);
+      LAUNCH(prof_mark(ctx, PE_PROF_O_PROJ, true));
       LAUNCH(launch_gemm(p, a, A_BF16, EPI_RESID, st));
+      LAUNCH(prof_mark(ctx, PE_PROF_O_PROJ, false));
     }
     {  // a7: RMSNorm, gate/up, SwiGLU
       GemmArgs a = base;
@@ -615,7 +621,9 @@ static pe_status layers_bf16(pe_ctx* ctx, int32_t B, int32_t K, const int32_t* r
       a.Wp_raw = ctx->fp8 ? ctx->q_down[l] : p.ki4 ? ctx->p_down4[l] : ctx->p_down[l];
       a.wscale = ctx->fp8 ? ctx->s_down[l] : nullptr;
       a.nssq_out = nssq = gemm_ssq_parts(p);
+      LAUNCH(prof_mark(ctx, PE_PROF_DOWN, true));
       LAUNCH(launch_gemm(p, a, A_BF16, EPI_RESID, st));
+      LAUNCH(prof_mark(ctx, PE_PROF_DOWN, false));
     }
   }
   return PE_OK;

@@ -233,10 +233,14 @@ pe_status pe_device_flags(pe_ctx* ctx, int32_t clear, int32_t* flags);
  * summed duration in milliseconds and the number of recorded launches of one kernel. */
 typedef enum {
   PE_PROF_LM_HEAD = 0,     /* LM-head GEMM with fused argmax partials */
-  PE_PROF_ATTENTION = 1,   /* attention main kernel (every layer) */
-  PE_PROF_GATE_UP = 2,     /* MLP gate/up GEMM (every layer) */
+  PE_PROF_ATTENTION = 1,   /* attention: every kernel of it, the split merge included (every layer) */
+  PE_PROF_GATE_UP = 2,     /* MLP gate/up GEMM with SwiGLU (every layer) */
   PE_PROF_VERIFY_SCAN = 3, /* verify's vocabulary argmax scan */
-  PE_PROF_COUNT = 4
+  PE_PROF_QKV = 4,         /* QKV GEMM with RoPE and KV append (every layer) */
+  PE_PROF_O_PROJ = 5,      /* attention output projection + residual (every layer) */
+  PE_PROF_DOWN = 6,        /* MLP down projection + residual (every layer) */
+  PE_PROF_ROWS = 7,        /* input-row build (fc projection + embeddings) */
+  PE_PROF_COUNT = 8
 } pe_prof_kernel;
 pe_status pe_profile_enable(pe_ctx* ctx, int32_t mask);
 pe_status pe_profile_read(pe_ctx* ctx, int32_t which, double* total_ms, int64_t* launches);

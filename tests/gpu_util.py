@@ -1,9 +1,18 @@
 """Helpers of the GPU parity tests: run the HIP path through the C ABI and compare with the oracle.
 
-Tolerances (fixed by the target of this path): per-row relative logit error
-max_v |gpu - oracle| / max_v |oracle| <= 1e-4 for the fp32 drafter and 2e-2 for bf16; draft tokens identical
-except where the oracle's top-2 logit gap is below tol * max_v |oracle|, in which case the GPU's token
-must be within that margin of the oracle's maximum. Verify and compaction outputs are integers: bit-exact.
+Tolerances: per-row relative logit error max_v |gpu - oracle| / max_v |oracle| <= 1e-4 for the fp32
+drafter and 2e-2 for bf16 (fixed by the target of this path); draft tokens identical except where the
+oracle's top-2 logit gap is below tol * max_v |oracle|, in which case the GPU's token must be within that
+margin of the oracle's maximum. Verify and compaction outputs are integers: bit-exact.
+
+K/V rows appended to the cache are checked per (position, kv head), the same row-relative measure over
+hd values. Their tolerance is not fixed by the target (it names logits); KV_TOL derives it from the bf16
+drafter's arithmetic: oracle.bf16_rounding_budget runs the oracle with bf16 rounding at exactly the points
+where the kernels round (normalised operands, queries, cache keys and values, softmax weights, attention and
+SwiGLU outputs; float64 elsewhere) and finds per-head K/V differences from the plain oracle of up to
+1.76e-2 at the last layer of a 15-row catch-up step (1.3e-2 at layer 2), against 1.16e-2 for its logits.
+The kernels add their own float32 accumulation orders and rounding realisations to that, so K/V rows get
+2.5e-2 (bf16) and logits keep 2e-2; the fp32 drafter keeps 1e-4 for both.
 """
 
 from __future__ import annotations
@@ -19,6 +28,7 @@ from synth.device import config_args, to_device, upload_kv, upload_state, upload
 from synth.inputs import kv_block, to_f64
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
+KV_TOL = {"f32": 1e-4, "bf16": 2.5e-2}
 
 
 def log(msg):
@@ -173,5 +183,5 @@ def check_verify(got, T_host_exact, draft, finished, req_slot, seq_len):
     return v, c
 
 
-__all__ = ["TOL", "log", "GpuDrafter", "shape_weights", "shape_weights64", "oracle_draft", "check_logits", "check_rows",
+__all__ = ["TOL", "KV_TOL", "log", "GpuDrafter", "shape_weights", "shape_weights64", "oracle_draft", "check_logits", "check_rows",
            "check_tokens", "run_verify", "check_verify", "to_device"]

@@ -14,7 +14,7 @@ import pytest
 from oracle import pe_oracle as O
 from synth import QWEN3_CODER, WORKLOADS, Workload
 from synth.inputs import kv_block, to_f64
-from tests.gpu_util import TOL, GpuDrafter, check_logits, check_rows, check_tokens, log, shape_weights64
+from tests.gpu_util import KV_TOL, TOL, GpuDrafter, check_logits, check_rows, check_tokens, log, shape_weights64
 
 pytestmark = pytest.mark.gpu
 
@@ -69,8 +69,8 @@ def test_autoregressive_parity(name):
         for l in range(w.shape.n_layers):
             for i, b in enumerate(req):
                 k, v = g.kv_rows(l, b, K + 1)
-                kv_err = max(kv_err, check_rows(k, ref["k_new"][l][i], tol, f"{name} K rows l{l} b{b}"),
-                             check_rows(v, ref["v_new"][l][i], tol, f"{name} V rows l{l} b{b}"))
+                kv_err = max(kv_err, check_rows(k, ref["k_new"][l][i], KV_TOL[w.shape.dtype], f"{name} K rows l{l} b{b}"),
+                             check_rows(v, ref["v_new"][l][i], KV_TOL[w.shape.dtype], f"{name} V rows l{l} b{b}"))
         log(f"  {w.name}: tokens strict {strict}/{len(req) * K}, exempt {exempt}, kv err {kv_err:.2e}")
     finally:
         g.close()

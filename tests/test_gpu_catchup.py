@@ -3,10 +3,10 @@
 Request b runs n_real[b] real rows (an emitted token with the target hidden states that produced it) and
 then placeholder rows, R + K rows in all, from position seq_len[b]; its K drafts come from rows
 n_real[b] - 1 .. n_real[b] + K - 2. Per request: draft logits within the row-relative tolerance, draft
-tokens identical up to the top-2-gap exemption, and the K/V of all R + K rows within the same tolerance,
-each position's row taken over all kv heads (Hkv * hd values), as a logits row is taken over the whole
-vocabulary. (Taken per head, the 128-value rows of the 15-row B 8 K 7 case reach 2.0e-2 at the
-bf16 tolerance's edge: a request with one real row runs 14 placeholder rows through 4 layers.)
+tokens identical up to the top-2-gap exemption, and the K/V of all R + K rows per (position, kv head), as
+in every other draft test, within the K/V tolerance of tests/gpu_util.py (derived there from the bf16
+drafter's rounding points; the 15-row case here is the one that sets it: the rounding-point oracle alone
+reaches 1.76e-2 per head at its last layer).
 Row counts cover the small-batch kernels, the weight-stream kernel (the row build too) and the 128 x 128
 tiled kernel; n_real mixes 1 (a plain step) and R (a fully accepted previous step).
 """
@@ -18,7 +18,7 @@ from oracle import pe_oracle as O
 from synth import QWEN3_CODER, TINY_FP32, Workload
 from synth.device import to_device
 from synth.inputs import catchup_inputs, kv_block, to_f64
-from tests.gpu_util import TOL, GpuDrafter, check_logits, check_rows, check_tokens, log, shape_weights64
+from tests.gpu_util import KV_TOL, TOL, GpuDrafter, check_logits, check_rows, check_tokens, log, shape_weights64
 
 pytestmark = pytest.mark.gpu
 
@@ -47,6 +47,17 @@ def _oracle_catchup(w, W64, state, K, inp, req):
     return O.draft_step_catchup(w.shape, W64, st, ctx, K)
 
 
+def _check_kv(g, ref, req, rows, tol):
+    """Every layer's K and V rows of the sampled requests, row-relative per (position, kv head)."""
+    err = 0.0
+    for l in range(g.w.shape.n_layers):
+        for i, b in enumerate(req):
+            k, v = g.kv_rows(l, b, rows)  # [rows, Hkv, hd]
+            err = max(err, check_rows(k, ref["k_new"][l][i], tol, f"{g.w.name} K rows l{l} b{b}"),
+                      check_rows(v, ref["v_new"][l][i], tol, f"{g.w.name} V rows l{l} b{b}"))
+    return err
+
+
 CASES = [  # B, K, R: layer rows B (R + K), LM-head rows B K
     (1, 3, 4),    # 7 / 3: small-batch kernels, a fully accepted previous step
     (4, 3, 4),    # 28 / 12: layers on the weight-stream kernel, LM head on the stream kernel
@@ -70,16 +81,7 @@ def test_catchup_parity(B, K, R):
         ref = _oracle_catchup(w, shape_weights64(w.shape), g.state, K, inp, req)
         err = check_logits(z[req], ref["logits"], tol, w.name)
         strict, exempt = check_tokens(draft[req], ref["logits"], tol, w.name)
-        kv_err = 0.0
-        for l in range(w.shape.n_layers):
-            for i, b in enumerate(req):
-                k, v = g.kv_rows(l, b, R + K)
-                # row-relative per position over all kv heads ([R + K, Hkv * hd]), as logits are per position
-                # over the vocabulary
-                kv_err = max(kv_err, check_rows(k.reshape(R + K, -1), ref["k_new"][l][i].reshape(R + K, -1), tol,
-                                                f"{w.name} K rows l{l} b{b}"),
-                             check_rows(v.reshape(R + K, -1), ref["v_new"][l][i].reshape(R + K, -1), tol,
-                                        f"{w.name} V rows l{l} b{b}"))
+        kv_err = _check_kv(g, ref, req, R + K, KV_TOL[w.shape.dtype])
         log(f"  logit err {err:.2e}, kv err {kv_err:.2e}, tokens strict {strict}/{len(req) * K}, exempt {exempt}")
     finally:
         g.close()
@@ -102,8 +104,9 @@ def test_catchup_parity_bench_workloads(name, R):
         ref = _oracle_catchup(w, shape_weights64(w.shape), g.state, K, inp, req)
         err = check_logits(z[req], ref["logits"], tol, w.name)
         strict, exempt = check_tokens(draft[req], ref["logits"], tol, w.name)
-        log(f"  n_real {inp['n_real'][req].tolist()}, logit err {err:.2e}, tokens strict {strict}/{len(req) * K}, "
-            f"exempt {exempt}")
+        kv_err = _check_kv(g, ref, req, R + K, KV_TOL[w.shape.dtype])
+        log(f"  n_real {inp['n_real'][req].tolist()}, logit err {err:.2e}, kv err {kv_err:.2e}, "
+            f"tokens strict {strict}/{len(req) * K}, exempt {exempt}")
     finally:
         g.close()
 

@@ -16,7 +16,7 @@ from oracle import pe_oracle as O
 from synth import Workload
 from synth.inputs import kv_block, to_f64
 from synth.workloads import QWEN3_CODER_CONCAT
-from tests.gpu_util import TOL, GpuDrafter, check_logits, check_rows, check_tokens, log, shape_weights64
+from tests.gpu_util import KV_TOL, TOL, GpuDrafter, check_logits, check_rows, check_tokens, log, shape_weights64
 
 pytestmark = pytest.mark.gpu
 
@@ -50,8 +50,8 @@ def test_concat_rows_parity(B, K):
         for l in range(w.shape.n_layers):
             for i, b in enumerate(req):
                 k, v = g.kv_rows(l, b, K + 1)
-                kv_err = max(kv_err, check_rows(k, ref["k_new"][l][i], tol, f"{w.name} K rows l{l} b{b}"),
-                             check_rows(v, ref["v_new"][l][i], tol, f"{w.name} V rows l{l} b{b}"))
+                kv_err = max(kv_err, check_rows(k, ref["k_new"][l][i], KV_TOL[w.shape.dtype], f"{w.name} K rows l{l} b{b}"),
+                             check_rows(v, ref["v_new"][l][i], KV_TOL[w.shape.dtype], f"{w.name} V rows l{l} b{b}"))
         log(f"  logit err {err:.2e}, kv err {kv_err:.2e}, tokens strict {strict}/{len(req) * K}, exempt {exempt}")
     finally:
         g.close()

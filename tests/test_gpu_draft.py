@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from synth import WORKLOADS, Workload, TINY_FP32, QWEN3_CODER, make_state
-from tests.gpu_util import (TOL, GpuDrafter, check_logits, check_rows, check_tokens, log, oracle_draft,
+from tests.gpu_util import (KV_TOL, TOL, GpuDrafter, check_logits, check_rows, check_tokens, log, oracle_draft,
                             shape_weights64)
 
 pytestmark = pytest.mark.gpu
@@ -32,8 +32,9 @@ def _parity(g, requests, K=None, rows=None, rows_host=None, check_kv=True):
         for l in range(w.shape.n_layers):
             for i, b in enumerate(req):
                 k, v = g.kv_rows(l, b, K)
-                kv_err = max(kv_err, check_rows(k, ref["k_new"][l][i], tol, f"{w.name} K rows l{l} b{b}"),
-                             check_rows(v, ref["v_new"][l][i], tol, f"{w.name} V rows l{l} b{b}"))
+                kt = KV_TOL[w.shape.dtype]
+                kv_err = max(kv_err, check_rows(k, ref["k_new"][l][i], kt, f"{w.name} K rows l{l} b{b}"),
+                             check_rows(v, ref["v_new"][l][i], kt, f"{w.name} V rows l{l} b{b}"))
     log(f"  {w.name}: requests {req[:6]}{'...' if len(req) > 6 else ''} logit err {err:.2e}, kv err {kv_err:.2e}, "
         f"tokens strict {strict}/{len(req) * K}, exempt {exempt}")
     return draft, z, ref

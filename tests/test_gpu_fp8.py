@@ -13,7 +13,7 @@ import pytest
 
 from oracle import pe_oracle as O
 from synth import QWEN3_CODER, WORKLOADS, Workload
-from tests.gpu_util import TOL, GpuDrafter, check_logits, check_rows, check_tokens, log, oracle_draft, shape_weights64
+from tests.gpu_util import KV_TOL, TOL, GpuDrafter, check_logits, check_rows, check_tokens, log, oracle_draft, shape_weights64
 
 pytestmark = pytest.mark.gpu
 
@@ -47,8 +47,8 @@ def test_fp8_weights_parity(name):
         for l in range(w.shape.n_layers):
             for i, b in enumerate(req):
                 k, v = g.kv_rows(l, b, w.K)
-                kv_err = max(kv_err, check_rows(k, ref["k_new"][l][i], tol, f"{w.name} K rows l{l} b{b}"),
-                             check_rows(v, ref["v_new"][l][i], tol, f"{w.name} V rows l{l} b{b}"))
+                kv_err = max(kv_err, check_rows(k, ref["k_new"][l][i], KV_TOL[w.shape.dtype], f"{w.name} K rows l{l} b{b}"),
+                             check_rows(v, ref["v_new"][l][i], KV_TOL[w.shape.dtype], f"{w.name} V rows l{l} b{b}"))
         # the quantization is visible: the bf16 oracle differs from the FP8 one by more than rounding
         d_bf16 = oracle_draft(w, shape_weights64(w.shape), st, w.K, req[:1])["logits"][0]
         rel_q = np.abs(d_bf16 - ref["logits"][0]).max() / np.abs(ref["logits"][0]).max()
@@ -77,8 +77,8 @@ def test_fp8_weights_parity_stream_kernel(name):
         for l in range(w.shape.n_layers):
             for i, b in enumerate(req):
                 k, v = g.kv_rows(l, b, w.K)
-                kv_err = max(kv_err, check_rows(k, ref["k_new"][l][i], tol, f"{w.name} K rows l{l} b{b}"),
-                             check_rows(v, ref["v_new"][l][i], tol, f"{w.name} V rows l{l} b{b}"))
+                kv_err = max(kv_err, check_rows(k, ref["k_new"][l][i], KV_TOL[w.shape.dtype], f"{w.name} K rows l{l} b{b}"),
+                             check_rows(v, ref["v_new"][l][i], KV_TOL[w.shape.dtype], f"{w.name} V rows l{l} b{b}"))
         log(f"  logit err {err:.2e}, kv err {kv_err:.2e}, tokens strict {strict}/{len(req) * w.K}, exempt {exempt}")
     finally:
         g.close()
@@ -103,8 +103,8 @@ def test_fp8_weights_parity_tiled_kernel():
         for l in range(w.shape.n_layers):
             for i, b in enumerate(req):
                 k, v = g.kv_rows(l, b, w.K)
-                kv_err = max(kv_err, check_rows(k, ref["k_new"][l][i], tol, f"{w.name} K rows l{l} b{b}"),
-                             check_rows(v, ref["v_new"][l][i], tol, f"{w.name} V rows l{l} b{b}"))
+                kv_err = max(kv_err, check_rows(k, ref["k_new"][l][i], KV_TOL[w.shape.dtype], f"{w.name} K rows l{l} b{b}"),
+                             check_rows(v, ref["v_new"][l][i], KV_TOL[w.shape.dtype], f"{w.name} V rows l{l} b{b}"))
         log(f"  logit err {err:.2e}, kv err {kv_err:.2e}, tokens strict {strict}/{len(req) * w.K}, exempt {exempt}")
     finally:
         g.close()

@@ -1,12 +1,28 @@
 """GPU parity of pe_verify_sampled (temperature > 0) against the oracle's verify_sampled.
 
 Inputs: the harness's draft tokens, planted target logits, and seeded uniforms. The oracle decides in
-float64 and the kernels in float32, so acceptance uniforms closer than 1e-3 to their decision boundary
-p_i(draft) are redrawn (then every acceptance decision is fixed). The accepted drafts, accept_len and all
-integer metadata must then match exactly. The draw after the accepted drafts must be a token that an exact
-inverse-CDF draw picks for a threshold within 1e-4 of the total weight of the given one (the float32 sums
-over up to 201088 weights differ from the float64 ones by far less), and must carry weight (never the
-rejected draft).
+float64 and the kernels in float32, so a decision whose float64 margin is below the float32 error bound
+of the kernels' arithmetic is not fixed by the definition alone. That bound, relative to the quantity it
+bounds, is derived from how the kernels compute (unit roundoff 2^-24):
+
+  * each weight exp(x / tau - m): the product x * (1 / tau) rounds once, an error of at most A ulp in the
+    exponent with A = max |x| / tau over the row; the subtraction and the exponential's own scaling give
+    at most |x / tau - m| ulp more and the hardware exp2 two more. Summed over a row, the |x / tau - m|
+    parts weigh sum_t w_t |log w_t| <= 2 S ln V (w_t <= 1, S = sum w_t), so a total S or a weight carries
+    at most (A + 4 ln V + 2) ulp from the exponentials;
+  * each lane's running sum over its ~32 elements of a 2048-token chunk (an add, or a rescale with a
+    multiply and an add: three roundings per element), then at most 20 pairwise merges (shuffles, waves,
+    chunks; three roundings each): 3 (32 + 20) ulp;
+  * the acceptance test u < ed / S divides two such quantities: p carries at most twice the above;
+  * a draw compares its threshold v (S - ed) with a running total over up to nchunks chunk totals (one
+    rounding each) and a 256-thread block scan inside the chunk (~40 roundings).
+
+The tests take twice that bound: an acceptance uniform within w_acc * p of p_i(draft) is redrawn (about
+3e-5 * p to 5e-5 * p here, against the former 1e-3 absolute), and a draw passes if it is the token an exact
+inverse-CDF draw picks for a threshold within w_draw * total of the given one (about 5e-5 of the row's
+mass). The accepted drafts, accept_len and all integer metadata must then match exactly, and a drawn token
+must carry weight (never the rejected draft). test_sampled_verify_near_boundaries places uniforms at 1.5
+times these windows on either side of a decision, so decisions next to their boundary are exercised.
 """
 
 import numpy as np
@@ -20,7 +36,21 @@ from tests.test_gpu_verify import VerifyCtx
 
 pytestmark = pytest.mark.gpu
 
-TOL_DRAW = 1e-4
+ULP = 2.0 ** -24
+
+
+def _window_acc(row, tau):
+    """Twice the float32 bound on the relative error of p(x) for one target row (docstring)."""
+    A = float(np.abs(row).max()) / tau
+    return 2.0 * (2 * A + 8 * np.log(row.shape[-1]) + 3 * (32 + 20) + 10) * ULP
+
+
+def _window_draw(row, tau):
+    """Twice the float32 bound on a draw's threshold and running totals, relative to the row's mass."""
+    V = row.shape[-1]
+    nchunks = -(-V // 2048)  # the kernels' ~2048-token chunks
+    A = float(np.abs(row).max()) / tau
+    return 2.0 * (2 * A + 8 * np.log(V) + 3 * (32 + 20) + nchunks + 40) * ULP
 
 
 def _exact(T, dtype):
@@ -28,14 +58,15 @@ def _exact(T, dtype):
 
 
 def _uniforms(T, draft, tau, seed):
-    """u [B, K] away from every p_i(draft) by at least 1e-3, v [B, K+1]."""
+    """u [B, K] outside the float32 window around every p_i(draft), v [B, K+1]."""
     rng = np.random.default_rng(seed)
     B, K = draft.shape
     u = rng.random((B, K))
     for b in range(B):
         for i in range(K):
             p = O.softmax_temperature(T[b, i], tau)[draft[b, i]]
-            while abs(u[b, i] - p) < 1e-3:
+            w = _window_acc(T[b, i], tau) * p
+            while abs(float(np.float32(u[b, i])) - p) <= w:
                 u[b, i] = rng.random()
     v = rng.random((B, K + 1))
     return u.astype(np.float32), v.astype(np.float32)
@@ -77,9 +108,10 @@ def _check(got, T, draft, tau, u, v, finished, slot, seq):
             w[draft[b, n]] = 0.0
         c = np.cumsum(w)
         theta = float(v[b, n]) * c[-1]
-        lo = c[x - 1] if x > 0 else 0.0
+        tol = _window_draw(T[b, n], tau) * c[-1]
         assert 0 <= x < w.shape[0] and w[x] > 0.0, f"request {b}: drew a token without weight ({x})"
-        assert lo <= theta + TOL_DRAW * c[-1] and c[x] > theta - TOL_DRAW * c[-1], \
+        lo = c[x - 1] if x > 0 else 0.0
+        assert lo <= theta + tol and c[x] > theta - tol, \
             f"request {b}: draw {x} inconsistent with the threshold (oracle {ref['t'][b, n]})"
         t_gpu[b, : n + 1] = toks
     mine = {"t": t_gpu, "accept_len": got["accept_len"], "bonus": t_gpu[np.arange(B), ref["n"]]}
@@ -118,6 +150,71 @@ def test_sampled_verify_parity(name, tau):
         ctx.close()
     ref, _ = _check(got, T_exact, draft, tau, u, v, fin, st["req_slot"], st["seq_len"])
     log(f"  mean accept_len {ref['accept_len'].mean():.3f}")
+
+
+@pytest.mark.parametrize("V,dtype", [(4096, "f32"), (151936, "bf16")])
+def test_sampled_verify_near_boundaries(V, dtype):
+    """Decisions placed just outside the float32 window (1.5 times the doubled bound) on either side of
+    their boundary. Request b accepts its drafts before position b % (K + 1) with u just below p_i(draft),
+    rejects there with u just above it (or, at K, makes the bonus draw); the draw's threshold sits just
+    past the start of a chosen token's bin (even b) or just short of its end (odd b). Every decision is
+    then fixed by the definition, and the GPU must take it: accept_len, the accepted drafts and the drawn
+    token exactly."""
+    rng = np.random.default_rng(91 + V)
+    B, K, tau = 8, 3, 0.3
+    T = rng.standard_normal((B, K + 1, V)).astype(np.float32) * 2.0
+    if dtype == "bf16":
+        from synth.inputs import bf16_bits
+        T_dev_host = bf16_bits(T)
+        T = bf16_bits_to_f32(T_dev_host)
+    else:
+        T_dev_host = T
+    draft = np.empty((B, K), dtype=np.int32)
+    u = np.empty((B, K), dtype=np.float64)
+    v = rng.random((B, K + 1))
+    want_tok = np.empty(B, dtype=np.int64)
+    for b in range(B):
+        n = b % (K + 1)
+        for i in range(K):
+            p = O.softmax_temperature(T[b, i], tau)
+            # a draft with enough mass that u = p (1 +- 1.5 w) stays inside (0, 1)
+            draft[b, i] = int(np.argsort(p)[-2 - (b + i) % 3])
+            w = 1.5 * _window_acc(T[b, i], tau)
+            u[b, i] = p[draft[b, i]] * (1.0 - w) if i < n else p[draft[b, i]] * (1.0 + w)
+            assert 0.0 < u[b, i] < 1.0
+        # the draw at position n: weights without the rejected draft (n < K) or p_K itself
+        wts = O.softmax_temperature(T[b, n], tau)
+        if n < K:
+            wts[draft[b, n]] = 0.0
+        c = np.cumsum(wts)
+        tot = c[-1]
+        tol = 1.5 * _window_draw(T[b, n], tau) * tot
+        heavy = [int(o) for o in np.argsort(wts)[::-1][:6] if wts[o] > 4 * tol]
+        x = heavy[b % len(heavy)]  # a heavy token, not always the heaviest
+        lo = c[x - 1] if x > 0 else 0.0
+        theta = lo + tol if b % 2 == 0 else c[x] - tol
+        v[b, n] = theta / tot
+        want_tok[b] = x
+    u32, v32 = u.astype(np.float32), v.astype(np.float32)
+    # the float32 uniforms keep every decision on its side (their rounding is far inside the windows)
+    ref = O.verify_sampled(T, draft, tau, u32.astype(np.float64), v32.astype(np.float64))
+    assert np.array_equal(ref["n"], np.arange(B) % (K + 1))
+    assert np.array_equal(ref["bonus"], want_tok)
+    slot = np.arange(B, dtype=np.int32)
+    seq = np.full(B, 100, dtype=np.int32)
+    ctx = VerifyCtx(V, dtype, B, K)
+    try:
+        got = _run(ctx.pe, ctx.ctx, to_device(T_dev_host, dtype), draft, tau, u32, v32, None, slot, seq)
+    finally:
+        ctx.close()
+    assert np.array_equal(got["accept_len"], ref["accept_len"])
+    cu = got["cu_accept"]
+    for b in range(B):
+        n = int(ref["n"][b])
+        toks = got["out_tokens"][cu[b]:cu[b + 1]]
+        assert np.array_equal(toks[:n], draft[b, :n])
+        assert int(toks[n]) == want_tok[b], (b, int(toks[n]), want_tok[b])
+    _check(got, T, draft, tau, u32, v32, None, slot, seq)
 
 
 def test_sampled_verify_rejects_bad_temperature():

@@ -763,3 +763,28 @@ def test_sampled_verify_near_zero_temperature_is_greedy():
     assert np.array_equal(s["bonus"], g["bonus"])
     for b in range(B):
         assert np.array_equal(s["t"][b, :g["accept_len"][b]], g["t"][b, :g["accept_len"][b]])
+
+
+def test_weights_fp8_quantizes_exactly_the_projection_matrices():
+    # the FP8 reading stores the seven projection matrices (fc, every layer's wqkv / wo / wgate / wup / wdown,
+    # lm_head) as per-row E4M3 codes; everything else (embedding table, mask embedding, shared hidden, norm
+    # gains) keeps its exact value. Checked key by key on a 2-layer drafter.
+    W = _weights64(MINI, 63)
+    Q = O.weights_fp8(MINI, W)
+    assert set(Q) == set(W)
+    proj = {"fc", "lm_head"} | {f"l{l}.{n}" for l in range(MINI.n_layers)
+                                for n in ("wqkv", "wo", "wgate", "wup", "wdown")}
+    assert proj <= set(W) and len(proj) == 2 + 5 * MINI.n_layers
+    for k, v in W.items():
+        if k in proj:
+            assert Q[k].shape == v.shape
+            assert not np.array_equal(Q[k], v), f"{k}: not quantized"
+            # every row is the per-row quantization of that source row alone
+            for n in (0, v.shape[0] // 2, v.shape[0] - 1):
+                assert np.array_equal(Q[k][n], O.quantize_fp8_rows(v[n:n + 1])[0]), (k, n)
+            # and every value sits on its row's E4M3 grid: q / s is an E4M3 value
+            s = np.float64(np.float32(np.abs(v.astype(np.float32)).max(axis=1)) / np.float32(448.0))
+            codes = Q[k] / s[:, None]
+            assert np.array_equal(O.fp8_e4m3_round(codes), codes), k
+        else:
+            assert np.array_equal(Q[k], v), f"{k}: changed by the FP8 conversion"
