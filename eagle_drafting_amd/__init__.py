@@ -39,5 +39,6 @@ from .binding import (  # noqa: F401
     pe_status_string,
     pe_verify,
     pe_verify_sampled,
+    pe_verify_static,
     pe_weights,
 )

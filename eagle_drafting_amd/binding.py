@@ -25,7 +25,7 @@ PE_PROF_COUNT = 8
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpe.so")
 
 EXPORTED = ["pe_config_validate", "pe_init", "pe_draft_step", "pe_draft_rows", "pe_draft_ar", "pe_draft_catchup",
-            "pe_verify", "pe_verify_sampled",
+            "pe_verify", "pe_verify_sampled", "pe_verify_static",
             "pe_destroy",
             "pe_device_flags", "pe_profile_enable", "pe_profile_read", "pe_status_string", "pe_last_error"]
 
@@ -91,6 +91,7 @@ def load_library(path: str = LIB_PATH):
         "pe_verify": ([vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp], i32),
         "pe_verify_sampled": ([vp, i32, i32, vp, vp, c_float, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
                               i32),
+        "pe_verify_static": ([i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp], i32),
         "pe_destroy": ([vp], i32),
         "pe_device_flags": ([vp, i32, POINTER(i32)], i32),
         "pe_profile_enable": ([vp, i32], i32),
@@ -178,6 +179,18 @@ def pe_verify_sampled(ctx, B, K, target_logits, draft_tokens, temperature, u, v,
         _ptr(n_keep), _ptr(req_slot_next), _ptr(seq_len_next), _ptr(last_token_next)), ctx)
 
 
+def pe_verify_static(B, K, vocab, dtype, target_logits, draft_tokens, finished, req_slot, seq_len, accept_len,
+                     cu_accept, out_tokens, keep_index, n_keep, req_slot_next, seq_len_next, last_token_next,
+                     stream=0):
+    """pe_verify without a ctx and without allocating (static scratch inside the library).
+    dtype: "f32" / "bf16" or PE_F32 / PE_BF16."""
+    dt = {"f32": PE_F32, "bf16": PE_BF16}.get(dtype, dtype)
+    _check(load_library().pe_verify_static(
+        B, K, vocab, int(dt), _ptr(target_logits), _ptr(draft_tokens), _ptr(finished), _ptr(req_slot),
+        _ptr(seq_len), _ptr(accept_len), _ptr(cu_accept), _ptr(out_tokens), _ptr(keep_index), _ptr(n_keep),
+        _ptr(req_slot_next), _ptr(seq_len_next), _ptr(last_token_next), stream or None))
+
+
 def pe_destroy(ctx):
     _check(load_library().pe_destroy(ctx))
 
@@ -188,7 +201,7 @@ def pe_device_flags(ctx, clear: bool = False) -> int:
     return out.value
 
 
-def pe_profile_enable(ctx, mask: int = (1 << 4) - 1):
+def pe_profile_enable(ctx, mask: int = (1 << PE_PROF_COUNT) - 1):
     """Record per-launch events for the kernels whose bit (1 << PE_PROF_*) is set; 0 stops."""
     _check(load_library().pe_profile_enable(ctx, int(mask)), ctx)
 

@@ -2,6 +2,7 @@
 // weight repacking, and the launch sequence of one parallel draft step and one greedy verify.
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -830,5 +831,77 @@ extern "C" pe_status pe_verify(pe_ctx* ctx, int32_t B, int32_t K, const void* ta
   LAUNCH(launch_accept_compact(ctx->am_val, ctx->am_idx, nch, B, K, draft_tokens, finished, req_slot, seq_len,
                                ctx->t_ws, accept_len, cu_accept, out_tokens, keep_index, n_keep, req_slot_next,
                                seq_len_next, last_token_next, st));
+  return PE_OK;
+}
+
+// ---- greedy verify without a ctx: scratch in a static device array ----------------------------------
+// The argmax partials and target tokens of pe_verify live in `scratch`, a file-scope device array of which
+// every GPU holds its own copy. In host code its name is only a stand-in for the symbol, so each device's
+// address is looked up once (hipGetSymbolAddress with that device current) and only that address is passed
+// to the kernels.
+static __device__ __align__(256) char scratch[PE_VERIFY_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_dev[kMaxDevices] = {};
+}  // namespace
+
+static pe_status static_scratch(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(nullptr, PE_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(nullptr, PE_ERR_UNSUPPORTED, "device index beyond 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(nullptr, PE_ERR_HIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+      return fail(nullptr, PE_ERR_UNSUPPORTED, std::string("device is ") + prop.gcnArchName + ", not gfx950");
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(nullptr, PE_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_dev[dev] = (char*)p;
+  }
+  *out = g_scratch_dev[dev];
+  return PE_OK;
+}
+
+extern "C" pe_status pe_verify_static(int32_t B, int32_t K, int32_t vocab, pe_dtype dtype, const void* target_logits,
+                                      const int32_t* draft_tokens, const uint8_t* finished, const int32_t* req_slot,
+                                      const int32_t* seq_len, int32_t* accept_len, int32_t* cu_accept,
+                                      int32_t* out_tokens, int32_t* keep_index, int32_t* n_keep,
+                                      int32_t* req_slot_next, int32_t* seq_len_next, int32_t* last_token_next,
+                                      void* stream) {
+  if (B < 1 || B > PE_MAX_BATCH) return fail(nullptr, PE_ERR_INVALID, "B out of [1, 1024]");
+  if (K < 1 || K > PE_MAX_K) return fail(nullptr, PE_ERR_INVALID, "K out of [1, 16]");
+  if (vocab < 8 || vocab % 8) return fail(nullptr, PE_ERR_INVALID, "vocab must be a positive multiple of 8");
+  if (dtype != PE_F32 && dtype != PE_BF16) return fail(nullptr, PE_ERR_INVALID, "dtype must be PE_F32 or PE_BF16");
+  if (!target_logits || !draft_tokens || !req_slot || !seq_len || !accept_len || !cu_accept || !out_tokens ||
+      !keep_index || !n_keep || !req_slot_next || !seq_len_next || !last_token_next)
+    return fail(nullptr, PE_ERR_INVALID, "NULL argument");
+  if ((uintptr_t)target_logits & 15) return fail(nullptr, PE_ERR_INVALID, "target_logits not 16-byte aligned");
+  // scratch layout: argmax partial values [rows, nch], their indices [rows, nch], target tokens [B, K + 1]
+  const int rows = B * (K + 1);
+  const int nch = plan_argmax_chunks(rows, vocab);
+  const size_t part = align256((size_t)rows * nch * sizeof(float));
+  const size_t need = 2 * part + (size_t)rows * sizeof(int);
+  if (need > (size_t)PE_VERIFY_STATIC_SCRATCH_BYTES)
+    return fail(nullptr, PE_ERR_INVALID, "B and K need more than the static scratch holds");
+  char* base = nullptr;
+  PE_TRY(static_scratch(&base));
+  float* pv = (float*)base;
+  int* pi = (int*)(base + part);
+  int* t_ws = (int*)(base + 2 * part);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_argmax_rows(dtype == PE_BF16 ? 1 : 0, target_logits, rows, vocab, nch, pv, pi, st);
+  if (e == hipSuccess)
+    e = launch_accept_compact(pv, pi, nch, B, K, draft_tokens, finished, req_slot, seq_len, t_ws, accept_len,
+                              cu_accept, out_tokens, keep_index, n_keep, req_slot_next, seq_len_next, last_token_next,
+                              st);
+  if (e != hipSuccess) return fail(nullptr, PE_ERR_HIP, std::string("pe_verify_static: ") + hipGetErrorString(e));
   return PE_OK;
 }

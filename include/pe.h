@@ -219,6 +219,25 @@ pe_status pe_verify_sampled(pe_ctx* ctx, int32_t B, int32_t K, const void* targe
                             int32_t* n_keep, int32_t* req_slot_next, int32_t* seq_len_next,
                             int32_t* last_token_next);
 
+/* Greedy verification exactly as pe_verify (same inputs, outputs, contract and results), without a ctx and
+ * without allocating anything. For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Its scratch memory (the vocabulary
+ * argmax partials and the per-position target tokens) is a static array inside the library, one per GPU,
+ * PE_VERIFY_STATIC_SCRATCH_BYTES (256 KiB) in size; the first call on a device looks up that device's copy
+ * (the device current at the call, which must be gfx950), later calls reuse it. Every call on one GPU
+ * shares that array, so calls that overlap on one GPU (two streams, or two host threads) race and must be
+ * serialised by the caller; consecutive calls in one stream are safe (nothing in the array needs to start
+ * at zero). vocab: V, a positive multiple of 8; dtype: element type of target_logits (PE_F32 or PE_BF16);
+ * 1 <= B <= 1024, 1 <= K <= 16 (every such size fits the array; a size that would not is rejected with
+ * PE_ERR_INVALID). stream: a hipStream_t (NULL = default stream). Errors before anything is enqueued
+ * (PE_ERR_INVALID / PE_ERR_UNSUPPORTED / PE_ERR_HIP); pe_last_error(NULL) gives the message. */
+#define PE_VERIFY_STATIC_SCRATCH_BYTES (256 * 1024)
+pe_status pe_verify_static(int32_t B, int32_t K, int32_t vocab, pe_dtype dtype, const void* target_logits,
+                           const int32_t* draft_tokens, const uint8_t* finished, const int32_t* req_slot,
+                           const int32_t* seq_len, int32_t* accept_len, int32_t* cu_accept, int32_t* out_tokens,
+                           int32_t* keep_index, int32_t* n_keep, int32_t* req_slot_next, int32_t* seq_len_next,
+                           int32_t* last_token_next, void* stream);
+
 /* Waits for the ctx's stream, then frees everything pe_init allocated. NULL is allowed. */
 pe_status pe_destroy(pe_ctx* ctx);
 

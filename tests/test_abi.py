@@ -97,3 +97,36 @@ def test_python_binding_fails_loudly_without_library(tmp_path):
             b.load_library(str(tmp_path / "missing.so"))
     finally:
         b._lib = saved
+
+
+def test_static_verify_rejects_bad_arguments_on_the_host(lib):
+    from eagle_drafting_amd import binding as b
+    good = dict(B=4, K=3, vocab=4096, dtype=b.PE_BF16)
+    ptrs = [16] * 13  # non-null, 16-byte aligned stand-ins: never dereferenced, the checks fail first
+    for kw in ({"B": 0}, {"B": 1025}, {"K": 0}, {"K": 17}, {"vocab": 4100}, {"vocab": 0}, {"dtype": 7}):
+        a = {**good, **kw}
+        assert lib.pe_verify_static(a["B"], a["K"], a["vocab"], a["dtype"], *ptrs, None) == b.PE_ERR_INVALID, kw
+        assert b.pe_last_error(None)
+    assert lib.pe_verify_static(4, 3, 4096, b.PE_BF16, None, *ptrs[1:], None) == b.PE_ERR_INVALID
+    assert lib.pe_verify_static(4, 3, 4096, b.PE_BF16, 8, *ptrs[1:], None) == b.PE_ERR_INVALID  # misaligned
+
+
+def test_gpu_calls_without_a_device_return_hip_errors(lib):
+    # on a host without a usable GPU the first HIP call fails; the library reports PE_ERR_HIP instead of
+    # aborting (valid arguments, so the host checks pass)
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    from eagle_drafting_amd import binding as b
+    assert lib.pe_verify_static(4, 3, 4096, b.PE_BF16, *([16] * 13), None) == b.PE_ERR_HIP
+    assert "hip" in b.pe_last_error(None).lower()
+    w = b.pe_weights()
+    for f in ("fc", "embed", "emb_mask", "h_shared", "final_norm", "lm_head"):
+        setattr(w, f, 16)
+    kv = b.pe_kv()
+    for l in range(4):
+        for arr in (w.attn_norm, w.wqkv, w.wo, w.mlp_norm, w.wgate, w.wup, w.wdown, kv.k, kv.v):
+            arr[l] = 16
+    with pytest.raises(b.PeError) as e:
+        b.pe_init(_good(), w, kv, 0)
+    assert e.value.status == b.PE_ERR_HIP
