@@ -22,7 +22,8 @@ PE_PROF_LM_HEAD, PE_PROF_ATTENTION, PE_PROF_GATE_UP, PE_PROF_VERIFY_SCAN = 0, 1,
 PE_PROF_QKV, PE_PROF_O_PROJ, PE_PROF_DOWN, PE_PROF_ROWS = 4, 5, 6, 7
 PE_PROF_COUNT = 8
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpe.so")
+# the in-tree build; PE_LIBRARY names another build of the same library (e.g. one with host sanitizers)
+LIB_PATH = os.environ.get("PE_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpe.so")
 
 EXPORTED = ["pe_config_validate", "pe_init", "pe_draft_step", "pe_draft_rows", "pe_draft_ar", "pe_draft_catchup",
             "pe_verify", "pe_verify_sampled", "pe_verify_static",

@@ -870,7 +870,7 @@ static pe_status static_scratch(char** out) {
   return PE_OK;
 }
 
-extern "C" pe_status pe_verify_static(int32_t B, int32_t K, int32_t vocab, pe_dtype dtype, const void* target_logits,
+extern "C" pe_status pe_verify_static(int32_t B, int32_t K, int32_t vocab, int32_t dtype, const void* target_logits,
                                       const int32_t* draft_tokens, const uint8_t* finished, const int32_t* req_slot,
                                       const int32_t* seq_len, int32_t* accept_len, int32_t* cu_accept,
                                       int32_t* out_tokens, int32_t* keep_index, int32_t* n_keep,

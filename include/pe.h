@@ -227,12 +227,13 @@ pe_status pe_verify_sampled(pe_ctx* ctx, int32_t B, int32_t K, const void* targe
  * (the device current at the call, which must be gfx950), later calls reuse it. Every call on one GPU
  * shares that array, so calls that overlap on one GPU (two streams, or two host threads) race and must be
  * serialised by the caller; consecutive calls in one stream are safe (nothing in the array needs to start
- * at zero). vocab: V, a positive multiple of 8; dtype: element type of target_logits (PE_F32 or PE_BF16);
+ * at zero). vocab: V, a positive multiple of 8; dtype: element type of target_logits (a pe_dtype value:
+ * PE_F32 or PE_BF16, passed as int32_t so that any other value is rejected rather than read as an enum);
  * 1 <= B <= 1024, 1 <= K <= 16 (every such size fits the array; a size that would not is rejected with
  * PE_ERR_INVALID). stream: a hipStream_t (NULL = default stream). Errors before anything is enqueued
  * (PE_ERR_INVALID / PE_ERR_UNSUPPORTED / PE_ERR_HIP); pe_last_error(NULL) gives the message. */
 #define PE_VERIFY_STATIC_SCRATCH_BYTES (256 * 1024)
-pe_status pe_verify_static(int32_t B, int32_t K, int32_t vocab, pe_dtype dtype, const void* target_logits,
+pe_status pe_verify_static(int32_t B, int32_t K, int32_t vocab, int32_t dtype, const void* target_logits,
                            const int32_t* draft_tokens, const uint8_t* finished, const int32_t* req_slot,
                            const int32_t* seq_len, int32_t* accept_len, int32_t* cu_accept, int32_t* out_tokens,
                            int32_t* keep_index, int32_t* n_keep, int32_t* req_slot_next, int32_t* seq_len_next,

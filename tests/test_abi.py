@@ -26,10 +26,10 @@ def lib():
 def test_library_exports_every_declared_function(lib):
     names = _declared_functions()
     assert "pe_init" in names and "pe_draft_step" in names and "pe_verify" in names
-    raw = ctypes.CDLL(os.path.join(ROOT, "eagle_drafting_amd", "libpe.so"))
+    from eagle_drafting_amd import binding
+    raw = ctypes.CDLL(binding.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
-    from eagle_drafting_amd import binding
     assert sorted(binding.EXPORTED) == names
 
 
