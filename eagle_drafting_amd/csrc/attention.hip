@@ -113,8 +113,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) vo
   // staging: this thread moves keys PK kq .. PK kq + PK - 1, dimensions 8 c8 .. 8 c8 + 7 of each round.
   // Keys past k_end are clamped to the last valid key (finite values; their scores are masked out).
   const int kq = tid / C8, c8 = tid % C8;
-  bf16x8_t rk[PK], rv[PK];
-  auto gload = [&](int base) {
+  typedef bf16x8_t RoundRegs[PK];
+  RoundRegs rkA, rvA;
+  auto gload = [&](int base, RoundRegs& rk, RoundRegs& rv) {
     if (base + KEYS <= k_end) {  // the whole round is inside the split: one address, immediate offsets
       const size_t o = (size_t)(base + PK * kq) * HD + 8 * c8;
 #pragma unroll
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) vo
       }
     }
   };
-  auto sstore = [&]() {
+  auto sstore = [&](const RoundRegs& rk, const RoundRegs& rv) {
 #pragma unroll
     for (int q = 0; q < PK; ++q) {
       const int k = PK * kq + q;  // k = 32 a' + 8 a + 4 h + r  ->  row 32 a' + 16 h + 4 a + r
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) vo
     }
   };
 
-  gload(k_begin);
+  gload(k_begin, rkA, rvA);
 
   const bf16x8_t zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
   bf16x8_t qf[NR][HS];
@@ -178,105 +179,172 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) vo
     }
   }
 
+  // (measured: a second register set two rounds ahead made the 8-wave kernels slower, 222 -> 262 us per
+  // GPT-OSS layer: its registers cost the second workgroup per compute unit)
   for (int base = k_begin; base < k_end; base += KEYS) {
     if (base != k_begin) __syncthreads();  // every wave is done with the previous round's tiles
-    sstore();
+    sstore(rkA, rvA);
     __syncthreads();
-    if (base + KEYS < k_end) gload(base + KEYS);
-    if (nrt > 0) {
+    if (base + KEYS < k_end) gload(base + KEYS, rkA, rvA);
+    // a round every query row fully sees (all its keys are context keys, inside the split) on a straight
+    // path: all score products, one running-max update for the round's keys, all value products (head
+    // dimension 64 only: with 128 the path's registers cost the 8-wave kernel its second workgroup per
+    // compute unit. Measured: GPT-OSS B 64 K 10 224 -> 210 us per layer; with 128 included, Qwen B 8 K 11 went 28 -> 31 us)
+    if (HD == 64 && nrt > 0 && sub == 1 && base + KEYS <= k_end && base + KEYS <= L + 1) {
+      f32x4_t sc[NKT][2];
+#pragma unroll
       for (int kt = 0; kt < NKT; ++kt) {
-        const int tb = base + kt * KT;
-        if (tb >= k_end) break;
-        if (sub > 1 && (((tb - k_begin) / KT) % sub) != ks_id) continue;
-        bf16x8_t pf[NR];
-        float alpha[NR];
+        bf16x8_t ka[HS][2];
 #pragma unroll
-        for (int t = 0; t < NR; ++t) {
-          pf[t] = zero8;
-          alpha[t] = 1.f;
-          if (t >= nrt) continue;
-          f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-          // every key fragment of the tile is read before the first product, so the LDS reads overlap
-          // instead of each product waiting for its own
-          bf16x8_t ka[HS][2];
-#pragma unroll
-          for (int hs = 0; hs < HS; ++hs) {
-            ka[hs][0] = *(const bf16x8_t*)(sK + (kt * KT + lr) * STR + 32 * hs + 8 * lq);
-            ka[hs][1] = *(const bf16x8_t*)(sK + (kt * KT + 16 + lr) * STR + 32 * hs + 8 * lq);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int hs = 0; hs < HS; ++hs) {
-            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[hs][0], qf[t][hs], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[hs][1], qf[t][hs], s1, 0, 0, 0);
-          }
-          const int row = (rt0 + 4 * t) * 16 + lr;
-          float psum = 0.f, pe[8], mnew;
-          if (tb + KT <= L + 1 && tb + KT <= k_end) {
-            // every query row sees every key of the tile (row j sees keys < L + j + 1): no mask; the
-            // scale (which includes log2 e, so scores are in log2 units) is applied inside the exponent
-            const float sr[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-            float rmax = fmaxf(fmaxf(fmaxf(sr[0], sr[4]), fmaxf(sr[1], sr[5])),
-                               fmaxf(fmaxf(sr[2], sr[6]), fmaxf(sr[3], sr[7])));
-            rmax = rows_max(rmax);  // over the 4 lanes (l, l ^ 16, l ^ 32, l ^ 48) of query row lr
-            mnew = fmaxf(m_run[t], rmax * scale);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {  // pf element e: key tb + 8 lq + e
-              const int r = e & 3, hi = e >> 2;
-              pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[4 * hi + r], scale, -mnew));
-              psum += pe[e];
-            }
-          } else {
-            const int lim = row < R ? min(k_end, L + (row % K) + 1) : 0;  // visible keys: < lim
-            float sv[8];
-            float tmax = -INFINITY;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int k0 = tb + 8 * lq + r, k1 = k0 + 4;  // keys of score rows 4 lq + r of tiles 0 and 1
-              sv[r] = k0 < lim ? s0[r] * scale : -INFINITY;
-              sv[4 + r] = k1 < lim ? s1[r] * scale : -INFINITY;
-              tmax = fmaxf(tmax, fmaxf(sv[r], sv[4 + r]));
-            }
-            tmax = rows_max(tmax);
-            mnew = fmaxf(m_run[t], tmax);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              pe[e] = __builtin_amdgcn_exp2f(sv[e] - mnew);
-              psum += pe[e];
-            }
-          }
-          alpha[t] = __builtin_amdgcn_exp2f(m_run[t] - mnew);
-          typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-          const u32x4_t pk = {f32x2_to_bf16x2(pe[0], pe[1]), f32x2_to_bf16x2(pe[2], pe[3]),
-                              f32x2_to_bf16x2(pe[4], pe[5]), f32x2_to_bf16x2(pe[6], pe[7])};
-          pf[t] = __builtin_bit_cast(bf16x8_t, pk);
-          psum = rows_sum(psum);
-          l_run[t] = l_run[t] * alpha[t] + psum;
-          m_run[t] = mnew;
+        for (int hs = 0; hs < HS; ++hs) {
+          ka[hs][0] = *(const bf16x8_t*)(sK + (kt * KT + lr) * STR + 32 * hs + 8 * lq);
+          ka[hs][1] = *(const bf16x8_t*)(sK + (kt * KT + 16 + lr) * STR + 32 * hs + 8 * lq);
         }
-        // the running max rarely moves after the first tiles: rescale only when some lane's did (a
-        // wave-uniform branch of its own, so the common case costs no multiplies or selects)
+        sc[kt][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        sc[kt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < NR; ++t) {
-          if (t < nrt && __any(alpha[t] != 1.f)) {
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) o[t][ct][r] *= alpha[t];
-          }
+        for (int hs = 0; hs < HS; ++hs) {
+          sc[kt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[hs][0], qf[0][hs], sc[kt][0], 0, 0, 0);
+          sc[kt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[hs][1], qf[0][hs], sc[kt][1], 0, 0, 0);
         }
-        // value fragments likewise: all reads first, then the products
+      }
+      float rmax = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rmax = fmaxf(rmax, fmaxf(sc[kt][0][r], sc[kt][1][r]));
+      rmax = rows_max(rmax);
+      const float mnew = fmaxf(m_run[0], rmax * scale);
+      float psum = 0.f;
+      bf16x8_t pf[NKT];
+      typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
+        float pe[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {  // element e: key base + kt KT + 8 lq + e
+          pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(e < 4 ? sc[kt][0][e] : sc[kt][1][e - 4], scale, -mnew));
+          psum += pe[e];
+        }
+        const u32x4_t pk = {f32x2_to_bf16x2(pe[0], pe[1]), f32x2_to_bf16x2(pe[2], pe[3]),
+                            f32x2_to_bf16x2(pe[4], pe[5]), f32x2_to_bf16x2(pe[6], pe[7])};
+        pf[kt] = __builtin_bit_cast(bf16x8_t, pk);
+      }
+      const float alpha = __builtin_amdgcn_exp2f(m_run[0] - mnew);
+      psum = rows_sum(psum);
+      l_run[0] = l_run[0] * alpha + psum;
+      m_run[0] = mnew;
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[0][ct][r] *= alpha;
+      }
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
         bf16x8_t va[CT];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
           va[ct] = *(const bf16x8_t*)(sVt + (ct * 16 + lr) * VSTR + ((kt * KT + 8 * lq) ^ (8 * vsw(ct * 16 + lr))));
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
+        for (int ct = 0; ct < CT; ++ct) o[0][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[ct], pf[kt], o[0][ct], 0, 0, 0);
+      }
+    } else {
+      if (nrt > 0) {
+        for (int kt = 0; kt < NKT; ++kt) {
+          const int tb = base + kt * KT;
+          if (tb >= k_end) break;
+          if (sub > 1 && (((tb - k_begin) / KT) % sub) != ks_id) continue;
+          bf16x8_t pf[NR];
+          float alpha[NR];
 #pragma unroll
           for (int t = 0; t < NR; ++t) {
+            pf[t] = zero8;
+            alpha[t] = 1.f;
             if (t >= nrt) continue;
-            o[t][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[ct], pf[t], o[t][ct], 0, 0, 0);
+            f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+            // every key fragment of the tile is read before the first product, so the LDS reads overlap
+            // instead of each product waiting for its own
+            bf16x8_t ka[HS][2];
+#pragma unroll
+            for (int hs = 0; hs < HS; ++hs) {
+              ka[hs][0] = *(const bf16x8_t*)(sK + (kt * KT + lr) * STR + 32 * hs + 8 * lq);
+              ka[hs][1] = *(const bf16x8_t*)(sK + (kt * KT + 16 + lr) * STR + 32 * hs + 8 * lq);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int hs = 0; hs < HS; ++hs) {
+              s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[hs][0], qf[t][hs], s0, 0, 0, 0);
+              s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[hs][1], qf[t][hs], s1, 0, 0, 0);
+            }
+            const int row = (rt0 + 4 * t) * 16 + lr;
+            float psum = 0.f, pe[8], mnew;
+            if (tb + KT <= L + 1 && tb + KT <= k_end) {
+              // every query row sees every key of the tile (row j sees keys < L + j + 1): no mask; the
+              // scale (which includes log2 e, so scores are in log2 units) is applied inside the exponent
+              const float sr[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+              float rmax = fmaxf(fmaxf(fmaxf(sr[0], sr[4]), fmaxf(sr[1], sr[5])),
+                                 fmaxf(fmaxf(sr[2], sr[6]), fmaxf(sr[3], sr[7])));
+              rmax = rows_max(rmax);  // over the 4 lanes (l, l ^ 16, l ^ 32, l ^ 48) of query row lr
+              mnew = fmaxf(m_run[t], rmax * scale);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {  // pf element e: key tb + 8 lq + e
+                const int r = e & 3, hi = e >> 2;
+                pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[4 * hi + r], scale, -mnew));
+                psum += pe[e];
+              }
+            } else {
+              const int lim = row < R ? min(k_end, L + (row % K) + 1) : 0;  // visible keys: < lim
+              float sv[8];
+              float tmax = -INFINITY;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int k0 = tb + 8 * lq + r, k1 = k0 + 4;  // keys of score rows 4 lq + r of tiles 0 and 1
+                sv[r] = k0 < lim ? s0[r] * scale : -INFINITY;
+                sv[4 + r] = k1 < lim ? s1[r] * scale : -INFINITY;
+                tmax = fmaxf(tmax, fmaxf(sv[r], sv[4 + r]));
+              }
+              tmax = rows_max(tmax);
+              mnew = fmaxf(m_run[t], tmax);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                pe[e] = __builtin_amdgcn_exp2f(sv[e] - mnew);
+                psum += pe[e];
+              }
+            }
+            alpha[t] = __builtin_amdgcn_exp2f(m_run[t] - mnew);
+            typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+            const u32x4_t pk = {f32x2_to_bf16x2(pe[0], pe[1]), f32x2_to_bf16x2(pe[2], pe[3]),
+                                f32x2_to_bf16x2(pe[4], pe[5]), f32x2_to_bf16x2(pe[6], pe[7])};
+            pf[t] = __builtin_bit_cast(bf16x8_t, pk);
+            psum = rows_sum(psum);
+            l_run[t] = l_run[t] * alpha[t] + psum;
+            m_run[t] = mnew;
+          }
+          // the running max rarely moves after the first tiles: rescale only when some lane's did (a
+          // wave-uniform branch of its own, so the common case costs no multiplies or selects)
+#pragma unroll
+          for (int t = 0; t < NR; ++t) {
+            if (t < nrt && __any(alpha[t] != 1.f)) {
+#pragma unroll
+              for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[t][ct][r] *= alpha[t];
+            }
+          }
+          // value fragments likewise: all reads first, then the products
+          bf16x8_t va[CT];
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+            va[ct] = *(const bf16x8_t*)(sVt + (ct * 16 + lr) * VSTR + ((kt * KT + 8 * lq) ^ (8 * vsw(ct * 16 + lr))));
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+            for (int t = 0; t < NR; ++t) {
+              if (t >= nrt) continue;
+              o[t][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[ct], pf[t], o[t][ct], 0, 0, 0);
+            }
           }
         }
       }
