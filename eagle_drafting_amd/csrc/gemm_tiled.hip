@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
   bf16x8_t(*As)[2][8][64] = (bf16x8_t(*)[2][8][64])smem;                      // [buffer][k-step][m-tile][lane]
   float* Cs = (float*)smem;                                                  // [BM][BN], after the main loop
 
-  const int M = g.M, N = g.N, Ks = g.Ks, Nt = g.Nt;
+  const int M = g.M, Ks = g.Ks, Nt = g.Nt;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   // Workgroup w runs on XCD w % 8 (round-robin dispatch). Each XCD takes every 8th column group and runs
@@ -61,7 +61,6 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
 
   const __amdgpu_buffer_rsrc_t a_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, gemm_a_rows(g) * g.lda * 2, 0x00020000);
-  const bf16x8_t* W = (const bf16x8_t*)g.Wp_raw;
   const uint4* W8 = (const uint4*)g.Wp_raw;  // F8: fragment pairs, (Ks + 1) / 2 per tile
   const int Ks2 = (Ks + 1) / 2;
 
@@ -88,15 +87,31 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
     const int row = m0 + ((tid + 256 * q) >> 3);
     a_row0[q] = row < M ? gemm_a_row(g, row) * g.lda : -1;
   }
+  // Load offsets are fixed per lane for the whole loop and a stage adds a wave-uniform amount (fewer
+  // address instructions per load). Activations: the byte offset of the piece at the first stage, and the
+  // number of k-steps its row still has from there (beyond them, and for rows past M, the load takes an
+  // out-of-range offset and returns zeros). Weights (bf16): the fragment's offset inside the column
+  // group's eight tiles, from a descriptor based at the group's first tile (so 32-bit offsets suffice for
+  // any weight size), plus the k-step (1 KiB) as the scalar offset.
+  uint32_t a_off[4];
+  int a_lim[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int seg = (tid + 256 * q) & 7;
+    a_off[q] = a_row0[q] >= 0 ? (uint32_t)((a_row0[q] + (kb + (seg >> 2)) * 32 + 8 * (seg & 3)) * 2) : 0u;
+    a_lim[q] = a_row0[q] >= 0 ? ke - kb - (seg >> 2) : -1;
+  }
+  uint32_t b_off[4];  // [u * 2 + j]
+#pragma unroll
+  for (int uj = 0; uj < 4; ++uj) {
+    const int ntile = min(nt0 + wn * 4 + 2 * (uj & 1) + fr_t, Nt - 1);
+    b_off[uj] = (uint32_t)(((ntile - nt0) * Ks * 64 + fr_l + 32 * (uj >> 1)) * 16);
+  }
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)g.Wp_raw + (size_t)nt0 * Ks * 1024), (short)0, 0x7ffffff0, 0x00020000);
   auto gload_a1 = [&](RegA& r, int st, int q) {
-    {
-      const int p = tid + 256 * q;
-      const int seg = p & 7;
-      const int akstep = kb + 2 * st + (seg >> 2);
-      const int off =
-          a_row0[q] >= 0 && akstep < ke ? (a_row0[q] + akstep * 32 + 8 * (seg & 3)) * 2 : 0x7ffffff0;
-      r[q] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0));
-    }
+    const uint32_t off = 2 * st < a_lim[q] ? a_off[q] + 128u * st : 0x7ffffff0u;
+    r[q] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0));
   };
   auto gload_b1 = [&](RegB& r, int st, int idx) {  // idx = (ks * 2 + u) * 2 + j
     const int ks = idx >> 2, u = (idx >> 1) & 1, j = idx & 1;
@@ -108,7 +123,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
       }
     } else {
       const int kstep = min(kb + 2 * st + ks, Ks - 1);
-      r[idx] = W[((size_t)ntile * Ks + kstep) * 64 + fr_l + 32 * u];
+      r[idx] = __builtin_bit_cast(bf16x8_t,
+                                  __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, b_off[u * 2 + j], kstep * 1024, 0));
     }
   };
   auto gload_a = [&](RegA& r, int st) {
@@ -283,7 +299,7 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs g) {
 template <int EP, bool SCALE>
 __device__ void tile_epilogue(const GemmArgs& g, const float* Cs, const float* s_inv, int m0, int nt0, int ng,
                               int rbeg, int rend) {
-  constexpr int BM = 128, BN = 128;
+  constexpr int BN = 128;
   const int M = g.M, N = g.N, Nt = g.Nt;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 

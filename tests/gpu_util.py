@@ -99,7 +99,9 @@ class GpuDrafter:
         return k.astype(np.float64), v.astype(np.float64)
 
     def close(self):
-        self.pe.pe_destroy(self.ctx)
+        if self.ctx is not None:
+            ctx, self.ctx = self.ctx, None
+            self.pe.pe_destroy(ctx)
 
 
 def oracle_draft(w, W64, state, K, requests, rows=None):

@@ -10,7 +10,7 @@ independent, so a sampled request's oracle result is exact for it).
 import numpy as np
 import pytest
 
-from synth import WORKLOADS, Workload, TINY_FP32, QWEN3_CODER, make_state
+from synth import WORKLOADS, Workload, TINY_FP32, QWEN3_CODER, GPT_OSS_20B, make_state
 from tests.gpu_util import (KV_TOL, TOL, GpuDrafter, check_logits, check_rows, check_tokens, log, oracle_draft,
                             shape_weights64)
 
@@ -175,5 +175,24 @@ def test_stream_kernel_row_counts_parity(B, K):
     g = GpuDrafter(w)
     try:
         _parity(g, _sample(w, g.state))
+    finally:
+        g.close()
+
+
+@pytest.mark.parametrize("K", [3, 4, 10, 15], ids=lambda v: f"K{v}")
+def test_gptoss_attention_row_tiles(K):
+    """GPT-OSS-shaped drafter (head dimension 64, 8 query heads per kv head). Attention runs the K draft rows
+    plus the trailing placeholder row, so a kv head has 8 (K + 1) query rows: K 3 gives 32 (16-row tiles),
+    K 4 / 10 / 15 give 40 / 88 / 128 (two, three and four 32-row tiles, keys and values copied straight
+    into LDS; 128 is the most the configuration allows). Contexts 0, 37 and 700: a request with only its
+    own rows, one whose keys end inside the first 64-key round, and one spread over several key splits
+    with a ragged last round. Every request against the oracle, K/V rows included."""
+    w = Workload(f"gptoss20b-bf16-B3-K{K}-rowtiles", GPT_OSS_20B, 3, K, (0, 700), 0.7, 7800 + K)
+    state = make_state(w)
+    state["seq_len"][:] = [0, 37, 700]
+    log(f"GPT-OSS attention row tiles: K {K} ({8 * (K + 1)} query rows per kv head)")
+    g = GpuDrafter(w, state=state)
+    try:
+        _parity(g, range(w.B))
     finally:
         g.close()
