@@ -149,6 +149,7 @@ struct AttnPlan {
   int chunk;   // keys per split
   int nsplit;  // splits (grid y)
   int sub;     // key sub-streams per split inside a workgroup
+  int split_major;  // 1: consecutive workgroups take consecutive splits of one (request, kv head)
 };
 AttnPlan plan_attention(int B, int K, int Hq, int Hkv, int hd, int max_ctx);
 size_t attn_partial_floats(int M, int Hq, int hd, const AttnPlan& p);
