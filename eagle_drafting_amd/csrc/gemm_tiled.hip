@@ -27,7 +27,7 @@ namespace pe {
 // s_inv[r] is row r's 1/RMS.
 template <int EP, bool SCALE>
 __device__ void tile_epilogue(const GemmArgs& g, const float* Cs, const float* s_inv, int m0, int nt0, int ng,
-                              int rbeg = 0, int rend = 128);
+                              int rbeg = 0, int rend = 128, int etid = -1);
 
 // SPLIT: the workgroup covers k-steps [blockIdx.y * g.kper, + g.kper) and writes its fp32 partial tile
 // (row-scaled for a normalised operand) to g.part[blockIdx.y]; gemm_split_reduce_kernel adds the partials
@@ -240,6 +240,162 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
   else tile_epilogue<EP, AM == A_NORM>(g, Cs, s_inv, m0, nt0, ng);
 }
 
+// Vocabulary projection above 128 rows (bound by the bf16 MFMA rate): 128 x 512 workgroup tiles, 8 waves
+// of 64 x 128 (2 x 4 blocks of v_mfma_f32_32x32x16_bf16). Both operands go from memory straight into LDS
+// with buffer loads that write LDS (one 1 KiB wave load per 16 x 32 fragment, in the fragment order the
+// operand reads use, so the reads are lane-linear 16-byte chunks): per 32-deep k-step 8 activation
+// fragments (per-lane row addresses, zeros past the last row) and 32 weight fragments (packed contiguous;
+// zeros past the last tile). Three k-step buffers (40 KiB each) keep two k-steps in flight behind the one
+// being multiplied, without registers; every operand is read from memory once per workgroup (the 128 x
+// 128 kernel loads each weight fragment into the registers of two waves). Workgroups are ordered
+// XCD-aware as in the 128 x 128 kernel (a 512-column weight group leaves HBM once; its other row blocks
+// hit the XCD's L2). The 128 x 512 product goes through LDS as four 128 x 128 quarters, two at a time,
+// into the shared epilogue (waves 0-3 and 4-7 each run one quarter's).
+template <int AM, int EP>
+__global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g) {
+  constexpr int BM = 128;
+  constexpr int FA = 8, FB = 32;            // fragments per k-step: 16-row activation tiles, 16-column weight tiles
+  constexpr int SB = (FA + FB) * 1024;      // bytes per k-step buffer
+  constexpr int NBUF = 3;
+  constexpr int SMEM = 2 * 128 * 128 * 4;   // two 128 x 128 fp32 quarters for the epilogue (>= NBUF * SB)
+  static_assert(NBUF * SB <= SMEM, "k-step buffers exceed the epilogue area");
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+  __shared__ float s_inv[BM];
+
+  const int M = g.M, Ks = g.Ks, Nt = g.Nt;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave >> 2, wc = wave & 3;  // 64-row half, 128-column quarter of the tile
+  const int nwide = (g.ngroups + 3) / 4;    // 512-column groups
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int gw = (slot / g.mblocks) * 8 + xcd;
+  if (gw >= nwide) return;
+  const int m0 = (slot % g.mblocks) * BM;
+  const int nt0 = gw * 32;                  // first 16-column tile
+
+  // wave w moves activation fragment w (rows m0 + 16 w .. + 15) and weight fragments w, w + 8, w + 16,
+  // w + 24 of every k-step; fragment lane l holds row (or column) l % 16, k elements 8 (l / 16) .. + 7
+  const __amdgpu_buffer_rsrc_t a_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, gemm_a_rows(g) * g.lda * 2, 0x00020000);
+  const int ntw = min(32, Nt - nt0);        // weight tiles of this group that exist
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)g.Wp_raw + (size_t)nt0 * Ks * 1024), (short)0, ntw * Ks * 1024, 0x00020000);
+  const int arow = m0 + 16 * wave + (lane & 15);
+  const uint32_t a_off = arow < M ? (uint32_t)((gemm_a_row(g, arow) * g.lda + 8 * (lane >> 4)) * 2) : 0x7ffffff0u;
+  const uint32_t w_off = (uint32_t)(wave * Ks * 1024 + 16 * lane);
+  auto dma_kstep = [&](int ks) {
+    char* buf = smem + (ks % NBUF) * SB;
+    {
+      __attribute__((address_space(3))) void* dst = (__attribute__((address_space(3))) void*)(buf + wave * 1024);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dst, 16, a_off == 0x7ffffff0u ? a_off : a_off + 64 * ks, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      __attribute__((address_space(3))) void* dst =
+          (__attribute__((address_space(3))) void*)(buf + FA * 1024 + (wave + 8 * q) * 1024);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, dst, 16, w_off + 8 * q * Ks * 1024, ks * 1024, 0, 0);
+    }
+  };
+
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  // operand lane l of 32 rows (or columns) 32 b .. + 31, k-half u: fragment 2 b + (l % 32) / 16, fragment
+  // lane l % 16 + 16 (2 u + l / 32)
+  const int fr_t = (lane & 31) >> 4, fr_l = (lane & 15) + 16 * (lane >> 5);
+  // LDS byte addresses of this lane's first activation (block i = 0, k-half 0) and weight (block j = 0)
+  // fragment reads within a k-step buffer; block i + 1 / j + 1 is 2 KiB further, k-half 1 512 bytes
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  const uint32_t a_lane = (uint32_t)(((4 * wr + fr_t) * 64 + fr_l) * 16);
+  const uint32_t b_lane = (uint32_t)(FA * 1024 + ((8 * wc + fr_t) * 64 + fr_l) * 16);
+
+  dma_kstep(0);
+  if (Ks > 1) dma_kstep(1);
+  for (int ks = 0; ks < Ks; ++ks) {
+    // this wave's loads of k-step ks are done once only those of k-step ks + 1 (five) may remain; the barrier
+    // then covers every wave's loads of ks and every wave's reads of ks - 1
+    if (ks + 1 < Ks) __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (ks + 2 < Ks) dma_kstep(ks + 2);  // into the buffer of k-step ks - 1
+    // the k-step's 12 fragment reads in one block that also waits for them (the compiler's own wait
+    // insertion would otherwise wait for every outstanding k-step load before them)
+    const uint32_t ab = lds_base + (uint32_t)((ks % NBUF) * SB) + a_lane;
+    const uint32_t bb = lds_base + (uint32_t)((ks % NBUF) * SB) + b_lane;
+    bf16x8_t a00, a10, a01, a11, b00, b10, b20, b30, b01, b11, b21, b31;
+    asm volatile(
+        "ds_read_b128 %0, %12\n\t"
+        "ds_read_b128 %1, %12 offset:2048\n\t"
+        "ds_read_b128 %4, %13\n\t"
+        "ds_read_b128 %5, %13 offset:2048\n\t"
+        "ds_read_b128 %6, %13 offset:4096\n\t"
+        "ds_read_b128 %7, %13 offset:6144\n\t"
+        "ds_read_b128 %2, %12 offset:512\n\t"
+        "ds_read_b128 %3, %12 offset:2560\n\t"
+        "ds_read_b128 %8, %13 offset:512\n\t"
+        "ds_read_b128 %9, %13 offset:2560\n\t"
+        "ds_read_b128 %10, %13 offset:4608\n\t"
+        "ds_read_b128 %11, %13 offset:6656\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a00), "=&v"(a10), "=&v"(a01), "=&v"(a11), "=&v"(b00), "=&v"(b10), "=&v"(b20), "=&v"(b30),
+          "=&v"(b01), "=&v"(b11), "=&v"(b21), "=&v"(b31)
+        : "v"(ab), "v"(bb)
+        : "memory");
+    const bf16x8_t af[2][2] = {{a00, a01}, {a10, a11}};           // [i][u]
+    const bf16x8_t bw[4][2] = {{b00, b01}, {b10, b11}, {b20, b21}, {b30, b31}};  // [j][u]
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][u], bw[j][u], acc[i][j], 0, 0, 0);
+  }
+
+  if (AM == A_NORM && tid < 256) {
+    // 1 / RMS per row from the producer's partial sums of squares (two threads per row)
+    const int r = tid >> 1, h = tid & 1;
+    float t = 0.f;
+    if (m0 + r < M) {
+      const float* src = g.ssq_in + (size_t)gemm_a_row(g, m0 + r) * g.nssq;
+      for (int i = h; i < g.nssq; i += 2) t += src[i];
+    }
+    t += __shfl_xor(t, 1, PE_WAVE);
+    if (h == 0) s_inv[r] = rsqrtf(t / (float)g.Kd + g.eps);
+  }
+  // two passes of two 128 x 128 quarters: quarter 2 p + s (columns 128 (2 p + s) ..) is held by the waves
+  // with wc = 2 p + s and goes to Cs[s] (column XOR-swizzle as in the 128 x 128 kernel), then waves
+  // 4 s .. 4 s + 3 run its epilogue
+  const int c = lane & 31, hq = lane >> 5;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    __syncthreads();  // the k-step buffers (or the previous pass's quarters) are no longer read
+    if ((wc >> 1) == p) {
+      float* C = (float*)smem + (wc & 1) * 128 * 128;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int row = 64 * wr + 32 * i + 8 * (e >> 2) + 4 * hq + (e & 3);
+            const int col = (32 * j + c) ^ (hq << 5);
+            C[row * 128 + col] = acc[i][j][e];
+          }
+    }
+    __syncthreads();
+    const int s = wave >> 2;
+    const int ng = 4 * gw + 2 * p + s;
+    if (ng < g.ngroups)
+      tile_epilogue<EP, AM == A_NORM>(g, (const float*)smem + s * 128 * 128, s_inv, m0, ng * 8, ng, 0, 128, tid & 255);
+  }
+}
+
 // the fixed-order sum of the K-split partials of rows [16 y, 16 y + 16) of one 128 x 128 tile
 // (y = blockIdx.y), then the epilogue of those rows
 template <int EP>
@@ -298,10 +454,11 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs g) {
 
 template <int EP, bool SCALE>
 __device__ void tile_epilogue(const GemmArgs& g, const float* Cs, const float* s_inv, int m0, int nt0, int ng,
-                              int rbeg, int rend) {
+                              int rbeg, int rend, int etid) {
   constexpr int BN = 128;
   const int M = g.M, N = g.N, Nt = g.Nt;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // 256 threads run the epilogue (etid: the caller's thread index among them; default threadIdx.x)
+  const int tid = etid >= 0 ? etid : (int)threadIdx.x, wave = tid >> 6, lane = tid & 63;
 
   // 4 consecutive columns [c0, c0 + 4) of local row rl, scaled by 1/RMS for a normalised operand
   auto cload = [&](int rl, int c0) {
@@ -821,6 +978,12 @@ static hipError_t launch_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode,
 
 hipError_t launch_gemm_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st) {
   if (p.tiled == 2) return launch_gemm_stream(p, a, a_mode, epi, st);
+  if (p.tiled == 3 && !a.wscale && p.ksplit == 1 && a_mode == A_NORM && epi == EPI_ARGMAX) {
+    const int nwide = (p.ngroups + 3) / 4;
+    const dim3 grid(8 * ((nwide + 7) / 8) * p.mblocks);
+    hipLaunchKernelGGL((gemm_wide_kernel<A_NORM, EPI_ARGMAX>), grid, dim3(512), 0, st, a);
+    return hipGetLastError();
+  }
   return a.wscale ? launch_tiled<1>(p, a, a_mode, epi, st) : launch_tiled<0>(p, a, a_mode, epi, st);
 }
 

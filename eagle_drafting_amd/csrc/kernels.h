@@ -37,7 +37,8 @@ struct GemmPlan {
   int NT;       // 16-column tiles per workgroup
   int NW;       // waves per workgroup (they split the reduction dimension NW/NT ways)
   int ngroups;  // workgroups along N
-  int tiled;    // 2: weight-stream kernel (9..128 rows); 1: LDS-tiled 128 x 128 kernel (larger M); 0: skinny split-K kernel
+  int tiled;    // 2: weight-stream kernel (9..128 rows); 1: LDS-tiled 128 x 128 kernel (larger M); 3: the vocabulary
+                // projection's 128 x 512 kernel (128 x 128 with FP8 weights); 0: skinny split-K kernel
   int ksplit;   // tiled: workgroups along the reduction dimension (1 = none); > 1 adds a reduce kernel
   int kper;     // tiled: k-steps (32 columns each) per split, a multiple of 4
   int ki4;      // skinny on PACK_KI4 weights: 4-column tiles (Nt counts them), 128-wide k-steps
