@@ -274,26 +274,39 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g) {
   const int nt0 = gw * 32;                  // first 16-column tile
 
   // wave w moves activation fragment w (rows m0 + 16 w .. + 15) and weight fragments w, w + 8, w + 16,
-  // w + 24 of every k-step; fragment lane l holds row (or column) l % 16, k elements 8 (l / 16) .. + 7
-  const __amdgpu_buffer_rsrc_t a_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, gemm_a_rows(g) * g.lda * 2, 0x00020000);
-  const int ntw = min(32, Nt - nt0);        // weight tiles of this group that exist
-  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const char*)g.Wp_raw + (size_t)nt0 * Ks * 1024), (short)0, ntw * Ks * 1024, 0x00020000);
+  // w + 24 of every k-step; fragment lane l holds row (or column) l % 16, k elements 8 (l / 16) .. + 7.
+  // The loads are written as inline assembly: the compiler then does not know they write LDS, and does
+  // not wait for every outstanding k-step before each fragment read; the explicit waits below order them.
+  typedef int i32x4_t __attribute__((ext_vector_type(4)));
+  auto rsrc4 = [](const void* base, int num) {  // raw buffer descriptor: base, stride 0, num_records
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    i32x4_t r;
+    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+    r.z = __builtin_amdgcn_readfirstlane(num);
+    r.w = __builtin_amdgcn_readfirstlane(0x00020000);
+    return r;
+  };
+  const i32x4_t a_rsrc = rsrc4(g.A, gemm_a_rows(g) * g.lda * 2);
+  const int ntw = min(32, Nt - nt0);        // weight tiles of this group that exist (past them: zeros)
+  const i32x4_t w_rsrc = rsrc4((const char*)g.Wp_raw + (size_t)nt0 * Ks * 1024, ntw * Ks * 1024);
   const int arow = m0 + 16 * wave + (lane & 15);
-  const uint32_t a_off = arow < M ? (uint32_t)((gemm_a_row(g, arow) * g.lda + 8 * (lane >> 4)) * 2) : 0x7ffffff0u;
+  const bool a_ok = arow < M;
+  const uint32_t a_off = a_ok ? (uint32_t)((gemm_a_row(g, arow) * g.lda + 8 * (lane >> 4)) * 2) : 0x7ffffff0u;
   const uint32_t w_off = (uint32_t)(wave * Ks * 1024 + 16 * lane);
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
   auto dma_kstep = [&](int ks) {
-    char* buf = smem + (ks % NBUF) * SB;
-    {
-      __attribute__((address_space(3))) void* dst = (__attribute__((address_space(3))) void*)(buf + wave * 1024);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dst, 16, a_off == 0x7ffffff0u ? a_off : a_off + 64 * ks, 0, 0, 0);
-    }
+    const uint32_t buf = lds_base + (uint32_t)((ks % NBUF) * SB);
+    const uint32_t aoff = a_ok ? a_off + 64u * ks : a_off;
+    const uint32_t m0a = buf + wave * 1024;
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(aoff), "s"(a_rsrc), "{m0}"(m0a) : "memory");
+    const int soff = ks * 1024;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      __attribute__((address_space(3))) void* dst =
-          (__attribute__((address_space(3))) void*)(buf + FA * 1024 + (wave + 8 * q) * 1024);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, dst, 16, w_off + 8 * q * Ks * 1024, ks * 1024, 0, 0);
+      const uint32_t m0b = buf + FA * 1024 + (wave + 8 * q) * 1024;
+      asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(w_off + 8 * q * Ks * 1024), "s"(w_rsrc),
+                   "s"(soff), "{m0}"(m0b)
+                   : "memory");
     }
   };
 
@@ -305,57 +318,55 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   // operand lane l of 32 rows (or columns) 32 b .. + 31, k-half u: fragment 2 b + (l % 32) / 16, fragment
-  // lane l % 16 + 16 (2 u + l / 32)
+  // lane l % 16 + 16 (2 u + l / 32). Byte offsets of this lane's first activation (block i = 0, k-half 0)
+  // and weight (block j = 0) reads inside a k-step buffer; block + 1 is 2 KiB further, k-half 1 512 bytes.
   const int fr_t = (lane & 31) >> 4, fr_l = (lane & 15) + 16 * (lane >> 5);
-  // LDS byte addresses of this lane's first activation (block i = 0, k-half 0) and weight (block j = 0)
-  // fragment reads within a k-step buffer; block i + 1 / j + 1 is 2 KiB further, k-half 1 512 bytes
-  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
-  const uint32_t a_lane = (uint32_t)(((4 * wr + fr_t) * 64 + fr_l) * 16);
-  const uint32_t b_lane = (uint32_t)(FA * 1024 + ((8 * wc + fr_t) * 64 + fr_l) * 16);
-
-  dma_kstep(0);
-  if (Ks > 1) dma_kstep(1);
-  for (int ks = 0; ks < Ks; ++ks) {
-    // this wave's loads of k-step ks are done once only those of k-step ks + 1 (five) may remain; the barrier
-    // then covers every wave's loads of ks and every wave's reads of ks - 1
-    if (ks + 1 < Ks) __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
+  const int a_lane = ((4 * wr + fr_t) * 64 + fr_l) * 16;
+  const int b_lane = FA * 1024 + ((8 * wc + fr_t) * 64 + fr_l) * 16;
+  // the fragments of k-step ks are read while the k-half-1 products of k-step ks - 1 run (their operands
+  // are held over from the previous k-step), then the k-half-0 products of ks; the accumulation order is
+  // the plain k order
+  bf16x8_t fr0[12], fr1[12];  // [0..3]: activation (i, u) at 2 i + u; [4..11]: weight (j, u) at 4 + 2 j + u
+  auto lds_read = [&](bf16x8_t (&f)[12], int ks) {
+    const char* b = smem + (ks % NBUF) * SB;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) f[2 * i + u] = *(const bf16x8_t*)(b + a_lane + i * 2048 + u * 512);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) f[4 + 2 * j + u] = *(const bf16x8_t*)(b + b_lane + j * 2048 + u * 512);
+  };
+  auto mfma_half = [&](const bf16x8_t (&f)[12], int u) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[2 * i + u], f[4 + 2 * j + u], acc[i][j], 0, 0, 0);
+  };
+  // k-step ks: this wave's reads of ks - 1 and its loads of ks are done (only the loads of ks + 1, five,
+  // may remain); the barrier then covers every wave, so the buffer of ks - 1 takes the loads of ks + 2
+  auto step = [&](int ks, bf16x8_t (&rd)[12], const bf16x8_t (&prv)[12], bool prev) {
+    if (ks + 1 < Ks) __builtin_amdgcn_s_waitcnt(0x0075);  // vmcnt(5) lgkmcnt(0)
+    else __builtin_amdgcn_s_waitcnt(0x0070);              // vmcnt(0) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (ks + 2 < Ks) dma_kstep(ks + 2);  // into the buffer of k-step ks - 1
-    // the k-step's 12 fragment reads in one block that also waits for them (the compiler's own wait
-    // insertion would otherwise wait for every outstanding k-step load before them)
-    const uint32_t ab = lds_base + (uint32_t)((ks % NBUF) * SB) + a_lane;
-    const uint32_t bb = lds_base + (uint32_t)((ks % NBUF) * SB) + b_lane;
-    bf16x8_t a00, a10, a01, a11, b00, b10, b20, b30, b01, b11, b21, b31;
-    asm volatile(
-        "ds_read_b128 %0, %12\n\t"
-        "ds_read_b128 %1, %12 offset:2048\n\t"
-        "ds_read_b128 %4, %13\n\t"
-        "ds_read_b128 %5, %13 offset:2048\n\t"
-        "ds_read_b128 %6, %13 offset:4096\n\t"
-        "ds_read_b128 %7, %13 offset:6144\n\t"
-        "ds_read_b128 %2, %12 offset:512\n\t"
-        "ds_read_b128 %3, %12 offset:2560\n\t"
-        "ds_read_b128 %8, %13 offset:512\n\t"
-        "ds_read_b128 %9, %13 offset:2560\n\t"
-        "ds_read_b128 %10, %13 offset:4608\n\t"
-        "ds_read_b128 %11, %13 offset:6656\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a00), "=&v"(a10), "=&v"(a01), "=&v"(a11), "=&v"(b00), "=&v"(b10), "=&v"(b20), "=&v"(b30),
-          "=&v"(b01), "=&v"(b11), "=&v"(b21), "=&v"(b31)
-        : "v"(ab), "v"(bb)
-        : "memory");
-    const bf16x8_t af[2][2] = {{a00, a01}, {a10, a11}};           // [i][u]
-    const bf16x8_t bw[4][2] = {{b00, b01}, {b10, b11}, {b20, b21}, {b30, b31}};  // [j][u]
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][u], bw[j][u], acc[i][j], 0, 0, 0);
+    if (ks + 2 < Ks) dma_kstep(ks + 2);
+    lds_read(rd, ks);
+    __builtin_amdgcn_sched_barrier(0);
+    if (prev) mfma_half(prv, 1);
+    mfma_half(rd, 0);
+  };
+
+  // (Ks is even: the plan takes this kernel only then)
+  dma_kstep(0);
+  dma_kstep(1);
+  for (int ks = 0; ks < Ks; ks += 2) {
+    step(ks, fr0, fr1, ks > 0);
+    step(ks + 1, fr1, fr0, true);
   }
+  mfma_half(fr1, 1);
 
   if (AM == A_NORM && tid < 256) {
     // 1 / RMS per row from the producer's partial sums of squares (two threads per row)
