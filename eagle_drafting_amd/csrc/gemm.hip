@@ -207,10 +207,9 @@ GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok, bool skinny_o
     p.NW = 4;
     p.mblocks = tm;
     p.ngroups = tg;
-    // the vocabulary projection runs on 128 x 512 tiles (both operands through LDS) when that still gives
-    // at least two workgroups per compute unit and the k-step count is even; FP8 weights keep the 128 x 128
-    // kernel
-    if (argmax && Ks % 2 == 0 && (long long)((tg + 3) / 4) * tm >= 512) p.tiled = 3;
+    // the vocabulary projection runs on 128 x 512 tiles when that still gives at least two workgroups per
+    // compute unit; FP8 weights keep the 128 x 128 kernel
+    if (argmax && (long long)((tg + 3) / 4) * tm >= 512) p.tiled = 3;
     if (!argmax) {
       int ks = 1;
       while (tg * tm * ks < 512 && Ks >= 16 * ks && (8LL * ks * M <= Kd || tg * tm * ks < 256)) ks *= 2;

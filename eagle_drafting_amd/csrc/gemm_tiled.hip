@@ -241,31 +241,28 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
 }
 
 // Vocabulary projection above 128 rows (bound by the bf16 MFMA rate): 128 x 512 workgroup tiles, 8 waves
-// of 64 x 128 (2 x 4 blocks of v_mfma_f32_32x32x16_bf16). Both operands go from memory straight into LDS
-// with buffer loads that write LDS (one 1 KiB wave load per 16 x 32 fragment, in the fragment order the
-// operand reads use, so the reads are lane-linear 16-byte chunks): per 32-deep k-step 8 activation
-// fragments (per-lane row addresses, zeros past the last row) and 32 weight fragments (packed contiguous;
-// zeros past the last tile). Three k-step buffers (40 KiB each) keep two k-steps in flight behind the one
-// being multiplied, without registers; every operand is read from memory once per workgroup (the 128 x
-// 128 kernel loads each weight fragment into the registers of two waves). Workgroups are ordered
+// side by side, each 128 rows x 64 columns (4 x 2 blocks of v_mfma_f32_32x32x16_bf16). Each weight
+// fragment is used by exactly one wave, so weights go from the packed fragments straight into that wave's
+// registers (16-byte lane loads in operand order), two k-steps ahead; the activations, used by all eight
+// waves, go from memory straight into LDS with buffer loads that write LDS (one 1 KiB wave load per 16 x
+// 32 fragment, in the order the operand reads use, so the reads are lane-linear 16-byte chunks; zeros past
+// the last row) through three k-step buffers. Per 32-deep k-step a compute unit then moves 40 KiB through
+// its vector-memory path and 72 KiB through LDS for 128 products per SIMD. Workgroups are ordered
 // XCD-aware as in the 128 x 128 kernel (a 512-column weight group leaves HBM once; its other row blocks
 // hit the XCD's L2). The 128 x 512 product goes through LDS as four 128 x 128 quarters, two at a time,
 // into the shared epilogue (waves 0-3 and 4-7 each run one quarter's).
 template <int AM, int EP>
 __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g) {
   constexpr int BM = 128;
-  constexpr int FA = 8, FB = 32;            // fragments per k-step: 16-row activation tiles, 16-column weight tiles
-  constexpr int SB = (FA + FB) * 1024;      // bytes per k-step buffer
-  constexpr int NBUF = 3;
-  constexpr int SMEM = 2 * 128 * 128 * 4;   // two 128 x 128 fp32 quarters for the epilogue (>= NBUF * SB)
-  static_assert(NBUF * SB <= SMEM, "k-step buffers exceed the epilogue area");
+  constexpr int SB = 8 * 1024;              // bytes per k-step activation buffer (8 fragments)
+  constexpr int SMEM = 2 * 128 * 128 * 4;   // two 128 x 128 fp32 quarters for the epilogue
+  static_assert(3 * SB <= SMEM, "k-step buffers exceed the epilogue area");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   __shared__ float s_inv[BM];
 
   const int M = g.M, Ks = g.Ks, Nt = g.Nt;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wr = wave >> 2, wc = wave & 3;  // 64-row half, 128-column quarter of the tile
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // columns 64 wave .. + 63 of the tile
   const int nwide = (g.ngroups + 3) / 4;    // 512-column groups
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int gw = (slot / g.mblocks) * 8 + xcd;
@@ -273,100 +270,97 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g) {
   const int m0 = (slot % g.mblocks) * BM;
   const int nt0 = gw * 32;                  // first 16-column tile
 
-  // wave w moves activation fragment w (rows m0 + 16 w .. + 15) and weight fragments w, w + 8, w + 16,
-  // w + 24 of every k-step; fragment lane l holds row (or column) l % 16, k elements 8 (l / 16) .. + 7.
-  // The loads are written as inline assembly: the compiler then does not know they write LDS, and does
-  // not wait for every outstanding k-step before each fragment read; the explicit waits below order them.
-  typedef int i32x4_t __attribute__((ext_vector_type(4)));
-  auto rsrc4 = [](const void* base, int num) {  // raw buffer descriptor: base, stride 0, num_records
-    const uint64_t a = (uint64_t)(uintptr_t)base;
-    i32x4_t r;
-    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
-    r.z = __builtin_amdgcn_readfirstlane(num);
-    r.w = __builtin_amdgcn_readfirstlane(0x00020000);
-    return r;
+  // operand lane l of 32 rows (or columns) 32 b .. + 31, k-half u: fragment 2 b + (l % 32) / 16, fragment
+  // lane l % 16 + 16 (2 u + l / 32)
+  const int fr_t = (lane & 31) >> 4, fr_l = (lane & 15) + 16 * (lane >> 5);
+  // weights: load (j, u) of a k-step brings column block j, k-half u of this wave's 64 columns (fragment
+  // tile nt0 + 4 wave + 2 j + fr_t); tiles past the last one read zeros (descriptor bound)
+  const int ntw = min(32, Nt - nt0);
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)g.Wp_raw + (size_t)nt0 * Ks * 1024), (short)0, ntw * Ks * 1024, 0x00020000);
+  uint32_t w_off[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) w_off[j][u] = (uint32_t)(((4 * wave + 2 * j + fr_t) * Ks * 64 + fr_l + 32 * u) * 16);
+  typedef bf16x8_t RegW[4];  // [2 j + u]
+  auto wload = [&](RegW& r, int ks) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        r[2 * j + u] =
+            __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_off[j][u], ks * 1024, 0));
   };
-  const i32x4_t a_rsrc = rsrc4(g.A, gemm_a_rows(g) * g.lda * 2);
-  const int ntw = min(32, Nt - nt0);        // weight tiles of this group that exist (past them: zeros)
-  const i32x4_t w_rsrc = rsrc4((const char*)g.Wp_raw + (size_t)nt0 * Ks * 1024, ntw * Ks * 1024);
+  // activations: wave w moves fragment w (rows m0 + 16 w .. + 15; fragment lane l holds row l % 16, k
+  // elements 8 (l / 16) .. + 7). The load is inline assembly so that the compiler, which does not see it
+  // write LDS, does not wait for it before every fragment read; the explicit waits below order it.
+  typedef int i32x4_t __attribute__((ext_vector_type(4)));
+  i32x4_t a_rsrc;
+  {
+    const uint64_t a = (uint64_t)(uintptr_t)g.A;
+    a_rsrc.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    a_rsrc.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+    a_rsrc.z = __builtin_amdgcn_readfirstlane(gemm_a_rows(g) * g.lda * 2);
+    a_rsrc.w = __builtin_amdgcn_readfirstlane(0x00020000);
+  }
   const int arow = m0 + 16 * wave + (lane & 15);
   const bool a_ok = arow < M;
   const uint32_t a_off = a_ok ? (uint32_t)((gemm_a_row(g, arow) * g.lda + 8 * (lane >> 4)) * 2) : 0x7ffffff0u;
-  const uint32_t w_off = (uint32_t)(wave * Ks * 1024 + 16 * lane);
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
-  auto dma_kstep = [&](int ks) {
-    const uint32_t buf = lds_base + (uint32_t)((ks % NBUF) * SB);
-    const uint32_t aoff = a_ok ? a_off + 64u * ks : a_off;
-    const uint32_t m0a = buf + wave * 1024;
+  auto adma = [&](int ks, int buf) {  // k-steps past the last one read zeros
+    const uint32_t aoff = a_ok && ks < Ks ? a_off + 64u * ks : 0x7ffffff0u;
+    const uint32_t m0a = lds_base + (uint32_t)(buf * SB + wave * 1024);
     asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(aoff), "s"(a_rsrc), "{m0}"(m0a) : "memory");
-    const int soff = ks * 1024;
+  };
+  const int a_lane = (fr_t * 64 + fr_l) * 16;  // row block i: + 2048 i; k-half 1: + 512
+
+  f32x16_t acc[4][2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t m0b = buf + FA * 1024 + (wave + 8 * q) * 1024;
-      asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(w_off + 8 * q * Ks * 1024), "s"(w_rsrc),
-                   "s"(soff), "{m0}"(m0b)
-                   : "memory");
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // k-step ks (its weights in wr, its activations in buffer ks % 3): this wave's loads of ks are done once
+  // only those of ks + 1 (four weight loads, then one activation load) may remain, and the barrier then
+  // covers every wave's activation load of ks and every wave's reads of ks - 1, whose buffer takes the
+  // activations of ks + 2. The loop runs a multiple of three k-steps with every load unconditional, so the
+  // compiler's own wait counts for the weight registers stay exact; k-steps past the last one multiply
+  // zero activations (their weight loads repeat the last k-step)
+  auto step = [&](int ks, int buf, const RegW& wr, RegW& wnext, int buf2) {
+    __builtin_amdgcn_s_waitcnt(0x0075);  // vmcnt(5) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    wload(wnext, min(ks + 2, Ks - 1));
+    adma(ks + 2, buf2);
+    const char* b = smem + buf * SB + a_lane;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      bf16x8_t af[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8_t*)(b + i * 2048 + u * 512);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], wr[2 * j + u], acc[i][j], 0, 0, 0);
     }
   };
 
-  f32x16_t acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-  // operand lane l of 32 rows (or columns) 32 b .. + 31, k-half u: fragment 2 b + (l % 32) / 16, fragment
-  // lane l % 16 + 16 (2 u + l / 32). Byte offsets of this lane's first activation (block i = 0, k-half 0)
-  // and weight (block j = 0) reads inside a k-step buffer; block + 1 is 2 KiB further, k-half 1 512 bytes.
-  const int fr_t = (lane & 31) >> 4, fr_l = (lane & 15) + 16 * (lane >> 5);
-  const int a_lane = ((4 * wr + fr_t) * 64 + fr_l) * 16;
-  const int b_lane = FA * 1024 + ((8 * wc + fr_t) * 64 + fr_l) * 16;
-  // the fragments of k-step ks are read while the k-half-1 products of k-step ks - 1 run (their operands
-  // are held over from the previous k-step), then the k-half-0 products of ks; the accumulation order is
-  // the plain k order
-  bf16x8_t fr0[12], fr1[12];  // [0..3]: activation (i, u) at 2 i + u; [4..11]: weight (j, u) at 4 + 2 j + u
-  auto lds_read = [&](bf16x8_t (&f)[12], int ks) {
-    const char* b = smem + (ks % NBUF) * SB;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) f[2 * i + u] = *(const bf16x8_t*)(b + a_lane + i * 2048 + u * 512);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) f[4 + 2 * j + u] = *(const bf16x8_t*)(b + b_lane + j * 2048 + u * 512);
-  };
-  auto mfma_half = [&](const bf16x8_t (&f)[12], int u) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[2 * i + u], f[4 + 2 * j + u], acc[i][j], 0, 0, 0);
-  };
-  // k-step ks: this wave's reads of ks - 1 and its loads of ks are done (only the loads of ks + 1, five,
-  // may remain); the barrier then covers every wave, so the buffer of ks - 1 takes the loads of ks + 2
-  auto step = [&](int ks, bf16x8_t (&rd)[12], const bf16x8_t (&prv)[12], bool prev) {
-    if (ks + 1 < Ks) __builtin_amdgcn_s_waitcnt(0x0075);  // vmcnt(5) lgkmcnt(0)
-    else __builtin_amdgcn_s_waitcnt(0x0070);              // vmcnt(0) lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (ks + 2 < Ks) dma_kstep(ks + 2);
-    lds_read(rd, ks);
-    __builtin_amdgcn_sched_barrier(0);
-    if (prev) mfma_half(prv, 1);
-    mfma_half(rd, 0);
-  };
-
-  // (Ks is even: the plan takes this kernel only then)
-  dma_kstep(0);
-  dma_kstep(1);
-  for (int ks = 0; ks < Ks; ks += 2) {
-    step(ks, fr0, fr1, ks > 0);
-    step(ks + 1, fr1, fr0, true);
+  RegW w0, w1, w2;
+  wload(w0, 0);
+  adma(0, 0);
+  wload(w1, min(1, Ks - 1));
+  adma(1, 1);
+  const int nsteps = (Ks + 2) / 3 * 3;
+  for (int ks = 0; ks < nsteps; ks += 3) {
+    step(ks, 0, w0, w2, 2);
+    step(ks + 1, 1, w1, w0, 0);
+    step(ks + 2, 2, w2, w1, 1);
   }
-  mfma_half(fr1, 1);
+  __builtin_amdgcn_s_waitcnt(0x0070);  // the loads of the two k-steps past the loop have landed
 
   if (AM == A_NORM && tid < 256) {
     // 1 / RMS per row from the producer's partial sums of squares (two threads per row)
@@ -379,23 +373,23 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g) {
     t += __shfl_xor(t, 1, PE_WAVE);
     if (h == 0) s_inv[r] = rsqrtf(t / (float)g.Kd + g.eps);
   }
-  // two passes of two 128 x 128 quarters: quarter 2 p + s (columns 128 (2 p + s) ..) is held by the waves
-  // with wc = 2 p + s and goes to Cs[s] (column XOR-swizzle as in the 128 x 128 kernel), then waves
-  // 4 s .. 4 s + 3 run its epilogue
+  // two passes of two 128 x 128 quarters: quarter 2 p + s (columns 128 (2 p + s) ..) is held by waves
+  // 4 p + 2 s and 4 p + 2 s + 1 and goes to LDS quarter s (column XOR-swizzle as in the 128 x 128 kernel),
+  // then waves 4 s .. 4 s + 3 run its epilogue
   const int c = lane & 31, hq = lane >> 5;
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     __syncthreads();  // the k-step buffers (or the previous pass's quarters) are no longer read
-    if ((wc >> 1) == p) {
-      float* C = (float*)smem + (wc & 1) * 128 * 128;
+    if ((wave >> 2) == p) {
+      float* C = (float*)smem + ((wave >> 1) & 1) * 128 * 128;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const int row = 64 * wr + 32 * i + 8 * (e >> 2) + 4 * hq + (e & 3);
-            const int col = (32 * j + c) ^ (hq << 5);
+            const int row = 32 * i + 8 * (e >> 2) + 4 * hq + (e & 3);
+            const int col = (64 * (wave & 1) + 32 * j + c) ^ (hq << 5);
             C[row * 128 + col] = acc[i][j][e];
           }
     }
