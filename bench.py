@@ -107,23 +107,29 @@ def kernel_roofline(name, us, launches, nbytes, flops, rows):
             "bytes_per_launch": nbytes, "flops_per_launch": flops}
 
 
-def kernel_source_digest():
-    """sha256 over the sources that define the projection kernels (the LM head among them)."""
+KERNEL_SOURCES = {
+    "lm_head": ("gemm.hip", "gemm_tiled.hip", "kernels.h", "common.h"),
+    "attention": ("attention.hip", "kernels.h", "common.h"),
+}
+
+
+def kernel_source_digest(kernel="lm_head"):
+    """sha256 over the sources that define a kernel family (the projections, or attention)."""
     h = hashlib.sha256()
-    for name in ("gemm.hip", "gemm_tiled.hip", "kernels.h", "common.h"):
+    for name in KERNEL_SOURCES.get(kernel, KERNEL_SOURCES["lm_head"]):
         h.update(open(os.path.join(ROOT, "eagle_drafting_amd", "csrc", name), "rb").read())
     return h.hexdigest()
 
 
-def traffic_from_profile(workload_name):
-    """HBM bytes per LM-head launch measured by rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, scaled by the
-    plain-copy calibration), if the committed measurement was taken on this workload with the current
-    projection sources."""
-    path = os.path.join(ROOT, "profiles", f"lm_head_traffic_{workload_name}.json")
+def traffic_from_profile(kernel, workload_name):
+    """HBM bytes per launch of a kernel measured by rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, scaled by
+    the plain-copy calibration), if the committed measurement was taken on this workload with the current
+    sources of that kernel."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic_{workload_name}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("workload") != workload_name or rec.get("kernel_src_sha256") != kernel_source_digest():
+    if rec.get("workload") != workload_name or rec.get("kernel_src_sha256") != kernel_source_digest(kernel):
         return None
     return rec.get("bytes_per_launch")
 
@@ -177,6 +183,16 @@ class Run:
     def verify_call(self):
         self.pe.pe_verify(self.ctx, self.w.B, self.w.K, self.T, self.draft, self.fin, self.d["req_slot"],
                           self.d["seq_len"], *self.outs)
+
+    def verify_sampled_call(self):
+        """The sampling form of verify at temperature 0.3 (the pages' example request), seeded uniforms."""
+        if not hasattr(self, "u_s"):
+            torch, w = self.torch, self.w
+            rng = np.random.default_rng(w.seed + 23)
+            self.u_s = torch.from_numpy(rng.random((w.B, w.K), dtype=np.float32)).cuda()
+            self.v_s = torch.from_numpy(rng.random((w.B, w.K + 1), dtype=np.float32)).cuda()
+        self.pe.pe_verify_sampled(self.ctx, self.w.B, self.w.K, self.T, self.draft, 0.3, self.u_s, self.v_s, self.fin,
+                                  self.d["req_slot"], self.d["seq_len"], *self.outs)
 
     def step(self):
         self.draft_call()
@@ -537,6 +553,9 @@ def measure(r, steps, warmup, reps):
     out = {"ms_per_step": ms / steps, "wall_ms_per_step": 1e3 * wall / steps,
            "step_us": r.per_call(r.step, reps), "draft_us": r.per_call(r.draft_call, reps),
            "verify_us": r.per_call(r.verify_call, reps)}
+    r.verify_sampled_call()
+    out["verify_sampled_us"] = r.per_call(r.verify_sampled_call, reps)
+    r.verify_call()  # leave the greedy verify's outputs (accept lengths) in place
     out["kernels"] = r.kernel_times(max(10, reps // 5))
     out["rooflines"] = r.rooflines(out["kernels"])
     return out
@@ -548,6 +567,7 @@ def target_entry(r, m):
     t_draft = m["draft_us"]["median"]
     e = {"workload": w.name, "B": w.B, "K": w.K, "ms_per_step": m["ms_per_step"],
          "step_us": m["step_us"], "t_draft_us": m["draft_us"], "t_verify_us": m["verify_us"],
+         "t_verify_sampled_us": m["verify_sampled_us"],
          "draft_tokens_per_s": w.B * w.K / (m["ms_per_step"] * 1e-3), "steps_per_s": 1e3 / m["ms_per_step"],
          "draft_hbm_frac": ab["draft"] / (t_draft * 1e-6) / (PEAK_HBM_GBS * 1e9),
          "algorithmic_MB": {k: v / 1e6 for k, v in ab.items()},
@@ -600,7 +620,7 @@ def main():
                    key=lambda k: rl[k]["avg_launch_us"] * rl[k]["launches"])
     roof = dict(rl[dominant])
     roof["kernel"] = dominant
-    roof["traffic"] = traffic_from_profile(w.name) if dominant == "lm_head" else None
+    roof["traffic"] = traffic_from_profile(dominant, w.name)
     headline_cpu = {"w": w, "state": r.state, "T_host": r.T_host, "draft": r.draft.cpu().numpy()}
     result = {
         "metric": METRIC,
@@ -623,6 +643,7 @@ def main():
         "step_us": m["step_us"],
         "t_draft_us": m["draft_us"],
         "t_verify_us": m["verify_us"],
+        "t_verify_sampled_us": m["verify_sampled_us"],
         "step_hbm_frac": ab["step"] / (m["ms_per_step"] * 1e-3) / (PEAK_HBM_GBS * 1e9),
         "draft_hbm_frac": ab["draft"] / (m["draft_us"]["median"] * 1e-6) / (PEAK_HBM_GBS * 1e9),
         "algorithmic_MB": {k: v / 1e6 for k, v in ab.items()},
