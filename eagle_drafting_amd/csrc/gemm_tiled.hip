@@ -240,22 +240,26 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
   else tile_epilogue<EP, AM == A_NORM>(g, Cs, s_inv, m0, nt0, ng);
 }
 
-// Vocabulary projection above 128 rows (bound by the bf16 MFMA rate): 128 x 512 workgroup tiles, 8 waves
-// side by side, each 128 rows x 64 columns (4 x 2 blocks of v_mfma_f32_32x32x16_bf16). Each weight
-// fragment is used by exactly one wave, so weights go from the packed fragments straight into that wave's
-// registers (16-byte lane loads in operand order), two k-steps ahead; the activations, used by all eight
-// waves, go from memory straight into LDS with buffer loads that write LDS (one 1 KiB wave load per 16 x
-// 32 fragment, in the order the operand reads use, so the reads are lane-linear 16-byte chunks; zeros past
-// the last row) through three k-step buffers. Per 32-deep k-step a compute unit then moves 40 KiB through
-// its vector-memory path and 72 KiB through LDS for 128 products per SIMD. Workgroups are ordered
-// XCD-aware as in the 128 x 128 kernel (a 512-column weight group leaves HBM once; its other row blocks
-// hit the XCD's L2). The 128 x 512 product goes through LDS as four 128 x 128 quarters, two at a time,
-// into the shared epilogue (waves 0-3 and 4-7 each run one quarter's).
-template <int AM, int EP>
-__global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g) {
+// Vocabulary projection above 128 rows (bound by the bf16 MFMA rate): 128 x 64 NWV workgroup tiles (NWV 8:
+// 128 x 512, one workgroup per compute unit; NWV 4: 128 x 256, two), NWV waves side by side, each 128 rows
+// x 64 columns (4 x 2 blocks of v_mfma_f32_32x32x16_bf16). Each weight fragment is used by exactly one
+// wave, so weights go from the packed fragments straight into that wave's registers (16-byte lane loads in
+// operand order), two k-steps ahead; the activations, used by every wave, go from memory straight into LDS
+// with buffer loads that write LDS (one 1 KiB wave load per 16 x 32 fragment, in the order the operand
+// reads use, so the reads are lane-linear 16-byte chunks; zeros past the last row) through three k-step
+// buffers. Per 32-deep k-step a compute unit then moves 40 (NWV 8) or 48 KiB (NWV 4) through its
+// vector-memory path and 72 or 80 KiB through LDS for 128 products per SIMD. Workgroups are ordered
+// XCD-aware as in the 128 x 128 kernel (a weight column group leaves HBM once; its other row blocks hit
+// the XCD's L2). The product goes through LDS as 128 x 128 quarters, QP at a time, into the shared
+// epilogue (each quarter's run by four waves).
+template <int AM, int EP, int NWV>
+__global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(GemmArgs g) {
   constexpr int BM = 128;
+  constexpr int TW = 4 * NWV;               // 16-column tiles per workgroup (64 columns per wave)
+  constexpr int QP = NWV / 4;               // 128 x 128 quarters per epilogue pass
+  constexpr int AD = 8 / NWV;               // activation fragments each wave moves per k-step
   constexpr int SB = 8 * 1024;              // bytes per k-step activation buffer (8 fragments)
-  constexpr int SMEM = 2 * 128 * 128 * 4;   // two 128 x 128 fp32 quarters for the epilogue
+  constexpr int SMEM = QP * 128 * 128 * 4;  // the epilogue's 128 x 128 fp32 quarters
   static_assert(3 * SB <= SMEM, "k-step buffers exceed the epilogue area");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   __shared__ float s_inv[BM];
@@ -263,19 +267,19 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g) {
   const int M = g.M, Ks = g.Ks, Nt = g.Nt;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // columns 64 wave .. + 63 of the tile
-  const int nwide = (g.ngroups + 3) / 4;    // 512-column groups
+  const int nwide = (Nt + TW - 1) / TW;     // column groups of TW tiles
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int gw = (slot / g.mblocks) * 8 + xcd;
   if (gw >= nwide) return;
   const int m0 = (slot % g.mblocks) * BM;
-  const int nt0 = gw * 32;                  // first 16-column tile
+  const int nt0 = gw * TW;                  // first 16-column tile
 
   // operand lane l of 32 rows (or columns) 32 b .. + 31, k-half u: fragment 2 b + (l % 32) / 16, fragment
   // lane l % 16 + 16 (2 u + l / 32)
   const int fr_t = (lane & 31) >> 4, fr_l = (lane & 15) + 16 * (lane >> 5);
   // weights: load (j, u) of a k-step brings column block j, k-half u of this wave's 64 columns (fragment
   // tile nt0 + 4 wave + 2 j + fr_t); tiles past the last one read zeros (descriptor bound)
-  const int ntw = min(32, Nt - nt0);
+  const int ntw = min(TW, Nt - nt0);
   const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((const char*)g.Wp_raw + (size_t)nt0 * Ks * 1024), (short)0, ntw * Ks * 1024, 0x00020000);
   uint32_t w_off[2][2];
@@ -304,14 +308,23 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g) {
     a_rsrc.z = __builtin_amdgcn_readfirstlane(gemm_a_rows(g) * g.lda * 2);
     a_rsrc.w = __builtin_amdgcn_readfirstlane(0x00020000);
   }
-  const int arow = m0 + 16 * wave + (lane & 15);
-  const bool a_ok = arow < M;
-  const uint32_t a_off = a_ok ? (uint32_t)((gemm_a_row(g, arow) * g.lda + 8 * (lane >> 4)) * 2) : 0x7ffffff0u;
+  // wave w moves activation fragments w + NWV q (q < AD)
+  bool a_ok[AD];
+  uint32_t a_off[AD];
+#pragma unroll
+  for (int q = 0; q < AD; ++q) {
+    const int arow = m0 + 16 * (wave + NWV * q) + (lane & 15);
+    a_ok[q] = arow < M;
+    a_off[q] = a_ok[q] ? (uint32_t)((gemm_a_row(g, arow) * g.lda + 8 * (lane >> 4)) * 2) : 0x7ffffff0u;
+  }
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
   auto adma = [&](int ks, int buf) {  // k-steps past the last one read zeros
-    const uint32_t aoff = a_ok && ks < Ks ? a_off + 64u * ks : 0x7ffffff0u;
-    const uint32_t m0a = lds_base + (uint32_t)(buf * SB + wave * 1024);
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(aoff), "s"(a_rsrc), "{m0}"(m0a) : "memory");
+#pragma unroll
+    for (int q = 0; q < AD; ++q) {
+      const uint32_t aoff = a_ok[q] && ks < Ks ? a_off[q] + 64u * ks : 0x7ffffff0u;
+      const uint32_t m0a = lds_base + (uint32_t)(buf * SB + (wave + NWV * q) * 1024);
+      asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(aoff), "s"(a_rsrc), "{m0}"(m0a) : "memory");
+    }
   };
   const int a_lane = (fr_t * 64 + fr_l) * 16;  // row block i: + 2048 i; k-half 1: + 512
 
@@ -324,13 +337,13 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   // k-step ks (its weights in wr, its activations in buffer ks % 3): this wave's loads of ks are done once
-  // only those of ks + 1 (four weight loads, then one activation load) may remain, and the barrier then
+  // only those of ks + 1 (four weight loads, then AD activation loads) may remain, and the barrier then
   // covers every wave's activation load of ks and every wave's reads of ks - 1, whose buffer takes the
   // activations of ks + 2. The loop runs a multiple of three k-steps with every load unconditional, so the
   // compiler's own wait counts for the weight registers stay exact; k-steps past the last one multiply
   // zero activations (their weight loads repeat the last k-step)
   auto step = [&](int ks, int buf, const RegW& wr, RegW& wnext, int buf2) {
-    __builtin_amdgcn_s_waitcnt(0x0075);  // vmcnt(5) lgkmcnt(0)
+    __builtin_amdgcn_s_waitcnt(0x0070 | (4 + AD));  // vmcnt(4 + AD) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     wload(wnext, min(ks + 2, Ks - 1));
@@ -373,15 +386,15 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g) {
     t += __shfl_xor(t, 1, PE_WAVE);
     if (h == 0) s_inv[r] = rsqrtf(t / (float)g.Kd + g.eps);
   }
-  // two passes of two 128 x 128 quarters: quarter 2 p + s (columns 128 (2 p + s) ..) is held by waves
-  // 4 p + 2 s and 4 p + 2 s + 1 and goes to LDS quarter s (column XOR-swizzle as in the 128 x 128 kernel),
-  // then waves 4 s .. 4 s + 3 run its epilogue
+  // two passes of QP 128 x 128 quarters: quarter QP p + s (columns 128 (QP p + s) ..) is held by waves
+  // 2 (QP p + s) and 2 (QP p + s) + 1 and goes to LDS quarter s (column XOR-swizzle as in the 128 x 128
+  // kernel), then waves 4 s .. 4 s + 3 run its epilogue
   const int c = lane & 31, hq = lane >> 5;
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     __syncthreads();  // the k-step buffers (or the previous pass's quarters) are no longer read
-    if ((wave >> 2) == p) {
-      float* C = (float*)smem + ((wave >> 1) & 1) * 128 * 128;
+    if ((wave >> 1) / QP == p) {
+      float* C = (float*)smem + ((wave >> 1) % QP) * 128 * 128;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -395,7 +408,7 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g) {
     }
     __syncthreads();
     const int s = wave >> 2;
-    const int ng = 4 * gw + 2 * p + s;
+    const int ng = nt0 / 8 + QP * p + s;
     if (ng < g.ngroups)
       tile_epilogue<EP, AM == A_NORM>(g, (const float*)smem + s * 128 * 128, s_inv, m0, ng * 8, ng, 0, 128, tid & 255);
   }
@@ -984,9 +997,18 @@ static hipError_t launch_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode,
 hipError_t launch_gemm_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st) {
   if (p.tiled == 2) return launch_gemm_stream(p, a, a_mode, epi, st);
   if (p.tiled == 3 && !a.wscale && p.ksplit == 1 && a_mode == A_NORM && epi == EPI_ARGMAX) {
-    const int nwide = (p.ngroups + 3) / 4;
-    const dim3 grid(8 * ((nwide + 7) / 8) * p.mblocks);
-    hipLaunchKernelGGL((gemm_wide_kernel<A_NORM, EPI_ARGMAX>), grid, dim3(512), 0, st, a);
+    // 8 waves (128 x 512, one workgroup per compute unit) or 4 waves (128 x 256, two per compute unit).
+    // Measured LM heads: Qwen (d 2048) B 128 K 7 668 -> 624 us and B 32 K 7 246 -> 222 us with 4 waves,
+    // GPT-OSS (d 2880) B 64 K 10 800 -> 811-829 us, so the longer reduction keeps 8
+    if (a.Ks <= 64) {
+      const int nwide = (p.Nt + 15) / 16;
+      hipLaunchKernelGGL((gemm_wide_kernel<A_NORM, EPI_ARGMAX, 4>), dim3(8 * ((nwide + 7) / 8) * p.mblocks), dim3(256), 0,
+                         st, a);
+    } else {
+      const int nwide = (p.Nt + 31) / 32;
+      hipLaunchKernelGGL((gemm_wide_kernel<A_NORM, EPI_ARGMAX, 8>), dim3(8 * ((nwide + 7) / 8) * p.mblocks), dim3(512), 0,
+                         st, a);
+    }
     return hipGetLastError();
   }
   return a.wscale ? launch_tiled<1>(p, a, a_mode, epi, st) : launch_tiled<0>(p, a, a_mode, epi, st);
