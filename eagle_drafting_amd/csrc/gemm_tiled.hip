@@ -240,9 +240,9 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
   else tile_epilogue<EP, AM == A_NORM>(g, Cs, s_inv, m0, nt0, ng);
 }
 
-// Vocabulary projection above 128 rows (bound by the bf16 MFMA rate): 128 x 64 NWV workgroup tiles (NWV 8:
-// 128 x 512, one workgroup per compute unit; NWV 4: 128 x 256, two), NWV waves side by side, each 128 rows
-// x 64 columns (4 x 2 blocks of v_mfma_f32_32x32x16_bf16). Each weight fragment is used by exactly one
+// Vocabulary projection above 128 rows (bound by the bf16 MFMA rate), and gate/up where it pays:
+// 128 x 64 NWV workgroup tiles (NWV 8: 128 x 512, one workgroup per compute unit; NWV 4: 128 x 256, two),
+// NWV waves side by side, each 128 rows x 64 columns (4 x 2 blocks of v_mfma_f32_32x32x16_bf16). Each weight fragment is used by exactly one
 // wave, so weights go from the packed fragments straight into that wave's registers (16-byte lane loads in
 // operand order), two k-steps ahead; the activations, used by every wave, go from memory straight into LDS
 // with buffer loads that write LDS (one 1 KiB wave load per 16 x 32 fragment, in the order the operand
@@ -996,6 +996,16 @@ static hipError_t launch_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode,
 
 hipError_t launch_gemm_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st) {
   if (p.tiled == 2) return launch_gemm_stream(p, a, a_mode, epi, st);
+  if (p.tiled == 1 && !a.wscale && p.ksplit == 1 && a_mode == A_NORM && epi == EPI_SWIGLU && a.Ks > 64 &&
+      (p.Nt + 15) / 16 * p.mblocks >= 256) {
+    // gate/up with a long reduction and at least one 128 x 256 tile per compute unit (measured: GPT-OSS
+    // B 64 K 10 (90 k-steps, 408 tiles) 123 -> 105 us; Qwen B 128 K 7 (64 k-steps, 384 tiles) 76 -> 79 us,
+    // so it stays on the 128 x 128 kernel)
+    const int nwide = (p.Nt + 15) / 16;
+    hipLaunchKernelGGL((gemm_wide_kernel<A_NORM, EPI_SWIGLU, 4>), dim3(8 * ((nwide + 7) / 8) * p.mblocks), dim3(256), 0,
+                       st, a);
+    return hipGetLastError();
+  }
   if (p.tiled == 3 && !a.wscale && p.ksplit == 1 && a_mode == A_NORM && epi == EPI_ARGMAX) {
     // 8 waves (128 x 512, one workgroup per compute unit) or 4 waves (128 x 256, two per compute unit).
     // Measured LM heads: Qwen (d 2048) B 128 K 7 668 -> 624 us and B 32 K 7 246 -> 222 us with 4 waves,
