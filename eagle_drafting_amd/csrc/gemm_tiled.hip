@@ -240,18 +240,18 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
   else tile_epilogue<EP, AM == A_NORM>(g, Cs, s_inv, m0, nt0, ng);
 }
 
-// Vocabulary projection above 128 rows (bound by the bf16 MFMA rate), and gate/up where it pays:
-// 128 x 64 NWV workgroup tiles (NWV 8: 128 x 512, one workgroup per compute unit; NWV 4: 128 x 256, two),
-// NWV waves side by side, each 128 rows x 64 columns (4 x 2 blocks of v_mfma_f32_32x32x16_bf16). Each weight fragment is used by exactly one
-// wave, so weights go from the packed fragments straight into that wave's registers (16-byte lane loads in
-// operand order), two k-steps ahead; the activations, used by every wave, go from memory straight into LDS
-// with buffer loads that write LDS (one 1 KiB wave load per 16 x 32 fragment, in the order the operand
-// reads use, so the reads are lane-linear 16-byte chunks; zeros past the last row) through three k-step
-// buffers. Per 32-deep k-step a compute unit then moves 40 (NWV 8) or 48 KiB (NWV 4) through its
-// vector-memory path and 72 or 80 KiB through LDS for 128 products per SIMD. Workgroups are ordered
-// XCD-aware as in the 128 x 128 kernel (a weight column group leaves HBM once; its other row blocks hit
-// the XCD's L2). The product goes through LDS as 128 x 128 quarters, QP at a time, into the shared
-// epilogue (each quarter's run by four waves).
+// Vocabulary projection above 128 rows (bound by the bf16 MFMA rate), and gate/up where it pays: 128 x 64 NWV
+// workgroup tiles (NWV 8: 128 x 512, one workgroup per compute unit; NWV 4: 128 x 256, two), NWV waves side
+// by side, each 128 rows x 64 columns (4 x 2 blocks of v_mfma_f32_32x32x16_bf16). Each weight fragment is
+// used by exactly one wave, so weights go from the packed fragments straight into that wave's registers
+// (16-byte lane loads in operand order), two k-steps ahead; the activations, used by every wave, go from
+// memory straight into LDS with buffer loads that write LDS (one 1 KiB wave load per 16 x 32 fragment, in the
+// order the operand reads use, so the reads are lane-linear 16-byte chunks; zeros past the last row) through
+// three k-step buffers. Per 32-deep k-step a compute unit then moves 40 (NWV 8) or 48 KiB (NWV 4) through its
+// vector-memory path and 72 or 80 KiB through LDS for 128 products per SIMD. Workgroups are ordered XCD-aware
+// as in the 128 x 128 kernel (a weight column group leaves HBM once; its other row blocks hit the XCD's L2).
+// The product goes through LDS as 128 x 128 quarters, QP at a time, into the shared epilogue (each quarter's
+// run by four waves).
 template <int AM, int EP, int NWV>
 __global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(GemmArgs g) {
   constexpr int BM = 128;
