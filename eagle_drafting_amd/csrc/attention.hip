@@ -509,6 +509,70 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
     out[c] = f32_to_bf16(((sred[0][c] + sred[1][c]) + (sred[2][c] + sred[3][c])) * inv);
 }
 
+// Same merge for rows with at most 16 splits: a quarter wave (16 lanes) per (row, head) pair, four pairs per
+// wave, sixteen per workgroup. Lane s of a quarter holds split s's (m, l); every lane loads HD / 16 columns
+// (as 8-byte pieces: a partial row is HD + 2 floats) of every split up front; the maximum and the
+// denominator are 16-lane shuffle reductions in a fixed pattern and the numerator adds the splits in order.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_combine_quarter_kernel(const float* __restrict__ part,
+                                                                   bf16_t* __restrict__ O,
+                                                                   const int* __restrict__ seq_len,
+                                                                   const int* __restrict__ req_slot, int K, int Hq,
+                                                                   int max_ctx, int n_slots, int chunk, int nsplit,
+                                                                   int npairs) {
+  constexpr int CPT = HD / 16, RS = HD + 2, SMAX = 16;
+  const int ql = threadIdx.x & 15;
+  const int rid = blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (rid >= npairs) return;  // whole quarters leave together (the shuffles stay inside a quarter)
+  const int j = rid % K, h = (rid / K) % Hq, b = rid / (K * Hq);
+  bf16_t* out = O + ((size_t)(b * K + j) * Hq + h) * HD + CPT * ql;
+  const int L = seq_len[b], slot = req_slot[b];
+  if (slot < 0 || slot >= n_slots || L < 0 || L + K > max_ctx) {
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) out[e] = 0;
+    return;
+  }
+  const int ns = (L + K + chunk - 1) / chunk;  // 1 .. nsplit <= SMAX
+  const float* src = part + (size_t)rid * nsplit * RS;
+  const int sl = min(ql, ns - 1);
+  const float m_l = src[(size_t)sl * RS + HD], l_l = src[(size_t)sl * RS + HD + 1];
+  float o[SMAX][CPT];
+#pragma unroll
+  for (int t = 0; t < SMAX; ++t) {
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) o[t][e] = 0.f;
+    if (t < ns) {
+#pragma unroll
+      for (int e = 0; e < CPT; e += 2) {
+        const float2 v = *(const float2*)(src + (size_t)t * RS + CPT * ql + e);
+        o[t][e] = v.x;
+        o[t][e + 1] = v.y;
+      }
+    }
+  }
+  float M = ql < ns ? m_l : -1e30f;
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 16));
+  const float w_l = ql < ns ? __builtin_amdgcn_exp2f(m_l - M) : 0.f;  // m in log2 units
+  float den = w_l * l_l;
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) den += __shfl_xor(den, off, 16);
+  float num[CPT];
+#pragma unroll
+  for (int e = 0; e < CPT; ++e) num[e] = 0.f;
+#pragma unroll
+  for (int t = 0; t < SMAX; ++t) {
+    if (t < ns) {
+      const float wt = __shfl(w_l, t, 16);
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) num[e] += wt * o[t][e];
+    }
+  }
+  const float inv = 1.f / den;
+#pragma unroll
+  for (int e = 0; e < CPT; ++e) out[e] = f32_to_bf16(num[e] * inv);
+}
+
 // Same merge for rows with at most 32 splits (larger batches: many (row, head) pairs, few splits each):
 // one wave per pair, four pairs per workgroup. Lane s holds split s's (m, l); every lane loads its HD / 64
 // columns of every split up front; the numerator adds the splits in order.
@@ -590,6 +654,17 @@ hipError_t launch_attention_combine_bf16(const AttnPlan& p, const float* part, v
                                          const int* req_slot, int B, int K, int Hq, int Hkv, int hd, int max_ctx,
                                          int n_slots, hipStream_t st) {
   (void)Hkv;
+  if (p.nsplit <= 16) {
+    const int npairs = B * Hq * K;
+    dim3 grid((npairs + 15) / 16), block(256);
+    if (hd == 128)
+      hipLaunchKernelGGL(attn_combine_quarter_kernel<128>, grid, block, 0, st, part, (bf16_t*)O, seq_len, req_slot, K,
+                         Hq, max_ctx, n_slots, p.chunk, p.nsplit, npairs);
+    else
+      hipLaunchKernelGGL(attn_combine_quarter_kernel<64>, grid, block, 0, st, part, (bf16_t*)O, seq_len, req_slot, K,
+                         Hq, max_ctx, n_slots, p.chunk, p.nsplit, npairs);
+    return hipGetLastError();
+  }
   if (p.nsplit <= 32) {
     const int npairs = B * Hq * K;
     dim3 grid((npairs + 3) / 4), block(256);
