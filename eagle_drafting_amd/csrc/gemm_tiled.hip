@@ -252,7 +252,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
 // as in the 128 x 128 kernel (a weight column group leaves HBM once; its other row blocks hit the XCD's L2).
 // The product goes through LDS as 128 x 128 quarters, QP at a time, into the shared epilogue (each quarter's
 // run by four waves).
-template <int AM, int EP, int NWV>
+template <int AM, int EP, int NWV, int NS>
 __global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(GemmArgs g) {
   constexpr int BM = 128;
   constexpr int TW = 4 * NWV;               // 16-column tiles per workgroup (64 columns per wave)
@@ -260,7 +260,8 @@ __global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(GemmArgs g) {
   constexpr int AD = 8 / NWV;               // activation fragments each wave moves per k-step
   constexpr int SB = 8 * 1024;              // bytes per k-step activation buffer (8 fragments)
   constexpr int SMEM = QP * 128 * 128 * 4;  // the epilogue's 128 x 128 fp32 quarters
-  static_assert(3 * SB <= SMEM, "k-step buffers exceed the epilogue area");
+  // NS k-step buffers and weight register sets: loads run NS - 1 k-steps ahead
+  static_assert(NS * SB <= SMEM, "k-step buffers exceed the epilogue area");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   __shared__ float s_inv[BM];
 
@@ -336,19 +337,19 @@ __global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // k-step ks (its weights in wr, its activations in buffer ks % 3): this wave's loads of ks are done once
-  // only those of ks + 1 (four weight loads, then AD activation loads) may remain, and the barrier then
-  // covers every wave's activation load of ks and every wave's reads of ks - 1, whose buffer takes the
-  // activations of ks + 2. The loop runs a multiple of three k-steps with every load unconditional, so the
-  // compiler's own wait counts for the weight registers stay exact; k-steps past the last one multiply
-  // zero activations (their weight loads repeat the last k-step)
-  auto step = [&](int ks, int buf, const RegW& wr, RegW& wnext, int buf2) {
-    __builtin_amdgcn_s_waitcnt(0x0070 | (4 + AD));  // vmcnt(4 + AD) lgkmcnt(0)
+  // k-step ks (its weights in wr, its activations in buffer ks % NS): this wave's loads of ks are done once
+  // only those of the next NS - 2 k-steps (four weight loads, then AD activation loads, each) may remain,
+  // and the barrier then covers every wave's activation load of ks and every wave's reads of ks - 1, whose
+  // buffer takes the activations of ks + NS - 1. The loop runs a multiple of NS k-steps with every load
+  // unconditional, so the compiler's own wait counts for the weight registers stay exact; k-steps past the
+  // last one multiply zero activations (their weight loads repeat the last k-step)
+  auto step = [&](int ks, const RegW& wr, RegW& wnext) {
+    __builtin_amdgcn_s_waitcnt(0x0070 | ((NS - 2) * (4 + AD)));  // vmcnt((NS - 2)(4 + AD)) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    wload(wnext, min(ks + 2, Ks - 1));
-    adma(ks + 2, buf2);
-    const char* b = smem + buf * SB + a_lane;
+    wload(wnext, min(ks + NS - 1, Ks - 1));
+    adma(ks + NS - 1, (ks + NS - 1) % NS);
+    const char* b = smem + (ks % NS) * SB + a_lane;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       bf16x8_t af[4];
@@ -362,18 +363,18 @@ __global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(GemmArgs g) {
     }
   };
 
-  RegW w0, w1, w2;
-  wload(w0, 0);
-  adma(0, 0);
-  wload(w1, min(1, Ks - 1));
-  adma(1, 1);
-  const int nsteps = (Ks + 2) / 3 * 3;
-  for (int ks = 0; ks < nsteps; ks += 3) {
-    step(ks, 0, w0, w2, 2);
-    step(ks + 1, 1, w1, w0, 0);
-    step(ks + 2, 2, w2, w1, 1);
+  RegW w[NS];
+#pragma unroll
+  for (int q = 0; q < NS - 1; ++q) {
+    wload(w[q], min(q, Ks - 1));
+    adma(q, q);
   }
-  __builtin_amdgcn_s_waitcnt(0x0070);  // the loads of the two k-steps past the loop have landed
+  const int nsteps = (Ks + NS - 1) / NS * NS;
+  for (int ks = 0; ks < nsteps; ks += NS) {
+#pragma unroll
+    for (int q = 0; q < NS; ++q) step(ks + q, w[q], w[(q + NS - 1) % NS]);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070);  // the loads of the k-steps past the loop have landed
 
   if (AM == A_NORM && tid < 256) {
     // 1 / RMS per row from the producer's partial sums of squares (two threads per row)
@@ -1002,8 +1003,12 @@ hipError_t launch_gemm_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode, i
     // B 64 K 10 (90 k-steps, 408 tiles) 123 -> 105 us; Qwen B 128 K 7 (64 k-steps, 384 tiles) 76 -> 79 us,
     // so it stays on the 128 x 128 kernel)
     const int nwide = (p.Nt + 15) / 16;
-    hipLaunchKernelGGL((gemm_wide_kernel<A_NORM, EPI_SWIGLU, 4>), dim3(8 * ((nwide + 7) / 8) * p.mblocks), dim3(256), 0,
-                       st, a);
+    if (a.Ks % 3 != 0 && a.Ks % 4 == 0)
+      hipLaunchKernelGGL((gemm_wide_kernel<A_NORM, EPI_SWIGLU, 4, 4>), dim3(8 * ((nwide + 7) / 8) * p.mblocks), dim3(256),
+                         0, st, a);
+    else
+      hipLaunchKernelGGL((gemm_wide_kernel<A_NORM, EPI_SWIGLU, 4, 3>), dim3(8 * ((nwide + 7) / 8) * p.mblocks), dim3(256),
+                         0, st, a);
     return hipGetLastError();
   }
   if (p.tiled == 3 && !a.wscale && p.ksplit == 1 && a_mode == A_NORM && epi == EPI_ARGMAX) {
@@ -1012,12 +1017,16 @@ hipError_t launch_gemm_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode, i
     // GPT-OSS (d 2880) B 64 K 10 800 -> 811-829 us, so the longer reduction keeps 8
     if (a.Ks <= 64) {
       const int nwide = (p.Nt + 15) / 16;
-      hipLaunchKernelGGL((gemm_wide_kernel<A_NORM, EPI_ARGMAX, 4>), dim3(8 * ((nwide + 7) / 8) * p.mblocks), dim3(256), 0,
-                         st, a);
+      if (a.Ks % 3 != 0 && a.Ks % 4 == 0)
+        hipLaunchKernelGGL((gemm_wide_kernel<A_NORM, EPI_ARGMAX, 4, 4>), dim3(8 * ((nwide + 7) / 8) * p.mblocks),
+                           dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((gemm_wide_kernel<A_NORM, EPI_ARGMAX, 4, 3>), dim3(8 * ((nwide + 7) / 8) * p.mblocks),
+                           dim3(256), 0, st, a);
     } else {
       const int nwide = (p.Nt + 31) / 32;
-      hipLaunchKernelGGL((gemm_wide_kernel<A_NORM, EPI_ARGMAX, 8>), dim3(8 * ((nwide + 7) / 8) * p.mblocks), dim3(512), 0,
-                         st, a);
+      hipLaunchKernelGGL((gemm_wide_kernel<A_NORM, EPI_ARGMAX, 8, 3>), dim3(8 * ((nwide + 7) / 8) * p.mblocks),
+                         dim3(512), 0, st, a);
     }
     return hipGetLastError();
   }
