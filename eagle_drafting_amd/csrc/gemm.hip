@@ -143,7 +143,7 @@ hipError_t launch_pack_bf16(const void* W0, const void* W1, int N, int Kd, int m
   return hipGetLastError();
 }
 
-GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok, bool skinny_only) {
+GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok, bool skinny_only, bool fp8) {
   GemmPlan p;
   const int Ks = k_steps(Kd);
   p.Nt = n_tiles(N);
@@ -151,6 +151,7 @@ GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok, bool skinny_o
   p.ksplit = 1;
   p.kper = Ks;
   p.ki4 = 0;
+  p.burst = 0;
   if (ki4_ok && !argmax && M <= 4 && p.Nt < 256) {
     // up to 4 rows and a narrow output: 4-column tiles (4x the workgroups of 16-column ones, so every
     // compute unit streams weights); 4 or 8 waves split the 128-wide k-steps so that each loads its share
@@ -181,6 +182,16 @@ GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok, bool skinny_o
     p.NW = 4;
     p.mblocks = 1;
     p.ngroups = tg;
+    if (!argmax && !fp8 && M <= 32 && Ks > GEMM_BURST_KS) {
+      // up to 32 rows: K-split on the burst kernel, GEMM_BURST_KS k-steps per workgroup with every load
+      // issued at once; 256-column workgroups when 128-column ones would exceed one per compute unit
+      // (measured: B 8 K 3 474 -> 454 us and B 4 K 7 467 -> 452 us per draft step; with 64 or 96 rows the
+      // weight-stream kernel stays as fast or faster)
+      p.ksplit = (Ks + GEMM_BURST_KS - 1) / GEMM_BURST_KS;
+      p.kper = GEMM_BURST_KS;
+      p.burst = tg * p.ksplit > 256 ? 8 : 4;
+      return p;
+    }
     if (!argmax) {
       int ks = 1;
       while (tg * ks < 192 && Ks >= 2 * step * ks && 8LL * (2 * ks) * M <= 2LL * Kd) ks *= 2;

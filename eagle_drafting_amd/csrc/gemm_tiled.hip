@@ -910,6 +910,156 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 3 ? 3
   else tile_epilogue<EP, AM == A_NORM>(g, Cs, s_inv, 0, nt0, ng, 0, 32 * RB);
 }
 
+// Short K-split products of 17..32 rows: every load of the workgroup in flight at once.
+//
+// A workgroup covers all rows (RB blocks of 32), 32 NWV columns (wave w: columns 32 w .. 32 w + 31) and at
+// most GEMM_BURST_KS k-steps (K-split blockIdx.y). With so few k-steps per workgroup, the chunk pipeline of
+// the weight-stream kernel waits about one memory latency per chunk; here each wave first moves its share
+// of the activations of all k-steps straight into LDS (buffer loads that write LDS, one 1 KiB wave load per
+// 16 x 32 fragment, in the order the operand reads use; rows >= M and k-steps past the split read zeros),
+// then issues every weight fragment of its columns into registers (two 16-byte lane loads per k-step), and
+// only then waits: once for the activations (and a barrier), then per k-step for that k-step's weights,
+// which arrive in issue order while the earlier products run. Workgroups take their k-steps in rotated
+// orders, so that concurrent ones start at different offsets of the weight tiles. The fp32 product goes
+// through LDS (the layout of the 128 x 128 kernel, one 128-column quarter per four waves) into the partial
+// epilogue, and gemm_split_reduce_kernel adds the splits in a fixed order. (With 64 or 96 rows the products
+// that follow the loads take as long as the loads, and the weight-stream kernel, which overlaps them, is as
+// fast or faster; measured.)
+template <int AM, int RB, int NWV>
+__global__ __launch_bounds__(NWV * 64) void gemm_burst_kernel(GemmArgs g) {
+  constexpr int KS = GEMM_BURST_KS;            // k-steps per workgroup (at most)
+  constexpr int FR = 2 * RB;                   // 16-row activation fragments per k-step
+  constexpr int KW = KS / NWV;                 // k-steps whose activations each wave moves
+  constexpr int SMEM = KS * FR * 1024;         // activations of every k-step; later the product quarters
+  static_assert(KS % NWV == 0, "every wave moves the activations of the same number of k-steps");
+  static_assert(SMEM >= (NWV / 4) * 32 * RB * 128 * 4, "product quarters must fit in the activation area");
+  static_assert(2 * KS <= 63 - 0, "weight loads outstanding must fit the vector-memory counter");
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+  __shared__ float s_inv[32 * RB];
+
+  const int M = g.M, Ks = g.Ks, Nt = g.Nt;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nt0 = blockIdx.x * 2 * NWV;  // first 16-column tile
+  const int kb = blockIdx.y * g.kper;
+  const int ke = min(Ks, kb + g.kper);
+
+  // activations: wave w moves every fragment (rows 16 r .. + 15, r < FR) of k-steps w + NWV j (j < KW);
+  // fragment lane l holds row l % 16, k elements 8 (l / 16) .. + 7. The per-lane row offsets are resolved
+  // before the first load, so that no wait on them separates the loads.
+  uint32_t a_off[FR];
+#pragma unroll
+  for (int r = 0; r < FR; ++r) {
+    const int row = 16 * r + (lane & 15);
+    a_off[r] = row < M ? (uint32_t)((gemm_a_row(g, row) * g.lda + 8 * (lane >> 4)) * 2) : 0x7ffffff0u;
+  }
+  typedef int i32x4_t __attribute__((ext_vector_type(4)));
+  i32x4_t a_rsrc;
+  {
+    const uint64_t a = (uint64_t)(uintptr_t)g.A;
+    a_rsrc.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    a_rsrc.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+    a_rsrc.z = __builtin_amdgcn_readfirstlane(gemm_a_rows(g) * g.lda * 2);
+    a_rsrc.w = __builtin_amdgcn_readfirstlane(0x00020000);
+  }
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+#pragma unroll
+  for (int j = 0; j < KW; ++j) {
+    const int s = wave + NWV * j, ks = kb + s;
+#pragma unroll
+    for (int r = 0; r < FR; ++r) {
+      const uint32_t aoff = ks < ke && a_off[r] != 0x7ffffff0u ? a_off[r] + 64u * ks : 0x7ffffff0u;
+      const uint32_t m0a = lds_base + (uint32_t)((s * FR + r) * 1024);
+      asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(aoff), "s"(a_rsrc), "{m0}"(m0a) : "memory");
+    }
+  }
+
+  // weights: k-step s, k-half u of this wave's 32 columns (tiles nt0 + 2 w + fr_t); tiles past the last one
+  // and k-steps past the split read zeros
+  const int fr_t = (lane & 31) >> 4, fr_l = (lane & 15) + 16 * (lane >> 5);
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)g.Wp_raw, (short)0, (int)((uint32_t)Nt * (uint32_t)Ks * 1024u), 0x00020000);
+  const int w_lane = fr_t * Ks * 1024 + fr_l * 16;
+  const int w_tile = (nt0 + 2 * wave) * Ks * 1024;
+  bf16x8_t wr[KS][2];
+  const int rot = __builtin_amdgcn_readfirstlane((int)((blockIdx.x * 5 + blockIdx.y * 3) % KS));  // first k-step
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {
+    const int s = (j + rot) % KS;
+    const int so = kb + s < ke && nt0 + 2 * wave < Nt ? w_tile + (kb + s) * 1024 : 0x7ffffff0;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      wr[j][u] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_lane + 512 * u, so, 0));
+  }
+
+  f32x16_t acc[RB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+
+  // this wave's activation loads (issued before its weight loads) and the first k-step's weights have
+  // landed once at most the other 2 (KS - 1) weight loads are outstanding; the barrier then covers every
+  // wave's activation loads. Later k-steps wait (compiler-counted) for their own weights only.
+  constexpr int VM = 2 * (KS - 1);
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | 0x0070);  // vmcnt(VM) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  const int a_lane = (fr_t * 64 + fr_l) * 16;  // row block i: + 2048 i; k-half 1: + 512
+  const int nk = ke - kb;
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {
+    const int s = (j + rot) % KS;
+    if (s < nk) {
+      const char* b = smem + s * FR * 1024 + a_lane;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8_t af[RB];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) af[i] = *(const bf16x8_t*)(b + i * 2048 + u * 512);
+#pragma unroll
+        for (int i = 0; i < RB; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], wr[j][u], acc[i], 0, 0, 0);
+      }
+    }
+  }
+
+  if (AM == A_NORM && tid < 256) {
+    // 1 / RMS of each row from the producer's partial sums of squares (as in the weight-stream kernel)
+    constexpr int TPR = RB == 1 ? 8 : RB == 2 ? 4 : 2;
+    const int r = tid / TPR, h = tid % TPR;
+    float t = 0.f;
+    if (r < M) {
+      const float* src = g.ssq_in + (size_t)gemm_a_row(g, r) * g.nssq;
+      for (int i0 = h; i0 < g.nssq; i0 += 8 * TPR) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = i0 + u * TPR < g.nssq ? src[i0 + u * TPR] : 0.f;
+        t += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+      }
+    }
+    for (int off = TPR / 2; off > 0; off >>= 1) t += __shfl_xor(t, off, PE_WAVE);
+    if (h == 0 && r < 32 * RB) s_inv[r] = rsqrtf(t / (float)g.Kd + g.eps);
+  }
+  __syncthreads();  // every wave is done reading the activations
+  {
+    // quarter wave / 4 (columns 128 (wave / 4) ..), row R's columns XOR-swizzled by 32 ((R >> 2) & 1)
+    float* Cs = (float*)smem + (wave >> 2) * 32 * RB * 128;
+    const int c = lane & 31, hq = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = 32 * i + 8 * (e >> 2) + 4 * hq + (e & 3);
+        Cs[row * 128 + ((32 * (wave & 3) + c) ^ (hq << 5))] = acc[i][e];
+      }
+  }
+  __syncthreads();
+  const int q = tid >> 8;
+  if (nt0 + 8 * q < Nt)
+    tile_epilogue<EPI_PARTIAL, AM == A_NORM>(g, (const float*)smem + q * 32 * RB * 128, s_inv, 0, nt0 + 8 * q,
+                                             nt0 / 8 + q, 0, 32 * RB, tid & 255);
+}
+
 template <int RB, int CH, int NWB, int F8 = 0>
 static hipError_t launch_stream_rb(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st) {
   const dim3 block(256);
@@ -943,8 +1093,29 @@ static hipError_t launch_split_reduce(const GemmPlan& p, const GemmArgs& a, int 
   return hipGetLastError();
 }
 
+template <int RB>
+static hipError_t launch_burst_rb(const GemmPlan& p, const GemmArgs& a, int a_mode, hipStream_t st) {
+  const int nb = (p.Nt + 2 * p.burst - 1) / (2 * p.burst);
+  const dim3 grid(nb, p.ksplit);
+  if (p.burst == 8) {
+    if (a_mode == A_BF16) hipLaunchKernelGGL((gemm_burst_kernel<A_BF16, RB, 8>), grid, dim3(512), 0, st, a);
+    else hipLaunchKernelGGL((gemm_burst_kernel<A_NORM, RB, 8>), grid, dim3(512), 0, st, a);
+  } else {
+    if (a_mode == A_BF16) hipLaunchKernelGGL((gemm_burst_kernel<A_BF16, RB, 4>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((gemm_burst_kernel<A_NORM, RB, 4>), grid, dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
 static hipError_t launch_gemm_stream(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st) {
   if (a.M < 1 || a.M > 128) return hipErrorInvalidValue;
+  if (p.burst && !a.wscale) {
+    if (p.ksplit <= 1 || p.kper > GEMM_BURST_KS || !a.part || epi == EPI_ARGMAX) return hipErrorInvalidValue;
+    if (a.M > 32) return hipErrorInvalidValue;
+    const hipError_t e = launch_burst_rb<1>(p, a, a_mode, st);
+    if (e != hipSuccess) return e;
+    return launch_split_reduce(p, a, epi, st);
+  }
   if (a.wscale) {  // FP8 weights
     hipError_t e;
     if (a.M <= 32) e = launch_stream_rb<1, GEMM_STREAM_CH, 2, 1>(p, a, a_mode, epi, st);

@@ -30,6 +30,8 @@ inline int k_steps_ki4(int Kd) { return (Kd + 127) / 128; }
 // k-steps (of 32) per activation chunk of the 9..128-row weight-stream kernel; its K-split plans use
 // multiples of four chunks per split
 constexpr int GEMM_STREAM_CH = 4;
+// k-steps per workgroup of the burst kernel (K-split weight-stream products with every load issued at once)
+constexpr int GEMM_BURST_KS = 16;
 struct GemmPlan {
   int Nt;       // 16-column tiles
   int MT;       // 16-row MFMA tiles per workgroup (1, 2, 4 or 8)
@@ -42,11 +44,14 @@ struct GemmPlan {
   int ksplit;   // tiled: workgroups along the reduction dimension (1 = none); > 1 adds a reduce kernel
   int kper;     // tiled: k-steps (32 columns each) per split, a multiple of 4
   int ki4;      // skinny on PACK_KI4 weights: 4-column tiles (Nt counts them), 128-wide k-steps
+  int burst;    // weight-stream K-split on the burst kernel: its waves per workgroup (4 or 8), else 0
 };
 // ki4_ok: the weights are also packed as PACK_KI4 (the residual-stream producers: fc, O, down), which the
 // plan uses for up to 4 rows when the plain layout would leave most compute units idle
 // skinny_only: the small-batch kernel whatever M (FP8 weights; M <= 16)
-GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok = false, bool skinny_only = false);
+// fp8: FP8 weights (the burst kernel has no FP8 path)
+GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok = false, bool skinny_only = false,
+                   bool fp8 = false);
 // Partial sums of squares per row that a residual-stream producer with plan p writes (one per 16 columns
 // for the skinny kernel, one per 4 columns on PACK_KI4 weights, one per 128-column workgroup tile for the
 // tiled one); the consumer sums exactly that many.

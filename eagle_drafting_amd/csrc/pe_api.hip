@@ -143,7 +143,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // two, 69 with four)
 static GemmPlan plan_for(const pe_ctx* ctx, int M, int N, int Kd, bool argmax, bool ki4_ok = false) {
   if (!ctx->fp8) return plan_gemm(M, N, Kd, argmax, ki4_ok);
-  if (M > 16) return plan_gemm(M, N, Kd, argmax, false);  // weight-stream or tiled kernel
+  if (M > 16) return plan_gemm(M, N, Kd, argmax, false, false, true);  // weight-stream or tiled kernel
   GemmPlan p = plan_gemm(M, N, Kd, argmax, false, true);
   if (argmax && p.MT == 1) {
     p.NT = 4;
@@ -328,7 +328,7 @@ extern "C" pe_status pe_init(const pe_config* cfg, const pe_weights* w, const pe
       // (and layer 0's QKV over concatenated rows, 2d wide)
       const int shapes[6][2] = {{qkvd, d}, {d, qd}, {2 * F, d}, {d, F}, {d, 3 * d}, {qkvd, 2 * d}};
       for (int sh = 0; sh < (c.row_concat ? 6 : 5); ++sh) {
-        const GemmPlan ps = plan_gemm(M, shapes[sh][0], shapes[sh][1], false);
+        const GemmPlan ps = plan_for(ctx, M, shapes[sh][0], shapes[sh][1], false);
         if (ps.ksplit > 1) part_floats = std::max(part_floats, (size_t)ps.ksplit * M * shapes[sh][0]);
       }
     } else {
