@@ -23,6 +23,14 @@
 
 namespace pe {
 
+// cache policy of the K-split partial stores: device scope (sc1), so that they are written through to
+// the memory side during the product rather than left dirty in the L2 for the end-of-kernel write-back
+// before the reduce kernel (measured: Qwen B 8 K 11 581 -> 571 us per draft step, B 128 K 7 2087 ->
+// 2072 us, GPT-OSS B 64 K 10 2653 -> 2642 us; non-temporal stores were no faster than plain ones)
+#ifndef PE_PART_AUX
+#define PE_PART_AUX 16
+#endif
+
 // Product tile epilogue (defined below): Cs holds the 128 x 128 fp32 tile, column-swizzled; with SCALE,
 // s_inv[r] is row r's 1/RMS.
 template <int EP, bool SCALE>
@@ -223,8 +231,9 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
               F8 ? acc[i][j][e] * g.wscale[min(nt0 * 16 + 64 * wn + 32 * j + c, Nt * 16 - 1)] : acc[i][j][e];
         }
   }
-  if (AM == A_NORM) {
-    // 1 / RMS per row from the producer's partial sums of squares (two threads per row)
+  if (AM == A_NORM && !SPLIT) {
+    // 1 / RMS per row from the producer's partial sums of squares (two threads per row); a K-split
+    // product leaves the row scale to the reduce kernel
     const int r = tid >> 1, h = tid & 1;
     float t = 0.f;
     if (m0 + r < M) {
@@ -236,7 +245,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
   }
   __syncthreads();
 
-  if (SPLIT) tile_epilogue<EPI_PARTIAL, AM == A_NORM>(g, Cs, s_inv, m0, nt0, ng);
+  if (SPLIT) tile_epilogue<EPI_PARTIAL, false>(g, Cs, s_inv, m0, nt0, ng);
   else tile_epilogue<EP, AM == A_NORM>(g, Cs, s_inv, m0, nt0, ng);
 }
 
@@ -416,11 +425,14 @@ __global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(GemmArgs g) {
 }
 
 // the fixed-order sum of the K-split partials of rows [16 y, 16 y + 16) of one 128 x 128 tile
-// (y = blockIdx.y), then the epilogue of those rows
-template <int EP>
+// (y = blockIdx.y), then the epilogue of those rows. SCALE: the operand was normalised and the partials
+// are unscaled; each row's 1/RMS comes from the producer's partial sums of squares, whose loads are
+// issued before the partials' so that both wait on memory once.
+template <int EP, bool SCALE>
 __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs g) {
   constexpr int BN = 128, RS = 16;
   __shared__ __attribute__((aligned(16))) float Cl[RS * BN];
+  __shared__ float s_il[RS];
   const int M = g.M, N = g.N;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int ng = (slot / g.mblocks) * 8 + xcd;
@@ -429,6 +441,16 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs g) {
   const int rbeg = RS * blockIdx.y;
   if (m0 + rbeg >= M) return;
   float* Cs = Cl - rbeg * BN;  // tile-row indexing: rows rbeg .. rbeg + 15 live in Cl
+  // SCALE: 16 threads per row, partials h, h + 16, ... (eight per thread per pass)
+  const int sr = threadIdx.x >> 4, sh = threadIdx.x & 15;
+  float sv[8];
+  const float* ssrc = nullptr;
+  if (SCALE) {
+    const int m = m0 + rbeg + sr;
+    if (m < M) ssrc = g.ssq_in + (size_t)gemm_a_row(g, m) * g.nssq;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sv[u] = ssrc && sh + 16 * u < g.nssq ? ssrc[sh + 16 * u] : 0.f;
+  }
   const int nt0 = ng * 8;
   const int n0 = nt0 * 16;
   const bool vec = (N & 3) == 0;
@@ -467,8 +489,14 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs g) {
     }
     *(float4*)&Cs[rl * BN + (c0 ^ (((rl >> 2) & 1) << 5))] = acc;
   }
+  if (SCALE) {
+    float st = ((sv[0] + sv[1]) + (sv[2] + sv[3])) + ((sv[4] + sv[5]) + (sv[6] + sv[7]));
+    for (int i0 = sh + 128; ssrc && i0 < g.nssq; i0 += 16) st += ssrc[i0];  // more than 128 partials
+    for (int off = 8; off > 0; off >>= 1) st += __shfl_xor(st, off, PE_WAVE);
+    if (sh == 0) s_il[sr] = rsqrtf(st / (float)g.Kd + g.eps);
+  }
   __syncthreads();
-  tile_epilogue<EP, false>(g, Cs, nullptr, m0, nt0, ng, rbeg, rbeg + RS);
+  tile_epilogue<EP, SCALE>(g, Cs, s_il - rbeg, m0, nt0, ng, rbeg, rbeg + RS);
 }
 
 template <int EP, bool SCALE>
@@ -491,15 +519,22 @@ __device__ void tile_epilogue(const GemmArgs& g, const float* Cs, const float* s
   const int n0 = nt0 * 16;
 
   if (EP == EPI_PARTIAL) {
-    // raw (row-scaled) partial tile of K-split blockIdx.y
+    // raw partial tile of K-split blockIdx.y
     const int h = lane & 31;
     const int c0 = 4 * h, n = n0 + c0;
+    const size_t pbytes = (size_t)g.ksplit * M * N * 4;
+    const __amdgpu_buffer_rsrc_t p_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)g.part, (short)0, (int)(pbytes < 0x7fffffffu ? pbytes : 0x7fffffffu), 0x00020000);
     for (int rl = rbeg + 2 * wave + (lane >> 5); rl < rend; rl += 8) {
       const int m = m0 + rl;
       if (m >= M) continue;
       const float4 v = cload(rl, c0);
-      float* dst = g.part + ((size_t)blockIdx.y * M + m) * N + n;
-      if (n + 3 < N && (N & 3) == 0) {
+      const size_t idx = ((size_t)blockIdx.y * M + m) * N + n;
+      float* dst = g.part + idx;
+      if (n + 3 < N && (N & 3) == 0 && pbytes < 0x7fffffffu) {
+        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), p_rsrc, (int)(idx * 4), 0, PE_PART_AUX);
+      } else if (n + 3 < N && (N & 3) == 0) {
         *(float4*)dst = v;
       } else {
         if (n < N) dst[0] = v.x;
@@ -887,9 +922,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 3 ? 3
         Cs[row * BN + ((32 * wave + c) ^ (hq << 5))] = F8 ? acc[i][e] * wsc : acc[i][e];
       }
   }
-  if (AM == A_NORM) {
+  if (AM == A_NORM && !SPLIT) {
     // 1 / RMS of each row from the producer's partial sums of squares (up to 512 per row): TPR threads per
-    // row, eight loads in flight per thread, partials combined in a fixed order
+    // row, eight loads in flight per thread, partials combined in a fixed order (a K-split product leaves
+    // the row scale to the reduce kernel)
     constexpr int TPR = RB == 1 ? 8 : RB == 2 ? 4 : 2;
     const int r = tid / TPR, h = tid % TPR;
     float t = 0.f;
@@ -906,7 +942,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 3 ? 3
     if (h == 0 && r < 32 * RB) s_inv[r] = rsqrtf(t / (float)g.Kd + g.eps);
   }
   __syncthreads();
-  if (SPLIT) tile_epilogue<EPI_PARTIAL, AM == A_NORM>(g, Cs, s_inv, 0, nt0, ng, 0, 32 * RB);
+  if (SPLIT) tile_epilogue<EPI_PARTIAL, false>(g, Cs, s_inv, 0, nt0, ng, 0, 32 * RB);
   else tile_epilogue<EP, AM == A_NORM>(g, Cs, s_inv, 0, nt0, ng, 0, 32 * RB);
 }
 
@@ -922,7 +958,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 3 ? 3
 // which arrive in issue order while the earlier products run. Workgroups take their k-steps in rotated
 // orders, so that concurrent ones start at different offsets of the weight tiles. The fp32 product goes
 // through LDS (the layout of the 128 x 128 kernel, one 128-column quarter per four waves) into the partial
-// epilogue, and gemm_split_reduce_kernel adds the splits in a fixed order. (With 64 or 96 rows the products
+// epilogue, and gemm_split_reduce_kernel adds the splits in a fixed order and applies a normalised operand's
+// row scale. (With 64 or 96 rows the products
 // that follow the loads take as long as the loads, and the weight-stream kernel, which overlaps them, is as
 // fast or faster; measured.)
 template <int AM, int RB, int NWV>
@@ -935,7 +972,6 @@ __global__ __launch_bounds__(NWV * 64) void gemm_burst_kernel(GemmArgs g) {
   static_assert(SMEM >= (NWV / 4) * 32 * RB * 128 * 4, "product quarters must fit in the activation area");
   static_assert(2 * KS <= 63 - 0, "weight loads outstanding must fit the vector-memory counter");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
-  __shared__ float s_inv[32 * RB];
 
   const int M = g.M, Ks = g.Ks, Nt = g.Nt;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1023,23 +1059,6 @@ __global__ __launch_bounds__(NWV * 64) void gemm_burst_kernel(GemmArgs g) {
     }
   }
 
-  if (AM == A_NORM && tid < 256) {
-    // 1 / RMS of each row from the producer's partial sums of squares (as in the weight-stream kernel)
-    constexpr int TPR = RB == 1 ? 8 : RB == 2 ? 4 : 2;
-    const int r = tid / TPR, h = tid % TPR;
-    float t = 0.f;
-    if (r < M) {
-      const float* src = g.ssq_in + (size_t)gemm_a_row(g, r) * g.nssq;
-      for (int i0 = h; i0 < g.nssq; i0 += 8 * TPR) {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = i0 + u * TPR < g.nssq ? src[i0 + u * TPR] : 0.f;
-        t += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
-      }
-    }
-    for (int off = TPR / 2; off > 0; off >>= 1) t += __shfl_xor(t, off, PE_WAVE);
-    if (h == 0 && r < 32 * RB) s_inv[r] = rsqrtf(t / (float)g.Kd + g.eps);
-  }
   __syncthreads();  // every wave is done reading the activations
   {
     // quarter wave / 4 (columns 128 (wave / 4) ..), row R's columns XOR-swizzled by 32 ((R >> 2) & 1)
@@ -1056,8 +1075,8 @@ __global__ __launch_bounds__(NWV * 64) void gemm_burst_kernel(GemmArgs g) {
   __syncthreads();
   const int q = tid >> 8;
   if (nt0 + 8 * q < Nt)
-    tile_epilogue<EPI_PARTIAL, AM == A_NORM>(g, (const float*)smem + q * 32 * RB * 128, s_inv, 0, nt0 + 8 * q,
-                                             nt0 / 8 + q, 0, 32 * RB, tid & 255);
+    tile_epilogue<EPI_PARTIAL, false>(g, (const float*)smem + q * 32 * RB * 128, nullptr, 0, nt0 + 8 * q,
+                                      nt0 / 8 + q, 0, 32 * RB, tid & 255);
 }
 
 template <int RB, int CH, int NWB, int F8 = 0>
@@ -1082,13 +1101,14 @@ static hipError_t launch_stream_rb(const GemmPlan& p, const GemmArgs& a, int a_m
 }
 
 // the K-split partials of a weight-stream product: sum and epilogue
-static hipError_t launch_split_reduce(const GemmPlan& p, const GemmArgs& a, int epi, hipStream_t st) {
+static hipError_t launch_split_reduce(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st) {
   const dim3 rgrid(8 * ((p.ngroups + 7) / 8), 8);  // 16-row slices of each 128-column tile
   const dim3 block(256);
-  if (epi == EPI_RESID) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_RESID>), rgrid, block, 0, st, a);
-  else if (epi == EPI_ROWS) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_ROWS>), rgrid, block, 0, st, a);
-  else if (epi == EPI_QKV) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_QKV>), rgrid, block, 0, st, a);
-  else if (epi == EPI_SWIGLU) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_SWIGLU>), rgrid, block, 0, st, a);
+  if (epi == EPI_RESID && a_mode == A_BF16) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_RESID, false>), rgrid, block, 0, st, a);
+  else if (epi == EPI_ROWS && a_mode == A_BF16) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_ROWS, false>), rgrid, block, 0, st, a);
+  else if (epi == EPI_QKV && a_mode == A_NORM) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_QKV, true>), rgrid, block, 0, st, a);
+  else if (epi == EPI_QKV && a_mode == A_BF16) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_QKV, false>), rgrid, block, 0, st, a);
+  else if (epi == EPI_SWIGLU && a_mode == A_NORM) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_SWIGLU, true>), rgrid, block, 0, st, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -1114,7 +1134,7 @@ static hipError_t launch_gemm_stream(const GemmPlan& p, const GemmArgs& a, int a
     if (a.M > 32) return hipErrorInvalidValue;
     const hipError_t e = launch_burst_rb<1>(p, a, a_mode, st);
     if (e != hipSuccess) return e;
-    return launch_split_reduce(p, a, epi, st);
+    return launch_split_reduce(p, a, a_mode, epi, st);
   }
   if (a.wscale) {  // FP8 weights
     hipError_t e;
@@ -1123,7 +1143,7 @@ static hipError_t launch_gemm_stream(const GemmPlan& p, const GemmArgs& a, int a
     else if (a.M <= 96) e = launch_stream_rb<3, GEMM_STREAM_CH, 2, 1>(p, a, a_mode, epi, st);
     else e = launch_stream_rb<4, GEMM_STREAM_CH, 2, 1>(p, a, a_mode, epi, st);
     if (e != hipSuccess || p.ksplit <= 1) return e;
-    return launch_split_reduce(p, a, epi, st);
+    return launch_split_reduce(p, a, a_mode, epi, st);
   }
   // weights one chunk ahead (measured: two chunks ahead, with a six-step unroll, was no faster for the
   // 88-row vocabulary projection and slower for the four-chunk K-split products)
@@ -1133,7 +1153,7 @@ static hipError_t launch_gemm_stream(const GemmPlan& p, const GemmArgs& a, int a
   else if (a.M <= 96) e = launch_stream_rb<3, GEMM_STREAM_CH, 2>(p, a, a_mode, epi, st);
   else e = launch_stream_rb<4, GEMM_STREAM_CH, 2>(p, a, a_mode, epi, st);
   if (e != hipSuccess || p.ksplit <= 1) return e;
-  return launch_split_reduce(p, a, epi, st);
+  return launch_split_reduce(p, a, a_mode, epi, st);
 }
 
 template <int F8>
@@ -1148,10 +1168,11 @@ static hipError_t launch_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode,
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 rgrid(tiles, 8);  // 16-row slices of each tile
-    if (epi == EPI_RESID) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_RESID>), rgrid, block, 0, st, a);
-    else if (epi == EPI_ROWS) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_ROWS>), rgrid, block, 0, st, a);
-    else if (epi == EPI_QKV) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_QKV>), rgrid, block, 0, st, a);
-    else if (epi == EPI_SWIGLU) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_SWIGLU>), rgrid, block, 0, st, a);
+    if (epi == EPI_RESID && a_mode == A_BF16) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_RESID, false>), rgrid, block, 0, st, a);
+    else if (epi == EPI_ROWS && a_mode == A_BF16) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_ROWS, false>), rgrid, block, 0, st, a);
+    else if (epi == EPI_QKV && a_mode == A_NORM) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_QKV, true>), rgrid, block, 0, st, a);
+    else if (epi == EPI_QKV && a_mode == A_BF16) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_QKV, false>), rgrid, block, 0, st, a);
+    else if (epi == EPI_SWIGLU && a_mode == A_NORM) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_SWIGLU, true>), rgrid, block, 0, st, a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
   }
