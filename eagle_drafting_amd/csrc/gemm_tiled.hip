@@ -595,9 +595,15 @@ __device__ void tile_epilogue(const GemmArgs& g, const float* Cs, const float* s
               }
             }
             bf16_t* xg = g.XGout + (size_t)m * N;
+            if (full) {
+              uint2 w;
+              w.x = (uint32_t)f32_to_bf16(x[0] * gn[0]) | ((uint32_t)f32_to_bf16(x[1] * gn[1]) << 16);
+              w.y = (uint32_t)f32_to_bf16(x[2] * gn[2]) | ((uint32_t)f32_to_bf16(x[3] * gn[3]) << 16);
+              *(uint2*)(xg + n) = w;
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              if (n + e < N) xg[n + e] = f32_to_bf16(x[e] * gn[e]);
+              if (!full && n + e < N) xg[n + e] = f32_to_bf16(x[e] * gn[e]);
               sq0 += x[e] * x[e];
             }
           } else {
@@ -625,6 +631,15 @@ __device__ void tile_epilogue(const GemmArgs& g, const float* Cs, const float* s
             auto put = [&](int lr, const float* src, const float* srce) {  // layer row b Kr + lr
               float* xr = g.Xout + (size_t)(b * Kr + lr) * N;
               bf16_t* xg = g.XGout + (size_t)(b * Kr + lr) * N;
+              if (n + 3 < N && (N & 3) == 0) {  // whole 4-column pieces: 16- and 8-byte stores
+                *(float4*)(xr + n) = make_float4(src[0], src[1], src[2], src[3]);
+                uint2 w;
+                w.x = (uint32_t)f32_to_bf16(src[0] * gn[0]) | ((uint32_t)f32_to_bf16(src[1] * gn[1]) << 16);
+                w.y = (uint32_t)f32_to_bf16(src[2] * gn[2]) | ((uint32_t)f32_to_bf16(src[3] * gn[3]) << 16);
+                *(uint2*)(xg + n) = w;
+                if (g.Xe) *(float4*)(g.Xe + (size_t)(b * Kr + lr) * N + n) = make_float4(srce[0], srce[1], srce[2], srce[3]);
+                return;
+              }
 #pragma unroll
               for (int e = 0; e < 4; ++e)
                 if (n + e < N) {
