@@ -7,6 +7,13 @@
 
 namespace pe {
 
+// 16 bytes of a row that is read once (target or draft logits): non-temporal load
+template <typename T>
+__device__ __forceinline__ uint4 nt_load16(const T* p) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4_t*)p));
+}
+
 int plan_argmax_chunks(int rows, int V) {
   // ~1024 workgroups, each scanning at least 2048 entries of its row
   int c = (1024 + rows - 1) / rows;
@@ -34,7 +41,7 @@ __global__ __launch_bounds__(256) void argmax_rows_kernel(const T* __restrict__ 
   for (; i + 3 * 256 * VEC + VEC <= end; i += 4 * 256 * VEC) {
     union { uint4 u; T e[VEC]; } ld[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ld[q].u = *(const uint4*)(x + i + q * 256 * VEC);
+    for (int q = 0; q < 4; ++q) ld[q].u = nt_load16(x + i + q * 256 * VEC);
 #pragma unroll
     for (int q = 0; q < 4; ++q)  // increasing index order, so a strict > keeps the first maximum
 #pragma unroll
@@ -46,7 +53,7 @@ __global__ __launch_bounds__(256) void argmax_rows_kernel(const T* __restrict__ 
   for (; i < end; i += 256 * VEC) {
     if (i + VEC <= end) {
       union { uint4 u; T e[VEC]; } ld;
-      ld.u = *(const uint4*)(x + i);
+      ld.u = nt_load16(x + i);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         const float v = to_f32<T>(ld.e[e]);
@@ -311,7 +318,7 @@ __global__ __launch_bounds__(256) void softmax_stats_kernel(const T* __restrict_
   for (; i + 3 * STEP + VEC <= end; i += 4 * STEP) {
     union { uint4 u; T e[VEC]; } ld[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ld[q].u = *(const uint4*)(x + i + q * STEP);
+    for (int q = 0; q < 4; ++q) ld[q].u = nt_load16(x + i + q * STEP);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -320,7 +327,7 @@ __global__ __launch_bounds__(256) void softmax_stats_kernel(const T* __restrict_
   for (; i < end; i += STEP) {
     if (i + VEC <= end) {
       union { uint4 u; T e[VEC]; } ld;
-      ld.u = *(const uint4*)(x + i);
+      ld.u = nt_load16(x + i);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) add(to_f32<T>(ld.e[e]));
     } else {

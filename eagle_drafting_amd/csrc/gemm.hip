@@ -343,13 +343,17 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
         a[kk][mt] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0));
       }
     }
+    // weights are read once per launch: non-temporal loads (measured on a streaming read: 7.0 TB/s against
+    // 6.3 TB/s with plain loads)
+    typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
     if (F8) {
 #pragma unroll
       for (int kk = 0; kk < KC; kk += 2)
-        b8[kk / 2] = wsrc8[(size_t)(min(c0 + min(kk, nk - 1), Ks - 1) >> 1) * 64];
+        b8[kk / 2] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+            (const u32x4_t*)(wsrc8 + (size_t)(min(c0 + min(kk, nk - 1), Ks - 1) >> 1) * 64)));
     } else {
 #pragma unroll
-      for (int kk = 0; kk < KC; ++kk) b[kk] = wsrc[(size_t)min(c0 + min(kk, nk - 1), Ks - 1) * 64];
+      for (int kk = 0; kk < KC; ++kk) b[kk] = __builtin_nontemporal_load(wsrc + (size_t)min(c0 + min(kk, nk - 1), Ks - 1) * 64);
     }
   };
   auto mma_round = [&](int c0) {
