@@ -288,7 +288,8 @@ __device__ __forceinline__ void sm_merge(float& m, float& s, float m2, float s2)
 
 // (max, sum of exp(x - max)) of x = logit / temperature over one chunk of one row. WPC waves per chunk: 1 (four
 // chunks per workgroup, no block barrier; many rows) or 4 (one chunk per workgroup; few rows, so more waves
-// share the scan). Each lane keeps its running pair over its elements in order; lanes merge by xor-shuffles
+// share the scan). Each lane keeps its running pair over its elements in order (32 at a time: the batch
+// maximum, one rescale, then the batch's exponentials); lanes merge by xor-shuffles
 // in a fixed pattern, then (WPC = 4) the four waves in order.
 template <typename T, int WPC>
 __global__ __launch_bounds__(256) void softmax_stats_kernel(const T* __restrict__ X, int V, int chunk, int nchunks,
@@ -319,10 +320,23 @@ __global__ __launch_bounds__(256) void softmax_stats_kernel(const T* __restrict_
     union { uint4 u; T e[VEC]; } ld[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) ld[q].u = nt_load16(x + i + q * STEP);
+    // the batch's maximum first: one rescale per batch, then a plain sum of exponentials (measured: sampled
+    // verify at GPT-OSS B 64 K 10 108 -> 92 us, Qwen B 128 K 7 112 -> 94 us, against a running
+    // maximum per element with its branch)
+    float v[4 * VEC], bm = -INFINITY;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) add(to_f32<T>(ld[q].e[e]));
+      for (int e = 0; e < VEC; ++e) {
+        v[q * VEC + e] = to_f32<T>(ld[q].e[e]) * inv_temp;
+        bm = fmaxf(bm, v[q * VEC + e]);
+      }
+    if (bm > m) {
+      s *= __expf(m - bm);
+      m = bm;
+    }
+#pragma unroll
+    for (int k = 0; k < 4 * VEC; ++k) s += __expf(v[k] - m);
   }
   for (; i < end; i += STEP) {
     if (i + VEC <= end) {

@@ -10,9 +10,9 @@ bounds, is derived from how the kernels compute (unit roundoff 2^-24):
     at most |x / tau - m| ulp more and the hardware exp2 two more. Summed over a row, the |x / tau - m|
     parts weigh sum_t w_t |log w_t| <= 2 S ln V (w_t <= 1, S = sum w_t), so a total S or a weight carries
     at most (A + 4 ln V + 2) ulp from the exponentials;
-  * each lane's running sum over its ~32 elements of a 2048-token chunk (an add, or a rescale with a
-    multiply and an add: three roundings per element), then at most 20 pairwise merges (shuffles, waves,
-    chunks; three roundings each): 3 (32 + 20) ulp;
+  * each lane's running sum over its ~32 elements of a 2048-token chunk (an add per element and, per
+    batch of 32 elements, a rescale by one multiply: at most three roundings per element), then at most
+    20 pairwise merges (shuffles, waves, chunks; three roundings each): 3 (32 + 20) ulp;
   * the acceptance test u < ed / S divides two such quantities: p carries at most twice the above;
   * a draw compares its threshold v (S - ed) with a running total over up to nchunks chunk totals (one
     rounding each) and a 256-thread block scan inside the chunk (~40 roundings).
