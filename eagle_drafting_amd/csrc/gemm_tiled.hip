@@ -430,13 +430,15 @@ __global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(GemmArgs g) {
   }
 }
 
-// the fixed-order sum of the K-split partials of rows [16 y, 16 y + 16) of one 128 x 128 tile
+// the fixed-order sum of the K-split partials of rows [RS y, RS y + RS) of one 128 x 128 tile
 // (y = blockIdx.y), then the epilogue of those rows. SCALE: the operand was normalised and the partials
 // are unscaled; each row's 1/RMS comes from the producer's partial sums of squares, whose loads are
-// issued before the partials' so that both wait on memory once.
-template <int EP, bool SCALE>
+// issued before the partials' so that both wait on memory once. RS = 4 for the row build, whose epilogue
+// writes every request's placeholder rows too (four times the workgroups for the same rows).
+template <int EP, bool SCALE, int RS = 16>
 __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs g) {
-  constexpr int BN = 128, RS = 16;
+  static_assert(!SCALE || RS == 16, "the row scale takes 16 threads per row of a 16-row slice");
+  constexpr int BN = 128;
   __shared__ __attribute__((aligned(16))) float Cl[RS * BN];
   __shared__ float s_il[RS];
   const int M = g.M, N = g.N;
@@ -446,7 +448,7 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs g) {
   const int m0 = (slot % g.mblocks) * 128;
   const int rbeg = RS * blockIdx.y;
   if (m0 + rbeg >= M) return;
-  float* Cs = Cl - rbeg * BN;  // tile-row indexing: rows rbeg .. rbeg + 15 live in Cl
+  float* Cs = Cl - rbeg * BN;  // tile-row indexing: rows rbeg .. rbeg + RS - 1 live in Cl
   // SCALE: 16 threads per row, partials h, h + 16, ... (eight per thread per pass)
   const int sr = threadIdx.x >> 4, sh = threadIdx.x & 15;
   float sv[8];
@@ -1125,8 +1127,11 @@ static hipError_t launch_stream_rb(const GemmPlan& p, const GemmArgs& a, int a_m
 static hipError_t launch_split_reduce(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st) {
   const dim3 rgrid(8 * ((p.ngroups + 7) / 8), 8);  // 16-row slices of each 128-column tile
   const dim3 block(256);
+  if (epi == EPI_ROWS && a_mode == A_BF16) {  // 4-row slices
+    hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_ROWS, false, 4>), dim3(rgrid.x, 32), block, 0, st, a);
+    return hipGetLastError();
+  }
   if (epi == EPI_RESID && a_mode == A_BF16) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_RESID, false>), rgrid, block, 0, st, a);
-  else if (epi == EPI_ROWS && a_mode == A_BF16) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_ROWS, false>), rgrid, block, 0, st, a);
   else if (epi == EPI_QKV && a_mode == A_NORM) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_QKV, true>), rgrid, block, 0, st, a);
   else if (epi == EPI_QKV && a_mode == A_BF16) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_QKV, false>), rgrid, block, 0, st, a);
   else if (epi == EPI_SWIGLU && a_mode == A_NORM) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_SWIGLU, true>), rgrid, block, 0, st, a);
@@ -1190,7 +1195,8 @@ static hipError_t launch_tiled(const GemmPlan& p, const GemmArgs& a, int a_mode,
     if (e != hipSuccess) return e;
     const dim3 rgrid(tiles, 8);  // 16-row slices of each tile
     if (epi == EPI_RESID && a_mode == A_BF16) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_RESID, false>), rgrid, block, 0, st, a);
-    else if (epi == EPI_ROWS && a_mode == A_BF16) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_ROWS, false>), rgrid, block, 0, st, a);
+    else if (epi == EPI_ROWS && a_mode == A_BF16)  // 4-row slices
+      hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_ROWS, false, 4>), dim3(tiles, 32), block, 0, st, a);
     else if (epi == EPI_QKV && a_mode == A_NORM) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_QKV, true>), rgrid, block, 0, st, a);
     else if (epi == EPI_QKV && a_mode == A_BF16) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_QKV, false>), rgrid, block, 0, st, a);
     else if (epi == EPI_SWIGLU && a_mode == A_NORM) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_SWIGLU, true>), rgrid, block, 0, st, a);
