@@ -433,12 +433,13 @@ __global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(GemmArgs g) {
 // the fixed-order sum of the K-split partials of rows [RS y, RS y + RS) of one 128 x 128 tile
 // (y = blockIdx.y), then the epilogue of those rows. SCALE: the operand was normalised and the partials
 // are unscaled; each row's 1/RMS comes from the producer's partial sums of squares, whose loads are
-// issued before the partials' so that both wait on memory once. RS = 4 for the row build, whose epilogue
-// writes every request's placeholder rows too (four times the workgroups for the same rows).
+// issued before the partials' so that both wait on memory once (256 / RS threads per row). RS = 4 for the
+// products of at most 128 rows and for the row build (whose epilogue writes every request's placeholder
+// rows too): four times the workgroups for the same rows.
 template <int EP, bool SCALE, int RS = 16>
 __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs g) {
-  static_assert(!SCALE || RS == 16, "the row scale takes 16 threads per row of a 16-row slice");
   constexpr int BN = 128;
+  constexpr int TPR = 256 / RS;  // threads per row of the row scale
   __shared__ __attribute__((aligned(16))) float Cl[RS * BN];
   __shared__ float s_il[RS];
   const int M = g.M, N = g.N;
@@ -449,15 +450,15 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs g) {
   const int rbeg = RS * blockIdx.y;
   if (m0 + rbeg >= M) return;
   float* Cs = Cl - rbeg * BN;  // tile-row indexing: rows rbeg .. rbeg + RS - 1 live in Cl
-  // SCALE: 16 threads per row, partials h, h + 16, ... (eight per thread per pass)
-  const int sr = threadIdx.x >> 4, sh = threadIdx.x & 15;
+  // SCALE: TPR threads per row, partials h, h + TPR, ... (eight per thread per pass)
+  const int sr = threadIdx.x / TPR, sh = threadIdx.x % TPR;
   float sv[8];
   const float* ssrc = nullptr;
   if (SCALE) {
     const int m = m0 + rbeg + sr;
     if (m < M) ssrc = g.ssq_in + (size_t)gemm_a_row(g, m) * g.nssq;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) sv[u] = ssrc && sh + 16 * u < g.nssq ? ssrc[sh + 16 * u] : 0.f;
+    for (int u = 0; u < 8; ++u) sv[u] = ssrc && sh + TPR * u < g.nssq ? ssrc[sh + TPR * u] : 0.f;
   }
   const int nt0 = ng * 8;
   const int n0 = nt0 * 16;
@@ -499,8 +500,8 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs g) {
   }
   if (SCALE) {
     float st = ((sv[0] + sv[1]) + (sv[2] + sv[3])) + ((sv[4] + sv[5]) + (sv[6] + sv[7]));
-    for (int i0 = sh + 128; ssrc && i0 < g.nssq; i0 += 16) st += ssrc[i0];  // more than 128 partials
-    for (int off = 8; off > 0; off >>= 1) st += __shfl_xor(st, off, PE_WAVE);
+    for (int i0 = sh + 8 * TPR; ssrc && i0 < g.nssq; i0 += TPR) st += ssrc[i0];  // more than 8 TPR partials
+    for (int off = TPR / 2; off > 0; off >>= 1) st += __shfl_xor(st, off, PE_WAVE);
     if (sh == 0) s_il[sr] = rsqrtf(st / (float)g.Kd + g.eps);
   }
   __syncthreads();
@@ -1124,17 +1125,17 @@ static hipError_t launch_stream_rb(const GemmPlan& p, const GemmArgs& a, int a_m
 }
 
 // the K-split partials of a weight-stream product: sum and epilogue
+// (one 128-row block of at most 128 rows: 4-row slices, four times the workgroups of 16-row ones; measured:
+// Qwen B8 K11 552 -> 536 us per draft step, B8 K3 421 -> 401 us, B4 K11 490 -> 463 us; on the 128 x 128
+// kernel's products, with several row blocks, 4-row slices changed nothing)
 static hipError_t launch_split_reduce(const GemmPlan& p, const GemmArgs& a, int a_mode, int epi, hipStream_t st) {
-  const dim3 rgrid(8 * ((p.ngroups + 7) / 8), 8);  // 16-row slices of each 128-column tile
+  const dim3 rgrid(8 * ((p.ngroups + 7) / 8), 32);  // 4-row slices of each 128-column tile
   const dim3 block(256);
-  if (epi == EPI_ROWS && a_mode == A_BF16) {  // 4-row slices
-    hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_ROWS, false, 4>), dim3(rgrid.x, 32), block, 0, st, a);
-    return hipGetLastError();
-  }
-  if (epi == EPI_RESID && a_mode == A_BF16) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_RESID, false>), rgrid, block, 0, st, a);
-  else if (epi == EPI_QKV && a_mode == A_NORM) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_QKV, true>), rgrid, block, 0, st, a);
-  else if (epi == EPI_QKV && a_mode == A_BF16) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_QKV, false>), rgrid, block, 0, st, a);
-  else if (epi == EPI_SWIGLU && a_mode == A_NORM) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_SWIGLU, true>), rgrid, block, 0, st, a);
+  if (epi == EPI_RESID && a_mode == A_BF16) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_RESID, false, 4>), rgrid, block, 0, st, a);
+  else if (epi == EPI_ROWS && a_mode == A_BF16) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_ROWS, false, 4>), rgrid, block, 0, st, a);
+  else if (epi == EPI_QKV && a_mode == A_NORM) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_QKV, true, 4>), rgrid, block, 0, st, a);
+  else if (epi == EPI_QKV && a_mode == A_BF16) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_QKV, false, 4>), rgrid, block, 0, st, a);
+  else if (epi == EPI_SWIGLU && a_mode == A_NORM) hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI_SWIGLU, true, 4>), rgrid, block, 0, st, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
