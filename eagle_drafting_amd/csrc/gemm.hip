@@ -170,10 +170,11 @@ GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok, bool skinny_o
   // from 17; the stream kernel addresses the packed weights with 32-bit buffer offsets)
   if (!skinny_only && M > (argmax ? 8 : 16) && M <= 128 && (long long)p.Nt * Ks * 1024 < 0x7ff00000LL) {
     // up to 128 rows: the weight-stream kernel (all rows and 128 columns per workgroup, activations staged
-    // once per chunk). Narrow or short products split the reduction over workgroups until there are about
-    // 192 of them, each with at least four chunks, and while the fp32 partials stay within the weight bytes
-    // (2 ksplit M N 4 <= N Kd 2); the split reduce kernel then runs the epilogue. (The partials go through
-    // HBM, so fewer splits win: at 96 rows a 192-workgroup target beats 384 by 2-3 % per step.)
+    // once per chunk). Narrow or short products split the reduction into whole 16-k-step (four-chunk)
+    // pieces, as many as give about 192 workgroups; the split reduce kernel then runs the epilogue.
+    // (Measured at 96 rows: two-chunk pieces for 256-384 workgroups were 2-3 % slower per step; taking the
+    // split count directly instead of doubling it while the fp32 partials stayed within the weight bytes
+    // runs down in 12 pieces instead of 6: Qwen B8 K11 540 -> 531 us, B8 K7 490 -> 481 us per draft step.)
     const int tg = (p.Nt + 7) / 8;
     constexpr int step = 4 * GEMM_STREAM_CH;
     p.tiled = 2;
@@ -193,10 +194,9 @@ GemmPlan plan_gemm(int M, int N, int Kd, bool argmax, bool ki4_ok, bool skinny_o
       return p;
     }
     if (!argmax) {
-      int ks = 1;
-      while (tg * ks < 192 && Ks >= 2 * step * ks && 8LL * (2 * ks) * M <= 2LL * Kd) ks *= 2;
-      if (ks > 1) {
-        p.kper = (((Ks + ks - 1) / ks) + step - 1) / step * step;
+      const int want = (192 + tg - 1) / tg;  // splits for about 192 workgroups
+      if (want > 1 && Ks >= 2 * step) {
+        p.kper = (((Ks + want - 1) / want) + step - 1) / step * step;  // whole 16-k-step pieces
         p.ksplit = (Ks + p.kper - 1) / p.kper;
         if (p.ksplit <= 1) p.kper = Ks;
       }
