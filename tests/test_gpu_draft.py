@@ -179,14 +179,16 @@ def test_stream_kernel_row_counts_parity(B, K):
         g.close()
 
 
-@pytest.mark.parametrize("K", [3, 4, 7, 10, 15], ids=lambda v: f"K{v}")
+@pytest.mark.parametrize("K", [3, 4, 7, 8, 10, 11, 15], ids=lambda v: f"K{v}")
 def test_gptoss_attention_row_tiles(K):
     """GPT-OSS-shaped drafter (head dimension 64, 8 query heads per kv head). Attention runs the K draft rows
-    plus the trailing placeholder row, so a kv head has 8 (K + 1) query rows: K 3 / 4 / 7 / 10 / 15 give
-    32 / 40 / 64 / 88 / 128 rows, i.e. 2 / 3 / 4 / 6 / 8 16-row tiles on 4- or 8-wave workgroups (128 is the
-    most the configuration allows). The layer rows, 3 (K + 1), reach the small-batch kernel (K 3, 4), the
-    burst kernel (K 7: 24 rows, whose reductions of 90 and 270 k-steps end in a short 16-k-step piece)
-    and the weight-stream kernel (K 10, 15). Contexts 0, 37 and 700: a request with only its own rows,
+    plus the trailing placeholder row, so a kv head has 8 (K + 1) query rows: K 3 / 4 / 7 / 8 / 10 / 11 / 15
+    give 32 / 40 / 64 / 72 / 88 / 96 / 128 rows, i.e. 2 / 3 / 4 / 5 / 6 / 6 / 8 16-row tiles on 4- or
+    8-wave workgroups (5 and 6 tiles leave waves without a row tile; 96 rows fill the last tile, 72 and 88
+    do not; 128 is the most the configuration allows). The layer rows,
+    3 (K + 1), reach the small-batch kernel (K 3, 4), the burst kernel (K 7, 8: 24 and 27 rows, whose
+    reductions of 90 and 270 k-steps end in a short 16-k-step piece) and the weight-stream kernel (K 10,
+    11, 15). Contexts 0, 37 and 700: a request with only its own rows,
     one whose keys end inside the first 128-key round, and one spread over several key splits with a
     ragged last round. Every request against the oracle, K/V rows included."""
     w = Workload(f"gptoss20b-bf16-B3-K{K}-rowtiles", GPT_OSS_20B, 3, K, (0, 700), 0.7, 7800 + K)
