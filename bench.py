@@ -591,7 +591,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--churn-steps", type=int, default=16)
-    ap.add_argument("--variants", action="store_true", help="also time catch-up, concatenated-row and FP8 steps")
+    ap.add_argument("--variants", action="store_true",
+                    help="also time catch-up, concatenated-row and FP8 steps (headline workload and the B = 1 target)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="start with the 1 GiB device copy (the known-size kernel that scales HBM counters)")
     args = ap.parse_args()
@@ -655,6 +656,9 @@ def main():
                     for k, v in rl.items()},
         "device_flags": pe.pe_device_flags(r.ctx),
     }
+    if args.variants:
+        note("variants on the headline workload")
+        result["variants"] = variants(r, max(10, args.steps // 2))
     r.close()
     del r
 
