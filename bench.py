@@ -480,8 +480,9 @@ def oracle_step(w, W64, state, T_host, req, K):
 
 def cpu_baseline(runs_cfg, budget_s):
     """The oracle as it stands (float64 NumPy, all BLAS threads), timed on this host: the median of three
-    draft + verify + compaction runs over a sample of the headline workload's requests; plus the same on the
-    Qwen-shaped workloads with one thread. Also the argmax rule's strict-match and exempt counts of the
+    draft + verify + compaction runs over a sample of the headline workload's requests; plus the same with one
+    thread on the tiny workload and the Qwen-shaped B 1 K 3 (median of five) and B 8 K 11 (one request,
+    median of three) workloads. Also the argmax rule's strict-match and exempt counts of the
     GPU's drafts on the sampled requests."""
     from synth.inputs import make_weights, to_f64
     info = host_info()
@@ -532,9 +533,10 @@ def cpu_baseline(runs_cfg, budget_s):
             stc = make_state(wc)
             Tc = plant_target_logits(wc, random_draft(wc), stc["alpha"])
             rq = sub or list(range(wc.B))
+            nrun = 3 if sub else 5  # the two single-request workloads: median of five runs
             with threadpool_limits(limits=1):
-                ts = [oracle_step(wc, Wc, stc, Tc, rq, wc.K)[0] for _ in range(3)]
-            one[name] = {"requests": len(rq), "median_s": float(np.median(ts)),
+                ts = [oracle_step(wc, Wc, stc, Tc, rq, wc.K)[0] for _ in range(nrun)]
+            one[name] = {"requests": len(rq), "median_s": float(np.median(ts)), "runs": nrun,
                          "draft_tokens_per_s": len(rq) * wc.K / float(np.median(ts)), "threads": 1}
         del Wq
     res["one_thread"] = one
