@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void argmax_rows_kernel(const T* __restrict__ 
       }
     }
   }
-  am_wave_reduce(best, bi, 64);
+  am_group_reduce<64>(best, bi);
   if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = best; si[threadIdx.x >> 6] = bi; }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -113,7 +113,7 @@ __device__ __forceinline__ int am_row_reduce(const float* __restrict__ pv, const
     const int k = pi[c];
     if (am_better(v, k, b, i)) { b = v; i = k; }
   }
-  am_wave_reduce(b, i, 64);
+  am_group_reduce<64>(b, i);
   return i;
 }
 
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(1024) void argmax_final_kernel(const float* __restr
     if (am_better(x[u], k[u], b, i)) { b = x[u]; i = k[u]; }
   for (int c = threadIdx.x + U * 1024; c < nchunks; c += 1024)
     if (am_better(v[c], ix[c], b, i)) { b = v[c]; i = ix[c]; }
-  am_wave_reduce(b, i, 64);
+  am_group_reduce<64>(b, i);
   if (lane == 0) { sv[wave] = b; si[wave] = i; }
   __syncthreads();
   if (threadIdx.x == 0) {

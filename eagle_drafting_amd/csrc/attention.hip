@@ -551,12 +551,10 @@ __global__ __launch_bounds__(256) void attn_combine_quarter_kernel(const float* 
     }
   }
   float M = ql < ns ? m_l : -1e30f;
-#pragma unroll
-  for (int off = 8; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 16));
+  M = group_max<16>(M);
   const float w_l = ql < ns ? __builtin_amdgcn_exp2f(m_l - M) : 0.f;  // m in log2 units
   float den = w_l * l_l;
-#pragma unroll
-  for (int off = 8; off > 0; off >>= 1) den += __shfl_xor(den, off, 16);
+  den = group_sum<16>(den);
   float num[CPT];
 #pragma unroll
   for (int e = 0; e < CPT; ++e) num[e] = 0.f;

@@ -55,11 +55,66 @@ __device__ __forceinline__ bool am_better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
-__device__ __forceinline__ void am_wave_reduce(float& v, int& i, int width) {
-  for (int off = width / 2; off > 0; off >>= 1) {
-    float ov = __shfl_xor(v, off, PE_WAVE);
-    int oi = __shfl_xor(i, off, PE_WAVE);
+// Reductions over aligned groups of W lanes (W = 2 .. 64) with register-to-register lane moves instead of
+// LDS permutes (whose latency a chain of them pays in full): DPP quad permutations (lane ^ 1, lane ^ 2), the
+// half-row and row mirrors (lane i of each 8 / 16 lanes meets lane 7 - i / 15 - i), v_permlane16_swap
+// between the 16-lane rows of a 32-lane half and v_permlane32_swap between the halves. Every step combines
+// a lane with a partner that holds the partner group's result, so each lane of the group ends with the
+// same value. The (value, index) maximum uses a total order (larger value, then lower index), so its
+// result does not depend on the pairing.
+template <int CTRL>
+__device__ __forceinline__ int dpp_move(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int W, typename Op>
+__device__ __forceinline__ float group_reduce(float v, Op op) {
+  static_assert(W >= 2 && W <= 64 && (W & (W - 1)) == 0, "group of 2 .. 64 lanes");
+  v = op(v, __int_as_float(dpp_move<0xB1>(__float_as_int(v))));                  // quad_perm [1, 0, 3, 2]
+  if (W >= 4) v = op(v, __int_as_float(dpp_move<0x4E>(__float_as_int(v))));      // quad_perm [2, 3, 0, 1]
+  if (W >= 8) v = op(v, __int_as_float(dpp_move<0x141>(__float_as_int(v))));     // row_half_mirror
+  if (W >= 16) v = op(v, __int_as_float(dpp_move<0x140>(__float_as_int(v))));    // row_mirror
+  if (W >= 32) {
+    // both results of a swap: the even row's and the odd row's value, in that order in both lanes
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  }
+  if (W >= 64) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  }
+  return v;
+}
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+  return group_reduce<W>(v, [](float x, float y) { return x + y; });
+}
+template <int W>
+__device__ __forceinline__ float group_max(float v) {
+  return group_reduce<W>(v, [](float x, float y) { return fmaxf(x, y); });
+}
+template <int W>
+__device__ __forceinline__ void am_group_reduce(float& v, int& i) {
+  static_assert(W >= 32 && (W == 32 || W == 64), "half-wave or wave groups");
+  auto step = [&](float ov, int oi) {
     if (am_better(ov, oi, v, i)) { v = ov; i = oi; }
+  };
+  step(__int_as_float(dpp_move<0xB1>(__float_as_int(v))), dpp_move<0xB1>(i));
+  step(__int_as_float(dpp_move<0x4E>(__float_as_int(v))), dpp_move<0x4E>(i));
+  step(__int_as_float(dpp_move<0x141>(__float_as_int(v))), dpp_move<0x141>(i));
+  step(__int_as_float(dpp_move<0x140>(__float_as_int(v))), dpp_move<0x140>(i));
+  {  // value and index of the same lane in the same result slot
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap((uint32_t)i, (uint32_t)i, false, false);
+    v = __uint_as_float(a[0]);
+    i = (int)b[0];
+    step(__uint_as_float(a[1]), (int)b[1]);
+  }
+  if (W == 64) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap((uint32_t)i, (uint32_t)i, false, false);
+    v = __uint_as_float(a[0]);
+    i = (int)b[0];
+    step(__uint_as_float(a[1]), (int)b[1]);
   }
 }
 
@@ -79,15 +134,9 @@ __device__ __forceinline__ float rows_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, PE_WAVE);
-  return v;
-}
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
-__device__ __forceinline__ float wave_max(float v) {
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, PE_WAVE));
-  return v;
-}
+__device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
 
 // sum over a block of NT threads (NT multiple of 64, <= 1024); every thread gets the total.
 // Fixed reduction order, so results are bit-reproducible.

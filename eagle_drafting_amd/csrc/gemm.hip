@@ -459,7 +459,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
       float v = ok ? Y(t, r, c) : -INFINITY;
       int idx = ok ? n : 0x7fffffff;
       if (g.logits && ok) g.logits[(size_t)m * g.ldz + n] = v;
-      am_wave_reduce(v, idx, 64);
+      am_group_reduce<64>(v, idx);
       if (lane == 0) {
         g.am_val[(size_t)m * g.ngroups + blockIdx.x] = v;
         g.am_idx[(size_t)m * g.ngroups + blockIdx.x] = idx;
@@ -477,7 +477,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
         g.XGout[(size_t)m * N + n] = f32_to_bf16(v * bf16_to_f32(g.gain_next[n]));
       }
       float sq = v * v;
-      for (int off = CW / 2; off > 0; off >>= 1) sq += __shfl_xor(sq, off, PE_WAVE);
+      sq = group_sum<CW>(sq);
       if (c == 0) g.ssq_out[(size_t)m * g.nssq_out + nt] = sq;
     }
   } else if (EP == EPI_ROWS) {
@@ -514,10 +514,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g) {
           }
       }
       float s0 = x0 * x0, s1 = ph * ph;
-      for (int off = CW / 2; off > 0; off >>= 1) {
-        s0 += __shfl_xor(s0, off, PE_WAVE);
-        s1 += __shfl_xor(s1, off, PE_WAVE);
-      }
+      s0 = group_sum<CW>(s0);
+      s1 = group_sum<CW>(s1);
       if (c == 0) {
         g.ssq_out[(size_t)(b * Kr + i) * g.nssq_out + nt] = s0;
         if (i == 0)
@@ -679,7 +677,7 @@ __global__ __launch_bounds__(256) void rows_ssq_kernel(const float* __restrict__
       XG[(size_t)m * d + c] = f32_to_bf16(v * bf16_to_f32(gain[c]));
     }
     float sq = v * v;
-    for (int off = 8; off > 0; off >>= 1) sq += __shfl_xor(sq, off, PE_WAVE);
+    sq = group_sum<16>(sq);
     if ((c & 15) == 0 && c / 16 < nssq) ssq[(size_t)m * nssq + c / 16] = sq;
   }
 }
@@ -716,7 +714,7 @@ __global__ __launch_bounds__(256) void ar_rows_kernel(float* __restrict__ X, bf1
       XG[(size_t)b * d + c] = f32_to_bf16(v * bf16_to_f32(gain[c]));
     }
     float sq = v * v;
-    for (int off = 8; off > 0; off >>= 1) sq += __shfl_xor(sq, off, PE_WAVE);
+    sq = group_sum<16>(sq);
     if ((c & 15) == 0 && c / 16 < nssq) ssq[(size_t)b * nssq + c / 16] = sq;
   }
 }

@@ -576,7 +576,7 @@ __device__ void tile_epilogue(const GemmArgs& g, const float* Cs, const float* s
             for (int e = 0; e < 4; ++e)
               if (n + e < N) z[n + e] = vv[e];
         }
-        am_wave_reduce(bv, bi, 32);
+        am_group_reduce<32>(bv, bi);
         if (h == 0 && m < M) {
           g.am_val[(size_t)m * g.ngroups + ng] = bv;
           g.am_idx[(size_t)m * g.ngroups + ng] = bi;
@@ -663,10 +663,8 @@ __device__ void tile_epilogue(const GemmArgs& g, const float* Cs, const float* s
           }
         }
         // one partial sum of squares per row and 128-column workgroup tile
-        for (int off = 16; off > 0; off >>= 1) {
-          sq0 += __shfl_xor(sq0, off, PE_WAVE);
-          if (EP == EPI_ROWS) sq1 += __shfl_xor(sq1, off, PE_WAVE);
-        }
+        sq0 = group_sum<32>(sq0);
+        if (EP == EPI_ROWS) sq1 = group_sum<32>(sq1);
         if (h == 0 && m < M) {
           if (EP == EPI_RESID) {
             g.ssq_out[(size_t)m * g.nssq_out + ng] = sq0;
