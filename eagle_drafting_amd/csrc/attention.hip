@@ -558,14 +558,15 @@ __global__ __launch_bounds__(256) void attn_combine_quarter_kernel(const float* 
   float num[CPT];
 #pragma unroll
   for (int e = 0; e < CPT; ++e) num[e] = 0.f;
-#pragma unroll
-  for (int t = 0; t < SMAX; ++t) {
+  // split t's weight: lane t of the quarter (a 16-lane DPP row) broadcast to the row (row_newbcast)
+  static_for<0, SMAX>([&](auto tc) {
+    constexpr int t = decltype(tc)::value;
     if (t < ns) {
-      const float wt = __shfl(w_l, t, 16);
+      const float wt = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(w_l), 0x150 + t, 0xF, 0xF, false));
 #pragma unroll
       for (int e = 0; e < CPT; ++e) num[e] += wt * o[t][e];
     }
-  }
+  });
   const float inv = 1.f / den;
 #pragma unroll
   for (int e = 0; e < CPT; ++e) out[e] = f32_to_bf16(num[e] * inv);
@@ -616,7 +617,7 @@ __global__ __launch_bounds__(256) void attn_combine_wave_kernel(const float* __r
 #pragma unroll
   for (int t = 0; t < SMAX; ++t) {
     if (t < ns) {
-      const float wt = __shfl(w_l, t, PE_WAVE);
+      const float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_l), t));  // lane t's weight
 #pragma unroll
       for (int e = 0; e < CPT; ++e) num[e] += wt * o[t][e];
     }

@@ -1,5 +1,6 @@
 // Device helpers shared by the gfx950 kernels of the P-EAGLE draft / verify path.
 #pragma once
+#include <type_traits>
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -62,6 +63,14 @@ __device__ __forceinline__ bool am_better(float v, int i, float bv, int bi) {
 // a lane with a partner that holds the partner group's result, so each lane of the group ends with the
 // same value. The (value, index) maximum uses a total order (larger value, then lower index), so its
 // result does not depend on the pairing.
+// f(std::integral_constant<int, T>()) for T = B .. E - 1 (compile-time lane and control indices)
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>());
+    static_for<B + 1, E>(f);
+  }
+}
 template <int CTRL>
 __device__ __forceinline__ int dpp_move(int v) {
   return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
