@@ -43,6 +43,30 @@ template <int EP, bool SCALE>
 __device__ void tile_epilogue(const GemmArgs& g, const float* Cs, const float* s_inv, int m0, int nt0, int ng,
                               int rbeg = 0, int rend = 128, int etid = -1);
 
+// 1 / RMS of the 128 rows of a tile from the producer's partial sums of squares, TPR threads per row (TPR =
+// threads / 128): start() issues the loads of up to eight partials per thread before the product loop, so
+// that their latency overlaps it, and finish() adds them (in a fixed order, then across the row's threads)
+// after it; partials beyond TPR * 8 are loaded there (none for the producers of these tiles' operands).
+template <int NTH>
+struct RowScale {
+  static constexpr int TPR = NTH / 128, PRE = 8;
+  float v[PRE];
+  const float* src = nullptr;
+  __device__ __forceinline__ void start(const GemmArgs& g, int m0, int tid) {
+    const int r = tid / TPR, h = tid % TPR;
+    if (m0 + r < g.M) src = g.ssq_in + (size_t)gemm_a_row(g, m0 + r) * g.nssq;
+#pragma unroll
+    for (int u = 0; u < PRE; ++u) v[u] = src && h + TPR * u < g.nssq ? src[h + TPR * u] : 0.f;
+  }
+  __device__ __forceinline__ void finish(const GemmArgs& g, float* s_inv, int tid) {
+    const int r = tid / TPR, h = tid % TPR;
+    float t = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    for (int i = h + TPR * PRE; src && i < g.nssq; i += TPR) t += src[i];
+    t = group_sum<TPR>(t);
+    if (h == 0) s_inv[r] = rsqrtf(t / (float)g.Kd + g.eps);
+  }
+};
+
 // SPLIT: the workgroup covers k-steps [blockIdx.y * g.kper, + g.kper) and writes its fp32 partial tile
 // (row-scaled for a normalised operand) to g.part[blockIdx.y]; gemm_split_reduce_kernel adds the partials
 // in a fixed order and runs the epilogue.
@@ -204,6 +228,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
     }
   };
 
+  RowScale<256> rs;
+  if (AM == A_NORM && !SPLIT) rs.start(g, m0, tid);
   // activations run two stages ahead (register set, then LDS buffer), weights one stage ahead
   gload_a(ra0, 0);
   gload_b(rb0, 0);
@@ -237,18 +263,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
               F8 ? acc[i][j][e] * g.wscale[min(nt0 * 16 + 64 * wn + 32 * j + c, Nt * 16 - 1)] : acc[i][j][e];
         }
   }
-  if (AM == A_NORM && !SPLIT) {
-    // 1 / RMS per row from the producer's partial sums of squares (two threads per row); a K-split
-    // product leaves the row scale to the reduce kernel
-    const int r = tid >> 1, h = tid & 1;
-    float t = 0.f;
-    if (m0 + r < M) {
-      const float* src = g.ssq_in + (size_t)gemm_a_row(g, m0 + r) * g.nssq;
-      for (int i = h; i < g.nssq; i += 2) t += src[i];
-    }
-    t += __shfl_xor(t, 1, PE_WAVE);
-    if (h == 0) s_inv[r] = rsqrtf(t / (float)g.Kd + g.eps);
-  }
+  // 1 / RMS per row (a K-split product leaves the row scale to the reduce kernel)
+  if (AM == A_NORM && !SPLIT) rs.finish(g, s_inv, tid);
   __syncthreads();
 
   if (SPLIT) tile_epilogue<EPI_PARTIAL, false>(g, Cs, s_inv, m0, nt0, ng);
@@ -378,6 +394,8 @@ __global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(GemmArgs g) {
     }
   };
 
+  RowScale<NWV * 64> rs;
+  if (AM == A_NORM) rs.start(g, m0, tid);
   RegW w[NS];
 #pragma unroll
   for (int q = 0; q < NS - 1; ++q) {
@@ -391,17 +409,7 @@ __global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(GemmArgs g) {
   }
   __builtin_amdgcn_s_waitcnt(0x0070);  // the loads of the k-steps past the loop have landed
 
-  if (AM == A_NORM && tid < 256) {
-    // 1 / RMS per row from the producer's partial sums of squares (two threads per row)
-    const int r = tid >> 1, h = tid & 1;
-    float t = 0.f;
-    if (m0 + r < M) {
-      const float* src = g.ssq_in + (size_t)gemm_a_row(g, m0 + r) * g.nssq;
-      for (int i = h; i < g.nssq; i += 2) t += src[i];
-    }
-    t += __shfl_xor(t, 1, PE_WAVE);
-    if (h == 0) s_inv[r] = rsqrtf(t / (float)g.Kd + g.eps);
-  }
+  if (AM == A_NORM) rs.finish(g, s_inv, tid);  // 1 / RMS per row
   // two passes of QP 128 x 128 quarters: quarter QP p + s (columns 128 (QP p + s) ..) is held by waves
   // 2 (QP p + s) and 2 (QP p + s) + 1 and goes to LDS quarter s (column XOR-swizzle as in the 128 x 128
   // kernel), then waves 4 s .. 4 s + 3 run its epilogue
