@@ -509,7 +509,7 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs g) {
   if (SCALE) {
     float st = ((sv[0] + sv[1]) + (sv[2] + sv[3])) + ((sv[4] + sv[5]) + (sv[6] + sv[7]));
     for (int i0 = sh + 8 * TPR; ssrc && i0 < g.nssq; i0 += TPR) st += ssrc[i0];  // more than 8 TPR partials
-    for (int off = TPR / 2; off > 0; off >>= 1) st += __shfl_xor(st, off, PE_WAVE);
+    st = group_sum<TPR>(st);
     if (sh == 0) s_il[sr] = rsqrtf(st / (float)g.Kd + g.eps);
   }
   __syncthreads();
@@ -968,7 +968,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 3 ? 3
         t += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
       }
     }
-    for (int off = TPR / 2; off > 0; off >>= 1) t += __shfl_xor(t, off, PE_WAVE);
+    t = group_sum<TPR>(t);
     if (h == 0 && r < 32 * RB) s_inv[r] = rsqrtf(t / (float)g.Kd + g.eps);
   }
   __syncthreads();

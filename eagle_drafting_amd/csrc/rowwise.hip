@@ -247,10 +247,8 @@ __global__ __launch_bounds__(256) void concat_norm_kernel(const float* __restric
     sh += x[c] * x[c];
     se += xe[c] * xe[c];
   }
-  for (int off = 32; off > 0; off >>= 1) {
-    sh += __shfl_xor(sh, off, PE_WAVE);
-    se += __shfl_xor(se, off, PE_WAVE);
-  }
+  sh = group_sum<64>(sh);
+  se = group_sum<64>(se);
   if (lane == 0) {
     red[0][wave] = sh;
     red[1][wave] = se;
